@@ -1,0 +1,202 @@
+"""Benchmark of the gated delta rule hot path on one MI355X.
+
+A step is one pass of the path over one batch of synthetic input:
+  * prefill: kda_prefill_chunked on the long-context workload
+    (B=1, H=16, d_k=d_v=128, T=262144, bf16 q/k/v, scalar alpha, C=64),
+    emitting o and the final state -- `value` is its throughput in tokens/s;
+  * decode: kda_decode_step on the batched-decode workload (B=256, H=16,
+    d=128, per-key alpha, fp32 state updated in place) -- reported in
+    `decode.us_per_step`.
+Inputs are generated on the GPU (seeded) and resident in HBM before timing.
+Kernel durations come from HIP events on the stream the kernels are launched
+on (torch's current stream). Roofline figures use algorithmic bytes and flops:
+  prefill bytes = q,k,v (bf16) + alpha + beta + o (fp32) + final state,
+  prefill flops per chunk-head = 6 C dk dv + 3 C^2 dk + 2 C^2 dv + C^3/3,
+  decode bytes = state read + write + q,k,v + alpha + beta + o.
+The CPU baseline is the fp64 oracle on the host's cores over a bounded
+token prefix of the same prefill workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill tokens/s @T=256K H16 d128; decode µs/step @B256; % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, TFLOP/s
+
+
+def prefill_algorithmic(T, H, dk, dv, n_seqs, per_key, qkv_bytes=2, C=64, with_init=False, n_snap=0):
+    b = T * H * (2 * dk + dv) * qkv_bytes          # q, k, v
+    b += T * H * (dk if per_key else 1) * 4        # alpha
+    b += T * H * 4                                 # beta
+    b += T * H * dv * 4                            # o
+    b += n_seqs * H * dv * dk * 4                  # final state
+    if with_init:
+        b += n_seqs * H * dv * dk * 4
+    b += n_snap * H * dv * dk * 4
+    chunks = T / C                                 # full chunks (all configs are multiples of 64 here)
+    f = chunks * H * (6 * C * dk * dv + 3 * C * C * dk + 2 * C * C * dv + C ** 3 / 3)
+    return b, f
+
+
+def decode_algorithmic(B, H, dk, dv, per_key, qkv_bytes=2):
+    b = 2 * B * H * dv * dk * 4                    # state read + write
+    b += B * H * (2 * dk + dv) * qkv_bytes
+    b += B * H * (dk if per_key else 1) * 4 + B * H * 4 + B * H * dv * 4
+    f = B * H * dv * (7 * dk)                      # decay, 2 dots, update, read-out
+    return b, f
+
+
+def time_prefill(kda, torch, inp, w, steps, warmup):
+    T, H, dk, dv = w.T, w.H, w.dk, w.dv
+    dev = inp["q"].device
+    shape = kda.make_shape(H, dk, dv, inp["q"].dtype, w.gate == "per_key")
+    cu_h = inp["cu_seqlens_host"]
+    o = torch.empty((T, H, dv), dtype=torch.float32, device=dev)
+    fin = torch.empty((w.num_seqs, H, dv, dk), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(kda.kda_prefill_workspace_size(shape, cu_h, 64, 0), 1), dtype=torch.uint8,
+                     device=dev)
+
+    def call():
+        kda.kda_prefill_chunked(shape, cu_h, inp["cu_seqlens"], inp["q"], inp["k"], inp["v"],
+                                inp["alpha"], inp["beta"], inp["initial_state"], o, fin, None, ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        call()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = [s.elapsed_time(e) for s, e in ev]
+    return ms, wall
+
+
+def time_decode(kda, torch, w, steps, warmup, n_buffers=4):
+    from gated_delta_rule_72_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    bufs = [wl.make_decode_inputs(w, dev, seed=w.seed + i) for i in range(n_buffers)]
+    outs = [torch.empty((w.num_seqs, w.H, w.dv), dtype=torch.float32, device=dev) for _ in bufs]
+    shape = kda.make_shape(w.H, w.dk, w.dv, bufs[0]["q"].dtype, w.gate == "per_key")
+
+    def call(i):
+        d = bufs[i % n_buffers]
+        kda.kda_decode_step(shape, w.num_seqs, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state"],
+                            outs[i % n_buffers])
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (s, e) in enumerate(ev):
+        s.record(stream)
+        call(i)
+        e.record(stream)
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) for s, e in ev]
+
+
+def cpu_baseline(w, inp, tokens: int):
+    """fp64 oracle on the host over the first `tokens` tokens of the workload."""
+    from gated_delta_rule_72_amd import workloads as wl
+    import oracle
+    sl = slice(0, tokens)
+    A = {n: wl.to_oracle_arrays(inp[n][sl]) for n in ("q", "k", "v", "alpha", "beta")}
+    import numpy as np
+    t0 = time.perf_counter()
+    rc, rep = oracle.ref_check(A["q"], A["k"], A["v"], A["alpha"], A["beta"],
+                               np.array([0, tokens], np.int64), None, 0)
+    secs = time.perf_counter() - t0
+    return {"value": tokens / secs, "unit": "tokens/s", "cores": int(rep["threads"]), "kind": "oracle",
+            "sample": f"first {tokens} of {w.T} tokens, all {w.H} heads, fp64 token-by-token recurrence",
+            "seconds": round(secs, 3)}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--cpu-tokens", type=int, default=4096,
+                    help="token prefix the CPU oracle baseline runs on (0 = skip)")
+    ap.add_argument("--skip-decode", action="store_true")
+    ap.add_argument("--prefill-only", action="store_true", help="profiling: only the prefill loop")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (every GPU box here "
+              f"has one GPU). Sharding is described in DESIGN.md.", file=sys.stderr)
+        return 2
+
+    import torch
+    import gated_delta_rule_72_amd as kda
+    from gated_delta_rule_72_amd import workloads as wl
+
+    kda.load()
+    dev = torch.device("cuda:0")
+    w = wl.LONG_PREFILL
+    inp = wl.make_prefill_inputs(w, dev)
+    torch.cuda.synchronize()
+    ms, wall = time_prefill(kda, torch, inp, w, args.steps, args.warmup)
+    ms_avg = sum(ms) / len(ms)
+    pb, pf = prefill_algorithmic(w.T, w.H, w.dk, w.dv, w.num_seqs, w.gate == "per_key")
+    gbs = pb / (ms_avg * 1e-3) / 1e9
+    tfl = pf / (ms_avg * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": w.T / (ms_avg * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_avg,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16-mfma/fp32-state",
+        "data": "synthetic (seeded; no dataset)",
+        "config": {"workload": w.name, "B": 1, "T": w.T, "H": w.H, "d_k": w.dk, "d_v": w.dv,
+                   "gate": w.gate, "chunk": w.chunk, "qkv": w.dtype},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "prefill_kernel<128,bf16,scalar>",
+                     "algorithmic_bytes_per_launch": int(pb), "algorithmic_flops_per_launch": int(pf),
+                     "mfma_tflops": round(tfl, 2), "mfma_frac": round(tfl / MFMA_F16_PEAK_TFLOPS, 4),
+                     "attainable_frac": round((pb / (HBM_PEAK_GBS * 1e9)) / (ms_avg * 1e-3), 4)},
+        "prefill_ms": {"avg": ms_avg, "min": min(ms), "max": max(ms)},
+        "kernel_level": "hip-gfx950-chunked-v1",
+    }
+    del inp
+    torch.cuda.empty_cache()
+    if not args.skip_decode and not args.prefill_only:
+        d = wl.DECODE
+        dms = time_decode(kda, torch, d, max(args.steps, 20), args.warmup)
+        davg = sum(dms) / len(dms)
+        db, df = decode_algorithmic(d.num_seqs, d.H, d.dk, d.dv, d.gate == "per_key")
+        dgbs = db / (davg * 1e-3) / 1e9
+        result["decode"] = {"workload": d.name, "us_per_step": davg * 1e3, "us_min": min(dms) * 1e3,
+                            "roofline": {"bound": "hbm", "achieved": round(dgbs, 1), "peak": HBM_PEAK_GBS,
+                                         "unit": "GB/s", "frac": round(dgbs / HBM_PEAK_GBS, 4),
+                                         "algorithmic_bytes_per_launch": int(db)},
+                            "kernel_level": "hip-gfx950-decode-v1"}
+    if args.cpu_tokens > 0 and not args.prefill_only:
+        inp = wl.make_prefill_inputs(w, dev)
+        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_tokens)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

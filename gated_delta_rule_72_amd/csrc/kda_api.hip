@@ -1,0 +1,220 @@
+// kda_api.hip — host side of libkda.so: argument validation, workspace
+// sizing and kernel launches for the C ABI declared in include/kda.h.
+// Nothing is enqueued before every check has passed.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// Alignment each pointer needs for the loads and stores the kernels issue on
+// it: q, k, v, per-key alpha and every state are moved in 16-byte vectors
+// (fp32 q/k/v and states) or 8-byte vectors (bf16 q/k/v in the decode step);
+// scalar alpha, beta and o are moved one fp32 at a time; cu_seqlens in int64.
+struct PtrReq {
+  const void* p;
+  uintptr_t align;
+  const char* name;
+};
+int check_align(const PtrReq* reqs, int n) {
+  for (int i = 0; i < n; ++i)
+    if (reqs[i].p && !aligned(reqs[i].p, reqs[i].align))
+      return fail(KDA_ERR_ALIGN, "%s (%p) must be %u-byte aligned", reqs[i].name, reqs[i].p,
+                  (unsigned)reqs[i].align);
+  return KDA_OK;
+}
+
+constexpr int64_t kChunk = 64;
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int check_shape(const kda_shape* s) {
+  if (!s) return fail(KDA_ERR_ARG, "shape is NULL");
+  if (s->num_heads <= 0) return fail(KDA_ERR_SHAPE, "num_heads must be positive (got %d)", s->num_heads);
+  if (s->d_k != s->d_v || (s->d_k != 64 && s->d_k != 128))
+    return fail(KDA_ERR_SHAPE, "d_k = d_v in {64, 128} required (got d_k=%d d_v=%d)", s->d_k, s->d_v);
+  if (s->qkv_dtype != KDA_BF16 && s->qkv_dtype != KDA_F32)
+    return fail(KDA_ERR_ARG, "qkv_dtype must be KDA_BF16 or KDA_F32 (got %d)", s->qkv_dtype);
+  if (s->gate != KDA_GATE_SCALAR && s->gate != KDA_GATE_PER_KEY)
+    return fail(KDA_ERR_ARG, "gate must be KDA_GATE_SCALAR or KDA_GATE_PER_KEY (got %d)", s->gate);
+  return KDA_OK;
+}
+
+// cu_seqlens: cu[0] == 0, nondecreasing, every length fits int32.
+int check_cu(int32_t num_seqs, const int64_t* cu) {
+  if (num_seqs < 0) return fail(KDA_ERR_ARG, "num_seqs must be >= 0 (got %d)", num_seqs);
+  if (!cu) return fail(KDA_ERR_ARG, "cu_seqlens_host is NULL");
+  if (cu[0] != 0) return fail(KDA_ERR_SHAPE, "cu_seqlens[0] must be 0 (got %lld)", (long long)cu[0]);
+  for (int32_t n = 0; n < num_seqs; ++n) {
+    const int64_t len = cu[n + 1] - cu[n];
+    if (len < 0) return fail(KDA_ERR_SHAPE, "cu_seqlens decreases at index %d", n + 1);
+    if (len > INT32_MAX - kChunk) return fail(KDA_ERR_SHAPE, "sequence %d is too long", n);
+  }
+  return KDA_OK;
+}
+
+int64_t snapshot_slots(int32_t num_seqs, const int64_t* cu, int64_t interval) {
+  if (interval <= 0) return 0;
+  int64_t total = 0;
+  for (int32_t n = 0; n < num_seqs; ++n) total += (cu[n + 1] - cu[n]) / interval;
+  return total;
+}
+
+struct PrefillPlan {
+  int32_t n_items;
+  size_t items_off, bytes;
+};
+
+PrefillPlan plan_prefill(const kda_shape* s, int32_t num_seqs, const int64_t* cu) {
+  (void)s;
+  (void)cu;
+  PrefillPlan p{};
+  p.n_items = num_seqs;
+  p.items_off = 0;
+  p.bytes = round_up(sizeof(kda::PrefillItem) * (size_t)(num_seqs > 0 ? num_seqs : 1));
+  return p;
+}
+
+int check_prefill_args(const kda_shape* shape, int32_t num_seqs, const int64_t* cu,
+                       int32_t chunk, int64_t interval) {
+  int rc = check_shape(shape);
+  if (rc != KDA_OK) return rc;
+  rc = check_cu(num_seqs, cu);
+  if (rc != KDA_OK) return rc;
+  if (chunk != kChunk) return fail(KDA_ERR_SHAPE, "chunk must be 64 (got %d)", chunk);
+  if (interval < 0 || interval % kChunk != 0)
+    return fail(KDA_ERR_SHAPE, "snapshot_interval must be 0 or a positive multiple of 64 (got %lld)",
+                (long long)interval);
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_last_error(void) { return g_err; }
+
+int kda_snapshot_count(int32_t num_seqs, const int64_t* cu_seqlens_host, int64_t interval,
+                       int64_t* n_snap) {
+  if (!n_snap) return fail(KDA_ERR_ARG, "n_snap is NULL");
+  int rc = check_cu(num_seqs, cu_seqlens_host);
+  if (rc != KDA_OK) return rc;
+  if (interval < 0) return fail(KDA_ERR_SHAPE, "interval must be >= 0");
+  *n_snap = snapshot_slots(num_seqs, cu_seqlens_host, interval);
+  g_err[0] = '\0';
+  return KDA_OK;
+}
+
+int kda_prefill_workspace_size(const kda_shape* shape, int32_t num_seqs,
+                               const int64_t* cu_seqlens_host, int32_t chunk,
+                               int64_t snapshot_interval, size_t* bytes) {
+  if (!bytes) return fail(KDA_ERR_ARG, "bytes is NULL");
+  int rc = check_prefill_args(shape, num_seqs, cu_seqlens_host, chunk, snapshot_interval);
+  if (rc != KDA_OK) return rc;
+  *bytes = plan_prefill(shape, num_seqs, cu_seqlens_host).bytes;
+  g_err[0] = '\0';
+  return KDA_OK;
+}
+
+int kda_prefill_chunked(const kda_shape* shape, int32_t num_seqs,
+                        const int64_t* cu_seqlens_host, const int64_t* cu_seqlens_dev,
+                        int32_t chunk, int64_t snapshot_interval,
+                        const void* q, const void* k, const void* v,
+                        const float* alpha, const float* beta,
+                        const float* initial_state,
+                        float* o, float* final_state, float* snapshots,
+                        void* workspace, size_t workspace_bytes, void* hip_stream) {
+  int rc = check_prefill_args(shape, num_seqs, cu_seqlens_host, chunk, snapshot_interval);
+  if (rc != KDA_OK) return rc;
+  const int64_t T = cu_seqlens_host[num_seqs];
+  const int64_t n_snap = snapshot_slots(num_seqs, cu_seqlens_host, snapshot_interval);
+  if (num_seqs > 0 && !cu_seqlens_dev) return fail(KDA_ERR_ARG, "cu_seqlens_dev is NULL");
+  if (T > 0 && (!q || !k || !v || !alpha || !beta || !o))
+    return fail(KDA_ERR_ARG, "q, k, v, alpha, beta and o must be non-NULL when T > 0");
+  if (num_seqs > 0 && !final_state) return fail(KDA_ERR_ARG, "final_state is NULL");
+  if (n_snap > 0 && !snapshots)
+    return fail(KDA_ERR_ARG, "snapshots is NULL but %lld snapshot slots are due", (long long)n_snap);
+  const uintptr_t a_alpha = shape->gate == KDA_GATE_PER_KEY ? 16 : 4;
+  const PtrReq reqs[] = {{q, 16, "q"}, {k, 16, "k"}, {v, 16, "v"}, {alpha, a_alpha, "alpha"},
+                         {beta, 4, "beta"}, {initial_state, 16, "initial_state"}, {o, 4, "o"},
+                         {final_state, 16, "final_state"},
+                         {n_snap > 0 ? snapshots : nullptr, 16, "snapshots"},
+                         {cu_seqlens_dev, 8, "cu_seqlens_dev"}, {workspace, 16, "workspace"}};
+  rc = check_align(reqs, (int)(sizeof reqs / sizeof reqs[0]));
+  if (rc != KDA_OK) return rc;
+  const PrefillPlan plan = plan_prefill(shape, num_seqs, cu_seqlens_host);
+  if (num_seqs > 0 && (!workspace || workspace_bytes < plan.bytes))
+    return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", plan.bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  if (num_seqs == 0) {
+    g_err[0] = '\0';
+    return KDA_OK;
+  }
+
+  kda::PrefillArgs a{};
+  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.init = initial_state;
+  a.o = o; a.final_state = final_state; a.snapshots = snapshots;
+  a.cu_dev = cu_seqlens_dev;
+  a.num_seqs = num_seqs;
+  a.H = shape->num_heads;
+  a.interval = snapshot_interval;
+  a.seg_chunks = 0;
+  a.n_items = plan.n_items;
+  a.items = reinterpret_cast<kda::PrefillItem*>(static_cast<char*>(workspace) + plan.items_off);
+  a.seg_maps = nullptr;
+  a.seg_states = nullptr;
+  hipError_t e = kda::launch_prefill(a, shape->d_k, shape->qkv_dtype == KDA_BF16,
+                                     shape->gate == KDA_GATE_PER_KEY,
+                                     static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "prefill launch failed: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return KDA_OK;
+}
+
+int kda_decode_step(const kda_shape* shape, int32_t batch, const void* q, const void* k,
+                    const void* v, const float* alpha, const float* beta, float* state,
+                    float* o, void* hip_stream) {
+  int rc = check_shape(shape);
+  if (rc != KDA_OK) return rc;
+  if (batch < 0) return fail(KDA_ERR_ARG, "batch must be >= 0 (got %d)", batch);
+  if (batch == 0) {
+    g_err[0] = '\0';
+    return KDA_OK;
+  }
+  if ((int64_t)batch * shape->num_heads > INT32_MAX / 2)
+    return fail(KDA_ERR_SHAPE, "batch * num_heads too large");
+  if (!q || !k || !v || !alpha || !beta || !state || !o)
+    return fail(KDA_ERR_ARG, "q, k, v, alpha, beta, state and o must be non-NULL");
+  const uintptr_t a_qkv = shape->qkv_dtype == KDA_BF16 ? 8 : 16;
+  const uintptr_t a_alpha = shape->gate == KDA_GATE_PER_KEY ? 16 : 4;
+  const PtrReq reqs[] = {{q, a_qkv, "q"}, {k, a_qkv, "k"}, {v, 4, "v"}, {alpha, a_alpha, "alpha"},
+                         {beta, 4, "beta"}, {state, 16, "state"}, {o, 4, "o"}};
+  rc = check_align(reqs, (int)(sizeof reqs / sizeof reqs[0]));
+  if (rc != KDA_OK) return rc;
+  kda::DecodeArgs a{q, k, v, alpha, beta, state, o, batch, shape->num_heads};
+  hipError_t e = kda::launch_decode(a, shape->d_k, shape->qkv_dtype == KDA_BF16,
+                                    shape->gate == KDA_GATE_PER_KEY,
+                                    static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "decode launch failed: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return KDA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,133 @@
+// kda_decode.hip — one O(1)-state decode step of the gated delta rule.
+//
+// Page "Modele hybrydowe: co Gated DeltaNet zastępuje w cache KV" (trefon.com),
+// section "Gated DeltaNet: dodaj zanik" (update) and "Atencja liniowa: stan o
+// stałym rozmiarze" (read-out o_t = S_t q_t). Row i of the d_v x d_k state is
+// updated on its own:
+//     s' = s_i * a          (decay on the key axis; scalar gate: a = alpha)
+//     p  = s' . k           (what the state predicts for k)
+//     r  = s' . q
+//     u  = beta (v_i - p)   (the written error)
+//     s_i <- s' + u k
+//     o_i = s_i . q = r + u (k . q)
+// The step reads and writes each state element exactly once; the kernel is
+// bound by HBM bandwidth (about 0.86 flop per byte).
+//
+// Mapping (D = d_k = d_v in {64, 128}): one workgroup per (sequence, head),
+// D/32 wavefronts, 32 state rows per wavefront. A row is D/4 lanes wide (one
+// 16-byte float4 per lane), so a wavefront holds G = 256/D rows side by side
+// and every load instruction moves G consecutive rows (1 KiB). Each lane group
+// keeps R = 32/G rows in registers and finishes all 2R dot products of its
+// rows with one butterfly reduce-scatter: log2(D/4) shuffle steps in which
+// the number of live partial sums halves, leaving lane j of the group with
+// the full sum of value j.
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+// Lanes [base, base+N) of a group hold vals[0..N) each; afterwards lane
+// base+j returns the sum over the group of vals[j].
+template <int N>
+__device__ __forceinline__ float reduce_scatter(float (&vals)[N], int lane_in_group) {
+#pragma unroll
+  for (int m = N / 2; m >= 1; m >>= 1) {
+    const bool upper = (lane_in_group & m) != 0;
+#pragma unroll
+    for (int j = 0; j < m; ++j) {
+      const float send = upper ? vals[j] : vals[j + m];
+      const float keep = upper ? vals[j + m] : vals[j];
+      vals[j] = keep + __shfl_xor(send, m);
+    }
+  }
+  return vals[0];
+}
+
+template <int N>
+__device__ __forceinline__ float group_allreduce(float x) {
+#pragma unroll
+  for (int m = N / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+template <int D, bool BF16, bool PER_KEY>
+__global__ __launch_bounds__(D * 2) void decode_kernel(DecodeArgs a) {
+  constexpr int LPR = D / 4;      // lanes per state row
+  constexpr int G = 64 / LPR;     // rows side by side in a wavefront
+  constexpr int R = 32 / G;       // rows per lane group
+  static_assert(2 * R == LPR, "one reduced value per lane");
+
+  const int bh = blockIdx.x;      // (sequence, head) = b * H + h
+  const int wave = threadIdx.x / 64;
+  const int lane = threadIdx.x % 64;
+  const int g = lane / LPR;       // lane group within the wavefront
+  const int li = lane % LPR;      // lane within the group; owns columns 4li..4li+3
+
+  const int64_t vec_off = (int64_t)bh * D;
+  const f32x4 kv = load4<BF16>(a.k, vec_off + 4 * li);
+  const f32x4 qv = load4<BF16>(a.q, vec_off + 4 * li);
+  f32x4 av;
+  if constexpr (PER_KEY) {
+    av = *reinterpret_cast<const f32x4*>(a.alpha + vec_off + 4 * li);
+  } else {
+    const float s = a.alpha[bh];
+    av = f32x4{s, s, s, s};
+  }
+  const float beta = a.beta[bh];
+
+  // rows of this lane group: wave*32 + r*G + g, r = 0..R-1
+  float* state = a.state + (int64_t)bh * D * D;
+  f32x4 s[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int row = wave * 32 + r * G + g;
+    s[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(state + (int64_t)row * D + 4 * li));
+  }
+
+  float kq = kv[0] * qv[0] + kv[1] * qv[1] + kv[2] * qv[2] + kv[3] * qv[3];
+  kq = group_allreduce<LPR>(kq);
+
+  float vals[2 * R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    s[r] = s[r] * av;
+    vals[2 * r] = s[r][0] * kv[0] + s[r][1] * kv[1] + s[r][2] * kv[2] + s[r][3] * kv[3];
+    vals[2 * r + 1] = s[r][0] * qv[0] + s[r][1] * qv[1] + s[r][2] * qv[2] + s[r][3] * qv[3];
+  }
+  // lane li = 2r holds p_r, lane li = 2r+1 holds (s'_r . q)
+  const float red = reduce_scatter<2 * R>(vals, li);
+  const int my_r = li >> 1;
+  const int my_row = wave * 32 + my_r * G + g;
+  float u = 0.f;
+  if ((li & 1) == 0) u = beta * (load1<BF16>(a.v, vec_off + my_row) - red);
+  const float u_pair = __shfl_xor(u, 1);
+  if (li & 1) a.o[vec_off + my_row] = red + u_pair * kq;
+
+  const int group_base = lane - li;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float ur = __shfl(u, group_base + 2 * r);
+    const int row = wave * 32 + r * G + g;
+    const f32x4 upd = s[r] + ur * kv;
+    __builtin_nontemporal_store(upd, reinterpret_cast<f32x4*>(state + (int64_t)row * D + 4 * li));
+  }
+}
+
+template <int D, bool BF16, bool PK>
+hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((decode_kernel<D, BF16, PK>), dim3(a.batch * a.H), dim3(D * 2), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, bool per_key, hipStream_t s) {
+  if (d == 64) {
+    if (bf16) return per_key ? launch_t<64, true, true>(a, s) : launch_t<64, true, false>(a, s);
+    return per_key ? launch_t<64, false, true>(a, s) : launch_t<64, false, false>(a, s);
+  }
+  if (bf16) return per_key ? launch_t<128, true, true>(a, s) : launch_t<128, true, false>(a, s);
+  return per_key ? launch_t<128, false, true>(a, s) : launch_t<128, false, false>(a, s);
+}
+
+}  // namespace kda

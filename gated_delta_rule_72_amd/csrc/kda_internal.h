@@ -1,0 +1,81 @@
+// kda_internal.h — shared definitions of the gfx950 kernels and the host API
+// of libkda.so (not part of the public ABI; see include/kda.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// bf16 bit pattern -> fp32 (exact: bf16 is the upper half of an fp32).
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Four consecutive q/k/v elements starting at element index `idx`.
+template <bool BF16>
+__device__ __forceinline__ f32x4 load4(const void* base, int64_t idx) {
+  if constexpr (BF16) {
+    const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + idx);
+    f32x4 r;
+    r[0] = bf16_bits_to_f32(w.x & 0xFFFFu);
+    r[1] = bf16_bits_to_f32(w.x >> 16);
+    r[2] = bf16_bits_to_f32(w.y & 0xFFFFu);
+    r[3] = bf16_bits_to_f32(w.y >> 16);
+    return r;
+  } else {
+    return *reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + idx);
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load1(const void* base, int64_t idx) {
+  if constexpr (BF16)
+    return bf16_bits_to_f32(static_cast<const uint16_t*>(base)[idx]);
+  else
+    return static_cast<const float*>(base)[idx];
+}
+
+// ---- launch entry points (defined in the .hip files) -----------------------
+
+struct DecodeArgs {
+  const void *q, *k, *v;
+  const float *alpha, *beta;
+  float *state, *o;
+  int32_t batch, H;
+};
+hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, bool per_key, hipStream_t s);
+
+// One unit of prefill work: a contiguous run of chunks of one sequence.
+struct PrefillItem {
+  int64_t tok_begin;   // first token (global index into q/k/v/o)
+  int32_t n_tokens;    // tokens in this item
+  int32_t seq;         // sequence index n
+  int32_t seg;         // segment index within the sequence (0 if unsegmented)
+  int32_t n_segs;      // segments of this sequence
+  int64_t tok_in_seq;  // position of tok_begin inside its sequence
+  int64_t snap_base;   // first snapshot slot of the sequence
+};
+
+struct PrefillArgs {
+  const void *q, *k, *v;
+  const float *alpha, *beta;
+  const float* init;         // [N,H,dv,dk] or null
+  float *o, *final_state, *snapshots;
+  const int64_t* cu_dev;     // [N+1]
+  int32_t num_seqs, H;
+  int64_t interval;          // snapshot interval (0 = none)
+  int32_t seg_chunks;        // chunks per segment (0 = unsegmented)
+  int32_t n_items;           // work items (sequence segments)
+  PrefillItem* items;        // workspace: [n_items]
+  float* seg_maps;           // workspace: per (item, head) M (dk x dk) and N (dv x dk)
+  float* seg_states;         // workspace: per (item, head) start state (dv x dk)
+};
+hipError_t launch_prefill(const PrefillArgs& a, int d, bool bf16, bool per_key, hipStream_t s);
+
+}  // namespace kda

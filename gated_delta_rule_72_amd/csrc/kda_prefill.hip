@@ -1,0 +1,660 @@
+// kda_prefill.hip — chunkwise-parallel prefill of the gated delta rule on gfx950.
+//
+// The update (page "Modele hybrydowe: co Gated DeltaNet zastępuje w cache KV",
+// trefon.com, section "Gated DeltaNet: dodaj zanik") with the per-key-channel
+// decay read as Diag(a_t) on the key axis:
+//     S_t = S_{t-1} Diag(a_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,  o_t = S_t q_t.
+// The same page (closing paragraph of "Co stan rekurencyjny zmienia przy
+// serwowaniu") states that inside a chunk the updates are dense matrix
+// products and only chunk-to-chunk is sequential. For a chunk of n <= 64
+// tokens with start state S0 and in-chunk cumulative log decay
+// G_r = sum_{i<=r} log2 a_i (row r = token r, column = key channel):
+//     L_ri = beta_r sum_j k_r[j] k_i[j] 2^(G_r[j]-G_i[j])   (i < r)
+//     A    = (I + L)^-1,  T~ = A Diag(beta)                 (UT / WY form)
+//     W    = T~ (K * 2^G),  U' = T~ V,  U = U' - W S0^T
+//     O    = (Q * 2^G) S0^T + B U,  B_ri = sum_j q_r[j] k_i[j] 2^(G_r[j]-G_i[j]) (i <= r)
+//     S_n  = S0 Diag(2^(G_n)) + U^T (K * 2^(G_n - G))
+//
+// Kernel structure. One workgroup per (sequence or segment, head); D/16
+// wavefronts (D = d_k = d_v). Wavefront w owns state rows 16w..16w+15 (a
+// "slice") and keeps S0^T for them in MFMA accumulator layout (fp32) for the
+// whole sequence. Per chunk:
+//   P1  raw q, k (fp16) and the decay cumsum G (fp32) to LDS; beta to LDS.
+//   P2  decayed operands in LDS: Q~ = Q*2^G [c][k], K^T*2^G and
+//       (K*2^(G_n-G))^T [k][c] (fp16).
+//   P3  Gram tiles on MFMA: L (fp32) and B (fp16). Scalar gate: exact
+//       fp16 products K K^T, Q K^T scaled by 2^(G_r-G_i) in fp32. Per-key
+//       gate: three-term bf16 products (hi*hi + hi*lo + lo*hi) of operands
+//       decayed relative to the first token of each 16-row block, so every
+//       factor stays in fp32/bf16 range.
+//   P4  (I + L)^-1 in LDS: four 16x16 unit-lower diagonal blocks by forward
+//       substitution (one column per lane), then the off-diagonal blocks in
+//       three dependent stages on fp32 MFMA.
+//   P5  T~ split into fp16 hi + lo; W = T~ (K*2^G) on MFMA.
+//   P6  per slice: U' = T~ V, U = U' - W S0^T, O = Q~ S0^T + B U,
+//       S0^T <- 2^(G_n) S0^T + (K*2^(G_n-G))^T U. U and T~ enter their
+//       products as fp16 hi + lo pairs; the state stays fp32. The next
+//       chunk's inputs are loaded into registers while P6 runs.
+// Accumulator layout of a 16x16 MFMA tile: lane l holds rows 4(l/16)+i,
+// column l%16. When an accumulator tile feeds the next product as its
+// K-operand, the K index is permuted (lane group g supplies rows 4g..4g+3 of
+// each of two tiles) and the other operand is read with the same permutation,
+// so no data moves between lanes.
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int C = 64;  // chunk length
+
+__device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Row (l%16) of a row-major fp16 matrix, the 8 K-elements of lane group
+// g = l/16 in the standard order: k0 + 8g .. k0 + 8g + 7.
+__device__ __forceinline__ f16x8 ld_std(const _Float16* base, int ld, int row0, int k0, int lane) {
+  return *reinterpret_cast<const f16x8*>(base + (row0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
+}
+// Same row, permuted K order: k0 + 4g + {0..3}, then k0 + 16 + 4g + {0..3}.
+__device__ __forceinline__ f16x8 ld_perm(const _Float16* base, int ld, int row0, int k0, int lane) {
+  const _Float16* p = base + (row0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4);
+  const f16x4 lo = *reinterpret_cast<const f16x4*>(p);
+  const f16x4 hi = *reinterpret_cast<const f16x4*>(p + 16);
+  return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+// Two accumulator tiles (rows k0..k0+15 and k0+16..k0+31) as a permuted-K operand.
+__device__ __forceinline__ f16x8 pack_perm(f32x4 t0, f32x4 t1) {
+  return f16x8{(_Float16)t0[0], (_Float16)t0[1], (_Float16)t0[2], (_Float16)t0[3],
+               (_Float16)t1[0], (_Float16)t1[1], (_Float16)t1[2], (_Float16)t1[3]};
+}
+__device__ __forceinline__ void split_perm(f32x4 t0, f32x4 t1, f16x8& hi, f16x8& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    hi[i] = (_Float16)t0[i];
+    lo[i] = (_Float16)(t0[i] - (float)hi[i]);
+    hi[4 + i] = (_Float16)t1[i];
+    lo[4 + i] = (_Float16)(t1[i] - (float)hi[4 + i]);
+  }
+}
+
+// ---- LDS layout -------------------------------------------------------------
+template <int D>
+struct Lds {
+  static constexpr int LDQ = D + 8;   // row stride of [64][D] fp16 arrays
+  static constexpr int LDT = C + 8;   // row stride of [D][64] / [64][64] fp16 arrays
+  static constexpr int LDL = C + 4;   // row stride of the fp32 64x64 L / inverse
+  static constexpr int LDG = D + 4;   // row stride of per-key G [64][D] fp32
+  // persistent through a chunk
+  static constexpr int OFF_QT = 0;                                  // Q~   [64][LDQ] f16
+  static constexpr int OFF_KHT = OFF_QT + C * LDQ * 2;              // K^  T [D][LDT] f16
+  static constexpr int OFF_KTT = OFF_KHT + D * LDT * 2;             // K~ T  [D][LDT] f16
+  static constexpr int OFF_B = OFF_KTT + D * LDT * 2;               // B    [64][LDT] f16
+  static constexpr int OFF_L = OFF_B + C * LDT * 2;                 // L/A  [64][LDL] f32
+  static constexpr int OFF_SMALL = OFF_L + C * LDL * 4;             // gL[D], beta[64], Gs[64]
+  static constexpr int SMALL_BYTES = (D + 2 * C) * 4;
+  static constexpr int OFF_A = OFF_SMALL + SMALL_BYTES;             // region A (aliased)
+  // region A, phase P1..P3: G [64][LDG] f32 (per-key), raw K, raw Q [64][LDQ] f16
+  static constexpr int A_G = 0;
+  static constexpr int A_RK = A_G + C * LDG * 4;
+  static constexpr int A_RQ = A_RK + C * LDQ * 2;
+  static constexpr int A_END1 = A_RQ + C * LDQ * 2;
+  // region A, phase P4..P6: W [64][LDQ] f16, T~ hi/lo [64][LDT] f16, V^T [D][LDT] f16
+  static constexpr int A_W = 0;
+  static constexpr int A_TH = A_W + C * LDQ * 2;
+  static constexpr int A_TL = A_TH + C * LDT * 2;
+  static constexpr int A_VT = A_TL + C * LDT * 2;
+  static constexpr int A_END2 = A_VT + D * LDT * 2;
+  static constexpr int A_BYTES = A_END1 > A_END2 ? A_END1 : A_END2;
+  static constexpr int TOTAL = OFF_A + A_BYTES;
+};
+
+template <bool BF16>
+struct RawGroup;  // 8 consecutive q/k/v elements of one token
+template <>
+struct RawGroup<true> { uint4 w; };
+template <>
+struct RawGroup<false> { f32x4 a, b; };
+
+template <bool BF16>
+__device__ __forceinline__ RawGroup<BF16> load_group(const void* base, int64_t idx, bool valid) {
+  RawGroup<BF16> r;
+  if constexpr (BF16) {
+    r.w = valid ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx)
+                : uint4{0, 0, 0, 0};
+  } else {
+    const float* p = static_cast<const float*>(base) + idx;
+    r.a = valid ? *reinterpret_cast<const f32x4*>(p) : f32x4{0, 0, 0, 0};
+    r.b = valid ? *reinterpret_cast<const f32x4*>(p + 4) : f32x4{0, 0, 0, 0};
+  }
+  return r;
+}
+template <bool BF16>
+__device__ __forceinline__ void unpack_group(const RawGroup<BF16>& r, float (&x)[8]) {
+  if constexpr (BF16) {
+    const uint32_t w[4] = {r.w.x, r.w.y, r.w.z, r.w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf16_bits_to_f32(w[i] & 0xFFFFu);
+      x[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = r.a[i];
+      x[4 + i] = r.b[i];
+    }
+  }
+}
+
+// Registers holding one chunk's raw inputs (prefetched during the previous chunk).
+template <int D, bool BF16, bool PER_KEY>
+struct ChunkRegs {
+  static constexpr int NT = D * 4;               // threads per workgroup
+  static constexpr int GROUPS = C * D / 8;       // 8-element groups per [64][D] tensor
+  static constexpr int GPT = GROUPS / NT;        // groups per thread (2)
+  RawGroup<BF16> k[GPT], q[GPT], v[GPT];
+  float alpha[PER_KEY ? 16 : 1];                 // per-key: 16 channels of token `lane`
+  float beta;
+};
+
+template <int D, bool BF16, bool PER_KEY>
+__device__ __forceinline__ void load_chunk(ChunkRegs<D, BF16, PER_KEY>& R, const PrefillArgs& a,
+                                           int64_t tok0, int n, int h, int tid) {
+  using CR = ChunkRegs<D, BF16, PER_KEY>;
+  const int64_t HD = (int64_t)a.H * D;
+#pragma unroll
+  for (int j = 0; j < CR::GPT; ++j) {
+    const int gi = tid + j * CR::NT;
+    const int c = gi / (D / 8), k8 = gi % (D / 8);
+    const bool valid = c < n;
+    const int64_t idx = (tok0 + (valid ? c : 0)) * HD + (int64_t)h * D + 8 * k8;
+    R.k[j] = load_group<BF16>(a.k, idx, valid);
+    R.q[j] = load_group<BF16>(a.q, idx, valid);
+    R.v[j] = load_group<BF16>(a.v, idx, valid);
+  }
+  const int wave = tid / 64, lane = tid % 64;
+  const bool valid = lane < n;
+  const int64_t tok = tok0 + (valid ? lane : 0);
+  if constexpr (PER_KEY) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(a.alpha + (tok * a.H + h) * D + 16 * wave);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 x = valid ? p[i] : f32x4{1.f, 1.f, 1.f, 1.f};
+      R.alpha[4 * i] = x[0]; R.alpha[4 * i + 1] = x[1]; R.alpha[4 * i + 2] = x[2]; R.alpha[4 * i + 3] = x[3];
+    }
+  } else {
+    R.alpha[0] = (wave == 0 && valid) ? a.alpha[tok * a.H + h] : 1.f;
+  }
+  R.beta = (wave == 0 && valid) ? a.beta[tok * a.H + h] : 0.f;
+}
+
+__device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const float y = __shfl_up(x, m);
+    if (lane >= m) x += y;
+  }
+  return x;
+}
+
+template <int D, bool BF16, bool PER_KEY>
+__global__ __launch_bounds__(D * 4) void prefill_kernel(PrefillArgs a) {
+  using L = Lds<D>;
+  using CR = ChunkRegs<D, BF16, PER_KEY>;
+  constexpr int NW = D / 16;     // wavefronts = state slices
+  constexpr int NT = D * 4;
+  constexpr int KT = D / 16;     // 16-row tiles along d_k
+  extern __shared__ __align__(16) unsigned char smem[];
+
+  _Float16* sQt = reinterpret_cast<_Float16*>(smem + L::OFF_QT);
+  _Float16* sKhT = reinterpret_cast<_Float16*>(smem + L::OFF_KHT);
+  _Float16* sKtT = reinterpret_cast<_Float16*>(smem + L::OFF_KTT);
+  _Float16* sB = reinterpret_cast<_Float16*>(smem + L::OFF_B);
+  float* sL = reinterpret_cast<float*>(smem + L::OFF_L);
+  float* sGL = reinterpret_cast<float*>(smem + L::OFF_SMALL);   // [D] G_n per channel
+  float* sBeta = sGL + D;                                         // [64]
+  float* sGs = sBeta + C;                                         // [64] scalar-gate G
+  unsigned char* regA = smem + L::OFF_A;
+  float* sG = reinterpret_cast<float*>(regA + L::A_G);
+  _Float16* sRK = reinterpret_cast<_Float16*>(regA + L::A_RK);
+  _Float16* sRQ = reinterpret_cast<_Float16*>(regA + L::A_RQ);
+  _Float16* sW = reinterpret_cast<_Float16*>(regA + L::A_W);
+  _Float16* sTh = reinterpret_cast<_Float16*>(regA + L::A_TH);
+  _Float16* sTl = reinterpret_cast<_Float16*>(regA + L::A_TL);
+  _Float16* sVT = reinterpret_cast<_Float16*>(regA + L::A_VT);
+
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
+  const int g = lane >> 4, l16 = lane & 15;
+  const int item_idx = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const PrefillItem item = a.items[item_idx];
+  const int64_t HD = (int64_t)a.H * D;
+  const int slice = wave;          // state rows 16*slice .. 16*slice+15
+
+  // ---- start state: S0^T in accumulator layout ------------------------------
+  // tile kt, lane l: S0^T[k = 16kt + 4g + i][v = 16 slice + l16] = S0[v][k]
+  f32x4 ST[KT];
+  {
+    const float* src = nullptr;
+    if (a.seg_chunks > 0 && item.seg > 0)
+      src = a.seg_states + ((int64_t)item_idx * a.H + h) * D * D;
+    else if (a.init)
+      src = a.init + ((int64_t)item.seq * a.H + h) * D * D;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+      ST[kt] = src ? *reinterpret_cast<const f32x4*>(src + (16 * slice + l16) * D + 16 * kt + 4 * g)
+                   : f32x4{0, 0, 0, 0};
+  }
+
+  const int n_chunks = (item.n_tokens + C - 1) / C;
+  CR regs;
+  if (n_chunks > 0) load_chunk<D, BF16, PER_KEY>(regs, a, item.tok_begin, min(C, item.n_tokens), h, tid);
+
+  for (int ch = 0; ch < n_chunks; ++ch) {
+    const int64_t tok0 = item.tok_begin + (int64_t)ch * C;
+    const int n = min(C, item.n_tokens - ch * C);
+
+    // ---- P1: raw q, k (fp16), cumulative log2 decay, beta ---------------------
+#pragma unroll
+    for (int j = 0; j < CR::GPT; ++j) {
+      const int gi = tid + j * NT;
+      const int c = gi / (D / 8), k8 = gi % (D / 8);
+      float x[8];
+      f16x8 hv;
+      unpack_group<BF16>(regs.k[j], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hv[e] = (_Float16)x[e];
+      *reinterpret_cast<f16x8*>(sRK + c * L::LDQ + 8 * k8) = hv;
+      unpack_group<BF16>(regs.q[j], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hv[e] = (_Float16)x[e];
+      *reinterpret_cast<f16x8*>(sRQ + c * L::LDQ + 8 * k8) = hv;
+    }
+    if constexpr (PER_KEY) {
+      // wave w: channels 16w..16w+15, lane = token
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float gcum = wave_inclusive_scan(log2f(regs.alpha[i]), lane);
+        sG[lane * L::LDG + 16 * wave + i] = gcum;
+        if (lane == C - 1) sGL[16 * wave + i] = gcum;
+      }
+    } else {
+      if (wave == 0) {
+        const float gcum = wave_inclusive_scan(log2f(regs.alpha[0]), lane);
+        sGs[lane] = gcum;
+        const float gl = __shfl(gcum, C - 1);
+        sGL[lane] = gl;
+        if (D > 64) sGL[lane + 64] = gl;
+      }
+    }
+    if (wave == 0) sBeta[lane] = regs.beta;
+    __syncthreads();
+
+    // ---- P2: decayed operands ------------------------------------------------
+#pragma unroll
+    for (int j = 0; j < CR::GPT; ++j) {
+      const int gi = tid + j * NT;
+      const int c = gi / (D / 8), k8 = gi % (D / 8);
+      float kx[8], qx[8];
+      unpack_group<BF16>(regs.k[j], kx);
+      unpack_group<BF16>(regs.q[j], qx);
+      f16x8 qt;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kk = 8 * k8 + e;
+        const float gc = PER_KEY ? sG[c * L::LDG + kk] : sGs[c];
+        const float dec = exp2f(gc);
+        const float rem = exp2f(sGL[kk] - gc);
+        // fp16 rounding of the bf16 inputs happens here, once
+        const float kf = (float)(_Float16)kx[e];
+        const float qf = (float)(_Float16)qx[e];
+        qt[e] = (_Float16)(qf * dec);
+        sKhT[kk * L::LDT + c] = (_Float16)(kf * dec);
+        sKtT[kk * L::LDT + c] = (_Float16)(kf * rem);
+      }
+      *reinterpret_cast<f16x8*>(sQt + c * L::LDQ + 8 * k8) = qt;
+    }
+
+    // ---- P3: Gram tiles L (fp32) and B (fp16) ------------------------------
+    // Upper blocks of B are zero; the 10 lower tiles (R >= I) go round-robin
+    // to the wavefronts.
+    for (int e = tid; e < 6 * 256; e += NT) {
+      const int t = e / 256, rr = (e % 256) / 16, cc = e % 16;
+      const int R = t < 3 ? 0 : (t < 5 ? 1 : 2);
+      const int I = t < 3 ? t + 1 : (t < 5 ? t - 1 : 3);
+      sB[(16 * R + rr) * L::LDT + 16 * I + cc] = (_Float16)0.f;
+    }
+    for (int t = wave; t < 10; t += NW) {
+      const int R = t < 1 ? 0 : (t < 3 ? 1 : (t < 6 ? 2 : 3));
+      const int I = t - R * (R + 1) / 2;
+      f32x4 accL = {0, 0, 0, 0}, accB = {0, 0, 0, 0};
+      if constexpr (!PER_KEY) {
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+          const f16x8 ka = ld_std(sRK, L::LDQ, 16 * R, 32 * ks, lane);
+          const f16x8 qa = ld_std(sRQ, L::LDQ, 16 * R, 32 * ks, lane);
+          const f16x8 kb = ld_std(sRK, L::LDQ, 16 * I, 32 * ks, lane);
+          accL = mfma_f16(ka, kb, accL);
+          accB = mfma_f16(qa, kb, accB);
+        }
+      } else {
+        // operands decayed relative to token 16R: A-side 2^(G_r - G_16R) <= 1,
+        // B-side 2^(G_16R - G_i) (<= 1 for i <= 16R, bounded inside block R).
+        const int r = 16 * R + l16, i = 16 * I + l16;
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+          bf16x8 kah, kal, qah, qal, kbh, kbl;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int kk = 32 * ks + 8 * g + e;
+            const float gref = sG[(16 * R) * L::LDG + kk];
+            const float fa = exp2f(sG[r * L::LDG + kk] - gref);
+            const float fb = exp2f(gref - sG[i * L::LDG + kk]);
+            const float ka = (float)sRK[r * L::LDQ + kk] * fa;
+            const float qa = (float)sRQ[r * L::LDQ + kk] * fa;
+            const float kb = (float)sRK[i * L::LDQ + kk] * fb;
+            kah[e] = (__bf16)ka; kal[e] = (__bf16)(ka - (float)kah[e]);
+            qah[e] = (__bf16)qa; qal[e] = (__bf16)(qa - (float)qah[e]);
+            kbh[e] = (__bf16)kb; kbl[e] = (__bf16)(kb - (float)kbh[e]);
+          }
+          accL = mfma_bf16(kah, kbh, accL);
+          accL = mfma_bf16(kah, kbl, accL);
+          accL = mfma_bf16(kal, kbh, accL);
+          accB = mfma_bf16(qah, kbh, accB);
+          accB = mfma_bf16(qah, kbl, accB);
+          accB = mfma_bf16(qal, kbh, accB);
+        }
+      }
+      // epilogue: lane holds rows r = 16R + 4g + i, column ic = 16I + l16
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * R + 4 * g + i, ic = 16 * I + l16;
+        float lv = accL[i], bv = accB[i];
+        if constexpr (!PER_KEY) {
+          const float f = exp2f(fminf(sGs[r] - sGs[ic], 0.f));
+          lv *= f;
+          bv *= f;
+        }
+        sL[r * L::LDL + ic] = (ic < r) ? lv * sBeta[r] : 0.f;
+        sB[r * L::LDT + ic] = (_Float16)((ic <= r) ? bv : 0.f);
+      }
+    }
+    __syncthreads();
+
+    // ---- P4: A = (I + L)^-1 -------------------------------------------------
+    // Diagonal 16x16 blocks by forward substitution (wave 0, one column per
+    // lane); A_bb overwrites L_bb. Other waves stage V^T meanwhile.
+    if (wave == 0) {
+      const int b = g, j = l16;
+      const float* Lb = sL + (16 * b) * L::LDL + 16 * b;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float s = (r == j) ? 1.f : 0.f;
+#pragma unroll
+        for (int i = 0; i < r; ++i) s -= Lb[r * L::LDL + i] * x[i];
+        x[r] = s;
+      }
+      float* Ab = sL + (16 * b) * L::LDL + 16 * b;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Ab[r * L::LDL + j] = x[r];
+    }
+    // V^T [v][c] into region A (G and raw q, k are dead after P3)
+#pragma unroll
+    for (int j = 0; j < CR::GPT; ++j) {
+      const int gi = tid + j * NT;
+      const int c = gi / (D / 8), k8 = gi % (D / 8);
+      float x[8];
+      unpack_group<BF16>(regs.v[j], x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sVT[(8 * k8 + e) * L::LDT + c] = (_Float16)x[e];
+    }
+    __syncthreads();
+    // Off-diagonal blocks, stage R = 1, 2, 3: job (R, I) on wave I,
+    //   A_RI = -A_RR * sum_{m=I}^{R-1} L_Rm A_mI, stored at block (I, R).
+#pragma unroll
+    for (int R = 1; R < 4; ++R) {
+      if (wave < R) {
+        const int I = wave;
+        f32x4 acc = {0, 0, 0, 0};
+        for (int m = I; m < R; ++m) {
+          // A_mI lives at block (I, m) for m > I, at (I, I) for m == I
+          const float* Amb = sL + (16 * I) * L::LDL + 16 * m;
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            const float av = sL[(16 * R + l16) * L::LDL + 16 * m + 4 * ks + g];
+            const float bv = Amb[(4 * ks + g) * L::LDL + l16];
+            acc = mfma_f32(av, bv, acc);
+          }
+        }
+        // -A_RR * acc, acc as the K-operand with permuted K (k = 4g + ks)
+        f32x4 res = {0, 0, 0, 0};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const float av = sL[(16 * R + l16) * L::LDL + 16 * R + 4 * g + ks];
+          res = mfma_f32(av, acc[ks], res);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sL[(16 * I + 4 * g + i) * L::LDL + 16 * R + l16] = -res[i];
+      }
+      __syncthreads();
+    }
+
+    // ---- P5: T~ = A Diag(beta) as fp16 hi + lo; W = T~ (K * 2^G) ------------
+    for (int e8 = tid; e8 < C * C / 8; e8 += NT) {
+      const int c = e8 / 8, i0 = 8 * (e8 % 8);
+      const int Rb = c / 16, Ib = i0 / 16;
+      f16x8 th, tl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = i0 + e;
+        float av = 0.f;
+        if (Rb > Ib) av = sL[(16 * Ib + c % 16) * L::LDL + 16 * Rb + i % 16];
+        else if (Rb == Ib) av = sL[c * L::LDL + i];
+        const float tv = av * sBeta[i];
+        th[e] = (_Float16)tv;
+        tl[e] = (_Float16)(tv - (float)th[e]);
+      }
+      *reinterpret_cast<f16x8*>(sTh + c * L::LDT + i0) = th;
+      *reinterpret_cast<f16x8*>(sTl + c * L::LDT + i0) = tl;
+    }
+    __syncthreads();
+    {
+      // wave w computes W[:, 16w..16w+15] (4 row tiles, K = 64)
+      const int kt = wave;
+      f32x4 acc[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const f16x8 bk = ld_std(sKhT, L::LDT, 16 * kt, 32 * ks, lane);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          acc[ct] = mfma_f16(ld_std(sTh, L::LDT, 16 * ct, 32 * ks, lane), bk, acc[ct]);
+          acc[ct] = mfma_f16(ld_std(sTl, L::LDT, 16 * ct, 32 * ks, lane), bk, acc[ct]);
+        }
+      }
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sW[(16 * ct + 4 * g + i) * L::LDQ + 16 * kt + l16] = (_Float16)acc[ct][i];
+    }
+    __syncthreads();
+
+    // prefetch the next chunk's raw inputs while the chain runs
+    if (ch + 1 < n_chunks)
+      load_chunk<D, BF16, PER_KEY>(regs, a, tok0 + C, min(C, item.n_tokens - (ch + 1) * C), h, tid);
+
+    // ---- P6: state passing for this wavefront's slice -----------------------
+    {
+      // U' = T~ V_s : rows c (4 tiles), column v = 16 slice + l16
+      f32x4 U[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) U[ct] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const f16x8 bv = ld_std(sVT, L::LDT, 16 * slice, 32 * ks, lane);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          U[ct] = mfma_f16(ld_std(sTh, L::LDT, 16 * ct, 32 * ks, lane), bv, U[ct]);
+          U[ct] = mfma_f16(ld_std(sTl, L::LDT, 16 * ct, 32 * ks, lane), bv, U[ct]);
+        }
+      }
+      // S0^T as the permuted-K operand (fp16), shared by W S0^T and Q~ S0^T
+      f16x8 sop[D / 32];
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) sop[ks] = pack_perm(ST[2 * ks], ST[2 * ks + 1]);
+      f32x4 P[4], O[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) { P[ct] = f32x4{0, 0, 0, 0}; O[ct] = f32x4{0, 0, 0, 0}; }
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          P[ct] = mfma_f16(ld_perm(sW, L::LDQ, 16 * ct, 32 * ks, lane), sop[ks], P[ct]);
+          O[ct] = mfma_f16(ld_perm(sQt, L::LDQ, 16 * ct, 32 * ks, lane), sop[ks], O[ct]);
+        }
+      }
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) U[ct] = U[ct] - P[ct];
+      // U as hi + lo permuted-K operands (K = chunk position, 2 steps)
+      f16x8 uh[2], ul[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) split_perm(U[2 * ks], U[2 * ks + 1], uh[ks], ul[ks]);
+      // O += B U
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const f16x8 ba = ld_perm(sB, L::LDT, 16 * ct, 32 * ks, lane);
+          O[ct] = mfma_f16(ba, uh[ks], O[ct]);
+          O[ct] = mfma_f16(ba, ul[ks], O[ct]);
+        }
+      }
+      // S^T <- 2^(G_n) S^T + K~^T U
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ST[kt][i] *= exp2f(sGL[16 * kt + 4 * g + i]);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const f16x8 ka = ld_perm(sKtT, L::LDT, 16 * kt, 32 * ks, lane);
+          ST[kt] = mfma_f16(ka, uh[ks], ST[kt]);
+          ST[kt] = mfma_f16(ka, ul[ks], ST[kt]);
+        }
+      }
+      // o rows of this chunk
+      float* obase = a.o + tok0 * HD + (int64_t)h * D + 16 * slice + l16;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = 16 * ct + 4 * g + i;
+          if (c < n) obase[(int64_t)c * HD] = O[ct][i];
+        }
+    }
+
+    // snapshot after this chunk if the sequence position is a multiple of the interval
+    if (a.interval > 0) {
+      const int64_t pos = item.tok_in_seq + (int64_t)ch * C + n;   // tokens of the sequence done
+      if (pos % a.interval == 0) {
+        const int64_t slot = item.snap_base + pos / a.interval - 1;
+        float* dst = a.snapshots + (slot * a.H + h) * D * D;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+          *reinterpret_cast<f32x4*>(dst + (16 * slice + l16) * D + 16 * kt + 4 * g) = ST[kt];
+      }
+    }
+    __syncthreads();
+  }
+
+  // final state of the sequence (or of the segment, for the segment scan)
+  {
+    float* dst = a.final_state + ((int64_t)item.seq * a.H + h) * D * D;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+      *reinterpret_cast<f32x4*>(dst + (16 * slice + l16) * D + 16 * kt + 4 * g) = ST[kt];
+  }
+}
+
+// Work table: one item per sequence, longest first (stable), with the first
+// snapshot slot of each sequence. A single workgroup; lengths read from the
+// device copy of cu_seqlens.
+__global__ __launch_bounds__(256) void build_items_kernel(const int64_t* cu, int32_t N,
+                                                          int64_t interval, PrefillItem* items) {
+  __shared__ int64_t carry;
+  __shared__ int64_t part[256];
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int32_t base = 0; base < N; base += 256) {
+    const int32_t n = base + threadIdx.x;
+    const int64_t len = n < N ? cu[n + 1] - cu[n] : 0;
+    const int64_t ns = (interval > 0) ? len / interval : 0;
+    part[threadIdx.x] = ns;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int64_t y = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+      __syncthreads();
+      part[threadIdx.x] += y;
+      __syncthreads();
+    }
+    if (n < N) {
+      int32_t rank = n;
+      if (N <= 8192) {  // longest first for load balance; ties keep sequence order
+        rank = 0;
+        for (int32_t m = 0; m < N; ++m) {
+          const int64_t lm = cu[m + 1] - cu[m];
+          rank += (lm > len) || (lm == len && m < n);
+        }
+      }
+      PrefillItem it;
+      it.tok_begin = cu[n];
+      it.n_tokens = (int32_t)len;
+      it.seq = n;
+      it.seg = 0;
+      it.n_segs = 1;
+      it.tok_in_seq = 0;
+      it.snap_base = carry + part[threadIdx.x] - ns;
+      items[rank] = it;
+    }
+    __syncthreads();
+    if (threadIdx.x == 255) carry += part[255];
+    __syncthreads();
+  }
+}
+
+template <int D, bool BF16, bool PK>
+hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
+  using L = Lds<D>;
+  static_assert(L::TOTAL <= 160 * 1024, "LDS budget");
+  auto kern = prefill_kernel<D, BF16, PK>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(a.n_items * a.H), dim3(D * 4), L::TOTAL, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, int d, bool bf16, bool per_key, hipStream_t s) {
+  hipLaunchKernelGGL(build_items_kernel, dim3(1), dim3(256), 0, s, a.cu_dev, a.num_seqs, a.interval,
+                     a.items);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (d == 64) {
+    if (bf16) return per_key ? launch_t<64, true, true>(a, s) : launch_t<64, true, false>(a, s);
+    return per_key ? launch_t<64, false, true>(a, s) : launch_t<64, false, false>(a, s);
+  }
+  if (bf16) return per_key ? launch_t<128, true, true>(a, s) : launch_t<128, true, false>(a, s);
+  return per_key ? launch_t<128, false, true>(a, s) : launch_t<128, false, false>(a, s);
+}
+
+}  // namespace kda

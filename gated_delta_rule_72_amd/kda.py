@@ -1,0 +1,191 @@
+"""Thin ctypes binding of libkda.so (include/kda.h).
+
+Argument marshalling only: every step of the recurrence runs in the HIP
+kernels of libkda.so. PyTorch supplies device memory and the current stream.
+There is no fallback: if libkda.so is missing or a call fails, this module
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
+
+KDA_OK, KDA_ERR_ARG, KDA_ERR_SHAPE, KDA_ERR_ALIGN, KDA_ERR_WORKSPACE, KDA_ERR_DEVICE = 0, -1, -2, -3, -4, -5
+KDA_BF16, KDA_F32 = 0, 1
+KDA_GATE_SCALAR, KDA_GATE_PER_KEY = 0, 1
+CHUNK = 64
+
+
+class KdaError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed with status {code}: {msg}")
+        self.code = code
+
+
+class KdaShape(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("qkv_dtype", ctypes.c_int32), ("gate", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Loads libkda.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run gated_delta_rule_72_amd/build.py "
+                          f"(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "kda_abi_version": ([], ctypes.c_int),
+        "kda_last_error": ([], ctypes.c_char_p),
+        "kda_snapshot_count": ([I32, P, I64, P], ctypes.c_int),
+        "kda_prefill_workspace_size": ([P, I32, P, I32, I64, P], ctypes.c_int),
+        "kda_prefill_chunked": ([P, I32, P, P, I32, I64, P, P, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
+        "kda_decode_step": ([P, I32, P, P, P, P, P, P, P, P], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = lib
+    return lib
+
+
+EXPORTED = ("kda_abi_version", "kda_last_error", "kda_snapshot_count", "kda_prefill_workspace_size",
+            "kda_prefill_chunked", "kda_decode_step")
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != KDA_OK:
+        raise KdaError(fn, rc, load().kda_last_error().decode(errors="replace"))
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def make_shape(num_heads: int, d_k: int, d_v: int, qkv_dtype: torch.dtype, per_key: bool) -> KdaShape:
+    dt = {torch.bfloat16: KDA_BF16, torch.float32: KDA_F32}.get(qkv_dtype)
+    if dt is None:
+        raise TypeError(f"q, k, v must be bfloat16 or float32 (got {qkv_dtype})")
+    return KdaShape(num_heads, d_k, d_v, dt, KDA_GATE_PER_KEY if per_key else KDA_GATE_SCALAR)
+
+
+# ---- the C ABI, name for name ----------------------------------------------
+
+def kda_abi_version() -> int:
+    return load().kda_abi_version()
+
+
+def kda_last_error() -> str:
+    return load().kda_last_error().decode(errors="replace")
+
+
+def kda_snapshot_count(cu_seqlens_host: torch.Tensor, interval: int) -> int:
+    cu = cu_seqlens_host.to("cpu", torch.int64).contiguous()
+    out = ctypes.c_int64(0)
+    _check("kda_snapshot_count",
+           load().kda_snapshot_count(cu.numel() - 1, _ptr(cu), int(interval), ctypes.byref(out)))
+    return out.value
+
+
+def kda_prefill_workspace_size(shape: KdaShape, cu_seqlens_host: torch.Tensor, chunk: int = CHUNK,
+                               snapshot_interval: int = 0) -> int:
+    cu = cu_seqlens_host.to("cpu", torch.int64).contiguous()
+    out = ctypes.c_size_t(0)
+    _check("kda_prefill_workspace_size",
+           load().kda_prefill_workspace_size(ctypes.byref(shape), cu.numel() - 1, _ptr(cu), int(chunk),
+                                             int(snapshot_interval), ctypes.byref(out)))
+    return out.value
+
+
+def kda_prefill_chunked(shape: KdaShape, cu_seqlens_host: torch.Tensor, cu_seqlens_dev: torch.Tensor,
+                        q, k, v, alpha, beta, initial_state, o, final_state, snapshots,
+                        workspace: torch.Tensor, chunk: int = CHUNK, snapshot_interval: int = 0,
+                        stream=None) -> None:
+    """Enqueues the prefill on `stream` (default: torch's current stream). All
+    tensors must already be allocated, contiguous, on one device."""
+    cu = cu_seqlens_host.to("cpu", torch.int64).contiguous()
+    dev = q.device
+    s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream_ptr(dev)
+    _check("kda_prefill_chunked", load().kda_prefill_chunked(
+        ctypes.byref(shape), cu.numel() - 1, _ptr(cu), _ptr(cu_seqlens_dev), int(chunk),
+        int(snapshot_interval), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state),
+        _ptr(o), _ptr(final_state), _ptr(snapshots), _ptr(workspace), workspace.numel(), s))
+
+
+def kda_decode_step(shape: KdaShape, batch: int, q, k, v, alpha, beta, state, o, stream=None) -> None:
+    s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream_ptr(q.device)
+    _check("kda_decode_step", load().kda_decode_step(
+        ctypes.byref(shape), int(batch), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+        _ptr(state), _ptr(o), s))
+
+
+# ---- convenience wrappers: allocate outputs with torch, then call the ABI ----
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
+def prefill_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
+                    beta: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None,
+                    initial_state: Optional[torch.Tensor] = None, snapshot_interval: int = 0,
+                    cu_seqlens_host: Optional[torch.Tensor] = None, chunk: int = CHUNK,
+                    out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+    """q, k [T,H,dk], v [T,H,dv] (bf16/fp32), alpha [T,H] or [T,H,dk], beta [T,H]
+    (fp32). cu_seqlens: int64 [N+1] (default: one sequence of length T).
+    Returns (o [T,H,dv] fp32, final_state [N,H,dv,dk], snapshots [S,H,dv,dk])."""
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    dev = q.device
+    if cu_seqlens is None:
+        cu_seqlens = torch.tensor([0, T], dtype=torch.int64, device=dev)
+    if cu_seqlens_host is None:
+        cu_seqlens_host = cu_seqlens.to("cpu")
+    cu_dev = cu_seqlens.to(dev, torch.int64).contiguous()
+    N = cu_seqlens_host.numel() - 1
+    _contig(q, k, v, alpha, beta, initial_state)
+    per_key = alpha.dim() == 3
+    shape = make_shape(H, dk, dv, q.dtype, per_key)
+    n_snap = kda_snapshot_count(cu_seqlens_host, snapshot_interval)
+    if out is None:
+        o = torch.empty((T, H, dv), dtype=torch.float32, device=dev)
+        fin = torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev)
+        snaps = torch.empty((n_snap, H, dv, dk), dtype=torch.float32, device=dev)
+    else:
+        o, fin, snaps = out
+    ws_bytes = kda_prefill_workspace_size(shape, cu_seqlens_host, chunk, snapshot_interval)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    kda_prefill_chunked(shape, cu_seqlens_host, cu_dev, q, k, v, alpha, beta, initial_state, o, fin,
+                        snaps if n_snap > 0 else None, ws, chunk, snapshot_interval)
+    return o, fin, snaps
+
+
+def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
+                beta: torch.Tensor, state: torch.Tensor, o: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One token per sequence; `state` [B,H,dv,dk] fp32 is updated in place.
+    Returns o [B,H,dv] fp32."""
+    B, H, dk = q.shape
+    dv = v.shape[2]
+    _contig(q, k, v, alpha, beta, state)
+    shape = make_shape(H, dk, dv, q.dtype, alpha.dim() == 3)
+    if o is None:
+        o = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
+    kda_decode_step(shape, B, q, k, v, alpha, beta, state, o)
+    return o

@@ -1,0 +1,145 @@
+/*
+ * kda.h — C ABI of libkda.so: the gated delta rule (Gated DeltaNet / KDA) on
+ * MI355X (gfx950), as hand-written HIP kernels.
+ *
+ * The operation (page "Modele hybrydowe: co Gated DeltaNet zastępuje w cache
+ * KV", trefon.com, section "Gated DeltaNet: dodaj zanik", with the read-out of
+ * section "Atencja liniowa: stan o stałym rozmiarze"): per sequence and head a
+ * d_v x d_k fp32 state S evolves token by token as
+ *
+ *     S_t = S_{t-1} Diag(a_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = S_t q_t,
+ *
+ * with a_t = alpha_t * 1 for the scalar gate and a_t in (0,1]^{d_k} for the
+ * per-key-channel (KDA) gate, applied on the key axis before the delta
+ * correction. No 1/sqrt(d_k) scale is applied to q: callers pre-scale it.
+ *
+ * Common conventions
+ *   - Every tensor is caller-owned device memory, row-major and contiguous.
+ *     The library never allocates: temporary storage comes from the caller's
+ *     workspace. Pointers must stay valid until the stream's work completes.
+ *   - q, k: [T, H, d_k]; v: [T, H, d_v] in bf16 (KDA_BF16) or fp32 (KDA_F32).
+ *     alpha: fp32 [T, H] (KDA_GATE_SCALAR) or [T, H, d_k] (KDA_GATE_PER_KEY),
+ *     values in (0, 1]. beta: fp32 [T, H] in [0, 1]. States are fp32
+ *     [.., H, d_v, d_k] (d_k contiguous). o is fp32 [T, H, d_v].
+ *   - Supported: d_k = d_v in {64, 128}; chunk = 64.
+ *   - Alignment: q, k, v, per-key alpha and every state 16 bytes (8 bytes
+ *     for bf16 q, k in kda_decode_step); scalar alpha, beta and o 4 bytes;
+ *     cu_seqlens_dev 8 bytes; workspace 16 bytes. Otherwise KDA_ERR_ALIGN.
+ *   - All compute entry points are asynchronous on the caller's hipStream_t
+ *     (passed as void*, NULL = default stream).
+ *   - Errors: negative status codes are detected on the host before anything
+ *     is enqueued; outputs are then untouched. KDA_ERR_DEVICE reports a HIP
+ *     launch failure (work may be partly enqueued). kda_last_error() gives the
+ *     text of the calling thread's last failure.
+ *   - Determinism: no atomics; results are bitwise reproducible run to run and
+ *     a sequence's results do not depend on the other sequences of the pack.
+ *
+ * Numerical preconditions of the chunked prefill (its matrix products run on
+ * fp16 MFMA with fp32 accumulation; see kda_prefill_chunked):
+ *     |q|, |k| entries <= 16, |v| entries <= 4096, state entries <= 4096, and,
+ *     for the per-key gate, within each aligned block of 16 tokens of a chunk
+ *     every key channel's decay product stays above 2^-100.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_ARG = -1,       /* NULL pointer, unsupported enum, negative size      */
+  KDA_ERR_SHAPE = -2,     /* unsupported d_k/d_v/chunk, bad cu_seqlens, interval */
+  KDA_ERR_ALIGN = -3,     /* a pointer is not 16-byte aligned                    */
+  KDA_ERR_WORKSPACE = -4, /* workspace missing or too small                      */
+  KDA_ERR_DEVICE = -5     /* HIP error while enqueueing                          */
+} kda_status;
+
+typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
+typedef enum { KDA_GATE_SCALAR = 0, KDA_GATE_PER_KEY = 1 } kda_gate;
+
+typedef struct {
+  int32_t num_heads; /* H                                   */
+  int32_t d_k;       /* key / query channels per head       */
+  int32_t d_v;       /* value channels per head             */
+  int32_t qkv_dtype; /* kda_dtype of q, k, v                */
+  int32_t gate;      /* kda_gate: layout of alpha           */
+} kda_shape;
+
+/* ABI version of the loaded library (KDA_ABI_VERSION at build time). */
+int kda_abi_version(void);
+
+/* Text of the calling thread's last non-OK status ("" if none). */
+const char* kda_last_error(void);
+
+/* Number of snapshot slots: sum over sequences of floor(len / interval), 0
+ * when interval == 0. Host-only. Page "Modele hybrydowe…", section "Co stan
+ * rekurencyjny zmienia przy serwowaniu", item 1 (state kept at position N).
+ * Errors: KDA_ERR_ARG (NULL), KDA_ERR_SHAPE (cu_seqlens not starting at 0 or
+ * decreasing, negative interval). */
+int kda_snapshot_count(int32_t num_seqs, const int64_t* cu_seqlens_host, int64_t interval,
+                       int64_t* n_snap);
+
+/* Bytes of device workspace kda_prefill_chunked needs for this packing
+ * (host-only). Same error codes as kda_prefill_chunked's validation. */
+int kda_prefill_workspace_size(const kda_shape* shape, int32_t num_seqs,
+                               const int64_t* cu_seqlens_host, int32_t chunk,
+                               int64_t snapshot_interval, size_t* bytes);
+
+/* Chunkwise-parallel prefill over a varlen pack.
+ *
+ * Same page, closing paragraph of "Co stan rekurencyjny zmienia przy
+ * serwowaniu": inside a chunk of tokens the updates are dense matrix
+ * products and only the passage from chunk to chunk is sequential. Chunks of
+ * `chunk` tokens restart at every sequence start (the last one may be
+ * partial). Per chunk the kernels form the decayed key Gram matrix, solve the
+ * unit-lower-triangular system of the UT/WY form in LDS, and pass the fp32
+ * state to the next chunk with MFMA products; long sequences with few heads
+ * are additionally split into segments whose affine state maps are composed.
+ *
+ * cu_seqlens_host / cu_seqlens_dev: the same int64 [num_seqs+1] offsets on
+ *   host (validation, grid sizing) and device (indexing); cu[0] = 0,
+ *   nondecreasing, T = cu[num_seqs]. Empty sequences are allowed.
+ * chunk: must be 64.
+ * snapshot_interval: 0, or a positive multiple of `chunk`. The state after
+ *   the first m*interval tokens of each sequence (m = 1..floor(len/interval))
+ *   is written to snapshots[base_n + m - 1], base_n = slots of the earlier
+ *   sequences ([n_snap, H, d_v, d_k], see kda_snapshot_count).
+ * initial_state: [num_seqs, H, d_v, d_k] or NULL (zeros). May alias
+ *   final_state.
+ * o: [T, H, d_v] (must not alias inputs); final_state: [num_seqs, H, d_v, d_k];
+ * snapshots: NULL iff the slot count is 0.
+ * workspace: device memory of at least kda_prefill_workspace_size bytes.
+ */
+int kda_prefill_chunked(const kda_shape* shape, int32_t num_seqs,
+                        const int64_t* cu_seqlens_host, const int64_t* cu_seqlens_dev,
+                        int32_t chunk, int64_t snapshot_interval,
+                        const void* q, const void* k, const void* v,
+                        const float* alpha, const float* beta,
+                        const float* initial_state,
+                        float* o, float* final_state, float* snapshots,
+                        void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* One decode step for `batch` independent sequences (one new token each),
+ * updating the fp32 state in place: O(1) work per token, one read and one
+ * write of S (page "kda-graft", ailist.pro, section "2. Decode: O(1) против
+ * O(L)": the step only touches the fixed-size state).
+ * q, k: [batch, H, d_k]; v: [batch, H, d_v]; alpha: [batch, H] or
+ * [batch, H, d_k]; beta: [batch, H]; state: [batch, H, d_v, d_k] (read and
+ * overwritten); o: [batch, H, d_v]. batch == 0 is a no-op. */
+int kda_decode_step(const kda_shape* shape, int32_t batch,
+                    const void* q, const void* k, const void* v,
+                    const float* alpha, const float* beta,
+                    float* state, float* o, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H */

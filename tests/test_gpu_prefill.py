@@ -1,0 +1,144 @@
+"""GPU parity of kda_prefill_chunked against the fp64 CPU oracle (through the C ABI).
+
+Tolerances: max relative error (slice-max normalised) 2e-3 on o and 1e-3 on
+final states and snapshots; bit-exact for cu_seqlens indexing and snapshot
+placement (exact-integer test).
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_72_amd as kda
+from gated_delta_rule_72_amd import workloads as wl
+
+from gpu_util import check_prefill, custom, device, run_prefill
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("gate", ["scalar", "per_key"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_prefill_small_varlen(d, gate, dtype):
+    dev = device()
+    w = custom(f"small_{d}_{gate}_{dtype}", H=3, d=d, lens=(200, 1, 0, 64, 129, 63), gate=gate,
+               dtype=dtype, interval=64, seed=11)
+    print(f"case {w.name} lens={w.seq_lens}", flush=True)
+    inp = wl.make_prefill_inputs(w, dev)
+    outs = run_prefill(inp, w.interval)
+    check_prefill(inp, outs, w.interval)
+
+
+@pytest.mark.parametrize("gate", ["scalar", "per_key"])
+def test_prefill_zero_initial_state_long(gate):
+    dev = device()
+    w = custom(f"long_{gate}", H=2, d=128, lens=(3000,), gate=gate, s0_std=0.0, seed=12,
+               alpha_bias=4.0 if gate == "scalar" else 5.0)
+    print(f"case {w.name}", flush=True)
+    inp = wl.make_prefill_inputs(w, dev)
+    check_prefill(inp, run_prefill(inp, 0), 0)
+
+
+def test_tiny_recurrence_config():
+    """B=1 H=1 d=64 T=256 fp32, scalar alpha, zero initial state."""
+    dev = device()
+    w = wl.TINY
+    inp = wl.make_prefill_inputs(w, dev)
+    check_prefill(inp, run_prefill(inp, 64), 64)
+
+
+def test_kda_layer_config():
+    """B=1 H=14 d=64 T=8192, per-key alpha, all heads checked."""
+    dev = device()
+    w = wl.KDA_LAYER
+    inp = wl.make_prefill_inputs(w, dev)
+    check_prefill(inp, run_prefill(inp, 64), 64)
+
+
+def test_exact_integer_placement_bitwise():
+    """alpha = beta = 1, one-hot keys k_t = e_{t mod d}, one-hot queries and
+    small-integer values: every chunk product is exact in fp16 x fp16 -> fp32,
+    so o, snapshots and final states equal the oracle bit for bit and every
+    state column names the (sequence, position) that wrote it."""
+    dev = device()
+    import oracle
+    d, H = 64, 2
+    lens = [130, 0, 64, 1, 257, 4096 + 64]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T = int(cu[-1])
+    k = np.zeros((T, H, d), np.float32)
+    q = np.zeros((T, H, d), np.float32)
+    v = np.zeros((T, H, d), np.float32)
+    for n, L in enumerate(lens):
+        p = np.arange(L)
+        t = cu[n] + p
+        for h in range(H):
+            k[t, h, (p + h) % d] = 1.0
+            q[t, h, (5 * p + 3 * h) % d] = 1.0
+            v[t, h, 0] = n + 1
+            v[t, h, 1] = p % 128
+            v[t, h, 2] = p // 128
+            v[t, h, 3] = h
+    to_bf = lambda x: torch.from_numpy(x).to(torch.bfloat16).to(dev)  # noqa: E731
+    alpha = torch.ones((T, H, d), dtype=torch.float32, device=dev)
+    beta = torch.ones((T, H), dtype=torch.float32, device=dev)
+    interval = 64
+    inp = dict(q=to_bf(q), k=to_bf(k), v=to_bf(v), alpha=alpha, beta=beta,
+               cu_seqlens=torch.from_numpy(cu).to(dev), cu_seqlens_host=torch.from_numpy(cu),
+               initial_state=None)
+    o, fin, snaps = run_prefill(inp, interval)
+    A = {n: wl.to_oracle_arrays(inp[n]) for n in ("q", "k", "v", "alpha", "beta")}
+    o_r, f_r, s_r = oracle.run(A["q"], A["k"], A["v"], A["alpha"], A["beta"], cu, None, interval)
+    assert snaps.shape[0] == s_r.shape[0] == sum(L // interval for L in lens)
+    assert np.array_equal(o.cpu().numpy().astype(np.float64), o_r)
+    assert np.array_equal(fin.cpu().numpy().astype(np.float64), f_r)
+    assert np.array_equal(snaps.cpu().numpy().astype(np.float64), s_r)
+
+
+def test_run_twice_bitwise_deterministic():
+    dev = device()
+    w = custom("determinism", H=4, d=128, lens=(500, 77, 1024), gate="per_key", interval=128, seed=13)
+    inp = wl.make_prefill_inputs(w, dev)
+    a = run_prefill(inp, w.interval)
+    b = run_prefill(inp, w.interval)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_packed_equals_solo_bitwise():
+    dev = device()
+    w = custom("packing", H=2, d=64, lens=(300, 0, 65, 128), gate="per_key", interval=64, seed=14)
+    inp = wl.make_prefill_inputs(w, dev)
+    o, fin, snaps = run_prefill(inp, w.interval)
+    cu = inp["cu_seqlens_host"].tolist()
+    slot = 0
+    for n, L in enumerate(w.seq_lens):
+        s, e = cu[n], cu[n + 1]
+        sub = dict(q=inp["q"][s:e], k=inp["k"][s:e], v=inp["v"][s:e], alpha=inp["alpha"][s:e],
+                   beta=inp["beta"][s:e], cu_seqlens=torch.tensor([0, L], device=dev),
+                   cu_seqlens_host=torch.tensor([0, L]),
+                   initial_state=inp["initial_state"][n:n + 1].contiguous())
+        o1, f1, s1 = run_prefill(sub, w.interval)
+        assert torch.equal(o[s:e], o1)
+        assert torch.equal(fin[n:n + 1], f1)
+        assert torch.equal(snaps[slot:slot + s1.shape[0]], s1)
+        slot += s1.shape[0]
+
+
+def test_prefix_split_resume_bitwise():
+    """Prefill of the first N tokens (N % 64 == 0), then the rest from its final
+    state, equals the unsplit run bit for bit; the snapshot at N equals the
+    prefix's final state."""
+    dev = device()
+    w = custom("prefix", H=2, d=128, lens=(1000,), gate="scalar", interval=256, seed=15)
+    inp = wl.make_prefill_inputs(w, dev)
+    o, fin, snaps = run_prefill(inp, w.interval)
+    N = 512
+    part = lambda s, e, init: dict(q=inp["q"][s:e], k=inp["k"][s:e], v=inp["v"][s:e],  # noqa: E731
+                                   alpha=inp["alpha"][s:e], beta=inp["beta"][s:e],
+                                   cu_seqlens=torch.tensor([0, e - s], device=dev),
+                                   cu_seqlens_host=torch.tensor([0, e - s]), initial_state=init)
+    o1, f1, _ = run_prefill(part(0, N, inp["initial_state"]), 0)
+    o2, f2, _ = run_prefill(part(N, 1000, f1), 0)
+    assert torch.equal(snaps[1], f1[0])
+    assert torch.equal(o[:N], o1) and torch.equal(o[N:], o2) and torch.equal(fin, f2)
