@@ -75,23 +75,74 @@ int64_t snapshot_slots(int32_t num_seqs, const int64_t* cu, int64_t interval) {
   return total;
 }
 
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
+// Work plan of one prefill call. Sequences longer than seg_chunks chunks are cut
+// into segments (affine-map scan); seg_chunks == 0 runs every (sequence, head)
+// chain in one workgroup.
 struct PrefillPlan {
-  int32_t n_items;
-  size_t items_off, bytes;
+  int32_t seg_chunks, n_items;
+  size_t items_off, first_off, maps_off, states_off, bytes;
 };
 
-PrefillPlan plan_prefill(const kda_shape* s, int32_t num_seqs, const int64_t* cu) {
-  (void)s;
-  (void)cu;
+PrefillPlan plan_prefill(const kda_shape* s, int32_t num_seqs, const int64_t* cu,
+                         int64_t segment_tokens, int cus) {
   PrefillPlan p{};
-  p.n_items = num_seqs;
-  p.items_off = 0;
-  p.bytes = round_up(sizeof(kda::PrefillItem) * (size_t)(num_seqs > 0 ? num_seqs : 1));
+  int64_t total_chunks = 0, max_chunks = 0;
+  for (int32_t n = 0; n < num_seqs; ++n) {
+    const int64_t ch = (cu[n + 1] - cu[n] + kChunk - 1) / kChunk;
+    total_chunks += ch;
+    if (ch > max_chunks) max_chunks = ch;
+  }
+  int64_t seg = 0;
+  if (segment_tokens > 0) {
+    seg = segment_tokens / kChunk;
+  } else if (segment_tokens < 0) {
+    // automatic: split only when the (sequence, head) chains cannot fill the
+    // device; aim at one workgroup per compute unit and at least 8 chunks per
+    // segment.
+    const int64_t units = (int64_t)num_seqs * s->num_heads;
+    if (units < cus) {
+      seg = (total_chunks * s->num_heads + cus - 1) / cus;
+      if (seg < 8) seg = 8;
+    }
+  }
+  if (seg >= max_chunks) seg = 0;   // no sequence would be split
+  p.seg_chunks = (int32_t)seg;
+  int64_t items = 0;
+  for (int32_t n = 0; n < num_seqs; ++n) {
+    const int64_t len = cu[n + 1] - cu[n];
+    const int64_t st = seg * kChunk;
+    items += (st > 0 && len > st) ? (len + st - 1) / st : 1;
+  }
+  p.n_items = (int32_t)items;
+  const size_t H = (size_t)s->num_heads, DD = (size_t)s->d_k * s->d_v;
+  size_t off = 0;
+  p.items_off = off;
+  off += round_up(sizeof(kda::PrefillItem) * (size_t)(items > 0 ? items : 1));
+  p.first_off = off;
+  off += round_up(sizeof(int32_t) * (size_t)(num_seqs > 0 ? num_seqs : 1));
+  p.maps_off = off;
+  if (seg > 0) off += round_up((size_t)items * H * 2 * DD * sizeof(float));
+  p.states_off = off;
+  if (seg > 0) off += round_up((size_t)items * H * DD * sizeof(float));
+  p.bytes = off;
   return p;
 }
 
 int check_prefill_args(const kda_shape* shape, int32_t num_seqs, const int64_t* cu,
-                       int32_t chunk, int64_t interval) {
+                       int32_t chunk, int64_t interval, int64_t segment_tokens) {
   int rc = check_shape(shape);
   if (rc != KDA_OK) return rc;
   rc = check_cu(num_seqs, cu);
@@ -100,6 +151,9 @@ int check_prefill_args(const kda_shape* shape, int32_t num_seqs, const int64_t* 
   if (interval < 0 || interval % kChunk != 0)
     return fail(KDA_ERR_SHAPE, "snapshot_interval must be 0 or a positive multiple of 64 (got %lld)",
                 (long long)interval);
+  if (segment_tokens < -1 || (segment_tokens > 0 && segment_tokens % kChunk != 0))
+    return fail(KDA_ERR_SHAPE, "segment_tokens must be -1, 0 or a positive multiple of 64 (got %lld)",
+                (long long)segment_tokens);
   return KDA_OK;
 }
 
@@ -124,24 +178,25 @@ int kda_snapshot_count(int32_t num_seqs, const int64_t* cu_seqlens_host, int64_t
 
 int kda_prefill_workspace_size(const kda_shape* shape, int32_t num_seqs,
                                const int64_t* cu_seqlens_host, int32_t chunk,
-                               int64_t snapshot_interval, size_t* bytes) {
+                               int64_t snapshot_interval, int64_t segment_tokens, size_t* bytes) {
   if (!bytes) return fail(KDA_ERR_ARG, "bytes is NULL");
-  int rc = check_prefill_args(shape, num_seqs, cu_seqlens_host, chunk, snapshot_interval);
+  int rc = check_prefill_args(shape, num_seqs, cu_seqlens_host, chunk, snapshot_interval, segment_tokens);
   if (rc != KDA_OK) return rc;
-  *bytes = plan_prefill(shape, num_seqs, cu_seqlens_host).bytes;
+  *bytes = plan_prefill(shape, num_seqs, cu_seqlens_host, segment_tokens,
+                        segment_tokens < 0 ? device_cu_count() : 0).bytes;
   g_err[0] = '\0';
   return KDA_OK;
 }
 
 int kda_prefill_chunked(const kda_shape* shape, int32_t num_seqs,
                         const int64_t* cu_seqlens_host, const int64_t* cu_seqlens_dev,
-                        int32_t chunk, int64_t snapshot_interval,
+                        int32_t chunk, int64_t snapshot_interval, int64_t segment_tokens,
                         const void* q, const void* k, const void* v,
                         const float* alpha, const float* beta,
                         const float* initial_state,
                         float* o, float* final_state, float* snapshots,
                         void* workspace, size_t workspace_bytes, void* hip_stream) {
-  int rc = check_prefill_args(shape, num_seqs, cu_seqlens_host, chunk, snapshot_interval);
+  int rc = check_prefill_args(shape, num_seqs, cu_seqlens_host, chunk, snapshot_interval, segment_tokens);
   if (rc != KDA_OK) return rc;
   const int64_t T = cu_seqlens_host[num_seqs];
   const int64_t n_snap = snapshot_slots(num_seqs, cu_seqlens_host, snapshot_interval);
@@ -159,7 +214,8 @@ int kda_prefill_chunked(const kda_shape* shape, int32_t num_seqs,
                          {cu_seqlens_dev, 8, "cu_seqlens_dev"}, {workspace, 16, "workspace"}};
   rc = check_align(reqs, (int)(sizeof reqs / sizeof reqs[0]));
   if (rc != KDA_OK) return rc;
-  const PrefillPlan plan = plan_prefill(shape, num_seqs, cu_seqlens_host);
+  const PrefillPlan plan = plan_prefill(shape, num_seqs, cu_seqlens_host, segment_tokens,
+                                        segment_tokens < 0 ? device_cu_count() : 0);
   if (num_seqs > 0 && (!workspace || workspace_bytes < plan.bytes))
     return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", plan.bytes,
                 workspace ? workspace_bytes : (size_t)0);
@@ -175,11 +231,14 @@ int kda_prefill_chunked(const kda_shape* shape, int32_t num_seqs,
   a.num_seqs = num_seqs;
   a.H = shape->num_heads;
   a.interval = snapshot_interval;
-  a.seg_chunks = 0;
+  a.seg_chunks = plan.seg_chunks;
   a.n_items = plan.n_items;
-  a.items = reinterpret_cast<kda::PrefillItem*>(static_cast<char*>(workspace) + plan.items_off);
-  a.seg_maps = nullptr;
-  a.seg_states = nullptr;
+  a.pass = 0;
+  char* ws = static_cast<char*>(workspace);
+  a.items = reinterpret_cast<kda::PrefillItem*>(ws + plan.items_off);
+  a.seq_first_item = reinterpret_cast<int32_t*>(ws + plan.first_off);
+  a.seg_maps = plan.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.maps_off) : nullptr;
+  a.seg_states = plan.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.states_off) : nullptr;
   hipError_t e = kda::launch_prefill(a, shape->d_k, shape->qkv_dtype == KDA_BF16,
                                      shape->gate == KDA_GATE_PER_KEY,
                                      static_cast<hipStream_t>(hip_stream));

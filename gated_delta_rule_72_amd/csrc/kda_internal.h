@@ -51,15 +51,16 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, bool per_key, hipStream_t s);
 
-// One unit of prefill work: a contiguous run of chunks of one sequence.
+// One unit of prefill work: a contiguous run of chunks of one sequence (the
+// whole sequence, or one segment of it).
 struct PrefillItem {
   int64_t tok_begin;   // first token (global index into q/k/v/o)
+  int64_t tok_in_seq;  // position of tok_begin inside its sequence
+  int64_t snap_base;   // first snapshot slot of the sequence
   int32_t n_tokens;    // tokens in this item
   int32_t seq;         // sequence index n
   int32_t seg;         // segment index within the sequence (0 if unsegmented)
   int32_t n_segs;      // segments of this sequence
-  int64_t tok_in_seq;  // position of tok_begin inside its sequence
-  int64_t snap_base;   // first snapshot slot of the sequence
 };
 
 struct PrefillArgs {
@@ -71,11 +72,13 @@ struct PrefillArgs {
   int32_t num_seqs, H;
   int64_t interval;          // snapshot interval (0 = none)
   int32_t seg_chunks;        // chunks per segment (0 = unsegmented)
-  int32_t n_items;           // work items (sequence segments)
+  int32_t n_items;           // work items (sequences or sequence segments)
+  int32_t pass;              // 0 unsegmented; 1 segment maps (+ first segments); 3 segment reruns
   PrefillItem* items;        // workspace: [n_items]
-  float* seg_maps;           // workspace: per (item, head) M (dk x dk) and N (dv x dk)
+  int32_t* seq_first_item;   // workspace: [N] first item of each sequence (segmented)
+  float* seg_maps;           // workspace: per (item, head) M (dk x dk) then N (dv x dk)
   float* seg_states;         // workspace: per (item, head) start state (dv x dk)
 };
-hipError_t launch_prefill(const PrefillArgs& a, int d, bool bf16, bool per_key, hipStream_t s);
+hipError_t launch_prefill(PrefillArgs a, int d, bool bf16, bool per_key, hipStream_t s);
 
 }  // namespace kda

@@ -14,12 +14,15 @@
 //     W    = T~ (K * 2^G),  U' = T~ V,  U = U' - W S0^T
 //     O    = (Q * 2^G) S0^T + B U,  B_ri = sum_j q_r[j] k_i[j] 2^(G_r[j]-G_i[j]) (i <= r)
 //     S_n  = S0 Diag(2^(G_n)) + U^T (K * 2^(G_n - G))
+// so S_n = S0 M + N with M = Diag(2^G_n) - W^T (K*2^(G_n-G)) and
+// N = U'^T (K*2^(G_n-G)): a chunk, and hence a run of chunks, acts on the
+// state as an affine map.
 //
-// Kernel structure. One workgroup per (sequence or segment, head); D/16
-// wavefronts (D = d_k = d_v). Wavefront w owns state rows 16w..16w+15 (a
-// "slice") and keeps S0^T for them in MFMA accumulator layout (fp32) for the
-// whole sequence. Per chunk:
-//   P1  raw q, k (fp16) and the decay cumsum G (fp32) to LDS; beta to LDS.
+// Kernel structure. One workgroup per (work item, head), D/16 wavefronts
+// (D = d_k = d_v). Wavefront w owns 16 rows of the state (a "slice") and
+// keeps them transposed, S0^T, in MFMA accumulator layout (fp32) for the whole
+// item. Per chunk:
+//   P1  raw q, k (fp16) and the decay cumsum G (fp32) into LDS; beta; 2^G_n.
 //   P2  decayed operands in LDS: Q~ = Q*2^G [c][k], K^T*2^G and
 //       (K*2^(G_n-G))^T [k][c] (fp16).
 //   P3  Gram tiles on MFMA: L (fp32) and B (fp16). Scalar gate: exact
@@ -35,6 +38,12 @@
 //       S0^T <- 2^(G_n) S0^T + (K*2^(G_n-G))^T U. U and T~ enter their
 //       products as fp16 hi + lo pairs; the state stays fp32. The next
 //       chunk's inputs are loaded into registers while P6 runs.
+// Run modes of a workgroup: OUT (the real chain: o, snapshots, final state),
+// MAP_N (the chain from S0 = 0: the item's N) and MAP_M (the chain with
+// v = 0 from the identity rows: the item's M). Long sequences with few heads
+// are split into segments: pass 1 computes each middle segment's (M, N) and
+// runs the first segment in OUT mode, a scan composes S_{s+1} = S_s M_s + N_s
+// in fp32, and pass 3 reruns segments 1.. in OUT mode from their true start.
 // Accumulator layout of a 16x16 MFMA tile: lane l holds rows 4(l/16)+i,
 // column l%16. When an accumulator tile feeds the next product as its
 // K-operand, the K index is permuted (lane group g supplies rows 4g..4g+3 of
@@ -47,6 +56,8 @@ namespace {
 
 constexpr int C = 64;  // chunk length
 
+enum Mode { MODE_OUT = 0, MODE_MAP_N = 1, MODE_MAP_M = 2, MODE_IDLE = 3 };
+
 __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
@@ -56,6 +67,9 @@ __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+// Hardware base-2 exponential and logarithm (v_exp_f32 / v_log_f32).
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 
 // Row (l%16) of a row-major fp16 matrix, the 8 K-elements of lane group
 // g = l/16 in the standard order: k0 + 8g .. k0 + 8g + 7.
@@ -93,12 +107,13 @@ struct Lds {
   static constexpr int LDG = D + 4;   // row stride of per-key G [64][D] fp32
   // persistent through a chunk
   static constexpr int OFF_QT = 0;                                  // Q~   [64][LDQ] f16
-  static constexpr int OFF_KHT = OFF_QT + C * LDQ * 2;              // K^  T [D][LDT] f16
-  static constexpr int OFF_KTT = OFF_KHT + D * LDT * 2;             // K~ T  [D][LDT] f16
+  static constexpr int OFF_KHT = OFF_QT + C * LDQ * 2;              // K^ T [D][LDT] f16
+  static constexpr int OFF_KTT = OFF_KHT + D * LDT * 2;             // K~ T [D][LDT] f16
   static constexpr int OFF_B = OFF_KTT + D * LDT * 2;               // B    [64][LDT] f16
   static constexpr int OFF_L = OFF_B + C * LDT * 2;                 // L/A  [64][LDL] f32
-  static constexpr int OFF_SMALL = OFF_L + C * LDL * 4;             // gL[D], beta[64], Gs[64]
-  static constexpr int SMALL_BYTES = (D + 2 * C) * 4;
+  static constexpr int OFF_SMALL = OFF_L + C * LDL * 4;
+  // small arrays: G_n[D], 2^G_n[D], beta[64], scalar G[64], scan partials[4][D]
+  static constexpr int SMALL_BYTES = (2 * D + 2 * C + 4 * D) * 4;
   static constexpr int OFF_A = OFF_SMALL + SMALL_BYTES;             // region A (aliased)
   // region A, phase P1..P3: G [64][LDG] f32 (per-key), raw K, raw Q [64][LDQ] f16
   static constexpr int A_G = 0;
@@ -160,13 +175,14 @@ struct ChunkRegs {
   static constexpr int GROUPS = C * D / 8;       // 8-element groups per [64][D] tensor
   static constexpr int GPT = GROUPS / NT;        // groups per thread (2)
   RawGroup<BF16> k[GPT], q[GPT], v[GPT];
-  float alpha[PER_KEY ? 16 : 1];                 // per-key: 16 channels of token `lane`
+  // per-key: channel tid % D, tokens 16 (tid / D) .. +15; scalar: token = lane (wave 0)
+  float alpha[PER_KEY ? 16 : 1];
   float beta;
 };
 
 template <int D, bool BF16, bool PER_KEY>
 __device__ __forceinline__ void load_chunk(ChunkRegs<D, BF16, PER_KEY>& R, const PrefillArgs& a,
-                                           int64_t tok0, int n, int h, int tid) {
+                                           int64_t tok0, int n, int h, int tid, bool need_v) {
   using CR = ChunkRegs<D, BF16, PER_KEY>;
   const int64_t HD = (int64_t)a.H * D;
 #pragma unroll
@@ -177,22 +193,25 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<D, BF16, PER_KEY>& R, const
     const int64_t idx = (tok0 + (valid ? c : 0)) * HD + (int64_t)h * D + 8 * k8;
     R.k[j] = load_group<BF16>(a.k, idx, valid);
     R.q[j] = load_group<BF16>(a.q, idx, valid);
-    R.v[j] = load_group<BF16>(a.v, idx, valid);
+    R.v[j] = load_group<BF16>(a.v, idx, valid && need_v);
   }
   const int wave = tid / 64, lane = tid % 64;
-  const bool valid = lane < n;
-  const int64_t tok = tok0 + (valid ? lane : 0);
   if constexpr (PER_KEY) {
-    const f32x4* p = reinterpret_cast<const f32x4*>(a.alpha + (tok * a.H + h) * D + 16 * wave);
+    const int kcol = tid % D, cb = tid / D;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 x = valid ? p[i] : f32x4{1.f, 1.f, 1.f, 1.f};
-      R.alpha[4 * i] = x[0]; R.alpha[4 * i + 1] = x[1]; R.alpha[4 * i + 2] = x[2]; R.alpha[4 * i + 3] = x[3];
+    for (int j = 0; j < 16; ++j) {
+      const int c = 16 * cb + j;
+      const bool valid = c < n;
+      R.alpha[j] = valid ? a.alpha[((tok0 + c) * a.H + h) * D + kcol] : 1.f;
     }
   } else {
-    R.alpha[0] = (wave == 0 && valid) ? a.alpha[tok * a.H + h] : 1.f;
+    const bool valid = lane < n;
+    R.alpha[0] = (wave == 0 && valid) ? a.alpha[(tok0 + lane) * a.H + h] : 1.f;
   }
-  R.beta = (wave == 0 && valid) ? a.beta[tok * a.H + h] : 0.f;
+  {
+    const bool valid = lane < n;
+    R.beta = (wave == 0 && valid) ? a.beta[(tok0 + lane) * a.H + h] : 0.f;
+  }
 }
 
 __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
@@ -219,8 +238,10 @@ __global__ __launch_bounds__(D * 4) void prefill_kernel(PrefillArgs a) {
   _Float16* sB = reinterpret_cast<_Float16*>(smem + L::OFF_B);
   float* sL = reinterpret_cast<float*>(smem + L::OFF_L);
   float* sGL = reinterpret_cast<float*>(smem + L::OFF_SMALL);   // [D] G_n per channel
-  float* sBeta = sGL + D;                                         // [64]
+  float* sGam = sGL + D;                                          // [D] 2^G_n
+  float* sBeta = sGam + D;                                        // [64]
   float* sGs = sBeta + C;                                         // [64] scalar-gate G
+  float* sPart = sGs + C;                                         // [4][D] cumsum partials
   unsigned char* regA = smem + L::OFF_A;
   float* sG = reinterpret_cast<float*>(regA + L::A_G);
   _Float16* sRK = reinterpret_cast<_Float16*>(regA + L::A_RK);
@@ -232,29 +253,52 @@ __global__ __launch_bounds__(D * 4) void prefill_kernel(PrefillArgs a) {
 
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int g = lane >> 4, l16 = lane & 15;
-  const int item_idx = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const int per_item = a.pass == 1 ? 2 : 1;
+  const int item_idx = blockIdx.x / (a.H * per_item);
+  const int rem = blockIdx.x % (a.H * per_item);
+  const int h = rem / per_item, which = rem % per_item;
   const PrefillItem item = a.items[item_idx];
+
+  int mode = MODE_OUT;
+  if (a.pass == 1) {
+    if (item.seg == 0) mode = which == 0 ? MODE_OUT : MODE_IDLE;
+    else if (item.seg < item.n_segs - 1) mode = which == 0 ? MODE_MAP_N : MODE_MAP_M;
+    else mode = MODE_IDLE;
+  } else if (a.pass == 3) {
+    mode = item.seg >= 1 ? MODE_OUT : MODE_IDLE;
+  }
+  if (mode == MODE_IDLE) return;   // uniform over the workgroup
+  const bool out_mode = mode == MODE_OUT;
+  const bool need_v = mode != MODE_MAP_M;
   const int64_t HD = (int64_t)a.H * D;
   const int slice = wave;          // state rows 16*slice .. 16*slice+15
+  const int64_t DD = (int64_t)D * D;
 
   // ---- start state: S0^T in accumulator layout ------------------------------
   // tile kt, lane l: S0^T[k = 16kt + 4g + i][v = 16 slice + l16] = S0[v][k]
   f32x4 ST[KT];
   {
     const float* src = nullptr;
-    if (a.seg_chunks > 0 && item.seg > 0)
-      src = a.seg_states + ((int64_t)item_idx * a.H + h) * D * D;
-    else if (a.init)
-      src = a.init + ((int64_t)item.seq * a.H + h) * D * D;
+    if (mode == MODE_OUT) {
+      if (item.seg > 0) src = a.seg_states + ((int64_t)item_idx * a.H + h) * DD;
+      else if (a.init) src = a.init + ((int64_t)item.seq * a.H + h) * DD;
+    }
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-      ST[kt] = src ? *reinterpret_cast<const f32x4*>(src + (16 * slice + l16) * D + 16 * kt + 4 * g)
-                   : f32x4{0, 0, 0, 0};
+    for (int kt = 0; kt < KT; ++kt) {
+      if (src) {
+        ST[kt] = *reinterpret_cast<const f32x4*>(src + (16 * slice + l16) * D + 16 * kt + 4 * g);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          ST[kt][i] = (mode == MODE_MAP_M && 16 * slice + l16 == 16 * kt + 4 * g + i) ? 1.f : 0.f;
+      }
+    }
   }
 
   const int n_chunks = (item.n_tokens + C - 1) / C;
   CR regs;
-  if (n_chunks > 0) load_chunk<D, BF16, PER_KEY>(regs, a, item.tok_begin, min(C, item.n_tokens), h, tid);
+  if (n_chunks > 0)
+    load_chunk<D, BF16, PER_KEY>(regs, a, item.tok_begin, min(C, item.n_tokens), h, tid, need_v);
 
   for (int ch = 0; ch < n_chunks; ++ch) {
     const int64_t tok0 = item.tok_begin + (int64_t)ch * C;
@@ -276,25 +320,43 @@ __global__ __launch_bounds__(D * 4) void prefill_kernel(PrefillArgs a) {
       for (int e = 0; e < 8; ++e) hv[e] = (_Float16)x[e];
       *reinterpret_cast<f16x8*>(sRQ + c * L::LDQ + 8 * k8) = hv;
     }
+    float gloc[PER_KEY ? 16 : 1];
     if constexpr (PER_KEY) {
-      // wave w: channels 16w..16w+15, lane = token
+      // thread: channel tid % D, tokens 16 cb .. 16 cb + 15; local scan, then
+      // the block totals of the 4 token blocks are combined through LDS.
+      const int kcol = tid % D, cb = tid / D;
+      float run = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float gcum = wave_inclusive_scan(log2f(regs.alpha[i]), lane);
-        sG[lane * L::LDG + 16 * wave + i] = gcum;
-        if (lane == C - 1) sGL[16 * wave + i] = gcum;
+      for (int j = 0; j < 16; ++j) {
+        run += log2_hw(regs.alpha[j]);
+        gloc[j] = run;
       }
+      sPart[cb * D + kcol] = run;
     } else {
       if (wave == 0) {
-        const float gcum = wave_inclusive_scan(log2f(regs.alpha[0]), lane);
+        const float gcum = wave_inclusive_scan(log2_hw(regs.alpha[0]), lane);
         sGs[lane] = gcum;
         const float gl = __shfl(gcum, C - 1);
+        const float gam = exp2_hw(gl);
         sGL[lane] = gl;
-        if (D > 64) sGL[lane + 64] = gl;
+        sGam[lane] = gam;
+        if (D > 64) { sGL[lane + 64] = gl; sGam[lane + 64] = gam; }
       }
     }
     if (wave == 0) sBeta[lane] = regs.beta;
     __syncthreads();
+    if constexpr (PER_KEY) {
+      const int kcol = tid % D, cb = tid / D;
+      float pre = 0.f;
+      for (int b = 0; b < cb; ++b) pre += sPart[b * D + kcol];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sG[(16 * cb + j) * L::LDG + kcol] = pre + gloc[j];
+      if (cb == 3) {
+        sGL[kcol] = pre + gloc[15];
+        sGam[kcol] = exp2_hw(pre + gloc[15]);
+      }
+      __syncthreads();
+    }
 
     // ---- P2: decayed operands ------------------------------------------------
 #pragma unroll
@@ -309,9 +371,9 @@ __global__ __launch_bounds__(D * 4) void prefill_kernel(PrefillArgs a) {
       for (int e = 0; e < 8; ++e) {
         const int kk = 8 * k8 + e;
         const float gc = PER_KEY ? sG[c * L::LDG + kk] : sGs[c];
-        const float dec = exp2f(gc);
-        const float rem = exp2f(sGL[kk] - gc);
-        // fp16 rounding of the bf16 inputs happens here, once
+        const float dec = exp2_hw(gc);
+        const float rem = exp2_hw(sGL[kk] - gc);
+        // fp16 rounding of the inputs happens here, once (as in the Gram)
         const float kf = (float)(_Float16)kx[e];
         const float qf = (float)(_Float16)qx[e];
         qt[e] = (_Float16)(qf * dec);
@@ -354,8 +416,8 @@ __global__ __launch_bounds__(D * 4) void prefill_kernel(PrefillArgs a) {
           for (int e = 0; e < 8; ++e) {
             const int kk = 32 * ks + 8 * g + e;
             const float gref = sG[(16 * R) * L::LDG + kk];
-            const float fa = exp2f(sG[r * L::LDG + kk] - gref);
-            const float fb = exp2f(gref - sG[i * L::LDG + kk]);
+            const float fa = exp2_hw(sG[r * L::LDG + kk] - gref);
+            const float fb = exp2_hw(gref - sG[i * L::LDG + kk]);
             const float ka = (float)sRK[r * L::LDQ + kk] * fa;
             const float qa = (float)sRQ[r * L::LDQ + kk] * fa;
             const float kb = (float)sRK[i * L::LDQ + kk] * fb;
@@ -377,7 +439,7 @@ __global__ __launch_bounds__(D * 4) void prefill_kernel(PrefillArgs a) {
         const int r = 16 * R + 4 * g + i, ic = 16 * I + l16;
         float lv = accL[i], bv = accB[i];
         if constexpr (!PER_KEY) {
-          const float f = exp2f(fminf(sGs[r] - sGs[ic], 0.f));
+          const float f = exp2_hw(fminf(sGs[r] - sGs[ic], 0.f));
           lv *= f;
           bv *= f;
         }
@@ -389,7 +451,7 @@ __global__ __launch_bounds__(D * 4) void prefill_kernel(PrefillArgs a) {
 
     // ---- P4: A = (I + L)^-1 -------------------------------------------------
     // Diagonal 16x16 blocks by forward substitution (wave 0, one column per
-    // lane); A_bb overwrites L_bb. Other waves stage V^T meanwhile.
+    // lane); A_bb overwrites L_bb. The other lanes of the workgroup stage V^T.
     if (wave == 0) {
       const int b = g, j = l16;
       const float* Lb = sL + (16 * b) * L::LDL + 16 * b;
@@ -406,14 +468,16 @@ __global__ __launch_bounds__(D * 4) void prefill_kernel(PrefillArgs a) {
       for (int r = 0; r < 16; ++r) Ab[r * L::LDL + j] = x[r];
     }
     // V^T [v][c] into region A (G and raw q, k are dead after P3)
+    if (need_v) {
 #pragma unroll
-    for (int j = 0; j < CR::GPT; ++j) {
-      const int gi = tid + j * NT;
-      const int c = gi / (D / 8), k8 = gi % (D / 8);
-      float x[8];
-      unpack_group<BF16>(regs.v[j], x);
+      for (int j = 0; j < CR::GPT; ++j) {
+        const int gi = tid + j * NT;
+        const int c = gi / (D / 8), k8 = gi % (D / 8);
+        float x[8];
+        unpack_group<BF16>(regs.v[j], x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sVT[(8 * k8 + e) * L::LDT + c] = (_Float16)x[e];
+        for (int e = 0; e < 8; ++e) sVT[(8 * k8 + e) * L::LDT + c] = (_Float16)x[e];
+      }
     }
     __syncthreads();
     // Off-diagonal blocks, stage R = 1, 2, 3: job (R, I) on wave I,
@@ -490,59 +554,77 @@ __global__ __launch_bounds__(D * 4) void prefill_kernel(PrefillArgs a) {
 
     // prefetch the next chunk's raw inputs while the chain runs
     if (ch + 1 < n_chunks)
-      load_chunk<D, BF16, PER_KEY>(regs, a, tok0 + C, min(C, item.n_tokens - (ch + 1) * C), h, tid);
+      load_chunk<D, BF16, PER_KEY>(regs, a, tok0 + C, min(C, item.n_tokens - (ch + 1) * C), h, tid,
+                                   need_v);
 
     // ---- P6: state passing for this wavefront's slice -----------------------
     {
-      // U' = T~ V_s : rows c (4 tiles), column v = 16 slice + l16
+      // U' = T~ V_s : rows c (4 tiles), column v = 16 slice + l16 (zero in MAP_M)
       f32x4 U[4];
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) U[ct] = f32x4{0, 0, 0, 0};
+      if (need_v) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const f16x8 bv = ld_std(sVT, L::LDT, 16 * slice, 32 * ks, lane);
+        for (int ks = 0; ks < 2; ++ks) {
+          const f16x8 bv = ld_std(sVT, L::LDT, 16 * slice, 32 * ks, lane);
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          U[ct] = mfma_f16(ld_std(sTh, L::LDT, 16 * ct, 32 * ks, lane), bv, U[ct]);
-          U[ct] = mfma_f16(ld_std(sTl, L::LDT, 16 * ct, 32 * ks, lane), bv, U[ct]);
+          for (int ct = 0; ct < 4; ++ct) {
+            U[ct] = mfma_f16(ld_std(sTh, L::LDT, 16 * ct, 32 * ks, lane), bv, U[ct]);
+            U[ct] = mfma_f16(ld_std(sTl, L::LDT, 16 * ct, 32 * ks, lane), bv, U[ct]);
+          }
         }
       }
       // S0^T as the permuted-K operand (fp16), shared by W S0^T and Q~ S0^T
       f16x8 sop[D / 32];
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) sop[ks] = pack_perm(ST[2 * ks], ST[2 * ks + 1]);
-      f32x4 P[4], O[4];
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) { P[ct] = f32x4{0, 0, 0, 0}; O[ct] = f32x4{0, 0, 0, 0}; }
+      // U -= W S0^T
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) {
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
-          P[ct] = mfma_f16(ld_perm(sW, L::LDQ, 16 * ct, 32 * ks, lane), sop[ks], P[ct]);
-          O[ct] = mfma_f16(ld_perm(sQt, L::LDQ, 16 * ct, 32 * ks, lane), sop[ks], O[ct]);
+          f32x4 p = {0, 0, 0, 0};
+          p = mfma_f16(ld_perm(sW, L::LDQ, 16 * ct, 32 * ks, lane), sop[ks], p);
+          U[ct] -= p;
         }
       }
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) U[ct] = U[ct] - P[ct];
       // U as hi + lo permuted-K operands (K = chunk position, 2 steps)
       f16x8 uh[2], ul[2];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) split_perm(U[2 * ks], U[2 * ks + 1], uh[ks], ul[ks]);
-      // O += B U
+      if (out_mode) {
+        // O = Q~ S0^T + B U
+        f32x4 O[4];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+        for (int ct = 0; ct < 4; ++ct) O[ct] = f32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          const f16x8 ba = ld_perm(sB, L::LDT, 16 * ct, 32 * ks, lane);
-          O[ct] = mfma_f16(ba, uh[ks], O[ct]);
-          O[ct] = mfma_f16(ba, ul[ks], O[ct]);
+        for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct)
+            O[ct] = mfma_f16(ld_perm(sQt, L::LDQ, 16 * ct, 32 * ks, lane), sop[ks], O[ct]);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) {
+            const f16x8 ba = ld_perm(sB, L::LDT, 16 * ct, 32 * ks, lane);
+            O[ct] = mfma_f16(ba, uh[ks], O[ct]);
+            O[ct] = mfma_f16(ba, ul[ks], O[ct]);
+          }
         }
+        float* obase = a.o + tok0 * HD + (int64_t)h * D + 16 * slice + l16;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int c = 16 * ct + 4 * g + i;
+            if (c < n) obase[(int64_t)c * HD] = O[ct][i];
+          }
       }
       // S^T <- 2^(G_n) S^T + K~^T U
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ST[kt][i] *= exp2f(sGL[16 * kt + 4 * g + i]);
+        const f32x4 gam = *reinterpret_cast<const f32x4*>(sGam + 16 * kt + 4 * g);
+        ST[kt] *= gam;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const f16x8 ka = ld_perm(sKtT, L::LDT, 16 * kt, 32 * ks, lane);
@@ -550,23 +632,14 @@ __global__ __launch_bounds__(D * 4) void prefill_kernel(PrefillArgs a) {
           ST[kt] = mfma_f16(ka, ul[ks], ST[kt]);
         }
       }
-      // o rows of this chunk
-      float* obase = a.o + tok0 * HD + (int64_t)h * D + 16 * slice + l16;
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int c = 16 * ct + 4 * g + i;
-          if (c < n) obase[(int64_t)c * HD] = O[ct][i];
-        }
     }
 
     // snapshot after this chunk if the sequence position is a multiple of the interval
-    if (a.interval > 0) {
+    if (out_mode && a.interval > 0) {
       const int64_t pos = item.tok_in_seq + (int64_t)ch * C + n;   // tokens of the sequence done
       if (pos % a.interval == 0) {
         const int64_t slot = item.snap_base + pos / a.interval - 1;
-        float* dst = a.snapshots + (slot * a.H + h) * D * D;
+        float* dst = a.snapshots + (slot * a.H + h) * DD;
 #pragma unroll
         for (int kt = 0; kt < KT; ++kt)
           *reinterpret_cast<f32x4*>(dst + (16 * slice + l16) * D + 16 * kt + 4 * g) = ST[kt];
@@ -575,78 +648,178 @@ __global__ __launch_bounds__(D * 4) void prefill_kernel(PrefillArgs a) {
     __syncthreads();
   }
 
-  // final state of the sequence (or of the segment, for the segment scan)
-  {
-    float* dst = a.final_state + ((int64_t)item.seq * a.H + h) * D * D;
+  // end of the item: final state, start state of the next segment, or (M, N)
+  float* dst;
+  if (mode == MODE_OUT) {
+    dst = (item.seg == item.n_segs - 1) ? a.final_state + ((int64_t)item.seq * a.H + h) * DD
+                                        : a.seg_states + ((int64_t)(item_idx + 1) * a.H + h) * DD;
+  } else {
+    dst = a.seg_maps + ((int64_t)item_idx * a.H + h) * 2 * DD + (mode == MODE_MAP_N ? DD : 0);
+  }
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-      *reinterpret_cast<f32x4*>(dst + (16 * slice + l16) * D + 16 * kt + 4 * g) = ST[kt];
+  for (int kt = 0; kt < KT; ++kt)
+    *reinterpret_cast<f32x4*>(dst + (16 * slice + l16) * D + 16 * kt + 4 * g) = ST[kt];
+}
+
+// Segment scan: for every sequence with more than two segments, head and block
+// of 16 state rows, S_{s+1} = S_s M_s + N_s for s = 1 .. n_segs-2 in fp32 (S_1
+// comes from the first segment's OUT run). Rows of S evolve independently.
+template <int D>
+__global__ __launch_bounds__(256) void segment_scan_kernel(PrefillArgs a) {
+  constexpr int RB = 16;                        // rows per workgroup
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* sM = reinterpret_cast<float*>(smem);   // [D][D]
+  float* sS = sM + D * D;                       // [RB][D]
+  const int nrb = D / RB;
+  const int n = blockIdx.x / (a.H * nrb);
+  const int rem = blockIdx.x % (a.H * nrb);
+  const int h = rem / nrb, rb = rem % nrb;
+  const int first = a.seq_first_item[n];
+  const int ns = a.items[first].n_segs;
+  if (ns <= 2) return;
+  const int64_t DD = (int64_t)D * D;
+  const int tid = threadIdx.x;
+  const int r = tid / 16, c0 = tid % 16;        // output row r, columns c0 + 16 j
+  {
+    const float* S1 = a.seg_states + ((int64_t)(first + 1) * a.H + h) * DD + (int64_t)rb * RB * D;
+    for (int e = tid; e < RB * D; e += 256) sS[e] = S1[e];
+  }
+  for (int s = 1; s <= ns - 2; ++s) {
+    const float* M = a.seg_maps + ((int64_t)(first + s) * a.H + h) * 2 * DD;
+    const float* Nm = M + DD + (int64_t)rb * RB * D;
+    __syncthreads();
+    for (int e = 4 * tid; e < D * D; e += 4 * 256)
+      *reinterpret_cast<f32x4*>(sM + e) = *reinterpret_cast<const f32x4*>(M + e);
+    __syncthreads();
+    float acc[D / 16];
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) acc[j] = Nm[r * D + c0 + 16 * j];
+    for (int k = 0; k < D; ++k) {
+      const float sv = sS[r * D + k];
+#pragma unroll
+      for (int j = 0; j < D / 16; ++j) acc[j] += sv * sM[k * D + c0 + 16 * j];
+    }
+    __syncthreads();
+    float* out = a.seg_states + ((int64_t)(first + s + 1) * a.H + h) * DD + (int64_t)rb * RB * D;
+#pragma unroll
+    for (int j = 0; j < D / 16; ++j) {
+      sS[r * D + c0 + 16 * j] = acc[j];
+      out[r * D + c0 + 16 * j] = acc[j];
+    }
   }
 }
 
-// Work table: one item per sequence, longest first (stable), with the first
-// snapshot slot of each sequence. A single workgroup; lengths read from the
-// device copy of cu_seqlens.
-__global__ __launch_bounds__(256) void build_items_kernel(const int64_t* cu, int32_t N,
-                                                          int64_t interval, PrefillItem* items) {
-  __shared__ int64_t carry;
-  __shared__ int64_t part[256];
-  if (threadIdx.x == 0) carry = 0;
+// Work table. Unsegmented: one item per sequence, longest first (ties keep
+// sequence order). Segmented: each sequence is cut into runs of seg_chunks
+// chunks, items in sequence then segment order, with each sequence's first
+// item recorded. Every item carries the first snapshot slot of its sequence.
+// A single workgroup; lengths come from the device copy of cu_seqlens.
+__global__ __launch_bounds__(256) void build_items_kernel(PrefillArgs a) {
+  __shared__ int64_t carry_snap;
+  __shared__ int32_t carry_items;
+  __shared__ int64_t part_snap[256];
+  __shared__ int32_t part_items[256];
+  const int32_t N = a.num_seqs;
+  const int64_t* cu = a.cu_dev;
+  const int64_t seg_tokens = (int64_t)a.seg_chunks * C;
+  if (threadIdx.x == 0) { carry_snap = 0; carry_items = 0; }
   __syncthreads();
   for (int32_t base = 0; base < N; base += 256) {
     const int32_t n = base + threadIdx.x;
     const int64_t len = n < N ? cu[n + 1] - cu[n] : 0;
-    const int64_t ns = (interval > 0) ? len / interval : 0;
-    part[threadIdx.x] = ns;
+    const int64_t ns = (n < N && a.interval > 0) ? len / a.interval : 0;
+    int32_t nseg = n < N ? 1 : 0;
+    if (n < N && seg_tokens > 0 && len > seg_tokens) nseg = (int32_t)((len + seg_tokens - 1) / seg_tokens);
+    part_snap[threadIdx.x] = ns;
+    part_items[threadIdx.x] = nseg;
     __syncthreads();
     for (int off = 1; off < 256; off <<= 1) {
-      const int64_t y = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+      const int64_t ys = threadIdx.x >= off ? part_snap[threadIdx.x - off] : 0;
+      const int32_t yi = threadIdx.x >= off ? part_items[threadIdx.x - off] : 0;
       __syncthreads();
-      part[threadIdx.x] += y;
+      part_snap[threadIdx.x] += ys;
+      part_items[threadIdx.x] += yi;
       __syncthreads();
     }
     if (n < N) {
-      int32_t rank = n;
-      if (N <= 8192) {  // longest first for load balance; ties keep sequence order
-        rank = 0;
-        for (int32_t m = 0; m < N; ++m) {
-          const int64_t lm = cu[m + 1] - cu[m];
-          rank += (lm > len) || (lm == len && m < n);
+      const int64_t snap_base = carry_snap + part_snap[threadIdx.x] - ns;
+      const int32_t first = carry_items + part_items[threadIdx.x] - nseg;
+      if (a.seg_chunks == 0) {
+        int32_t rank = n;
+        if (N <= 8192) {  // longest first for load balance
+          rank = 0;
+          for (int32_t m = 0; m < N; ++m) {
+            const int64_t lm = cu[m + 1] - cu[m];
+            rank += (lm > len) || (lm == len && m < n);
+          }
+        }
+        PrefillItem it;
+        it.tok_begin = cu[n];
+        it.tok_in_seq = 0;
+        it.snap_base = snap_base;
+        it.n_tokens = (int32_t)len;
+        it.seq = n;
+        it.seg = 0;
+        it.n_segs = 1;
+        a.items[rank] = it;
+      } else {
+        a.seq_first_item[n] = first;
+        for (int32_t s = 0; s < nseg; ++s) {
+          PrefillItem it;
+          it.tok_in_seq = (int64_t)s * seg_tokens;
+          it.tok_begin = cu[n] + it.tok_in_seq;
+          it.snap_base = snap_base;
+          it.n_tokens = (int32_t)(nseg == 1 ? len : min(seg_tokens, len - it.tok_in_seq));
+          it.seq = n;
+          it.seg = s;
+          it.n_segs = nseg;
+          a.items[first + s] = it;
         }
       }
-      PrefillItem it;
-      it.tok_begin = cu[n];
-      it.n_tokens = (int32_t)len;
-      it.seq = n;
-      it.seg = 0;
-      it.n_segs = 1;
-      it.tok_in_seq = 0;
-      it.snap_base = carry + part[threadIdx.x] - ns;
-      items[rank] = it;
     }
     __syncthreads();
-    if (threadIdx.x == 255) carry += part[255];
+    if (threadIdx.x == 255) {
+      carry_snap += part_snap[255];
+      carry_items += part_items[255];
+    }
     __syncthreads();
   }
 }
 
 template <int D, bool BF16, bool PK>
-hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
+hipError_t launch_pass(const PrefillArgs& a, int pass, hipStream_t s) {
   using L = Lds<D>;
   static_assert(L::TOTAL <= 160 * 1024, "LDS budget");
   auto kern = prefill_kernel<D, BF16, PK>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(a.n_items * a.H), dim3(D * 4), L::TOTAL, s, a);
+  PrefillArgs p = a;
+  p.pass = pass;
+  const int per_item = pass == 1 ? 2 : 1;
+  hipLaunchKernelGGL(kern, dim3(a.n_items * a.H * per_item), dim3(D * 4), L::TOTAL, s, p);
   return hipGetLastError();
+}
+
+template <int D, bool BF16, bool PK>
+hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
+  if (a.seg_chunks == 0) return launch_pass<D, BF16, PK>(a, 0, s);
+  hipError_t e = launch_pass<D, BF16, PK>(a, 1, s);
+  if (e != hipSuccess) return e;
+  constexpr int scan_lds = (D * D + 16 * D) * 4;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(segment_scan_kernel<D>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, scan_lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(segment_scan_kernel<D>, dim3(a.num_seqs * a.H * (D / 16)), dim3(256), scan_lds, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_pass<D, BF16, PK>(a, 3, s);
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs& a, int d, bool bf16, bool per_key, hipStream_t s) {
-  hipLaunchKernelGGL(build_items_kernel, dim3(1), dim3(256), 0, s, a.cu_dev, a.num_seqs, a.interval,
-                     a.items);
+hipError_t launch_prefill(PrefillArgs a, int d, bool bf16, bool per_key, hipStream_t s) {
+  hipLaunchKernelGGL(build_items_kernel, dim3(1), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (d == 64) {

@@ -49,8 +49,9 @@ def load() -> ctypes.CDLL:
         "kda_abi_version": ([], ctypes.c_int),
         "kda_last_error": ([], ctypes.c_char_p),
         "kda_snapshot_count": ([I32, P, I64, P], ctypes.c_int),
-        "kda_prefill_workspace_size": ([P, I32, P, I32, I64, P], ctypes.c_int),
-        "kda_prefill_chunked": ([P, I32, P, P, I32, I64, P, P, P, P, P, P, P, P, P, P, SZ, P], ctypes.c_int),
+        "kda_prefill_workspace_size": ([P, I32, P, I32, I64, I64, P], ctypes.c_int),
+        "kda_prefill_chunked": ([P, I32, P, P, I32, I64, I64, P, P, P, P, P, P, P, P, P, P, SZ, P],
+                                ctypes.c_int),
         "kda_decode_step": ([P, I32, P, P, P, P, P, P, P, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
@@ -104,19 +105,19 @@ def kda_snapshot_count(cu_seqlens_host: torch.Tensor, interval: int) -> int:
 
 
 def kda_prefill_workspace_size(shape: KdaShape, cu_seqlens_host: torch.Tensor, chunk: int = CHUNK,
-                               snapshot_interval: int = 0) -> int:
+                               snapshot_interval: int = 0, segment_tokens: int = -1) -> int:
     cu = cu_seqlens_host.to("cpu", torch.int64).contiguous()
     out = ctypes.c_size_t(0)
     _check("kda_prefill_workspace_size",
            load().kda_prefill_workspace_size(ctypes.byref(shape), cu.numel() - 1, _ptr(cu), int(chunk),
-                                             int(snapshot_interval), ctypes.byref(out)))
+                                             int(snapshot_interval), int(segment_tokens), ctypes.byref(out)))
     return out.value
 
 
 def kda_prefill_chunked(shape: KdaShape, cu_seqlens_host: torch.Tensor, cu_seqlens_dev: torch.Tensor,
                         q, k, v, alpha, beta, initial_state, o, final_state, snapshots,
                         workspace: torch.Tensor, chunk: int = CHUNK, snapshot_interval: int = 0,
-                        stream=None) -> None:
+                        segment_tokens: int = -1, stream=None) -> None:
     """Enqueues the prefill on `stream` (default: torch's current stream). All
     tensors must already be allocated, contiguous, on one device."""
     cu = cu_seqlens_host.to("cpu", torch.int64).contiguous()
@@ -124,7 +125,7 @@ def kda_prefill_chunked(shape: KdaShape, cu_seqlens_host: torch.Tensor, cu_seqle
     s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream_ptr(dev)
     _check("kda_prefill_chunked", load().kda_prefill_chunked(
         ctypes.byref(shape), cu.numel() - 1, _ptr(cu), _ptr(cu_seqlens_dev), int(chunk),
-        int(snapshot_interval), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state),
+        int(snapshot_interval), int(segment_tokens), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state),
         _ptr(o), _ptr(final_state), _ptr(snapshots), _ptr(workspace), workspace.numel(), s))
 
 
@@ -147,9 +148,11 @@ def prefill_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: to
                     beta: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None,
                     initial_state: Optional[torch.Tensor] = None, snapshot_interval: int = 0,
                     cu_seqlens_host: Optional[torch.Tensor] = None, chunk: int = CHUNK,
+                    segment_tokens: int = -1,
                     out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
     """q, k [T,H,dk], v [T,H,dv] (bf16/fp32), alpha [T,H] or [T,H,dk], beta [T,H]
     (fp32). cu_seqlens: int64 [N+1] (default: one sequence of length T).
+    segment_tokens: -1 automatic segment plan, 0 none, > 0 segment length.
     Returns (o [T,H,dv] fp32, final_state [N,H,dv,dk], snapshots [S,H,dv,dk])."""
     T, H, dk = q.shape
     dv = v.shape[2]
@@ -170,10 +173,10 @@ def prefill_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: to
         snaps = torch.empty((n_snap, H, dv, dk), dtype=torch.float32, device=dev)
     else:
         o, fin, snaps = out
-    ws_bytes = kda_prefill_workspace_size(shape, cu_seqlens_host, chunk, snapshot_interval)
+    ws_bytes = kda_prefill_workspace_size(shape, cu_seqlens_host, chunk, snapshot_interval, segment_tokens)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     kda_prefill_chunked(shape, cu_seqlens_host, cu_dev, q, k, v, alpha, beta, initial_state, o, fin,
-                        snaps if n_snap > 0 else None, ws, chunk, snapshot_interval)
+                        snaps if n_snap > 0 else None, ws, chunk, snapshot_interval, segment_tokens)
     return o, fin, snaps
 
 

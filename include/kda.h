@@ -32,8 +32,9 @@
  *     is enqueued; outputs are then untouched. KDA_ERR_DEVICE reports a HIP
  *     launch failure (work may be partly enqueued). kda_last_error() gives the
  *     text of the calling thread's last failure.
- *   - Determinism: no atomics; results are bitwise reproducible run to run and
- *     a sequence's results do not depend on the other sequences of the pack.
+ *   - Determinism: no atomics; results are bitwise reproducible run to run.
+ *     With a fixed segment plan (see kda_prefill_chunked) a sequence's
+ *     results do not depend on the other sequences of the pack.
  *
  * Numerical preconditions of the chunked prefill (its matrix products run on
  * fp16 MFMA with fp32 accumulation; see kda_prefill_chunked):
@@ -57,7 +58,7 @@ typedef enum {
   KDA_OK = 0,
   KDA_ERR_ARG = -1,       /* NULL pointer, unsupported enum, negative size      */
   KDA_ERR_SHAPE = -2,     /* unsupported d_k/d_v/chunk, bad cu_seqlens, interval */
-  KDA_ERR_ALIGN = -3,     /* a pointer is not 16-byte aligned                    */
+  KDA_ERR_ALIGN = -3,     /* a pointer is misaligned for the accesses made on it */
   KDA_ERR_WORKSPACE = -4, /* workspace missing or too small                      */
   KDA_ERR_DEVICE = -5     /* HIP error while enqueueing                          */
 } kda_status;
@@ -91,7 +92,8 @@ int kda_snapshot_count(int32_t num_seqs, const int64_t* cu_seqlens_host, int64_t
  * (host-only). Same error codes as kda_prefill_chunked's validation. */
 int kda_prefill_workspace_size(const kda_shape* shape, int32_t num_seqs,
                                const int64_t* cu_seqlens_host, int32_t chunk,
-                               int64_t snapshot_interval, size_t* bytes);
+                               int64_t snapshot_interval, int64_t segment_tokens,
+                               size_t* bytes);
 
 /* Chunkwise-parallel prefill over a varlen pack.
  *
@@ -101,13 +103,25 @@ int kda_prefill_workspace_size(const kda_shape* shape, int32_t num_seqs,
  * `chunk` tokens restart at every sequence start (the last one may be
  * partial). Per chunk the kernels form the decayed key Gram matrix, solve the
  * unit-lower-triangular system of the UT/WY form in LDS, and pass the fp32
- * state to the next chunk with MFMA products; long sequences with few heads
- * are additionally split into segments whose affine state maps are composed.
+ * state to the next chunk with MFMA products.
+ *
+ * Segments: a run of chunks maps the state affinely, S_end = S_start M + N.
+ * When the (sequence, head) chains are too few to fill the GPU, long
+ * sequences are cut into segments of `segment_tokens` tokens: one pass
+ * computes every middle segment's (M, N) and runs the first segment, a fp32
+ * scan composes the segment start states, and a last pass reruns the
+ * segments from their true start states.
  *
  * cu_seqlens_host / cu_seqlens_dev: the same int64 [num_seqs+1] offsets on
  *   host (validation, grid sizing) and device (indexing); cu[0] = 0,
  *   nondecreasing, T = cu[num_seqs]. Empty sequences are allowed.
  * chunk: must be 64.
+ * segment_tokens: -1 = automatic (segments only when num_seqs * H is below
+ *   the device's compute-unit count; the plan then depends on the whole
+ *   pack, so a sequence's rounding can differ from a solo run, within the
+ *   tolerances), 0 = never segment, > 0 = segment length, a multiple of 64.
+ *   With a fixed value (0 or > 0) each sequence's results are bitwise
+ *   independent of the rest of the pack.
  * snapshot_interval: 0, or a positive multiple of `chunk`. The state after
  *   the first m*interval tokens of each sequence (m = 1..floor(len/interval))
  *   is written to snapshots[base_n + m - 1], base_n = slots of the earlier
@@ -120,7 +134,7 @@ int kda_prefill_workspace_size(const kda_shape* shape, int32_t num_seqs,
  */
 int kda_prefill_chunked(const kda_shape* shape, int32_t num_seqs,
                         const int64_t* cu_seqlens_host, const int64_t* cu_seqlens_dev,
-                        int32_t chunk, int64_t snapshot_interval,
+                        int32_t chunk, int64_t snapshot_interval, int64_t segment_tokens,
                         const void* q, const void* k, const void* v,
                         const float* alpha, const float* beta,
                         const float* initial_state,

@@ -20,10 +20,11 @@ def device():
     return torch.device("cuda:0")
 
 
-def run_prefill(inp: dict, interval: int):
+def run_prefill(inp: dict, interval: int, segment_tokens: int = -1):
     o, fin, snaps = kda.prefill_chunked(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"],
                                         inp["cu_seqlens"], inp["initial_state"], interval,
-                                        cu_seqlens_host=inp["cu_seqlens_host"])
+                                        cu_seqlens_host=inp["cu_seqlens_host"],
+                                        segment_tokens=segment_tokens)
     torch.cuda.synchronize()
     return o, fin, snaps
 

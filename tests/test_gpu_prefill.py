@@ -105,11 +105,13 @@ def test_run_twice_bitwise_deterministic():
         assert torch.equal(x, y)
 
 
-def test_packed_equals_solo_bitwise():
+@pytest.mark.parametrize("segment_tokens", [0, 128])
+def test_packed_equals_solo_bitwise(segment_tokens):
+    """With a fixed segment plan a sequence's results do not depend on the pack."""
     dev = device()
-    w = custom("packing", H=2, d=64, lens=(300, 0, 65, 128), gate="per_key", interval=64, seed=14)
+    w = custom("packing", H=2, d=64, lens=(300, 0, 65, 128, 700), gate="per_key", interval=64, seed=14)
     inp = wl.make_prefill_inputs(w, dev)
-    o, fin, snaps = run_prefill(inp, w.interval)
+    o, fin, snaps = run_prefill(inp, w.interval, segment_tokens)
     cu = inp["cu_seqlens_host"].tolist()
     slot = 0
     for n, L in enumerate(w.seq_lens):
@@ -118,7 +120,7 @@ def test_packed_equals_solo_bitwise():
                    beta=inp["beta"][s:e], cu_seqlens=torch.tensor([0, L], device=dev),
                    cu_seqlens_host=torch.tensor([0, L]),
                    initial_state=inp["initial_state"][n:n + 1].contiguous())
-        o1, f1, s1 = run_prefill(sub, w.interval)
+        o1, f1, s1 = run_prefill(sub, w.interval, segment_tokens)
         assert torch.equal(o[s:e], o1)
         assert torch.equal(fin[n:n + 1], f1)
         assert torch.equal(snaps[slot:slot + s1.shape[0]], s1)
@@ -132,13 +134,58 @@ def test_prefix_split_resume_bitwise():
     dev = device()
     w = custom("prefix", H=2, d=128, lens=(1000,), gate="scalar", interval=256, seed=15)
     inp = wl.make_prefill_inputs(w, dev)
-    o, fin, snaps = run_prefill(inp, w.interval)
+    o, fin, snaps = run_prefill(inp, w.interval, 0)
     N = 512
     part = lambda s, e, init: dict(q=inp["q"][s:e], k=inp["k"][s:e], v=inp["v"][s:e],  # noqa: E731
                                    alpha=inp["alpha"][s:e], beta=inp["beta"][s:e],
                                    cu_seqlens=torch.tensor([0, e - s], device=dev),
                                    cu_seqlens_host=torch.tensor([0, e - s]), initial_state=init)
-    o1, f1, _ = run_prefill(part(0, N, inp["initial_state"]), 0)
-    o2, f2, _ = run_prefill(part(N, 1000, f1), 0)
+    o1, f1, _ = run_prefill(part(0, N, inp["initial_state"]), 0, 0)
+    o2, f2, _ = run_prefill(part(N, 1000, f1), 0, 0)
     assert torch.equal(snaps[1], f1[0])
     assert torch.equal(o[:N], o1) and torch.equal(o[N:], o2) and torch.equal(fin, f2)
+
+
+@pytest.mark.parametrize("segment_tokens", [64, 192, 1024])
+@pytest.mark.parametrize("gate", ["scalar", "per_key"])
+def test_segmented_plan_matches_oracle(segment_tokens, gate):
+    """Forced segment plans (segment maps, fp32 scan, reruns) on a varlen pack
+    with snapshots and initial states."""
+    dev = device()
+    w = custom(f"seg_{segment_tokens}_{gate}", H=2, d=128, lens=(2000, 70, 0, 1280, 64), gate=gate,
+               interval=128, seed=16)
+    print(f"case {w.name} lens={w.seq_lens}", flush=True)
+    inp = wl.make_prefill_inputs(w, dev)
+    check_prefill(inp, run_prefill(inp, w.interval, segment_tokens), w.interval)
+
+
+def test_segmented_close_to_unsegmented():
+    dev = device()
+    w = custom("seg_vs_plain", H=3, d=64, lens=(5000,), gate="per_key", interval=0, seed=17)
+    inp = wl.make_prefill_inputs(w, dev)
+    a = run_prefill(inp, 0, 0)
+    b = run_prefill(inp, 0, 512)
+    for x, y in zip(a[:2], b[:2]):
+        assert (x - y).abs().max().item() <= 1e-3 * x.abs().max().item()
+
+
+def test_long_prefill_config_sampled_heads():
+    """B=1 H=16 d=128 T=262144, scalar alpha, the measured launch (automatic
+    segment plan); the oracle checks heads 0 and 9 over the whole sequence."""
+    dev = device()
+    w = wl.LONG_PREFILL
+    inp = wl.make_prefill_inputs(w, dev)
+    outs = run_prefill(inp, 0)
+    check_prefill(inp, outs, 0, heads=(0, 9))
+
+
+def test_varlen_config_sampled_heads():
+    """32 packed sequences, H=32 d=128, per-key alpha, initial states,
+    snapshots every 4096 tokens; the oracle checks heads 5 and 30 of every
+    sequence, every snapshot and every final state."""
+    dev = device()
+    w = wl.VARLEN
+    inp = wl.make_prefill_inputs(w, dev)
+    outs = run_prefill(inp, w.interval)
+    assert outs[2].shape[0] == sum(L // w.interval for L in w.seq_lens)
+    check_prefill(inp, outs, w.interval, heads=(5, 30))
