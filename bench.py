@@ -61,12 +61,15 @@ def time_prefill(kda, torch, inp, w, steps, warmup):
     cu_h = inp["cu_seqlens_host"]
     o = torch.empty((T, H, dv), dtype=torch.float32, device=dev)
     fin = torch.empty((w.num_seqs, H, dv, dk), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(kda.kda_prefill_workspace_size(shape, cu_h, 64, 0), 1), dtype=torch.uint8,
-                     device=dev)
+    n_snap = kda.kda_snapshot_count(cu_h, w.interval)
+    snaps = torch.empty((n_snap, H, dv, dk), dtype=torch.float32, device=dev) if n_snap else None
+    ws = torch.empty(max(kda.kda_prefill_workspace_size(shape, cu_h, 64, w.interval), 1),
+                     dtype=torch.uint8, device=dev)
 
     def call():
         kda.kda_prefill_chunked(shape, cu_h, inp["cu_seqlens"], inp["q"], inp["k"], inp["v"],
-                                inp["alpha"], inp["beta"], inp["initial_state"], o, fin, None, ws)
+                                inp["alpha"], inp["beta"], inp["initial_state"], o, fin, snaps, ws,
+                                snapshot_interval=w.interval)
 
     for _ in range(warmup):
         call()
@@ -134,6 +137,8 @@ def main(argv=None):
                     help="token prefix the CPU oracle baseline runs on (0 = skip)")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="profiling: only the prefill loop")
+    ap.add_argument("--prefill-workload", default="long_prefill_T262144_H16_d128",
+                    help="workload name for the prefill line (default: the headline long prefill)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (every GPU box here "
@@ -146,12 +151,15 @@ def main(argv=None):
 
     kda.load()
     dev = torch.device("cuda:0")
-    w = wl.LONG_PREFILL
+    w = wl.ALL[args.prefill_workload]
     inp = wl.make_prefill_inputs(w, dev)
     torch.cuda.synchronize()
     ms, wall = time_prefill(kda, torch, inp, w, args.steps, args.warmup)
     ms_avg = sum(ms) / len(ms)
-    pb, pf = prefill_algorithmic(w.T, w.H, w.dk, w.dv, w.num_seqs, w.gate == "per_key")
+    n_snap = kda.kda_snapshot_count(inp["cu_seqlens_host"], w.interval)
+    pb, pf = prefill_algorithmic(w.T, w.H, w.dk, w.dv, w.num_seqs, w.gate == "per_key",
+                                 qkv_bytes=2 if w.dtype == "bf16" else 4,
+                                 with_init=inp["initial_state"] is not None, n_snap=n_snap)
     gbs = pb / (ms_avg * 1e-3) / 1e9
     tfl = pf / (ms_avg * 1e-3) / 1e12
     result = {
@@ -167,11 +175,11 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "fp16-mfma/fp32-state",
         "data": "synthetic (seeded; no dataset)",
-        "config": {"workload": w.name, "B": 1, "T": w.T, "H": w.H, "d_k": w.dk, "d_v": w.dv,
-                   "gate": w.gate, "chunk": w.chunk, "qkv": w.dtype},
+        "config": {"workload": w.name, "B": w.num_seqs, "T": w.T, "H": w.H, "d_k": w.dk, "d_v": w.dv,
+                   "gate": w.gate, "chunk": w.chunk, "qkv": w.dtype, "snapshot_interval": w.interval},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "prefill_kernel<128,bf16,scalar>",
+                     "kernel": f"prefill_kernel<{w.dk},{w.dtype},{w.gate}> (all passes)",
                      "algorithmic_bytes_per_launch": int(pb), "algorithmic_flops_per_launch": int(pf),
                      "mfma_tflops": round(tfl, 2), "mfma_frac": round(tfl / MFMA_F16_PEAK_TFLOPS, 4),
                      "attainable_frac": round((pb / (HBM_PEAK_GBS * 1e9)) / (ms_avg * 1e-3), 4)},

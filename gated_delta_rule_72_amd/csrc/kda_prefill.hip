@@ -18,10 +18,11 @@
 // N = U'^T (K*2^(G_n-G)): a chunk, and hence a run of chunks, acts on the
 // state as an affine map.
 //
-// Kernel structure. One workgroup per (work item, head), D/16 wavefronts
-// (D = d_k = d_v). Wavefront w owns 16 rows of the state (a "slice") and
-// keeps them transposed, S0^T, in MFMA accumulator layout (fp32) for the whole
-// item. Per chunk:
+// Kernel structure. One workgroup per (work item, head), four wavefronts (one
+// per SIMD, so each may use the full 512-entry register file). The state
+// (D = d_k = d_v rows) is cut into 16-row slices; wavefront w owns D/64 of
+// them and keeps them transposed, S0^T, in MFMA accumulator layout (fp32) for
+// the whole item. Per chunk:
 //   P1  raw q, k (fp16) and the decay cumsum G (fp32) into LDS; beta; 2^G_n.
 //   P2  decayed operands in LDS: Q~ = Q*2^G [c][k], K^T*2^G and
 //       (K*2^(G_n-G))^T [k][c] (fp16).
@@ -67,9 +68,18 @@ __device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+typedef __attribute__((address_space(1))) void gvoid_t;
+typedef __attribute__((address_space(3))) void lvoid_t;
+
 // Hardware base-2 exponential and logarithm (v_exp_f32 / v_log_f32).
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+// [k][c] fp16 arrays (K^T, K~^T, V^T) rotate each row by 8 * ((k / 8) % 8)
+// columns, so that the transposed staging writes of 16 consecutive
+// 8-channel groups land on distinct LDS banks; aligned groups of 4 and 8
+// columns stay contiguous, which is all the MFMA operand reads need.
+__device__ __forceinline__ int swz(int k, int c) { return (c + 8 * ((k >> 3) & 7)) & 63; }
 
 // Row (l%16) of a row-major fp16 matrix, the 8 K-elements of lane group
 // g = l/16 in the standard order: k0 + 8g .. k0 + 8g + 7.
@@ -81,6 +91,17 @@ __device__ __forceinline__ f16x8 ld_perm(const _Float16* base, int ld, int row0,
   const _Float16* p = base + (row0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4);
   const f16x4 lo = *reinterpret_cast<const f16x4*>(p);
   const f16x4 hi = *reinterpret_cast<const f16x4*>(p + 16);
+  return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+// The same two reads from a swizzled [k][c] array (row = k, K index = c).
+__device__ __forceinline__ f16x8 ld_std_swz(const _Float16* base, int ld, int row0, int k0, int lane) {
+  const int r = row0 + (lane & 15);
+  return *reinterpret_cast<const f16x8*>(base + r * ld + swz(r, k0 + 8 * (lane >> 4)));
+}
+__device__ __forceinline__ f16x8 ld_perm_swz(const _Float16* base, int ld, int row0, int k0, int lane) {
+  const int r = row0 + (lane & 15);
+  const f16x4 lo = *reinterpret_cast<const f16x4*>(base + r * ld + swz(r, k0 + 4 * (lane >> 4)));
+  const f16x4 hi = *reinterpret_cast<const f16x4*>(base + r * ld + swz(r, k0 + 16 + 4 * (lane >> 4)));
   return f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 // Two accumulator tiles (rows k0..k0+15 and k0+16..k0+31) as a permuted-K operand.
@@ -137,14 +158,16 @@ struct RawGroup<true> { uint4 w; };
 template <>
 struct RawGroup<false> { f32x4 a, b; };
 
+// `base` is uniform over the workgroup (scalar registers); `off` is the lane's
+// 32-bit element offset from it, so loads use the scalar-base addressing form.
 template <bool BF16>
-__device__ __forceinline__ RawGroup<BF16> load_group(const void* base, int64_t idx, bool valid) {
+__device__ __forceinline__ RawGroup<BF16> load_group(const void* base, uint32_t off, bool valid) {
   RawGroup<BF16> r;
   if constexpr (BF16) {
-    r.w = valid ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx)
+    r.w = valid ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off)
                 : uint4{0, 0, 0, 0};
   } else {
-    const float* p = static_cast<const float*>(base) + idx;
+    const float* p = static_cast<const float*>(base) + off;
     r.a = valid ? *reinterpret_cast<const f32x4*>(p) : f32x4{0, 0, 0, 0};
     r.b = valid ? *reinterpret_cast<const f32x4*>(p + 4) : f32x4{0, 0, 0, 0};
   }
@@ -169,49 +192,82 @@ __device__ __forceinline__ void unpack_group(const RawGroup<BF16>& r, float (&x)
 }
 
 // Registers holding one chunk's raw inputs (prefetched during the previous chunk).
+constexpr int NT = 256;   // threads per workgroup (four wavefronts)
+constexpr int NW_STAGE = NT / 64;
+
+// bf16 inputs: the raw q and k rows of a chunk go straight from HBM into LDS
+// (global_load_lds_dwordx4: lane l's 16 bytes land at base + 16 l), into
+// buffers that are dead during the state passing, so the prefetch of the
+// next chunk holds no registers. Rows past the chunk end are loaded from row
+// 0 and zeroed when they are read. `src` is the workgroup-uniform chunk base.
+template <int D>
+__device__ __forceinline__ void stage_rows_lds(const uint16_t* src, uint32_t HD, int n, void* lds,
+                                               int wave, int lane) {
+  constexpr int LPR = D / 8;                 // lanes per row (16 bytes each)
+  constexpr int RPI = 64 / LPR;              // rows per wavefront instruction (1 KiB)
+  constexpr int INSTR = C / RPI;             // instructions per chunk
+#pragma unroll
+  for (int j = 0; j < INSTR / NW_STAGE; ++j) {
+    const int i = wave + NW_STAGE * j;
+    const int row = i * RPI + lane / LPR;
+    const uint16_t* gp = src + (uint32_t)(row < n ? row : 0) * HD + 8 * (lane % LPR);
+    __builtin_amdgcn_global_load_lds((gvoid_t*)gp, (lvoid_t*)(static_cast<char*>(lds) + 1024 * i),
+                                     16, 0, 0);
+  }
+}
+
 template <int D, bool BF16, bool PER_KEY>
 struct ChunkRegs {
-  static constexpr int NT = D * 4;               // threads per workgroup
   static constexpr int GROUPS = C * D / 8;       // 8-element groups per [64][D] tensor
-  static constexpr int GPT = GROUPS / NT;        // groups per thread (2)
-  RawGroup<BF16> k[GPT], q[GPT], v[GPT];
-  // per-key: channel tid % D, tokens 16 (tid / D) .. +15; scalar: token = lane (wave 0)
-  float alpha[PER_KEY ? 16 : 1];
+  static constexpr int GPT = GROUPS / NT;        // groups per thread (D / 32)
+  static constexpr int TPB = C * D / NT;         // per-key alpha: tokens per thread (D / 4)
+  RawGroup<BF16> k[BF16 ? 1 : GPT], q[BF16 ? 1 : GPT], v[GPT];   // bf16: q, k staged in LDS
+  // per-key: channel tid % D, tokens TPB (tid / D) .. +TPB-1; scalar: token = lane (wave 0)
+  float alpha[PER_KEY ? TPB : 1];
   float beta;
 };
 
+// Every address is a workgroup-uniform base (scalar registers, cheap to
+// recompute per access) plus one 32-bit per-lane offset that does not depend
+// on the loop index, so no per-access offsets are kept live.
 template <int D, bool BF16, bool PER_KEY>
 __device__ __forceinline__ void load_chunk(ChunkRegs<D, BF16, PER_KEY>& R, const PrefillArgs& a,
                                            int64_t tok0, int n, int h, int tid, bool need_v) {
   using CR = ChunkRegs<D, BF16, PER_KEY>;
-  const int64_t HD = (int64_t)a.H * D;
+  constexpr int ROWS_PER_PASS = NT / (D / 8);     // tokens covered by one group pass
+  const int64_t HD = (int64_t)a.H * D;            // elements per token (all heads)
+  const int64_t row0 = (tok0 * a.H + h) * D;      // first element of this chunk and head
+  const int c0 = tid / (D / 8), k8 = tid % (D / 8);
+  const uint32_t lane_off = (uint32_t)c0 * (uint32_t)HD + 8u * k8;
 #pragma unroll
   for (int j = 0; j < CR::GPT; ++j) {
-    const int gi = tid + j * CR::NT;
-    const int c = gi / (D / 8), k8 = gi % (D / 8);
+    const int c = c0 + j * ROWS_PER_PASS;
     const bool valid = c < n;
-    const int64_t idx = (tok0 + (valid ? c : 0)) * HD + (int64_t)h * D + 8 * k8;
-    R.k[j] = load_group<BF16>(a.k, idx, valid);
-    R.q[j] = load_group<BF16>(a.q, idx, valid);
-    R.v[j] = load_group<BF16>(a.v, idx, valid && need_v);
+    const int64_t ub = row0 + (int64_t)j * ROWS_PER_PASS * HD;   // uniform
+    if constexpr (BF16) {
+      R.v[j] = load_group<true>(static_cast<const uint16_t*>(a.v) + ub, lane_off, valid && need_v);
+    } else {
+      R.k[j] = load_group<false>(static_cast<const float*>(a.k) + ub, lane_off, valid);
+      R.q[j] = load_group<false>(static_cast<const float*>(a.q) + ub, lane_off, valid);
+      R.v[j] = load_group<false>(static_cast<const float*>(a.v) + ub, lane_off, valid && need_v);
+    }
   }
   const int wave = tid / 64, lane = tid % 64;
   if constexpr (PER_KEY) {
     const int kcol = tid % D, cb = tid / D;
+    const uint32_t a_off = (uint32_t)(CR::TPB * cb) * (uint32_t)HD + (uint32_t)kcol;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int c = 16 * cb + j;
-      const bool valid = c < n;
-      R.alpha[j] = valid ? a.alpha[((tok0 + c) * a.H + h) * D + kcol] : 1.f;
+    for (int j = 0; j < CR::TPB; ++j) {
+      const int c = CR::TPB * cb + j;
+      const float* ab = a.alpha + row0 + (int64_t)j * HD;          // uniform
+      R.alpha[j] = c < n ? ab[a_off] : 1.f;
     }
   } else {
-    const bool valid = lane < n;
-    R.alpha[0] = (wave == 0 && valid) ? a.alpha[(tok0 + lane) * a.H + h] : 1.f;
+    const float* ab = a.alpha + tok0 * a.H + h;
+    R.alpha[0] = (wave == 0 && lane < n) ? ab[(uint32_t)lane * a.H] : 1.f;
   }
-  {
-    const bool valid = lane < n;
-    R.beta = (wave == 0 && valid) ? a.beta[(tok0 + lane) * a.H + h] : 0.f;
-  }
+  const float* bb = a.beta + tok0 * a.H + h;
+  R.beta = (wave == 0 && lane < n) ? bb[(uint32_t)lane * a.H] : 0.f;
 }
 
 __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
@@ -224,11 +280,12 @@ __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
 }
 
 template <int D, bool BF16, bool PER_KEY>
-__global__ __launch_bounds__(D * 4) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void prefill_kernel(PrefillArgs a) {
   using L = Lds<D>;
   using CR = ChunkRegs<D, BF16, PER_KEY>;
-  constexpr int NW = D / 16;     // wavefronts = state slices
-  constexpr int NT = D * 4;
+  constexpr int NW = NT / 64;    // wavefronts
+  constexpr int SPW = D / 64;    // state slices per wavefront
   constexpr int KT = D / 16;     // 16-row tiles along d_k
   extern __shared__ __align__(16) unsigned char smem[];
 
@@ -271,12 +328,12 @@ __global__ __launch_bounds__(D * 4) void prefill_kernel(PrefillArgs a) {
   const bool out_mode = mode == MODE_OUT;
   const bool need_v = mode != MODE_MAP_M;
   const int64_t HD = (int64_t)a.H * D;
-  const int slice = wave;          // state rows 16*slice .. 16*slice+15
   const int64_t DD = (int64_t)D * D;
 
   // ---- start state: S0^T in accumulator layout ------------------------------
+  // slice sl of this wavefront covers state rows 16 (SPW wave + sl) .. +15;
   // tile kt, lane l: S0^T[k = 16kt + 4g + i][v = 16 slice + l16] = S0[v][k]
-  f32x4 ST[KT];
+  f32x4 ST[SPW][KT];
   {
     const float* src = nullptr;
     if (mode == MODE_OUT) {
@@ -284,21 +341,36 @@ __global__ __launch_bounds__(D * 4) void prefill_kernel(PrefillArgs a) {
       else if (a.init) src = a.init + ((int64_t)item.seq * a.H + h) * DD;
     }
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt) {
-      if (src) {
-        ST[kt] = *reinterpret_cast<const f32x4*>(src + (16 * slice + l16) * D + 16 * kt + 4 * g);
-      } else {
+    for (int sl = 0; sl < SPW; ++sl) {
+      const int row = 16 * (SPW * wave + sl) + l16;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          ST[kt][i] = (mode == MODE_MAP_M && 16 * slice + l16 == 16 * kt + 4 * g + i) ? 1.f : 0.f;
+      for (int kt = 0; kt < KT; ++kt) {
+        if (src) {
+          ST[sl][kt] = *reinterpret_cast<const f32x4*>(src + row * D + 16 * kt + 4 * g);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            ST[sl][kt][i] = (mode == MODE_MAP_M && row == 16 * kt + 4 * g + i) ? 1.f : 0.f;
+        }
       }
     }
   }
 
   const int n_chunks = (item.n_tokens + C - 1) / C;
+  const uint32_t HDu = (uint32_t)a.H * D;
   CR regs;
-  if (n_chunks > 0)
+  if (n_chunks > 0) {
     load_chunk<D, BF16, PER_KEY>(regs, a, item.tok_begin, min(C, item.n_tokens), h, tid, need_v);
+    if constexpr (BF16) {
+      const int64_t row0 = (item.tok_begin * a.H + h) * D;
+      stage_rows_lds<D>(static_cast<const uint16_t*>(a.k) + row0, HDu, min(C, item.n_tokens),
+                        smem + L::OFF_KHT, wave, lane);
+      stage_rows_lds<D>(static_cast<const uint16_t*>(a.q) + row0, HDu, min(C, item.n_tokens),
+                        smem + L::OFF_L, wave, lane);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
+  }
 
   for (int ch = 0; ch < n_chunks; ++ch) {
     const int64_t tok0 = item.tok_begin + (int64_t)ch * C;
@@ -309,25 +381,40 @@ __global__ __launch_bounds__(D * 4) void prefill_kernel(PrefillArgs a) {
     for (int j = 0; j < CR::GPT; ++j) {
       const int gi = tid + j * NT;
       const int c = gi / (D / 8), k8 = gi % (D / 8);
-      float x[8];
-      f16x8 hv;
-      unpack_group<BF16>(regs.k[j], x);
+      f16x8 kh, qh;
+      if constexpr (BF16) {
+        // staged bf16 rows [64][D] (unpadded); rows >= n are stale and zeroed here
+        const uint4 kw = *reinterpret_cast<const uint4*>(smem + L::OFF_KHT + (c * D + 8 * k8) * 2);
+        const uint4 qw = *reinterpret_cast<const uint4*>(smem + L::OFF_L + (c * D + 8 * k8) * 2);
+        const uint32_t kk4[4] = {kw.x, kw.y, kw.z, kw.w}, qq4[4] = {qw.x, qw.y, qw.z, qw.w};
+        const bool live = c < n;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) hv[e] = (_Float16)x[e];
-      *reinterpret_cast<f16x8*>(sRK + c * L::LDQ + 8 * k8) = hv;
-      unpack_group<BF16>(regs.q[j], x);
+        for (int e = 0; e < 4; ++e) {
+          kh[2 * e] = (_Float16)(live ? bf16_bits_to_f32(kk4[e] & 0xFFFFu) : 0.f);
+          kh[2 * e + 1] = (_Float16)(live ? bf16_bits_to_f32(kk4[e] >> 16) : 0.f);
+          qh[2 * e] = (_Float16)(live ? bf16_bits_to_f32(qq4[e] & 0xFFFFu) : 0.f);
+          qh[2 * e + 1] = (_Float16)(live ? bf16_bits_to_f32(qq4[e] >> 16) : 0.f);
+        }
+      } else {
+        float x[8];
+        unpack_group<BF16>(regs.k[j], x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) hv[e] = (_Float16)x[e];
-      *reinterpret_cast<f16x8*>(sRQ + c * L::LDQ + 8 * k8) = hv;
+        for (int e = 0; e < 8; ++e) kh[e] = (_Float16)x[e];
+        unpack_group<BF16>(regs.q[j], x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qh[e] = (_Float16)x[e];
+      }
+      *reinterpret_cast<f16x8*>(sRK + c * L::LDQ + 8 * k8) = kh;
+      *reinterpret_cast<f16x8*>(sRQ + c * L::LDQ + 8 * k8) = qh;
     }
-    float gloc[PER_KEY ? 16 : 1];
+    float gloc[PER_KEY ? CR::TPB : 1];
     if constexpr (PER_KEY) {
-      // thread: channel tid % D, tokens 16 cb .. 16 cb + 15; local scan, then
-      // the block totals of the 4 token blocks are combined through LDS.
+      // thread: channel tid % D, tokens TPB cb .. TPB cb + TPB-1; local scan,
+      // then the block totals are combined through LDS.
       const int kcol = tid % D, cb = tid / D;
       float run = 0.f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
+      for (int j = 0; j < CR::TPB; ++j) {
         run += log2_hw(regs.alpha[j]);
         gloc[j] = run;
       }
@@ -350,10 +437,10 @@ __global__ __launch_bounds__(D * 4) void prefill_kernel(PrefillArgs a) {
       float pre = 0.f;
       for (int b = 0; b < cb; ++b) pre += sPart[b * D + kcol];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) sG[(16 * cb + j) * L::LDG + kcol] = pre + gloc[j];
-      if (cb == 3) {
-        sGL[kcol] = pre + gloc[15];
-        sGam[kcol] = exp2_hw(pre + gloc[15]);
+      for (int j = 0; j < CR::TPB; ++j) sG[(CR::TPB * cb + j) * L::LDG + kcol] = pre + gloc[j];
+      if (cb == NT / D - 1) {
+        sGL[kcol] = pre + gloc[CR::TPB - 1];
+        sGam[kcol] = exp2_hw(pre + gloc[CR::TPB - 1]);
       }
       __syncthreads();
     }
@@ -363,9 +450,8 @@ __global__ __launch_bounds__(D * 4) void prefill_kernel(PrefillArgs a) {
     for (int j = 0; j < CR::GPT; ++j) {
       const int gi = tid + j * NT;
       const int c = gi / (D / 8), k8 = gi % (D / 8);
-      float kx[8], qx[8];
-      unpack_group<BF16>(regs.k[j], kx);
-      unpack_group<BF16>(regs.q[j], qx);
+      const f16x8 kx = *reinterpret_cast<const f16x8*>(sRK + c * L::LDQ + 8 * k8);
+      const f16x8 qx = *reinterpret_cast<const f16x8*>(sRQ + c * L::LDQ + 8 * k8);
       f16x8 qt;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -373,12 +459,10 @@ __global__ __launch_bounds__(D * 4) void prefill_kernel(PrefillArgs a) {
         const float gc = PER_KEY ? sG[c * L::LDG + kk] : sGs[c];
         const float dec = exp2_hw(gc);
         const float rem = exp2_hw(sGL[kk] - gc);
-        // fp16 rounding of the inputs happens here, once (as in the Gram)
-        const float kf = (float)(_Float16)kx[e];
-        const float qf = (float)(_Float16)qx[e];
-        qt[e] = (_Float16)(qf * dec);
-        sKhT[kk * L::LDT + c] = (_Float16)(kf * dec);
-        sKtT[kk * L::LDT + c] = (_Float16)(kf * rem);
+        const float kf = (float)kx[e];
+        qt[e] = (_Float16)((float)qx[e] * dec);
+        sKhT[kk * L::LDT + swz(kk, c)] = (_Float16)(kf * dec);
+        sKtT[kk * L::LDT + swz(kk, c)] = (_Float16)(kf * rem);
       }
       *reinterpret_cast<f16x8*>(sQt + c * L::LDQ + 8 * k8) = qt;
     }
@@ -392,59 +476,54 @@ __global__ __launch_bounds__(D * 4) void prefill_kernel(PrefillArgs a) {
       const int I = t < 3 ? t + 1 : (t < 5 ? t - 1 : 3);
       sB[(16 * R + rr) * L::LDT + 16 * I + cc] = (_Float16)0.f;
     }
-    for (int t = wave; t < 10; t += NW) {
+    // scalar gate: jobs unrolled for overlap; per-key: one job at a time (the
+    // decayed operands of a job already fill the registers)
+#pragma unroll
+    for (int jj = 0; jj < (PER_KEY ? 1 : 20 / NW); ++jj)
+    for (int job = wave + NW * jj; job < 20; job += (PER_KEY ? NW : 20)) {
+      const int t = job >> 1;
+      const bool is_b = job & 1;                  // even: L tile, odd: B tile
       const int R = t < 1 ? 0 : (t < 3 ? 1 : (t < 6 ? 2 : 3));
       const int I = t - R * (R + 1) / 2;
-      f32x4 accL = {0, 0, 0, 0}, accB = {0, 0, 0, 0};
+      const _Float16* sA = is_b ? sRQ : sRK;
+      f32x4 acc = {0, 0, 0, 0};
       if constexpr (!PER_KEY) {
 #pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) {
-          const f16x8 ka = ld_std(sRK, L::LDQ, 16 * R, 32 * ks, lane);
-          const f16x8 qa = ld_std(sRQ, L::LDQ, 16 * R, 32 * ks, lane);
-          const f16x8 kb = ld_std(sRK, L::LDQ, 16 * I, 32 * ks, lane);
-          accL = mfma_f16(ka, kb, accL);
-          accB = mfma_f16(qa, kb, accB);
-        }
+        for (int ks = 0; ks < D / 32; ++ks)
+          acc = mfma_f16(ld_std(sA, L::LDQ, 16 * R, 32 * ks, lane), ld_std(sRK, L::LDQ, 16 * I, 32 * ks, lane),
+                         acc);
       } else {
         // operands decayed relative to token 16R: A-side 2^(G_r - G_16R) <= 1,
         // B-side 2^(G_16R - G_i) (<= 1 for i <= 16R, bounded inside block R).
         const int r = 16 * R + l16, i = 16 * I + l16;
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) {
-          bf16x8 kah, kal, qah, qal, kbh, kbl;
+          const int k0 = 32 * ks + 8 * g;
+          const f16x8 ar = *reinterpret_cast<const f16x8*>(sA + r * L::LDQ + k0);
+          const f16x8 br = *reinterpret_cast<const f16x8*>(sRK + i * L::LDQ + k0);
+          bf16x8 ah, al, bh, bl;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const int kk = 32 * ks + 8 * g + e;
+            const int kk = k0 + e;
             const float gref = sG[(16 * R) * L::LDG + kk];
-            const float fa = exp2_hw(sG[r * L::LDG + kk] - gref);
-            const float fb = exp2_hw(gref - sG[i * L::LDG + kk]);
-            const float ka = (float)sRK[r * L::LDQ + kk] * fa;
-            const float qa = (float)sRQ[r * L::LDQ + kk] * fa;
-            const float kb = (float)sRK[i * L::LDQ + kk] * fb;
-            kah[e] = (__bf16)ka; kal[e] = (__bf16)(ka - (float)kah[e]);
-            qah[e] = (__bf16)qa; qal[e] = (__bf16)(qa - (float)qah[e]);
-            kbh[e] = (__bf16)kb; kbl[e] = (__bf16)(kb - (float)kbh[e]);
+            const float av = (float)ar[e] * exp2_hw(sG[r * L::LDG + kk] - gref);
+            const float bv = (float)br[e] * exp2_hw(gref - sG[i * L::LDG + kk]);
+            ah[e] = (__bf16)av; al[e] = (__bf16)(av - (float)ah[e]);
+            bh[e] = (__bf16)bv; bl[e] = (__bf16)(bv - (float)bh[e]);
           }
-          accL = mfma_bf16(kah, kbh, accL);
-          accL = mfma_bf16(kah, kbl, accL);
-          accL = mfma_bf16(kal, kbh, accL);
-          accB = mfma_bf16(qah, kbh, accB);
-          accB = mfma_bf16(qah, kbl, accB);
-          accB = mfma_bf16(qal, kbh, accB);
+          acc = mfma_bf16(ah, bh, acc);
+          acc = mfma_bf16(ah, bl, acc);
+          acc = mfma_bf16(al, bh, acc);
         }
       }
       // epilogue: lane holds rows r = 16R + 4g + i, column ic = 16I + l16
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * R + 4 * g + i, ic = 16 * I + l16;
-        float lv = accL[i], bv = accB[i];
-        if constexpr (!PER_KEY) {
-          const float f = exp2_hw(fminf(sGs[r] - sGs[ic], 0.f));
-          lv *= f;
-          bv *= f;
-        }
-        sL[r * L::LDL + ic] = (ic < r) ? lv * sBeta[r] : 0.f;
-        sB[r * L::LDT + ic] = (_Float16)((ic <= r) ? bv : 0.f);
+        float v = acc[i];
+        if constexpr (!PER_KEY) v *= exp2_hw(fminf(sGs[r] - sGs[ic], 0.f));
+        if (is_b) sB[r * L::LDT + ic] = (_Float16)((ic <= r) ? v : 0.f);
+        else sL[r * L::LDL + ic] = (ic < r) ? v * sBeta[r] : 0.f;
       }
     }
     __syncthreads();
@@ -458,10 +537,19 @@ __global__ __launch_bounds__(D * 4) void prefill_kernel(PrefillArgs a) {
       float x[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float s = (r == j) ? 1.f : 0.f;
+        float lrow[16];
 #pragma unroll
-        for (int i = 0; i < r; ++i) s -= Lb[r * L::LDL + i] * x[i];
-        x[r] = s;
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 t = *reinterpret_cast<const f32x4*>(Lb + r * L::LDL + 4 * q4);
+          lrow[4 * q4] = t[0]; lrow[4 * q4 + 1] = t[1]; lrow[4 * q4 + 2] = t[2]; lrow[4 * q4 + 3] = t[3];
+        }
+        float s0 = (r == j) ? 1.f : 0.f, s1 = 0.f;
+#pragma unroll
+        for (int i = 0; i < r; i += 2) {
+          s0 -= lrow[i] * x[i];
+          if (i + 1 < r) s1 -= lrow[i + 1] * x[i + 1];
+        }
+        x[r] = s0 + s1;
       }
       float* Ab = sL + (16 * b) * L::LDL + 16 * b;
 #pragma unroll
@@ -476,7 +564,7 @@ __global__ __launch_bounds__(D * 4) void prefill_kernel(PrefillArgs a) {
         float x[8];
         unpack_group<BF16>(regs.v[j], x);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sVT[(8 * k8 + e) * L::LDT + c] = (_Float16)x[e];
+        for (int e = 0; e < 8; ++e) sVT[(8 * k8 + e) * L::LDT + swz(8 * k8 + e, c)] = (_Float16)x[e];
       }
     }
     __syncthreads();
@@ -514,14 +602,17 @@ __global__ __launch_bounds__(D * 4) void prefill_kernel(PrefillArgs a) {
     for (int e8 = tid; e8 < C * C / 8; e8 += NT) {
       const int c = e8 / 8, i0 = 8 * (e8 % 8);
       const int Rb = c / 16, Ib = i0 / 16;
+      // A_RI (R > I) sits at block (I, R); diagonal blocks in place; zero above
+      const int src = (Rb > Ib) ? (16 * Ib + c % 16) * L::LDL + 16 * Rb + i0 % 16 : c * L::LDL + i0;
+      const float keep = (Rb >= Ib) ? 1.f : 0.f;
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(sL + src);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(sL + src + 4);
+      const f32x4 b0 = *reinterpret_cast<const f32x4*>(sBeta + i0);
+      const f32x4 b1 = *reinterpret_cast<const f32x4*>(sBeta + i0 + 4);
       f16x8 th, tl;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int i = i0 + e;
-        float av = 0.f;
-        if (Rb > Ib) av = sL[(16 * Ib + c % 16) * L::LDL + 16 * Rb + i % 16];
-        else if (Rb == Ib) av = sL[c * L::LDL + i];
-        const float tv = av * sBeta[i];
+        const float tv = keep * (e < 4 ? a0[e] * b0[e] : a1[e - 4] * b1[e - 4]);
         th[e] = (_Float16)tv;
         tl[e] = (_Float16)(tv - (float)th[e]);
       }
@@ -530,106 +621,162 @@ __global__ __launch_bounds__(D * 4) void prefill_kernel(PrefillArgs a) {
     }
     __syncthreads();
     {
-      // wave w computes W[:, 16w..16w+15] (4 row tiles, K = 64)
-      const int kt = wave;
-      f32x4 acc[4];
+      // wave w computes W[:, 16kt..16kt+15] for kt = w, w + NW, ... (K = 64)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4{0, 0, 0, 0};
+      for (int kj = 0; kj < KT / NW; ++kj) {
+        const int kt = wave + NW * kj;
+        f32x4 acc[4];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const f16x8 bk = ld_std(sKhT, L::LDT, 16 * kt, 32 * ks, lane);
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          acc[ct] = mfma_f16(ld_std(sTh, L::LDT, 16 * ct, 32 * ks, lane), bk, acc[ct]);
-          acc[ct] = mfma_f16(ld_std(sTl, L::LDT, 16 * ct, 32 * ks, lane), bk, acc[ct]);
-        }
-      }
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sW[(16 * ct + 4 * g + i) * L::LDQ + 16 * kt + l16] = (_Float16)acc[ct][i];
-    }
-    __syncthreads();
-
-    // prefetch the next chunk's raw inputs while the chain runs
-    if (ch + 1 < n_chunks)
-      load_chunk<D, BF16, PER_KEY>(regs, a, tok0 + C, min(C, item.n_tokens - (ch + 1) * C), h, tid,
-                                   need_v);
-
-    // ---- P6: state passing for this wavefront's slice -----------------------
-    {
-      // U' = T~ V_s : rows c (4 tiles), column v = 16 slice + l16 (zero in MAP_M)
-      f32x4 U[4];
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) U[ct] = f32x4{0, 0, 0, 0};
-      if (need_v) {
+        for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4{0, 0, 0, 0};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const f16x8 bv = ld_std(sVT, L::LDT, 16 * slice, 32 * ks, lane);
+          const f16x8 bk = ld_std_swz(sKhT, L::LDT, 16 * kt, 32 * ks, lane);
 #pragma unroll
           for (int ct = 0; ct < 4; ++ct) {
-            U[ct] = mfma_f16(ld_std(sTh, L::LDT, 16 * ct, 32 * ks, lane), bv, U[ct]);
-            U[ct] = mfma_f16(ld_std(sTl, L::LDT, 16 * ct, 32 * ks, lane), bv, U[ct]);
+            acc[ct] = mfma_f16(ld_std(sTh, L::LDT, 16 * ct, 32 * ks, lane), bk, acc[ct]);
+            acc[ct] = mfma_f16(ld_std(sTl, L::LDT, 16 * ct, 32 * ks, lane), bk, acc[ct]);
           }
         }
-      }
-      // S0^T as the permuted-K operand (fp16), shared by W S0^T and Q~ S0^T
-      f16x8 sop[D / 32];
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) sop[ks] = pack_perm(ST[2 * ks], ST[2 * ks + 1]);
-      // U -= W S0^T
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) {
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          f32x4 p = {0, 0, 0, 0};
-          p = mfma_f16(ld_perm(sW, L::LDQ, 16 * ct, 32 * ks, lane), sop[ks], p);
-          U[ct] -= p;
-        }
-      }
-      // U as hi + lo permuted-K operands (K = chunk position, 2 steps)
-      f16x8 uh[2], ul[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) split_perm(U[2 * ks], U[2 * ks + 1], uh[ks], ul[ks]);
-      if (out_mode) {
-        // O = Q~ S0^T + B U
-        f32x4 O[4];
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) O[ct] = f32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks)
-#pragma unroll
-          for (int ct = 0; ct < 4; ++ct)
-            O[ct] = mfma_f16(ld_perm(sQt, L::LDQ, 16 * ct, 32 * ks, lane), sop[ks], O[ct]);
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-          for (int ct = 0; ct < 4; ++ct) {
-            const f16x8 ba = ld_perm(sB, L::LDT, 16 * ct, 32 * ks, lane);
-            O[ct] = mfma_f16(ba, uh[ks], O[ct]);
-            O[ct] = mfma_f16(ba, ul[ks], O[ct]);
-          }
-        }
-        float* obase = a.o + tok0 * HD + (int64_t)h * D + 16 * slice + l16;
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int c = 16 * ct + 4 * g + i;
-            if (c < n) obase[(int64_t)c * HD] = O[ct][i];
-          }
+          for (int i = 0; i < 4; ++i)
+            sW[(16 * ct + 4 * g + i) * L::LDQ + 16 * kt + l16] = (_Float16)acc[ct][i];
       }
-      // S^T <- 2^(G_n) S^T + K~^T U
+    }
+    __syncthreads();
+
+    // prefetch the next chunk's raw inputs while the chain runs (bf16 q, k go
+    // to LDS: the K^T and L buffers are not read again in this chunk)
+    if (ch + 1 < n_chunks) {
+      const int n_next = min(C, item.n_tokens - (ch + 1) * C);
+      load_chunk<D, BF16, PER_KEY>(regs, a, tok0 + C, n_next, h, tid, need_v);
+      if constexpr (BF16) {
+        const int64_t row0 = ((tok0 + C) * a.H + h) * D;
+        stage_rows_lds<D>(static_cast<const uint16_t*>(a.k) + row0, HDu, n_next, smem + L::OFF_KHT,
+                          wave, lane);
+        stage_rows_lds<D>(static_cast<const uint16_t*>(a.q) + row0, HDu, n_next, smem + L::OFF_L,
+                          wave, lane);
+      }
+    }
+
+    // ---- P6: state passing for this wavefront's slices ---------------------
+    // Every A-operand tile read from LDS (T~, W, Q~, B, K~^T) feeds the MFMAs of
+    // all SPW slices of the wavefront, which divides the LDS read traffic by SPW.
+    // Operand tiles are read in batches ahead of their MFMAs (the scheduling
+    // barriers keep each batch of reads in flight together).
+    {
+      // U' = T~ V_s (zero in MAP_M): rows c (4 tiles), column v = 16 slice + l16
+      f32x4 U[SPW][4];
 #pragma unroll
-      for (int kt = 0; kt < KT; ++kt) {
-        const f32x4 gam = *reinterpret_cast<const f32x4*>(sGam + 16 * kt + 4 * g);
-        ST[kt] *= gam;
+      for (int sl = 0; sl < SPW; ++sl)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) U[sl][ct] = f32x4{0, 0, 0, 0};
+      if (need_v) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          const f16x8 ka = ld_perm(sKtT, L::LDT, 16 * kt, 32 * ks, lane);
-          ST[kt] = mfma_f16(ka, uh[ks], ST[kt]);
-          ST[kt] = mfma_f16(ka, ul[ks], ST[kt]);
+          f16x8 bv[SPW], th[4], tl[4];
+#pragma unroll
+          for (int sl = 0; sl < SPW; ++sl)
+            bv[sl] = ld_std_swz(sVT, L::LDT, 16 * (SPW * wave + sl), 32 * ks, lane);
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) {
+            th[ct] = ld_std(sTh, L::LDT, 16 * ct, 32 * ks, lane);
+            tl[ct] = ld_std(sTl, L::LDT, 16 * ct, 32 * ks, lane);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int sl = 0; sl < SPW; ++sl) {
+              U[sl][ct] = mfma_f16(th[ct], bv[sl], U[sl][ct]);
+              U[sl][ct] = mfma_f16(tl[ct], bv[sl], U[sl][ct]);
+            }
+        }
+      }
+      // S0^T as the permuted-K operand (fp16), shared by W S0^T and Q~ S0^T;
+      // U = U' - W S0^T accumulates W (-S0^T) into U directly.
+      f16x8 sop[SPW][D / 32];
+#pragma unroll
+      for (int sl = 0; sl < SPW; ++sl)
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) sop[sl][ks] = pack_perm(ST[sl][2 * ks], ST[sl][2 * ks + 1]);
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        f16x8 w[4], nsop[SPW];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) w[ct] = ld_perm(sW, L::LDQ, 16 * ct, 32 * ks, lane);
+#pragma unroll
+        for (int sl = 0; sl < SPW; ++sl) nsop[sl] = -sop[sl][ks];
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int sl = 0; sl < SPW; ++sl) U[sl][ct] = mfma_f16(w[ct], nsop[sl], U[sl][ct]);
+      }
+      // U as hi + lo permuted-K operands (K = chunk position, 2 steps)
+      f16x8 uh[SPW][2], ul[SPW][2];
+#pragma unroll
+      for (int sl = 0; sl < SPW; ++sl)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) split_perm(U[sl][2 * ks], U[sl][2 * ks + 1], uh[sl][ks], ul[sl][ks]);
+      if (out_mode) {
+        // O = Q~ S0^T + B U, one 16-row tile at a time
+        const uint32_t olane = (uint32_t)(4 * g) * (uint32_t)HD + 16 * SPW * wave + l16;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          f16x8 qa[D / 32], ba[2];
+#pragma unroll
+          for (int ks = 0; ks < D / 32; ++ks) qa[ks] = ld_perm(sQt, L::LDQ, 16 * ct, 32 * ks, lane);
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) ba[ks] = ld_perm(sB, L::LDT, 16 * ct, 32 * ks, lane);
+          __builtin_amdgcn_sched_barrier(0);
+          f32x4 O[SPW];
+#pragma unroll
+          for (int sl = 0; sl < SPW; ++sl) O[sl] = f32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+            for (int sl = 0; sl < SPW; ++sl) O[sl] = mfma_f16(qa[ks], sop[sl][ks], O[sl]);
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int sl = 0; sl < SPW; ++sl) {
+              O[sl] = mfma_f16(ba[ks], uh[sl][ks], O[sl]);
+              O[sl] = mfma_f16(ba[ks], ul[sl][ks], O[sl]);
+            }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int c = 16 * ct + 4 * g + i;
+            float* ob = a.o + (tok0 + 16 * ct + i) * HD + (int64_t)h * D;   // uniform
+            if (c < n) {
+#pragma unroll
+              for (int sl = 0; sl < SPW; ++sl) ob[olane + 16 * sl] = O[sl][i];
+            }
+          }
+        }
+      }
+      // S^T <- 2^(G_n) S^T + K~^T U, four row tiles per batch
+#pragma unroll
+      for (int kb = 0; kb < KT; kb += 4) {
+        f16x8 ka[4][2];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) ka[t][ks] = ld_perm_swz(sKtT, L::LDT, 16 * (kb + t), 32 * ks, lane);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const f32x4 gam = *reinterpret_cast<const f32x4*>(sGam + 16 * (kb + t) + 4 * g);
+#pragma unroll
+          for (int sl = 0; sl < SPW; ++sl) ST[sl][kb + t] *= gam;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int sl = 0; sl < SPW; ++sl) {
+              ST[sl][kb + t] = mfma_f16(ka[t][ks], uh[sl][ks], ST[sl][kb + t]);
+              ST[sl][kb + t] = mfma_f16(ka[t][ks], ul[sl][ks], ST[sl][kb + t]);
+            }
         }
       }
     }
@@ -641,10 +788,13 @@ __global__ __launch_bounds__(D * 4) void prefill_kernel(PrefillArgs a) {
         const int64_t slot = item.snap_base + pos / a.interval - 1;
         float* dst = a.snapshots + (slot * a.H + h) * DD;
 #pragma unroll
-        for (int kt = 0; kt < KT; ++kt)
-          *reinterpret_cast<f32x4*>(dst + (16 * slice + l16) * D + 16 * kt + 4 * g) = ST[kt];
+        for (int sl = 0; sl < SPW; ++sl)
+#pragma unroll
+          for (int kt = 0; kt < KT; ++kt)
+            *reinterpret_cast<f32x4*>(dst + (16 * (SPW * wave + sl) + l16) * D + 16 * kt + 4 * g) = ST[sl][kt];
       }
     }
+    if constexpr (BF16) __builtin_amdgcn_s_waitcnt(0);   // staged rows have landed in LDS
     __syncthreads();
   }
 
@@ -657,8 +807,10 @@ __global__ __launch_bounds__(D * 4) void prefill_kernel(PrefillArgs a) {
     dst = a.seg_maps + ((int64_t)item_idx * a.H + h) * 2 * DD + (mode == MODE_MAP_N ? DD : 0);
   }
 #pragma unroll
-  for (int kt = 0; kt < KT; ++kt)
-    *reinterpret_cast<f32x4*>(dst + (16 * slice + l16) * D + 16 * kt + 4 * g) = ST[kt];
+  for (int sl = 0; sl < SPW; ++sl)
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+      *reinterpret_cast<f32x4*>(dst + (16 * (SPW * wave + sl) + l16) * D + 16 * kt + 4 * g) = ST[sl][kt];
 }
 
 // Segment scan: for every sequence with more than two segments, head and block
@@ -797,7 +949,7 @@ hipError_t launch_pass(const PrefillArgs& a, int pass, hipStream_t s) {
   PrefillArgs p = a;
   p.pass = pass;
   const int per_item = pass == 1 ? 2 : 1;
-  hipLaunchKernelGGL(kern, dim3(a.n_items * a.H * per_item), dim3(D * 4), L::TOTAL, s, p);
+  hipLaunchKernelGGL(kern, dim3(a.n_items * a.H * per_item), dim3(NT), L::TOTAL, s, p);
   return hipGetLastError();
 }
 
