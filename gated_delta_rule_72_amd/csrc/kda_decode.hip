@@ -26,27 +26,50 @@
 namespace kda {
 namespace {
 
+// x from lane (lane ^ M), M < 32: quad permutes (DPP) for M = 1, 2, the
+// swizzle crossbar in xor mode for larger M; neither touches LDS memory.
+template <int M>
+__device__ __forceinline__ float xor_lane(float x) {
+  const int xi = __float_as_int(x);
+  int r;
+  if constexpr (M == 1)
+    r = __builtin_amdgcn_update_dpp(xi, xi, 0xB1, 0xF, 0xF, false);      // quad_perm [1,0,3,2]
+  else if constexpr (M == 2)
+    r = __builtin_amdgcn_update_dpp(xi, xi, 0x4E, 0xF, 0xF, false);      // quad_perm [2,3,0,1]
+  else
+    r = __builtin_amdgcn_ds_swizzle(xi, 0x1F | (M << 10));               // bit mode: lane ^ M
+  return __int_as_float(r);
+}
+
 // Lanes [base, base+N) of a group hold vals[0..N) each; afterwards lane
 // base+j returns the sum over the group of vals[j].
+template <int N, int M>
+__device__ __forceinline__ void reduce_scatter_step(float (&vals)[N], int lane_in_group) {
+  const bool upper = (lane_in_group & M) != 0;
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    const float send = upper ? vals[j] : vals[j + M];
+    const float keep = upper ? vals[j + M] : vals[j];
+    vals[j] = keep + xor_lane<M>(send);
+  }
+}
 template <int N>
 __device__ __forceinline__ float reduce_scatter(float (&vals)[N], int lane_in_group) {
-#pragma unroll
-  for (int m = N / 2; m >= 1; m >>= 1) {
-    const bool upper = (lane_in_group & m) != 0;
-#pragma unroll
-    for (int j = 0; j < m; ++j) {
-      const float send = upper ? vals[j] : vals[j + m];
-      const float keep = upper ? vals[j + m] : vals[j];
-      vals[j] = keep + __shfl_xor(send, m);
-    }
-  }
+  if constexpr (N >= 32) reduce_scatter_step<N, 16>(vals, lane_in_group);
+  if constexpr (N >= 16) reduce_scatter_step<N, 8>(vals, lane_in_group);
+  if constexpr (N >= 8) reduce_scatter_step<N, 4>(vals, lane_in_group);
+  if constexpr (N >= 4) reduce_scatter_step<N, 2>(vals, lane_in_group);
+  reduce_scatter_step<N, 1>(vals, lane_in_group);
   return vals[0];
 }
 
 template <int N>
 __device__ __forceinline__ float group_allreduce(float x) {
-#pragma unroll
-  for (int m = N / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  if constexpr (N >= 32) x += xor_lane<16>(x);
+  if constexpr (N >= 16) x += xor_lane<8>(x);
+  x += xor_lane<4>(x);
+  x += xor_lane<2>(x);
+  x += xor_lane<1>(x);
   return x;
 }
 
@@ -100,13 +123,19 @@ __global__ __launch_bounds__(D * 2) void decode_kernel(DecodeArgs a) {
   const int my_row = wave * 32 + my_r * G + g;
   float u = 0.f;
   if ((li & 1) == 0) u = beta * (load1<BF16>(a.v, vec_off + my_row) - red);
-  const float u_pair = __shfl_xor(u, 1);
+  const float u_pair = xor_lane<1>(u);
   if (li & 1) a.o[vec_off + my_row] = red + u_pair * kq;
 
-  const int group_base = lane - li;
+  // u of row r sits in lane 2r of each lane group: read it wave-wide and keep
+  // the copy of this lane's group
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const float ur = __shfl(u, group_base + 2 * r);
+    float ur = 0.f;
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) {
+      const float x = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u), gg * LPR + 2 * r));
+      if (g == gg) ur = x;
+    }
     const int row = wave * 32 + r * G + g;
     const f32x4 upd = s[r] + ur * kv;
     __builtin_nontemporal_store(upd, reinterpret_cast<f32x4*>(state + (int64_t)row * D + 4 * li));
