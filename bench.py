@@ -133,12 +133,15 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--cpu-tokens", type=int, default=4096,
+    ap.add_argument("--cpu-tokens", type=int, default=262144,
                     help="token prefix the CPU oracle baseline runs on (0 = skip)")
     ap.add_argument("--skip-decode", action="store_true")
     ap.add_argument("--prefill-only", action="store_true", help="profiling: only the prefill loop")
     ap.add_argument("--prefill-workload", default="long_prefill_T262144_H16_d128",
                     help="workload name for the prefill line (default: the headline long prefill)")
+    ap.add_argument("--decode-only", action="store_true", help="profiling: only the decode loop")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="profiling: copy a 256 MiB fp32 buffer 3 times (known bytes for HBM counters)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (every GPU box here "
@@ -151,6 +154,21 @@ def main(argv=None):
 
     kda.load()
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        src = torch.ones(64 * 1024 * 1024, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read_per_copy": src.numel() * 4,
+                          "bytes_written_per_copy": dst.numel() * 4, "copies": 3}))
+        return 0
+    if args.decode_only:
+        d = wl.DECODE
+        dms = time_decode(kda, torch, d, max(args.steps, 20), args.warmup)
+        davg = sum(dms) / len(dms)
+        print(json.dumps({"decode_us_per_step": davg * 1e3, "steps": len(dms)}))
+        return 0
     w = wl.ALL[args.prefill_workload]
     inp = wl.make_prefill_inputs(w, dev)
     torch.cuda.synchronize()
@@ -179,11 +197,13 @@ def main(argv=None):
                    "gate": w.gate, "chunk": w.chunk, "qkv": w.dtype, "snapshot_interval": w.interval},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": f"prefill_kernel<{w.dk},{w.dtype},{w.gate}> (all passes)",
+                     "kernel": "kda_prefill_chunked = build_items + prefill_kernel pass 1 + "
+                               "segment_scan + prefill_kernel pass 3 (automatic segment plan)",
                      "algorithmic_bytes_per_launch": int(pb), "algorithmic_flops_per_launch": int(pf),
                      "mfma_tflops": round(tfl, 2), "mfma_frac": round(tfl / MFMA_F16_PEAK_TFLOPS, 4),
                      "attainable_frac": round((pb / (HBM_PEAK_GBS * 1e9)) / (ms_avg * 1e-3), 4)},
-        "prefill_ms": {"avg": ms_avg, "min": min(ms), "max": max(ms)},
+        "prefill_ms": {"avg": ms_avg, "min": min(ms), "max": max(ms),
+                       "timing": "HIP events on the launch stream around each kda_prefill_chunked call"},
         "kernel_level": "hip-gfx950-chunked-v1",
     }
     del inp

@@ -39,12 +39,13 @@
 //       S0^T <- 2^(G_n) S0^T + (K*2^(G_n-G))^T U. U and T~ enter their
 //       products as fp16 hi + lo pairs; the state stays fp32. The next
 //       chunk's inputs are loaded into registers while P6 runs.
-// Run modes of a workgroup: OUT (the real chain: o, snapshots, final state),
-// MAP_N (the chain from S0 = 0: the item's N) and MAP_M (the chain with
-// v = 0 from the identity rows: the item's M). Long sequences with few heads
-// are split into segments: pass 1 computes each middle segment's (M, N) and
-// runs the first segment in OUT mode, a scan composes S_{s+1} = S_s M_s + N_s
-// in fp32, and pass 3 reruns segments 1.. in OUT mode from their true start.
+// Two instantiations: OUT (the real chain: o, snapshots, final state) and MAP
+// (a segment's affine map: each wavefront advances its N rows, the chain from
+// S0 = 0, and its M rows, the chain with v = 0 from identity rows, side by side;
+// q, Q~, B and o are skipped). Long sequences with few heads are split into
+// segments: pass 1 maps every segment but the last, a scan composes
+// S_{s+1} = S_s M_s + N_s in fp32 from the initial state, and pass 3 runs
+// every segment in OUT mode from its true start.
 // Accumulator layout of a 16x16 MFMA tile: lane l holds rows 4(l/16)+i,
 // column l%16. When an accumulator tile feeds the next product as its
 // K-operand, the K index is permuted (lane group g supplies rows 4g..4g+3 of
@@ -57,7 +58,6 @@ namespace {
 
 constexpr int C = 64;  // chunk length
 
-enum Mode { MODE_OUT = 0, MODE_MAP_N = 1, MODE_MAP_M = 2, MODE_IDLE = 3 };
 
 __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -279,13 +279,14 @@ __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
   return x;
 }
 
-template <int D, bool BF16, bool PER_KEY>
+template <int D, bool BF16, bool PER_KEY, bool MAP>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void prefill_kernel(PrefillArgs a) {
   using L = Lds<D>;
   using CR = ChunkRegs<D, BF16, PER_KEY>;
   constexpr int NW = NT / 64;    // wavefronts
   constexpr int SPW = D / 64;    // state slices per wavefront
+  constexpr int NSL = MAP ? 2 * SPW : SPW;   // MAP: SPW N slices, then SPW M slices
   constexpr int KT = D / 16;     // 16-row tiles along d_k
   extern __shared__ __align__(16) unsigned char smem[];
 
@@ -310,39 +311,30 @@ void prefill_kernel(PrefillArgs a) {
 
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int g = lane >> 4, l16 = lane & 15;
-  const int per_item = a.pass == 1 ? 2 : 1;
-  const int item_idx = blockIdx.x / (a.H * per_item);
-  const int rem = blockIdx.x % (a.H * per_item);
-  const int h = rem / per_item, which = rem % per_item;
+  const int item_idx = blockIdx.x / a.H, h = blockIdx.x % a.H;
   const PrefillItem item = a.items[item_idx];
-
-  int mode = MODE_OUT;
-  if (a.pass == 1) {
-    if (item.seg == 0) mode = which == 0 ? MODE_OUT : MODE_IDLE;
-    else if (item.seg < item.n_segs - 1) mode = which == 0 ? MODE_MAP_N : MODE_MAP_M;
-    else mode = MODE_IDLE;
-  } else if (a.pass == 3) {
-    mode = item.seg >= 1 ? MODE_OUT : MODE_IDLE;
+  if constexpr (MAP) {
+    if (item.seg >= item.n_segs - 1) return;   // the last segment needs no map (uniform)
   }
-  if (mode == MODE_IDLE) return;   // uniform over the workgroup
-  const bool out_mode = mode == MODE_OUT;
-  const bool need_v = mode != MODE_MAP_M;
+  constexpr bool out_mode = !MAP;
+  constexpr bool need_v = true;
   const int64_t HD = (int64_t)a.H * D;
   const int64_t DD = (int64_t)D * D;
 
   // ---- start state: S0^T in accumulator layout ------------------------------
-  // slice sl of this wavefront covers state rows 16 (SPW wave + sl) .. +15;
+  // slice sl of this wavefront covers state rows 16 (SPW wave + sl % SPW) .. +15
+  // (MAP: sl < SPW are N rows, sl >= SPW the same rows of M);
   // tile kt, lane l: S0^T[k = 16kt + 4g + i][v = 16 slice + l16] = S0[v][k]
-  f32x4 ST[SPW][KT];
+  f32x4 ST[NSL][KT];
   {
     const float* src = nullptr;
-    if (mode == MODE_OUT) {
+    if constexpr (!MAP) {
       if (item.seg > 0) src = a.seg_states + ((int64_t)item_idx * a.H + h) * DD;
       else if (a.init) src = a.init + ((int64_t)item.seq * a.H + h) * DD;
     }
 #pragma unroll
-    for (int sl = 0; sl < SPW; ++sl) {
-      const int row = 16 * (SPW * wave + sl) + l16;
+    for (int sl = 0; sl < NSL; ++sl) {
+      const int row = 16 * (SPW * wave + sl % SPW) + l16;
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt) {
         if (src) {
@@ -350,7 +342,7 @@ void prefill_kernel(PrefillArgs a) {
         } else {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            ST[sl][kt][i] = (mode == MODE_MAP_M && row == 16 * kt + 4 * g + i) ? 1.f : 0.f;
+            ST[sl][kt][i] = (MAP && sl >= SPW && row == 16 * kt + 4 * g + i) ? 1.f : 0.f;
         }
       }
     }
@@ -365,8 +357,9 @@ void prefill_kernel(PrefillArgs a) {
       const int64_t row0 = (item.tok_begin * a.H + h) * D;
       stage_rows_lds<D>(static_cast<const uint16_t*>(a.k) + row0, HDu, min(C, item.n_tokens),
                         smem + L::OFF_KHT, wave, lane);
-      stage_rows_lds<D>(static_cast<const uint16_t*>(a.q) + row0, HDu, min(C, item.n_tokens),
-                        smem + L::OFF_L, wave, lane);
+      if constexpr (!MAP)
+        stage_rows_lds<D>(static_cast<const uint16_t*>(a.q) + row0, HDu, min(C, item.n_tokens),
+                          smem + L::OFF_L, wave, lane);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
     }
@@ -385,7 +378,8 @@ void prefill_kernel(PrefillArgs a) {
       if constexpr (BF16) {
         // staged bf16 rows [64][D] (unpadded); rows >= n are stale and zeroed here
         const uint4 kw = *reinterpret_cast<const uint4*>(smem + L::OFF_KHT + (c * D + 8 * k8) * 2);
-        const uint4 qw = *reinterpret_cast<const uint4*>(smem + L::OFF_L + (c * D + 8 * k8) * 2);
+        const uint4 qw = MAP ? uint4{0, 0, 0, 0}
+                             : *reinterpret_cast<const uint4*>(smem + L::OFF_L + (c * D + 8 * k8) * 2);
         const uint32_t kk4[4] = {kw.x, kw.y, kw.z, kw.w}, qq4[4] = {qw.x, qw.y, qw.z, qw.w};
         const bool live = c < n;
 #pragma unroll
@@ -405,7 +399,7 @@ void prefill_kernel(PrefillArgs a) {
         for (int e = 0; e < 8; ++e) qh[e] = (_Float16)x[e];
       }
       *reinterpret_cast<f16x8*>(sRK + c * L::LDQ + 8 * k8) = kh;
-      *reinterpret_cast<f16x8*>(sRQ + c * L::LDQ + 8 * k8) = qh;
+      if constexpr (!MAP) *reinterpret_cast<f16x8*>(sRQ + c * L::LDQ + 8 * k8) = qh;
     }
     float gloc[PER_KEY ? CR::TPB : 1];
     if constexpr (PER_KEY) {
@@ -451,7 +445,7 @@ void prefill_kernel(PrefillArgs a) {
       const int gi = tid + j * NT;
       const int c = gi / (D / 8), k8 = gi % (D / 8);
       const f16x8 kx = *reinterpret_cast<const f16x8*>(sRK + c * L::LDQ + 8 * k8);
-      const f16x8 qx = *reinterpret_cast<const f16x8*>(sRQ + c * L::LDQ + 8 * k8);
+      const f16x8 qx = MAP ? f16x8{} : *reinterpret_cast<const f16x8*>(sRQ + c * L::LDQ + 8 * k8);
       f16x8 qt;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -464,13 +458,13 @@ void prefill_kernel(PrefillArgs a) {
         sKhT[kk * L::LDT + swz(kk, c)] = (_Float16)(kf * dec);
         sKtT[kk * L::LDT + swz(kk, c)] = (_Float16)(kf * rem);
       }
-      *reinterpret_cast<f16x8*>(sQt + c * L::LDQ + 8 * k8) = qt;
+      if constexpr (!MAP) *reinterpret_cast<f16x8*>(sQt + c * L::LDQ + 8 * k8) = qt;
     }
 
     // ---- P3: Gram tiles L (fp32) and B (fp16) ------------------------------
     // Upper blocks of B are zero; the 10 lower tiles (R >= I) go round-robin
     // to the wavefronts.
-    for (int e = tid; e < 6 * 256; e += NT) {
+    for (int e = tid; e < (MAP ? 0 : 6 * 256); e += NT) {
       const int t = e / 256, rr = (e % 256) / 16, cc = e % 16;
       const int R = t < 3 ? 0 : (t < 5 ? 1 : 2);
       const int I = t < 3 ? t + 1 : (t < 5 ? t - 1 : 3);
@@ -478,11 +472,12 @@ void prefill_kernel(PrefillArgs a) {
     }
     // scalar gate: jobs unrolled for overlap; per-key: one job at a time (the
     // decayed operands of a job already fill the registers)
+    constexpr int NJOBS = MAP ? 10 : 20;          // MAP needs no B tiles
 #pragma unroll
-    for (int jj = 0; jj < (PER_KEY ? 1 : 20 / NW); ++jj)
-    for (int job = wave + NW * jj; job < 20; job += (PER_KEY ? NW : 20)) {
-      const int t = job >> 1;
-      const bool is_b = job & 1;                  // even: L tile, odd: B tile
+    for (int jj = 0; jj < (PER_KEY ? 1 : (NJOBS + NW - 1) / NW); ++jj)
+    for (int job = wave + NW * jj; job < NJOBS; job += (PER_KEY ? NW : NJOBS)) {
+      const int t = MAP ? job : job >> 1;
+      const bool is_b = MAP ? false : (job & 1);  // OUT: even L tile, odd B tile
       const int R = t < 1 ? 0 : (t < 3 ? 1 : (t < 6 ? 2 : 3));
       const int I = t - R * (R + 1) / 2;
       const _Float16* sA = is_b ? sRQ : sRK;
@@ -655,8 +650,9 @@ void prefill_kernel(PrefillArgs a) {
         const int64_t row0 = ((tok0 + C) * a.H + h) * D;
         stage_rows_lds<D>(static_cast<const uint16_t*>(a.k) + row0, HDu, n_next, smem + L::OFF_KHT,
                           wave, lane);
-        stage_rows_lds<D>(static_cast<const uint16_t*>(a.q) + row0, HDu, n_next, smem + L::OFF_L,
-                          wave, lane);
+        if constexpr (!MAP)
+          stage_rows_lds<D>(static_cast<const uint16_t*>(a.q) + row0, HDu, n_next, smem + L::OFF_L,
+                            wave, lane);
       }
     }
 
@@ -666,10 +662,11 @@ void prefill_kernel(PrefillArgs a) {
     // Operand tiles are read in batches ahead of their MFMAs (the scheduling
     // barriers keep each batch of reads in flight together).
     {
-      // U' = T~ V_s (zero in MAP_M): rows c (4 tiles), column v = 16 slice + l16
-      f32x4 U[SPW][4];
+      // U' = T~ V_s (the first SPW slices; zero for M slices): rows c (4 tiles),
+      // column v = 16 slice + l16
+      f32x4 U[NSL][4];
 #pragma unroll
-      for (int sl = 0; sl < SPW; ++sl)
+      for (int sl = 0; sl < NSL; ++sl)
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) U[sl][ct] = f32x4{0, 0, 0, 0};
       if (need_v) {
@@ -696,31 +693,31 @@ void prefill_kernel(PrefillArgs a) {
       }
       // S0^T as the permuted-K operand (fp16), shared by W S0^T and Q~ S0^T;
       // U = U' - W S0^T accumulates W (-S0^T) into U directly.
-      f16x8 sop[SPW][D / 32];
+      f16x8 sop[NSL][D / 32];
 #pragma unroll
-      for (int sl = 0; sl < SPW; ++sl)
+      for (int sl = 0; sl < NSL; ++sl)
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) sop[sl][ks] = pack_perm(ST[sl][2 * ks], ST[sl][2 * ks + 1]);
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) {
-        f16x8 w[4], nsop[SPW];
+        f16x8 w[4], nsop[NSL];
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) w[ct] = ld_perm(sW, L::LDQ, 16 * ct, 32 * ks, lane);
 #pragma unroll
-        for (int sl = 0; sl < SPW; ++sl) nsop[sl] = -sop[sl][ks];
+        for (int sl = 0; sl < NSL; ++sl) nsop[sl] = -sop[sl][ks];
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-          for (int sl = 0; sl < SPW; ++sl) U[sl][ct] = mfma_f16(w[ct], nsop[sl], U[sl][ct]);
+          for (int sl = 0; sl < NSL; ++sl) U[sl][ct] = mfma_f16(w[ct], nsop[sl], U[sl][ct]);
       }
       // U as hi + lo permuted-K operands (K = chunk position, 2 steps)
-      f16x8 uh[SPW][2], ul[SPW][2];
+      f16x8 uh[NSL][2], ul[NSL][2];
 #pragma unroll
-      for (int sl = 0; sl < SPW; ++sl)
+      for (int sl = 0; sl < NSL; ++sl)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) split_perm(U[sl][2 * ks], U[sl][2 * ks + 1], uh[sl][ks], ul[sl][ks]);
-      if (out_mode) {
+      if constexpr (out_mode) {
         // O = Q~ S0^T + B U, one 16-row tile at a time
         const uint32_t olane = (uint32_t)(4 * g) * (uint32_t)HD + 16 * SPW * wave + l16;
 #pragma unroll
@@ -769,11 +766,11 @@ void prefill_kernel(PrefillArgs a) {
         for (int t = 0; t < 4; ++t) {
           const f32x4 gam = *reinterpret_cast<const f32x4*>(sGam + 16 * (kb + t) + 4 * g);
 #pragma unroll
-          for (int sl = 0; sl < SPW; ++sl) ST[sl][kb + t] *= gam;
+          for (int sl = 0; sl < NSL; ++sl) ST[sl][kb + t] *= gam;
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int sl = 0; sl < SPW; ++sl) {
+            for (int sl = 0; sl < NSL; ++sl) {
               ST[sl][kb + t] = mfma_f16(ka[t][ks], uh[sl][ks], ST[sl][kb + t]);
               ST[sl][kb + t] = mfma_f16(ka[t][ks], ul[sl][ks], ST[sl][kb + t]);
             }
@@ -782,7 +779,7 @@ void prefill_kernel(PrefillArgs a) {
     }
 
     // snapshot after this chunk if the sequence position is a multiple of the interval
-    if (out_mode && a.interval > 0) {
+    if (out_mode && a.interval > 0) {   // OUT only (constant false in MAP)
       const int64_t pos = item.tok_in_seq + (int64_t)ch * C + n;   // tokens of the sequence done
       if (pos % a.interval == 0) {
         const int64_t slot = item.snap_base + pos / a.interval - 1;
@@ -798,24 +795,34 @@ void prefill_kernel(PrefillArgs a) {
     __syncthreads();
   }
 
-  // end of the item: final state, start state of the next segment, or (M, N)
-  float* dst;
-  if (mode == MODE_OUT) {
-    dst = (item.seg == item.n_segs - 1) ? a.final_state + ((int64_t)item.seq * a.H + h) * DD
-                                        : a.seg_states + ((int64_t)(item_idx + 1) * a.H + h) * DD;
+  // end of the item: the final state (OUT, last segment of the sequence) or the
+  // segment's map (MAP: N rows from the first SPW slices, M rows from the rest)
+  if constexpr (!MAP) {
+    if (item.seg == item.n_segs - 1) {
+      float* dst = a.final_state + ((int64_t)item.seq * a.H + h) * DD;
+#pragma unroll
+      for (int sl = 0; sl < NSL; ++sl)
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+          *reinterpret_cast<f32x4*>(dst + (16 * (SPW * wave + sl) + l16) * D + 16 * kt + 4 * g) = ST[sl][kt];
+    }
   } else {
-    dst = a.seg_maps + ((int64_t)item_idx * a.H + h) * 2 * DD + (mode == MODE_MAP_N ? DD : 0);
+    float* maps = a.seg_maps + ((int64_t)item_idx * a.H + h) * 2 * DD;   // [M, N]
+#pragma unroll
+    for (int sl = 0; sl < NSL; ++sl) {
+      float* dst = maps + (sl < SPW ? DD : 0);
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+        *reinterpret_cast<f32x4*>(dst + (16 * (SPW * wave + sl % SPW) + l16) * D + 16 * kt + 4 * g) =
+            ST[sl][kt];
+    }
   }
-#pragma unroll
-  for (int sl = 0; sl < SPW; ++sl)
-#pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-      *reinterpret_cast<f32x4*>(dst + (16 * (SPW * wave + sl) + l16) * D + 16 * kt + 4 * g) = ST[sl][kt];
 }
 
-// Segment scan: for every sequence with more than two segments, head and block
-// of 16 state rows, S_{s+1} = S_s M_s + N_s for s = 1 .. n_segs-2 in fp32 (S_1
-// comes from the first segment's OUT run). Rows of S evolve independently.
+// Segment scan: for every segmented sequence, head and block of 16 state rows,
+// S_{s+1} = S_s M_s + N_s for s = 0 .. n_segs-2 in fp32, from S_0 = the initial
+// state (or zeros); S_{s+1} is the start state of segment s+1. Rows of S
+// evolve independently.
 template <int D>
 __global__ __launch_bounds__(256) void segment_scan_kernel(PrefillArgs a) {
   constexpr int RB = 16;                        // rows per workgroup
@@ -828,15 +835,15 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(PrefillArgs a) {
   const int h = rem / nrb, rb = rem % nrb;
   const int first = a.seq_first_item[n];
   const int ns = a.items[first].n_segs;
-  if (ns <= 2) return;
+  if (ns <= 1) return;
   const int64_t DD = (int64_t)D * D;
   const int tid = threadIdx.x;
   const int r = tid / 16, c0 = tid % 16;        // output row r, columns c0 + 16 j
   {
-    const float* S1 = a.seg_states + ((int64_t)(first + 1) * a.H + h) * DD + (int64_t)rb * RB * D;
-    for (int e = tid; e < RB * D; e += 256) sS[e] = S1[e];
+    const float* S0 = a.init ? a.init + ((int64_t)n * a.H + h) * DD + (int64_t)rb * RB * D : nullptr;
+    for (int e = tid; e < RB * D; e += 256) sS[e] = S0 ? S0[e] : 0.f;
   }
-  for (int s = 1; s <= ns - 2; ++s) {
+  for (int s = 0; s <= ns - 2; ++s) {
     const float* M = a.seg_maps + ((int64_t)(first + s) * a.H + h) * 2 * DD;
     const float* Nm = M + DD + (int64_t)rb * RB * D;
     __syncthreads();
@@ -938,25 +945,22 @@ __global__ __launch_bounds__(256) void build_items_kernel(PrefillArgs a) {
   }
 }
 
-template <int D, bool BF16, bool PK>
-hipError_t launch_pass(const PrefillArgs& a, int pass, hipStream_t s) {
+template <int D, bool BF16, bool PK, bool MAP>
+hipError_t launch_pass(const PrefillArgs& a, hipStream_t s) {
   using L = Lds<D>;
   static_assert(L::TOTAL <= 160 * 1024, "LDS budget");
-  auto kern = prefill_kernel<D, BF16, PK>;
+  auto kern = prefill_kernel<D, BF16, PK, MAP>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL);
   if (e != hipSuccess) return e;
-  PrefillArgs p = a;
-  p.pass = pass;
-  const int per_item = pass == 1 ? 2 : 1;
-  hipLaunchKernelGGL(kern, dim3(a.n_items * a.H * per_item), dim3(NT), L::TOTAL, s, p);
+  hipLaunchKernelGGL(kern, dim3(a.n_items * a.H), dim3(NT), L::TOTAL, s, a);
   return hipGetLastError();
 }
 
 template <int D, bool BF16, bool PK>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
-  if (a.seg_chunks == 0) return launch_pass<D, BF16, PK>(a, 0, s);
-  hipError_t e = launch_pass<D, BF16, PK>(a, 1, s);
+  if (a.seg_chunks == 0) return launch_pass<D, BF16, PK, false>(a, s);
+  hipError_t e = launch_pass<D, BF16, PK, true>(a, s);          // pass 1: segment maps
   if (e != hipSuccess) return e;
   constexpr int scan_lds = (D * D + 16 * D) * 4;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(segment_scan_kernel<D>),
@@ -965,7 +969,7 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(segment_scan_kernel<D>, dim3(a.num_seqs * a.H * (D / 16)), dim3(256), scan_lds, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_pass<D, BF16, PK>(a, 3, s);
+  return launch_pass<D, BF16, PK, false>(a, s);                 // pass 3: every segment
 }
 
 }  // namespace
