@@ -462,63 +462,107 @@ void prefill_kernel(PrefillArgs a) {
     }
 
     // ---- P3: Gram tiles L (fp32) and B (fp16) ------------------------------
-    // Upper blocks of B are zero; the 10 lower tiles (R >= I) go round-robin
-    // to the wavefronts.
+    // Upper blocks of B are zero. The 10 lower tile pairs (R >= I) are split
+    // 2/3/3/2 over the wavefronts so that a wavefront keeps one row block R:
+    //   wave 0: R=3, I=0,1   wave 1: R=2, I=0..2   wave 2: R=1, I=0,1 and R=0   wave 3: R=3, I=2,3
+    // Each pair computes the transposed tiles L^T and B^T (column block I as the
+    // A operand, row block R as the B operand), so a lane ends with four
+    // consecutive columns i of one row r and stores them as one vector.
     for (int e = tid; e < (MAP ? 0 : 6 * 256); e += NT) {
       const int t = e / 256, rr = (e % 256) / 16, cc = e % 16;
       const int R = t < 3 ? 0 : (t < 5 ? 1 : 2);
       const int I = t < 3 ? t + 1 : (t < 5 ? t - 1 : 3);
       sB[(16 * R + rr) * L::LDT + 16 * I + cc] = (_Float16)0.f;
     }
-    // scalar gate: jobs unrolled for overlap; per-key: one job at a time (the
-    // decayed operands of a job already fill the registers)
-    constexpr int NJOBS = MAP ? 10 : 20;          // MAP needs no B tiles
+    {
+      // (R, I-range) runs of this wavefront
+      const int nrun = wave == 2 ? 2 : 1;
 #pragma unroll
-    for (int jj = 0; jj < (PER_KEY ? 1 : (NJOBS + NW - 1) / NW); ++jj)
-    for (int job = wave + NW * jj; job < NJOBS; job += (PER_KEY ? NW : NJOBS)) {
-      const int t = MAP ? job : job >> 1;
-      const bool is_b = MAP ? false : (job & 1);  // OUT: even L tile, odd B tile
-      const int R = t < 1 ? 0 : (t < 3 ? 1 : (t < 6 ? 2 : 3));
-      const int I = t - R * (R + 1) / 2;
-      const _Float16* sA = is_b ? sRQ : sRK;
-      f32x4 acc = {0, 0, 0, 0};
-      if constexpr (!PER_KEY) {
+      for (int run = 0; run < 2; ++run) {
+        if (run >= nrun) break;
+        const int R = wave == 0 ? 3 : wave == 1 ? 2 : wave == 3 ? 3 : (run == 0 ? 1 : 0);
+        const int I0 = wave == 3 ? 2 : 0;
+        const int I1 = wave == 0 ? 1 : wave == 1 ? 2 : wave == 3 ? 3 : (run == 0 ? 1 : 0);
+        const int r = 16 * R + l16;                  // this lane's row of L / B
+        if constexpr (!PER_KEY) {
+          // exact fp16 products of the staged inputs; decay applied per element
+          f16x8 kr[D / 32], qr[D / 32];
 #pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks)
-          acc = mfma_f16(ld_std(sA, L::LDQ, 16 * R, 32 * ks, lane), ld_std(sRK, L::LDQ, 16 * I, 32 * ks, lane),
-                         acc);
-      } else {
-        // operands decayed relative to token 16R: A-side 2^(G_r - G_16R) <= 1,
-        // B-side 2^(G_16R - G_i) (<= 1 for i <= 16R, bounded inside block R).
-        const int r = 16 * R + l16, i = 16 * I + l16;
-#pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) {
-          const int k0 = 32 * ks + 8 * g;
-          const f16x8 ar = *reinterpret_cast<const f16x8*>(sA + r * L::LDQ + k0);
-          const f16x8 br = *reinterpret_cast<const f16x8*>(sRK + i * L::LDQ + k0);
-          bf16x8 ah, al, bh, bl;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int kk = k0 + e;
-            const float gref = sG[(16 * R) * L::LDG + kk];
-            const float av = (float)ar[e] * exp2_hw(sG[r * L::LDG + kk] - gref);
-            const float bv = (float)br[e] * exp2_hw(gref - sG[i * L::LDG + kk]);
-            ah[e] = (__bf16)av; al[e] = (__bf16)(av - (float)ah[e]);
-            bh[e] = (__bf16)bv; bl[e] = (__bf16)(bv - (float)bh[e]);
+          for (int ks = 0; ks < D / 32; ++ks) {
+            kr[ks] = ld_std(sRK, L::LDQ, 16 * R, 32 * ks, lane);
+            if constexpr (!MAP) qr[ks] = ld_std(sRQ, L::LDQ, 16 * R, 32 * ks, lane);
           }
-          acc = mfma_bf16(ah, bh, acc);
-          acc = mfma_bf16(ah, bl, acc);
-          acc = mfma_bf16(al, bh, acc);
-        }
-      }
-      // epilogue: lane holds rows r = 16R + 4g + i, column ic = 16I + l16
+          const float gr = sGs[r], br = sBeta[r];
+          for (int I = I0; I <= I1; ++I) {
+            f32x4 accL = {0, 0, 0, 0}, accB = {0, 0, 0, 0};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * R + 4 * g + i, ic = 16 * I + l16;
-        float v = acc[i];
-        if constexpr (!PER_KEY) v *= exp2_hw(fminf(sGs[r] - sGs[ic], 0.f));
-        if (is_b) sB[r * L::LDT + ic] = (_Float16)((ic <= r) ? v : 0.f);
-        else sL[r * L::LDL + ic] = (ic < r) ? v * sBeta[r] : 0.f;
+            for (int ks = 0; ks < D / 32; ++ks) {
+              const f16x8 ki = ld_std(sRK, L::LDQ, 16 * I, 32 * ks, lane);
+              accL = mfma_f16(ki, kr[ks], accL);
+              if constexpr (!MAP) accB = mfma_f16(ki, qr[ks], accB);
+            }
+            const int i0 = 16 * I + 4 * g;           // columns i0..i0+3 of row r
+            const f32x4 gi = *reinterpret_cast<const f32x4*>(sGs + i0);
+            f32x4 lv;
+            f16x4 bv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float f = exp2_hw(fminf(gr - gi[e], 0.f));
+              lv[e] = (i0 + e < r) ? accL[e] * f * br : 0.f;
+              bv[e] = (_Float16)((i0 + e <= r) ? accB[e] * f : 0.f);
+            }
+            *reinterpret_cast<f32x4*>(sL + r * L::LDL + i0) = lv;
+            if constexpr (!MAP) *reinterpret_cast<f16x4*>(sB + r * L::LDT + i0) = bv;
+          }
+        } else {
+          // three-term bf16 products of operands decayed relative to token 16R:
+          // row side 2^(G_r - G_16R) <= 1, column side 2^(G_16R - G_i) (<= 1
+          // for i <= 16R, bounded inside block R). L and B share the column
+          // operand and the row-side factors.
+          const float br = sBeta[r];
+          for (int I = I0; I <= I1; ++I) {
+            const int i = 16 * I + l16;              // this lane's row of the column block
+            f32x4 accL = {0, 0, 0, 0}, accB = {0, 0, 0, 0};
+#pragma unroll
+            for (int ks = 0; ks < D / 32; ++ks) {
+              const int k0 = 32 * ks + 8 * g;
+              const f16x8 kraw = *reinterpret_cast<const f16x8*>(sRK + r * L::LDQ + k0);
+              const f16x8 iraw = *reinterpret_cast<const f16x8*>(sRK + i * L::LDQ + k0);
+              f16x8 qraw = {};
+              if constexpr (!MAP) qraw = *reinterpret_cast<const f16x8*>(sRQ + r * L::LDQ + k0);
+              bf16x8 kh, kl, qh, ql, ih, il;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const int kk = k0 + e;
+                const float gref = sG[(16 * R) * L::LDG + kk];
+                const float f = exp2_hw(sG[r * L::LDG + kk] - gref);
+                const float kv = (float)kraw[e] * f, qv = (float)qraw[e] * f;
+                const float iv = (float)iraw[e] * exp2_hw(gref - sG[i * L::LDG + kk]);
+                kh[e] = (__bf16)kv; kl[e] = (__bf16)(kv - (float)kh[e]);
+                qh[e] = (__bf16)qv; ql[e] = (__bf16)(qv - (float)qh[e]);
+                ih[e] = (__bf16)iv; il[e] = (__bf16)(iv - (float)ih[e]);
+              }
+              accL = mfma_bf16(ih, kh, accL);
+              accL = mfma_bf16(ih, kl, accL);
+              accL = mfma_bf16(il, kh, accL);
+              if constexpr (!MAP) {
+                accB = mfma_bf16(ih, qh, accB);
+                accB = mfma_bf16(ih, ql, accB);
+                accB = mfma_bf16(il, qh, accB);
+              }
+            }
+            const int i0 = 16 * I + 4 * g;
+            f32x4 lv;
+            f16x4 bv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              lv[e] = (i0 + e < r) ? accL[e] * br : 0.f;
+              bv[e] = (_Float16)((i0 + e <= r) ? accB[e] : 0.f);
+            }
+            *reinterpret_cast<f32x4*>(sL + r * L::LDL + i0) = lv;
+            if constexpr (!MAP) *reinterpret_cast<f16x4*>(sB + r * L::LDT + i0) = bv;
+          }
+        }
       }
     }
     __syncthreads();
