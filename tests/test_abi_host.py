@@ -1,0 +1,184 @@
+"""Host-side checks of the two C libraries (no GPU needed, no kernel launched).
+
+- libkda.so exports every function include/kda.h declares, and the Python
+  binding offers each under the same name;
+- liboracle_kda.so exports every function include/kda_oracle.h declares;
+- argument validation of the C ABI: every rejected call returns its status
+  before anything touches a device (fake, never-dereferenced pointers are used
+  where only alignment or presence is checked);
+- the product package fails loudly when libkda.so is missing and never imports
+  the oracle.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared(header: str):
+    text = open(os.path.join(ROOT, "include", header)).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(kda_[a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def K():
+    from gated_delta_rule_72_amd import build as B
+    if not os.path.exists(B.LIB):
+        B.build()
+    import gated_delta_rule_72_amd.kda as K
+    K.load()
+    return K
+
+
+def test_kda_header_symbols_exported(K):
+    names = _declared("kda.h")
+    assert set(names) == {"kda_abi_version", "kda_last_error", "kda_snapshot_count",
+                          "kda_prefill_workspace_size", "kda_prefill_chunked", "kda_decode_step"}
+    lib = ctypes.CDLL(K.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+        assert callable(getattr(K, n)), n
+    assert set(K.EXPORTED) == set(names)
+    assert K.kda_abi_version() == 1
+
+
+def test_oracle_header_symbols_exported():
+    import oracle
+    names = _declared("kda_oracle.h")
+    assert set(names) == {"kda_oracle_snapshot_count", "kda_oracle_run", "kda_recurrent_ref_check"}
+    lib = oracle.load()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_snapshot_count(K):
+    cu = torch.tensor([0, 100, 100, 300, 556], dtype=torch.int64)
+    assert K.kda_snapshot_count(cu, 0) == 0
+    assert K.kda_snapshot_count(cu, 64) == 1 + 0 + 3 + 4
+    assert K.kda_snapshot_count(cu, 128) == 0 + 0 + 1 + 2
+    with pytest.raises(K.KdaError) as e:
+        K.kda_snapshot_count(torch.tensor([1, 5], dtype=torch.int64), 64)
+    assert e.value.code == K.KDA_ERR_SHAPE
+    with pytest.raises(K.KdaError) as e:
+        K.kda_snapshot_count(torch.tensor([0, 5, 3], dtype=torch.int64), 64)
+    assert e.value.code == K.KDA_ERR_SHAPE and "decreases" in K.kda_last_error()
+
+
+def test_workspace_size_plans(K):
+    sh = K.make_shape(2, 64, 64, torch.bfloat16, True)
+    cu = torch.tensor([0, 100, 300], dtype=torch.int64)
+    plain = K.kda_prefill_workspace_size(sh, cu, 64, 64, 0)
+    seg = K.kda_prefill_workspace_size(sh, cu, 64, 64, 128)
+    assert 0 < plain <= 1024
+    # 128-token segments: 1 + 2 items, each with (M, N) maps and a start state
+    items, H, DD = 3, 2, 64 * 64
+    assert seg >= plain + items * H * 3 * DD * 4
+    # a segment as long as the longest sequence splits nothing
+    assert K.kda_prefill_workspace_size(sh, cu, 64, 64, 256) == plain
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("d_k", 96, "KDA_ERR_SHAPE"), ("d_v", 64, "KDA_ERR_SHAPE"), ("num_heads", 0, "KDA_ERR_SHAPE"),
+    ("qkv_dtype", 7, "KDA_ERR_ARG"), ("gate", 2, "KDA_ERR_ARG")])
+def test_bad_shapes_rejected(K, field, value, code):
+    sh = K.make_shape(2, 128, 128, torch.bfloat16, False)
+    setattr(sh, field, value)
+    with pytest.raises(K.KdaError) as e:
+        K.kda_prefill_workspace_size(sh, torch.tensor([0, 64], dtype=torch.int64), 64, 0, 0)
+    assert e.value.code == getattr(K, code)
+
+
+@pytest.mark.parametrize("chunk,interval,seg", [(32, 0, 0), (64, 100, 0), (64, -64, 0), (64, 0, 100),
+                                                (64, 0, -2)])
+def test_bad_plan_arguments_rejected(K, chunk, interval, seg):
+    sh = K.make_shape(1, 64, 64, torch.float32, False)
+    with pytest.raises(K.KdaError) as e:
+        K.kda_prefill_workspace_size(sh, torch.tensor([0, 64], dtype=torch.int64), chunk, interval, seg)
+    assert e.value.code == K.KDA_ERR_SHAPE
+
+
+def _fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def _prefill_raw(K, sh, cu, ptrs, ws_bytes, interval=0, seg=0):
+    cu = cu.contiguous()
+    lib = K.load()
+    p = dict(cu_dev=0x10000, q=0x20000, k=0x30000, v=0x40000, alpha=0x50000, beta=0x60000, init=None,
+             o=0x70000, fin=0x80000, snaps=None, ws=0x90000)
+    p.update(ptrs)
+    f = lambda n: None if p[n] is None else _fake(p[n])  # noqa: E731
+    return lib.kda_prefill_chunked(ctypes.byref(sh), cu.numel() - 1, ctypes.c_void_p(cu.data_ptr()),
+                                   f("cu_dev"), 64, interval, seg, f("q"), f("k"), f("v"), f("alpha"),
+                                   f("beta"), f("init"), f("o"), f("fin"), f("snaps"), f("ws"),
+                                   ws_bytes, None)
+
+
+def test_prefill_host_rejections(K):
+    """Each call below fails a host check, so no pointer is ever dereferenced."""
+    sh = K.make_shape(2, 64, 64, torch.bfloat16, True)
+    cu = torch.tensor([0, 100, 300], dtype=torch.int64)
+    need = K.kda_prefill_workspace_size(sh, cu, 64, 0, 0)
+    assert _prefill_raw(K, sh, cu, {"q": 0x20008}, need) == K.KDA_ERR_ALIGN
+    assert "q" in K.kda_last_error()
+    assert _prefill_raw(K, sh, cu, {"alpha": 0x50004}, need) == K.KDA_ERR_ALIGN   # per-key: 16 B
+    assert _prefill_raw(K, sh, cu, {"fin": 0x80004}, need) == K.KDA_ERR_ALIGN
+    assert _prefill_raw(K, sh, cu, {"q": None}, need) == K.KDA_ERR_ARG
+    assert _prefill_raw(K, sh, cu, {"fin": None}, need) == K.KDA_ERR_ARG
+    assert _prefill_raw(K, sh, cu, {"cu_dev": None}, need) == K.KDA_ERR_ARG
+    assert _prefill_raw(K, sh, cu, {}, need - 1) == K.KDA_ERR_WORKSPACE
+    assert _prefill_raw(K, sh, cu, {"ws": None}, need) == K.KDA_ERR_WORKSPACE
+    # snapshots due (interval 64 -> 1 + 3 slots) but no buffer
+    assert _prefill_raw(K, sh, cu, {}, need, interval=64) == K.KDA_ERR_ARG
+    assert "snapshot" in K.kda_last_error()
+    # scalar gate needs only 4-byte alpha
+    sh_s = K.make_shape(2, 64, 64, torch.bfloat16, False)
+    assert _prefill_raw(K, sh_s, cu, {"alpha": 0x50004, "q": 0x20008}, need) == K.KDA_ERR_ALIGN
+    assert "q" in K.kda_last_error()
+    # nothing to do: no sequences
+    assert _prefill_raw(K, sh, torch.tensor([0], dtype=torch.int64), {}, 0) == K.KDA_OK
+
+
+def test_decode_host_rejections(K):
+    lib = K.load()
+    f = _fake
+
+    def call(sh, batch, **kw):
+        p = dict(q=0x1000, k=0x2000, v=0x3000, alpha=0x4000, beta=0x5000, state=0x6000, o=0x7000)
+        p.update(kw)
+        a = [None if p[n] is None else f(p[n]) for n in ("q", "k", "v", "alpha", "beta", "state", "o")]
+        return lib.kda_decode_step(ctypes.byref(sh), batch, *a, None)
+
+    bf = K.make_shape(4, 128, 128, torch.bfloat16, True)
+    fp = K.make_shape(4, 128, 128, torch.float32, False)
+    assert call(bf, 0) == K.KDA_OK                      # empty batch: nothing enqueued
+    assert call(bf, -1) == K.KDA_ERR_ARG
+    assert call(bf, 2, state=None) == K.KDA_ERR_ARG
+    assert call(bf, 2, q=0x1004) == K.KDA_ERR_ALIGN     # bf16 q: 8 B
+    assert call(fp, 2, q=0x1008) == K.KDA_ERR_ALIGN     # fp32 q: 16 B
+    assert call(bf, 2, state=0x6008) == K.KDA_ERR_ALIGN
+    assert call(bf, 2, alpha=0x4004) == K.KDA_ERR_ALIGN  # per-key alpha: 16 B
+    bad = K.make_shape(4, 64, 128, torch.bfloat16, True)
+    assert call(bad, 2) == K.KDA_ERR_SHAPE
+
+
+def test_binding_fails_loudly_without_library(K, monkeypatch, tmp_path):
+    monkeypatch.setattr(K, "_lib", None)
+    monkeypatch.setattr(K, "LIB_PATH", str(tmp_path / "missing" / "libkda.so"))
+    with pytest.raises(ImportError):
+        K.load()
+
+
+def test_product_package_never_uses_the_oracle():
+    pkg = os.path.join(ROOT, "gated_delta_rule_72_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                src = open(os.path.join(dirpath, fn)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", src, flags=re.M), fn
+                assert "kda_oracle" not in src and "liboracle" not in src, fn
