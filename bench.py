@@ -54,6 +54,36 @@ def decode_algorithmic(B, H, dk, dv, per_key, qkv_bytes=2):
     return b, f
 
 
+def kernel_sources_digest() -> str:
+    """sha256 over the kernel sources and headers: HBM counter figures stored
+    under profiles/ are only reported while the kernels they were taken on are
+    unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gated_delta_rule_72_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        if fn.endswith((".hip", ".h")):
+            h.update(fn.encode())
+            h.update(open(os.path.join(csrc, fn), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(name: str):
+    """HBM bytes per launch from the counter summary profiles/<name>_traffic.md
+    (FETCH_SIZE and WRITE_SIZE passes, each scaled by the plain-copy
+    calibration), or None if it is missing or was taken on other kernel sources."""
+    import re
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"^sources_sha256_16:\s*([0-9a-f]{16})\s*$", text, flags=re.M)
+    b = re.search(r"^traffic_bytes_per_launch:\s*([0-9]+)\s*$", text, flags=re.M)
+    if not m or not b or m.group(1) != kernel_sources_digest():
+        return None
+    return int(b.group(1))
+
+
 def time_prefill(kda, torch, inp, w, steps, warmup):
     T, H, dk, dv = w.T, w.H, w.dk, w.dv
     dev = inp["q"].device
@@ -114,6 +144,7 @@ def time_decode(kda, torch, w, steps, warmup, n_buffers=4):
 
 def cpu_baseline(w, inp, tokens: int):
     """fp64 oracle on the host over the first `tokens` tokens of the workload."""
+    tokens = min(tokens, w.T)
     from gated_delta_rule_72_amd import workloads as wl
     import oracle
     sl = slice(0, tokens)
@@ -124,15 +155,16 @@ def cpu_baseline(w, inp, tokens: int):
                                np.array([0, tokens], np.int64), None, 0)
     secs = time.perf_counter() - t0
     return {"value": tokens / secs, "unit": "tokens/s", "cores": int(rep["threads"]), "kind": "oracle",
-            "sample": f"first {tokens} of {w.T} tokens, all {w.H} heads, fp64 token-by-token recurrence",
+            "sample": (f"first {tokens} of {w.T} tokens" if tokens < w.T else f"all {w.T} tokens")
+                      + f" of {w.name}, all {w.H} heads, fp64 token-by-token recurrence",
             "seconds": round(secs, 3)}
 
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--cpu-tokens", type=int, default=262144,
                     help="token prefix the CPU oracle baseline runs on (0 = skip)")
     ap.add_argument("--skip-decode", action="store_true")
@@ -196,15 +228,16 @@ def main(argv=None):
         "config": {"workload": w.name, "B": w.num_seqs, "T": w.T, "H": w.H, "d_k": w.dk, "d_v": w.dv,
                    "gate": w.gate, "chunk": w.chunk, "qkv": w.dtype, "snapshot_interval": w.interval},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": stored_traffic(w.name),
                      "kernel": "kda_prefill_chunked = build_items + prefill_kernel pass 1 + "
                                "segment_scan + prefill_kernel pass 3 (automatic segment plan)",
                      "algorithmic_bytes_per_launch": int(pb), "algorithmic_flops_per_launch": int(pf),
                      "mfma_tflops": round(tfl, 2), "mfma_frac": round(tfl / MFMA_F16_PEAK_TFLOPS, 4),
                      "attainable_frac": round((pb / (HBM_PEAK_GBS * 1e9)) / (ms_avg * 1e-3), 4)},
-        "prefill_ms": {"avg": ms_avg, "min": min(ms), "max": max(ms),
+        "prefill_ms": {"avg": ms_avg, "median": sorted(ms)[len(ms) // 2], "min": min(ms), "max": max(ms),
                        "timing": "HIP events on the launch stream around each kda_prefill_chunked call"},
         "kernel_level": "hip-gfx950-chunked-v1",
+        "kernel_sources_sha256_16": kernel_sources_digest(),
     }
     del inp
     torch.cuda.empty_cache()
@@ -214,9 +247,11 @@ def main(argv=None):
         davg = sum(dms) / len(dms)
         db, df = decode_algorithmic(d.num_seqs, d.H, d.dk, d.dv, d.gate == "per_key")
         dgbs = db / (davg * 1e-3) / 1e9
-        result["decode"] = {"workload": d.name, "us_per_step": davg * 1e3, "us_min": min(dms) * 1e3,
+        result["decode"] = {"workload": d.name, "us_per_step": davg * 1e3,
+                            "us_median": sorted(dms)[len(dms) // 2] * 1e3, "us_min": min(dms) * 1e3,
                             "roofline": {"bound": "hbm", "achieved": round(dgbs, 1), "peak": HBM_PEAK_GBS,
                                          "unit": "GB/s", "frac": round(dgbs / HBM_PEAK_GBS, 4),
+                                         "traffic": stored_traffic(d.name),
                                          "algorithmic_bytes_per_launch": int(db)},
                             "kernel_level": "hip-gfx950-decode-v1"}
     if args.cpu_tokens > 0 and not args.prefill_only:

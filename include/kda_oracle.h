@@ -19,6 +19,9 @@
  * is not printed on the pages; the decay is read as acting on the key axis
  * before the delta correction, which keeps the printed order (decay multiplies
  * S_{t-1} first) and reduces to the scalar form when all channels are equal.
+ * Parity unpinned for that one point: with non-uniform a_t and overlapping
+ * keys, nothing on the pages fixes the placement; the pins cover the scalar
+ * and channel-uniform forms and the orthogonal-key (linear attention) case.
  *
  * Snapshots (same page, section "Co stan rekurencyjny zmienia przy
  * serwowaniu", item 1: prefix reuse needs the state taken at position N):

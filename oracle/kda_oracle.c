@@ -26,6 +26,13 @@
  *
  * Snapshots follow section "Co stan rekurencyjny zmienia przy serwowaniu",
  * item 1: the state at position N is kept, here at N = m * interval.
+ *
+ * Pins (tests/test_oracle_pins.py, tests/test_chunk_rederivation.py) fix the
+ * scalar form, the channel-uniform per-key form and, for non-uniform per-key
+ * decay, the decayed linear-attention reduction (orthogonal keys, where the
+ * read S' k_t vanishes). Parity unpinned: for non-uniform a_t with keys that
+ * overlap, no page prints where Diag(a_t) sits relative to the read S' k_t;
+ * the printed scalar order (decay first, then read and write) is carried over.
  */
 #define _GNU_SOURCE
 #include "../include/kda_oracle.h"
