@@ -329,7 +329,10 @@ void prefill_kernel(PrefillArgs a) {
   {
     const float* src = nullptr;
     if constexpr (!MAP) {
-      if (item.seg > 0) src = a.seg_states + ((int64_t)item_idx * a.H + h) * DD;
+      // a split sequence takes every start state, S_0 included, from the scan,
+      // so this pass never reads initial_state (which may alias final_state,
+      // written by the sequence's last segment)
+      if (item.n_segs > 1) src = a.seg_states + ((int64_t)item_idx * a.H + h) * DD;
       else if (a.init) src = a.init + ((int64_t)item.seq * a.H + h) * DD;
     }
 #pragma unroll
@@ -865,8 +868,8 @@ void prefill_kernel(PrefillArgs a) {
 
 // Segment scan: for every segmented sequence, head and block of 16 state rows,
 // S_{s+1} = S_s M_s + N_s for s = 0 .. n_segs-2 in fp32, from S_0 = the initial
-// state (or zeros); S_{s+1} is the start state of segment s+1. Rows of S
-// evolve independently.
+// state (or zeros); S_s is stored as the start state of segment s (S_0
+// included). Rows of S evolve independently.
 template <int D>
 __global__ __launch_bounds__(256) void segment_scan_kernel(PrefillArgs a) {
   constexpr int RB = 16;                        // rows per workgroup
@@ -885,7 +888,12 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(PrefillArgs a) {
   const int r = tid / 16, c0 = tid % 16;        // output row r, columns c0 + 16 j
   {
     const float* S0 = a.init ? a.init + ((int64_t)n * a.H + h) * DD + (int64_t)rb * RB * D : nullptr;
-    for (int e = tid; e < RB * D; e += 256) sS[e] = S0 ? S0[e] : 0.f;
+    float* out0 = a.seg_states + ((int64_t)first * a.H + h) * DD + (int64_t)rb * RB * D;
+    for (int e = tid; e < RB * D; e += 256) {
+      const float x = S0 ? S0[e] : 0.f;
+      sS[e] = x;
+      out0[e] = x;
+    }
   }
   for (int s = 0; s <= ns - 2; ++s) {
     const float* M = a.seg_maps + ((int64_t)(first + s) * a.H + h) * 2 * DD;

@@ -189,3 +189,24 @@ def test_varlen_config_sampled_heads():
     outs = run_prefill(inp, w.interval)
     assert outs[2].shape[0] == sum(L // w.interval for L in w.seq_lens)
     check_prefill(inp, outs, w.interval, heads=(5, 30))
+
+
+@pytest.mark.parametrize("segment_tokens", [0, 64, -1])
+def test_initial_state_may_alias_final_state(segment_tokens):
+    """final_state may be the initial_state buffer: results equal those of a
+    run with separate buffers, bit for bit, also when a split sequence's
+    segments (more workgroups than compute units at 64-token segments) run
+    in one pass."""
+    dev = device()
+    w = custom(f"alias_{segment_tokens}", H=8, d=64, lens=(4096, 300, 0, 1000), gate="per_key", seed=18)
+    inp = wl.make_prefill_inputs(w, dev)
+    o_ref, f_ref, _ = run_prefill(inp, 0, segment_tokens)
+    state = inp["initial_state"].clone()
+    o = torch.empty_like(o_ref)
+    snaps = torch.empty((0,) + tuple(f_ref.shape[1:]), dtype=torch.float32, device=dev)
+    kda.prefill_chunked(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["cu_seqlens"], state, 0,
+                        cu_seqlens_host=inp["cu_seqlens_host"], segment_tokens=segment_tokens,
+                        out=(o, state, snaps))
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref)
+    assert torch.equal(state, f_ref)
