@@ -191,24 +191,26 @@ __device__ __forceinline__ void unpack_group(const RawGroup<BF16>& r, float (&x)
   }
 }
 
-// Registers holding one chunk's raw inputs (prefetched during the previous chunk).
-constexpr int NT = 256;   // threads per workgroup (four wavefronts)
-constexpr int NW_STAGE = NT / 64;
+// Wavefronts per workgroup: one 16-row state slice per wavefront at d = 128
+// (two wavefronts per SIMD), two slices per wavefront at d = 64 (one per SIMD).
+template <int D>
+constexpr int waves_for() { return D == 128 ? 8 : 4; }
 
 // bf16 inputs: the raw q and k rows of a chunk go straight from HBM into LDS
 // (global_load_lds_dwordx4: lane l's 16 bytes land at base + 16 l), into
 // buffers that are dead during the state passing, so the prefetch of the
 // next chunk holds no registers. Rows past the chunk end are loaded from row
 // 0 and zeroed when they are read. `src` is the workgroup-uniform chunk base.
-template <int D>
+template <int D, int NW>
 __device__ __forceinline__ void stage_rows_lds(const uint16_t* src, uint32_t HD, int n, void* lds,
                                                int wave, int lane) {
   constexpr int LPR = D / 8;                 // lanes per row (16 bytes each)
   constexpr int RPI = 64 / LPR;              // rows per wavefront instruction (1 KiB)
   constexpr int INSTR = C / RPI;             // instructions per chunk
+  static_assert(INSTR % NW == 0, "every wavefront issues the same number of rows");
 #pragma unroll
-  for (int j = 0; j < INSTR / NW_STAGE; ++j) {
-    const int i = wave + NW_STAGE * j;
+  for (int j = 0; j < INSTR / NW; ++j) {
+    const int i = wave + NW * j;
     const int row = i * RPI + lane / LPR;
     const uint16_t* gp = src + (uint32_t)(row < n ? row : 0) * HD + 8 * (lane % LPR);
     __builtin_amdgcn_global_load_lds((gvoid_t*)gp, (lvoid_t*)(static_cast<char*>(lds) + 1024 * i),
@@ -216,11 +218,12 @@ __device__ __forceinline__ void stage_rows_lds(const uint16_t* src, uint32_t HD,
   }
 }
 
-template <int D, bool BF16, bool PER_KEY>
+// Registers holding one chunk's raw inputs (prefetched during the previous chunk).
+template <int D, bool BF16, bool PER_KEY, int NT>
 struct ChunkRegs {
   static constexpr int GROUPS = C * D / 8;       // 8-element groups per [64][D] tensor
-  static constexpr int GPT = GROUPS / NT;        // groups per thread (D / 32)
-  static constexpr int TPB = C * D / NT;         // per-key alpha: tokens per thread (D / 4)
+  static constexpr int GPT = GROUPS / NT;        // groups per thread
+  static constexpr int TPB = C * D / NT;         // per-key alpha: tokens per thread
   RawGroup<BF16> k[BF16 ? 1 : GPT], q[BF16 ? 1 : GPT], v[GPT];   // bf16: q, k staged in LDS
   // per-key: channel tid % D, tokens TPB (tid / D) .. +TPB-1; scalar: token = lane (wave 0)
   float alpha[PER_KEY ? TPB : 1];
@@ -230,10 +233,10 @@ struct ChunkRegs {
 // Every address is a workgroup-uniform base (scalar registers, cheap to
 // recompute per access) plus one 32-bit per-lane offset that does not depend
 // on the loop index, so no per-access offsets are kept live.
-template <int D, bool BF16, bool PER_KEY>
-__device__ __forceinline__ void load_chunk(ChunkRegs<D, BF16, PER_KEY>& R, const PrefillArgs& a,
+template <int D, bool BF16, bool PER_KEY, int NT>
+__device__ __forceinline__ void load_chunk(ChunkRegs<D, BF16, PER_KEY, NT>& R, const PrefillArgs& a,
                                            int64_t tok0, int n, int h, int tid, bool need_v) {
-  using CR = ChunkRegs<D, BF16, PER_KEY>;
+  using CR = ChunkRegs<D, BF16, PER_KEY, NT>;
   constexpr int ROWS_PER_PASS = NT / (D / 8);     // tokens covered by one group pass
   const int64_t HD = (int64_t)a.H * D;            // elements per token (all heads)
   const int64_t row0 = (tok0 * a.H + h) * D;      // first element of this chunk and head
@@ -270,6 +273,32 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<D, BF16, PER_KEY>& R, const
   R.beta = (wave == 0 && lane < n) ? bb[(uint32_t)lane * a.H] : 0.f;
 }
 
+// Gram tile pairs (R, I), R >= I, as runs of one row block per wavefront:
+// run `run` of wavefront `wave` covers (R, I0..I1); false when it has none.
+// Four wavefronts (one per SIMD): 2/3/3/2 pairs,
+//   w0: R3 I0-1   w1: R2 I0-2   w2: R1 I0-1, then R0 I0   w3: R3 I2-3.
+// Eight wavefronts (wavefronts w and w+4 share a SIMD): 3/2/3/2 pairs per SIMD,
+//   w0: R3 I0-1  w1: R3 I2-3  w2: R2 I0-1  w3: R2 I2  w4: R0 I0  w6: R1 I0  w7: R1 I1.
+template <int NW>
+__device__ __forceinline__ bool gram_run(int wave, int run, int& R, int& I0, int& I1) {
+  if constexpr (NW == 4) {
+    if (run == 1 && wave != 2) return false;
+    R = wave == 0 ? 3 : wave == 1 ? 2 : wave == 3 ? 3 : (run == 0 ? 1 : 0);
+    I0 = wave == 3 ? 2 : 0;
+    I1 = wave == 0 ? 1 : wave == 1 ? 2 : wave == 3 ? 3 : (run == 0 ? 1 : 0);
+    return true;
+  } else {
+    static_assert(NW == 8, "four or eight wavefronts");
+    if (run == 1 || wave == 5) return false;
+    // per-wavefront nibbles (wavefront 0 lowest): R 3,3,2,2,0,0,1,1;
+    // I0 0,2,0,2,0,0,0,1; I1 1,3,1,2,0,0,0,1
+    R = (0x11002233u >> (4 * wave)) & 15u;
+    I0 = (0x10002020u >> (4 * wave)) & 15u;
+    I1 = (0x10002131u >> (4 * wave)) & 15u;
+    return true;
+  }
+}
+
 __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) {
@@ -279,13 +308,15 @@ __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
   return x;
 }
 
-template <int D, bool BF16, bool PER_KEY, bool MAP>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int D, bool BF16, bool PER_KEY, bool MAP, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void prefill_kernel(PrefillArgs a) {
+  constexpr int NT = 64 * NW;    // threads
   using L = Lds<D>;
-  using CR = ChunkRegs<D, BF16, PER_KEY>;
-  constexpr int NW = NT / 64;    // wavefronts
-  constexpr int SPW = D / 64;    // state slices per wavefront
+  using CR = ChunkRegs<D, BF16, PER_KEY, NT>;
+  constexpr int SPW = D / (16 * NW);   // state slices per wavefront
+  static_assert(SPW >= 1 && SPW * 16 * NW == D, "slices cover the state");
+  static_assert(NT / D >= 1 && NT / D <= 4, "per-key scan partials: at most four blocks of tokens");
   constexpr int NSL = MAP ? 2 * SPW : SPW;   // MAP: SPW N slices, then SPW M slices
   constexpr int KT = D / 16;     // 16-row tiles along d_k
   extern __shared__ __align__(16) unsigned char smem[];
@@ -300,6 +331,8 @@ void prefill_kernel(PrefillArgs a) {
   float* sBeta = sGam + D;                                        // [64]
   float* sGs = sBeta + C;                                         // [64] scalar-gate G
   float* sPart = sGs + C;                                         // [4][D] cumsum partials
+  float* sDec = sPart;         // scalar gate (sPart unused): [64] 2^G_c, then [64] 2^(G_n - G_c)
+  float* sRem = sPart + C;
   unsigned char* regA = smem + L::OFF_A;
   float* sG = reinterpret_cast<float*>(regA + L::A_G);
   _Float16* sRK = reinterpret_cast<_Float16*>(regA + L::A_RK);
@@ -318,6 +351,10 @@ void prefill_kernel(PrefillArgs a) {
   }
   constexpr bool out_mode = !MAP;
   constexpr bool need_v = true;
+  // MAP with bf16 inputs stages v rows in LDS as well (into the Q~ buffer,
+  // which MAP never uses), so its prefetch holds no registers across P6
+  constexpr bool v_in_lds = MAP && BF16;
+  constexpr bool v_in_regs = need_v && !v_in_lds;
   const int64_t HD = (int64_t)a.H * D;
   const int64_t DD = (int64_t)D * D;
 
@@ -355,13 +392,16 @@ void prefill_kernel(PrefillArgs a) {
   const uint32_t HDu = (uint32_t)a.H * D;
   CR regs;
   if (n_chunks > 0) {
-    load_chunk<D, BF16, PER_KEY>(regs, a, item.tok_begin, min(C, item.n_tokens), h, tid, need_v);
+    load_chunk<D, BF16, PER_KEY, NT>(regs, a, item.tok_begin, min(C, item.n_tokens), h, tid, v_in_regs);
     if constexpr (BF16) {
       const int64_t row0 = (item.tok_begin * a.H + h) * D;
-      stage_rows_lds<D>(static_cast<const uint16_t*>(a.k) + row0, HDu, min(C, item.n_tokens),
+      if constexpr (v_in_lds)
+        stage_rows_lds<D, NW>(static_cast<const uint16_t*>(a.v) + row0, HDu, min(C, item.n_tokens),
+                          smem + L::OFF_QT, wave, lane);
+      stage_rows_lds<D, NW>(static_cast<const uint16_t*>(a.k) + row0, HDu, min(C, item.n_tokens),
                         smem + L::OFF_KHT, wave, lane);
       if constexpr (!MAP)
-        stage_rows_lds<D>(static_cast<const uint16_t*>(a.q) + row0, HDu, min(C, item.n_tokens),
+        stage_rows_lds<D, NW>(static_cast<const uint16_t*>(a.q) + row0, HDu, min(C, item.n_tokens),
                           smem + L::OFF_L, wave, lane);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
@@ -371,6 +411,11 @@ void prefill_kernel(PrefillArgs a) {
   for (int ch = 0; ch < n_chunks; ++ch) {
     const int64_t tok0 = item.tok_begin + (int64_t)ch * C;
     const int n = min(C, item.n_tokens - ch * C);
+    // Per-lane index arithmetic is redone every chunk: hoisted out of the
+    // loop it would hold dozens of registers for the whole item.
+    int tid_c = tid;
+    asm volatile("" : "+v"(tid_c));
+    const int tid = tid_c, lane = tid_c % 64, g = lane >> 4, l16 = lane & 15;
 
     // ---- P1: raw q, k (fp16), cumulative log2 decay, beta ---------------------
 #pragma unroll
@@ -424,6 +469,8 @@ void prefill_kernel(PrefillArgs a) {
         const float gam = exp2_hw(gl);
         sGL[lane] = gl;
         sGam[lane] = gam;
+        sDec[lane] = exp2_hw(gcum);
+        sRem[lane] = exp2_hw(gl - gcum);
         if (D > 64) { sGL[lane + 64] = gl; sGam[lane + 64] = gam; }
       }
     }
@@ -450,12 +497,17 @@ void prefill_kernel(PrefillArgs a) {
       const f16x8 kx = *reinterpret_cast<const f16x8*>(sRK + c * L::LDQ + 8 * k8);
       const f16x8 qx = MAP ? f16x8{} : *reinterpret_cast<const f16x8*>(sRQ + c * L::LDQ + 8 * k8);
       f16x8 qt;
+      // scalar gate: one factor pair per token, computed once in P1
+      const float dec_c = PER_KEY ? 0.f : sDec[c], rem_c = PER_KEY ? 0.f : sRem[c];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int kk = 8 * k8 + e;
-        const float gc = PER_KEY ? sG[c * L::LDG + kk] : sGs[c];
-        const float dec = exp2_hw(gc);
-        const float rem = exp2_hw(sGL[kk] - gc);
+        float dec = dec_c, rem = rem_c;
+        if constexpr (PER_KEY) {
+          const float gc = sG[c * L::LDG + kk];
+          dec = exp2_hw(gc);
+          rem = exp2_hw(sGL[kk] - gc);
+        }
         const float kf = (float)kx[e];
         qt[e] = (_Float16)((float)qx[e] * dec);
         sKhT[kk * L::LDT + swz(kk, c)] = (_Float16)(kf * dec);
@@ -465,10 +517,8 @@ void prefill_kernel(PrefillArgs a) {
     }
 
     // ---- P3: Gram tiles L (fp32) and B (fp16) ------------------------------
-    // Upper blocks of B are zero. The 10 lower tile pairs (R >= I) are split
-    // 2/3/3/2 over the wavefronts so that a wavefront keeps one row block R:
-    //   wave 0: R=3, I=0,1   wave 1: R=2, I=0..2   wave 2: R=1, I=0,1 and R=0   wave 3: R=3, I=2,3
-    // Each pair computes the transposed tiles L^T and B^T (column block I as the
+    // Upper blocks of B are zero. The 10 lower tile pairs (R >= I) go to the
+    // wavefronts as runs (R, I0..I1) of one row block (gram_run). Each pair computes the transposed tiles L^T and B^T (column block I as the
     // A operand, row block R as the B operand), so a lane ends with four
     // consecutive columns i of one row r and stores them as one vector.
     for (int e = tid; e < (MAP ? 0 : 6 * 256); e += NT) {
@@ -478,14 +528,10 @@ void prefill_kernel(PrefillArgs a) {
       sB[(16 * R + rr) * L::LDT + 16 * I + cc] = (_Float16)0.f;
     }
     {
-      // (R, I-range) runs of this wavefront
-      const int nrun = wave == 2 ? 2 : 1;
 #pragma unroll
       for (int run = 0; run < 2; ++run) {
-        if (run >= nrun) break;
-        const int R = wave == 0 ? 3 : wave == 1 ? 2 : wave == 3 ? 3 : (run == 0 ? 1 : 0);
-        const int I0 = wave == 3 ? 2 : 0;
-        const int I1 = wave == 0 ? 1 : wave == 1 ? 2 : wave == 3 ? 3 : (run == 0 ? 1 : 0);
+        int R, I0, I1;
+        if (!gram_run<NW>(wave, run, R, I0, I1)) break;
         const int r = 16 * R + l16;                  // this lane's row of L / B
         if constexpr (!PER_KEY) {
           // exact fp16 products of the staged inputs; decay applied per element
@@ -604,7 +650,19 @@ void prefill_kernel(PrefillArgs a) {
         const int gi = tid + j * NT;
         const int c = gi / (D / 8), k8 = gi % (D / 8);
         float x[8];
-        unpack_group<BF16>(regs.v[j], x);
+        if constexpr (v_in_lds) {
+          // staged bf16 rows [64][D] (unpadded); rows >= n are stale and zeroed here
+          const uint4 vw = *reinterpret_cast<const uint4*>(smem + L::OFF_QT + (c * D + 8 * k8) * 2);
+          const uint32_t vv4[4] = {vw.x, vw.y, vw.z, vw.w};
+          const bool live = c < n;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[2 * e] = live ? bf16_bits_to_f32(vv4[e] & 0xFFFFu) : 0.f;
+            x[2 * e + 1] = live ? bf16_bits_to_f32(vv4[e] >> 16) : 0.f;
+          }
+        } else {
+          unpack_group<BF16>(regs.v[j], x);
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) sVT[(8 * k8 + e) * L::LDT + swz(8 * k8 + e, c)] = (_Float16)x[e];
       }
@@ -692,13 +750,16 @@ void prefill_kernel(PrefillArgs a) {
     // to LDS: the K^T and L buffers are not read again in this chunk)
     if (ch + 1 < n_chunks) {
       const int n_next = min(C, item.n_tokens - (ch + 1) * C);
-      load_chunk<D, BF16, PER_KEY>(regs, a, tok0 + C, n_next, h, tid, need_v);
+      load_chunk<D, BF16, PER_KEY, NT>(regs, a, tok0 + C, n_next, h, tid, v_in_regs);
       if constexpr (BF16) {
         const int64_t row0 = ((tok0 + C) * a.H + h) * D;
-        stage_rows_lds<D>(static_cast<const uint16_t*>(a.k) + row0, HDu, n_next, smem + L::OFF_KHT,
+        if constexpr (v_in_lds)
+          stage_rows_lds<D, NW>(static_cast<const uint16_t*>(a.v) + row0, HDu, n_next, smem + L::OFF_QT,
+                            wave, lane);
+        stage_rows_lds<D, NW>(static_cast<const uint16_t*>(a.k) + row0, HDu, n_next, smem + L::OFF_KHT,
                           wave, lane);
         if constexpr (!MAP)
-          stage_rows_lds<D>(static_cast<const uint16_t*>(a.q) + row0, HDu, n_next, smem + L::OFF_L,
+          stage_rows_lds<D, NW>(static_cast<const uint16_t*>(a.q) + row0, HDu, n_next, smem + L::OFF_L,
                             wave, lane);
       }
     }
@@ -1001,7 +1062,8 @@ template <int D, bool BF16, bool PK, bool MAP>
 hipError_t launch_pass(const PrefillArgs& a, hipStream_t s) {
   using L = Lds<D>;
   static_assert(L::TOTAL <= 160 * 1024, "LDS budget");
-  auto kern = prefill_kernel<D, BF16, PK, MAP>;
+  constexpr int NT = 64 * waves_for<D>();
+  auto kern = prefill_kernel<D, BF16, PK, MAP, waves_for<D>()>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL);
   if (e != hipSuccess) return e;

@@ -2,7 +2,8 @@
 
 - libkda.so exports every function include/kda.h declares, and the Python
   binding offers each under the same name;
-- liboracle_kda.so exports every function include/kda_oracle.h declares;
+- liboracle_kda.so exports every function include/kda_oracle.h declares, and
+  libkda_calib.so every function of include/kda_calib.h;
 - argument validation of the C ABI: every rejected call returns its status
   before anything touches a device (fake, never-dereferenced pointers are used
   where only alignment or presence is checked);
@@ -54,6 +55,27 @@ def test_oracle_header_symbols_exported():
     lib = oracle.load()
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_calib_header_symbols_exported_and_checked(K):
+    from gated_delta_rule_72_amd import build as B
+    if not os.path.exists(B.CALIB_LIB):
+        B.build()
+    names = _declared("kda_calib.h")
+    assert set(names) == {"kda_calib_mfma_f16", "kda_calib_copy"}
+    lib = ctypes.CDLL(B.CALIB_LIB)
+    for n in names:
+        assert hasattr(lib, n), n
+    lib.kda_calib_mfma_f16.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    lib.kda_calib_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                   ctypes.c_void_p]
+    # rejected on the host, nothing launched
+    assert lib.kda_calib_mfma_f16(0, 10, _fake(0x1000), None) == -1
+    assert lib.kda_calib_mfma_f16(4, 10, _fake(0x1004), None) == -1
+    assert lib.kda_calib_mfma_f16(4, 10, None, None) == -1
+    assert lib.kda_calib_copy(_fake(0x1000), _fake(0x2000), -1, 4, None) == -1
+    assert lib.kda_calib_copy(_fake(0x1008), _fake(0x2000), 16, 4, None) == -1
+    assert lib.kda_calib_copy(None, None, 0, 4, None) == 0
 
 
 def test_snapshot_count(K):
