@@ -720,29 +720,54 @@ void prefill_kernel(PrefillArgs a) {
       *reinterpret_cast<f16x8*>(sTl + c * L::LDT + i0) = tl;
     }
     __syncthreads();
+    // W[:, 16kt..16kt+15] for kt = wave, wave + NW, ... and U' = T~ V for the
+    // wavefront's own value slices (K = 64), sharing each T~ hi/lo tile read;
+    // U' stays in registers for P6.
+    f32x4 Up[SPW][4];
     {
-      // wave w computes W[:, 16kt..16kt+15] for kt = w, w + NW, ... (K = 64)
+      f32x4 acc[KT / NW][4];
 #pragma unroll
-      for (int kj = 0; kj < KT / NW; ++kj) {
-        const int kt = wave + NW * kj;
-        f32x4 acc[4];
+      for (int kj = 0; kj < KT / NW; ++kj)
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) acc[ct] = f32x4{0, 0, 0, 0};
+        for (int ct = 0; ct < 4; ++ct) acc[kj][ct] = f32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const f16x8 bk = ld_std_swz(sKhT, L::LDT, 16 * kt, 32 * ks, lane);
+      for (int sl = 0; sl < SPW; ++sl)
 #pragma unroll
-          for (int ct = 0; ct < 4; ++ct) {
-            acc[ct] = mfma_f16(ld_std(sTh, L::LDT, 16 * ct, 32 * ks, lane), bk, acc[ct]);
-            acc[ct] = mfma_f16(ld_std(sTl, L::LDT, 16 * ct, 32 * ks, lane), bk, acc[ct]);
+        for (int ct = 0; ct < 4; ++ct) Up[sl][ct] = f32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        f16x8 th[4], tl[4], bk[KT / NW], bv[SPW];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          th[ct] = ld_std(sTh, L::LDT, 16 * ct, 32 * ks, lane);
+          tl[ct] = ld_std(sTl, L::LDT, 16 * ct, 32 * ks, lane);
+        }
+#pragma unroll
+        for (int kj = 0; kj < KT / NW; ++kj) bk[kj] = ld_std_swz(sKhT, L::LDT, 16 * (wave + NW * kj), 32 * ks, lane);
+#pragma unroll
+        for (int sl = 0; sl < SPW; ++sl) bv[sl] = ld_std_swz(sVT, L::LDT, 16 * (SPW * wave + sl), 32 * ks, lane);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+#pragma unroll
+          for (int kj = 0; kj < KT / NW; ++kj) {
+            acc[kj][ct] = mfma_f16(th[ct], bk[kj], acc[kj][ct]);
+            acc[kj][ct] = mfma_f16(tl[ct], bk[kj], acc[kj][ct]);
+          }
+#pragma unroll
+          for (int sl = 0; sl < SPW; ++sl) {
+            Up[sl][ct] = mfma_f16(th[ct], bv[sl], Up[sl][ct]);
+            Up[sl][ct] = mfma_f16(tl[ct], bv[sl], Up[sl][ct]);
           }
         }
+      }
+#pragma unroll
+      for (int kj = 0; kj < KT / NW; ++kj)
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            sW[(16 * ct + 4 * g + i) * L::LDQ + 16 * kt + l16] = (_Float16)acc[ct][i];
-      }
+            sW[(16 * ct + 4 * g + i) * L::LDQ + 16 * (wave + NW * kj) + l16] = (_Float16)acc[kj][ct][i];
     }
     __syncthreads();
 
@@ -770,35 +795,13 @@ void prefill_kernel(PrefillArgs a) {
     // Operand tiles are read in batches ahead of their MFMAs (the scheduling
     // barriers keep each batch of reads in flight together).
     {
-      // U' = T~ V_s (the first SPW slices; zero for M slices): rows c (4 tiles),
-      // column v = 16 slice + l16
+      // U starts as U' (from P5) for the first SPW slices, zero for M slices:
+      // rows c (4 tiles), column v = 16 slice + l16
       f32x4 U[NSL][4];
 #pragma unroll
       for (int sl = 0; sl < NSL; ++sl)
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) U[sl][ct] = f32x4{0, 0, 0, 0};
-      if (need_v) {
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          f16x8 bv[SPW], th[4], tl[4];
-#pragma unroll
-          for (int sl = 0; sl < SPW; ++sl)
-            bv[sl] = ld_std_swz(sVT, L::LDT, 16 * (SPW * wave + sl), 32 * ks, lane);
-#pragma unroll
-          for (int ct = 0; ct < 4; ++ct) {
-            th[ct] = ld_std(sTh, L::LDT, 16 * ct, 32 * ks, lane);
-            tl[ct] = ld_std(sTl, L::LDT, 16 * ct, 32 * ks, lane);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-            for (int sl = 0; sl < SPW; ++sl) {
-              U[sl][ct] = mfma_f16(th[ct], bv[sl], U[sl][ct]);
-              U[sl][ct] = mfma_f16(tl[ct], bv[sl], U[sl][ct]);
-            }
-        }
-      }
+        for (int ct = 0; ct < 4; ++ct) U[sl][ct] = sl < SPW ? Up[sl % SPW][ct] : f32x4{0, 0, 0, 0};
       // S0^T as the permuted-K operand (fp16), shared by W S0^T and Q~ S0^T;
       // U = U' - W S0^T accumulates W (-S0^T) into U directly.
       f16x8 sop[NSL][D / 32];
