@@ -275,28 +275,43 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<D, BF16, PER_KEY, NT>& R, c
 
 // Gram tile pairs (R, I), R >= I, as runs of one row block per wavefront:
 // run `run` of wavefront `wave` covers (R, I0..I1); false when it has none.
-// Four wavefronts (one per SIMD): 2/3/3/2 pairs,
-//   w0: R3 I0-1   w1: R2 I0-2   w2: R1 I0-1, then R0 I0   w3: R3 I2-3.
-// Eight wavefronts (wavefronts w and w+4 share a SIMD): 3/2/3/2 pairs per SIMD,
-//   w0: R3 I0-1  w1: R3 I2-3  w2: R2 I0-1  w3: R2 I2  w4: R0 I0  w6: R1 I0  w7: R1 I1.
+// Two wavefronts compute two diagonal pairs each and then invert both
+// diagonal blocks together (gram_diag). Balance counts a pair and an
+// inversion as one unit each, per SIMD:
+//   four wavefronts:  w0: R3 I0-2 | w1: R2 I0-1, R1 I0 | w2: R0 I0, R1 I1, inv 0,1
+//                     | w3: R2 I2, R3 I3, inv 2,3                       (3/3/3/3)
+//   eight wavefronts (w and w+4 share a SIMD): w0: R0 I0, R1 I1, inv 0,1 |
+//                     w1: R2 I2, R3 I3, inv 2,3 | w2: R3 I0-1 | w3: R3 I2, R2 I1 |
+//                     w6: R2 I0 | w7: R1 I0                            (3/3/3/3)
 template <int NW>
 __device__ __forceinline__ bool gram_run(int wave, int run, int& R, int& I0, int& I1) {
+  // packed per wavefront: for each run a nibble triple (R, I0, I1); 0xF = no run
+  uint32_t code;
   if constexpr (NW == 4) {
-    if (run == 1 && wave != 2) return false;
-    R = wave == 0 ? 3 : wave == 1 ? 2 : wave == 3 ? 3 : (run == 0 ? 1 : 0);
-    I0 = wave == 3 ? 2 : 0;
-    I1 = wave == 0 ? 1 : wave == 1 ? 2 : wave == 3 ? 3 : (run == 0 ? 1 : 0);
-    return true;
+    constexpr uint32_t kRun0[4] = {0x302, 0x201, 0x000, 0x222};
+    constexpr uint32_t kRun1[4] = {0xFFF, 0x100, 0x111, 0x333};
+    code = run == 0 ? kRun0[wave & 3] : kRun1[wave & 3];
   } else {
     static_assert(NW == 8, "four or eight wavefronts");
-    if (run == 1 || wave == 5) return false;
-    // per-wavefront nibbles (wavefront 0 lowest): R 3,3,2,2,0,0,1,1;
-    // I0 0,2,0,2,0,0,0,1; I1 1,3,1,2,0,0,0,1
-    R = (0x11002233u >> (4 * wave)) & 15u;
-    I0 = (0x10002020u >> (4 * wave)) & 15u;
-    I1 = (0x10002131u >> (4 * wave)) & 15u;
-    return true;
+    constexpr uint32_t kRun0[8] = {0x000, 0x222, 0x301, 0x322, 0xFFF, 0xFFF, 0x200, 0x100};
+    constexpr uint32_t kRun1[8] = {0x111, 0x333, 0xFFF, 0x211, 0xFFF, 0xFFF, 0xFFF, 0xFFF};
+    code = run == 0 ? kRun0[wave & 7] : kRun1[wave & 7];
   }
+  if (code == 0xFFF) return false;
+  R = code >> 8;
+  I0 = (code >> 4) & 15;
+  I1 = code & 15;
+  return true;
+}
+// Diagonal blocks this wavefront inverts after its runs (d0, d1), or false.
+template <int NW>
+__device__ __forceinline__ bool gram_diag(int wave, int& d0, int& d1) {
+  const int w0 = 2, w1 = 3;                      // four wavefronts
+  const int v0 = 0, v1 = 1;                      // eight wavefronts
+  const int wa = NW == 4 ? w0 : v0, wb = NW == 4 ? w1 : v1;
+  if (wave == wa) { d0 = 0; d1 = 1; return true; }
+  if (wave == wb) { d0 = 2; d1 = 3; return true; }
+  return false;
 }
 
 __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
@@ -562,6 +577,14 @@ void prefill_kernel(PrefillArgs a) {
             }
             *reinterpret_cast<f32x4*>(sL + r * L::LDL + i0) = lv;
             if constexpr (!MAP) *reinterpret_cast<f16x4*>(sB + r * L::LDT + i0) = bv;
+            if (I == R) {
+              // diagonal tile: L_RR^T also into its upper triangle (column i
+              // of L_RR becomes row i there); issued after the row stores, so
+              // it lands after their zeros
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (i0 + e < r) sL[(i0 + e) * L::LDL + r] = lv[e];
+            }
           }
         } else {
           // three-term bf16 products of operands decayed relative to token 16R:
@@ -610,38 +633,94 @@ void prefill_kernel(PrefillArgs a) {
             }
             *reinterpret_cast<f32x4*>(sL + r * L::LDL + i0) = lv;
             if constexpr (!MAP) *reinterpret_cast<f16x4*>(sB + r * L::LDT + i0) = bv;
+            if (I == R) {
+              // diagonal tile: L_RR^T also into its upper triangle (column i
+              // of L_RR becomes row i there); issued after the row stores, so
+              // it lands after their zeros
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (i0 + e < r) sL[(i0 + e) * L::LDL + r] = lv[e];
+            }
           }
+        }
+      }
+      int d0, d1;
+      if (gram_diag<NW>(wave, d0, d1)) {
+        // Replace L_bb by the inverse of the unit lower block I + L_bb for the
+        // two diagonal blocks this wavefront computed: lane groups 0-1 take
+        // block d0, 2-3 block d1, one column j per lane (groups 0 and 2
+        // store). Right-looking: once x_i is final, every later row r takes
+        // -L[r][i] x_i, read from row i of the transposed copy in the block's
+        // upper triangle.
+        __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): the tiles are in LDS
+        __builtin_amdgcn_wave_barrier();
+        const int b = g < 2 ? d0 : d1;
+        float* Lb = sL + (16 * b) * L::LDL + 16 * b;
+        float x[16];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) x[rr] = (rr == l16) ? 1.f : 0.f;
+#pragma unroll
+        for (int i = 0; i < 15; ++i) {
+          float col[16];                             // col[r] = L[r][i] for r > i
+#pragma unroll
+          for (int q4 = i / 4; q4 < 4; ++q4) {
+            const f32x4 t = *reinterpret_cast<const f32x4*>(Lb + i * L::LDL + 4 * q4);
+            col[4 * q4] = t[0]; col[4 * q4 + 1] = t[1]; col[4 * q4 + 2] = t[2]; col[4 * q4 + 3] = t[3];
+          }
+#pragma unroll
+          for (int rr = i + 1; rr < 16; ++rr) x[rr] -= col[rr] * x[i];
+        }
+        __builtin_amdgcn_wave_barrier();
+        if ((g & 1) == 0) {
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) Lb[rr * L::LDL + l16] = x[rr];
         }
       }
     }
     __syncthreads();
 
     // ---- P4: A = (I + L)^-1 -------------------------------------------------
-    // Diagonal 16x16 blocks by forward substitution (wave 0, one column per
-    // lane); A_bb overwrites L_bb. The other lanes of the workgroup stage V^T.
-    if (wave == 0) {
-      const int b = g, j = l16;
-      const float* Lb = sL + (16 * b) * L::LDL + 16 * b;
-      float x[16];
+    // The diagonal blocks A_RR are in place (P3). Block column I of the
+    // off-diagonal part is one dependent chain on wavefront I (I = 0, 1, 2),
+    //   A_RI = -A_RR (L_RI A_II + sum_{I<m<R} L_Rm A_mI),   R = I+1 .. 3,
+    // on fp32 MFMA with the column's earlier blocks kept in accumulator
+    // registers; A_RI is stored at block (I, R). Meanwhile every wavefront
+    // stages V^T.
+    if (wave < 3) {
+      const int I = wave;
+      f32x4 Acol[4];                                  // A_mI, m > I (accumulator layout)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float lrow[16];
+      for (int R = 1; R < 4; ++R) {
+        if (R > I) {
+          f32x4 acc = {0, 0, 0, 0};
+          // L_RI A_II, A_II read from LDS in the standard K order
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x4 t = *reinterpret_cast<const f32x4*>(Lb + r * L::LDL + 4 * q4);
-          lrow[4 * q4] = t[0]; lrow[4 * q4 + 1] = t[1]; lrow[4 * q4 + 2] = t[2]; lrow[4 * q4 + 3] = t[3];
+          for (int ks = 0; ks < 4; ++ks) {
+            const float av = sL[(16 * R + l16) * L::LDL + 16 * I + 4 * ks + g];
+            const float bv = sL[(16 * I + 4 * ks + g) * L::LDL + 16 * I + l16];
+            acc = mfma_f32(av, bv, acc);
+          }
+          // L_Rm A_mI for I < m < R, A_mI from registers (permuted K: k = 4g + ks)
+#pragma unroll
+          for (int m = 1; m < 3; ++m) {
+            if (m > I && m < R) {
+#pragma unroll
+              for (int ks = 0; ks < 4; ++ks)
+                acc = mfma_f32(sL[(16 * R + l16) * L::LDL + 16 * m + 4 * g + ks], Acol[m][ks], acc);
+            }
+          }
+          // -A_RR acc, acc as the permuted-K operand
+          f32x4 res = {0, 0, 0, 0};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks)
+            res = mfma_f32(sL[(16 * R + l16) * L::LDL + 16 * R + 4 * g + ks], acc[ks], res);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            Acol[R][i] = -res[i];
+            sL[(16 * I + 4 * g + i) * L::LDL + 16 * R + l16] = -res[i];
+          }
         }
-        float s0 = (r == j) ? 1.f : 0.f, s1 = 0.f;
-#pragma unroll
-        for (int i = 0; i < r; i += 2) {
-          s0 -= lrow[i] * x[i];
-          if (i + 1 < r) s1 -= lrow[i + 1] * x[i + 1];
-        }
-        x[r] = s0 + s1;
       }
-      float* Ab = sL + (16 * b) * L::LDL + 16 * b;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) Ab[r * L::LDL + j] = x[r];
     }
     // V^T [v][c] into region A (G and raw q, k are dead after P3)
     if (need_v) {
@@ -668,35 +747,6 @@ void prefill_kernel(PrefillArgs a) {
       }
     }
     __syncthreads();
-    // Off-diagonal blocks, stage R = 1, 2, 3: job (R, I) on wave I,
-    //   A_RI = -A_RR * sum_{m=I}^{R-1} L_Rm A_mI, stored at block (I, R).
-#pragma unroll
-    for (int R = 1; R < 4; ++R) {
-      if (wave < R) {
-        const int I = wave;
-        f32x4 acc = {0, 0, 0, 0};
-        for (int m = I; m < R; ++m) {
-          // A_mI lives at block (I, m) for m > I, at (I, I) for m == I
-          const float* Amb = sL + (16 * I) * L::LDL + 16 * m;
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const float av = sL[(16 * R + l16) * L::LDL + 16 * m + 4 * ks + g];
-            const float bv = Amb[(4 * ks + g) * L::LDL + l16];
-            acc = mfma_f32(av, bv, acc);
-          }
-        }
-        // -A_RR * acc, acc as the K-operand with permuted K (k = 4g + ks)
-        f32x4 res = {0, 0, 0, 0};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const float av = sL[(16 * R + l16) * L::LDL + 16 * R + 4 * g + ks];
-          res = mfma_f32(av, acc[ks], res);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sL[(16 * I + 4 * g + i) * L::LDL + 16 * R + l16] = -res[i];
-      }
-      __syncthreads();
-    }
 
     // ---- P5: T~ = A Diag(beta) as fp16 hi + lo; W = T~ (K * 2^G) ------------
     for (int e8 = tid; e8 < C * C / 8; e8 += NT) {
