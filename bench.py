@@ -185,6 +185,43 @@ def time_decode(kda, torch, w, steps, warmup, n_buffers=4):
     return [s.elapsed_time(e) for s, e in ev]
 
 
+def time_decode_tokens(kda, torch, w, n_tok, steps, warmup, keep_states, n_buffers=4):
+    """kda_decode_tokens over n_tok tokens per sequence of the decode workload,
+    committing every token; optionally writing the per-token states."""
+    from gated_delta_rule_72_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    B = w.num_seqs
+    ws = w.with_(seq_lens=(n_tok,) * B)
+    bufs = []
+    for i in range(n_buffers):
+        inp = wl.make_prefill_inputs(ws, dev, seed=w.seed + 100 + i)
+        x = {y: inp[y].view(B, n_tok, *inp[y].shape[1:]) for y in ("q", "k", "v", "alpha", "beta")}
+        x["state"] = inp["initial_state"]
+        bufs.append(x)
+    shape = kda.make_shape(w.H, w.dk, w.dv, bufs[0]["q"].dtype, w.gate == "per_key")
+    o = torch.empty((B, n_tok, w.H, w.dv), dtype=torch.float32, device=dev)
+    ts = torch.empty((B, n_tok, w.H, w.dv, w.dk), dtype=torch.float32, device=dev) if keep_states else None
+
+    def call(i):
+        d = bufs[i % n_buffers]
+        kda.kda_decode_tokens(shape, B, n_tok, d["q"], d["k"], d["v"], d["alpha"], d["beta"], d["state"], o, ts)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (s0, e0) in enumerate(ev):
+        s0.record(stream)
+        call(i)
+        e0.record(stream)
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    del bufs, o, ts
+    torch.cuda.empty_cache()
+    return ms
+
+
 def cpu_baseline(w, inp, tokens: int):
     """fp64 oracle on the host over the first `tokens` tokens of the workload."""
     tokens = min(tokens, w.T)
@@ -215,6 +252,8 @@ def main(argv=None):
     ap.add_argument("--prefill-workload", default="long_prefill_T262144_H16_d128",
                     help="workload name for the prefill line (default: the headline long prefill)")
     ap.add_argument("--decode-only", action="store_true", help="profiling: only the decode loop")
+    ap.add_argument("--no-other-prefill", action="store_true",
+                    help="skip timing the other prefill workloads (KDA layer shape, varlen pack)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="profiling: copy a 256 MiB fp32 buffer 3 times (known bytes for HBM counters)")
     args = ap.parse_args(argv)
@@ -287,6 +326,25 @@ def main(argv=None):
     }
     del inp
     torch.cuda.empty_cache()
+    if not args.no_other_prefill and not args.prefill_only:
+        other = {}
+        for ow in (wl.KDA_LAYER, wl.VARLEN):
+            oinp = wl.make_prefill_inputs(ow, dev)
+            torch.cuda.synchronize()
+            oms, _ = time_prefill(kda, torch, oinp, ow, max(5, args.steps // 2), args.warmup)
+            oavg = sum(oms) / len(oms)
+            on_snap = kda.kda_snapshot_count(oinp["cu_seqlens_host"], ow.interval)
+            ob, of = prefill_algorithmic(ow.T, ow.H, ow.dk, ow.dv, ow.num_seqs, ow.gate == "per_key",
+                                         qkv_bytes=2 if ow.dtype == "bf16" else 4,
+                                         with_init=oinp["initial_state"] is not None, n_snap=on_snap)
+            ogbs = ob / (oavg * 1e-3) / 1e9
+            other[ow.name] = {"ms_per_call": round(oavg, 4), "tokens_per_s": round(ow.T / (oavg * 1e-3), 1),
+                              "hbm_GBs": round(ogbs, 1), "hbm_frac": round(ogbs / HBM_PEAK_GBS, 4),
+                              "mfma_frac": round(of / (oavg * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                              "algorithmic_bytes": int(ob), "algorithmic_flops": int(of), "calls": len(oms)}
+            del oinp
+            torch.cuda.empty_cache()
+        result["other_prefill"] = other
     if not args.skip_decode and not args.prefill_only:
         d = wl.DECODE
         dms = time_decode(kda, torch, d, max(args.steps, 20), args.warmup)
@@ -301,6 +359,23 @@ def main(argv=None):
                                          "traffic": stored_traffic(d.name),
                                          "algorithmic_bytes_per_launch": int(db)},
                             "kernel_level": "hip-gfx950-decode-v1"}
+        n_draft = 4
+        draft = {}
+        for keep in (False, True):
+            tms = time_decode_tokens(kda, torch, d, n_draft, max(args.steps, 20), args.warmup, keep)
+            tavg = sum(tms) / len(tms)
+            tb, _ = decode_algorithmic(d.num_seqs, d.H, d.dk, d.dv, d.gate == "per_key")
+            st_bytes = 2 * d.num_seqs * d.H * d.dv * d.dk * 4
+            tb = st_bytes + n_draft * (tb - st_bytes)          # state once, per-token inputs and o
+            if keep:
+                tb += n_draft * st_bytes // 2                   # one state written per token
+            tgbs = tb / (tavg * 1e-3) / 1e9
+            draft["with_token_states" if keep else "commit_only"] = {
+                "us_per_call": round(tavg * 1e3, 2), "us_per_token": round(tavg * 1e3 / n_draft, 2),
+                "hbm_GBs": round(tgbs, 1), "hbm_frac": round(tgbs / HBM_PEAK_GBS, 4),
+                "algorithmic_bytes_per_launch": int(tb)}
+        result["decode_tokens"] = {"workload": f"{d.name}_x{n_draft}_tokens", "tokens_per_sequence": n_draft,
+                                   **draft}
     if args.cpu_tokens > 0 and not args.prefill_only:
         inp = wl.make_prefill_inputs(w, dev)
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_tokens)

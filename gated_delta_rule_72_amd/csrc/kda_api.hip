@@ -276,4 +276,37 @@ int kda_decode_step(const kda_shape* shape, int32_t batch, const void* q, const 
   return KDA_OK;
 }
 
+int kda_decode_tokens(const kda_shape* shape, int32_t batch, int32_t n_tok, const void* q,
+                      const void* k, const void* v, const float* alpha, const float* beta,
+                      float* state, float* o, float* token_states, const int32_t* commit,
+                      void* hip_stream) {
+  int rc = check_shape(shape);
+  if (rc != KDA_OK) return rc;
+  if (batch < 0) return fail(KDA_ERR_ARG, "batch must be >= 0 (got %d)", batch);
+  if (n_tok < 0) return fail(KDA_ERR_ARG, "n_tok must be >= 0 (got %d)", n_tok);
+  if (batch == 0 || n_tok == 0) {
+    g_err[0] = '\0';
+    return KDA_OK;
+  }
+  if ((int64_t)batch * shape->num_heads > INT32_MAX / 2 ||
+      (int64_t)batch * n_tok * shape->num_heads > INT32_MAX / 2)
+    return fail(KDA_ERR_SHAPE, "batch * n_tok * num_heads too large");
+  if (!q || !k || !v || !alpha || !beta || !state || !o)
+    return fail(KDA_ERR_ARG, "q, k, v, alpha, beta, state and o must be non-NULL");
+  const uintptr_t a_qkv = shape->qkv_dtype == KDA_BF16 ? 8 : 16;
+  const uintptr_t a_alpha = shape->gate == KDA_GATE_PER_KEY ? 16 : 4;
+  const PtrReq reqs[] = {{q, a_qkv, "q"}, {k, a_qkv, "k"}, {v, 4, "v"}, {alpha, a_alpha, "alpha"},
+                         {beta, 4, "beta"}, {state, 16, "state"}, {o, 4, "o"},
+                         {token_states, 16, "token_states"}, {commit, 4, "commit"}};
+  rc = check_align(reqs, (int)(sizeof reqs / sizeof reqs[0]));
+  if (rc != KDA_OK) return rc;
+  kda::DecodeArgs a{q, k, v, alpha, beta, state, o, batch, shape->num_heads, n_tok, token_states, commit};
+  hipError_t e = kda::launch_decode_tokens(a, shape->d_k, shape->qkv_dtype == KDA_BF16,
+                                           shape->gate == KDA_GATE_PER_KEY,
+                                           static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "decode launch failed: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return KDA_OK;
+}
+
 }  // extern "C"

@@ -73,7 +73,10 @@ __device__ __forceinline__ float group_allreduce(float x) {
   return x;
 }
 
-template <int D, bool BF16, bool PER_KEY>
+// MULTI: n_tok tokens per sequence ([batch, n_tok, H, d] inputs), the state
+// kept in registers between them; the state after token t goes to
+// token_states (if given) and, for t + 1 == commit, back to `state`.
+template <int D, bool BF16, bool PER_KEY, bool MULTI>
 __global__ __launch_bounds__(D * 2) void decode_kernel(DecodeArgs a) {
   constexpr int LPR = D / 4;      // lanes per state row
   constexpr int G = 64 / LPR;     // rows side by side in a wavefront
@@ -81,22 +84,11 @@ __global__ __launch_bounds__(D * 2) void decode_kernel(DecodeArgs a) {
   static_assert(2 * R == LPR, "one reduced value per lane");
 
   const int bh = blockIdx.x;      // (sequence, head) = b * H + h
+  const int b = bh / a.H, h = bh % a.H;
   const int wave = threadIdx.x / 64;
   const int lane = threadIdx.x % 64;
   const int g = lane / LPR;       // lane group within the wavefront
   const int li = lane % LPR;      // lane within the group; owns columns 4li..4li+3
-
-  const int64_t vec_off = (int64_t)bh * D;
-  const f32x4 kv = load4<BF16>(a.k, vec_off + 4 * li);
-  const f32x4 qv = load4<BF16>(a.q, vec_off + 4 * li);
-  f32x4 av;
-  if constexpr (PER_KEY) {
-    av = *reinterpret_cast<const f32x4*>(a.alpha + vec_off + 4 * li);
-  } else {
-    const float s = a.alpha[bh];
-    av = f32x4{s, s, s, s};
-  }
-  const float beta = a.beta[bh];
 
   // rows of this lane group: wave*32 + r*G + g, r = 0..R-1
   float* state = a.state + (int64_t)bh * D * D;
@@ -107,56 +99,88 @@ __global__ __launch_bounds__(D * 2) void decode_kernel(DecodeArgs a) {
     s[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(state + (int64_t)row * D + 4 * li));
   }
 
-  float kq = kv[0] * qv[0] + kv[1] * qv[1] + kv[2] * qv[2] + kv[3] * qv[3];
-  kq = group_allreduce<LPR>(kq);
+  const int n_tok = MULTI ? a.n_tok : 1;
+  int commit = n_tok;
+  if (MULTI && a.commit) commit = min(max(a.commit[b], 0), n_tok);
 
-  float vals[2 * R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    s[r] = s[r] * av;
-    vals[2 * r] = s[r][0] * kv[0] + s[r][1] * kv[1] + s[r][2] * kv[2] + s[r][3] * kv[3];
-    vals[2 * r + 1] = s[r][0] * qv[0] + s[r][1] * qv[1] + s[r][2] * qv[2] + s[r][3] * qv[3];
-  }
-  // lane li = 2r holds p_r, lane li = 2r+1 holds (s'_r . q)
-  const float red = reduce_scatter<2 * R>(vals, li);
-  const int my_r = li >> 1;
-  const int my_row = wave * 32 + my_r * G + g;
-  float u = 0.f;
-  if ((li & 1) == 0) u = beta * (load1<BF16>(a.v, vec_off + my_row) - red);
-  const float u_pair = xor_lane<1>(u);
-  if (li & 1) a.o[vec_off + my_row] = red + u_pair * kq;
-
-  // u of row r sits in lane 2r of each lane group: read it wave-wide and keep
-  // the copy of this lane's group
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    float ur = 0.f;
-#pragma unroll
-    for (int gg = 0; gg < G; ++gg) {
-      const float x = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u), gg * LPR + 2 * r));
-      if (g == gg) ur = x;
+  for (int t = 0; t < n_tok; ++t) {
+    const int64_t tok = MULTI ? ((int64_t)b * n_tok + t) * a.H + h : bh;   // (sequence, token, head)
+    const int64_t vec_off = tok * D;
+    const f32x4 kv = load4<BF16>(a.k, vec_off + 4 * li);
+    const f32x4 qv = load4<BF16>(a.q, vec_off + 4 * li);
+    f32x4 av;
+    if constexpr (PER_KEY) {
+      av = *reinterpret_cast<const f32x4*>(a.alpha + vec_off + 4 * li);
+    } else {
+      const float x = a.alpha[tok];
+      av = f32x4{x, x, x, x};
     }
-    const int row = wave * 32 + r * G + g;
-    const f32x4 upd = s[r] + ur * kv;
-    __builtin_nontemporal_store(upd, reinterpret_cast<f32x4*>(state + (int64_t)row * D + 4 * li));
+    const float beta = a.beta[tok];
+
+    float kq = kv[0] * qv[0] + kv[1] * qv[1] + kv[2] * qv[2] + kv[3] * qv[3];
+    kq = group_allreduce<LPR>(kq);
+
+    float vals[2 * R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      s[r] = s[r] * av;
+      vals[2 * r] = s[r][0] * kv[0] + s[r][1] * kv[1] + s[r][2] * kv[2] + s[r][3] * kv[3];
+      vals[2 * r + 1] = s[r][0] * qv[0] + s[r][1] * qv[1] + s[r][2] * qv[2] + s[r][3] * qv[3];
+    }
+    // lane li = 2r holds p_r, lane li = 2r+1 holds (s'_r . q)
+    const float red = reduce_scatter<2 * R>(vals, li);
+    const int my_r = li >> 1;
+    const int my_row = wave * 32 + my_r * G + g;
+    float u = 0.f;
+    if ((li & 1) == 0) u = beta * (load1<BF16>(a.v, vec_off + my_row) - red);
+    const float u_pair = xor_lane<1>(u);
+    if (li & 1) a.o[vec_off + my_row] = red + u_pair * kq;
+
+    // u of row r sits in lane 2r of each lane group: read it wave-wide and keep
+    // the copy of this lane's group
+    float* snap = (MULTI && a.token_states) ? a.token_states + tok * D * D : nullptr;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float ur = 0.f;
+#pragma unroll
+      for (int gg = 0; gg < G; ++gg) {
+        const float x = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u), gg * LPR + 2 * r));
+        if (g == gg) ur = x;
+      }
+      s[r] = s[r] + ur * kv;
+      const int row = wave * 32 + r * G + g;
+      if (MULTI && snap)
+        __builtin_nontemporal_store(s[r], reinterpret_cast<f32x4*>(snap + (int64_t)row * D + 4 * li));
+      if (t + 1 == commit)
+        __builtin_nontemporal_store(s[r], reinterpret_cast<f32x4*>(state + (int64_t)row * D + 4 * li));
+    }
   }
 }
 
-template <int D, bool BF16, bool PK>
+template <int D, bool BF16, bool PK, bool MULTI>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((decode_kernel<D, BF16, PK>), dim3(a.batch * a.H), dim3(D * 2), 0, s, a);
+  hipLaunchKernelGGL((decode_kernel<D, BF16, PK, MULTI>), dim3(a.batch * a.H), dim3(D * 2), 0, s, a);
   return hipGetLastError();
+}
+
+template <bool MULTI>
+hipError_t launch_any(const DecodeArgs& a, int d, bool bf16, bool per_key, hipStream_t s) {
+  if (d == 64) {
+    if (bf16) return per_key ? launch_t<64, true, true, MULTI>(a, s) : launch_t<64, true, false, MULTI>(a, s);
+    return per_key ? launch_t<64, false, true, MULTI>(a, s) : launch_t<64, false, false, MULTI>(a, s);
+  }
+  if (bf16) return per_key ? launch_t<128, true, true, MULTI>(a, s) : launch_t<128, true, false, MULTI>(a, s);
+  return per_key ? launch_t<128, false, true, MULTI>(a, s) : launch_t<128, false, false, MULTI>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, bool per_key, hipStream_t s) {
-  if (d == 64) {
-    if (bf16) return per_key ? launch_t<64, true, true>(a, s) : launch_t<64, true, false>(a, s);
-    return per_key ? launch_t<64, false, true>(a, s) : launch_t<64, false, false>(a, s);
-  }
-  if (bf16) return per_key ? launch_t<128, true, true>(a, s) : launch_t<128, true, false>(a, s);
-  return per_key ? launch_t<128, false, true>(a, s) : launch_t<128, false, false>(a, s);
+  return launch_any<false>(a, d, bf16, per_key, s);
+}
+
+hipError_t launch_decode_tokens(const DecodeArgs& a, int d, bool bf16, bool per_key, hipStream_t s) {
+  return launch_any<true>(a, d, bf16, per_key, s);
 }
 
 }  // namespace kda

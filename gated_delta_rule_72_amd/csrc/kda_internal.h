@@ -48,8 +48,12 @@ struct DecodeArgs {
   const float *alpha, *beta;
   float *state, *o;
   int32_t batch, H;
+  int32_t n_tok;             // tokens per sequence (multi-token path)
+  float* token_states;       // [batch, n_tok, H, dv, dk] or null
+  const int32_t* commit;     // [batch] tokens to commit to `state`, or null (all)
 };
 hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, bool per_key, hipStream_t s);
+hipError_t launch_decode_tokens(const DecodeArgs& a, int d, bool bf16, bool per_key, hipStream_t s);
 
 // One unit of prefill work: a contiguous run of chunks of one sequence (the
 // whole sequence, or one segment of it).

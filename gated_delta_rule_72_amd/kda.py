@@ -53,6 +53,7 @@ def load() -> ctypes.CDLL:
         "kda_prefill_chunked": ([P, I32, P, P, I32, I64, I64, P, P, P, P, P, P, P, P, P, P, SZ, P],
                                 ctypes.c_int),
         "kda_decode_step": ([P, I32, P, P, P, P, P, P, P, P], ctypes.c_int),
+        "kda_decode_tokens": ([P, I32, I32, P, P, P, P, P, P, P, P, P, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -63,7 +64,7 @@ def load() -> ctypes.CDLL:
 
 
 EXPORTED = ("kda_abi_version", "kda_last_error", "kda_snapshot_count", "kda_prefill_workspace_size",
-            "kda_prefill_chunked", "kda_decode_step")
+            "kda_prefill_chunked", "kda_decode_step", "kda_decode_tokens")
 
 
 def _check(fn: str, rc: int) -> None:
@@ -136,6 +137,14 @@ def kda_decode_step(shape: KdaShape, batch: int, q, k, v, alpha, beta, state, o,
         _ptr(state), _ptr(o), s))
 
 
+def kda_decode_tokens(shape: KdaShape, batch: int, n_tok: int, q, k, v, alpha, beta, state, o,
+                      token_states=None, commit=None, stream=None) -> None:
+    s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream_ptr(q.device)
+    _check("kda_decode_tokens", load().kda_decode_tokens(
+        ctypes.byref(shape), int(batch), int(n_tok), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
+        _ptr(state), _ptr(o), _ptr(token_states), _ptr(commit), s))
+
+
 # ---- convenience wrappers: allocate outputs with torch, then call the ABI ----
 
 def _contig(*ts):
@@ -192,3 +201,23 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.
         o = torch.empty((B, H, dv), dtype=torch.float32, device=q.device)
     kda_decode_step(shape, B, q, k, v, alpha, beta, state, o)
     return o
+
+
+def decode_tokens(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
+                  beta: torch.Tensor, state: torch.Tensor, commit: Optional[torch.Tensor] = None,
+                  keep_token_states: bool = False, o: Optional[torch.Tensor] = None):
+    """Several tokens per sequence: q, k [B,n,H,dk], v [B,n,H,dv], alpha [B,n,H(,dk)],
+    beta [B,n,H]; `state` [B,H,dv,dk] fp32 receives the state after the first
+    commit[b] tokens (all when commit is None; int32 [B] on the device).
+    Returns (o [B,n,H,dv], token_states [B,n,H,dv,dk] or None)."""
+    B, n, H, dk = q.shape
+    dv = v.shape[3]
+    _contig(q, k, v, alpha, beta, state, commit)
+    shape = make_shape(H, dk, dv, q.dtype, alpha.dim() == 4)
+    if o is None:
+        o = torch.empty((B, n, H, dv), dtype=torch.float32, device=q.device)
+    ts = torch.empty((B, n, H, dv, dk), dtype=torch.float32, device=q.device) if keep_token_states else None
+    if commit is not None and commit.dtype != torch.int32:
+        raise TypeError("commit must be int32")
+    kda_decode_tokens(shape, B, n, q, k, v, alpha, beta, state, o, ts, commit)
+    return o, ts

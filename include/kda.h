@@ -153,6 +153,34 @@ int kda_decode_step(const kda_shape* shape, int32_t batch,
                     const float* alpha, const float* beta,
                     float* state, float* o, void* hip_stream);
 
+/* Several new tokens per sequence in one call -- a speculative draft, or a
+ * short extension of a prompt -- with the state after every token kept for
+ * rollback (page "Modele hybrydowe: co Gated DeltaNet zastępuje w cache KV",
+ * trefon.com, section "Co stan rekurencyjny zmienia przy serwowaniu", item 2:
+ * once the state has absorbed draft tokens that are then rejected, the
+ * engine needs the state from before them back). Each token is exactly one
+ * kda_decode_step; the state stays on chip between the tokens of a call.
+ * q, k: [batch, n_tok, H, d_k]; v: [batch, n_tok, H, d_v]; alpha:
+ * [batch, n_tok, H] or [batch, n_tok, H, d_k]; beta: [batch, n_tok, H]
+ * (token-major within each sequence, i.e. a varlen pack of equal lengths).
+ * state: [batch, H, d_v, d_k], read; overwritten with the state after the
+ *   first commit[b] tokens of sequence b (left untouched where that is 0).
+ * o: [batch, n_tok, H, d_v], written for every token.
+ * token_states: NULL, or [batch, n_tok, H, d_v, d_k]: the state after each
+ *   token (16-byte aligned).
+ * commit: NULL (commit all n_tok tokens), or device int32 [batch]; values
+ *   are clamped to [0, n_tok]. Two ways to roll back: run the draft with
+ *   commit = 0 (scores only, state unchanged) and then rerun the accepted
+ *   prefix with commit = its length; or run once with token_states and keep
+ *   the state of the last accepted token.
+ * batch == 0 or n_tok == 0 is a no-op. Alignment as kda_decode_step;
+ * commit 4 bytes. */
+int kda_decode_tokens(const kda_shape* shape, int32_t batch, int32_t n_tok,
+                      const void* q, const void* k, const void* v,
+                      const float* alpha, const float* beta,
+                      float* state, float* o, float* token_states, const int32_t* commit,
+                      void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

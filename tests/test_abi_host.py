@@ -39,7 +39,8 @@ def K():
 def test_kda_header_symbols_exported(K):
     names = _declared("kda.h")
     assert set(names) == {"kda_abi_version", "kda_last_error", "kda_snapshot_count",
-                          "kda_prefill_workspace_size", "kda_prefill_chunked", "kda_decode_step"}
+                          "kda_prefill_workspace_size", "kda_prefill_chunked", "kda_decode_step",
+                          "kda_decode_tokens"}
     lib = ctypes.CDLL(K.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -187,6 +188,26 @@ def test_decode_host_rejections(K):
     assert call(bf, 2, alpha=0x4004) == K.KDA_ERR_ALIGN  # per-key alpha: 16 B
     bad = K.make_shape(4, 64, 128, torch.bfloat16, True)
     assert call(bad, 2) == K.KDA_ERR_SHAPE
+
+
+def test_decode_tokens_host_rejections(K):
+    lib = K.load()
+
+    def call(sh, batch, n, **kw):
+        p = dict(q=0x1000, k=0x2000, v=0x3000, alpha=0x4000, beta=0x5000, state=0x6000, o=0x7000,
+                 ts=None, commit=None)
+        p.update(kw)
+        a = [None if p[x] is None else _fake(p[x]) for x in ("q", "k", "v", "alpha", "beta", "state", "o", "ts",
+                                                            "commit")]
+        return lib.kda_decode_tokens(ctypes.byref(sh), batch, n, *a, None)
+
+    bf = K.make_shape(4, 128, 128, torch.bfloat16, True)
+    assert call(bf, 0, 4) == K.KDA_OK and call(bf, 3, 0) == K.KDA_OK      # nothing to do
+    assert call(bf, 2, -1) == K.KDA_ERR_ARG
+    assert call(bf, 2, 4, o=None) == K.KDA_ERR_ARG
+    assert call(bf, 2, 4, ts=0x8008) == K.KDA_ERR_ALIGN
+    assert call(bf, 2, 4, commit=0x9002) == K.KDA_ERR_ALIGN
+    assert call(bf, 1 << 20, 1 << 10) == K.KDA_ERR_SHAPE
 
 
 def test_binding_fails_loudly_without_library(K, monkeypatch, tmp_path):

@@ -1,0 +1,137 @@
+"""GPU parity of kda_decode_tokens (several tokens per sequence, per-token
+states, commit / rollback) against the fp64 CPU oracle, through the C ABI.
+
+The oracle runs the same tokens as a varlen pack of equal lengths with a
+snapshot after every token (interval 1): its snapshots are the per-token
+states, in the same [sequence, token] order.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_72_amd as kda
+import oracle
+from gated_delta_rule_72_amd import workloads as wl
+
+from gpu_util import O_TOL, STATE_TOL, custom, device
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(B, n, H, d, gate, dtype, seed):
+    w = custom(f"draft_{B}x{n}", H=H, d=d, lens=(n,) * B, gate=gate, dtype=dtype, seed=seed)
+    inp = wl.make_prefill_inputs(w, device())
+    view = {x: inp[x].view(B, n, *inp[x].shape[1:]) for x in ("q", "k", "v", "alpha", "beta")}
+    return w, inp, view
+
+
+def _oracle_check(inp, o, state, token_states, heads=None):
+    """o [B,n,H,dv], state (all tokens committed), token_states [B,n,H,dv,dk]."""
+    T, H = inp["q"].shape[:2]
+    hs = list(range(H)) if heads is None else list(heads)
+    idx = torch.tensor(hs, device=inp["q"].device)
+    sel = lambda t, ax: t.index_select(ax, idx)  # noqa: E731
+    A = {x: wl.to_oracle_arrays(sel(inp[x], 1)) for x in ("q", "k", "v", "alpha", "beta")}
+    rc, rep = oracle.ref_check(A["q"], A["k"], A["v"], A["alpha"], A["beta"], inp["cu_seqlens_host"].numpy(),
+                               sel(inp["initial_state"], 1).cpu().numpy(), 1,
+                               sel(o.reshape(T, H, -1), 1).cpu().numpy(), sel(state, 1).cpu().numpy(),
+                               sel(token_states.reshape(T, H, *token_states.shape[3:]), 1).cpu().numpy(),
+                               O_TOL, STATE_TOL)
+    print(f"oracle report: {rep}", flush=True)
+    assert rc == oracle.OK, rep
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("gate", ["scalar", "per_key"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_decode_tokens_small(d, gate, dtype):
+    B, n, H = 5, 4, 3
+    w, inp, x = _inputs(B, n, H, d, gate, dtype, seed=31)
+    state = inp["initial_state"].clone()
+    o, ts = kda.decode_tokens(x["q"], x["k"], x["v"], x["alpha"], x["beta"], state, keep_token_states=True)
+    torch.cuda.synchronize()
+    _oracle_check(inp, o, state, ts)
+    # the same call with per-sequence commit counts: the state after commit[b]
+    # tokens (untouched for 0), the same outputs, bit for bit
+    commit = torch.tensor([0, 1, 4, 2, 3], dtype=torch.int32, device=state.device)
+    state2 = inp["initial_state"].clone()
+    o2, _ = kda.decode_tokens(x["q"], x["k"], x["v"], x["alpha"], x["beta"], state2, commit=commit)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o)
+    for b, c in enumerate(commit.tolist()):
+        want = inp["initial_state"][b] if c == 0 else ts[b, c - 1]
+        assert torch.equal(state2[b], want), (b, c)
+
+
+def test_one_token_equals_decode_step_bitwise():
+    B, H, d = 7, 4, 128
+    w, inp, x = _inputs(B, 1, H, d, "per_key", "bf16", seed=32)
+    s_a = inp["initial_state"].clone()
+    s_b = inp["initial_state"].clone()
+    o_a, _ = kda.decode_tokens(x["q"], x["k"], x["v"], x["alpha"], x["beta"], s_a)
+    o_b = kda.decode_step(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], s_b)
+    torch.cuda.synchronize()
+    assert torch.equal(o_a[:, 0], o_b) and torch.equal(s_a, s_b)
+
+
+def test_tokens_equal_sequential_decode_steps_bitwise():
+    B, n, H, d = 6, 3, 2, 64
+    w, inp, x = _inputs(B, n, H, d, "scalar", "bf16", seed=33)
+    s_a = inp["initial_state"].clone()
+    o_a, _ = kda.decode_tokens(x["q"], x["k"], x["v"], x["alpha"], x["beta"], s_a)
+    s_b = inp["initial_state"].clone()
+    for t in range(n):
+        step = {y: x[y][:, t].contiguous() for y in x}
+        o_t = kda.decode_step(step["q"], step["k"], step["v"], step["alpha"], step["beta"], s_b)
+        torch.cuda.synchronize()
+        assert torch.equal(o_a[:, t], o_t), t
+    assert torch.equal(s_a, s_b)
+
+
+def test_draft_then_commit_rolls_back():
+    """Score a 4-token draft without touching the state (commit 0), then
+    commit the accepted prefix: the result equals the state after that many
+    tokens."""
+    B, n, H, d = 8, 4, 2, 128
+    w, inp, x = _inputs(B, n, H, d, "per_key", "bf16", seed=34)
+    dev = inp["q"].device
+    ref_state = inp["initial_state"].clone()
+    o_ref, ts = kda.decode_tokens(x["q"], x["k"], x["v"], x["alpha"], x["beta"], ref_state,
+                                  keep_token_states=True)
+    state = inp["initial_state"].clone()
+    o_draft, _ = kda.decode_tokens(x["q"], x["k"], x["v"], x["alpha"], x["beta"], state,
+                                   commit=torch.zeros(B, dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+    assert torch.equal(state, inp["initial_state"]) and torch.equal(o_draft, o_ref)
+    accepted = torch.tensor([2, 0, 4, 1, 3, 2, 4, 0], dtype=torch.int32, device=dev)
+    kda.decode_tokens(x["q"], x["k"], x["v"], x["alpha"], x["beta"], state, commit=accepted)
+    torch.cuda.synchronize()
+    for b, c in enumerate(accepted.tolist()):
+        want = inp["initial_state"][b] if c == 0 else ts[b, c - 1]
+        assert torch.equal(state[b], want), (b, c)
+
+
+def test_out_of_range_commit_is_clamped():
+    B, n, H, d = 3, 2, 2, 64
+    w, inp, x = _inputs(B, n, H, d, "scalar", "fp32", seed=35)
+    dev = inp["q"].device
+    ref = inp["initial_state"].clone()
+    _, ts = kda.decode_tokens(x["q"], x["k"], x["v"], x["alpha"], x["beta"], ref, keep_token_states=True)
+    state = inp["initial_state"].clone()
+    kda.decode_tokens(x["q"], x["k"], x["v"], x["alpha"], x["beta"], state,
+                      commit=torch.tensor([-3, 9, 1], dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+    assert torch.equal(state[0], inp["initial_state"][0])
+    assert torch.equal(state[1], ts[1, n - 1])
+    assert torch.equal(state[2], ts[2, 0])
+
+
+def test_draft_full_size_sampled_heads():
+    """B=256 sequences x 4 draft tokens, H=16, d=128, per-key alpha: heads 0
+    and 11 of every sequence against the oracle, every per-token state."""
+    B, n, H, d = 256, 4, 16, 128
+    w, inp, x = _inputs(B, n, H, d, "per_key", "bf16", seed=36)
+    state = inp["initial_state"].clone()
+    o, ts = kda.decode_tokens(x["q"], x["k"], x["v"], x["alpha"], x["beta"], state, keep_token_states=True)
+    torch.cuda.synchronize()
+    _oracle_check(inp, o, state, ts, heads=(0, 11))
