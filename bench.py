@@ -127,7 +127,7 @@ def measure_ceilings(torch, reps: int = 5) -> dict:
                    "fp16 16x16x32 MFMA loop, 1024 workgroups x 4 wavefronts x 8 independent chains"}
 
 
-def time_prefill(kda, torch, inp, w, steps, warmup):
+def time_prefill(kda, torch, inp, w, steps, warmup, snaps_on_host=False):
     T, H, dk, dv = w.T, w.H, w.dk, w.dv
     dev = inp["q"].device
     shape = kda.make_shape(H, dk, dv, inp["q"].dtype, w.gate == "per_key")
@@ -135,7 +135,10 @@ def time_prefill(kda, torch, inp, w, steps, warmup):
     o = torch.empty((T, H, dv), dtype=torch.float32, device=dev)
     fin = torch.empty((w.num_seqs, H, dv, dk), dtype=torch.float32, device=dev)
     n_snap = kda.kda_snapshot_count(cu_h, w.interval)
-    snaps = torch.empty((n_snap, H, dv, dk), dtype=torch.float32, device=dev) if n_snap else None
+    snaps = None
+    if n_snap:
+        snaps = (torch.empty((n_snap, H, dv, dk), dtype=torch.float32, pin_memory=True) if snaps_on_host
+                 else torch.empty((n_snap, H, dv, dk), dtype=torch.float32, device=dev))
     ws = torch.empty(max(kda.kda_prefill_workspace_size(shape, cu_h, 64, w.interval), 1),
                      dtype=torch.uint8, device=dev)
 
@@ -342,6 +345,10 @@ def main(argv=None):
                               "hbm_GBs": round(ogbs, 1), "hbm_frac": round(ogbs / HBM_PEAK_GBS, 4),
                               "mfma_frac": round(of / (oavg * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
                               "algorithmic_bytes": int(ob), "algorithmic_flops": int(of), "calls": len(oms)}
+            if on_snap:
+                hms, _ = time_prefill(kda, torch, oinp, ow, max(5, args.steps // 2), args.warmup, snaps_on_host=True)
+                other[ow.name]["ms_per_call_snapshots_to_pinned_host"] = round(sum(hms) / len(hms), 4)
+                other[ow.name]["snapshot_bytes_to_host"] = on_snap * ow.H * ow.dv * ow.dk * 4
             del oinp
             torch.cuda.empty_cache()
         result["other_prefill"] = other

@@ -75,6 +75,28 @@ int64_t snapshot_slots(int32_t num_seqs, const int64_t* cu, int64_t interval) {
   return total;
 }
 
+// The snapshots buffer may be device memory or pinned host memory (then the
+// kernels write the states over the bus while the prefill runs). Resolves
+// the address the kernels use; pageable host memory is rejected.
+int resolve_snapshots(float* p, float** dev_p) {
+  hipPointerAttribute_t attr;
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(KDA_ERR_ARG, "snapshots (%p) is neither device memory nor pinned host memory", (void*)p);
+  }
+  if (attr.type == hipMemoryTypeHost) {
+    if (!attr.devicePointer)
+      return fail(KDA_ERR_ARG, "snapshots (%p): pinned host memory not mapped for the device", (void*)p);
+    *dev_p = static_cast<float*>(attr.devicePointer);
+    return KDA_OK;
+  }
+  if (attr.type == hipMemoryTypeDevice || attr.type == hipMemoryTypeManaged) {
+    *dev_p = p;
+    return KDA_OK;
+  }
+  return fail(KDA_ERR_ARG, "snapshots (%p) is neither device memory nor pinned host memory", (void*)p);
+}
+
 int device_cu_count() {
   static int cached[64] = {0};
   int dev = 0;
@@ -223,10 +245,15 @@ int kda_prefill_chunked(const kda_shape* shape, int32_t num_seqs,
     g_err[0] = '\0';
     return KDA_OK;
   }
+  float* snaps_dev = nullptr;
+  if (n_snap > 0) {
+    rc = resolve_snapshots(snapshots, &snaps_dev);
+    if (rc != KDA_OK) return rc;
+  }
 
   kda::PrefillArgs a{};
   a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.init = initial_state;
-  a.o = o; a.final_state = final_state; a.snapshots = snapshots;
+  a.o = o; a.final_state = final_state; a.snapshots = snaps_dev;
   a.cu_dev = cu_seqlens_dev;
   a.num_seqs = num_seqs;
   a.H = shape->num_heads;

@@ -13,6 +13,12 @@
 // The step reads and writes each state element exactly once; the kernel is
 // bound by HBM bandwidth (about 0.86 flop per byte).
 //
+// Several tokens per sequence (kda_decode_tokens: a speculative draft) run the
+// same step in a loop with the state held in registers; the state after each
+// token can be written out (rollback points, same page, section "Co stan
+// rekurencyjny zmienia przy serwowaniu", item 2) and the state after a chosen
+// prefix goes back to HBM.
+//
 // Mapping (D = d_k = d_v in {64, 128}): one workgroup per (sequence, head),
 // D/32 wavefronts, 32 state rows per wavefront. A row is D/4 lanes wide (one
 // 16-byte float4 per lane), so a wavefront holds G = 256/D rows side by side

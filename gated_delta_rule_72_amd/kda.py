@@ -158,10 +158,13 @@ def prefill_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: to
                     initial_state: Optional[torch.Tensor] = None, snapshot_interval: int = 0,
                     cu_seqlens_host: Optional[torch.Tensor] = None, chunk: int = CHUNK,
                     segment_tokens: int = -1,
-                    out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None):
+                    out: Optional[Tuple[torch.Tensor, torch.Tensor, torch.Tensor]] = None,
+                    snapshots_on_host: bool = False):
     """q, k [T,H,dk], v [T,H,dv] (bf16/fp32), alpha [T,H] or [T,H,dk], beta [T,H]
     (fp32). cu_seqlens: int64 [N+1] (default: one sequence of length T).
     segment_tokens: -1 automatic segment plan, 0 none, > 0 segment length.
+    snapshots_on_host: snapshots go to pinned host memory, written by the
+    kernels during the prefill.
     Returns (o [T,H,dv] fp32, final_state [N,H,dv,dk], snapshots [S,H,dv,dk])."""
     T, H, dk = q.shape
     dv = v.shape[2]
@@ -179,9 +182,14 @@ def prefill_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: to
     if out is None:
         o = torch.empty((T, H, dv), dtype=torch.float32, device=dev)
         fin = torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev)
-        snaps = torch.empty((n_snap, H, dv, dk), dtype=torch.float32, device=dev)
+        if snapshots_on_host:
+            snaps = torch.empty((n_snap, H, dv, dk), dtype=torch.float32, pin_memory=True)
+        else:
+            snaps = torch.empty((n_snap, H, dv, dk), dtype=torch.float32, device=dev)
     else:
         o, fin, snaps = out
+    if snaps is not None and snaps.numel() and snaps.device.type == "cpu" and not snaps.is_pinned():
+        raise ValueError("host snapshots must be pinned memory (pin_memory=True)")
     ws_bytes = kda_prefill_workspace_size(shape, cu_seqlens_host, chunk, snapshot_interval, segment_tokens)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     kda_prefill_chunked(shape, cu_seqlens_host, cu_dev, q, k, v, alpha, beta, initial_state, o, fin,

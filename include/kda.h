@@ -129,7 +129,13 @@ int kda_prefill_workspace_size(const kda_shape* shape, int32_t num_seqs,
  * initial_state: [num_seqs, H, d_v, d_k] or NULL (zeros). May alias
  *   final_state.
  * o: [T, H, d_v] (must not alias inputs); final_state: [num_seqs, H, d_v, d_k];
- * snapshots: NULL iff the slot count is 0.
+ * snapshots: NULL iff the slot count is 0. Device memory, or pinned host
+ *   memory (hipHostMalloc; torch pin_memory=True): the kernels then write the
+ *   snapshot states over the bus while the prefill runs, which offloads them
+ *   to host RAM for prefix reuse without a separate copy (same page, section
+ *   "Co stan rekurencyjny zmienia przy serwowaniu", item 1 and the rule on
+ *   planning host memory for checkpoints). Pageable host memory is rejected
+ *   with KDA_ERR_ARG.
  * workspace: device memory of at least kda_prefill_workspace_size bytes.
  */
 int kda_prefill_chunked(const kda_shape* shape, int32_t num_seqs,

@@ -210,3 +210,33 @@ def test_initial_state_may_alias_final_state(segment_tokens):
     torch.cuda.synchronize()
     assert torch.equal(o, o_ref)
     assert torch.equal(state, f_ref)
+
+
+def test_snapshots_to_pinned_host_memory_bitwise():
+    """Snapshots written straight into pinned host memory by the kernels equal
+    the device-memory snapshots bit for bit (segmented and plain plans)."""
+    dev = device()
+    w = custom("host_snaps", H=4, d=128, lens=(3000, 64, 0, 1300), gate="per_key", interval=128, seed=19)
+    inp = wl.make_prefill_inputs(w, dev)
+    for seg in (0, -1):
+        o_d, f_d, s_d = run_prefill(inp, w.interval, seg)
+        o_h, f_h, s_h = kda.prefill_chunked(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"],
+                                            inp["cu_seqlens"], inp["initial_state"], w.interval,
+                                            cu_seqlens_host=inp["cu_seqlens_host"], segment_tokens=seg,
+                                            snapshots_on_host=True)
+        torch.cuda.synchronize()
+        assert s_h.device.type == "cpu" and s_h.is_pinned()
+        assert torch.equal(s_h, s_d.cpu()) and torch.equal(o_h, o_d) and torch.equal(f_h, f_d)
+
+
+def test_pageable_host_snapshots_rejected_by_binding():
+    dev = device()
+    w = custom("pageable", H=1, d=64, lens=(128,), gate="scalar", interval=64, seed=20)
+    inp = wl.make_prefill_inputs(w, dev)
+    o = torch.empty((128, 1, 64), dtype=torch.float32, device=dev)
+    fin = torch.empty((1, 1, 64, 64), dtype=torch.float32, device=dev)
+    snaps = torch.empty((2, 1, 64, 64), dtype=torch.float32)          # pageable
+    with pytest.raises(ValueError):
+        kda.prefill_chunked(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["cu_seqlens"],
+                            inp["initial_state"], w.interval, cu_seqlens_host=inp["cu_seqlens_host"],
+                            out=(o, fin, snaps))
