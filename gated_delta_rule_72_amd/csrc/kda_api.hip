@@ -115,7 +115,7 @@ int device_cu_count() {
 // chain in one workgroup.
 struct PrefillPlan {
   int32_t seg_chunks, n_items;
-  size_t items_off, first_off, maps_off, states_off, bytes;
+  size_t items_off, first_off, maps_off, states_off, inverse_off, bytes;
 };
 
 PrefillPlan plan_prefill(const kda_shape* s, int32_t num_seqs, const int64_t* cu,
@@ -159,6 +159,8 @@ PrefillPlan plan_prefill(const kda_shape* s, int32_t num_seqs, const int64_t* cu
   if (seg > 0) off += round_up((size_t)items * H * 2 * DD * sizeof(float));
   p.states_off = off;
   if (seg > 0) off += round_up((size_t)items * H * DD * sizeof(float));
+  p.inverse_off = off;
+  if (seg > 0) off += round_up((size_t)items * H * (size_t)seg * kda::kInverseBytes);
   p.bytes = off;
   return p;
 }
@@ -266,6 +268,7 @@ int kda_prefill_chunked(const kda_shape* shape, int32_t num_seqs,
   a.seq_first_item = reinterpret_cast<int32_t*>(ws + plan.first_off);
   a.seg_maps = plan.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.maps_off) : nullptr;
   a.seg_states = plan.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.states_off) : nullptr;
+  a.seg_inverse = plan.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.inverse_off) : nullptr;
   hipError_t e = kda::launch_prefill(a, shape->d_k, shape->qkv_dtype == KDA_BF16,
                                      shape->gate == KDA_GATE_PER_KEY,
                                      static_cast<hipStream_t>(hip_stream));

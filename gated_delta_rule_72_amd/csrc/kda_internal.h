@@ -82,7 +82,11 @@ struct PrefillArgs {
   int32_t* seq_first_item;   // workspace: [N] first item of each sequence (segmented)
   float* seg_maps;           // workspace: per (item, head) M (dk x dk) then N (dv x dk)
   float* seg_states;         // workspace: per (item, head) start state (dv x dk)
+  float* seg_inverse;        // workspace: per (item, head, chunk) the chunk's (I + L)^-1 block
+                             // layout as the map pass leaves it in LDS, reused by pass 3
 };
 hipError_t launch_prefill(PrefillArgs a, int d, bool bf16, bool per_key, hipStream_t s);
+// bytes of one chunk's stored inverse: 64 rows of 68 fp32 (the LDS row stride)
+constexpr size_t kInverseBytes = 64 * 68 * 4;
 
 }  // namespace kda

@@ -148,6 +148,11 @@ struct Lds {
   static constexpr int A_VT = A_TL + C * LDT * 2;
   static constexpr int A_END2 = A_VT + D * LDT * 2;
   static constexpr int A_BYTES = A_END1 > A_END2 ? A_END1 : A_END2;
+  // raw bf16 q rows of the next chunk [64][D], staged during P6 into the T~
+  // space (dead after P5) below raw K (written again in P1 after q is read)
+  static constexpr int A_QSTAGE = A_TH;
+  static_assert(A_QSTAGE + C * D * 2 <= A_RK, "q staging must not reach raw K");
+  static_assert(A_QSTAGE >= A_W + C * LDQ * 2, "q staging must not touch W");
   static constexpr int TOTAL = OFF_A + A_BYTES;
 };
 
@@ -216,6 +221,15 @@ __device__ __forceinline__ void stage_rows_lds(const uint16_t* src, uint32_t HD,
     __builtin_amdgcn_global_load_lds((gvoid_t*)gp, (lvoid_t*)(static_cast<char*>(lds) + 1024 * i),
                                      16, 0, 0);
   }
+}
+
+// A contiguous block of n_kib KiB from HBM into LDS, one KiB per wavefront
+// instruction (lane l moves bytes 16 l .. 16 l + 15 of it).
+template <int NW>
+__device__ __forceinline__ void stage_block_lds(const void* src, int n_kib, void* lds, int wave, int lane) {
+  for (int i = wave; i < n_kib; i += NW)
+    __builtin_amdgcn_global_load_lds((gvoid_t*)(static_cast<const char*>(src) + 1024 * i + 16 * lane),
+                                     (lvoid_t*)(static_cast<char*>(lds) + 1024 * i), 16, 0, 0);
 }
 
 // Registers holding one chunk's raw inputs (prefetched during the previous chunk).
@@ -362,7 +376,9 @@ void prefill_kernel(PrefillArgs a) {
   const int item_idx = blockIdx.x / a.H, h = blockIdx.x % a.H;
   const PrefillItem item = a.items[item_idx];
   if constexpr (MAP) {
-    if (item.seg >= item.n_segs - 1) return;   // the last segment needs no map (uniform)
+    // every segment of a split sequence: the maps of all but the last feed the
+    // scan, and each chunk's inverse is kept for pass 3
+    if (item.n_segs <= 1) return;                // (uniform)
   }
   constexpr bool out_mode = !MAP;
   constexpr bool need_v = true;
@@ -370,6 +386,15 @@ void prefill_kernel(PrefillArgs a) {
   // which MAP never uses), so its prefetch holds no registers across P6
   constexpr bool v_in_lds = MAP && BF16;
   constexpr bool v_in_regs = need_v && !v_in_lds;
+  // Pass 3 of a split sequence's segment: the map pass already formed
+  // each chunk's inverse (I + L)^-1 and stored it; it is loaded into the L
+  // buffer instead of being recomputed (same arithmetic, same bits).
+  static_assert(C * L::LDL * 4 == (int)kInverseBytes && kInverseBytes % 1024 == 0, "stored inverse layout");
+  constexpr int INV_KIB = (int)(kInverseBytes / 1024);
+  const bool have_inv = !MAP && a.seg_chunks > 0 && item.n_segs > 1;
+  float* inv_base = a.seg_chunks > 0
+                        ? a.seg_inverse + ((int64_t)item_idx * a.H + h) * a.seg_chunks * (int64_t)(kInverseBytes / 4)
+                        : nullptr;
   const int64_t HD = (int64_t)a.H * D;
   const int64_t DD = (int64_t)D * D;
 
@@ -417,8 +442,11 @@ void prefill_kernel(PrefillArgs a) {
                         smem + L::OFF_KHT, wave, lane);
       if constexpr (!MAP)
         stage_rows_lds<D, NW>(static_cast<const uint16_t*>(a.q) + row0, HDu, min(C, item.n_tokens),
-                          smem + L::OFF_L, wave, lane);
-      __builtin_amdgcn_s_waitcnt(0);
+                          regA + L::A_QSTAGE, wave, lane);
+    }
+    if (have_inv) stage_block_lds<NW>(inv_base, INV_KIB, smem + L::OFF_L, wave, lane);
+    if (BF16 || have_inv) {
+      __builtin_amdgcn_s_waitcnt(0);   // staged rows and the inverse have landed in LDS
       __syncthreads();
     }
   }
@@ -442,7 +470,7 @@ void prefill_kernel(PrefillArgs a) {
         // staged bf16 rows [64][D] (unpadded); rows >= n are stale and zeroed here
         const uint4 kw = *reinterpret_cast<const uint4*>(smem + L::OFF_KHT + (c * D + 8 * k8) * 2);
         const uint4 qw = MAP ? uint4{0, 0, 0, 0}
-                             : *reinterpret_cast<const uint4*>(smem + L::OFF_L + (c * D + 8 * k8) * 2);
+                             : *reinterpret_cast<const uint4*>(regA + L::A_QSTAGE + (c * D + 8 * k8) * 2);
         const uint32_t kk4[4] = {kw.x, kw.y, kw.z, kw.w}, qq4[4] = {qw.x, qw.y, qw.z, qw.w};
         const bool live = c < n;
 #pragma unroll
@@ -562,7 +590,7 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks) {
               const f16x8 ki = ld_std(sRK, L::LDQ, 16 * I, 32 * ks, lane);
-              accL = mfma_f16(ki, kr[ks], accL);
+              if (!have_inv) accL = mfma_f16(ki, kr[ks], accL);
               if constexpr (!MAP) accB = mfma_f16(ki, qr[ks], accB);
             }
             const int i0 = 16 * I + 4 * g;           // columns i0..i0+3 of row r
@@ -575,9 +603,9 @@ void prefill_kernel(PrefillArgs a) {
               lv[e] = (i0 + e < r) ? accL[e] * f * br : 0.f;
               bv[e] = (_Float16)((i0 + e <= r) ? accB[e] * f : 0.f);
             }
-            *reinterpret_cast<f32x4*>(sL + r * L::LDL + i0) = lv;
+            if (!have_inv) *reinterpret_cast<f32x4*>(sL + r * L::LDL + i0) = lv;
             if constexpr (!MAP) *reinterpret_cast<f16x4*>(sB + r * L::LDT + i0) = bv;
-            if (I == R) {
+            if (I == R && !have_inv) {
               // diagonal tile: L_RR^T also into its upper triangle (column i
               // of L_RR becomes row i there); issued after the row stores, so
               // it lands after their zeros
@@ -614,9 +642,11 @@ void prefill_kernel(PrefillArgs a) {
                 qh[e] = (__bf16)qv; ql[e] = (__bf16)(qv - (float)qh[e]);
                 ih[e] = (__bf16)iv; il[e] = (__bf16)(iv - (float)ih[e]);
               }
-              accL = mfma_bf16(ih, kh, accL);
-              accL = mfma_bf16(ih, kl, accL);
-              accL = mfma_bf16(il, kh, accL);
+              if (!have_inv) {
+                accL = mfma_bf16(ih, kh, accL);
+                accL = mfma_bf16(ih, kl, accL);
+                accL = mfma_bf16(il, kh, accL);
+              }
               if constexpr (!MAP) {
                 accB = mfma_bf16(ih, qh, accB);
                 accB = mfma_bf16(ih, ql, accB);
@@ -631,9 +661,9 @@ void prefill_kernel(PrefillArgs a) {
               lv[e] = (i0 + e < r) ? accL[e] * br : 0.f;
               bv[e] = (_Float16)((i0 + e <= r) ? accB[e] : 0.f);
             }
-            *reinterpret_cast<f32x4*>(sL + r * L::LDL + i0) = lv;
+            if (!have_inv) *reinterpret_cast<f32x4*>(sL + r * L::LDL + i0) = lv;
             if constexpr (!MAP) *reinterpret_cast<f16x4*>(sB + r * L::LDT + i0) = bv;
-            if (I == R) {
+            if (I == R && !have_inv) {
               // diagonal tile: L_RR^T also into its upper triangle (column i
               // of L_RR becomes row i there); issued after the row stores, so
               // it lands after their zeros
@@ -645,7 +675,7 @@ void prefill_kernel(PrefillArgs a) {
         }
       }
       int d0, d1;
-      if (gram_diag<NW>(wave, d0, d1)) {
+      if (!have_inv && gram_diag<NW>(wave, d0, d1)) {
         // Replace L_bb by the inverse of the unit lower block I + L_bb for the
         // two diagonal blocks this wavefront computed: lane groups 0-1 take
         // block d0, 2-3 block d1, one column j per lane (groups 0 and 2
@@ -686,7 +716,7 @@ void prefill_kernel(PrefillArgs a) {
     // on fp32 MFMA with the column's earlier blocks kept in accumulator
     // registers; A_RI is stored at block (I, R). Meanwhile every wavefront
     // stages V^T.
-    if (wave < 3) {
+    if (wave < 3 && !have_inv) {
       const int I = wave;
       f32x4 Acol[4];                                  // A_mI, m > I (accumulator layout)
 #pragma unroll
@@ -747,6 +777,13 @@ void prefill_kernel(PrefillArgs a) {
       }
     }
     __syncthreads();
+
+    if constexpr (MAP) {
+      // keep this chunk's inverse for pass 3 (the L buffer as laid out above)
+      float* dst = inv_base + (int64_t)ch * (int64_t)(kInverseBytes / 4);
+      for (int e = tid; e < (int)(kInverseBytes / 16); e += NT)
+        *reinterpret_cast<f32x4*>(dst + 4 * e) = *reinterpret_cast<const f32x4*>(sL + 4 * e);
+    }
 
     // ---- P5: T~ = A Diag(beta) as fp16 hi + lo; W = T~ (K * 2^G) ------------
     for (int e8 = tid; e8 < C * C / 8; e8 += NT) {
@@ -834,9 +871,13 @@ void prefill_kernel(PrefillArgs a) {
         stage_rows_lds<D, NW>(static_cast<const uint16_t*>(a.k) + row0, HDu, n_next, smem + L::OFF_KHT,
                           wave, lane);
         if constexpr (!MAP)
-          stage_rows_lds<D, NW>(static_cast<const uint16_t*>(a.q) + row0, HDu, n_next, smem + L::OFF_L,
+          stage_rows_lds<D, NW>(static_cast<const uint16_t*>(a.q) + row0, HDu, n_next, regA + L::A_QSTAGE,
                             wave, lane);
       }
+      // the L buffer is dead until the next chunk's P5
+      if (have_inv)
+        stage_block_lds<NW>(inv_base + (int64_t)(ch + 1) * (int64_t)(kInverseBytes / 4), INV_KIB, smem + L::OFF_L,
+                            wave, lane);
     }
 
     // ---- P6: state passing for this wavefront's slices ---------------------
@@ -952,7 +993,7 @@ void prefill_kernel(PrefillArgs a) {
             *reinterpret_cast<f32x4*>(dst + (16 * (SPW * wave + sl) + l16) * D + 16 * kt + 4 * g) = ST[sl][kt];
       }
     }
-    if constexpr (BF16) __builtin_amdgcn_s_waitcnt(0);   // staged rows have landed in LDS
+    if (BF16 || have_inv) __builtin_amdgcn_s_waitcnt(0);   // staged rows (and inverse) have landed in LDS
     __syncthreads();
   }
 
@@ -1127,7 +1168,7 @@ hipError_t launch_pass(const PrefillArgs& a, hipStream_t s) {
 template <int D, bool BF16, bool PK>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
   if (a.seg_chunks == 0) return launch_pass<D, BF16, PK, false>(a, s);
-  hipError_t e = launch_pass<D, BF16, PK, true>(a, s);          // pass 1: segment maps
+  hipError_t e = launch_pass<D, BF16, PK, true>(a, s);          // pass 1: segment maps, inverses
   if (e != hipSuccess) return e;
   constexpr int scan_lds = (D * D + 16 * D) * 4;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(segment_scan_kernel<D>),
