@@ -18,34 +18,39 @@
 // N = U'^T (K*2^(G_n-G)): a chunk, and hence a run of chunks, acts on the
 // state as an affine map.
 //
-// Kernel structure. One workgroup per (work item, head), four wavefronts (one
-// per SIMD, so each may use the full 512-entry register file). The state
-// (D = d_k = d_v rows) is cut into 16-row slices; wavefront w owns D/64 of
-// them and keeps them transposed, S0^T, in MFMA accumulator layout (fp32) for
-// the whole item. Per chunk:
-//   P1  raw q, k (fp16) and the decay cumsum G (fp32) into LDS; beta; 2^G_n.
+// Kernel structure. One workgroup per (work item, head). The state
+// (D = d_k = d_v rows) is cut into 16-row slices, one per wavefront at
+// D = 128 (eight wavefronts, two per SIMD) and two per wavefront at D = 64
+// (four wavefronts, one per SIMD); each wavefront keeps its slices
+// transposed, S0^T, in MFMA accumulator layout (fp32) for the whole item.
+// Per chunk:
+//   P1  raw q, k (fp16) from rows staged in LDS by the previous chunk, and
+//       the decay cumsum G (fp32); beta; 2^G_n.
 //   P2  decayed operands in LDS: Q~ = Q*2^G [c][k], K^T*2^G and
 //       (K*2^(G_n-G))^T [k][c] (fp16).
-//   P3  Gram tiles on MFMA: L (fp32) and B (fp16). Scalar gate: exact
+//   P3  Gram tile pairs on MFMA: L (fp32) and B (fp16). Scalar gate: exact
 //       fp16 products K K^T, Q K^T scaled by 2^(G_r-G_i) in fp32. Per-key
 //       gate: three-term bf16 products (hi*hi + hi*lo + lo*hi) of operands
 //       decayed relative to the first token of each 16-row block, so every
-//       factor stays in fp32/bf16 range.
-//   P4  (I + L)^-1 in LDS: four 16x16 unit-lower diagonal blocks by forward
-//       substitution (one column per lane), then the off-diagonal blocks in
-//       three dependent stages on fp32 MFMA.
-//   P5  T~ split into fp16 hi + lo; W = T~ (K*2^G) on MFMA.
-//   P6  per slice: U' = T~ V, U = U' - W S0^T, O = Q~ S0^T + B U,
-//       S0^T <- 2^(G_n) S0^T + (K*2^(G_n-G))^T U. U and T~ enter their
-//       products as fp16 hi + lo pairs; the state stays fp32. The next
-//       chunk's inputs are loaded into registers while P6 runs.
+//       factor stays in fp32/bf16 range. Two wavefronts then invert the four
+//       16x16 unit-lower diagonal blocks of I + L (right-looking
+//       substitution, one column per lane).
+//   P4  off-diagonal blocks of (I + L)^-1: one register-resident chain of
+//       fp32 MFMA products per block column; V^T staged in LDS.
+//   P5  T~ = (I + L)^-1 Diag(beta) split into fp16 hi + lo; W = T~ (K*2^G)
+//       and U' = T~ V on MFMA from the same T~ tiles.
+//   P6  per slice: U = U' - W S0^T, O = Q~ S0^T + B U,
+//       S0^T <- 2^(G_n) S0^T + (K*2^(G_n-G))^T U. U enters its products as
+//       fp16 hi + lo; the state stays fp32. The next chunk's inputs are
+//       fetched (q, k rows straight into LDS) while P6 runs.
 // Two instantiations: OUT (the real chain: o, snapshots, final state) and MAP
 // (a segment's affine map: each wavefront advances its N rows, the chain from
 // S0 = 0, and its M rows, the chain with v = 0 from identity rows, side by side;
 // q, Q~, B and o are skipped). Long sequences with few heads are split into
-// segments: pass 1 maps every segment but the last, a scan composes
-// S_{s+1} = S_s M_s + N_s in fp32 from the initial state, and pass 3 runs
-// every segment in OUT mode from its true start.
+// segments: pass 1 maps every segment (and keeps each chunk's inverse from
+// P3-P4), a scan composes S_{s+1} = S_s M_s + N_s in fp32 from the initial
+// state, and pass 3 runs every segment in OUT mode from its true start,
+// loading the stored inverses instead of forming L and inverting it again.
 // Accumulator layout of a 16x16 MFMA tile: lane l holds rows 4(l/16)+i,
 // column l%16. When an accumulator tile feeds the next product as its
 // K-operand, the K index is permuted (lane group g supplies rows 4g..4g+3 of
