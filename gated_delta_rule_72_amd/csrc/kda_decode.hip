@@ -109,19 +109,39 @@ __global__ __launch_bounds__(D * 2) void decode_kernel(DecodeArgs a) {
   int commit = n_tok;
   if (MULTI && a.commit) commit = min(max(a.commit[b], 0), n_tok);
 
+  // this lane's value row (lanes with even li use it)
+  const int my_r = li >> 1;
+  const int my_row = wave * 32 + my_r * G + g;
+  struct TokenIn {
+    f32x4 k, q, a;
+    float beta, v;
+  };
+  // a token's inputs; the next token's are fetched while the current one runs
+  auto load_token = [&](int t) {
+    const int64_t tok = MULTI ? ((int64_t)b * n_tok + t) * a.H + h : bh;   // (sequence, token, head)
+    const int64_t vec_off = tok * D;
+    TokenIn x;
+    x.k = load4<BF16>(a.k, vec_off + 4 * li);
+    x.q = load4<BF16>(a.q, vec_off + 4 * li);
+    if constexpr (PER_KEY) {
+      x.a = *reinterpret_cast<const f32x4*>(a.alpha + vec_off + 4 * li);
+    } else {
+      const float al = a.alpha[tok];
+      x.a = f32x4{al, al, al, al};
+    }
+    x.beta = a.beta[tok];
+    x.v = load1<BF16>(a.v, vec_off + my_row);
+    return x;
+  };
+  TokenIn next = load_token(0);
+
   for (int t = 0; t < n_tok; ++t) {
     const int64_t tok = MULTI ? ((int64_t)b * n_tok + t) * a.H + h : bh;   // (sequence, token, head)
     const int64_t vec_off = tok * D;
-    const f32x4 kv = load4<BF16>(a.k, vec_off + 4 * li);
-    const f32x4 qv = load4<BF16>(a.q, vec_off + 4 * li);
-    f32x4 av;
-    if constexpr (PER_KEY) {
-      av = *reinterpret_cast<const f32x4*>(a.alpha + vec_off + 4 * li);
-    } else {
-      const float x = a.alpha[tok];
-      av = f32x4{x, x, x, x};
-    }
-    const float beta = a.beta[tok];
+    const TokenIn cur = next;
+    if (MULTI && t + 1 < n_tok) next = load_token(t + 1);
+    const f32x4 kv = cur.k, qv = cur.q, av = cur.a;
+    const float beta = cur.beta;
 
     float kq = kv[0] * qv[0] + kv[1] * qv[1] + kv[2] * qv[2] + kv[3] * qv[3];
     kq = group_allreduce<LPR>(kq);
@@ -135,10 +155,8 @@ __global__ __launch_bounds__(D * 2) void decode_kernel(DecodeArgs a) {
     }
     // lane li = 2r holds p_r, lane li = 2r+1 holds (s'_r . q)
     const float red = reduce_scatter<2 * R>(vals, li);
-    const int my_r = li >> 1;
-    const int my_row = wave * 32 + my_r * G + g;
     float u = 0.f;
-    if ((li & 1) == 0) u = beta * (load1<BF16>(a.v, vec_off + my_row) - red);
+    if ((li & 1) == 0) u = beta * (cur.v - red);
     const float u_pair = xor_lane<1>(u);
     if (li & 1) a.o[vec_off + my_row] = red + u_pair * kq;
 
