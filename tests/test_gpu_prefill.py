@@ -240,3 +240,18 @@ def test_pageable_host_snapshots_rejected_by_binding():
         kda.prefill_chunked(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["cu_seqlens"],
                             inp["initial_state"], w.interval, cu_seqlens_host=inp["cu_seqlens_host"],
                             out=(o, fin, snaps))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("gate", ["scalar", "per_key"])
+def test_segmented_every_variant(d, dtype, gate):
+    """Forced 128-token segments for every (d, input dtype, gate) variant: the
+    map pass, its stored inverses, the scan and the output pass, on a varlen
+    pack with a ragged tail, snapshots and initial states."""
+    dev = device()
+    w = custom(f"segvar_{d}_{dtype}_{gate}", H=2, d=d, lens=(700, 130, 0, 64), gate=gate, dtype=dtype,
+               interval=64, seed=21)
+    print(f"case {w.name}", flush=True)
+    inp = wl.make_prefill_inputs(w, dev)
+    check_prefill(inp, run_prefill(inp, w.interval, 128), w.interval)
