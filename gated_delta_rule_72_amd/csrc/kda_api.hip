@@ -262,7 +262,6 @@ int kda_prefill_chunked(const kda_shape* shape, int32_t num_seqs,
   a.interval = snapshot_interval;
   a.seg_chunks = plan.seg_chunks;
   a.n_items = plan.n_items;
-  a.pass = 0;
   char* ws = static_cast<char*>(workspace);
   a.items = reinterpret_cast<kda::PrefillItem*>(ws + plan.items_off);
   a.seq_first_item = reinterpret_cast<int32_t*>(ws + plan.first_off);

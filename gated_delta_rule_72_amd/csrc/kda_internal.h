@@ -77,7 +77,6 @@ struct PrefillArgs {
   int64_t interval;          // snapshot interval (0 = none)
   int32_t seg_chunks;        // chunks per segment (0 = unsegmented)
   int32_t n_items;           // work items (sequences or sequence segments)
-  int32_t pass;              // 0 unsegmented; 1 segment maps (+ first segments); 3 segment reruns
   PrefillItem* items;        // workspace: [n_items]
   int32_t* seq_first_item;   // workspace: [N] first item of each sequence (segmented)
   float* seg_maps;           // workspace: per (item, head) M (dk x dk) then N (dv x dk)

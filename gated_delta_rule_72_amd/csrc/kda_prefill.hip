@@ -254,7 +254,7 @@ struct ChunkRegs {
 // on the loop index, so no per-access offsets are kept live.
 template <int D, bool BF16, bool PER_KEY, int NT>
 __device__ __forceinline__ void load_chunk(ChunkRegs<D, BF16, PER_KEY, NT>& R, const PrefillArgs& a,
-                                           int64_t tok0, int n, int h, int tid, bool need_v) {
+                                           int64_t tok0, int n, int h, int tid, bool load_v) {
   using CR = ChunkRegs<D, BF16, PER_KEY, NT>;
   constexpr int ROWS_PER_PASS = NT / (D / 8);     // tokens covered by one group pass
   const int64_t HD = (int64_t)a.H * D;            // elements per token (all heads)
@@ -267,11 +267,11 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<D, BF16, PER_KEY, NT>& R, c
     const bool valid = c < n;
     const int64_t ub = row0 + (int64_t)j * ROWS_PER_PASS * HD;   // uniform
     if constexpr (BF16) {
-      R.v[j] = load_group<true>(static_cast<const uint16_t*>(a.v) + ub, lane_off, valid && need_v);
+      R.v[j] = load_group<true>(static_cast<const uint16_t*>(a.v) + ub, lane_off, valid && load_v);
     } else {
       R.k[j] = load_group<false>(static_cast<const float*>(a.k) + ub, lane_off, valid);
       R.q[j] = load_group<false>(static_cast<const float*>(a.q) + ub, lane_off, valid);
-      R.v[j] = load_group<false>(static_cast<const float*>(a.v) + ub, lane_off, valid && need_v);
+      R.v[j] = load_group<false>(static_cast<const float*>(a.v) + ub, lane_off, valid && load_v);
     }
   }
   const int wave = tid / 64, lane = tid % 64;
@@ -386,11 +386,10 @@ void prefill_kernel(PrefillArgs a) {
     if (item.n_segs <= 1) return;                // (uniform)
   }
   constexpr bool out_mode = !MAP;
-  constexpr bool need_v = true;
   // MAP with bf16 inputs stages v rows in LDS as well (into the Q~ buffer,
   // which MAP never uses), so its prefetch holds no registers across P6
   constexpr bool v_in_lds = MAP && BF16;
-  constexpr bool v_in_regs = need_v && !v_in_lds;
+  constexpr bool v_in_regs = !v_in_lds;
   // Pass 3 of a split sequence's segment: the map pass already formed
   // each chunk's inverse (I + L)^-1 and stored it; it is loaded into the L
   // buffer instead of being recomputed (same arithmetic, same bits).
@@ -758,7 +757,7 @@ void prefill_kernel(PrefillArgs a) {
       }
     }
     // V^T [v][c] into region A (G and raw q, k are dead after P3)
-    if (need_v) {
+    {
 #pragma unroll
       for (int j = 0; j < CR::GPT; ++j) {
         const int gi = tid + j * NT;
