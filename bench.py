@@ -225,6 +225,70 @@ def time_decode_tokens(kda, torch, w, n_tok, steps, warmup, keep_states, n_buffe
     return ms
 
 
+def layer_algorithmic(T, H, d, n_seqs, per_key, qkv_bytes=2, out_bytes=2):
+    """Bytes the layer front and back end must move once each: front reads
+    xq, xk, xv, the gate logits, the taps and the carried conv state and writes
+    q, k, v, alpha, beta and the new conv state; back reads o and the gate
+    logits (fp32) and writes the output."""
+    rows = T * H
+    a_el = rows * (d if per_key else 1)
+    front = (2 * 3 * rows * d * qkv_bytes + 2 * a_el * 4 + 2 * rows * 4 + 3 * H * d * 4 * 4
+             + 2 * n_seqs * 9 * H * d * qkv_bytes + (n_seqs + 1) * 8)
+    back = rows * d * (4 + 4 + out_bytes) + d * 4
+    return front, back
+
+
+def time_layer(kda, torch, w, steps, warmup):
+    """HIP-event times of kda_layer_front (with carried conv state in and out)
+    and kda_layer_back, and of front + kda_prefill_chunked + back."""
+    from gated_delta_rule_72_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    li = wl.make_layer_inputs(w, dev)
+    pinp = wl.make_prefill_inputs(w, dev)
+    T, H, d = w.T, w.H, w.dk
+    shape = kda.make_shape(H, d, d, li["xq"].dtype, w.gate == "per_key")
+    q, k, v = (torch.empty_like(li["xq"]) for _ in range(3))
+    alpha = torch.empty_like(li["alpha_logit"])
+    beta = torch.empty_like(li["beta_logit"])
+    st = torch.empty_like(li["conv_state"])
+    out = torch.empty((T, H, d), dtype=torch.bfloat16, device=dev)
+    cu_h = li["cu_seqlens_host"]
+    o = torch.empty((T, H, d), dtype=torch.float32, device=dev)
+    fin = torch.empty((w.num_seqs, H, d, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(kda.kda_prefill_workspace_size(shape, cu_h, 64, 0), 1), dtype=torch.uint8, device=dev)
+
+    def front():
+        kda.kda_layer_front(shape, cu_h, li["cu_seqlens"], li["xq"], li["xk"], li["xv"], li["conv_w"],
+                            li["conv_state"], li["alpha_logit"], 5.0, li["beta_logit"], q, k, v, alpha, beta, st)
+
+    def back(src):
+        kda.kda_layer_back(shape, T, src, li["g_logit"], li["norm_w"], 1e-6, kda.KDA_BF16, out)
+
+    def layer():
+        front()
+        kda.kda_prefill_chunked(shape, cu_h, li["cu_seqlens"], q, k, v, alpha, beta, pinp["initial_state"],
+                                o, fin, None, ws)
+        back(o)
+
+    res = {}
+    stream = torch.cuda.current_stream()
+    for name, fn in (("front", front), ("back", lambda: back(li["o"])), ("layer", layer)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for s_, e_ in ev:
+            s_.record(stream)
+            fn()
+            e_.record(stream)
+        torch.cuda.synchronize()
+        ms = [s_.elapsed_time(e_) for s_, e_ in ev]
+        res[name] = sum(ms) / len(ms)
+    del li, pinp
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w, inp, tokens: int):
     """fp64 oracle on the host over the first `tokens` tokens of the workload."""
     tokens = min(tokens, w.T)
@@ -257,6 +321,8 @@ def main(argv=None):
     ap.add_argument("--decode-only", action="store_true", help="profiling: only the decode loop")
     ap.add_argument("--no-other-prefill", action="store_true",
                     help="skip timing the other prefill workloads (KDA layer shape, varlen pack)")
+    ap.add_argument("--no-layer", action="store_true",
+                    help="skip timing the KDA layer front and back end")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="profiling: copy a 256 MiB fp32 buffer 3 times (known bytes for HBM counters)")
     args = ap.parse_args(argv)
@@ -352,6 +418,22 @@ def main(argv=None):
             del oinp
             torch.cuda.empty_cache()
         result["other_prefill"] = other
+    if not args.no_layer and not args.prefill_only:
+        layer = {}
+        for lw in (wl.KDA_LAYER, wl.LONG_PREFILL):
+            t = time_layer(kda, torch, lw, max(5, args.steps // 2), args.warmup)
+            fb, bb = layer_algorithmic(lw.T, lw.H, lw.dk, lw.num_seqs, lw.gate == "per_key",
+                                       qkv_bytes=2 if lw.dtype == "bf16" else 4)
+            layer[lw.name] = {
+                "front_us": round(t["front"] * 1e3, 2), "back_us": round(t["back"] * 1e3, 2),
+                "front_hbm_GBs": round(fb / (t["front"] * 1e-3) / 1e9, 1),
+                "back_hbm_GBs": round(bb / (t["back"] * 1e-3) / 1e9, 1),
+                "front_hbm_frac": round(fb / (t["front"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "back_hbm_frac": round(bb / (t["back"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "front_algorithmic_bytes": int(fb), "back_algorithmic_bytes": int(bb),
+                "front_recurrence_back_ms": round(t["layer"], 4),
+                "front_recurrence_back_tokens_per_s": round(lw.T / (t["layer"] * 1e-3), 1)}
+        result["layer_front_back"] = layer
     if not args.skip_decode and not args.prefill_only:
         d = wl.DECODE
         dms = time_decode(kda, torch, d, max(args.steps, 20), args.warmup)

@@ -338,4 +338,72 @@ int kda_decode_tokens(const kda_shape* shape, int32_t batch, int32_t n_tok, cons
   return KDA_OK;
 }
 
+int kda_layer_front(const kda_shape* shape, int32_t num_seqs, const int64_t* cu_seqlens_host,
+                    const int64_t* cu_seqlens_dev, const void* xq, const void* xk, const void* xv,
+                    const float* conv_w, const void* conv_state_in, const float* alpha_logit,
+                    float alpha_bias, const float* beta_logit, void* q, void* k, void* v, float* alpha,
+                    float* beta, void* conv_state_out, void* hip_stream) {
+  int rc = check_shape(shape);
+  if (rc != KDA_OK) return rc;
+  rc = check_cu(num_seqs, cu_seqlens_host);
+  if (rc != KDA_OK) return rc;
+  const int64_t T = cu_seqlens_host[num_seqs];
+  if (num_seqs > 0 && !cu_seqlens_dev) return fail(KDA_ERR_ARG, "cu_seqlens_dev is NULL");
+  if (T > 0 && (!xq || !xk || !xv || !conv_w || !alpha_logit || !beta_logit || !q || !k || !v || !alpha || !beta))
+    return fail(KDA_ERR_ARG, "inputs, conv_w, gate logits and outputs must be non-NULL when T > 0");
+  if (num_seqs > 0 && !conv_w) return fail(KDA_ERR_ARG, "conv_w is NULL");
+  const uintptr_t a_alpha = shape->gate == KDA_GATE_PER_KEY ? 16 : 4;
+  const PtrReq reqs[] = {{xq, 16, "xq"}, {xk, 16, "xk"}, {xv, 16, "xv"}, {conv_w, 16, "conv_w"},
+                         {conv_state_in, 16, "conv_state_in"}, {alpha_logit, a_alpha, "alpha_logit"},
+                         {beta_logit, 4, "beta_logit"}, {q, 16, "q"}, {k, 16, "k"}, {v, 16, "v"},
+                         {alpha, a_alpha, "alpha"}, {beta, 4, "beta"}, {conv_state_out, 16, "conv_state_out"},
+                         {cu_seqlens_dev, 8, "cu_seqlens_dev"}};
+  rc = check_align(reqs, (int)(sizeof reqs / sizeof reqs[0]));
+  if (rc != KDA_OK) return rc;
+  // neighbouring workgroups read the 3 rows before their first token, and the
+  // carried-state pass shifts within a sequence's slots: no output may be an input
+  if ((q && (q == xq || q == xk || q == xv)) || (k && (k == xq || k == xk || k == xv)) ||
+      (v && (v == xq || v == xk || v == xv)))
+    return fail(KDA_ERR_ARG, "q, k, v must not alias xq, xk, xv");
+  if (conv_state_out && conv_state_out == conv_state_in)
+    return fail(KDA_ERR_ARG, "conv_state_out must not alias conv_state_in");
+  kda::LayerFrontArgs a{};
+  a.xq = xq; a.xk = xk; a.xv = xv; a.conv_w = conv_w; a.conv_state_in = conv_state_in;
+  a.alpha_logit = alpha_logit; a.beta_logit = beta_logit; a.alpha_bias = alpha_bias;
+  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.conv_state_out = conv_state_out;
+  a.cu = cu_seqlens_dev; a.num_seqs = num_seqs; a.H = shape->num_heads; a.T = T;
+  if (num_seqs == 0) {
+    g_err[0] = '\0';
+    return KDA_OK;
+  }
+  hipError_t e = kda::launch_layer_front(a, shape->d_k, shape->qkv_dtype == KDA_BF16,
+                                         shape->gate == KDA_GATE_PER_KEY, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "layer front launch failed: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return KDA_OK;
+}
+
+int kda_layer_back(const kda_shape* shape, int64_t num_tokens, const float* o, const float* g_logit,
+                   const float* norm_w, float eps, int32_t out_dtype, void* out, void* hip_stream) {
+  int rc = check_shape(shape);
+  if (rc != KDA_OK) return rc;
+  if (num_tokens < 0) return fail(KDA_ERR_ARG, "num_tokens must be >= 0");
+  if (out_dtype != KDA_BF16 && out_dtype != KDA_F32)
+    return fail(KDA_ERR_ARG, "out_dtype must be KDA_BF16 or KDA_F32 (got %d)", out_dtype);
+  if (!(eps >= 0.f)) return fail(KDA_ERR_ARG, "eps must be >= 0");
+  if (num_tokens == 0) {
+    g_err[0] = '\0';
+    return KDA_OK;
+  }
+  if (!o || !g_logit || !norm_w || !out) return fail(KDA_ERR_ARG, "o, g_logit, norm_w and out must be non-NULL");
+  const PtrReq reqs[] = {{o, 16, "o"}, {g_logit, 16, "g_logit"}, {norm_w, 16, "norm_w"}, {out, 16, "out"}};
+  rc = check_align(reqs, (int)(sizeof reqs / sizeof reqs[0]));
+  if (rc != KDA_OK) return rc;
+  kda::LayerBackArgs a{o, g_logit, norm_w, out, eps, num_tokens * shape->num_heads};
+  hipError_t e = kda::launch_layer_back(a, shape->d_v, out_dtype == KDA_BF16, static_cast<hipStream_t>(hip_stream));
+  if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "layer back launch failed: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return KDA_OK;
+}
+
 }  // extern "C"

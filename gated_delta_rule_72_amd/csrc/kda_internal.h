@@ -88,4 +88,29 @@ hipError_t launch_prefill(PrefillArgs a, int d, bool bf16, bool per_key, hipStre
 // bytes of one chunk's stored inverse: 64 rows of 68 fp32 (the LDS row stride)
 constexpr size_t kInverseBytes = 64 * 68 * 4;
 
+// Layer front end: conv-4 + SiLU (+ L2 norm for q, k), gates, carried conv state.
+struct LayerFrontArgs {
+  const void *xq, *xk, *xv;         // [T, H, d] conv inputs (qkv dtype)
+  const float* conv_w;              // [3, H, d, 4] taps, oldest first
+  const void* conv_state_in;        // [N, 3, 3, H, d] (qkv dtype) or null
+  const float *alpha_logit, *beta_logit;
+  float alpha_bias;
+  void *q, *k, *v;                  // [T, H, d] outputs (qkv dtype)
+  float *alpha, *beta;
+  void* conv_state_out;             // [N, 3, 3, H, d] or null
+  const int64_t* cu;                // device cu_seqlens [N+1]
+  int32_t num_seqs, H;
+  int64_t T;
+};
+hipError_t launch_layer_front(const LayerFrontArgs& a, int d, bool bf16, bool per_key, hipStream_t s);
+
+// Layer back end: RMSNorm over d_v times a sigmoid output gate.
+struct LayerBackArgs {
+  const float *o, *g_logit, *norm_w;
+  void* out;
+  float eps;
+  int64_t rows;                     // T * H
+};
+hipError_t launch_layer_back(const LayerBackArgs& a, int d, bool out_bf16, hipStream_t s);
+
 }  // namespace kda

@@ -54,6 +54,9 @@ def load() -> ctypes.CDLL:
                                 ctypes.c_int),
         "kda_decode_step": ([P, I32, P, P, P, P, P, P, P, P], ctypes.c_int),
         "kda_decode_tokens": ([P, I32, I32, P, P, P, P, P, P, P, P, P, P], ctypes.c_int),
+        "kda_layer_front": ([P, I32, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, P, P],
+                            ctypes.c_int),
+        "kda_layer_back": ([P, I64, P, P, P, ctypes.c_float, I32, P, P], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -64,7 +67,8 @@ def load() -> ctypes.CDLL:
 
 
 EXPORTED = ("kda_abi_version", "kda_last_error", "kda_snapshot_count", "kda_prefill_workspace_size",
-            "kda_prefill_chunked", "kda_decode_step", "kda_decode_tokens")
+            "kda_prefill_chunked", "kda_decode_step", "kda_decode_tokens", "kda_layer_front",
+            "kda_layer_back")
 
 
 def _check(fn: str, rc: int) -> None:
@@ -143,6 +147,25 @@ def kda_decode_tokens(shape: KdaShape, batch: int, n_tok: int, q, k, v, alpha, b
     _check("kda_decode_tokens", load().kda_decode_tokens(
         ctypes.byref(shape), int(batch), int(n_tok), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
         _ptr(state), _ptr(o), _ptr(token_states), _ptr(commit), s))
+
+
+def kda_layer_front(shape: KdaShape, cu_seqlens_host: torch.Tensor, cu_seqlens_dev: torch.Tensor, xq, xk, xv,
+                    conv_w, conv_state_in, alpha_logit, alpha_bias: float, beta_logit, q, k, v, alpha, beta,
+                    conv_state_out, stream=None) -> None:
+    cu = cu_seqlens_host.to("cpu", torch.int64).contiguous()
+    s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream_ptr(xq.device)
+    _check("kda_layer_front", load().kda_layer_front(
+        ctypes.byref(shape), cu.numel() - 1, _ptr(cu), _ptr(cu_seqlens_dev), _ptr(xq), _ptr(xk), _ptr(xv),
+        _ptr(conv_w), _ptr(conv_state_in), _ptr(alpha_logit), float(alpha_bias), _ptr(beta_logit), _ptr(q),
+        _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(conv_state_out), s))
+
+
+def kda_layer_back(shape: KdaShape, num_tokens: int, o, g_logit, norm_w, eps: float, out_dtype: int, out,
+                   stream=None) -> None:
+    s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream_ptr(o.device)
+    _check("kda_layer_back", load().kda_layer_back(
+        ctypes.byref(shape), int(num_tokens), _ptr(o), _ptr(g_logit), _ptr(norm_w), float(eps), int(out_dtype),
+        _ptr(out), s))
 
 
 # ---- convenience wrappers: allocate outputs with torch, then call the ABI ----
@@ -229,3 +252,40 @@ def decode_tokens(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torc
         raise TypeError("commit must be int32")
     kda_decode_tokens(shape, B, n, q, k, v, alpha, beta, state, o, ts, commit)
     return o, ts
+
+
+def layer_front(xq: torch.Tensor, xk: torch.Tensor, xv: torch.Tensor, conv_w: torch.Tensor,
+                alpha_logit: torch.Tensor, beta_logit: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None,
+                conv_state: Optional[torch.Tensor] = None, alpha_bias: float = 5.0,
+                cu_seqlens_host: Optional[torch.Tensor] = None, keep_state: bool = True):
+    """KDA layer front end: xq, xk, xv [T,H,d] (bf16/fp32), conv_w [3,H,d,4] fp32,
+    alpha_logit [T,H] or [T,H,d], beta_logit [T,H]; conv_state [N,3,3,H,d] or None.
+    Returns (q, k, v, alpha, beta, conv_state_out or None), ready for prefill_chunked."""
+    T, H, d = xq.shape
+    dev = xq.device
+    if cu_seqlens is None:
+        cu_seqlens = torch.tensor([0, T], dtype=torch.int64, device=dev)
+    if cu_seqlens_host is None:
+        cu_seqlens_host = cu_seqlens.to("cpu")
+    cu_dev = cu_seqlens.to(dev, torch.int64).contiguous()
+    N = cu_seqlens_host.numel() - 1
+    _contig(xq, xk, xv, conv_w, alpha_logit, beta_logit, conv_state)
+    shape = make_shape(H, d, d, xq.dtype, alpha_logit.dim() == 3)
+    q, k, v = (torch.empty_like(xq) for _ in range(3))
+    alpha = torch.empty_like(alpha_logit, dtype=torch.float32)
+    beta = torch.empty_like(beta_logit, dtype=torch.float32)
+    st = torch.empty((N, 3, 3, H, d), dtype=xq.dtype, device=dev) if keep_state else None
+    kda_layer_front(shape, cu_seqlens_host, cu_dev, xq, xk, xv, conv_w, conv_state, alpha_logit, alpha_bias,
+                    beta_logit, q, k, v, alpha, beta, st)
+    return q, k, v, alpha, beta, st
+
+
+def layer_back(o: torch.Tensor, g_logit: torch.Tensor, norm_w: torch.Tensor, eps: float = 1e-6,
+               out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """KDA layer back end: RMSNorm(o) * norm_w * sigmoid(g_logit) over d_v; o, g_logit [T,H,dv] fp32."""
+    T, H, dv = o.shape
+    _contig(o, g_logit, norm_w)
+    shape = make_shape(H, dv, dv, torch.bfloat16, False)
+    out = torch.empty((T, H, dv), dtype=out_dtype, device=o.device)
+    kda_layer_back(shape, T, o, g_logit, norm_w, eps, KDA_BF16 if out_dtype == torch.bfloat16 else KDA_F32, out)
+    return out

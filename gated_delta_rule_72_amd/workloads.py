@@ -153,3 +153,32 @@ def to_oracle_arrays(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
     return t.numpy()
+
+
+def make_layer_inputs(wl: Workload, device="cpu", seed: Optional[int] = None, conv_state: bool = True) -> dict:
+    """Inputs of the layer front and back end around the recurrence: conv inputs
+    xq, xk, xv ~ N(0,1) [T,H,d] (storage dtype); conv taps [3,H,d,4] fp32 =
+    identity tap (oldest first: 0,0,0,1) + N(0, 0.3); carried conv state
+    ~ N(0,1) [N,3,3,H,d] or None; alpha logits ~ N(0,1) [T,H] or [T,H,d_k] and
+    beta logits ~ N(0,1) [T,H]; for the back end o ~ N(0,1), gate logits ~ N(0,1)
+    [T,H,d_v] and norm weights ~ U(0.5, 1.5) [d_v], all fp32."""
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(wl.seed + 7 if seed is None else seed)
+    T, H, d = wl.T, wl.H, wl.dk
+    st = _torch_dtype(wl.dtype)
+    xq, xk, xv = (_normal((T, H, d), gen, device).to(st) for _ in range(3))
+    conv_w = _normal((3, H, d, 4), gen, device, std=0.3)
+    conv_w[..., 3] += 1.0
+    state = _normal((wl.num_seqs, 3, 3, H, d), gen, device).to(st) if conv_state else None
+    a_shape = (T, H, d) if wl.gate == "per_key" else (T, H)
+    alpha_logit = _normal(a_shape, gen, device)
+    beta_logit = _normal((T, H), gen, device)
+    o = _normal((T, H, wl.dv), gen, device)
+    g_logit = _normal((T, H, wl.dv), gen, device)
+    norm_w = torch.rand((wl.dv,), generator=gen, device=device) + 0.5
+    cu_host = torch.zeros(wl.num_seqs + 1, dtype=torch.int64)
+    cu_host[1:] = torch.cumsum(torch.tensor(wl.seq_lens, dtype=torch.int64), 0)
+    return dict(xq=xq, xk=xk, xv=xv, conv_w=conv_w, conv_state=state, alpha_logit=alpha_logit,
+                beta_logit=beta_logit, o=o, g_logit=g_logit, norm_w=norm_w, cu_seqlens=cu_host.to(device),
+                cu_seqlens_host=cu_host)

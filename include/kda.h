@@ -187,6 +187,44 @@ int kda_decode_tokens(const kda_shape* shape, int32_t batch, int32_t n_tok,
                       float* state, float* o, float* token_states, const int32_t* commit,
                       void* hip_stream);
 
+/* Front end of a KDA layer, the step between the q/k/v and gate projections
+ * and the recurrence (page "kda-graft: Qwen2.5-0.5B с трансплантированным
+ * KDA", ailist.pro, section "Идея и архитектура": a 4-tap convolution
+ * initialised as an identity tap, the alpha gate with bias +5, beta). The page
+ * gives no formulas; computed here, per sequence of the pack:
+ *   q, k, v = SiLU(conv4(x)), conv4 causal and depthwise over the sequence's
+ *             tokens, taps oldest first (identity = {0, 0, 0, 1}), the 3
+ *             positions before its first token read conv_state_in (or 0);
+ *   q, k   /= sqrt(sum over d of squares + 1e-6)   per (token, head);
+ *   alpha   = sigmoid(alpha_logit + alpha_bias);  beta = sigmoid(beta_logit).
+ * The outputs are laid out as kda_prefill_chunked takes them.
+ * xq, xk, xv: [T, H, d] (qkv dtype; d = d_k = d_v); conv_w: fp32 [3, H, d, 4]
+ * (q, k, v). conv_state_in: NULL or [num_seqs, 3, 3, H, d] (q, k, v; 3 carried
+ * inputs oldest first; qkv dtype). alpha_logit: fp32 [T, H] or [T, H, d_k]
+ * (gate of the shape); beta_logit: fp32 [T, H]. q, k, v: [T, H, d] (qkv
+ * dtype); alpha, beta: fp32 like their logits. conv_state_out: NULL or
+ * [num_seqs, 3, 3, H, d]: each sequence's last 3 conv inputs, shifted in from
+ * conv_state_in when the sequence is shorter (must not alias conv_state_in).
+ * Alignment: 16 bytes for every tensor except scalar-gate logits/alpha and
+ * beta (4) and cu_seqlens_dev (8). q, k, v may not be any of xq, xk, xv
+ * (KDA_ERR_ARG: a workgroup reads the 3 rows before its first token, which
+ * another one writes). Errors as kda_prefill_chunked. */
+int kda_layer_front(const kda_shape* shape, int32_t num_seqs,
+                    const int64_t* cu_seqlens_host, const int64_t* cu_seqlens_dev,
+                    const void* xq, const void* xk, const void* xv, const float* conv_w,
+                    const void* conv_state_in, const float* alpha_logit, float alpha_bias,
+                    const float* beta_logit, void* q, void* k, void* v, float* alpha, float* beta,
+                    void* conv_state_out, void* hip_stream);
+
+/* Back end of a KDA layer (same page and section: RMSNorm and the output
+ * gate): out = o * rsqrt(mean over d_v of o^2 + eps) * norm_w * sigmoid(g_logit)
+ * per (token, head). o, g_logit: fp32 [num_tokens, H, d_v]; norm_w: fp32 [d_v];
+ * out: [num_tokens, H, d_v] in out_dtype (KDA_BF16 or KDA_F32), may alias
+ * neither input. All pointers 16-byte aligned. */
+int kda_layer_back(const kda_shape* shape, int64_t num_tokens, const float* o,
+                   const float* g_logit, const float* norm_w, float eps, int32_t out_dtype,
+                   void* out, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

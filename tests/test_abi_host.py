@@ -40,7 +40,7 @@ def test_kda_header_symbols_exported(K):
     names = _declared("kda.h")
     assert set(names) == {"kda_abi_version", "kda_last_error", "kda_snapshot_count",
                           "kda_prefill_workspace_size", "kda_prefill_chunked", "kda_decode_step",
-                          "kda_decode_tokens"}
+                          "kda_decode_tokens", "kda_layer_front", "kda_layer_back"}
     lib = ctypes.CDLL(K.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -208,6 +208,50 @@ def test_decode_tokens_host_rejections(K):
     assert call(bf, 2, 4, ts=0x8008) == K.KDA_ERR_ALIGN
     assert call(bf, 2, 4, commit=0x9002) == K.KDA_ERR_ALIGN
     assert call(bf, 1 << 20, 1 << 10) == K.KDA_ERR_SHAPE
+
+
+def test_layer_host_rejections(K):
+    lib = K.load()
+    cu = torch.tensor([0, 10, 30], dtype=torch.int64)
+
+    def front(sh, cu_h, **kw):
+        p = dict(cu_dev=0x100, xq=0x1000, xk=0x2000, xv=0x3000, w=0x4000, st_in=None, al=0x5000, bl=0x6000,
+                 q=0x7000, k=0x8000, v=0x9000, a=0xA000, b=0xB000, st_out=None)
+        p.update(kw)
+        f = lambda n: None if p[n] is None else _fake(p[n])  # noqa: E731
+        return lib.kda_layer_front(ctypes.byref(sh), cu_h.numel() - 1,
+                                   cu_h.numpy().ctypes.data_as(ctypes.c_void_p), f("cu_dev"), f("xq"), f("xk"),
+                                   f("xv"), f("w"), f("st_in"), f("al"), ctypes.c_float(5.0), f("bl"), f("q"),
+                                   f("k"), f("v"), f("a"), f("b"), f("st_out"), None)
+
+    pk = K.make_shape(2, 64, 64, torch.bfloat16, True)
+    sc = K.make_shape(2, 64, 64, torch.bfloat16, False)
+    assert front(pk, torch.tensor([0], dtype=torch.int64)) == K.KDA_OK       # no sequences
+    assert front(pk, torch.tensor([1, 5], dtype=torch.int64)) == K.KDA_ERR_SHAPE
+    assert front(pk, cu, xq=None) == K.KDA_ERR_ARG
+    assert front(pk, cu, cu_dev=None) == K.KDA_ERR_ARG
+    assert front(pk, cu, xk=0x2008) == K.KDA_ERR_ALIGN
+    assert front(pk, cu, al=0x5004) == K.KDA_ERR_ALIGN                      # per-key logits: 16 B
+    assert front(sc, cu, al=0x5004, xk=0x2008) == K.KDA_ERR_ALIGN
+    assert "xk" in K.kda_last_error()                                        # scalar logits: 4 B is fine
+    assert front(pk, cu, st_out=0xC008) == K.KDA_ERR_ALIGN
+    assert front(pk, cu, q=0x1000) == K.KDA_ERR_ARG and "alias" in K.kda_last_error()
+    assert front(pk, cu, st_in=0xC000, st_out=0xC000) == K.KDA_ERR_ARG
+
+    def back(sh, n, out_dtype=K.KDA_BF16, eps=1e-6, **kw):
+        p = dict(o=0x1000, g=0x2000, w=0x3000, out=0x4000)
+        p.update(kw)
+        f = lambda n: None if p[n] is None else _fake(p[n])  # noqa: E731
+        return lib.kda_layer_back(ctypes.byref(sh), n, f("o"), f("g"), f("w"), ctypes.c_float(eps), out_dtype,
+                                  f("out"), None)
+
+    assert back(pk, 0) == K.KDA_OK
+    assert back(pk, -1) == K.KDA_ERR_ARG
+    assert back(pk, 4, out_dtype=99) == K.KDA_ERR_ARG
+    assert back(pk, 4, eps=-1.0) == K.KDA_ERR_ARG
+    assert back(pk, 4, eps=float("nan")) == K.KDA_ERR_ARG
+    assert back(pk, 4, out=None) == K.KDA_ERR_ARG
+    assert back(pk, 4, g=0x2004) == K.KDA_ERR_ALIGN
 
 
 def test_binding_fails_loudly_without_library(K, monkeypatch, tmp_path):
