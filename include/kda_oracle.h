@@ -75,6 +75,25 @@ int kda_oracle_run(int32_t num_seqs, const int64_t* cu_seqlens,
                    const float* initial_state, int32_t num_threads,
                    double* o, double* final_state, double* snapshots);
 
+/* Backward pass of the same recurrence in fp64: for the loss
+ *   sum_t <d_o_t, o_t> + sum_n <d_final_n, S_final_n>
+ * writes its gradients with respect to q, k, v ([T, H, d]), alpha (like
+ * alpha), beta ([T, H]) and the initial state ([num_seqs, H, d_v, d_k]; may be
+ * NULL). d_o: fp32 [T, H, d_v]; d_final: fp32 [num_seqs, H, d_v, d_k] or NULL
+ * (zero). The token update is differentiated in reverse token order with the
+ * states recomputed from checkpoints; nothing is chunked. Returns
+ * KDA_ORACLE_ERR_ARG on bad arguments or when memory runs out,
+ * KDA_ORACLE_ERR_DOMAIN as kda_oracle_run. */
+int kda_oracle_backward(int32_t num_seqs, const int64_t* cu_seqlens,
+                        int32_t num_heads, int32_t d_k, int32_t d_v,
+                        int32_t qkv_is_bf16, int32_t per_key_gate,
+                        const void* q, const void* k, const void* v,
+                        const float* alpha, const float* beta,
+                        const float* initial_state, const float* d_o,
+                        const float* d_final, int32_t num_threads,
+                        double* dq, double* dk, double* dv, double* dalpha,
+                        double* dbeta, double* d_initial_state);
+
 typedef struct {
   double o_rel;      /* max over (seq, head) of max|o - o_ref| / max|o_ref|     */
   double final_rel;  /* same over (seq, head) final-state slices                 */

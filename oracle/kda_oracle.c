@@ -350,3 +350,216 @@ int kda_recurrent_ref_check(int32_t num_seqs, const int64_t* cu, int32_t H, int3
   if (!snap_ref) free(s_buf);
   return rc;
 }
+
+/* ------------------------------------------------------------------------- *
+ * Backward pass (gradients of the recurrence above).
+ *
+ * For a loss that depends on the outputs o_t and on the final states, the
+ * gradients with respect to q, k, v, the gate a, beta and the initial state
+ * follow from the chain rule applied to the token update in reverse token
+ * order. With S' = S_{t-1} Diag(a_t), p = S' k_t, u = v_t - p (so that
+ * S_t = S' + beta_t u k_t^T) and dS the gradient arriving at S_t from later
+ * tokens and the final state:
+ *   6'  read-out o_t = S_t q_t:     dS <- dS + do_t q_t^T,  dq_t = S_t^T do_t
+ *   5'  S_t = S' + beta u k^T:      w = dS k,  dbeta_t = u . w,
+ *                                   du = beta w,  dk_t = beta dS^T u,
+ *                                   dS' = dS - du k^T
+ *   4'  u = v - p:                  dv_t = du,  dp = -du
+ *   3'  p = S' k:                   dS' <- dS' + dp k^T (folded into 5'),
+ *                                   dk_t <- dk_t + S'^T dp
+ *   2'  S' = S_{t-1} Diag(a):       da_t[j] = sum_i dS'[i][j] S_{t-1}[i][j]
+ *                                   (scalar gate: the sum over j as well),
+ *                                   dS_{t-1} = dS' Diag(a_t)
+ * and the gradient of the initial state is dS after the first token. The
+ * states S_{t-1} are recomputed forward from checkpoints kept every CK tokens
+ * (CK about sqrt(len)), with the same token update as the forward loop, so
+ * each backward step sees exactly the forward's values. One (sequence, head)
+ * is one unit of work: the rows of dS are coupled through dk.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int32_t num_seqs, H, dk, dv, is_bf16, per_key;
+  const int64_t* cu;
+  const void *q, *k, *v;
+  const float *alpha, *beta, *init, *d_o, *d_final;
+  double *dq, *dk_out, *dv_out, *dalpha, *dbeta, *d_init;
+  int64_t n_units, next_unit;
+  pthread_mutex_t lock;
+  int failed;
+} bwd_job;
+
+/* one forward token update of the whole d_v x d_k state, in place */
+static void fwd_token(const bwd_job* J, int32_t h, int64_t tok, double* S, double* kt, double* at) {
+  const int32_t H = J->H, dk = J->dk, dv = J->dv;
+  const int64_t qk_off = (tok * H + h) * (int64_t)dk;
+  for (int32_t j = 0; j < dk; ++j) {
+    kt[j] = load_elem(J->k, J->is_bf16, qk_off + j);
+    at[j] = J->per_key ? (double)J->alpha[qk_off + j] : (double)J->alpha[tok * H + h];
+  }
+  const double beta = (double)J->beta[tok * H + h];
+  for (int32_t i = 0; i < dv; ++i) {
+    double* s = S + (int64_t)i * dk;
+    const double vi = load_elem(J->v, J->is_bf16, (tok * H + h) * (int64_t)dv + i);
+    for (int32_t j = 0; j < dk; ++j) s[j] = s[j] * at[j];
+    double p = 0.0;
+    for (int32_t j = 0; j < dk; ++j) p += s[j] * kt[j];
+    const double u = beta * (vi - p);
+    for (int32_t j = 0; j < dk; ++j) s[j] = s[j] + u * kt[j];
+  }
+}
+
+static int bwd_unit(bwd_job* J, int64_t unit) {
+  const int32_t H = J->H, dk = J->dk, dv = J->dv;
+  const int32_t n = (int32_t)(unit / H), h = (int32_t)(unit % H);
+  const int64_t t_begin = J->cu[n], len = J->cu[n + 1] - J->cu[n];
+  const int64_t se = (int64_t)dv * dk;
+  int64_t CK = 1;
+  while (CK * CK < len) ++CK;
+  const int64_t nck = len > 0 ? (len + CK - 1) / CK : 0;
+  double* ckpt = (double*)malloc(sizeof(double) * (size_t)((nck > 0 ? nck : 1) * se));
+  double* buf = (double*)malloc(sizeof(double) * (size_t)((CK + 1) * se));
+  double* dS = (double*)malloc(sizeof(double) * (size_t)se);
+  double* vec = (double*)malloc(sizeof(double) * (size_t)(5 * dk + 4 * dv));
+  if (!ckpt || !buf || !dS || !vec) { free(ckpt); free(buf); free(dS); free(vec); return -1; }
+  double *kt = vec, *qt = vec + dk, *at = vec + 2 * dk, *dkt = vec + 3 * dk, *dat = vec + 4 * dk;
+  double *dot = vec + 5 * dk, *u = dot + dv, *w = u + dv, *vt = w + dv;
+
+  /* forward: the state before token m*CK of the sequence, m = 0 .. nck-1 */
+  double* S = buf;
+  for (int64_t e = 0; e < se; ++e)
+    S[e] = J->init ? (double)J->init[((int64_t)n * H + h) * se + e] : 0.0;
+  for (int64_t t = 0; t < len; ++t) {
+    if (t % CK == 0) memcpy(ckpt + (t / CK) * se, S, sizeof(double) * (size_t)se);
+    fwd_token(J, h, t_begin + t, S, kt, at);
+  }
+
+  for (int64_t e = 0; e < se; ++e)
+    dS[e] = J->d_final ? (double)J->d_final[((int64_t)n * H + h) * se + e] : 0.0;
+
+  for (int64_t m = nck - 1; m >= 0; --m) {
+    const int64_t t0 = m * CK, t1 = (t0 + CK < len) ? t0 + CK : len;
+    /* buf[r] = state before token t0 + r, r = 0 .. t1 - t0 (the last: after t1 - 1) */
+    memcpy(buf, ckpt + m * se, sizeof(double) * (size_t)se);
+    for (int64_t t = t0; t < t1; ++t) {
+      memcpy(buf + (t - t0 + 1) * se, buf + (t - t0) * se, sizeof(double) * (size_t)se);
+      fwd_token(J, h, t_begin + t, buf + (t - t0 + 1) * se, kt, at);
+    }
+    for (int64_t t = t1 - 1; t >= t0; --t) {
+      const int64_t tok = t_begin + t;
+      const double* Sp = buf + (t - t0) * se;      /* S_{t-1} */
+      const double* St = buf + (t - t0 + 1) * se;  /* S_t */
+      const int64_t qk_off = (tok * H + h) * (int64_t)dk, v_off = (tok * H + h) * (int64_t)dv;
+      for (int32_t j = 0; j < dk; ++j) {
+        kt[j] = load_elem(J->k, J->is_bf16, qk_off + j);
+        qt[j] = load_elem(J->q, J->is_bf16, qk_off + j);
+        at[j] = J->per_key ? (double)J->alpha[qk_off + j] : (double)J->alpha[tok * H + h];
+      }
+      const double beta = (double)J->beta[tok * H + h];
+      for (int32_t i = 0; i < dv; ++i) {
+        dot[i] = (double)J->d_o[v_off + i];
+        vt[i] = load_elem(J->v, J->is_bf16, v_off + i);
+      }
+      /* forward quantities of this token: u = v - S' k */
+      for (int32_t i = 0; i < dv; ++i) {
+        double p = 0.0;
+        for (int32_t j = 0; j < dk; ++j) p += Sp[(int64_t)i * dk + j] * at[j] * kt[j];
+        u[i] = vt[i] - p;
+      }
+      /* 6' read-out */
+      for (int32_t i = 0; i < dv; ++i)
+        for (int32_t j = 0; j < dk; ++j) dS[(int64_t)i * dk + j] += dot[i] * qt[j];
+      for (int32_t j = 0; j < dk; ++j) {
+        double r = 0.0;
+        for (int32_t i = 0; i < dv; ++i) r += St[(int64_t)i * dk + j] * dot[i];
+        J->dq[qk_off + j] = r;
+      }
+      /* 5' the written correction */
+      double db = 0.0;
+      for (int32_t i = 0; i < dv; ++i) {
+        double r = 0.0;
+        for (int32_t j = 0; j < dk; ++j) r += dS[(int64_t)i * dk + j] * kt[j];
+        w[i] = r;
+        db += u[i] * r;
+      }
+      J->dbeta[tok * H + h] = db;
+      for (int32_t j = 0; j < dk; ++j) {
+        double r = 0.0;
+        for (int32_t i = 0; i < dv; ++i) r += dS[(int64_t)i * dk + j] * u[i];
+        dkt[j] = beta * r;
+      }
+      /* 4' / 3': du = beta w = dv_t, dp = -du */
+      for (int32_t i = 0; i < dv; ++i) J->dv_out[v_off + i] = beta * w[i];
+      for (int32_t j = 0; j < dk; ++j) {
+        double r = 0.0;
+        for (int32_t i = 0; i < dv; ++i) r += Sp[(int64_t)i * dk + j] * at[j] * (beta * w[i]);
+        dkt[j] -= r;
+        J->dk_out[qk_off + j] = dkt[j];
+      }
+      /* dS' = dS - du k^T, then 2' the decay */
+      for (int32_t j = 0; j < dk; ++j) dat[j] = 0.0;
+      for (int32_t i = 0; i < dv; ++i)
+        for (int32_t j = 0; j < dk; ++j) {
+          const double g = dS[(int64_t)i * dk + j] - beta * w[i] * kt[j];
+          dat[j] += g * Sp[(int64_t)i * dk + j];
+          dS[(int64_t)i * dk + j] = g * at[j];
+        }
+      if (J->per_key) {
+        for (int32_t j = 0; j < dk; ++j) J->dalpha[qk_off + j] = dat[j];
+      } else {
+        double r = 0.0;
+        for (int32_t j = 0; j < dk; ++j) r += dat[j];
+        J->dalpha[tok * H + h] = r;
+      }
+    }
+  }
+  if (J->d_init) memcpy(J->d_init + ((int64_t)n * H + h) * se, dS, sizeof(double) * (size_t)se);
+  free(ckpt); free(buf); free(dS); free(vec);
+  return 0;
+}
+
+static void* bwd_worker(void* arg) {
+  bwd_job* J = (bwd_job*)arg;
+  for (;;) {
+    pthread_mutex_lock(&J->lock);
+    int64_t unit = J->next_unit++;
+    pthread_mutex_unlock(&J->lock);
+    if (unit >= J->n_units) break;
+    if (bwd_unit(J, unit) != 0) {
+      pthread_mutex_lock(&J->lock);
+      J->failed = 1;
+      pthread_mutex_unlock(&J->lock);
+    }
+  }
+  return NULL;
+}
+
+int kda_oracle_backward(int32_t num_seqs, const int64_t* cu, int32_t H, int32_t dk, int32_t dv,
+                        int32_t is_bf16, int32_t per_key, const void* q, const void* k, const void* v,
+                        const float* alpha, const float* beta, const float* init, const float* d_o,
+                        const float* d_final, int32_t num_threads, double* dq, double* dk_out,
+                        double* dv_out, double* dalpha, double* dbeta, double* d_init) {
+  int rc = validate(num_seqs, cu, H, dk, dv, 0, q, k, v, alpha, beta, per_key);
+  if (rc != KDA_ORACLE_OK) return rc;
+  const int64_t T = cu[num_seqs];
+  if (T > 0 && (!d_o || !dq || !dk_out || !dv_out || !dalpha || !dbeta)) return KDA_ORACLE_ERR_ARG;
+  int nthreads = num_threads > 0 ? num_threads : affinity_cpus();
+  bwd_job J;
+  memset(&J, 0, sizeof J);
+  J.num_seqs = num_seqs; J.H = H; J.dk = dk; J.dv = dv; J.is_bf16 = is_bf16; J.per_key = per_key;
+  J.cu = cu; J.q = q; J.k = k; J.v = v; J.alpha = alpha; J.beta = beta; J.init = init;
+  J.d_o = d_o; J.d_final = d_final;
+  J.dq = dq; J.dk_out = dk_out; J.dv_out = dv_out; J.dalpha = dalpha; J.dbeta = dbeta; J.d_init = d_init;
+  J.n_units = (int64_t)num_seqs * H;
+  pthread_mutex_init(&J.lock, NULL);
+  if (nthreads > J.n_units) nthreads = (int)(J.n_units > 0 ? J.n_units : 1);
+  pthread_t* tids = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  char* ok = (char*)calloc((size_t)nthreads, 1);
+  for (int i = 1; tids && ok && i < nthreads; ++i)
+    ok[i] = pthread_create(&tids[i], NULL, bwd_worker, &J) == 0;
+  bwd_worker(&J);
+  for (int i = 1; tids && ok && i < nthreads; ++i)
+    if (ok[i]) pthread_join(tids[i], NULL);
+  free(ok);
+  free(tids);
+  pthread_mutex_destroy(&J.lock);
+  return J.failed ? KDA_ORACLE_ERR_ARG : KDA_ORACLE_OK;
+}

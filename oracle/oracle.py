@@ -66,7 +66,10 @@ def load() -> ctypes.CDLL:
         lib.kda_recurrent_ref_check.argtypes = [I32, P, I32, I32, I32, I32, I32, I64,
                                                 P, P, P, P, P, P, P, P, P, D, D, I32,
                                                 P, P, P, P]
-        for f in (lib.kda_oracle_snapshot_count, lib.kda_oracle_run, lib.kda_recurrent_ref_check):
+        lib.kda_oracle_backward.argtypes = [I32, P, I32, I32, I32, I32, I32, P, P, P, P, P, P, P, P,
+                                            I32, P, P, P, P, P, P]
+        for f in (lib.kda_oracle_snapshot_count, lib.kda_oracle_run, lib.kda_recurrent_ref_check,
+                  lib.kda_oracle_backward):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -165,3 +168,29 @@ def ref_check(q, k, v, alpha, beta, cu_seqlens, initial_state=None, interval: in
         raise ValueError(f"oracle rejected its inputs (rc={rc})")
     out = (rc, rep.as_dict())
     return out + (refs,) if want_ref else out
+
+
+def backward(q, k, v, alpha, beta, cu_seqlens, initial_state=None, d_o=None, d_final=None,
+             threads: int = 0) -> dict:
+    """fp64 gradients of sum <d_o, o> + sum <d_final, S_final> (kda_oracle_backward).
+    d_o float32 [T, H, d_v]; d_final float32 [N, H, d_v, d_k] or None. Returns a
+    dict with dq, dk, dv, dalpha (shaped like alpha), dbeta and d_initial."""
+    q, k, v, alpha, beta, cu, init, (N, T, H, dk, dv, per_key, is_bf16) = _prep(
+        q, k, v, alpha, beta, cu_seqlens, initial_state)
+    d_o = np.ascontiguousarray(np.zeros((T, H, dv)) if d_o is None else d_o, dtype=np.float32)
+    if d_o.shape != (T, H, dv):
+        raise ValueError("d_o must be [T,H,d_v]")
+    dfin = None
+    if d_final is not None:
+        dfin = np.ascontiguousarray(d_final, dtype=np.float32)
+        if dfin.shape != (N, H, dv, dk):
+            raise ValueError("d_final must be [N,H,d_v,d_k]")
+    out = {"dq": np.zeros((T, H, dk)), "dk": np.zeros((T, H, dk)), "dv": np.zeros((T, H, dv)),
+           "dalpha": np.zeros(alpha.shape), "dbeta": np.zeros((T, H)), "d_initial": np.zeros((N, H, dv, dk))}
+    rc = load().kda_oracle_backward(N, _ptr(cu), H, dk, dv, is_bf16, per_key, _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(alpha), _ptr(beta), _ptr(init), _ptr(d_o), _ptr(dfin), int(threads),
+                                    _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dalpha"]),
+                                    _ptr(out["dbeta"]), _ptr(out["d_initial"]))
+    if rc != OK:
+        raise ValueError(f"oracle rejected its inputs (rc={rc})")
+    return out

@@ -1,9 +1,10 @@
 """Each plausible mistake planted in a copy of the oracle is caught by the pins.
 
 The mutants are built from the oracle's C source by a one-line text change, in
-a temporary directory, on the CPU; the pin suites (test_oracle_pins.py and
-test_chunk_rederivation.py) then run against each mutant in a subprocess and
-must fail. A mutant that crashes also counts as caught.
+a temporary directory, on the CPU; the pin suites then run against each mutant
+in a subprocess and must fail: test_oracle_pins.py and
+test_chunk_rederivation.py for the forward recurrence, test_oracle_backward.py
+for the backward pass. A mutant that crashes also counts as caught.
 """
 import os
 import shutil
@@ -39,12 +40,32 @@ MUTANTS = {
 }
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
+BACKWARD_MUTANTS = {
+    "bwd_readout_term_dropped": [("dS[(int64_t)i * dk + j] += dot[i] * qt[j];",
+                                  "dS[(int64_t)i * dk + j] += 0.0 * dot[i] * qt[j];")],
+    "bwd_dq_from_previous_state": [("r += St[(int64_t)i * dk + j] * dot[i];", "r += Sp[(int64_t)i * dk + j] * dot[i];")],
+    "bwd_dk_read_term_sign": [("dkt[j] -= r;", "dkt[j] += r;")],
+    "bwd_dalpha_from_new_state": [("dat[j] += g * Sp[(int64_t)i * dk + j];", "dat[j] += g * St[(int64_t)i * dk + j];")],
+    "bwd_decay_not_propagated": [("dS[(int64_t)i * dk + j] = g * at[j];", "dS[(int64_t)i * dk + j] = g;")],
+    "bwd_dbeta_scaled_by_beta": [("db += u[i] * r;", "db += beta * u[i] * r;")],
+    "bwd_dv_unscaled": [("J->dv_out[v_off + i] = beta * w[i];", "J->dv_out[v_off + i] = w[i];")],
+    "bwd_correction_not_removed": [("const double g = dS[(int64_t)i * dk + j] - beta * w[i] * kt[j];",
+                                    "const double g = dS[(int64_t)i * dk + j];")],
+    "bwd_wrong_checkpoint": [("memcpy(buf, ckpt + m * se,", "memcpy(buf, ckpt + (m > 0 ? m - 1 : 0) * se,")],
+    "bwd_final_gradient_ignored": [("dS[e] = J->d_final ? ", "dS[e] = 0 ? ")],
+}
+
+FORWARD_SUITES = ("test_oracle_pins.py", "test_chunk_rederivation.py")
+BACKWARD_SUITES = ("test_oracle_backward.py",)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS) + sorted(BACKWARD_MUTANTS))
 def test_pins_catch_planted_mistake(name, tmp_path):
     if shutil.which("gcc") is None:
         pytest.skip("no C compiler")
     src = open(SRC).read()
-    for old, new in MUTANTS[name]:
+    edits, suites = (MUTANTS[name], FORWARD_SUITES) if name in MUTANTS else (BACKWARD_MUTANTS[name], BACKWARD_SUITES)
+    for old, new in edits:
         assert old in src, f"mutation anchor not found: {old!r}"
         src = src.replace(old, new, 1)
     inc = os.path.join(ROOT, "include")
@@ -55,7 +76,6 @@ def test_pins_catch_planted_mistake(name, tmp_path):
                     str(csrc), "-lpthread", "-lm"], check=True)
     env = dict(os.environ, KDA_ORACLE_LIB=str(lib))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py"),
-                        os.path.join(ROOT, "tests", "test_chunk_rederivation.py")],
+                        *[os.path.join(ROOT, "tests", f) for f in suites]],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
