@@ -52,7 +52,8 @@ def test_kda_header_symbols_exported(K):
 def test_oracle_header_symbols_exported():
     import oracle
     names = _declared("kda_oracle.h")
-    assert set(names) == {"kda_oracle_snapshot_count", "kda_oracle_run", "kda_recurrent_ref_check"}
+    assert set(names) == {"kda_oracle_snapshot_count", "kda_oracle_run", "kda_recurrent_ref_check",
+                          "kda_oracle_backward"}
     lib = oracle.load()
     for n in names:
         assert hasattr(lib, n), n
