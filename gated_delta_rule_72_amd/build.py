@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_prefill.hip", "kda_layer.hip"]
+SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_prefill.hip", "kda_layer.hip", "kda_backward.hip"]
 # measured device ceilings for the benchmark's roofline figures (include/kda_calib.h)
 CALIB_LIB = os.path.join(PKG, "libkda_calib.so")
 CALIB_SOURCES = ["kda_calib.hip"]

@@ -181,6 +181,38 @@ int check_prefill_args(const kda_shape* shape, int32_t num_seqs, const int64_t* 
   return KDA_OK;
 }
 
+// Workspace of one backward call: the forward's own plan, its o / final
+// scratch and the states after every 64 tokens, the chunk tables, then the
+// per-(chunk, head) fp32 arrays of the backward kernels.
+struct BackwardPlan {
+  PrefillPlan fwd;
+  int64_t n_chunks, n_snap;
+  size_t o_off, fin_off, snap_off, cb_off, sb_off, ws_off, bytes;
+};
+
+BackwardPlan plan_backward(const kda_shape* s, int32_t num_seqs, const int64_t* cu, int cus) {
+  BackwardPlan p{};
+  p.fwd = plan_prefill(s, num_seqs, cu, -1, cus);
+  for (int32_t n = 0; n < num_seqs; ++n) p.n_chunks += (cu[n + 1] - cu[n] + kChunk - 1) / kChunk;
+  p.n_snap = snapshot_slots(num_seqs, cu, kChunk);
+  const size_t H = (size_t)s->num_heads, D = (size_t)s->d_k, T = (size_t)cu[num_seqs];
+  size_t off = round_up(p.fwd.bytes);
+  p.o_off = off;
+  off += round_up(T * H * D * sizeof(float));
+  p.fin_off = off;
+  off += round_up((size_t)num_seqs * H * D * D * sizeof(float));
+  p.snap_off = off;
+  off += round_up((size_t)p.n_snap * H * D * D * sizeof(float));
+  p.cb_off = off;
+  off += round_up(((size_t)num_seqs + 1) * sizeof(int64_t));
+  p.sb_off = off;
+  off += round_up(((size_t)num_seqs + 1) * sizeof(int64_t));
+  p.ws_off = off;
+  off += round_up((size_t)kda::bwd::floats(p.n_chunks * s->num_heads, s->d_k) * sizeof(float));
+  p.bytes = off;
+  return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -402,6 +434,91 @@ int kda_layer_back(const kda_shape* shape, int64_t num_tokens, const float* o, c
   kda::LayerBackArgs a{o, g_logit, norm_w, out, eps, num_tokens * shape->num_heads};
   hipError_t e = kda::launch_layer_back(a, shape->d_v, out_dtype == KDA_BF16, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "layer back launch failed: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return KDA_OK;
+}
+
+int kda_prefill_backward_workspace_size(const kda_shape* shape, int32_t num_seqs,
+                                        const int64_t* cu_seqlens_host, size_t* bytes) {
+  if (!bytes) return fail(KDA_ERR_ARG, "bytes is NULL");
+  int rc = check_shape(shape);
+  if (rc != KDA_OK) return rc;
+  rc = check_cu(num_seqs, cu_seqlens_host);
+  if (rc != KDA_OK) return rc;
+  *bytes = plan_backward(shape, num_seqs, cu_seqlens_host, device_cu_count()).bytes;
+  g_err[0] = '\0';
+  return KDA_OK;
+}
+
+int kda_prefill_backward(const kda_shape* shape, int32_t num_seqs, const int64_t* cu_seqlens_host,
+                         const int64_t* cu_seqlens_dev, const void* q, const void* k, const void* v,
+                         const float* alpha, const float* beta, const float* initial_state, const float* d_o,
+                         const float* d_final_state, float* dq, float* dk, float* dv, float* dalpha,
+                         float* dbeta, float* d_initial_state, void* workspace, size_t workspace_bytes,
+                         void* hip_stream) {
+  int rc = check_shape(shape);
+  if (rc != KDA_OK) return rc;
+  rc = check_cu(num_seqs, cu_seqlens_host);
+  if (rc != KDA_OK) return rc;
+  const int64_t T = cu_seqlens_host[num_seqs];
+  if (num_seqs > 0 && !cu_seqlens_dev) return fail(KDA_ERR_ARG, "cu_seqlens_dev is NULL");
+  if (T > 0 && (!q || !k || !v || !alpha || !beta || !d_o || !dq || !dk || !dv || !dalpha || !dbeta))
+    return fail(KDA_ERR_ARG, "inputs, d_o and the gradient outputs must be non-NULL when T > 0");
+  const uintptr_t a_alpha = shape->gate == KDA_GATE_PER_KEY ? 16 : 4;
+  const PtrReq reqs[] = {{q, 16, "q"}, {k, 16, "k"}, {v, 16, "v"}, {alpha, a_alpha, "alpha"},
+                         {beta, 4, "beta"}, {initial_state, 16, "initial_state"}, {d_o, 4, "d_o"},
+                         {d_final_state, 16, "d_final_state"}, {dq, 4, "dq"}, {dk, 4, "dk"}, {dv, 4, "dv"},
+                         {dalpha, 4, "dalpha"}, {dbeta, 4, "dbeta"}, {d_initial_state, 16, "d_initial_state"},
+                         {cu_seqlens_dev, 8, "cu_seqlens_dev"}, {workspace, 16, "workspace"}};
+  rc = check_align(reqs, (int)(sizeof reqs / sizeof reqs[0]));
+  if (rc != KDA_OK) return rc;
+  if (num_seqs == 0) {
+    g_err[0] = '\0';
+    return KDA_OK;
+  }
+  const BackwardPlan plan = plan_backward(shape, num_seqs, cu_seqlens_host, device_cu_count());
+  if (!workspace || workspace_bytes < plan.bytes)
+    return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", plan.bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  char* ws = static_cast<char*>(workspace);
+  const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const bool bf16 = shape->qkv_dtype == KDA_BF16, pk = shape->gate == KDA_GATE_PER_KEY;
+
+  // 1. the forward again, keeping the state after every 64 tokens
+  kda::PrefillArgs f{};
+  f.q = q; f.k = k; f.v = v; f.alpha = alpha; f.beta = beta; f.init = initial_state;
+  f.o = reinterpret_cast<float*>(ws + plan.o_off);
+  f.final_state = reinterpret_cast<float*>(ws + plan.fin_off);
+  f.snapshots = plan.n_snap > 0 ? reinterpret_cast<float*>(ws + plan.snap_off) : nullptr;
+  f.cu_dev = cu_seqlens_dev;
+  f.num_seqs = num_seqs;
+  f.H = shape->num_heads;
+  f.interval = kChunk;
+  f.seg_chunks = plan.fwd.seg_chunks;
+  f.n_items = plan.fwd.n_items;
+  f.items = reinterpret_cast<kda::PrefillItem*>(ws + plan.fwd.items_off);
+  f.seq_first_item = reinterpret_cast<int32_t*>(ws + plan.fwd.first_off);
+  f.seg_maps = plan.fwd.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.fwd.maps_off) : nullptr;
+  f.seg_states = plan.fwd.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.fwd.states_off) : nullptr;
+  f.seg_inverse = plan.fwd.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.fwd.inverse_off) : nullptr;
+  hipError_t e = kda::launch_prefill(f, shape->d_k, bf16, pk, st);
+  if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "backward: forward launch failed: %s", hipGetErrorString(e));
+
+  // 2. the backward kernels
+  kda::BackwardArgs b{};
+  b.q = q; b.k = k; b.v = v; b.alpha = alpha; b.beta = beta; b.init = initial_state;
+  b.d_o = d_o; b.d_final = d_final_state;
+  b.dq = dq; b.dk = dk; b.dv = dv; b.dalpha = dalpha; b.dbeta = dbeta; b.d_init = d_initial_state;
+  b.cu_dev = cu_seqlens_dev;
+  b.num_seqs = num_seqs;
+  b.H = shape->num_heads;
+  b.n_chunks = plan.n_chunks;
+  b.states = reinterpret_cast<const float*>(ws + plan.snap_off);
+  b.chunk_base = reinterpret_cast<int64_t*>(ws + plan.cb_off);
+  b.snap_base = reinterpret_cast<int64_t*>(ws + plan.sb_off);
+  b.ws = reinterpret_cast<float*>(ws + plan.ws_off);
+  e = kda::launch_backward(b, shape->d_k, bf16, pk, st);
+  if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "backward launch failed: %s", hipGetErrorString(e));
   g_err[0] = '\0';
   return KDA_OK;
 }

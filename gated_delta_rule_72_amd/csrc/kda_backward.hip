@@ -1,0 +1,496 @@
+// kda_backward.hip — backward pass of the chunked prefill on gfx950.
+//
+// Gradients of the loss sum_t <dO_t, o_t> + sum_n <dS_n, S_final,n> with
+// respect to q, k, v, the gate, beta and the initial state, for the update of
+// page "Modele hybrydowe: co Gated DeltaNet zastępuje w cache KV"
+// (trefon.com), section "Gated DeltaNet: dodaj zanik", in the chunked form the
+// forward uses (closing paragraph of "Co stan rekurencyjny zmienia przy
+// serwowaniu": inside a chunk everything is a dense product; only chunk to
+// chunk is sequential). With Gamma the in-chunk cumulative natural-log decay,
+// a reference row c (row 31, or the last row of a shorter chunk: it cancels
+// in every product and keeps each factor inside fp32), and per chunk
+//   Kp = K e^(G-G_c), Km = K e^(G_c-G), Qp = Q e^(G-G_c), Ka = K e^G,
+//   Qa = Q e^G, Kt = K e^(G_n-G), P = Kp Km^T, A = (I + strict_lower(B P))^-1,
+//   X = B Ka, Y = B V, W = A X, U = A Y - W S0^T, Bm = lower(Qp Km^T)
+// (B = Diag(beta)), the forward is O = Qa S0^T + Bm U and
+// S_n = S0 Diag(e^G_n) + U^T Kt, and the gradients are
+//   Z = Bm^T dO, E = dO^T Qa - Z^T W                    (before the scan)
+//   dS_start = dS_end (Diag(e^G_n) - Kt^T W) + E         (reverse scan)
+//   dU = Z + Kt dS_n^T, dBm = lower(dO U^T), dQp = dBm Km, dQa = dO S0,
+//   dKm = dBm^T Qp + dL^T B Kp, dKt = U dS_n, dW = -dU S0,
+//   dA = dW X^T + dU Y^T, dX = A^T dW, dY = A^T dU,
+//   dL = strict_lower(-A^T dA A^T), dKp = B dL Km,
+// then per element the chain through the decay factors and a reverse
+// cumulative sum over rows gives d(log a), and d(alpha) = d(log a) / alpha.
+//
+// Structure: the forward prefill (snapshots every 64 tokens) supplies every
+// chunk's start state; then per (chunk, head) unit, all units in parallel:
+// prep (factors), one batched fp32 MFMA GEMM per product (64 x 64 output tiles
+// staged through LDS), the 64 x 64 unit-lower inverse (one column per lane);
+// the reverse scan over chunks per (sequence, head) keeps dS^T in MFMA
+// accumulator registers (one 16-column slice per wavefront); a final kernel
+// assembles dq, dk, dv, dalpha and dbeta. Everything is fp32 (16x16x4 fp32
+// MFMA); a padded row of a short chunk has q = k = v = dO = 0, beta = 0 and
+// no decay, which leaves every product unchanged.
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+using namespace bwd;
+constexpr int C = 64;  // chunk length
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load1(const void* base, int64_t idx) {
+  if constexpr (BF16) return bf16_bits_to_f32(static_cast<const uint16_t*>(base)[idx]);
+  else return static_cast<const float*>(base)[idx];
+}
+
+// chunk_base[n] = sum over earlier sequences of ceil(len / 64) (chunks);
+// snap_base[n] = the same of floor(len / 64) (64-token state slots).
+__global__ __launch_bounds__(1024) void chunk_base_kernel(const int64_t* cu, int32_t N, int64_t* chunk_base,
+                                                          int64_t* snap_base) {
+  __shared__ int64_t pc[1024], ps[1024];
+  const int tid = threadIdx.x;
+  const int64_t per = ((int64_t)N + 1023) / 1024;
+  const int64_t n0 = tid * per, n1 = n0 + per < (int64_t)N ? n0 + per : (int64_t)N;
+  int64_t sc = 0, ss = 0;
+  for (int64_t n = n0; n < n1; ++n) {
+    const int64_t len = cu[n + 1] - cu[n];
+    sc += (len + C - 1) / C;
+    ss += len / C;
+  }
+  pc[tid] = sc;
+  ps[tid] = ss;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int64_t vc = tid >= off ? pc[tid - off] : 0, vs = tid >= off ? ps[tid - off] : 0;
+    __syncthreads();
+    pc[tid] += vc;
+    ps[tid] += vs;
+    __syncthreads();
+  }
+  int64_t bc = pc[tid] - sc, bs = ps[tid] - ss;
+  for (int64_t n = n0; n < n1; ++n) {
+    chunk_base[n] = bc;
+    snap_base[n] = bs;
+    const int64_t len = cu[n + 1] - cu[n];
+    bc += (len + C - 1) / C;
+    bs += len / C;
+  }
+  if (tid == 1023) {
+    chunk_base[N] = pc[1023];
+    snap_base[N] = ps[1023];
+  }
+}
+
+struct ChunkPos {
+  int32_t n, len;
+  int64_t c, t0;
+};
+// The sequence holding chunk ch: the last n with chunk_base[n] <= ch (empty
+// sequences share their successor's base and are skipped that way).
+__device__ __forceinline__ ChunkPos chunk_pos(const BackwardArgs& a, int64_t ch) {
+  int lo = 0, hi = a.num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.chunk_base[mid] <= ch) lo = mid; else hi = mid - 1;
+  }
+  ChunkPos p;
+  p.n = lo;
+  p.c = ch - a.chunk_base[lo];
+  p.t0 = a.cu_dev[lo] + C * p.c;
+  const int64_t rem = a.cu_dev[lo + 1] - p.t0;
+  p.len = (int32_t)(rem < C ? rem : C);
+  return p;
+}
+
+__device__ __forceinline__ int ref_row(int len) { return (len < 32 ? len : 32) - 1; }
+
+// ---- prep: decay factors, scaled operands, the chunk's start state ---------
+template <int D, bool BF16, bool PER_KEY>
+__global__ __launch_bounds__(256) void prep_kernel(BackwardArgs a) {
+  constexpr int LDG = D + 1;
+  __shared__ float sG[C * LDG];
+  __shared__ float sB[C];
+  const int64_t units = a.n_chunks * a.H;
+  const int64_t b = blockIdx.x;
+  const int h = (int)(b % a.H);
+  const ChunkPos p = chunk_pos(a, b / a.H);
+  const int tid = threadIdx.x;
+  if (tid < D) {                        // Gamma per channel: running sum of ln alpha
+    float g = 0.f;
+    for (int r = 0; r < C; ++r) {
+      if (r < p.len) {
+        const int64_t t = p.t0 + r;
+        g += __logf(PER_KEY ? a.alpha[(t * a.H + h) * D + tid] : a.alpha[t * a.H + h]);
+      }
+      sG[r * LDG + tid] = g;
+    }
+  }
+  if (tid < C) sB[tid] = tid < p.len ? a.beta[(p.t0 + tid) * a.H + h] : 0.f;
+  __syncthreads();
+  const int cref = ref_row(p.len);
+  float* ws = a.ws;
+  for (int idx = tid; idx < C * D; idx += 256) {
+    const int r = idx / D, j = idx % D;
+    float qv = 0.f, kv = 0.f, vv = 0.f, dov = 0.f;
+    if (r < p.len) {
+      const int64_t e = ((p.t0 + r) * a.H + h) * D + j;
+      qv = load1<BF16>(a.q, e);
+      kv = load1<BF16>(a.k, e);
+      vv = load1<BF16>(a.v, e);
+      dov = a.d_o[e];
+    }
+    const float G = sG[r * LDG + j], Gc = sG[cref * LDG + j], Gn = sG[(C - 1) * LDG + j];
+    const float be = sB[r];
+    const float eRel = __expf(G - Gc), eInv = __expf(Gc - G), eAbs = __expf(G), eTail = __expf(Gn - G);
+    const int64_t o = b * C * D + idx;
+    ws[nd_off(KP, units, D) + o] = kv * eRel;
+    ws[nd_off(KM, units, D) + o] = kv * eInv;
+    ws[nd_off(QP, units, D) + o] = qv * eRel;
+    ws[nd_off(KA, units, D) + o] = kv * eAbs;
+    ws[nd_off(XA, units, D) + o] = be * (kv * eAbs);
+    ws[nd_off(QA, units, D) + o] = qv * eAbs;
+    ws[nd_off(KT, units, D) + o] = kv * eTail;
+    ws[nd_off(VF, units, D) + o] = vv;
+    ws[nd_off(YB, units, D) + o] = be * vv;
+    ws[nd_off(DOF, units, D) + o] = dov;
+    ws[nd_off(XP, units, D) + o] = be * (kv * eRel);
+    ws[nd_off(GG, units, D) + o] = G;
+  }
+  if (tid < D) ws[egn_off(units, D) + b * D + tid] = __expf(sG[(C - 1) * LDG + tid]);
+  if (tid < C) ws[beta_off(units, D) + b * C + tid] = sB[tid];
+  // start state of the chunk: the initial state (or 0) for a sequence's first
+  // chunk, else the forward state after its first 64 c tokens
+  const float* src = nullptr;
+  if (p.c == 0) {
+    if (a.init) src = a.init + ((int64_t)p.n * a.H + h) * D * D;
+  } else {
+    src = a.states + ((a.snap_base[p.n] + p.c - 1) * a.H + h) * D * D;
+  }
+  float* dst = ws + dd_off(S0M, units, D) + b * D * D;
+  for (int e = tid * 4; e < D * D; e += 1024)
+    *reinterpret_cast<f32x4*>(dst + e) = src ? *reinterpret_cast<const f32x4*>(src + e) : f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// ---- batched GEMM: C_b = alpha op(A_b) op(B_b) (+ C_b), fp32 MFMA ----------
+struct GemmArgs {
+  const float *A, *B;
+  float* C;
+  const float* rs;           // per-row scale of the product (or null)
+  int64_t sA, sB, sC, srs;   // per-unit strides
+  int32_t lda, ldb, ldc, M, N, K;
+  float alpha;
+  int32_t accumulate;        // add into C
+  int32_t mask;              // 0: none, 1: keep row > col, 2: keep row >= col
+};
+
+// One workgroup = one 64 x 64 output tile of one unit; four wavefronts of 16
+// rows. K advances in blocks of 32 staged in LDS: A as [m][k] (row stride 36)
+// and B as [k][n] (row stride 80), strides that put the 64 lanes of each
+// operand read on distinct banks.
+template <bool TA, bool TB>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
+  constexpr int KB = 32, LDA = 36, LDB = 80;
+  __shared__ float As[64 * LDA];
+  __shared__ float Bs[KB * LDB];
+  const int tn = g.N / 64, tiles = (g.M / 64) * tn;
+  const int64_t b = blockIdx.x / tiles;
+  const int tile = (int)(blockIdx.x % tiles);
+  const int m0 = (tile / tn) * 64, n0 = (tile % tn) * 64;
+  const float* A = g.A + b * g.sA;
+  const float* B = g.B + b * g.sB;
+  float* Cp = g.C + b * g.sC;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, gq = lane >> 4;
+  f32x4 acc[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < g.K; k0 += KB) {
+#pragma unroll
+    for (int e = tid; e < 512; e += 256) {
+      if constexpr (!TA) {
+        const int r = e >> 3, c = (e & 7) * 4;
+        *reinterpret_cast<f32x4*>(As + r * LDA + c) =
+            *reinterpret_cast<const f32x4*>(A + (int64_t)(m0 + r) * g.lda + k0 + c);
+      } else {
+        const int kk = e >> 4, c = (e & 15) * 4;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(A + (int64_t)(k0 + kk) * g.lda + m0 + c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) As[(c + i) * LDA + kk] = v[i];
+      }
+      if constexpr (!TB) {
+        const int kk = e >> 4, c = (e & 15) * 4;
+        *reinterpret_cast<f32x4*>(Bs + kk * LDB + c) =
+            *reinterpret_cast<const f32x4*>(B + (int64_t)(k0 + kk) * g.ldb + n0 + c);
+      } else {
+        const int n = e >> 3, c = (e & 7) * 4;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(B + (int64_t)(n0 + n) * g.ldb + k0 + c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Bs[(c + i) * LDB + n] = v[i];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < KB / 4; ++ks) {
+      const float av = As[(16 * w + l16) * LDA + 4 * ks + gq];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[t] = mfma4(av, Bs[(4 * ks + gq) * LDB + 16 * t + l16], acc[t]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = m0 + 16 * w + 4 * gq + i, col = n0 + 16 * t + l16;
+      float x = g.alpha * acc[t][i];
+      if ((g.mask == 1 && row <= col) || (g.mask == 2 && row < col)) x = 0.f;
+      if (g.rs) x *= g.rs[b * g.srs + row];
+      float* cp = Cp + (int64_t)row * g.ldc + col;
+      *cp = g.accumulate ? *cp + x : x;
+    }
+}
+
+// ---- (I + L)^-1 with L = strict_lower(Diag(beta) P): one column per lane --
+__global__ __launch_bounds__(64) void inverse_kernel(BackwardArgs a, int32_t d) {
+  __shared__ float Ls[C * (C + 1)];
+  const int64_t units = a.n_chunks * a.H, b = blockIdx.x;
+  const float* P = a.ws + nn_off(PM, units, d) + b * C * C;
+  const float* beta = a.ws + beta_off(units, d) + b * C;
+  float* Ao = a.ws + nn_off(AM, units, d) + b * C * C;
+  const int j = threadIdx.x;
+  for (int r = 0; r < C; ++r) Ls[r * (C + 1) + j] = j < r ? beta[r] * P[r * C + j] : 0.f;
+  __syncthreads();
+  float x[C];
+#pragma unroll
+  for (int i = 0; i < C; ++i) {        // forward substitution down column j
+    float s = i == j ? 1.f : 0.f;
+#pragma unroll
+    for (int m = 0; m < i; ++m) s -= Ls[i * (C + 1) + m] * x[m];
+    x[i] = s;
+  }
+#pragma unroll
+  for (int i = 0; i < C; ++i) Ao[i * C + j] = x[i];
+}
+
+// ---- reverse scan over chunks: dS_start = dS_end (Diag(e^G_n) - Kt^T W) + E ----
+// Works on R = dS^T (d_k x d_v): R_start = Diag(e^G_n) R_end - W^T (Kt R_end) + E^T.
+// Wavefront w owns columns 16w..16w+15 of R as D/16 accumulator tiles: lane
+// (g, l) holds R(16t + 4g + i, 16w + l), i.e. dS(16w + l, 16t + 4g + i). Both
+// products contract over the tile rows, which enter as the permuted-K operand.
+template <int D>
+__global__ __launch_bounds__(D * 4) void scan_kernel(BackwardArgs a) {
+  constexpr int LD = D + 4;
+  __shared__ float Kts[C * LD];
+  __shared__ float Ws[C * LD];
+  const int n = (int)(blockIdx.x / a.H), h = (int)(blockIdx.x % a.H);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, gq = lane >> 4;
+  const int64_t units = a.n_chunks * a.H, DD = (int64_t)D * D;
+  const int64_t rowoff = (int64_t)(16 * w + l16) * D;
+  f32x4 R[D / 16];
+  const float* df = a.d_final ? a.d_final + ((int64_t)n * a.H + h) * DD + rowoff : nullptr;
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t)
+    R[t] = df ? *reinterpret_cast<const f32x4*>(df + 16 * t + 4 * gq) : f32x4{0.f, 0.f, 0.f, 0.f};
+  const int64_t cb = a.chunk_base[n], nch = a.chunk_base[n + 1] - cb;
+  for (int64_t c = nch - 1; c >= 0; --c) {
+    const int64_t b = (cb + c) * a.H + h;
+    float* dsn = a.ws + dd_off(DSN, units, D) + b * DD + rowoff;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) *reinterpret_cast<f32x4*>(dsn + 16 * t + 4 * gq) = R[t];
+    const float* kt = a.ws + nd_off(KT, units, D) + b * C * D;
+    const float* wm = a.ws + nd_off(WM, units, D) + b * C * D;
+    for (int e = tid; e < C * D / 4; e += D * 4) {
+      const int r = e / (D / 4), c4 = (e % (D / 4)) * 4;
+      *reinterpret_cast<f32x4*>(Kts + r * LD + c4) = *reinterpret_cast<const f32x4*>(kt + (int64_t)r * D + c4);
+      *reinterpret_cast<f32x4*>(Ws + r * LD + c4) = *reinterpret_cast<const f32x4*>(wm + (int64_t)r * D + c4);
+    }
+    __syncthreads();
+    f32x4 V1[4];                       // Kt R_w: chunk rows 16s.., columns 16w..
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      V1[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        const f32x4 av = *reinterpret_cast<const f32x4*>(Kts + (16 * s + l16) * LD + 16 * t + 4 * gq);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) V1[s] = mfma4(av[i], R[t][i], V1[s]);
+      }
+    }
+    const float* E = a.ws + dd_off(EM, units, D) + b * DD + rowoff;
+    const float* eg = a.ws + egn_off(units, D) + b * D;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x = mfma4(Ws[(16 * s + 4 * gq + i) * LD + 16 * t + l16], V1[s][i], x);
+      const f32x4 ev = *reinterpret_cast<const f32x4*>(E + 16 * t + 4 * gq);
+      const f32x4 gv = *reinterpret_cast<const f32x4*>(eg + 16 * t + 4 * gq);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) R[t][i] = gv[i] * R[t][i] - x[i] + ev[i];
+    }
+    __syncthreads();
+  }
+  if (a.d_init) {
+    float* di = a.d_init + ((int64_t)n * a.H + h) * DD + rowoff;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) *reinterpret_cast<f32x4*>(di + 16 * t + 4 * gq) = R[t];
+  }
+}
+
+// ---- assembly: dq, dk, dv, dbeta, and dalpha through the decay factors ----
+template <int D, bool PER_KEY>
+__global__ __launch_bounds__(256) void assemble_kernel(BackwardArgs a) {
+  __shared__ float sLn[PER_KEY ? 1 : C * (D + 1)];
+  const int64_t units = a.n_chunks * a.H;
+  const int64_t b = blockIdx.x;
+  const int h = (int)(b % a.H);
+  const ChunkPos p = chunk_pos(a, b / a.H);
+  const int tid = threadIdx.x;
+  const float* ws = a.ws;
+  auto nd = [&](int arr) { return ws + nd_off(arr, units, D) + b * C * D; };
+  auto nn = [&](int arr) { return ws + nn_off(arr, units, D) + b * C * C; };
+  const float* beta = ws + beta_off(units, D) + b * C;
+  {                                     // dbeta: four lanes per row
+    const int r = tid >> 2, part = tid & 3;
+    const float *dY = nd(DY), *V = nd(VF), *dX = nd(DX), *Ka = nd(KA), *dL = nn(DLM), *P = nn(PM);
+    float s = 0.f;
+    for (int j = part; j < D; j += 4) s += dY[r * D + j] * V[r * D + j] + dX[r * D + j] * Ka[r * D + j];
+    for (int i = part; i < C; i += 4) s += dL[r * C + i] * P[r * C + i];
+    s += __shfl_xor(s, 1, 4);
+    s += __shfl_xor(s, 2, 4);
+    if (part == 0 && r < p.len) a.dbeta[(p.t0 + r) * a.H + h] = s;
+  }
+  if (tid < D) {                        // one channel per thread, rows in reverse
+    const int j = tid;
+    const float *G = nd(GG), *dQp = nd(DQP), *dQa = nd(DQA), *dKp = nd(DKP), *dKm = nd(DKM), *dX = nd(DX),
+                *dKt = nd(DKT), *dY = nd(DY), *Qp = nd(QP), *Qa = nd(QA), *Kp = nd(KP), *Km = nd(KM),
+                *Ka = nd(KA), *Kt = nd(KT);
+    const float* dSn = ws + dd_off(DSN, units, D) + b * D * D;
+    const float* S0 = ws + dd_off(S0M, units, D) + b * D * D;
+    // gradient of G_n (the last row's Gamma), counted in every row's sum below
+    float acc = 0.f, st = 0.f;
+    for (int r = 0; r < C; ++r) acc += dKt[r * D + j] * Kt[r * D + j];
+    for (int i = 0; i < D; ++i) st += dSn[(int64_t)i * D + j] * S0[(int64_t)i * D + j];
+    acc += st * ws[egn_off(units, D) + b * D + j];
+    const float Gc = G[ref_row(p.len) * D + j], Gn = G[(C - 1) * D + j];
+    for (int r = C - 1; r >= 0; --r) {
+      const int e = r * D + j;
+      const float g = G[e];
+      const float eRel = __expf(g - Gc), eInv = __expf(Gc - g), eAbs = __expf(g), eTail = __expf(Gn - g);
+      const float dKa = beta[r] * dX[e];
+      acc += dQp[e] * Qp[e] + dQa[e] * Qa[e] + dKp[e] * Kp[e] - dKm[e] * Km[e] + dKa * Ka[e] - dKt[e] * Kt[e];
+      if (r < p.len) {
+        const int64_t o = ((p.t0 + r) * a.H + h) * D + j;
+        a.dq[o] = dQp[e] * eRel + dQa[e] * eAbs;
+        a.dk[o] = dKp[e] * eRel + dKm[e] * eInv + dKa * eAbs + dKt[e] * eTail;
+        a.dv[o] = beta[r] * dY[e];
+        if constexpr (PER_KEY) a.dalpha[o] = acc / a.alpha[o];
+        else sLn[r * (D + 1) + j] = acc;
+      }
+    }
+  }
+  if constexpr (!PER_KEY) {
+    __syncthreads();
+    if (tid < p.len) {
+      float s = 0.f;
+      for (int j = 0; j < D; ++j) s += sLn[tid * (D + 1) + j];
+      const int64_t th = (p.t0 + tid) * a.H + h;
+      a.dalpha[th] = s / a.alpha[th];
+    }
+  }
+}
+
+hipError_t gemm(bool ta, bool tb, int64_t units, int d, int M, int N, int K, const float* A, int lda, int64_t sA,
+                const float* B, int ldb, int64_t sB, float* Cm, int ldc, int64_t sC, float alpha, bool accumulate,
+                int mask, const float* rs, hipStream_t s) {
+  GemmArgs g{A, B, Cm, rs, sA, sB, sC, C, lda, ldb, ldc, M, N, K, alpha, accumulate ? 1 : 0, mask};
+  (void)d;
+  const dim3 grid((unsigned)(units * (M / 64) * (N / 64)));
+  if (!ta && !tb) hipLaunchKernelGGL((gemm_kernel<false, false>), grid, dim3(256), 0, s, g);
+  else if (!ta && tb) hipLaunchKernelGGL((gemm_kernel<false, true>), grid, dim3(256), 0, s, g);
+  else if (ta && !tb) hipLaunchKernelGGL((gemm_kernel<true, false>), grid, dim3(256), 0, s, g);
+  else hipLaunchKernelGGL((gemm_kernel<true, true>), grid, dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
+template <int D, bool BF16, bool PK>
+hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(chunk_base_kernel, dim3(1), dim3(1024), 0, s, a.cu_dev, a.num_seqs, a.chunk_base,
+                     a.snap_base);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t U = a.n_chunks * a.H;
+  if (U > 0) {
+    float* w = a.ws;
+    auto ND = [&](int arr) { return w + nd_off(arr, U, D); };
+    auto NN = [&](int arr) { return w + nn_off(arr, U, D); };
+    auto DDp = [&](int arr) { return w + dd_off(arr, U, D); };
+    const int64_t sND = (int64_t)C * D, sNN = (int64_t)C * C, sDD = (int64_t)D * D;
+    hipLaunchKernelGGL((prep_kernel<D, BF16, PK>), dim3((unsigned)U), dim3(256), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+#define G_(...) if ((e = gemm(__VA_ARGS__, s)) != hipSuccess) return e
+    // forward quantities
+    G_(false, true, U, D, C, C, D, ND(KP), D, sND, ND(KM), D, sND, NN(PM), C, sNN, 1.f, false, 0, nullptr);
+    hipLaunchKernelGGL(inverse_kernel, dim3((unsigned)U), dim3(64), 0, s, a, (int32_t)D);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    G_(false, false, U, D, C, D, C, NN(AM), C, sNN, ND(XA), D, sND, ND(WM), D, sND, 1.f, false, 0, nullptr);
+    G_(false, false, U, D, C, D, C, NN(AM), C, sNN, ND(YB), D, sND, ND(UM), D, sND, 1.f, false, 0, nullptr);
+    G_(false, true, U, D, C, D, D, ND(WM), D, sND, DDp(S0M), D, sDD, ND(UM), D, sND, -1.f, true, 0, nullptr);
+    G_(false, true, U, D, C, C, D, ND(QP), D, sND, ND(KM), D, sND, NN(BM), C, sNN, 1.f, false, 2, nullptr);
+    // inputs of the reverse scan
+    G_(true, false, U, D, C, D, C, NN(BM), C, sNN, ND(DOF), D, sND, ND(ZU), D, sND, 1.f, false, 0, nullptr);
+    G_(true, false, U, D, D, D, C, ND(DOF), D, sND, ND(QA), D, sND, DDp(EM), D, sDD, 1.f, false, 0, nullptr);
+    G_(true, false, U, D, D, D, C, ND(ZU), D, sND, ND(WM), D, sND, DDp(EM), D, sDD, -1.f, true, 0, nullptr);
+  }
+  hipLaunchKernelGGL((scan_kernel<D>), dim3((unsigned)((int64_t)a.num_seqs * a.H)), dim3(D * 4), 0, s, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (U > 0) {
+    float* w = a.ws;
+    auto ND = [&](int arr) { return w + nd_off(arr, U, D); };
+    auto NN = [&](int arr) { return w + nn_off(arr, U, D); };
+    auto DDp = [&](int arr) { return w + dd_off(arr, U, D); };
+    const int64_t sND = (int64_t)C * D, sNN = (int64_t)C * C, sDD = (int64_t)D * D;
+    // local gradients
+    G_(false, true, U, D, C, D, D, ND(KT), D, sND, DDp(DSN), D, sDD, ND(ZU), D, sND, 1.f, true, 0, nullptr);
+    G_(false, true, U, D, C, C, D, ND(DOF), D, sND, ND(UM), D, sND, NN(DBM), C, sNN, 1.f, false, 2, nullptr);
+    G_(false, false, U, D, C, D, C, NN(DBM), C, sNN, ND(KM), D, sND, ND(DQP), D, sND, 1.f, false, 0, nullptr);
+    G_(false, false, U, D, C, D, D, ND(DOF), D, sND, DDp(S0M), D, sDD, ND(DQA), D, sND, 1.f, false, 0, nullptr);
+    G_(true, false, U, D, C, D, C, NN(DBM), C, sNN, ND(QP), D, sND, ND(DKM), D, sND, 1.f, false, 0, nullptr);
+    G_(false, false, U, D, C, D, D, ND(UM), D, sND, DDp(DSN), D, sDD, ND(DKT), D, sND, 1.f, false, 0, nullptr);
+    G_(false, false, U, D, C, D, D, ND(ZU), D, sND, DDp(S0M), D, sDD, ND(DW), D, sND, -1.f, false, 0, nullptr);
+    G_(false, true, U, D, C, C, D, ND(DW), D, sND, ND(XA), D, sND, NN(DAM), C, sNN, 1.f, false, 0, nullptr);
+    G_(false, true, U, D, C, C, D, ND(ZU), D, sND, ND(YB), D, sND, NN(DAM), C, sNN, 1.f, true, 0, nullptr);
+    G_(true, false, U, D, C, D, C, NN(AM), C, sNN, ND(DW), D, sND, ND(DX), D, sND, 1.f, false, 0, nullptr);
+    G_(true, false, U, D, C, D, C, NN(AM), C, sNN, ND(ZU), D, sND, ND(DY), D, sND, 1.f, false, 0, nullptr);
+    G_(false, true, U, D, C, C, C, NN(DAM), C, sNN, NN(AM), C, sNN, NN(TM), C, sNN, 1.f, false, 0, nullptr);
+    G_(true, false, U, D, C, C, C, NN(AM), C, sNN, NN(TM), C, sNN, NN(DLM), C, sNN, -1.f, false, 1, nullptr);
+    G_(false, false, U, D, C, D, C, NN(DLM), C, sNN, ND(KM), D, sND, ND(DKP), D, sND, 1.f, false, 0,
+       w + beta_off(U, D));
+    G_(true, false, U, D, C, D, C, NN(DLM), C, sNN, ND(XP), D, sND, ND(DKM), D, sND, 1.f, true, 0, nullptr);
+#undef G_
+    hipLaunchKernelGGL((assemble_kernel<D, PK>), dim3((unsigned)U), dim3(256), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BackwardArgs& a, int d, bool bf16, bool per_key, hipStream_t s) {
+  if (d == 64) {
+    if (bf16) return per_key ? backward_t<64, true, true>(a, s) : backward_t<64, true, false>(a, s);
+    return per_key ? backward_t<64, false, true>(a, s) : backward_t<64, false, false>(a, s);
+  }
+  if (bf16) return per_key ? backward_t<128, true, true>(a, s) : backward_t<128, true, false>(a, s);
+  return per_key ? backward_t<128, false, true>(a, s) : backward_t<128, false, false>(a, s);
+}
+
+}  // namespace kda

@@ -113,4 +113,42 @@ struct LayerBackArgs {
 };
 hipError_t launch_layer_back(const LayerBackArgs& a, int d, bool out_bf16, hipStream_t s);
 
+// Backward pass of the chunked prefill (gradients of the token recurrence).
+// Per (chunk, head) unit b = chunk * H + h, the workspace holds fp32 arrays of
+// 64 x D (chunk rows x channels), 64 x 64 and D x D, each as one region of
+// n_units consecutive blocks, followed by exp(Gamma_n) [D] and beta [64].
+namespace bwd {
+enum ArrND { KP, KM, QP, KA, XA, QA, KT, VF, YB, DOF, XP, WM, UM, ZU, DQP, DQA, DKM, DKT, DW, DX, DY, DKP, GG, N_ND };
+enum ArrNN { PM, AM, BM, DBM, DAM, TM, DLM, N_NN };
+enum ArrDD { S0M, DSN, EM, N_DD };
+__host__ __device__ constexpr int64_t nd_off(int a, int64_t units, int d) { return (int64_t)a * units * 64 * d; }
+__host__ __device__ constexpr int64_t nn_off(int a, int64_t units, int d) {
+  return nd_off(N_ND, units, d) + (int64_t)a * units * 64 * 64;
+}
+__host__ __device__ constexpr int64_t dd_off(int a, int64_t units, int d) {
+  return nn_off(N_NN, units, d) + (int64_t)a * units * d * d;
+}
+__host__ __device__ constexpr int64_t egn_off(int64_t units, int d) { return dd_off(N_DD, units, d); }
+__host__ __device__ constexpr int64_t beta_off(int64_t units, int d) { return egn_off(units, d) + units * d; }
+__host__ __device__ constexpr int64_t floats(int64_t units, int d) { return beta_off(units, d) + units * 64; }
+}  // namespace bwd
+
+struct BackwardArgs {
+  const void *q, *k, *v;
+  const float *alpha, *beta;
+  const float* init;         // [N,H,dv,dk] or null
+  const float* d_o;          // [T,H,dv]
+  const float* d_final;      // [N,H,dv,dk] or null
+  float *dq, *dk, *dv, *dalpha, *dbeta;
+  float* d_init;             // [N,H,dv,dk] or null
+  const int64_t* cu_dev;     // [N+1]
+  int32_t num_seqs, H;
+  int64_t n_chunks;          // chunks over all sequences
+  const float* states;       // forward states after every 64 tokens, snapshot slot order
+  int64_t* chunk_base;       // workspace [N+1]: first chunk of each sequence
+  int64_t* snap_base;        // workspace [N+1]: first 64-token state slot of each sequence
+  float* ws;                 // workspace: bwd::floats(n_chunks * H, d) fp32
+};
+hipError_t launch_backward(const BackwardArgs& a, int d, bool bf16, bool per_key, hipStream_t s);
+
 }  // namespace kda

@@ -57,6 +57,9 @@ def load() -> ctypes.CDLL:
         "kda_layer_front": ([P, I32, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, P, P],
                             ctypes.c_int),
         "kda_layer_back": ([P, I64, P, P, P, ctypes.c_float, I32, P, P], ctypes.c_int),
+        "kda_prefill_backward_workspace_size": ([P, I32, P, P], ctypes.c_int),
+        "kda_prefill_backward": ([P, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+                                 ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -68,7 +71,7 @@ def load() -> ctypes.CDLL:
 
 EXPORTED = ("kda_abi_version", "kda_last_error", "kda_snapshot_count", "kda_prefill_workspace_size",
             "kda_prefill_chunked", "kda_decode_step", "kda_decode_tokens", "kda_layer_front",
-            "kda_layer_back")
+            "kda_layer_back", "kda_prefill_backward_workspace_size", "kda_prefill_backward")
 
 
 def _check(fn: str, rc: int) -> None:
@@ -166,6 +169,27 @@ def kda_layer_back(shape: KdaShape, num_tokens: int, o, g_logit, norm_w, eps: fl
     _check("kda_layer_back", load().kda_layer_back(
         ctypes.byref(shape), int(num_tokens), _ptr(o), _ptr(g_logit), _ptr(norm_w), float(eps), int(out_dtype),
         _ptr(out), s))
+
+
+def kda_prefill_backward_workspace_size(shape: KdaShape, cu_seqlens_host: torch.Tensor) -> int:
+    cu = cu_seqlens_host.to("cpu", torch.int64).contiguous()
+    out = ctypes.c_size_t(0)
+    _check("kda_prefill_backward_workspace_size",
+           load().kda_prefill_backward_workspace_size(ctypes.byref(shape), cu.numel() - 1, _ptr(cu),
+                                                      ctypes.byref(out)))
+    return out.value
+
+
+def kda_prefill_backward(shape: KdaShape, cu_seqlens_host: torch.Tensor, cu_seqlens_dev: torch.Tensor,
+                         q, k, v, alpha, beta, initial_state, d_o, d_final_state, dq, dk, dv, dalpha, dbeta,
+                         d_initial_state, workspace: torch.Tensor, stream=None) -> None:
+    cu = cu_seqlens_host.to("cpu", torch.int64).contiguous()
+    s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream_ptr(q.device)
+    _check("kda_prefill_backward", load().kda_prefill_backward(
+        ctypes.byref(shape), cu.numel() - 1, _ptr(cu), _ptr(cu_seqlens_dev), _ptr(q), _ptr(k), _ptr(v),
+        _ptr(alpha), _ptr(beta), _ptr(initial_state), _ptr(d_o), _ptr(d_final_state), _ptr(dq), _ptr(dk),
+        _ptr(dv), _ptr(dalpha), _ptr(dbeta), _ptr(d_initial_state), _ptr(workspace),
+        ctypes.c_size_t(workspace.numel() * workspace.element_size()), s))
 
 
 # ---- convenience wrappers: allocate outputs with torch, then call the ABI ----
@@ -289,3 +313,34 @@ def layer_back(o: torch.Tensor, g_logit: torch.Tensor, norm_w: torch.Tensor, eps
     out = torch.empty((T, H, dv), dtype=out_dtype, device=o.device)
     kda_layer_back(shape, T, o, g_logit, norm_w, eps, KDA_BF16 if out_dtype == torch.bfloat16 else KDA_F32, out)
     return out
+
+
+def prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
+                     d_o: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None,
+                     initial_state: Optional[torch.Tensor] = None, d_final_state: Optional[torch.Tensor] = None,
+                     cu_seqlens_host: Optional[torch.Tensor] = None, want_d_initial: bool = True):
+    """Gradients of sum <d_o, o> + sum <d_final_state, final_state> of
+    prefill_chunked. Returns (dq, dk, dv, dalpha, dbeta, d_initial_state or
+    None), all fp32."""
+    T, H, dk_ = q.shape
+    dv_ = v.shape[2]
+    dev = q.device
+    if cu_seqlens is None:
+        cu_seqlens = torch.tensor([0, T], dtype=torch.int64, device=dev)
+    if cu_seqlens_host is None:
+        cu_seqlens_host = cu_seqlens.to("cpu")
+    cu_dev = cu_seqlens.to(dev, torch.int64).contiguous()
+    N = cu_seqlens_host.numel() - 1
+    _contig(q, k, v, alpha, beta, d_o, initial_state, d_final_state)
+    shape = make_shape(H, dk_, dv_, q.dtype, alpha.dim() == 3)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq, dk = torch.empty((T, H, dk_), **f32), torch.empty((T, H, dk_), **f32)
+    dv = torch.empty((T, H, dv_), **f32)
+    dalpha = torch.empty(alpha.shape, **f32)
+    dbeta = torch.empty((T, H), **f32)
+    d_init = torch.empty((N, H, dv_, dk_), **f32) if want_d_initial else None
+    ws = torch.empty(max(kda_prefill_backward_workspace_size(shape, cu_seqlens_host), 1), dtype=torch.uint8,
+                     device=dev)
+    kda_prefill_backward(shape, cu_seqlens_host, cu_dev, q, k, v, alpha, beta, initial_state, d_o, d_final_state,
+                         dq, dk, dv, dalpha, dbeta, d_init, ws)
+    return dq, dk, dv, dalpha, dbeta, d_init

@@ -225,6 +225,44 @@ int kda_layer_back(const kda_shape* shape, int64_t num_tokens, const float* o,
                    const float* g_logit, const float* norm_w, float eps, int32_t out_dtype,
                    void* out, void* hip_stream);
 
+/* Workspace bytes of kda_prefill_backward for this packing (device memory,
+ * caller-owned, 16-byte aligned). It holds the recomputed forward (its states
+ * after every 64 tokens) and about 1 MB per (chunk, head) at d = 128
+ * (0.3 MB at d = 64) of intermediate fp32 arrays. */
+int kda_prefill_backward_workspace_size(const kda_shape* shape, int32_t num_seqs,
+                                        const int64_t* cu_seqlens_host, size_t* bytes);
+
+/* Backward pass of kda_prefill_chunked: the gradients of the loss
+ *   sum_t <d_o_t, o_t> + sum_n <d_final_state_n, S_final_n>
+ * with respect to q, k, v, alpha, beta and the initial state, for the update
+ * of page "Modele hybrydowe: co Gated DeltaNet zastępuje w cache KV"
+ * (trefon.com), section "Gated DeltaNet: dodaj zanik", differentiated through
+ * the chunked form (closing paragraph of "Co stan rekurencyjny zmienia przy
+ * serwowaniu"). The forward is recomputed inside (states every 64 tokens);
+ * the gradients of each chunk are dense fp32 products, and the gradient of
+ * the state runs over the chunks of each sequence in reverse.
+ * Inputs as kda_prefill_chunked (q, k, v, alpha, beta, initial_state or NULL,
+ * cu_seqlens on host and device). d_o: fp32 [T, H, d_v]. d_final_state: fp32
+ * [num_seqs, H, d_v, d_k] or NULL (zero). Outputs, all fp32: dq, dk [T, H, d_k],
+ * dv [T, H, d_v], dalpha shaped like alpha, dbeta [T, H], d_initial_state
+ * [num_seqs, H, d_v, d_k] or NULL (not wanted). Outputs must not overlap the
+ * inputs, except that d_initial_state may be d_final_state.
+ * Alignment: q, k, v, per-key alpha, initial_state, d_final_state,
+ * d_initial_state and workspace 16 bytes; the rest 4 (cu_seqlens_dev 8).
+ * Precondition (beyond kda_prefill_chunked's): within each 64-token chunk the
+ * decay over any 32 consecutive tokens is at least 2^-120 per channel, so the
+ * decay factors relative to the chunk's middle row stay inside fp32.
+ * Errors as kda_prefill_chunked; KDA_ERR_WORKSPACE if workspace_bytes is below
+ * kda_prefill_backward_workspace_size. num_seqs == 0 is a no-op. */
+int kda_prefill_backward(const kda_shape* shape, int32_t num_seqs,
+                         const int64_t* cu_seqlens_host, const int64_t* cu_seqlens_dev,
+                         const void* q, const void* k, const void* v,
+                         const float* alpha, const float* beta, const float* initial_state,
+                         const float* d_o, const float* d_final_state,
+                         float* dq, float* dk, float* dv, float* dalpha, float* dbeta,
+                         float* d_initial_state, void* workspace, size_t workspace_bytes,
+                         void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -40,7 +40,8 @@ def test_kda_header_symbols_exported(K):
     names = _declared("kda.h")
     assert set(names) == {"kda_abi_version", "kda_last_error", "kda_snapshot_count",
                           "kda_prefill_workspace_size", "kda_prefill_chunked", "kda_decode_step",
-                          "kda_decode_tokens", "kda_layer_front", "kda_layer_back"}
+                          "kda_decode_tokens", "kda_layer_front", "kda_layer_back",
+                          "kda_prefill_backward_workspace_size", "kda_prefill_backward"}
     lib = ctypes.CDLL(K.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
