@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "prefill tokens/s @T=256K H16 d128; decode µs/step @B256; % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, TFLOP/s
+MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 MFMA, TFLOP/s
 
 
 def prefill_algorithmic(T, H, dk, dv, n_seqs, per_key, qkv_bytes=2, C=64, with_init=False, n_snap=0):
@@ -43,6 +44,20 @@ def prefill_algorithmic(T, H, dk, dv, n_seqs, per_key, qkv_bytes=2, C=64, with_i
     b += n_snap * H * dv * dk * 4
     chunks = T / C                                 # full chunks (all configs are multiples of 64 here)
     f = chunks * H * (6 * C * dk * dv + 3 * C * C * dk + 2 * C * C * dv + C ** 3 / 3)
+    return b, f
+
+
+def backward_algorithmic(T, H, d, n_seqs, per_key, qkv_bytes=2, C=64, with_init=False, with_final=False):
+    """Bytes: q, k, v, alpha, beta and d_o read once, dq, dk, dv, dalpha, dbeta
+    (fp32) written once (plus the states when given/wanted). Flops per
+    (chunk, head) of the chunked backward's products (dense, the lower
+    triangles of Bm and dBm at half): 18 C d^2 + 26 C^2 d + (13/3) C^3; the
+    forward recomputed for the chunk-start states is not counted."""
+    a_el = d if per_key else 1
+    b = T * H * 3 * d * qkv_bytes + T * H * (a_el + 1) * 4 + T * H * d * 4        # inputs, d_o
+    b += T * H * 3 * d * 4 + T * H * (a_el + 1) * 4                               # gradients
+    b += n_seqs * H * d * d * 4 * (1 + int(with_init) + int(with_final))          # d_init (+ init, d_final)
+    f = (T / C) * H * (18 * C * d * d + 26 * C * C * d + 13 / 3 * C ** 3)
     return b, f
 
 
@@ -289,6 +304,46 @@ def time_layer(kda, torch, w, steps, warmup):
     return res
 
 
+def time_backward(kda, torch, w, steps, warmup):
+    """HIP-event time of kda_prefill_backward (outputs and workspace allocated
+    beforehand; the recomputed forward is inside the call)."""
+    from gated_delta_rule_72_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    inp = wl.make_prefill_inputs(w, dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed + 11)
+    d_o = torch.randn((w.T, w.H, w.dv), generator=g, device=dev)
+    shape = kda.make_shape(w.H, w.dk, w.dv, inp["q"].dtype, w.gate == "per_key")
+    cu_h = inp["cu_seqlens_host"]
+    f32 = dict(dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty((w.T, w.H, w.dk), **f32) for _ in range(3))
+    da = torch.empty(inp["alpha"].shape, **f32)
+    db = torch.empty((w.T, w.H), **f32)
+    di = torch.empty((w.num_seqs, w.H, w.dv, w.dk), **f32)
+    ws_bytes = kda.kda_prefill_backward_workspace_size(shape, cu_h)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
+    def call():
+        kda.kda_prefill_backward(shape, cu_h, inp["cu_seqlens"], inp["q"], inp["k"], inp["v"], inp["alpha"],
+                                 inp["beta"], inp["initial_state"], d_o, None, dq, dk, dv, da, db, di, ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for s_, e_ in ev:
+        s_.record(stream)
+        call()
+        e_.record(stream)
+    torch.cuda.synchronize()
+    ms = [s_.elapsed_time(e_) for s_, e_ in ev]
+    with_init = inp["initial_state"] is not None
+    del inp, d_o, dq, dk, dv, da, db, di, ws
+    torch.cuda.empty_cache()
+    return sum(ms) / len(ms), ws_bytes, with_init
+
+
 def cpu_baseline(w, inp, tokens: int):
     """fp64 oracle on the host over the first `tokens` tokens of the workload."""
     tokens = min(tokens, w.T)
@@ -321,6 +376,7 @@ def main(argv=None):
     ap.add_argument("--decode-only", action="store_true", help="profiling: only the decode loop")
     ap.add_argument("--no-other-prefill", action="store_true",
                     help="skip timing the other prefill workloads (KDA layer shape, varlen pack)")
+    ap.add_argument("--no-backward", action="store_true", help="skip timing the backward pass")
     ap.add_argument("--no-layer", action="store_true",
                     help="skip timing the KDA layer front and back end")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -434,6 +490,22 @@ def main(argv=None):
                 "front_recurrence_back_ms": round(t["layer"], 4),
                 "front_recurrence_back_tokens_per_s": round(lw.T / (t["layer"] * 1e-3), 1)}
         result["layer_front_back"] = layer
+    if not args.no_backward and not args.prefill_only:
+        bwd = {}
+        for bw in (wl.KDA_LAYER, wl.LONG_PREFILL):
+            bms, ws_bytes, with_init = time_backward(kda, torch, bw, max(3, args.steps // 5), 1)
+            bb, bf = backward_algorithmic(bw.T, bw.H, bw.dk, bw.num_seqs, bw.gate == "per_key",
+                                          qkv_bytes=2 if bw.dtype == "bf16" else 4, with_init=with_init)
+            tfl = bf / (bms * 1e-3) / 1e12
+            bwd[bw.name] = {"ms_per_call": round(bms, 4), "tokens_per_s": round(bw.T / (bms * 1e-3), 1),
+                            "roofline": {"bound": "mfma", "achieved": round(tfl, 2), "peak": MFMA_F32_PEAK_TFLOPS,
+                                         "unit": "TFLOP/s", "frac": round(tfl / MFMA_F32_PEAK_TFLOPS, 4),
+                                         "dtype": "fp32 MFMA"},
+                            "algorithmic_flops": int(bf), "algorithmic_bytes": int(bb),
+                            "hbm_frac": round(bb / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                            "workspace_bytes": int(ws_bytes),
+                            "includes": "forward recompute (states every 64 tokens) + backward kernels"}
+        result["backward"] = bwd
     if not args.skip_decode and not args.prefill_only:
         d = wl.DECODE
         dms = time_decode(kda, torch, d, max(args.steps, 20), args.warmup)

@@ -186,15 +186,38 @@ int check_prefill_args(const kda_shape* shape, int32_t num_seqs, const int64_t* 
 // per-(chunk, head) fp32 arrays of the backward kernels.
 struct BackwardPlan {
   PrefillPlan fwd;
-  int64_t n_chunks, n_snap;
-  size_t o_off, fin_off, snap_off, cb_off, sb_off, ws_off, bytes;
+  int64_t n_chunks, n_snap, n_items;
+  int32_t seg_chunks;
+  size_t o_off, fin_off, snap_off, cb_off, sb_off, ib_off, maps_off, ends_off, ws_off, bytes;
 };
 
 BackwardPlan plan_backward(const kda_shape* s, int32_t num_seqs, const int64_t* cu, int cus) {
   BackwardPlan p{};
   p.fwd = plan_prefill(s, num_seqs, cu, -1, cus);
-  for (int32_t n = 0; n < num_seqs; ++n) p.n_chunks += (cu[n + 1] - cu[n] + kChunk - 1) / kChunk;
+  int64_t max_chunks = 0;
+  for (int32_t n = 0; n < num_seqs; ++n) {
+    const int64_t ch = (cu[n + 1] - cu[n] + kChunk - 1) / kChunk;
+    p.n_chunks += ch;
+    if (ch > max_chunks) max_chunks = ch;
+  }
   p.n_snap = snapshot_slots(num_seqs, cu, kChunk);
+  // The reverse scan of the state gradient is sequential over the chunks of a
+  // (sequence, head). When those chains cannot fill the device, sequences are
+  // cut into segments (about two workgroups per compute unit, at least 8
+  // chunks each) that are mapped in parallel, joined by a short scan over
+  // segments, then run again from their true end gradients.
+  int64_t seg = 0;
+  if ((int64_t)num_seqs * s->num_heads < 2 * (int64_t)cus) {
+    seg = (p.n_chunks * s->num_heads + 2 * (int64_t)cus - 1) / (2 * (int64_t)cus);
+    if (seg < 8) seg = 8;
+    if (seg >= max_chunks) seg = 0;
+  }
+  p.seg_chunks = (int32_t)seg;
+  for (int32_t n = 0; n < num_seqs; ++n) {
+    const int64_t ch = (cu[n + 1] - cu[n] + kChunk - 1) / kChunk;
+    const int64_t it = seg > 0 ? (ch + seg - 1) / seg : 1;
+    p.n_items += it > 0 ? it : 1;
+  }
   const size_t H = (size_t)s->num_heads, D = (size_t)s->d_k, T = (size_t)cu[num_seqs];
   size_t off = round_up(p.fwd.bytes);
   p.o_off = off;
@@ -207,6 +230,12 @@ BackwardPlan plan_backward(const kda_shape* s, int32_t num_seqs, const int64_t* 
   off += round_up(((size_t)num_seqs + 1) * sizeof(int64_t));
   p.sb_off = off;
   off += round_up(((size_t)num_seqs + 1) * sizeof(int64_t));
+  p.ib_off = off;
+  off += round_up(((size_t)num_seqs + 1) * sizeof(int64_t));
+  p.maps_off = off;
+  if (seg > 0) off += round_up((size_t)p.n_items * H * 2 * D * D * sizeof(float));
+  p.ends_off = off;
+  if (seg > 0) off += round_up((size_t)p.n_items * H * D * D * sizeof(float));
   p.ws_off = off;
   off += round_up((size_t)kda::bwd::floats(p.n_chunks * s->num_heads, s->d_k) * sizeof(float));
   p.bytes = off;
@@ -516,6 +545,11 @@ int kda_prefill_backward(const kda_shape* shape, int32_t num_seqs, const int64_t
   b.states = reinterpret_cast<const float*>(ws + plan.snap_off);
   b.chunk_base = reinterpret_cast<int64_t*>(ws + plan.cb_off);
   b.snap_base = reinterpret_cast<int64_t*>(ws + plan.sb_off);
+  b.item_base = reinterpret_cast<int64_t*>(ws + plan.ib_off);
+  b.seg_chunks = plan.seg_chunks;
+  b.n_items = plan.n_items;
+  b.seg_maps = plan.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.maps_off) : nullptr;
+  b.seg_end = plan.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.ends_off) : nullptr;
   b.ws = reinterpret_cast<float*>(ws + plan.ws_off);
   e = kda::launch_backward(b, shape->d_k, bf16, pk, st);
   if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "backward launch failed: %s", hipGetErrorString(e));

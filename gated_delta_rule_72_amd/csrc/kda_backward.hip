@@ -51,40 +51,54 @@ __device__ __forceinline__ float load1(const void* base, int64_t idx) {
 }
 
 // chunk_base[n] = sum over earlier sequences of ceil(len / 64) (chunks);
-// snap_base[n] = the same of floor(len / 64) (64-token state slots).
-__global__ __launch_bounds__(1024) void chunk_base_kernel(const int64_t* cu, int32_t N, int64_t* chunk_base,
-                                                          int64_t* snap_base) {
-  __shared__ int64_t pc[1024], ps[1024];
+// snap_base[n] = the same of floor(len / 64) (64-token state slots);
+// item_base[n] = the same of the scan segments, max(1, ceil(chunks / seg)).
+__device__ __forceinline__ int64_t seq_items(int64_t nch, int32_t seg) {
+  const int64_t it = seg > 0 ? (nch + seg - 1) / seg : 1;
+  return it > 0 ? it : 1;
+}
+
+__global__ __launch_bounds__(1024) void chunk_base_kernel(const int64_t* cu, int32_t N, int32_t seg,
+                                                          int64_t* chunk_base, int64_t* snap_base,
+                                                          int64_t* item_base) {
+  __shared__ int64_t pc[1024], ps[1024], pi[1024];
   const int tid = threadIdx.x;
   const int64_t per = ((int64_t)N + 1023) / 1024;
   const int64_t n0 = tid * per, n1 = n0 + per < (int64_t)N ? n0 + per : (int64_t)N;
-  int64_t sc = 0, ss = 0;
+  int64_t sc = 0, ss = 0, si = 0;
   for (int64_t n = n0; n < n1; ++n) {
     const int64_t len = cu[n + 1] - cu[n];
     sc += (len + C - 1) / C;
     ss += len / C;
+    si += seq_items((len + C - 1) / C, seg);
   }
   pc[tid] = sc;
   ps[tid] = ss;
+  pi[tid] = si;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
-    const int64_t vc = tid >= off ? pc[tid - off] : 0, vs = tid >= off ? ps[tid - off] : 0;
+    const int64_t vc = tid >= off ? pc[tid - off] : 0, vs = tid >= off ? ps[tid - off] : 0,
+                  vi = tid >= off ? pi[tid - off] : 0;
     __syncthreads();
     pc[tid] += vc;
     ps[tid] += vs;
+    pi[tid] += vi;
     __syncthreads();
   }
-  int64_t bc = pc[tid] - sc, bs = ps[tid] - ss;
+  int64_t bc = pc[tid] - sc, bs = ps[tid] - ss, bi = pi[tid] - si;
   for (int64_t n = n0; n < n1; ++n) {
     chunk_base[n] = bc;
     snap_base[n] = bs;
+    item_base[n] = bi;
     const int64_t len = cu[n + 1] - cu[n];
     bc += (len + C - 1) / C;
     bs += len / C;
+    bi += seq_items((len + C - 1) / C, seg);
   }
   if (tid == 1023) {
     chunk_base[N] = pc[1023];
     snap_base[N] = ps[1023];
+    item_base[N] = pi[1023];
   }
 }
 
@@ -279,76 +293,190 @@ __global__ __launch_bounds__(64) void inverse_kernel(BackwardArgs a, int32_t d) 
 }
 
 // ---- reverse scan over chunks: dS_start = dS_end (Diag(e^G_n) - Kt^T W) + E ----
-// Works on R = dS^T (d_k x d_v): R_start = Diag(e^G_n) R_end - W^T (Kt R_end) + E^T.
-// Wavefront w owns columns 16w..16w+15 of R as D/16 accumulator tiles: lane
-// (g, l) holds R(16t + 4g + i, 16w + l), i.e. dS(16w + l, 16t + 4g + i). Both
-// products contract over the tile rows, which enter as the permuted-K operand.
-template <int D>
+// Works on R = dS^T (d_k x d_v): R_start = Diag(e^G_n) R_end - W^T (Kt R_end) + E^T,
+// and every column of R evolves on its own. Wavefront w owns columns
+// 16w..16w+15 as D/16 accumulator tiles: lane (g, l) holds R(16t + 4g + i, 16w + l),
+// i.e. dS(16w + l, 16t + 4g + i). Both products contract over the tile rows,
+// which enter as the permuted-K operand. One workgroup runs one segment of
+// one (sequence, head): OUT mode from the segment's true end gradient, storing
+// dS at every chunk end (and d_initial at a sequence's first segment); MAP
+// mode, for a sequence cut into segments, one of two chains per workgroup:
+// from the identity without E (the segment's M) or from zero with E (its N),
+// so that R_start = M R_end + N.
+__device__ __forceinline__ int item_seq(const BackwardArgs& a, int64_t item) {
+  int lo = 0, hi = a.num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.item_base[mid] <= item) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <int D, bool MAP>
 __global__ __launch_bounds__(D * 4) void scan_kernel(BackwardArgs a) {
   constexpr int LD = D + 4;
+  constexpr int NT = D / 16;                       // accumulator tiles per chain
+  constexpr int PF = C * D / 4 / (D * 4);          // float4 of Kt (and of W) per thread per chunk
   __shared__ float Kts[C * LD];
   __shared__ float Ws[C * LD];
-  const int n = (int)(blockIdx.x / a.H), h = (int)(blockIdx.x % a.H);
+  const int chain = MAP ? (int)(blockIdx.x & 1) : 0;      // MAP: 0 = M, 1 = N
+  const int64_t unit = MAP ? blockIdx.x >> 1 : blockIdx.x;
+  const int64_t item = unit / a.H;
+  const int h = (int)(unit % a.H);
+  const int n = item_seq(a, item);
+  const int64_t seg = item - a.item_base[n];
+  const int64_t n_seg = a.item_base[n + 1] - a.item_base[n];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, gq = lane >> 4;
   const int64_t units = a.n_chunks * a.H, DD = (int64_t)D * D;
   const int64_t rowoff = (int64_t)(16 * w + l16) * D;
-  f32x4 R[D / 16];
-  const float* df = a.d_final ? a.d_final + ((int64_t)n * a.H + h) * DD + rowoff : nullptr;
-#pragma unroll
-  for (int t = 0; t < D / 16; ++t)
-    R[t] = df ? *reinterpret_cast<const f32x4*>(df + 16 * t + 4 * gq) : f32x4{0.f, 0.f, 0.f, 0.f};
   const int64_t cb = a.chunk_base[n], nch = a.chunk_base[n + 1] - cb;
-  for (int64_t c = nch - 1; c >= 0; --c) {
-    const int64_t b = (cb + c) * a.H + h;
-    float* dsn = a.ws + dd_off(DSN, units, D) + b * DD + rowoff;
+  const int64_t c0 = a.seg_chunks > 0 ? seg * a.seg_chunks : 0;
+  const int64_t c1 = a.seg_chunks > 0 && c0 + a.seg_chunks < nch ? c0 + a.seg_chunks : nch;
+
+  f32x4 R[NT];
+  if constexpr (MAP) {
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) *reinterpret_cast<f32x4*>(dsn + 16 * t + 4 * gq) = R[t];
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) R[t][i] = (chain == 0 && 16 * t + 4 * gq + i == 16 * w + l16) ? 1.f : 0.f;
+  } else {
+    const float* src = nullptr;
+    if (seg + 1 < n_seg) src = a.seg_end + (item * a.H + h) * DD + rowoff;
+    else if (a.d_final) src = a.d_final + ((int64_t)n * a.H + h) * DD + rowoff;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      R[t] = src ? *reinterpret_cast<const f32x4*>(src + 16 * t + 4 * gq) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  // the next chunk's Kt and W, fetched into registers while this one computes
+  f32x4 pk[PF], pw[PF];
+  auto fetch = [&](int64_t c) {
+    const int64_t b = (cb + c) * a.H + h;
     const float* kt = a.ws + nd_off(KT, units, D) + b * C * D;
     const float* wm = a.ws + nd_off(WM, units, D) + b * C * D;
-    for (int e = tid; e < C * D / 4; e += D * 4) {
+#pragma unroll
+    for (int q = 0; q < PF; ++q) {
+      const int e = tid + q * D * 4;
+      pk[q] = *reinterpret_cast<const f32x4*>(kt + (int64_t)(e / (D / 4)) * D + (e % (D / 4)) * 4);
+      pw[q] = *reinterpret_cast<const f32x4*>(wm + (int64_t)(e / (D / 4)) * D + (e % (D / 4)) * 4);
+    }
+  };
+  if (c1 > c0) fetch(c1 - 1);
+  for (int64_t c = c1 - 1; c >= c0; --c) {
+    const int64_t b = (cb + c) * a.H + h;
+    if constexpr (!MAP) {
+      float* dsn = a.ws + dd_off(DSN, units, D) + b * DD + rowoff;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4*>(dsn + 16 * t + 4 * gq) = R[t];
+    }
+#pragma unroll
+    for (int q = 0; q < PF; ++q) {
+      const int e = tid + q * D * 4;
       const int r = e / (D / 4), c4 = (e % (D / 4)) * 4;
-      *reinterpret_cast<f32x4*>(Kts + r * LD + c4) = *reinterpret_cast<const f32x4*>(kt + (int64_t)r * D + c4);
-      *reinterpret_cast<f32x4*>(Ws + r * LD + c4) = *reinterpret_cast<const f32x4*>(wm + (int64_t)r * D + c4);
+      *reinterpret_cast<f32x4*>(Kts + r * LD + c4) = pk[q];
+      *reinterpret_cast<f32x4*>(Ws + r * LD + c4) = pw[q];
     }
     __syncthreads();
-    f32x4 V1[4];                       // Kt R_w: chunk rows 16s.., columns 16w..
+    if (c > c0) fetch(c - 1);
+    const float* E = a.ws + dd_off(EM, units, D) + b * DD + rowoff;
+    const float* eg = a.ws + egn_off(units, D) + b * D;
+    f32x4 V1[4];                                    // Kt R: chunk rows 16s.., columns 16w..
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       V1[s] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
+      for (int t = 0; t < NT; ++t) {
         const f32x4 av = *reinterpret_cast<const f32x4*>(Kts + (16 * s + l16) * LD + 16 * t + 4 * gq);
 #pragma unroll
         for (int i = 0; i < 4; ++i) V1[s] = mfma4(av[i], R[t][i], V1[s]);
       }
     }
-    const float* E = a.ws + dd_off(EM, units, D) + b * DD + rowoff;
-    const float* eg = a.ws + egn_off(units, D) + b * D;
+    const bool with_e = !MAP || chain == 1;
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
+    for (int t = 0; t < NT; ++t) {
       f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int i = 0; i < 4; ++i) x = mfma4(Ws[(16 * s + 4 * gq + i) * LD + 16 * t + l16], V1[s][i], x);
-      const f32x4 ev = *reinterpret_cast<const f32x4*>(E + 16 * t + 4 * gq);
       const f32x4 gv = *reinterpret_cast<const f32x4*>(eg + 16 * t + 4 * gq);
+      const f32x4 ev = with_e ? *reinterpret_cast<const f32x4*>(E + 16 * t + 4 * gq) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < 4; ++i) R[t][i] = gv[i] * R[t][i] - x[i] + ev[i];
     }
     __syncthreads();
   }
-  if (a.d_init) {
+  if constexpr (MAP) {
+    float* m = a.seg_maps + (item * a.H + h) * 2 * DD + chain * DD + rowoff;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4*>(m + 16 * t + 4 * gq) = R[t];
+  } else if (seg == 0 && a.d_init) {
     float* di = a.d_init + ((int64_t)n * a.H + h) * DD + rowoff;
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) *reinterpret_cast<f32x4*>(di + 16 * t + 4 * gq) = R[t];
+    for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4*>(di + 16 * t + 4 * gq) = R[t];
+  }
+}
+
+// End gradient of every segment but the last, from the segment maps, in
+// reverse: R_end(s) = M_{s+1} R_end(s+1) + N_{s+1}, R_end(last) = d_final^T.
+// Same layout as the scan; M is read straight from memory as the A operand.
+template <int D>
+__global__ __launch_bounds__(D * 4) void segment_end_kernel(BackwardArgs a) {
+  constexpr int NT = D / 16, LD = D + 4;
+  __shared__ float Ms[D * LD];
+  const int n = (int)(blockIdx.x / a.H), h = (int)(blockIdx.x % a.H);
+  const int64_t ib = a.item_base[n], ns = a.item_base[n + 1] - ib;
+  if (ns < 2) return;                       // uniform over the workgroup
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, gq = lane >> 4;
+  const int64_t DD = (int64_t)D * D, rowoff = (int64_t)(16 * w + l16) * D;
+  f32x4 R[NT];
+  const float* df = a.d_final ? a.d_final + ((int64_t)n * a.H + h) * DD + rowoff : nullptr;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) R[t] = df ? *reinterpret_cast<const f32x4*>(df + 16 * t + 4 * gq) : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int64_t s = ns - 1; s >= 1; --s) {
+    // maps are stored as the scan stores dS: element (r, c) of M at [c * D + r]
+    const float* M = a.seg_maps + ((ib + s) * a.H + h) * 2 * DD;
+    const float* N = M + DD + rowoff;
+    for (int e = tid; e < D * D / 4; e += D * 4) {
+      const int r = e / (D / 4), c4 = (e % (D / 4)) * 4;
+      *reinterpret_cast<f32x4*>(Ms + r * LD + c4) = *reinterpret_cast<const f32x4*>(M + (int64_t)r * D + c4);
+    }
+    __syncthreads();
+    f32x4 X[NT];
+#pragma unroll
+    for (int t2 = 0; t2 < NT; ++t2) {
+      X[t2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) X[t2] = mfma4(Ms[(16 * t + 4 * gq + i) * LD + 16 * t2 + l16], R[t][i], X[t2]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const f32x4 nv = *reinterpret_cast<const f32x4*>(N + 16 * t + 4 * gq);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) R[t][i] = X[t][i] + nv[i];
+    }
+    float* e = a.seg_end + ((ib + s - 1) * a.H + h) * DD + rowoff;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4*>(e + 16 * t + 4 * gq) = R[t];
   }
 }
 
 // ---- assembly: dq, dk, dv, dbeta, and dalpha through the decay factors ----
-template <int D, bool PER_KEY>
+// Every element (row r, channel j) in parallel: dq, dk, dv and the row's
+// dGamma term, with the decay factors formed again from q, k and Gamma (the
+// same expressions as the prep, so the same values); dGamma goes to LDS. The
+// gradient of Gamma_n (which every row's log-decay contains) and dbeta are
+// reductions over rows or channels; a last pass per channel sums dGamma over
+// rows in reverse, which is the gradient of log alpha.
+template <int D, bool BF16, bool PER_KEY>
 __global__ __launch_bounds__(256) void assemble_kernel(BackwardArgs a) {
-  __shared__ float sLn[PER_KEY ? 1 : C * (D + 1)];
+  constexpr int LDG = D + 1, RG = 256 / D;      // RG threads share a channel
+  __shared__ float sdG[C * LDG];
+  __shared__ float sPart[RG * D];
+  __shared__ float sGn[D];
   const int64_t units = a.n_chunks * a.H;
   const int64_t b = blockIdx.x;
   const int h = (int)(b % a.H);
@@ -358,50 +486,80 @@ __global__ __launch_bounds__(256) void assemble_kernel(BackwardArgs a) {
   auto nd = [&](int arr) { return ws + nd_off(arr, units, D) + b * C * D; };
   auto nn = [&](int arr) { return ws + nn_off(arr, units, D) + b * C * C; };
   const float* beta = ws + beta_off(units, D) + b * C;
+  const float *G = nd(GG), *dQp = nd(DQP), *dQa = nd(DQA), *dKp = nd(DKP), *dKm = nd(DKM), *dX = nd(DX),
+              *dKt = nd(DKT), *dY = nd(DY);
+  const int cref = ref_row(p.len);
+  const int j = tid % D, rg = tid / D;
+  {                                     // elementwise part
+    const float Gc = G[cref * D + j], Gn = G[(C - 1) * D + j];
+    float kt_part = 0.f;
+#pragma unroll 4
+    for (int r = rg; r < C; r += RG) {
+      const int e = r * D + j;
+      float qv = 0.f, kv = 0.f;
+      int64_t o = 0;
+      if (r < p.len) {
+        o = ((p.t0 + r) * a.H + h) * D + j;
+        qv = load1<BF16>(a.q, o);
+        kv = load1<BF16>(a.k, o);
+      }
+      const float g = G[e];
+      const float eRel = __expf(g - Gc), eInv = __expf(Gc - g), eAbs = __expf(g), eTail = __expf(Gn - g);
+      const float dKa = beta[r] * dX[e];
+      const float kt = kv * eTail;
+      sdG[r * LDG + j] = dQp[e] * (qv * eRel) + dQa[e] * (qv * eAbs) + dKp[e] * (kv * eRel) -
+                         dKm[e] * (kv * eInv) + dKa * (kv * eAbs) - dKt[e] * kt;
+      kt_part += dKt[e] * kt;
+      if (r < p.len) {
+        a.dq[o] = dQp[e] * eRel + dQa[e] * eAbs;
+        a.dk[o] = dKp[e] * eRel + dKm[e] * eInv + dKa * eAbs + dKt[e] * eTail;
+        a.dv[o] = beta[r] * dY[e];
+      }
+    }
+    // gradient of Gamma_n: sum over rows of dKt * Kt, and colsum(dS_n * S0) e^Gamma_n
+    const float* dSn = ws + dd_off(DSN, units, D) + b * D * D;
+    const float* S0 = ws + dd_off(S0M, units, D) + b * D * D;
+    float st = 0.f;
+#pragma unroll 4
+    for (int i = rg; i < D; i += RG) st += dSn[(int64_t)i * D + j] * S0[(int64_t)i * D + j];
+    sPart[rg * D + j] = kt_part + st * ws[egn_off(units, D) + b * D + j];
+  }
   {                                     // dbeta: four lanes per row
     const int r = tid >> 2, part = tid & 3;
-    const float *dY = nd(DY), *V = nd(VF), *dX = nd(DX), *Ka = nd(KA), *dL = nn(DLM), *P = nn(PM);
+    const float *V = nd(VF), *Ka = nd(KA), *dL = nn(DLM), *P = nn(PM);
     float s = 0.f;
-    for (int j = part; j < D; j += 4) s += dY[r * D + j] * V[r * D + j] + dX[r * D + j] * Ka[r * D + j];
+    for (int jj = part; jj < D; jj += 4) s += dY[r * D + jj] * V[r * D + jj] + dX[r * D + jj] * Ka[r * D + jj];
     for (int i = part; i < C; i += 4) s += dL[r * C + i] * P[r * C + i];
     s += __shfl_xor(s, 1, 4);
     s += __shfl_xor(s, 2, 4);
     if (part == 0 && r < p.len) a.dbeta[(p.t0 + r) * a.H + h] = s;
   }
-  if (tid < D) {                        // one channel per thread, rows in reverse
-    const int j = tid;
-    const float *G = nd(GG), *dQp = nd(DQP), *dQa = nd(DQA), *dKp = nd(DKP), *dKm = nd(DKM), *dX = nd(DX),
-                *dKt = nd(DKT), *dY = nd(DY), *Qp = nd(QP), *Qa = nd(QA), *Kp = nd(KP), *Km = nd(KM),
-                *Ka = nd(KA), *Kt = nd(KT);
-    const float* dSn = ws + dd_off(DSN, units, D) + b * D * D;
-    const float* S0 = ws + dd_off(S0M, units, D) + b * D * D;
-    // gradient of G_n (the last row's Gamma), counted in every row's sum below
-    float acc = 0.f, st = 0.f;
-    for (int r = 0; r < C; ++r) acc += dKt[r * D + j] * Kt[r * D + j];
-    for (int i = 0; i < D; ++i) st += dSn[(int64_t)i * D + j] * S0[(int64_t)i * D + j];
-    acc += st * ws[egn_off(units, D) + b * D + j];
-    const float Gc = G[ref_row(p.len) * D + j], Gn = G[(C - 1) * D + j];
+  __syncthreads();
+  if (tid < D) {
+    float acc = 0.f;
+#pragma unroll
+    for (int q = 0; q < RG; ++q) acc += sPart[q * D + tid];
+    sGn[tid] = acc;
+  }
+  __syncthreads();
+  if (tid < D) {                        // reverse cumulative sum over rows
+    float acc = sGn[tid];
     for (int r = C - 1; r >= 0; --r) {
-      const int e = r * D + j;
-      const float g = G[e];
-      const float eRel = __expf(g - Gc), eInv = __expf(Gc - g), eAbs = __expf(g), eTail = __expf(Gn - g);
-      const float dKa = beta[r] * dX[e];
-      acc += dQp[e] * Qp[e] + dQa[e] * Qa[e] + dKp[e] * Kp[e] - dKm[e] * Km[e] + dKa * Ka[e] - dKt[e] * Kt[e];
-      if (r < p.len) {
-        const int64_t o = ((p.t0 + r) * a.H + h) * D + j;
-        a.dq[o] = dQp[e] * eRel + dQa[e] * eAbs;
-        a.dk[o] = dKp[e] * eRel + dKm[e] * eInv + dKa * eAbs + dKt[e] * eTail;
-        a.dv[o] = beta[r] * dY[e];
-        if constexpr (PER_KEY) a.dalpha[o] = acc / a.alpha[o];
-        else sLn[r * (D + 1) + j] = acc;
-      }
+      acc += sdG[r * LDG + tid];
+      sdG[r * LDG + tid] = acc;
     }
   }
-  if constexpr (!PER_KEY) {
-    __syncthreads();
+  __syncthreads();
+  if constexpr (PER_KEY) {
+    for (int idx = tid; idx < p.len * D; idx += 256) {
+      const int r = idx / D, jj = idx % D;
+      const int64_t o = ((p.t0 + r) * a.H + h) * D + jj;
+      a.dalpha[o] = sdG[r * LDG + jj] / a.alpha[o];
+    }
+  } else {
     if (tid < p.len) {
       float s = 0.f;
-      for (int j = 0; j < D; ++j) s += sLn[tid * (D + 1) + j];
+      for (int jj = 0; jj < D; ++jj) s += sdG[tid * LDG + jj];
       const int64_t th = (p.t0 + tid) * a.H + h;
       a.dalpha[th] = s / a.alpha[th];
     }
@@ -423,8 +581,8 @@ hipError_t gemm(bool ta, bool tb, int64_t units, int d, int M, int N, int K, con
 
 template <int D, bool BF16, bool PK>
 hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(chunk_base_kernel, dim3(1), dim3(1024), 0, s, a.cu_dev, a.num_seqs, a.chunk_base,
-                     a.snap_base);
+  hipLaunchKernelGGL(chunk_base_kernel, dim3(1), dim3(1024), 0, s, a.cu_dev, a.num_seqs, a.seg_chunks,
+                     a.chunk_base, a.snap_base, a.item_base);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t U = a.n_chunks * a.H;
@@ -450,7 +608,14 @@ hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
     G_(true, false, U, D, D, D, C, ND(DOF), D, sND, ND(QA), D, sND, DDp(EM), D, sDD, 1.f, false, 0, nullptr);
     G_(true, false, U, D, D, D, C, ND(ZU), D, sND, ND(WM), D, sND, DDp(EM), D, sDD, -1.f, true, 0, nullptr);
   }
-  hipLaunchKernelGGL((scan_kernel<D>), dim3((unsigned)((int64_t)a.num_seqs * a.H)), dim3(D * 4), 0, s, a);
+  const dim3 scan_grid((unsigned)(a.n_items * a.H));
+  if (a.seg_chunks > 0) {
+    hipLaunchKernelGGL((scan_kernel<D, true>), dim3((unsigned)(a.n_items * a.H * 2)), dim3(D * 4), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((segment_end_kernel<D>), dim3((unsigned)((int64_t)a.num_seqs * a.H)), dim3(D * 4), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((scan_kernel<D, false>), scan_grid, dim3(D * 4), 0, s, a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (U > 0) {
     float* w = a.ws;
@@ -476,7 +641,7 @@ hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
        w + beta_off(U, D));
     G_(true, false, U, D, C, D, C, NN(DLM), C, sNN, ND(XP), D, sND, ND(DKM), D, sND, 1.f, true, 0, nullptr);
 #undef G_
-    hipLaunchKernelGGL((assemble_kernel<D, PK>), dim3((unsigned)U), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((assemble_kernel<D, BF16, PK>), dim3((unsigned)U), dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

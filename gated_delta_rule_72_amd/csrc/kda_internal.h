@@ -147,6 +147,11 @@ struct BackwardArgs {
   const float* states;       // forward states after every 64 tokens, snapshot slot order
   int64_t* chunk_base;       // workspace [N+1]: first chunk of each sequence
   int64_t* snap_base;        // workspace [N+1]: first 64-token state slot of each sequence
+  int64_t* item_base;        // workspace [N+1]: first scan segment of each sequence
+  int32_t seg_chunks;        // chunks per scan segment (0: one segment per sequence)
+  int64_t n_items;           // scan segments over all sequences (at least one per sequence)
+  float* seg_maps;           // workspace [n_items, H, 2, d, d]: each segment's map (M, then N)
+  float* seg_end;            // workspace [n_items, H, d, d]: dS^T at each segment's end
   float* ws;                 // workspace: bwd::floats(n_chunks * H, d) fp32
 };
 hipError_t launch_backward(const BackwardArgs& a, int d, bool bf16, bool per_key, hipStream_t s);

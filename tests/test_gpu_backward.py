@@ -86,6 +86,15 @@ def test_backward_small_varlen(d, gate, dtype):
     _check(inp, d_o, d_f, _run(inp, d_o, d_f))
 
 
+@pytest.mark.parametrize("d,gate", [(64, "per_key"), (128, "scalar"), (128, "per_key")])
+def test_backward_segmented_scan(d, gate):
+    """Sequences of 18 and 10 chunks with few heads: the state-gradient scan is
+    cut into segments (maps, a scan over segments, then each segment again)."""
+    w = custom(f"bwd_seg_{d}_{gate}", H=2, d=d, lens=(1100, 600, 3, 0), gate=gate, s0_std=0.05, seed=79)
+    inp, d_o, d_f = _grads_in(w, device(), seed=80)
+    _check(inp, d_o, d_f, _run(inp, d_o, d_f))
+
+
 def test_backward_without_initial_or_final_state():
     w = custom("bwd_zero_states", H=2, d=64, lens=(150, 70), gate="per_key", s0_std=0.0, seed=72)
     inp, d_o, _ = _grads_in(w, device(), seed=73, with_final=False)
