@@ -130,3 +130,14 @@ def test_backward_kda_layer_shape():
     inp, d_o, d_f = _grads_in(w, device(), seed=78)
     got = _run(inp, d_o, d_f)
     _check(inp, d_o, d_f, got, heads=(0, 9))
+
+
+def test_backward_long_prefill_full_size():
+    """The long-prefill workload (T=262144, H=16, d=128, scalar gate) at full
+    size in the benchmark's launch configuration (automatic segment plans for
+    the forward recompute and the state-gradient scan); heads 0 and 9 against
+    the oracle (about 40 s of host time, one thread per head)."""
+    w = wl.LONG_PREFILL
+    inp, d_o, d_f = _grads_in(w, device(), seed=81)
+    got = _run(inp, d_o, d_f)
+    _check(inp, d_o, d_f, got, heads=(0, 9))
