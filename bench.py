@@ -383,8 +383,8 @@ def main(argv=None):
                     help="profiling: copy a 256 MiB fp32 buffer 3 times (known bytes for HBM counters)")
     args = ap.parse_args(argv)
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (every GPU box here "
-              f"has one GPU). Sharding is described in DESIGN.md.", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the path runs on a "
+              f"single GPU (sequences and heads would shard across GPUs without exchange).", file=sys.stderr)
         return 2
 
     import torch

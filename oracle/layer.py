@@ -1,7 +1,6 @@
 """Front and back end of a KDA layer around the recurrence, in fp64 numpy.
 
-TEST INFRASTRUCTURE: used only by tests/ and bench.py's CPU baseline, never by
-the GPU library.
+TEST INFRASTRUCTURE: used only by tests/, never by the GPU library.
 
 Page "kda-graft: Qwen2.5-0.5B с трансплантированным KDA" (ailist.pro), section
 "Идея и архитектура": each KDA layer adds a 4-tap convolution initialised as
