@@ -95,6 +95,24 @@ def make_shape(num_heads: int, d_k: int, d_v: int, qkv_dtype: torch.dtype, per_k
 
 
 # ---- the C ABI, name for name ----------------------------------------------
+# The library sees raw pointers, so each binding first checks what a pointer
+# cannot tell it: dtype and contiguity of every tensor passed.
+
+def _args(fn: str, shape: Optional[KdaShape], **named) -> None:
+    """named: name=(tensor or None, expected dtype; "qkv" = the shape's q/k/v dtype)."""
+    for name, (t, dt) in named.items():
+        if t is None:
+            continue
+        if dt == "qkv":
+            dt = torch.bfloat16 if shape.qkv_dtype == KDA_BF16 else torch.float32
+        if t.dtype != dt:
+            raise TypeError(f"{fn}: {name} must be {dt} (got {t.dtype})")
+        if not t.is_contiguous():
+            raise ValueError(f"{fn}: {name} must be contiguous")
+
+
+F32, I64, I32_ = torch.float32, torch.int64, torch.int32
+
 
 def kda_abi_version() -> int:
     return load().kda_abi_version()
@@ -128,16 +146,22 @@ def kda_prefill_chunked(shape: KdaShape, cu_seqlens_host: torch.Tensor, cu_seqle
                         segment_tokens: int = -1, stream=None) -> None:
     """Enqueues the prefill on `stream` (default: torch's current stream). All
     tensors must already be allocated, contiguous, on one device."""
+    _args("kda_prefill_chunked", shape, q=(q, "qkv"), k=(k, "qkv"), v=(v, "qkv"), alpha=(alpha, F32),
+          beta=(beta, F32), initial_state=(initial_state, F32), o=(o, F32), final_state=(final_state, F32),
+          snapshots=(snapshots, F32), cu_seqlens_dev=(cu_seqlens_dev, I64))
     cu = cu_seqlens_host.to("cpu", torch.int64).contiguous()
     dev = q.device
     s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream_ptr(dev)
     _check("kda_prefill_chunked", load().kda_prefill_chunked(
         ctypes.byref(shape), cu.numel() - 1, _ptr(cu), _ptr(cu_seqlens_dev), int(chunk),
         int(snapshot_interval), int(segment_tokens), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state),
-        _ptr(o), _ptr(final_state), _ptr(snapshots), _ptr(workspace), workspace.numel(), s))
+        _ptr(o), _ptr(final_state), _ptr(snapshots), _ptr(workspace),
+        ctypes.c_size_t(workspace.numel() * workspace.element_size()), s))
 
 
 def kda_decode_step(shape: KdaShape, batch: int, q, k, v, alpha, beta, state, o, stream=None) -> None:
+    _args("kda_decode_step", shape, q=(q, "qkv"), k=(k, "qkv"), v=(v, "qkv"), alpha=(alpha, F32),
+          beta=(beta, F32), state=(state, F32), o=(o, F32))
     s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream_ptr(q.device)
     _check("kda_decode_step", load().kda_decode_step(
         ctypes.byref(shape), int(batch), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
@@ -146,6 +170,9 @@ def kda_decode_step(shape: KdaShape, batch: int, q, k, v, alpha, beta, state, o,
 
 def kda_decode_tokens(shape: KdaShape, batch: int, n_tok: int, q, k, v, alpha, beta, state, o,
                       token_states=None, commit=None, stream=None) -> None:
+    _args("kda_decode_tokens", shape, q=(q, "qkv"), k=(k, "qkv"), v=(v, "qkv"), alpha=(alpha, F32),
+          beta=(beta, F32), state=(state, F32), o=(o, F32), token_states=(token_states, F32),
+          commit=(commit, I32_))
     s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream_ptr(q.device)
     _check("kda_decode_tokens", load().kda_decode_tokens(
         ctypes.byref(shape), int(batch), int(n_tok), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
@@ -155,6 +182,10 @@ def kda_decode_tokens(shape: KdaShape, batch: int, n_tok: int, q, k, v, alpha, b
 def kda_layer_front(shape: KdaShape, cu_seqlens_host: torch.Tensor, cu_seqlens_dev: torch.Tensor, xq, xk, xv,
                     conv_w, conv_state_in, alpha_logit, alpha_bias: float, beta_logit, q, k, v, alpha, beta,
                     conv_state_out, stream=None) -> None:
+    _args("kda_layer_front", shape, xq=(xq, "qkv"), xk=(xk, "qkv"), xv=(xv, "qkv"), conv_w=(conv_w, F32),
+          conv_state_in=(conv_state_in, "qkv"), alpha_logit=(alpha_logit, F32), beta_logit=(beta_logit, F32),
+          q=(q, "qkv"), k=(k, "qkv"), v=(v, "qkv"), alpha=(alpha, F32), beta=(beta, F32),
+          conv_state_out=(conv_state_out, "qkv"), cu_seqlens_dev=(cu_seqlens_dev, I64))
     cu = cu_seqlens_host.to("cpu", torch.int64).contiguous()
     s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream_ptr(xq.device)
     _check("kda_layer_front", load().kda_layer_front(
@@ -165,6 +196,8 @@ def kda_layer_front(shape: KdaShape, cu_seqlens_host: torch.Tensor, cu_seqlens_d
 
 def kda_layer_back(shape: KdaShape, num_tokens: int, o, g_logit, norm_w, eps: float, out_dtype: int, out,
                    stream=None) -> None:
+    _args("kda_layer_back", shape, o=(o, F32), g_logit=(g_logit, F32), norm_w=(norm_w, F32),
+          out=(out, torch.bfloat16 if out_dtype == KDA_BF16 else F32))
     s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream_ptr(o.device)
     _check("kda_layer_back", load().kda_layer_back(
         ctypes.byref(shape), int(num_tokens), _ptr(o), _ptr(g_logit), _ptr(norm_w), float(eps), int(out_dtype),
@@ -183,6 +216,10 @@ def kda_prefill_backward_workspace_size(shape: KdaShape, cu_seqlens_host: torch.
 def kda_prefill_backward(shape: KdaShape, cu_seqlens_host: torch.Tensor, cu_seqlens_dev: torch.Tensor,
                          q, k, v, alpha, beta, initial_state, d_o, d_final_state, dq, dk, dv, dalpha, dbeta,
                          d_initial_state, workspace: torch.Tensor, stream=None) -> None:
+    _args("kda_prefill_backward", shape, q=(q, "qkv"), k=(k, "qkv"), v=(v, "qkv"), alpha=(alpha, F32),
+          beta=(beta, F32), initial_state=(initial_state, F32), d_o=(d_o, F32), d_final_state=(d_final_state, F32),
+          dq=(dq, F32), dk=(dk, F32), dv=(dv, F32), dalpha=(dalpha, F32), dbeta=(dbeta, F32),
+          d_initial_state=(d_initial_state, F32), cu_seqlens_dev=(cu_seqlens_dev, I64))
     cu = cu_seqlens_host.to("cpu", torch.int64).contiguous()
     s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream_ptr(q.device)
     _check("kda_prefill_backward", load().kda_prefill_backward(
@@ -200,6 +237,13 @@ def _contig(*ts):
             raise ValueError("all tensors must be contiguous")
 
 
+def _shapes(fn: str, **named) -> None:
+    """named: name=(tensor or None, expected shape tuple)."""
+    for name, (t, sh) in named.items():
+        if t is not None and tuple(t.shape) != tuple(sh):
+            raise ValueError(f"{fn}: {name} has shape {tuple(t.shape)}, expected {tuple(sh)}")
+
+
 def prefill_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor,
                     beta: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None,
                     initial_state: Optional[torch.Tensor] = None, snapshot_interval: int = 0,
@@ -215,6 +259,8 @@ def prefill_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: to
     Returns (o [T,H,dv] fp32, final_state [N,H,dv,dk], snapshots [S,H,dv,dk])."""
     T, H, dk = q.shape
     dv = v.shape[2]
+    _shapes("prefill_chunked", k=(k, (T, H, dk)), v=(v, (T, H, dv)), beta=(beta, (T, H)),
+            alpha=(alpha, (T, H, dk) if alpha.dim() == 3 else (T, H)))
     dev = q.device
     if cu_seqlens is None:
         cu_seqlens = torch.tensor([0, T], dtype=torch.int64, device=dev)
@@ -286,6 +332,9 @@ def layer_front(xq: torch.Tensor, xk: torch.Tensor, xv: torch.Tensor, conv_w: to
     alpha_logit [T,H] or [T,H,d], beta_logit [T,H]; conv_state [N,3,3,H,d] or None.
     Returns (q, k, v, alpha, beta, conv_state_out or None), ready for prefill_chunked."""
     T, H, d = xq.shape
+    _shapes("layer_front", xk=(xk, (T, H, d)), xv=(xv, (T, H, d)), conv_w=(conv_w, (3, H, d, 4)),
+            beta_logit=(beta_logit, (T, H)),
+            alpha_logit=(alpha_logit, (T, H, d) if alpha_logit.dim() == 3 else (T, H)))
     dev = xq.device
     if cu_seqlens is None:
         cu_seqlens = torch.tensor([0, T], dtype=torch.int64, device=dev)
@@ -308,6 +357,7 @@ def layer_back(o: torch.Tensor, g_logit: torch.Tensor, norm_w: torch.Tensor, eps
                out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
     """KDA layer back end: RMSNorm(o) * norm_w * sigmoid(g_logit) over d_v; o, g_logit [T,H,dv] fp32."""
     T, H, dv = o.shape
+    _shapes("layer_back", g_logit=(g_logit, (T, H, dv)), norm_w=(norm_w, (dv,)))
     _contig(o, g_logit, norm_w)
     shape = make_shape(H, dv, dv, torch.bfloat16, False)
     out = torch.empty((T, H, dv), dtype=out_dtype, device=o.device)
@@ -324,6 +374,8 @@ def prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: t
     None), all fp32."""
     T, H, dk_ = q.shape
     dv_ = v.shape[2]
+    _shapes("prefill_backward", k=(k, (T, H, dk_)), v=(v, (T, H, dv_)), beta=(beta, (T, H)), d_o=(d_o, (T, H, dv_)),
+            alpha=(alpha, (T, H, dk_) if alpha.dim() == 3 else (T, H)))
     dev = q.device
     if cu_seqlens is None:
         cu_seqlens = torch.tensor([0, T], dtype=torch.int64, device=dev)

@@ -176,7 +176,7 @@ def make_layer_inputs(wl: Workload, device="cpu", seed: Optional[int] = None, co
     beta_logit = _normal((T, H), gen, device)
     o = _normal((T, H, wl.dv), gen, device)
     g_logit = _normal((T, H, wl.dv), gen, device)
-    norm_w = torch.rand((wl.dv,), generator=gen, device=device) + 0.5
+    norm_w = torch.rand((wl.dv,), generator=gen, device=device, dtype=torch.float32) + 0.5
     cu_host = torch.zeros(wl.num_seqs + 1, dtype=torch.int64)
     cu_host[1:] = torch.cumsum(torch.tensor(wl.seq_lens, dtype=torch.int64), 0)
     return dict(xq=xq, xk=xk, xv=xv, conv_w=conv_w, conv_state=state, alpha_logit=alpha_logit,

@@ -256,6 +256,45 @@ def test_layer_host_rejections(K):
     assert back(pk, 4, g=0x2004) == K.KDA_ERR_ALIGN
 
 
+def test_binding_checks_dtypes_and_shapes(K):
+    """The library sees raw pointers, so the binding rejects a tensor of the
+    wrong dtype or shape before any call (all checks run on CPU tensors)."""
+    sh = K.make_shape(2, 64, 64, torch.bfloat16, False)
+    f32 = lambda *s: torch.zeros(s, dtype=torch.float32)  # noqa: E731
+    o, g = f32(5, 2, 64), f32(5, 2, 64)
+    out = torch.zeros((5, 2, 64), dtype=torch.bfloat16)
+    with pytest.raises(TypeError, match="norm_w"):
+        K.kda_layer_back(sh, 5, o, g, torch.zeros(64, dtype=torch.float64), 1e-6, K.KDA_BF16, out)
+    with pytest.raises(TypeError, match="out"):
+        K.kda_layer_back(sh, 5, o, g, f32(64), 1e-6, K.KDA_F32, out)
+    with pytest.raises(ValueError, match="contiguous"):
+        K.kda_layer_back(sh, 5, o.transpose(0, 1), g, f32(64), 1e-6, K.KDA_BF16, out)
+    with pytest.raises(ValueError, match="norm_w"):
+        K.layer_back(o, g, f32(32))
+    q = torch.zeros((5, 2, 64), dtype=torch.float32)          # shape says bf16
+    with pytest.raises(TypeError, match="q"):
+        K.kda_decode_step(sh, 5, q, q, q, f32(5, 2), f32(5, 2), f32(5, 2, 64, 64), f32(5, 2, 64))
+    qb = q.to(torch.bfloat16)
+    with pytest.raises(ValueError, match="beta"):
+        K.prefill_chunked(qb, qb, qb, f32(5, 2), f32(5, 3))
+
+
+def test_input_generators_keep_fp32_under_another_default_dtype():
+    from gated_delta_rule_72_amd import workloads as wl
+    old = torch.get_default_dtype()
+    torch.set_default_dtype(torch.float64)
+    try:
+        w = wl.Workload("dtype_check", H=2, dk=64, dv=64, seq_lens=(9,), dtype="bf16", gate="per_key")
+        li = wl.make_layer_inputs(w, "cpu")
+        pi = wl.make_prefill_inputs(w, "cpu")
+    finally:
+        torch.set_default_dtype(old)
+    for name in ("conv_w", "alpha_logit", "beta_logit", "o", "g_logit", "norm_w"):
+        assert li[name].dtype == torch.float32, name
+    for name in ("alpha", "beta"):
+        assert pi[name].dtype == torch.float32, name
+
+
 def test_binding_fails_loudly_without_library(K, monkeypatch, tmp_path):
     monkeypatch.setattr(K, "_lib", None)
     monkeypatch.setattr(K, "LIB_PATH", str(tmp_path / "missing" / "libkda.so"))

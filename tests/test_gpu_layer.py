@@ -25,6 +25,10 @@ def _np(t):
 
 def _rel(x, ref, cu=None):
     x = x.astype(np.float64)
+    if not np.all(np.isfinite(x)) or not np.all(np.isfinite(ref)):
+        bad = np.argwhere(~np.isfinite(x))
+        print(f"non-finite: candidate {len(bad)} (first {bad[:4].tolist()}), "
+              f"reference {int(np.sum(~np.isfinite(ref)))}", flush=True)
     if cu is None:
         return np.max(np.abs(x - ref)) / max(np.max(np.abs(ref)), 1e-30)
     worst = 0.0

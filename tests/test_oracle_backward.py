@@ -16,7 +16,6 @@ import torch
 
 import oracle
 
-torch.set_default_dtype(torch.float64)
 
 
 def _inputs(seed, cu, H, dk, dv, per_key, grid=None):
@@ -43,7 +42,7 @@ def _inputs(seed, cu, H, dk, dv, per_key, grid=None):
 
 def _autograd(q, k, v, a, b, cu, s0, d_o, d_f, per_key):
     """Plain fp64 token loop + torch.autograd."""
-    t = {n: torch.tensor(x.astype(np.float64), requires_grad=True)
+    t = {n: torch.tensor(x.astype(np.float64), dtype=torch.float64, requires_grad=True)
          for n, x in dict(q=q, k=k, v=v, a=a, b=b, s0=s0).items()}
     loss = 0.0
     for n in range(len(cu) - 1):
@@ -55,8 +54,8 @@ def _autograd(q, k, v, a, b, cu, s0, d_o, d_f, per_key):
             u = t["b"][tok][:, None] * (t["v"][tok] - p)
             S = S + u[:, :, None] * t["k"][tok][:, None, :]
             o = torch.einsum("hij,hj->hi", S, t["q"][tok])
-            loss = loss + (o * torch.tensor(d_o[tok].astype(np.float64))).sum()
-        loss = loss + (S * torch.tensor(d_f[n].astype(np.float64))).sum()
+            loss = loss + (o * torch.tensor(d_o[tok].astype(np.float64), dtype=torch.float64)).sum()
+        loss = loss + (S * torch.tensor(d_f[n].astype(np.float64), dtype=torch.float64)).sum()
     names = ["q", "k", "v", "a", "b", "s0"]
     grads = torch.autograd.grad(loss, [t[n] for n in names], allow_unused=True)
     return {n: (np.zeros(t[n].shape) if g is None else g.numpy()) for n, g in zip(names, grads)}
