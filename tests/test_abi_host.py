@@ -256,6 +256,43 @@ def test_layer_host_rejections(K):
     assert back(pk, 4, g=0x2004) == K.KDA_ERR_ALIGN
 
 
+def test_backward_host_rejections(K):
+    """kda_prefill_backward: every call below fails a host check before anything is enqueued."""
+    lib = K.load()
+    cu = torch.tensor([0, 100, 300], dtype=torch.int64)
+    sh = K.make_shape(2, 64, 64, torch.bfloat16, True)
+    need = K.kda_prefill_backward_workspace_size(sh, cu)
+    assert need > 0
+
+    def call(shape, cu_h, ws_bytes, **kw):
+        p = dict(cu_dev=0x100, q=0x1000, k=0x2000, v=0x3000, a=0x4000, b=0x5000, init=None, do=0x6000, df=None,
+                 dq=0x7000, dk=0x8000, dv=0x9000, da=0xA000, db=0xB000, di=None, ws=0x100000)
+        p.update(kw)
+        f = lambda n: None if p[n] is None else _fake(p[n])  # noqa: E731
+        return lib.kda_prefill_backward(ctypes.byref(shape), cu_h.numel() - 1,
+                                        cu_h.numpy().ctypes.data_as(ctypes.c_void_p), f("cu_dev"), f("q"), f("k"),
+                                        f("v"), f("a"), f("b"), f("init"), f("do"), f("df"), f("dq"), f("dk"),
+                                        f("dv"), f("da"), f("db"), f("di"), f("ws"), ws_bytes, None)
+
+    assert call(sh, torch.tensor([0], dtype=torch.int64), 0) == K.KDA_OK              # no sequences
+    assert call(sh, torch.tensor([2, 5], dtype=torch.int64), need) == K.KDA_ERR_SHAPE
+    assert call(sh, cu, need, do=None) == K.KDA_ERR_ARG
+    assert call(sh, cu, need, da=None) == K.KDA_ERR_ARG
+    assert call(sh, cu, need, cu_dev=None) == K.KDA_ERR_ARG
+    assert call(sh, cu, need, q=0x1008) == K.KDA_ERR_ALIGN                           # 16 B
+    assert call(sh, cu, need, a=0x4004) == K.KDA_ERR_ALIGN                           # per-key alpha: 16 B
+    assert call(sh, cu, need, df=0xC008) == K.KDA_ERR_ALIGN
+    assert call(sh, cu, need, di=0xD004) == K.KDA_ERR_ALIGN
+    assert call(sh, cu, need - 1) == K.KDA_ERR_WORKSPACE
+    assert call(sh, cu, need, ws=None) == K.KDA_ERR_WORKSPACE
+    assert "workspace" in K.kda_last_error()
+    bad = K.make_shape(2, 64, 128, torch.bfloat16, True)
+    assert call(bad, cu, need) == K.KDA_ERR_SHAPE
+    # the plan grows with the work: more chunks, more workspace
+    more = K.kda_prefill_backward_workspace_size(sh, torch.tensor([0, 100, 300, 1000], dtype=torch.int64))
+    assert more > need
+
+
 def test_binding_checks_dtypes_and_shapes(K):
     """The library sees raw pointers, so the binding rejects a tensor of the
     wrong dtype or shape before any call (all checks run on CPU tensors)."""
