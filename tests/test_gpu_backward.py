@@ -114,6 +114,24 @@ def test_backward_only_final_gradient_and_empty_sequences():
     _check(inp, d_o, d_f, got)
 
 
+def test_backward_all_sequences_empty():
+    """T = 0 with two (empty) sequences: no token gradients, and d_initial is
+    d_final bit for bit (zero when d_final is not given)."""
+    dev = device()
+    H, d = 2, 64
+    z = lambda *s: torch.zeros(s, dtype=torch.float32, device=dev)  # noqa: E731
+    q = torch.zeros((0, H, d), dtype=torch.bfloat16, device=dev)
+    cu = torch.tensor([0, 0, 0], dtype=torch.int64, device=dev)
+    d_f = torch.randn((2, H, d, d), device=dev)
+    out = kda.prefill_backward(q, q, q, z(0, H, d), z(0, H), z(0, H, d), cu, None, d_f)
+    torch.cuda.synchronize()
+    assert all(x.numel() == 0 for x in out[:5])
+    assert torch.equal(out[5], d_f)
+    out = kda.prefill_backward(q, q, q, z(0, H, d), z(0, H), z(0, H, d), cu, None, None)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out[5]) == 0
+
+
 def test_backward_deterministic():
     w = custom("bwd_det", H=2, d=128, lens=(300, 5), gate="per_key", seed=76)
     inp, d_o, d_f = _grads_in(w, device(), seed=77)

@@ -90,6 +90,19 @@ def test_front_without_state_and_state_handoff_bitwise():
         assert torch.equal(p2[5], full[5])
 
 
+def test_front_all_sequences_empty_passes_state_through():
+    dev = device()
+    H, d = 2, 64
+    x = torch.zeros((0, H, d), dtype=torch.bfloat16, device=dev)
+    cu = torch.tensor([0, 0, 0], dtype=torch.int64, device=dev)
+    st = torch.randn((2, 3, 3, H, d), device=dev).to(torch.bfloat16)
+    w = torch.zeros((3, H, d, 4), dtype=torch.float32, device=dev)
+    z = torch.zeros((0, H), dtype=torch.float32, device=dev)
+    q, k, v, a, b, st_out = kda.layer_front(x, x, x, w, z, z, cu, st)
+    torch.cuda.synchronize()
+    assert q.numel() == 0 and torch.equal(st_out, st)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32])
 def test_back_matches_oracle(d, out_dtype):
