@@ -9,3 +9,4 @@ from .kda import (  # noqa: F401
     kda_last_error, kda_layer_back, kda_layer_front, kda_prefill_backward, kda_prefill_backward_workspace_size,
     kda_prefill_chunked, kda_prefill_workspace_size,
     kda_snapshot_count, layer_back, layer_front, load, make_shape, prefill_backward, prefill_chunked)
+from .autograd import gated_delta_rule  # noqa: F401,E402

@@ -159,3 +159,18 @@ def test_backward_long_prefill_full_size():
     inp, d_o, d_f = _grads_in(w, device(), seed=81)
     got = _run(inp, d_o, d_f)
     _check(inp, d_o, d_f, got, heads=(0, 9))
+
+
+def test_autograd_function_routes_gradients():
+    """gated_delta_rule (torch.autograd glue): loss.backward() gives exactly
+    what kda.prefill_backward gives for the same incoming gradients."""
+    w = custom("bwd_autograd", H=2, d=64, lens=(150, 30), gate="per_key", dtype="fp32", s0_std=0.05, seed=82)
+    inp, d_o, d_f = _grads_in(w, device(), seed=83)
+    leaves = {n: inp[n].clone().requires_grad_(True) for n in ("q", "k", "v", "alpha", "beta", "initial_state")}
+    o, fin = kda.gated_delta_rule(leaves["q"], leaves["k"], leaves["v"], leaves["alpha"], leaves["beta"],
+                                  inp["cu_seqlens"], leaves["initial_state"], inp["cu_seqlens_host"])
+    ((o * d_o).sum() + (fin * d_f).sum()).backward()
+    torch.cuda.synchronize()
+    ref = _run(inp, d_o, d_f)
+    for (n, x), r in zip(leaves.items(), ref):
+        assert torch.equal(x.grad, r), n
