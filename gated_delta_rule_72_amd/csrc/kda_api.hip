@@ -496,8 +496,8 @@ int kda_prefill_backward(const kda_shape* shape, int32_t num_seqs, const int64_t
   const uintptr_t a_alpha = shape->gate == KDA_GATE_PER_KEY ? 16 : 4;
   const PtrReq reqs[] = {{q, 16, "q"}, {k, 16, "k"}, {v, 16, "v"}, {alpha, a_alpha, "alpha"},
                          {beta, 4, "beta"}, {initial_state, 16, "initial_state"}, {d_o, 4, "d_o"},
-                         {d_final_state, 16, "d_final_state"}, {dq, 4, "dq"}, {dk, 4, "dk"}, {dv, 4, "dv"},
-                         {dalpha, 4, "dalpha"}, {dbeta, 4, "dbeta"}, {d_initial_state, 16, "d_initial_state"},
+                         {d_final_state, 16, "d_final_state"}, {dq, 16, "dq"}, {dk, 16, "dk"}, {dv, 16, "dv"},
+                         {dalpha, a_alpha, "dalpha"}, {dbeta, 4, "dbeta"}, {d_initial_state, 16, "d_initial_state"},
                          {cu_seqlens_dev, 8, "cu_seqlens_dev"}, {workspace, 16, "workspace"}};
   rc = check_align(reqs, (int)(sizeof reqs / sizeof reqs[0]));
   if (rc != KDA_OK) return rc;

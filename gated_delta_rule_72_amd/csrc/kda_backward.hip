@@ -202,6 +202,12 @@ struct GemmArgs {
   float alpha;
   int32_t accumulate;        // add into C
   int32_t mask;              // 0: none, 1: keep row > col, 2: keep row >= col
+  // optional second product of the same transposition, added before the
+  // epilogue: C = alpha (op(A) op(B) + ratio2 op(A2) op(B2)) (ratio2 = +-1)
+  const float *A2, *B2;
+  int64_t sA2, sB2;
+  int32_t lda2, ldb2, K2;
+  float ratio2;
 };
 
 // One workgroup = one 64 x 64 output tile of one unit; four wavefronts of 16
@@ -217,45 +223,50 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   const int64_t b = blockIdx.x / tiles;
   const int tile = (int)(blockIdx.x % tiles);
   const int m0 = (tile / tn) * 64, n0 = (tile % tn) * 64;
-  const float* A = g.A + b * g.sA;
-  const float* B = g.B + b * g.sB;
   float* Cp = g.C + b * g.sC;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, gq = lane >> 4;
   f32x4 acc[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < g.K; k0 += KB) {
+  for (int term = 0; term < (g.A2 ? 2 : 1); ++term) {
+    const float* A = term == 0 ? g.A + b * g.sA : g.A2 + b * g.sA2;
+    const float* B = term == 0 ? g.B + b * g.sB : g.B2 + b * g.sB2;
+    const int lda = term == 0 ? g.lda : g.lda2, ldb = term == 0 ? g.ldb : g.ldb2;
+    const int K = term == 0 ? g.K : g.K2;
+    const float sc = term == 0 ? 1.f : g.ratio2;      // applied to A while staging (exact for +-1)
+    for (int k0 = 0; k0 < K; k0 += KB) {
 #pragma unroll
-    for (int e = tid; e < 512; e += 256) {
-      if constexpr (!TA) {
-        const int r = e >> 3, c = (e & 7) * 4;
-        *reinterpret_cast<f32x4*>(As + r * LDA + c) =
-            *reinterpret_cast<const f32x4*>(A + (int64_t)(m0 + r) * g.lda + k0 + c);
-      } else {
-        const int kk = e >> 4, c = (e & 15) * 4;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(A + (int64_t)(k0 + kk) * g.lda + m0 + c);
+      for (int e = tid; e < 512; e += 256) {
+        if constexpr (!TA) {
+          const int r = e >> 3, c = (e & 7) * 4;
+          *reinterpret_cast<f32x4*>(As + r * LDA + c) =
+              sc * *reinterpret_cast<const f32x4*>(A + (int64_t)(m0 + r) * lda + k0 + c);
+        } else {
+          const int kk = e >> 4, c = (e & 15) * 4;
+          const f32x4 v = *reinterpret_cast<const f32x4*>(A + (int64_t)(k0 + kk) * lda + m0 + c);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) As[(c + i) * LDA + kk] = v[i];
+          for (int i = 0; i < 4; ++i) As[(c + i) * LDA + kk] = sc * v[i];
+        }
+        if constexpr (!TB) {
+          const int kk = e >> 4, c = (e & 15) * 4;
+          *reinterpret_cast<f32x4*>(Bs + kk * LDB + c) =
+              *reinterpret_cast<const f32x4*>(B + (int64_t)(k0 + kk) * ldb + n0 + c);
+        } else {
+          const int n = e >> 3, c = (e & 7) * 4;
+          const f32x4 v = *reinterpret_cast<const f32x4*>(B + (int64_t)(n0 + n) * ldb + k0 + c);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Bs[(c + i) * LDB + n] = v[i];
+        }
       }
-      if constexpr (!TB) {
-        const int kk = e >> 4, c = (e & 15) * 4;
-        *reinterpret_cast<f32x4*>(Bs + kk * LDB + c) =
-            *reinterpret_cast<const f32x4*>(B + (int64_t)(k0 + kk) * g.ldb + n0 + c);
-      } else {
-        const int n = e >> 3, c = (e & 7) * 4;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(B + (int64_t)(n0 + n) * g.ldb + k0 + c);
+      __syncthreads();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Bs[(c + i) * LDB + n] = v[i];
+      for (int ks = 0; ks < KB / 4; ++ks) {
+        const float av = As[(16 * w + l16) * LDA + 4 * ks + gq];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[t] = mfma4(av, Bs[(4 * ks + gq) * LDB + 16 * t + l16], acc[t]);
       }
+      __syncthreads();
     }
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < KB / 4; ++ks) {
-      const float av = As[(16 * w + l16) * LDA + 4 * ks + gq];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) acc[t] = mfma4(av, Bs[(4 * ks + gq) * LDB + 16 * t + l16], acc[t]);
-    }
-    __syncthreads();
   }
 #pragma unroll
   for (int t = 0; t < 4; ++t)
@@ -473,7 +484,8 @@ __global__ __launch_bounds__(D * 4) void segment_end_kernel(BackwardArgs a) {
 // rows in reverse, which is the gradient of log alpha.
 template <int D, bool BF16, bool PER_KEY>
 __global__ __launch_bounds__(256) void assemble_kernel(BackwardArgs a) {
-  constexpr int LDG = D + 1, RG = 256 / D;      // RG threads share a channel
+  constexpr int CQ = D / 4, RG = 256 / CQ;     // a thread owns 4 channels; RG threads share them
+  constexpr int LDG = D + 4;
   __shared__ float sdG[C * LDG];
   __shared__ float sPart[RG * D];
   __shared__ float sGn[D];
@@ -485,51 +497,68 @@ __global__ __launch_bounds__(256) void assemble_kernel(BackwardArgs a) {
   const float* ws = a.ws;
   auto nd = [&](int arr) { return ws + nd_off(arr, units, D) + b * C * D; };
   auto nn = [&](int arr) { return ws + nn_off(arr, units, D) + b * C * C; };
+  auto ld4 = [](const float* p_) { return *reinterpret_cast<const f32x4*>(p_); };
   const float* beta = ws + beta_off(units, D) + b * C;
   const float *G = nd(GG), *dQp = nd(DQP), *dQa = nd(DQA), *dKp = nd(DKP), *dKm = nd(DKM), *dX = nd(DX),
               *dKt = nd(DKT), *dY = nd(DY);
   const int cref = ref_row(p.len);
-  const int j = tid % D, rg = tid / D;
-  {                                     // elementwise part
-    const float Gc = G[cref * D + j], Gn = G[(C - 1) * D + j];
-    float kt_part = 0.f;
-#pragma unroll 4
+  const int j4 = 4 * (tid % CQ), rg = tid / CQ;
+  {                                     // elementwise part, four channels per thread
+    const f32x4 Gc = ld4(G + cref * D + j4), Gn = ld4(G + (C - 1) * D + j4);
+    f32x4 kt_part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
     for (int r = rg; r < C; r += RG) {
-      const int e = r * D + j;
-      float qv = 0.f, kv = 0.f;
+      const int e = r * D + j4;
+      f32x4 qv = {0.f, 0.f, 0.f, 0.f}, kv = {0.f, 0.f, 0.f, 0.f};
       int64_t o = 0;
       if (r < p.len) {
-        o = ((p.t0 + r) * a.H + h) * D + j;
-        qv = load1<BF16>(a.q, o);
-        kv = load1<BF16>(a.k, o);
+        o = ((p.t0 + r) * a.H + h) * D + j4;
+        qv = load4<BF16>(a.q, o);
+        kv = load4<BF16>(a.k, o);
       }
-      const float g = G[e];
-      const float eRel = __expf(g - Gc), eInv = __expf(Gc - g), eAbs = __expf(g), eTail = __expf(Gn - g);
-      const float dKa = beta[r] * dX[e];
-      const float kt = kv * eTail;
-      sdG[r * LDG + j] = dQp[e] * (qv * eRel) + dQa[e] * (qv * eAbs) + dKp[e] * (kv * eRel) -
-                         dKm[e] * (kv * eInv) + dKa * (kv * eAbs) - dKt[e] * kt;
-      kt_part += dKt[e] * kt;
+      const f32x4 g = ld4(G + e), dqp = ld4(dQp + e), dqa = ld4(dQa + e), dkp = ld4(dKp + e), dkm = ld4(dKm + e),
+                  dx = ld4(dX + e), dkt = ld4(dKt + e), dy = ld4(dY + e);
+      const float br = beta[r];
+      f32x4 dG, dq, dk;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float eRel = __expf(g[i] - Gc[i]), eInv = __expf(Gc[i] - g[i]), eAbs = __expf(g[i]),
+                    eTail = __expf(Gn[i] - g[i]);
+        const float dKa = br * dx[i];
+        const float kt = kv[i] * eTail;
+        dG[i] = dqp[i] * (qv[i] * eRel) + dqa[i] * (qv[i] * eAbs) + dkp[i] * (kv[i] * eRel) -
+                dkm[i] * (kv[i] * eInv) + dKa * (kv[i] * eAbs) - dkt[i] * kt;
+        kt_part[i] += dkt[i] * kt;
+        dq[i] = dqp[i] * eRel + dqa[i] * eAbs;
+        dk[i] = dkp[i] * eRel + dkm[i] * eInv + dKa * eAbs + dkt[i] * eTail;
+      }
+      *reinterpret_cast<f32x4*>(sdG + r * LDG + j4) = dG;
       if (r < p.len) {
-        a.dq[o] = dQp[e] * eRel + dQa[e] * eAbs;
-        a.dk[o] = dKp[e] * eRel + dKm[e] * eInv + dKa * eAbs + dKt[e] * eTail;
-        a.dv[o] = beta[r] * dY[e];
+        *reinterpret_cast<f32x4*>(a.dq + o) = dq;
+        *reinterpret_cast<f32x4*>(a.dk + o) = dk;
+        *reinterpret_cast<f32x4*>(a.dv + o) = br * dy;
       }
     }
     // gradient of Gamma_n: sum over rows of dKt * Kt, and colsum(dS_n * S0) e^Gamma_n
     const float* dSn = ws + dd_off(DSN, units, D) + b * D * D;
     const float* S0 = ws + dd_off(S0M, units, D) + b * D * D;
-    float st = 0.f;
+    f32x4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-    for (int i = rg; i < D; i += RG) st += dSn[(int64_t)i * D + j] * S0[(int64_t)i * D + j];
-    sPart[rg * D + j] = kt_part + st * ws[egn_off(units, D) + b * D + j];
+    for (int i = rg; i < D; i += RG) st += ld4(dSn + (int64_t)i * D + j4) * ld4(S0 + (int64_t)i * D + j4);
+    *reinterpret_cast<f32x4*>(sPart + rg * D + j4) = kt_part + st * ld4(ws + egn_off(units, D) + b * D + j4);
   }
-  {                                     // dbeta: four lanes per row
+  {                                     // dbeta: four lanes per row, a quarter of the channels each
     const int r = tid >> 2, part = tid & 3;
     const float *V = nd(VF), *Ka = nd(KA), *dL = nn(DLM), *P = nn(PM);
-    float s = 0.f;
-    for (int jj = part; jj < D; jj += 4) s += dY[r * D + jj] * V[r * D + jj] + dX[r * D + jj] * Ka[r * D + jj];
-    for (int i = part; i < C; i += 4) s += dL[r * C + i] * P[r * C + i];
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int jj = part * (D / 4); jj < (part + 1) * (D / 4); jj += 4) {
+      const int e = r * D + jj;
+      acc += ld4(dY + e) * ld4(V + e) + ld4(dX + e) * ld4(Ka + e);
+    }
+#pragma unroll
+    for (int i = part * 16; i < part * 16 + 16; i += 4) acc += ld4(dL + r * C + i) * ld4(P + r * C + i);
+    float s = acc[0] + acc[1] + acc[2] + acc[3];
     s += __shfl_xor(s, 1, 4);
     s += __shfl_xor(s, 2, 4);
     if (part == 0 && r < p.len) a.dbeta[(p.t0 + r) * a.H + h] = s;
@@ -551,10 +580,10 @@ __global__ __launch_bounds__(256) void assemble_kernel(BackwardArgs a) {
   }
   __syncthreads();
   if constexpr (PER_KEY) {
-    for (int idx = tid; idx < p.len * D; idx += 256) {
-      const int r = idx / D, jj = idx % D;
+    for (int idx = tid; idx < p.len * CQ; idx += 256) {
+      const int r = idx / CQ, jj = 4 * (idx % CQ);
       const int64_t o = ((p.t0 + r) * a.H + h) * D + jj;
-      a.dalpha[o] = sdG[r * LDG + jj] / a.alpha[o];
+      *reinterpret_cast<f32x4*>(a.dalpha + o) = ld4(sdG + r * LDG + jj) / ld4(a.alpha + o);
     }
   } else {
     if (tid < p.len) {
@@ -566,10 +595,21 @@ __global__ __launch_bounds__(256) void assemble_kernel(BackwardArgs a) {
   }
 }
 
+struct Term2 {
+  const float *A = nullptr, *B = nullptr;
+  int lda = 0;
+  int64_t sA = 0;
+  int ldb = 0;
+  int64_t sB = 0;
+  int K = 0;
+  float ratio = 1.f;
+};
+
 hipError_t gemm(bool ta, bool tb, int64_t units, int d, int M, int N, int K, const float* A, int lda, int64_t sA,
                 const float* B, int ldb, int64_t sB, float* Cm, int ldc, int64_t sC, float alpha, bool accumulate,
-                int mask, const float* rs, hipStream_t s) {
-  GemmArgs g{A, B, Cm, rs, sA, sB, sC, C, lda, ldb, ldc, M, N, K, alpha, accumulate ? 1 : 0, mask};
+                int mask, const float* rs, const Term2& t2, hipStream_t s) {
+  GemmArgs g{A, B, Cm, rs, sA, sB, sC, C, lda, ldb, ldc, M, N, K, alpha, accumulate ? 1 : 0, mask,
+             t2.A, t2.B, t2.sA, t2.sB, t2.lda, t2.ldb, t2.K, t2.ratio};
   (void)d;
   const dim3 grid((unsigned)(units * (M / 64) * (N / 64)));
   if (!ta && !tb) hipLaunchKernelGGL((gemm_kernel<false, false>), grid, dim3(256), 0, s, g);
@@ -594,7 +634,8 @@ hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
     const int64_t sND = (int64_t)C * D, sNN = (int64_t)C * C, sDD = (int64_t)D * D;
     hipLaunchKernelGGL((prep_kernel<D, BF16, PK>), dim3((unsigned)U), dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-#define G_(...) if ((e = gemm(__VA_ARGS__, s)) != hipSuccess) return e
+#define G_(...) if ((e = gemm(__VA_ARGS__, Term2{}, s)) != hipSuccess) return e
+#define G2_(...) if ((e = gemm(__VA_ARGS__, s)) != hipSuccess) return e
     // forward quantities
     G_(false, true, U, D, C, C, D, ND(KP), D, sND, ND(KM), D, sND, NN(PM), C, sNN, 1.f, false, 0, nullptr);
     hipLaunchKernelGGL(inverse_kernel, dim3((unsigned)U), dim3(64), 0, s, a, (int32_t)D);
@@ -605,8 +646,9 @@ hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
     G_(false, true, U, D, C, C, D, ND(QP), D, sND, ND(KM), D, sND, NN(BM), C, sNN, 1.f, false, 2, nullptr);
     // inputs of the reverse scan
     G_(true, false, U, D, C, D, C, NN(BM), C, sNN, ND(DOF), D, sND, ND(ZU), D, sND, 1.f, false, 0, nullptr);
-    G_(true, false, U, D, D, D, C, ND(DOF), D, sND, ND(QA), D, sND, DDp(EM), D, sDD, 1.f, false, 0, nullptr);
-    G_(true, false, U, D, D, D, C, ND(ZU), D, sND, ND(WM), D, sND, DDp(EM), D, sDD, -1.f, true, 0, nullptr);
+    // E = dO^T Qa - Z^T W in one launch
+    G2_(true, false, U, D, D, D, C, ND(DOF), D, sND, ND(QA), D, sND, DDp(EM), D, sDD, 1.f, false, 0, nullptr,
+       Term2{ND(ZU), ND(WM), D, sND, D, sND, C, -1.f});
   }
   const dim3 scan_grid((unsigned)(a.n_items * a.H));
   if (a.seg_chunks > 0) {
@@ -628,19 +670,22 @@ hipError_t backward_t(const BackwardArgs& a, hipStream_t s) {
     G_(false, true, U, D, C, C, D, ND(DOF), D, sND, ND(UM), D, sND, NN(DBM), C, sNN, 1.f, false, 2, nullptr);
     G_(false, false, U, D, C, D, C, NN(DBM), C, sNN, ND(KM), D, sND, ND(DQP), D, sND, 1.f, false, 0, nullptr);
     G_(false, false, U, D, C, D, D, ND(DOF), D, sND, DDp(S0M), D, sDD, ND(DQA), D, sND, 1.f, false, 0, nullptr);
-    G_(true, false, U, D, C, D, C, NN(DBM), C, sNN, ND(QP), D, sND, ND(DKM), D, sND, 1.f, false, 0, nullptr);
     G_(false, false, U, D, C, D, D, ND(UM), D, sND, DDp(DSN), D, sDD, ND(DKT), D, sND, 1.f, false, 0, nullptr);
     G_(false, false, U, D, C, D, D, ND(ZU), D, sND, DDp(S0M), D, sDD, ND(DW), D, sND, -1.f, false, 0, nullptr);
-    G_(false, true, U, D, C, C, D, ND(DW), D, sND, ND(XA), D, sND, NN(DAM), C, sNN, 1.f, false, 0, nullptr);
-    G_(false, true, U, D, C, C, D, ND(ZU), D, sND, ND(YB), D, sND, NN(DAM), C, sNN, 1.f, true, 0, nullptr);
+    // dA = dW X^T + dU Y^T in one launch
+    G2_(false, true, U, D, C, C, D, ND(DW), D, sND, ND(XA), D, sND, NN(DAM), C, sNN, 1.f, false, 0, nullptr,
+       Term2{ND(ZU), ND(YB), D, sND, D, sND, D, 1.f});
     G_(true, false, U, D, C, D, C, NN(AM), C, sNN, ND(DW), D, sND, ND(DX), D, sND, 1.f, false, 0, nullptr);
     G_(true, false, U, D, C, D, C, NN(AM), C, sNN, ND(ZU), D, sND, ND(DY), D, sND, 1.f, false, 0, nullptr);
     G_(false, true, U, D, C, C, C, NN(DAM), C, sNN, NN(AM), C, sNN, NN(TM), C, sNN, 1.f, false, 0, nullptr);
     G_(true, false, U, D, C, C, C, NN(AM), C, sNN, NN(TM), C, sNN, NN(DLM), C, sNN, -1.f, false, 1, nullptr);
     G_(false, false, U, D, C, D, C, NN(DLM), C, sNN, ND(KM), D, sND, ND(DKP), D, sND, 1.f, false, 0,
        w + beta_off(U, D));
-    G_(true, false, U, D, C, D, C, NN(DLM), C, sNN, ND(XP), D, sND, ND(DKM), D, sND, 1.f, true, 0, nullptr);
+    // dKm = dBm^T Qp + dL^T (B Kp) in one launch
+    G2_(true, false, U, D, C, D, C, NN(DBM), C, sNN, ND(QP), D, sND, ND(DKM), D, sND, 1.f, false, 0, nullptr,
+       Term2{NN(DLM), ND(XP), C, sNN, D, sND, C, 1.f});
 #undef G_
+#undef G2_
     hipLaunchKernelGGL((assemble_kernel<D, BF16, PK>), dim3((unsigned)U), dim3(256), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

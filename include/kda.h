@@ -247,8 +247,9 @@ int kda_prefill_backward_workspace_size(const kda_shape* shape, int32_t num_seqs
  * dv [T, H, d_v], dalpha shaped like alpha, dbeta [T, H], d_initial_state
  * [num_seqs, H, d_v, d_k] or NULL (not wanted). Outputs must not overlap the
  * inputs, except that d_initial_state may be d_final_state.
- * Alignment: q, k, v, per-key alpha, initial_state, d_final_state,
- * d_initial_state and workspace 16 bytes; the rest 4 (cu_seqlens_dev 8).
+ * Alignment: q, k, v, per-key alpha and dalpha, initial_state,
+ * d_final_state, dq, dk, dv, d_initial_state and workspace 16 bytes; the
+ * rest 4 (cu_seqlens_dev 8).
  * Precondition (beyond kda_prefill_chunked's): within each 64-token chunk the
  * decay over any 32 consecutive tokens is at least 2^-120 per channel, so the
  * decay factors relative to the chunk's middle row stay inside fp32.
