@@ -167,11 +167,9 @@ __global__ __launch_bounds__(256) void prep_kernel(BackwardArgs a) {
     ws[nd_off(KP, units, D) + o] = kv * eRel;
     ws[nd_off(KM, units, D) + o] = kv * eInv;
     ws[nd_off(QP, units, D) + o] = qv * eRel;
-    ws[nd_off(KA, units, D) + o] = kv * eAbs;
     ws[nd_off(XA, units, D) + o] = be * (kv * eAbs);
     ws[nd_off(QA, units, D) + o] = qv * eAbs;
     ws[nd_off(KT, units, D) + o] = kv * eTail;
-    ws[nd_off(VF, units, D) + o] = vv;
     ws[nd_off(YB, units, D) + o] = be * vv;
     ws[nd_off(DOF, units, D) + o] = dov;
     ws[nd_off(XP, units, D) + o] = be * (kv * eRel);
@@ -489,6 +487,7 @@ __global__ __launch_bounds__(256) void assemble_kernel(BackwardArgs a) {
   __shared__ float sdG[C * LDG];
   __shared__ float sPart[RG * D];
   __shared__ float sGn[D];
+  __shared__ float sBp[C * CQ];                 // per row, per channel quad: dY*V + dX*Ka
   const int64_t units = a.n_chunks * a.H;
   const int64_t b = blockIdx.x;
   const int h = (int)(b % a.H);
@@ -509,17 +508,19 @@ __global__ __launch_bounds__(256) void assemble_kernel(BackwardArgs a) {
 #pragma unroll 2
     for (int r = rg; r < C; r += RG) {
       const int e = r * D + j4;
-      f32x4 qv = {0.f, 0.f, 0.f, 0.f}, kv = {0.f, 0.f, 0.f, 0.f};
+      f32x4 qv = {0.f, 0.f, 0.f, 0.f}, kv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
       int64_t o = 0;
       if (r < p.len) {
         o = ((p.t0 + r) * a.H + h) * D + j4;
         qv = load4<BF16>(a.q, o);
         kv = load4<BF16>(a.k, o);
+        vv = load4<BF16>(a.v, o);
       }
       const f32x4 g = ld4(G + e), dqp = ld4(dQp + e), dqa = ld4(dQa + e), dkp = ld4(dKp + e), dkm = ld4(dKm + e),
                   dx = ld4(dX + e), dkt = ld4(dKt + e), dy = ld4(dY + e);
       const float br = beta[r];
       f32x4 dG, dq, dk;
+      float bpart = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float eRel = __expf(g[i] - Gc[i]), eInv = __expf(Gc[i] - g[i]), eAbs = __expf(g[i]),
@@ -531,8 +532,10 @@ __global__ __launch_bounds__(256) void assemble_kernel(BackwardArgs a) {
         kt_part[i] += dkt[i] * kt;
         dq[i] = dqp[i] * eRel + dqa[i] * eAbs;
         dk[i] = dkp[i] * eRel + dkm[i] * eInv + dKa * eAbs + dkt[i] * eTail;
+        bpart += dy[i] * vv[i] + dx[i] * (kv[i] * eAbs);
       }
       *reinterpret_cast<f32x4*>(sdG + r * LDG + j4) = dG;
+      sBp[r * CQ + j4 / 4] = bpart;
       if (r < p.len) {
         *reinterpret_cast<f32x4*>(a.dq + o) = dq;
         *reinterpret_cast<f32x4*>(a.dk + o) = dk;
@@ -547,18 +550,15 @@ __global__ __launch_bounds__(256) void assemble_kernel(BackwardArgs a) {
     for (int i = rg; i < D; i += RG) st += ld4(dSn + (int64_t)i * D + j4) * ld4(S0 + (int64_t)i * D + j4);
     *reinterpret_cast<f32x4*>(sPart + rg * D + j4) = kt_part + st * ld4(ws + egn_off(units, D) + b * D + j4);
   }
-  {                                     // dbeta: four lanes per row, a quarter of the channels each
+  __syncthreads();
+  {                                     // dbeta: four lanes per row
     const int r = tid >> 2, part = tid & 3;
-    const float *V = nd(VF), *Ka = nd(KA), *dL = nn(DLM), *P = nn(PM);
+    const float *dL = nn(DLM), *P = nn(PM);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int jj = part * (D / 4); jj < (part + 1) * (D / 4); jj += 4) {
-      const int e = r * D + jj;
-      acc += ld4(dY + e) * ld4(V + e) + ld4(dX + e) * ld4(Ka + e);
-    }
 #pragma unroll
     for (int i = part * 16; i < part * 16 + 16; i += 4) acc += ld4(dL + r * C + i) * ld4(P + r * C + i);
     float s = acc[0] + acc[1] + acc[2] + acc[3];
+    for (int q = part * (CQ / 4); q < (part + 1) * (CQ / 4); ++q) s += sBp[r * CQ + q];
     s += __shfl_xor(s, 1, 4);
     s += __shfl_xor(s, 2, 4);
     if (part == 0 && r < p.len) a.dbeta[(p.t0 + r) * a.H + h] = s;

@@ -118,7 +118,7 @@ hipError_t launch_layer_back(const LayerBackArgs& a, int d, bool out_bf16, hipSt
 // 64 x D (chunk rows x channels), 64 x 64 and D x D, each as one region of
 // n_units consecutive blocks, followed by exp(Gamma_n) [D] and beta [64].
 namespace bwd {
-enum ArrND { KP, KM, QP, KA, XA, QA, KT, VF, YB, DOF, XP, WM, UM, ZU, DQP, DQA, DKM, DKT, DW, DX, DY, DKP, GG, N_ND };
+enum ArrND { KP, KM, QP, XA, QA, KT, YB, DOF, XP, WM, UM, ZU, DQP, DQA, DKM, DKT, DW, DX, DY, DKP, GG, N_ND };
 enum ArrNN { PM, AM, BM, DBM, DAM, TM, DLM, N_NN };
 enum ArrDD { S0M, DSN, EM, N_DD };
 __host__ __device__ constexpr int64_t nd_off(int a, int64_t units, int d) { return (int64_t)a * units * 64 * d; }
