@@ -321,13 +321,41 @@ __device__ __forceinline__ int item_seq(const BackwardArgs& a, int64_t item) {
   return lo;
 }
 
+// Three-term bf16 products: Kt and W^T are staged in LDS as bf16 hi + lo
+// (hi = bf16(x), lo = bf16(x - hi)), and R and V1 enter as hi + lo pairs of
+// their accumulator tiles (the permuted-K operand: lane group g supplies rows
+// 4g..4g+3 of two consecutive 16-row tiles), so each 16x16x32 product is
+// hi*hi + hi*lo + lo*hi (about 16 significant bits) accumulated in fp32.
+__device__ __forceinline__ void split_pair_bf16(f32x4 t0, f32x4 t1, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    hi[i] = (__bf16)t0[i];
+    lo[i] = (__bf16)(t0[i] - (float)hi[i]);
+    hi[4 + i] = (__bf16)t1[i];
+    lo[4 + i] = (__bf16)(t1[i] - (float)hi[4 + i]);
+  }
+}
+// elements k0 + 4g .. +3 and k0 + 16 + 4g .. +3 of one bf16 row
+__device__ __forceinline__ bf16x8 ld_perm_bf16(const __bf16* row, int k0, int gq) {
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  const bf16x4_t x0 = *reinterpret_cast<const bf16x4_t*>(row + k0 + 4 * gq);
+  const bf16x4_t x1 = *reinterpret_cast<const bf16x4_t*>(row + k0 + 16 + 4 * gq);
+  return bf16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+}
+__device__ __forceinline__ f32x4 mfma3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, f32x4 c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, c, 0, 0, 0);
+}
+
 template <int D, bool MAP>
 __global__ __launch_bounds__(D * 4) void scan_kernel(BackwardArgs a) {
-  constexpr int LD = D + 4;
+  constexpr int LDK = D + 8;                       // Kt hi/lo: [chunk row][d_k]
+  constexpr int LDW = C + 8;                       // W^T hi/lo: [d_k][chunk row]
   constexpr int NT = D / 16;                       // accumulator tiles per chain
   constexpr int PF = C * D / 4 / (D * 4);          // float4 of Kt (and of W) per thread per chunk
-  __shared__ float Kts[C * LD];
-  __shared__ float Ws[C * LD];
+  __shared__ __bf16 KtH[C * LDK], KtL[C * LDK];
+  __shared__ __bf16 WtH[D * LDW], WtL[D * LDW];
   const int chain = MAP ? (int)(blockIdx.x & 1) : 0;      // MAP: 0 = M, 1 = N
   const int64_t unit = MAP ? blockIdx.x >> 1 : blockIdx.x;
   const int64_t item = unit / a.H;
@@ -382,9 +410,19 @@ __global__ __launch_bounds__(D * 4) void scan_kernel(BackwardArgs a) {
     for (int q = 0; q < PF; ++q) {
       const int e = tid + q * D * 4;
       const int r = e / (D / 4), c4 = (e % (D / 4)) * 4;
-      *reinterpret_cast<f32x4*>(Kts + r * LD + c4) = pk[q];
-      *reinterpret_cast<f32x4*>(Ws + r * LD + c4) = pw[q];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const __bf16 kh = (__bf16)pk[q][i], wh = (__bf16)pw[q][i];
+        KtH[r * LDK + c4 + i] = kh;
+        KtL[r * LDK + c4 + i] = (__bf16)(pk[q][i] - (float)kh);
+        WtH[(c4 + i) * LDW + r] = wh;
+        WtL[(c4 + i) * LDW + r] = (__bf16)(pw[q][i] - (float)wh);
+      }
     }
+    // R as hi + lo permuted-K operands (K = d_k in steps of 32)
+    bf16x8 rh[D / 32], rl[D / 32];
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) split_pair_bf16(R[2 * ks], R[2 * ks + 1], rh[ks], rl[ks]);
     __syncthreads();
     if (c > c0) fetch(c - 1);
     const float* E = a.ws + dd_off(EM, units, D) + b * DD + rowoff;
@@ -393,21 +431,24 @@ __global__ __launch_bounds__(D * 4) void scan_kernel(BackwardArgs a) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       V1[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const __bf16* kh = KtH + (16 * s + l16) * LDK;
+      const __bf16* kl = KtL + (16 * s + l16) * LDK;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const f32x4 av = *reinterpret_cast<const f32x4*>(Kts + (16 * s + l16) * LD + 16 * t + 4 * gq);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) V1[s] = mfma4(av[i], R[t][i], V1[s]);
-      }
+      for (int ks = 0; ks < D / 32; ++ks)
+        V1[s] = mfma3(ld_perm_bf16(kh, 32 * ks, gq), ld_perm_bf16(kl, 32 * ks, gq), rh[ks], rl[ks], V1[s]);
     }
+    bf16x8 vh[2], vl[2];                            // V1 as operand (K = chunk rows, 2 steps)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) split_pair_bf16(V1[2 * ks], V1[2 * ks + 1], vh[ks], vl[ks]);
     const bool with_e = !MAP || chain == 1;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      const __bf16* wh = WtH + (16 * t + l16) * LDW;
+      const __bf16* wl = WtL + (16 * t + l16) * LDW;
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x = mfma4(Ws[(16 * s + 4 * gq + i) * LD + 16 * t + l16], V1[s][i], x);
+      for (int ks = 0; ks < 2; ++ks)
+        x = mfma3(ld_perm_bf16(wh, 32 * ks, gq), ld_perm_bf16(wl, 32 * ks, gq), vh[ks], vl[ks], x);
       const f32x4 gv = *reinterpret_cast<const f32x4*>(eg + 16 * t + 4 * gq);
       const f32x4 ev = with_e ? *reinterpret_cast<const f32x4*>(E + 16 * t + 4 * gq) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
