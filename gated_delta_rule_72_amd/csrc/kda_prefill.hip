@@ -302,20 +302,31 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<D, BF16, PER_KEY, NT>& R, c
 //   eight wavefronts (w and w+4 share a SIMD): w0: R0 I0, R1 I1, inv 0,1 |
 //                     w1: R2 I2, R3 I3, inv 2,3 | w2: R3 I0-1 | w3: R3 I2, R2 I1 |
 //                     w6: R2 I0 | w7: R1 I0                            (3/3/3/3)
+// Four 12-bit run codes in the 16-bit fields of one 64-bit constant (field w
+// for wavefront w): the lookup is register arithmetic, not a memory load.
+constexpr uint64_t pack_runs(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+  return (uint64_t)w0 | ((uint64_t)w1 << 16) | ((uint64_t)w2 << 32) | ((uint64_t)w3 << 48);
+}
 template <int NW>
-__device__ __forceinline__ bool gram_run(int wave, int run, int& R, int& I0, int& I1) {
-  // packed per wavefront: for each run a nibble triple (R, I0, I1); 0xF = no run
-  uint32_t code;
+__device__ __forceinline__ bool gram_run(int wave_lane, int run, int& R, int& I0, int& I1) {
+  // per wavefront and run a nibble triple (R, I0, I1); 0xFFF = no run. The
+  // wavefront index is uniform: the selection runs on scalar registers.
+  const int wave = __builtin_amdgcn_readfirstlane(wave_lane);
+  uint64_t packed;
   if constexpr (NW == 4) {
-    constexpr uint32_t kRun0[4] = {0x302, 0x201, 0x000, 0x222};
-    constexpr uint32_t kRun1[4] = {0xFFF, 0x100, 0x111, 0x333};
-    code = run == 0 ? kRun0[wave & 3] : kRun1[wave & 3];
+    constexpr uint64_t kRun0 = pack_runs(0x302, 0x201, 0x000, 0x222);
+    constexpr uint64_t kRun1 = pack_runs(0xFFF, 0x100, 0x111, 0x333);
+    packed = run == 0 ? kRun0 : kRun1;
   } else {
     static_assert(NW == 8, "four or eight wavefronts");
-    constexpr uint32_t kRun0[8] = {0x000, 0x222, 0x301, 0x322, 0xFFF, 0xFFF, 0x200, 0x100};
-    constexpr uint32_t kRun1[8] = {0x111, 0x333, 0xFFF, 0x211, 0xFFF, 0xFFF, 0xFFF, 0xFFF};
-    code = run == 0 ? kRun0[wave & 7] : kRun1[wave & 7];
+    constexpr uint64_t kRun0Lo = pack_runs(0x000, 0x222, 0x301, 0x322);   // wavefronts 0-3
+    constexpr uint64_t kRun0Hi = pack_runs(0xFFF, 0xFFF, 0x200, 0x100);   // wavefronts 4-7
+    constexpr uint64_t kRun1Lo = pack_runs(0x111, 0x333, 0xFFF, 0x211);
+    constexpr uint64_t kRun1Hi = pack_runs(0xFFF, 0xFFF, 0xFFF, 0xFFF);
+    const bool hi = (wave & 7) >= 4;
+    packed = run == 0 ? (hi ? kRun0Hi : kRun0Lo) : (hi ? kRun1Hi : kRun1Lo);
   }
+  const uint32_t code = (uint32_t)(packed >> (16 * (wave & 3))) & 0xFFFu;
   if (code == 0xFFF) return false;
   R = code >> 8;
   I0 = (code >> 4) & 15;
@@ -431,6 +442,11 @@ void prefill_kernel(PrefillArgs a) {
       }
     }
   }
+  // vmcnt(0): the start state has landed. Without this wait on every path into
+  // the chunk loop, the compiler keeps the load pending around the loop and
+  // waits for all vector memory traffic (the next chunk's prefetch included)
+  // before the state's first use in every chunk.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   const int n_chunks = (item.n_tokens + C - 1) / C;
   const uint32_t HDu = (uint32_t)a.H * D;
