@@ -115,7 +115,8 @@ int device_cu_count() {
 // chain in one workgroup.
 struct PrefillPlan {
   int32_t seg_chunks, n_items;
-  size_t items_off, first_off, maps_off, states_off, inverse_off, bytes;
+  int32_t any_whole;   // segmented: some sequence is short enough to stay whole
+  size_t items_off, first_off, maps_off, states_off, wu_off, bytes;
 };
 
 PrefillPlan plan_prefill(const kda_shape* s, int32_t num_seqs, const int64_t* cu,
@@ -146,7 +147,9 @@ PrefillPlan plan_prefill(const kda_shape* s, int32_t num_seqs, const int64_t* cu
   for (int32_t n = 0; n < num_seqs; ++n) {
     const int64_t len = cu[n + 1] - cu[n];
     const int64_t st = seg * kChunk;
-    items += (st > 0 && len > st) ? (len + st - 1) / st : 1;
+    const bool split = st > 0 && len > st;
+    items += split ? (len + st - 1) / st : 1;
+    if (!split) p.any_whole = 1;
   }
   p.n_items = (int32_t)items;
   const size_t H = (size_t)s->num_heads, DD = (size_t)s->d_k * s->d_v;
@@ -159,8 +162,8 @@ PrefillPlan plan_prefill(const kda_shape* s, int32_t num_seqs, const int64_t* cu
   if (seg > 0) off += round_up((size_t)items * H * 2 * DD * sizeof(float));
   p.states_off = off;
   if (seg > 0) off += round_up((size_t)items * H * DD * sizeof(float));
-  p.inverse_off = off;
-  if (seg > 0) off += round_up((size_t)items * H * (size_t)seg * kda::kInverseBytes);
+  p.wu_off = off;
+  if (seg > 0) off += round_up((size_t)items * H * (size_t)seg * kda::wu_chunk_bytes(s->d_k));
   p.bytes = off;
   return p;
 }
@@ -328,7 +331,8 @@ int kda_prefill_chunked(const kda_shape* shape, int32_t num_seqs,
   a.seq_first_item = reinterpret_cast<int32_t*>(ws + plan.first_off);
   a.seg_maps = plan.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.maps_off) : nullptr;
   a.seg_states = plan.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.states_off) : nullptr;
-  a.seg_inverse = plan.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.inverse_off) : nullptr;
+  a.seg_wu = plan.seg_chunks > 0 ? static_cast<void*>(ws + plan.wu_off) : nullptr;
+  a.any_whole = plan.any_whole;
   hipError_t e = kda::launch_prefill(a, shape->d_k, shape->qkv_dtype == KDA_BF16,
                                      shape->gate == KDA_GATE_PER_KEY,
                                      static_cast<hipStream_t>(hip_stream));
@@ -529,7 +533,8 @@ int kda_prefill_backward(const kda_shape* shape, int32_t num_seqs, const int64_t
   f.seq_first_item = reinterpret_cast<int32_t*>(ws + plan.fwd.first_off);
   f.seg_maps = plan.fwd.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.fwd.maps_off) : nullptr;
   f.seg_states = plan.fwd.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.fwd.states_off) : nullptr;
-  f.seg_inverse = plan.fwd.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.fwd.inverse_off) : nullptr;
+  f.seg_wu = plan.fwd.seg_chunks > 0 ? static_cast<void*>(ws + plan.fwd.wu_off) : nullptr;
+  f.any_whole = plan.fwd.any_whole;
   hipError_t e = kda::launch_prefill(f, shape->d_k, bf16, pk, st);
   if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "backward: forward launch failed: %s", hipGetErrorString(e));
 

@@ -81,12 +81,16 @@ struct PrefillArgs {
   int32_t* seq_first_item;   // workspace: [N] first item of each sequence (segmented)
   float* seg_maps;           // workspace: per (item, head) M (dk x dk) then N (dv x dk)
   float* seg_states;         // workspace: per (item, head) start state (dv x dk)
-  float* seg_inverse;        // workspace: per (item, head, chunk) the chunk's (I + L)^-1 block
-                             // layout as the map pass leaves it in LDS, reused by pass 3
+  void* seg_wu;              // workspace: per (item, head, chunk) the chunk's W (fp16, the
+                             // LDS layout the map pass leaves it in) and U' (fp32, one
+                             // accumulator tile per lane), reused by pass 3
+  int32_t any_whole;         // segmented plan: some sequence is not split (needs its own pass)
 };
 hipError_t launch_prefill(PrefillArgs a, int d, bool bf16, bool per_key, hipStream_t s);
-// bytes of one chunk's stored inverse: 64 rows of 68 fp32 (the LDS row stride)
-constexpr size_t kInverseBytes = 64 * 68 * 4;
+// Bytes of one chunk's stored W and U' at d = d_k = d_v: W as 64 rows of d + 8
+// fp16 (the LDS row stride, a whole number of KiB), then U' as 64 x d fp32.
+constexpr size_t wu_w_bytes(int d) { return (size_t)64 * (d + 8) * 2; }
+constexpr size_t wu_chunk_bytes(int d) { return wu_w_bytes(d) + (size_t)64 * d * 4; }
 
 // Layer front end: conv-4 + SiLU (+ L2 norm for q, k), gates, carried conv state.
 struct LayerFrontArgs {

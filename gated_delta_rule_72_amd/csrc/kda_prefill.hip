@@ -353,9 +353,10 @@ __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
   return x;
 }
 
-template <int D, bool BF16, bool PER_KEY, bool MAP, int NW>
+template <int D, bool BF16, bool PER_KEY, bool MAP, bool WU, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void prefill_kernel(PrefillArgs a) {
+  static_assert(!(MAP && WU), "the map pass forms W and U' itself");
   constexpr int NT = 64 * NW;    // threads
   using L = Lds<D>;
   using CR = ChunkRegs<D, BF16, PER_KEY, NT>;
@@ -382,7 +383,8 @@ void prefill_kernel(PrefillArgs a) {
   float* sG = reinterpret_cast<float*>(regA + L::A_G);
   _Float16* sRK = reinterpret_cast<_Float16*>(regA + L::A_RK);
   _Float16* sRQ = reinterpret_cast<_Float16*>(regA + L::A_RQ);
-  _Float16* sW = reinterpret_cast<_Float16*>(regA + L::A_W);
+  // WU: the stored W is loaded into the L buffer (no inverse is formed there)
+  _Float16* sW = reinterpret_cast<_Float16*>(WU ? smem + L::OFF_L : regA + L::A_W);
   _Float16* sTh = reinterpret_cast<_Float16*>(regA + L::A_TH);
   _Float16* sTl = reinterpret_cast<_Float16*>(regA + L::A_TL);
   _Float16* sVT = reinterpret_cast<_Float16*>(regA + L::A_VT);
@@ -391,25 +393,29 @@ void prefill_kernel(PrefillArgs a) {
   const int g = lane >> 4, l16 = lane & 15;
   const int item_idx = blockIdx.x / a.H, h = blockIdx.x % a.H;
   const PrefillItem item = a.items[item_idx];
-  if constexpr (MAP) {
+  if constexpr (MAP || WU) {
     // every segment of a split sequence: the maps of all but the last feed the
-    // scan, and each chunk's inverse is kept for pass 3
+    // scan, and each chunk's W and U' are kept for pass 3 (WU)
     if (item.n_segs <= 1) return;                // (uniform)
+  } else {
+    if (item.n_segs > 1) return;                 // split sequences run in WU
   }
   constexpr bool out_mode = !MAP;
   // MAP with bf16 inputs stages v rows in LDS as well (into the Q~ buffer,
   // which MAP never uses), so its prefetch holds no registers across P6
   constexpr bool v_in_lds = MAP && BF16;
-  constexpr bool v_in_regs = !v_in_lds;
-  // Pass 3 of a split sequence's segment: the map pass already formed
-  // each chunk's inverse (I + L)^-1 and stored it; it is loaded into the L
-  // buffer instead of being recomputed (same arithmetic, same bits).
-  static_assert(C * L::LDL * 4 == (int)kInverseBytes && kInverseBytes % 1024 == 0, "stored inverse layout");
-  constexpr int INV_KIB = (int)(kInverseBytes / 1024);
-  const bool have_inv = !MAP && a.seg_chunks > 0 && item.n_segs > 1;
-  float* inv_base = a.seg_chunks > 0
-                        ? a.seg_inverse + ((int64_t)item_idx * a.H + h) * a.seg_chunks * (int64_t)(kInverseBytes / 4)
-                        : nullptr;
+  constexpr bool v_in_regs = !v_in_lds && !WU;   // WU reads no v (U' is stored)
+  // Pass 3 of a split sequence's segment (WU): the map pass already formed each
+  // chunk's W and U' (P5) and stored them; they are loaded instead of being
+  // formed again from the inverse (same arithmetic, same bits). The stored W is
+  // the LDS image of the W buffer, 1 KiB per wavefront load.
+  constexpr int W_BYTES = (int)wu_w_bytes(D);
+  static_assert(W_BYTES == C * L::LDQ * 2 && W_BYTES % 1024 == 0 && W_BYTES <= C * L::LDL * 4,
+                "stored W layout");
+  constexpr int64_t WU_BYTES = (int64_t)wu_chunk_bytes(D);
+  unsigned char* wu_base = nullptr;
+  if constexpr (MAP || WU)
+    wu_base = static_cast<unsigned char*>(a.seg_wu) + ((int64_t)item_idx * a.H + h) * a.seg_chunks * WU_BYTES;
   const int64_t HD = (int64_t)a.H * D;
   const int64_t DD = (int64_t)D * D;
 
@@ -464,9 +470,8 @@ void prefill_kernel(PrefillArgs a) {
         stage_rows_lds<D, NW>(static_cast<const uint16_t*>(a.q) + row0, HDu, min(C, item.n_tokens),
                           regA + L::A_QSTAGE, wave, lane);
     }
-    if (have_inv) stage_block_lds<NW>(inv_base, INV_KIB, smem + L::OFF_L, wave, lane);
-    if (BF16 || have_inv) {
-      __builtin_amdgcn_s_waitcnt(0);   // staged rows and the inverse have landed in LDS
+    if constexpr (BF16) {
+      __builtin_amdgcn_s_waitcnt(0);   // staged rows have landed in LDS
       __syncthreads();
     }
   }
@@ -479,6 +484,19 @@ void prefill_kernel(PrefillArgs a) {
     int tid_c = tid;
     asm volatile("" : "+v"(tid_c));
     const int tid = tid_c, lane = tid_c % 64, g = lane >> 4, l16 = lane & 15;
+
+    // U' = T~ V for this wavefront's value slices (rows c in 4 tiles): formed in
+    // P5, or (WU) the stored one, fetched here with W and waited for after P3
+    f32x4 Up[SPW][4];
+    if constexpr (WU) {
+      const unsigned char* rec = wu_base + (int64_t)ch * WU_BYTES;
+      stage_block_lds<NW>(rec, W_BYTES / 1024, smem + L::OFF_L, wave, lane);
+      const f32x4* up = reinterpret_cast<const f32x4*>(rec + W_BYTES);
+#pragma unroll
+      for (int sl = 0; sl < SPW; ++sl)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) Up[sl][ct] = up[((SPW * wave + sl) * 4 + ct) * 64 + lane];
+    }
 
     // ---- P1: raw q, k (fp16), cumulative log2 decay, beta ---------------------
 #pragma unroll
@@ -573,7 +591,7 @@ void prefill_kernel(PrefillArgs a) {
         }
         const float kf = (float)kx[e];
         qt[e] = (_Float16)((float)qx[e] * dec);
-        sKhT[kk * L::LDT + swz(kk, c)] = (_Float16)(kf * dec);
+        if constexpr (!WU) sKhT[kk * L::LDT + swz(kk, c)] = (_Float16)(kf * dec);   // (W, P5)
         sKtT[kk * L::LDT + swz(kk, c)] = (_Float16)(kf * rem);
       }
       if constexpr (!MAP) *reinterpret_cast<f16x8*>(sQt + c * L::LDQ + 8 * k8) = qt;
@@ -610,7 +628,7 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks) {
               const f16x8 ki = ld_std(sRK, L::LDQ, 16 * I, 32 * ks, lane);
-              if (!have_inv) accL = mfma_f16(ki, kr[ks], accL);
+              if constexpr (!WU) accL = mfma_f16(ki, kr[ks], accL);
               if constexpr (!MAP) accB = mfma_f16(ki, qr[ks], accB);
             }
             const int i0 = 16 * I + 4 * g;           // columns i0..i0+3 of row r
@@ -623,9 +641,9 @@ void prefill_kernel(PrefillArgs a) {
               lv[e] = (i0 + e < r) ? accL[e] * f * br : 0.f;
               bv[e] = (_Float16)((i0 + e <= r) ? accB[e] * f : 0.f);
             }
-            if (!have_inv) *reinterpret_cast<f32x4*>(sL + r * L::LDL + i0) = lv;
+            if constexpr (!WU) *reinterpret_cast<f32x4*>(sL + r * L::LDL + i0) = lv;
             if constexpr (!MAP) *reinterpret_cast<f16x4*>(sB + r * L::LDT + i0) = bv;
-            if (I == R && !have_inv) {
+            if (!WU && I == R) {
               // diagonal tile: L_RR^T also into its upper triangle (column i
               // of L_RR becomes row i there); issued after the row stores, so
               // it lands after their zeros
@@ -662,7 +680,7 @@ void prefill_kernel(PrefillArgs a) {
                 qh[e] = (__bf16)qv; ql[e] = (__bf16)(qv - (float)qh[e]);
                 ih[e] = (__bf16)iv; il[e] = (__bf16)(iv - (float)ih[e]);
               }
-              if (!have_inv) {
+              if constexpr (!WU) {
                 accL = mfma_bf16(ih, kh, accL);
                 accL = mfma_bf16(ih, kl, accL);
                 accL = mfma_bf16(il, kh, accL);
@@ -681,9 +699,9 @@ void prefill_kernel(PrefillArgs a) {
               lv[e] = (i0 + e < r) ? accL[e] * br : 0.f;
               bv[e] = (_Float16)((i0 + e <= r) ? accB[e] : 0.f);
             }
-            if (!have_inv) *reinterpret_cast<f32x4*>(sL + r * L::LDL + i0) = lv;
+            if constexpr (!WU) *reinterpret_cast<f32x4*>(sL + r * L::LDL + i0) = lv;
             if constexpr (!MAP) *reinterpret_cast<f16x4*>(sB + r * L::LDT + i0) = bv;
-            if (I == R && !have_inv) {
+            if (!WU && I == R) {
               // diagonal tile: L_RR^T also into its upper triangle (column i
               // of L_RR becomes row i there); issued after the row stores, so
               // it lands after their zeros
@@ -695,7 +713,7 @@ void prefill_kernel(PrefillArgs a) {
         }
       }
       int d0, d1;
-      if (!have_inv && gram_diag<NW>(wave, d0, d1)) {
+      if (!WU && gram_diag<NW>(wave, d0, d1)) {
         // Replace L_bb by the inverse of the unit lower block I + L_bb for the
         // two diagonal blocks this wavefront computed: lane groups 0-1 take
         // block d0, 2-3 block d1, one column j per lane (groups 0 and 2
@@ -727,159 +745,167 @@ void prefill_kernel(PrefillArgs a) {
         }
       }
     }
+    if constexpr (WU) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): W in LDS, U' in registers
     __syncthreads();
 
-    // ---- P4: A = (I + L)^-1 -------------------------------------------------
-    // The diagonal blocks A_RR are in place (P3). Block column I of the
-    // off-diagonal part is one dependent chain on wavefront I (I = 0, 1, 2),
-    //   A_RI = -A_RR (L_RI A_II + sum_{I<m<R} L_Rm A_mI),   R = I+1 .. 3,
-    // on fp32 MFMA with the column's earlier blocks kept in accumulator
-    // registers; A_RI is stored at block (I, R). Meanwhile every wavefront
-    // stages V^T.
-    if (wave < 3 && !have_inv) {
-      const int I = wave;
-      f32x4 Acol[4];                                  // A_mI, m > I (accumulator layout)
+    if constexpr (!WU) {
+      // ---- P4: A = (I + L)^-1 -------------------------------------------------
+      // The diagonal blocks A_RR are in place (P3). Block column I of the
+      // off-diagonal part is one dependent chain on wavefront I (I = 0, 1, 2),
+      //   A_RI = -A_RR (L_RI A_II + sum_{I<m<R} L_Rm A_mI),   R = I+1 .. 3,
+      // on fp32 MFMA with the column's earlier blocks kept in accumulator
+      // registers; A_RI is stored at block (I, R). Meanwhile every wavefront
+      // stages V^T.
+      if (wave < 3) {
+        const int I = wave;
+        f32x4 Acol[4];                                  // A_mI, m > I (accumulator layout)
 #pragma unroll
-      for (int R = 1; R < 4; ++R) {
-        if (R > I) {
-          f32x4 acc = {0, 0, 0, 0};
-          // L_RI A_II, A_II read from LDS in the standard K order
+        for (int R = 1; R < 4; ++R) {
+          if (R > I) {
+            f32x4 acc = {0, 0, 0, 0};
+            // L_RI A_II, A_II read from LDS in the standard K order
 #pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const float av = sL[(16 * R + l16) * L::LDL + 16 * I + 4 * ks + g];
-            const float bv = sL[(16 * I + 4 * ks + g) * L::LDL + 16 * I + l16];
-            acc = mfma_f32(av, bv, acc);
-          }
-          // L_Rm A_mI for I < m < R, A_mI from registers (permuted K: k = 4g + ks)
+            for (int ks = 0; ks < 4; ++ks) {
+              const float av = sL[(16 * R + l16) * L::LDL + 16 * I + 4 * ks + g];
+              const float bv = sL[(16 * I + 4 * ks + g) * L::LDL + 16 * I + l16];
+              acc = mfma_f32(av, bv, acc);
+            }
+            // L_Rm A_mI for I < m < R, A_mI from registers (permuted K: k = 4g + ks)
 #pragma unroll
-          for (int m = 1; m < 3; ++m) {
-            if (m > I && m < R) {
+            for (int m = 1; m < 3; ++m) {
+              if (m > I && m < R) {
 #pragma unroll
-              for (int ks = 0; ks < 4; ++ks)
-                acc = mfma_f32(sL[(16 * R + l16) * L::LDL + 16 * m + 4 * g + ks], Acol[m][ks], acc);
+                for (int ks = 0; ks < 4; ++ks)
+                  acc = mfma_f32(sL[(16 * R + l16) * L::LDL + 16 * m + 4 * g + ks], Acol[m][ks], acc);
+              }
+            }
+            // -A_RR acc, acc as the permuted-K operand
+            f32x4 res = {0, 0, 0, 0};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+              res = mfma_f32(sL[(16 * R + l16) * L::LDL + 16 * R + 4 * g + ks], acc[ks], res);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              Acol[R][i] = -res[i];
+              sL[(16 * I + 4 * g + i) * L::LDL + 16 * R + l16] = -res[i];
             }
           }
-          // -A_RR acc, acc as the permuted-K operand
-          f32x4 res = {0, 0, 0, 0};
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks)
-            res = mfma_f32(sL[(16 * R + l16) * L::LDL + 16 * R + 4 * g + ks], acc[ks], res);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            Acol[R][i] = -res[i];
-            sL[(16 * I + 4 * g + i) * L::LDL + 16 * R + l16] = -res[i];
-          }
         }
       }
-    }
-    // V^T [v][c] into region A (G and raw q, k are dead after P3)
-    {
+      // V^T [v][c] into region A (G and raw q, k are dead after P3)
+      {
 #pragma unroll
-      for (int j = 0; j < CR::GPT; ++j) {
-        const int gi = tid + j * NT;
-        const int c = gi / (D / 8), k8 = gi % (D / 8);
-        float x[8];
-        if constexpr (v_in_lds) {
-          // staged bf16 rows [64][D] (unpadded); rows >= n are stale and zeroed here
-          const uint4 vw = *reinterpret_cast<const uint4*>(smem + L::OFF_QT + (c * D + 8 * k8) * 2);
-          const uint32_t vv4[4] = {vw.x, vw.y, vw.z, vw.w};
-          const bool live = c < n;
+        for (int j = 0; j < CR::GPT; ++j) {
+          const int gi = tid + j * NT;
+          const int c = gi / (D / 8), k8 = gi % (D / 8);
+          float x[8];
+          if constexpr (v_in_lds) {
+            // staged bf16 rows [64][D] (unpadded); rows >= n are stale and zeroed here
+            const uint4 vw = *reinterpret_cast<const uint4*>(smem + L::OFF_QT + (c * D + 8 * k8) * 2);
+            const uint32_t vv4[4] = {vw.x, vw.y, vw.z, vw.w};
+            const bool live = c < n;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            x[2 * e] = live ? bf16_bits_to_f32(vv4[e] & 0xFFFFu) : 0.f;
-            x[2 * e + 1] = live ? bf16_bits_to_f32(vv4[e] >> 16) : 0.f;
+            for (int e = 0; e < 4; ++e) {
+              x[2 * e] = live ? bf16_bits_to_f32(vv4[e] & 0xFFFFu) : 0.f;
+              x[2 * e + 1] = live ? bf16_bits_to_f32(vv4[e] >> 16) : 0.f;
+            }
+          } else {
+            unpack_group<BF16>(regs.v[j], x);
           }
-        } else {
-          unpack_group<BF16>(regs.v[j], x);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sVT[(8 * k8 + e) * L::LDT + swz(8 * k8 + e, c)] = (_Float16)x[e];
+        }
+      }
+      __syncthreads();
+
+      // ---- P5: T~ = A Diag(beta) as fp16 hi + lo; W = T~ (K * 2^G) ------------
+      for (int e8 = tid; e8 < C * C / 8; e8 += NT) {
+        const int c = e8 / 8, i0 = 8 * (e8 % 8);
+        const int Rb = c / 16, Ib = i0 / 16;
+        // A_RI (R > I) sits at block (I, R); diagonal blocks in place; zero above
+        const int src = (Rb > Ib) ? (16 * Ib + c % 16) * L::LDL + 16 * Rb + i0 % 16 : c * L::LDL + i0;
+        const float keep = (Rb >= Ib) ? 1.f : 0.f;
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(sL + src);
+        const f32x4 a1 = *reinterpret_cast<const f32x4*>(sL + src + 4);
+        const f32x4 b0 = *reinterpret_cast<const f32x4*>(sBeta + i0);
+        const f32x4 b1 = *reinterpret_cast<const f32x4*>(sBeta + i0 + 4);
+        f16x8 th, tl;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float tv = keep * (e < 4 ? a0[e] * b0[e] : a1[e - 4] * b1[e - 4]);
+          th[e] = (_Float16)tv;
+          tl[e] = (_Float16)(tv - (float)th[e]);
+        }
+        *reinterpret_cast<f16x8*>(sTh + c * L::LDT + i0) = th;
+        *reinterpret_cast<f16x8*>(sTl + c * L::LDT + i0) = tl;
+      }
+      __syncthreads();
+      // W[:, 16kt..16kt+15] for kt = wave, wave + NW, ... and U' = T~ V for the
+      // wavefront's own value slices (K = 64), sharing each T~ hi/lo tile read;
+      // U' stays in registers for P6.
+      {
+        f32x4 acc[KT / NW][4];
+#pragma unroll
+        for (int kj = 0; kj < KT / NW; ++kj)
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) acc[kj][ct] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int sl = 0; sl < SPW; ++sl)
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) Up[sl][ct] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          f16x8 th[4], tl[4], bk[KT / NW], bv[SPW];
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) {
+            th[ct] = ld_std(sTh, L::LDT, 16 * ct, 32 * ks, lane);
+            tl[ct] = ld_std(sTl, L::LDT, 16 * ct, 32 * ks, lane);
+          }
+#pragma unroll
+          for (int kj = 0; kj < KT / NW; ++kj) bk[kj] = ld_std_swz(sKhT, L::LDT, 16 * (wave + NW * kj), 32 * ks, lane);
+#pragma unroll
+          for (int sl = 0; sl < SPW; ++sl) bv[sl] = ld_std_swz(sVT, L::LDT, 16 * (SPW * wave + sl), 32 * ks, lane);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) {
+#pragma unroll
+            for (int kj = 0; kj < KT / NW; ++kj) {
+              acc[kj][ct] = mfma_f16(th[ct], bk[kj], acc[kj][ct]);
+              acc[kj][ct] = mfma_f16(tl[ct], bk[kj], acc[kj][ct]);
+            }
+#pragma unroll
+            for (int sl = 0; sl < SPW; ++sl) {
+              Up[sl][ct] = mfma_f16(th[ct], bv[sl], Up[sl][ct]);
+              Up[sl][ct] = mfma_f16(tl[ct], bv[sl], Up[sl][ct]);
+            }
+          }
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sVT[(8 * k8 + e) * L::LDT + swz(8 * k8 + e, c)] = (_Float16)x[e];
+        for (int kj = 0; kj < KT / NW; ++kj)
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              sW[(16 * ct + 4 * g + i) * L::LDQ + 16 * (wave + NW * kj) + l16] = (_Float16)acc[kj][ct][i];
       }
-    }
-    __syncthreads();
+      __syncthreads();
+    }  // !WU: P4, P5
 
     if constexpr (MAP) {
-      // keep this chunk's inverse for pass 3 (the L buffer as laid out above)
-      float* dst = inv_base + (int64_t)ch * (int64_t)(kInverseBytes / 4);
-      for (int e = tid; e < (int)(kInverseBytes / 16); e += NT)
-        *reinterpret_cast<f32x4*>(dst + 4 * e) = *reinterpret_cast<const f32x4*>(sL + 4 * e);
-    }
-
-    // ---- P5: T~ = A Diag(beta) as fp16 hi + lo; W = T~ (K * 2^G) ------------
-    for (int e8 = tid; e8 < C * C / 8; e8 += NT) {
-      const int c = e8 / 8, i0 = 8 * (e8 % 8);
-      const int Rb = c / 16, Ib = i0 / 16;
-      // A_RI (R > I) sits at block (I, R); diagonal blocks in place; zero above
-      const int src = (Rb > Ib) ? (16 * Ib + c % 16) * L::LDL + 16 * Rb + i0 % 16 : c * L::LDL + i0;
-      const float keep = (Rb >= Ib) ? 1.f : 0.f;
-      const f32x4 a0 = *reinterpret_cast<const f32x4*>(sL + src);
-      const f32x4 a1 = *reinterpret_cast<const f32x4*>(sL + src + 4);
-      const f32x4 b0 = *reinterpret_cast<const f32x4*>(sBeta + i0);
-      const f32x4 b1 = *reinterpret_cast<const f32x4*>(sBeta + i0 + 4);
-      f16x8 th, tl;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float tv = keep * (e < 4 ? a0[e] * b0[e] : a1[e - 4] * b1[e - 4]);
-        th[e] = (_Float16)tv;
-        tl[e] = (_Float16)(tv - (float)th[e]);
-      }
-      *reinterpret_cast<f16x8*>(sTh + c * L::LDT + i0) = th;
-      *reinterpret_cast<f16x8*>(sTl + c * L::LDT + i0) = tl;
-    }
-    __syncthreads();
-    // W[:, 16kt..16kt+15] for kt = wave, wave + NW, ... and U' = T~ V for the
-    // wavefront's own value slices (K = 64), sharing each T~ hi/lo tile read;
-    // U' stays in registers for P6.
-    f32x4 Up[SPW][4];
-    {
-      f32x4 acc[KT / NW][4];
-#pragma unroll
-      for (int kj = 0; kj < KT / NW; ++kj)
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) acc[kj][ct] = f32x4{0, 0, 0, 0};
+      // keep this chunk's W (the LDS image) and U' (one tile per lane) for pass 3
+      unsigned char* rec = wu_base + (int64_t)ch * WU_BYTES;
+      const unsigned char* wsrc = reinterpret_cast<const unsigned char*>(sW);
+      for (int e = tid; e < W_BYTES / 16; e += NT)
+        *reinterpret_cast<f32x4*>(rec + 16 * e) = *reinterpret_cast<const f32x4*>(wsrc + 16 * e);
+      f32x4* up = reinterpret_cast<f32x4*>(rec + W_BYTES);
 #pragma unroll
       for (int sl = 0; sl < SPW; ++sl)
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) Up[sl][ct] = f32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        f16x8 th[4], tl[4], bk[KT / NW], bv[SPW];
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          th[ct] = ld_std(sTh, L::LDT, 16 * ct, 32 * ks, lane);
-          tl[ct] = ld_std(sTl, L::LDT, 16 * ct, 32 * ks, lane);
-        }
-#pragma unroll
-        for (int kj = 0; kj < KT / NW; ++kj) bk[kj] = ld_std_swz(sKhT, L::LDT, 16 * (wave + NW * kj), 32 * ks, lane);
-#pragma unroll
-        for (int sl = 0; sl < SPW; ++sl) bv[sl] = ld_std_swz(sVT, L::LDT, 16 * (SPW * wave + sl), 32 * ks, lane);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-#pragma unroll
-          for (int kj = 0; kj < KT / NW; ++kj) {
-            acc[kj][ct] = mfma_f16(th[ct], bk[kj], acc[kj][ct]);
-            acc[kj][ct] = mfma_f16(tl[ct], bk[kj], acc[kj][ct]);
-          }
-#pragma unroll
-          for (int sl = 0; sl < SPW; ++sl) {
-            Up[sl][ct] = mfma_f16(th[ct], bv[sl], Up[sl][ct]);
-            Up[sl][ct] = mfma_f16(tl[ct], bv[sl], Up[sl][ct]);
-          }
-        }
-      }
-#pragma unroll
-      for (int kj = 0; kj < KT / NW; ++kj)
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            sW[(16 * ct + 4 * g + i) * L::LDQ + 16 * (wave + NW * kj) + l16] = (_Float16)acc[kj][ct][i];
+        for (int ct = 0; ct < 4; ++ct) up[((SPW * wave + sl) * 4 + ct) * 64 + lane] = Up[sl][ct];
     }
-    __syncthreads();
 
     // prefetch the next chunk's raw inputs while the chain runs (bf16 q, k go
-    // to LDS: the K^T and L buffers are not read again in this chunk)
+    // to LDS: the K^T buffer is not read again in this chunk)
     if (ch + 1 < n_chunks) {
       const int n_next = min(C, item.n_tokens - (ch + 1) * C);
       load_chunk<D, BF16, PER_KEY, NT>(regs, a, tok0 + C, n_next, h, tid, v_in_regs);
@@ -894,10 +920,6 @@ void prefill_kernel(PrefillArgs a) {
           stage_rows_lds<D, NW>(static_cast<const uint16_t*>(a.q) + row0, HDu, n_next, regA + L::A_QSTAGE,
                             wave, lane);
       }
-      // the L buffer is dead until the next chunk's P5
-      if (have_inv)
-        stage_block_lds<NW>(inv_base + (int64_t)(ch + 1) * (int64_t)(kInverseBytes / 4), INV_KIB, smem + L::OFF_L,
-                            wave, lane);
     }
 
     // ---- P6: state passing for this wavefront's slices ---------------------
@@ -1013,7 +1035,7 @@ void prefill_kernel(PrefillArgs a) {
             *reinterpret_cast<f32x4*>(dst + (16 * (SPW * wave + sl) + l16) * D + 16 * kt + 4 * g) = ST[sl][kt];
       }
     }
-    if (BF16 || have_inv) __builtin_amdgcn_s_waitcnt(0);   // staged rows (and inverse) have landed in LDS
+    if constexpr (BF16) __builtin_amdgcn_s_waitcnt(0);   // staged rows have landed in LDS
     __syncthreads();
   }
 
@@ -1172,12 +1194,12 @@ __global__ __launch_bounds__(256) void build_items_kernel(PrefillArgs a) {
   }
 }
 
-template <int D, bool BF16, bool PK, bool MAP>
+template <int D, bool BF16, bool PK, bool MAP, bool WU>
 hipError_t launch_pass(const PrefillArgs& a, hipStream_t s) {
   using L = Lds<D>;
   static_assert(L::TOTAL <= 160 * 1024, "LDS budget");
   constexpr int NT = 64 * waves_for<D>();
-  auto kern = prefill_kernel<D, BF16, PK, MAP, waves_for<D>()>;
+  auto kern = prefill_kernel<D, BF16, PK, MAP, WU, waves_for<D>()>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL);
   if (e != hipSuccess) return e;
@@ -1187,8 +1209,8 @@ hipError_t launch_pass(const PrefillArgs& a, hipStream_t s) {
 
 template <int D, bool BF16, bool PK>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
-  if (a.seg_chunks == 0) return launch_pass<D, BF16, PK, false>(a, s);
-  hipError_t e = launch_pass<D, BF16, PK, true>(a, s);          // pass 1: segment maps, inverses
+  if (a.seg_chunks == 0) return launch_pass<D, BF16, PK, false, false>(a, s);
+  hipError_t e = launch_pass<D, BF16, PK, true, false>(a, s);   // pass 1: segment maps, W and U' per chunk
   if (e != hipSuccess) return e;
   constexpr int scan_lds = (D * D + 16 * D) * 4;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(segment_scan_kernel<D>),
@@ -1197,7 +1219,9 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(segment_scan_kernel<D>, dim3(a.num_seqs * a.H * (D / 16)), dim3(256), scan_lds, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_pass<D, BF16, PK, false>(a, s);                 // pass 3: every segment
+  e = launch_pass<D, BF16, PK, false, true>(a, s);              // pass 3: every segment
+  if (e != hipSuccess || !a.any_whole) return e;
+  return launch_pass<D, BF16, PK, false, false>(a, s);          // sequences that are not split
 }
 
 }  // namespace
