@@ -296,7 +296,7 @@ int kda_prefill_chunked(const kda_shape* shape, int32_t num_seqs,
     return fail(KDA_ERR_ARG, "snapshots is NULL but %lld snapshot slots are due", (long long)n_snap);
   const uintptr_t a_alpha = shape->gate == KDA_GATE_PER_KEY ? 16 : 4;
   const PtrReq reqs[] = {{q, 16, "q"}, {k, 16, "k"}, {v, 16, "v"}, {alpha, a_alpha, "alpha"},
-                         {beta, 4, "beta"}, {initial_state, 16, "initial_state"}, {o, 4, "o"},
+                         {beta, 4, "beta"}, {initial_state, 16, "initial_state"}, {o, 16, "o"},
                          {final_state, 16, "final_state"},
                          {n_snap > 0 ? snapshots : nullptr, 16, "snapshots"},
                          {cu_seqlens_dev, 8, "cu_seqlens_dev"}, {workspace, 16, "workspace"}};

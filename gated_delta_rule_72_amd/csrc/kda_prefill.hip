@@ -486,11 +486,20 @@ void prefill_kernel(PrefillArgs a) {
     const int tid = tid_c, lane = tid_c % 64, g = lane >> 4, l16 = lane & 15;
 
     // U' = T~ V for this wavefront's value slices (rows c in 4 tiles): formed in
-    // P5, or (WU) the stored one, fetched here with W and waited for after P3
+    // P5, or (WU) the stored one, fetched here with W. W goes through registers
+    // and is written to LDS after P3: an LDS-bound load issued here would make
+    // the LDS reads of P1-P3 wait for it.
     f32x4 Up[SPW][4];
+    constexpr int W_VEC = W_BYTES / 16;               // 16-byte pieces of W
+    constexpr int W_PER_T = (W_VEC + NT - 1) / NT;
+    f32x4 wreg[WU ? W_PER_T : 1];
     if constexpr (WU) {
       const unsigned char* rec = wu_base + (int64_t)ch * WU_BYTES;
-      stage_block_lds<NW>(rec, W_BYTES / 1024, smem + L::OFF_L, wave, lane);
+#pragma unroll
+      for (int j = 0; j < W_PER_T; ++j) {
+        const int e = tid + j * NT;
+        if (e < W_VEC) wreg[j] = reinterpret_cast<const f32x4*>(rec)[e];
+      }
       const f32x4* up = reinterpret_cast<const f32x4*>(rec + W_BYTES);
 #pragma unroll
       for (int sl = 0; sl < SPW; ++sl)
@@ -745,7 +754,13 @@ void prefill_kernel(PrefillArgs a) {
         }
       }
     }
-    if constexpr (WU) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): W in LDS, U' in registers
+    if constexpr (WU) {
+#pragma unroll
+      for (int j = 0; j < W_PER_T; ++j) {
+        const int e = tid + j * NT;
+        if (e < W_VEC) reinterpret_cast<f32x4*>(sW)[e] = wreg[j];
+      }
+    }
     __syncthreads();
 
     if constexpr (!WU) {
@@ -891,18 +906,10 @@ void prefill_kernel(PrefillArgs a) {
       __syncthreads();
     }  // !WU: P4, P5
 
-    if constexpr (MAP) {
-      // keep this chunk's W (the LDS image) and U' (one tile per lane) for pass 3
-      unsigned char* rec = wu_base + (int64_t)ch * WU_BYTES;
-      const unsigned char* wsrc = reinterpret_cast<const unsigned char*>(sW);
-      for (int e = tid; e < W_BYTES / 16; e += NT)
-        *reinterpret_cast<f32x4*>(rec + 16 * e) = *reinterpret_cast<const f32x4*>(wsrc + 16 * e);
-      f32x4* up = reinterpret_cast<f32x4*>(rec + W_BYTES);
-#pragma unroll
-      for (int sl = 0; sl < SPW; ++sl)
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) up[((SPW * wave + sl) * 4 + ct) * 64 + lane] = Up[sl][ct];
-    }
+
+    // WU: U' (fetched at the chunk start) has long arrived; waiting for it here
+    // keeps the compiler from waiting for the prefetch below before P6 uses U'
+    if constexpr (WU) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
     // prefetch the next chunk's raw inputs while the chain runs (bf16 q, k go
     // to LDS: the K^T buffer is not read again in this chunk)
@@ -920,6 +927,20 @@ void prefill_kernel(PrefillArgs a) {
           stage_rows_lds<D, NW>(static_cast<const uint16_t*>(a.q) + row0, HDu, n_next, regA + L::A_QSTAGE,
                             wave, lane);
       }
+    }
+
+    if constexpr (MAP) {
+      // keep this chunk's W (the LDS image) and U' (one tile per lane) for pass 3;
+      // issued after the prefetch, so the stores drain while the chains run
+      unsigned char* rec = wu_base + (int64_t)ch * WU_BYTES;
+      const unsigned char* wsrc = reinterpret_cast<const unsigned char*>(sW);
+      for (int e = tid; e < W_BYTES / 16; e += NT)
+        *reinterpret_cast<f32x4*>(rec + 16 * e) = *reinterpret_cast<const f32x4*>(wsrc + 16 * e);
+      f32x4* up = reinterpret_cast<f32x4*>(rec + W_BYTES);
+#pragma unroll
+      for (int sl = 0; sl < SPW; ++sl)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) up[((SPW * wave + sl) * 4 + ct) * 64 + lane] = Up[sl][ct];
     }
 
     // ---- P6: state passing for this wavefront's slices ---------------------
@@ -949,7 +970,7 @@ void prefill_kernel(PrefillArgs a) {
         for (int ct = 0; ct < 4; ++ct) w[ct] = ld_perm(sW, L::LDQ, 16 * ct, 32 * ks, lane);
 #pragma unroll
         for (int sl = 0; sl < NSL; ++sl) nsop[sl] = -sop[sl][ks];
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!WU) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
@@ -962,8 +983,11 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) split_perm(U[sl][2 * ks], U[sl][2 * ks + 1], uh[sl][ks], ul[sl][ks]);
       if constexpr (out_mode) {
-        // O = Q~ S0^T + B U, one 16-row tile at a time
-        const uint32_t olane = (uint32_t)(4 * g) * (uint32_t)HD + 16 * SPW * wave + l16;
+        // O^T = S0 Q~^T + U^T B^T, one 16-token tile at a time. MFMA's A and B
+        // operands share one lane layout, so the S0^T and U operands above serve
+        // as A and the Q~ and B tiles as B: lane (g, l16) then holds
+        // O[token 16ct + l16][values 16 slice + 4g .. +3], one 16-byte store.
+        const int64_t obase = tok0 * HD + (int64_t)h * D + 16 * SPW * wave + 4 * g;
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
           f16x8 qa[D / 32], ba[2];
@@ -971,29 +995,26 @@ void prefill_kernel(PrefillArgs a) {
           for (int ks = 0; ks < D / 32; ++ks) qa[ks] = ld_perm(sQt, L::LDQ, 16 * ct, 32 * ks, lane);
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) ba[ks] = ld_perm(sB, L::LDT, 16 * ct, 32 * ks, lane);
-          __builtin_amdgcn_sched_barrier(0);
-          f32x4 O[SPW];
+          if constexpr (!WU) __builtin_amdgcn_sched_barrier(0);
+          f32x4 OT[SPW];
 #pragma unroll
-          for (int sl = 0; sl < SPW; ++sl) O[sl] = f32x4{0, 0, 0, 0};
+          for (int sl = 0; sl < SPW; ++sl) OT[sl] = f32x4{0, 0, 0, 0};
 #pragma unroll
           for (int ks = 0; ks < D / 32; ++ks)
 #pragma unroll
-            for (int sl = 0; sl < SPW; ++sl) O[sl] = mfma_f16(qa[ks], sop[sl][ks], O[sl]);
+            for (int sl = 0; sl < SPW; ++sl) OT[sl] = mfma_f16(sop[sl][ks], qa[ks], OT[sl]);
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
             for (int sl = 0; sl < SPW; ++sl) {
-              O[sl] = mfma_f16(ba[ks], uh[sl][ks], O[sl]);
-              O[sl] = mfma_f16(ba[ks], ul[sl][ks], O[sl]);
+              OT[sl] = mfma_f16(uh[sl][ks], ba[ks], OT[sl]);
+              OT[sl] = mfma_f16(ul[sl][ks], ba[ks], OT[sl]);
             }
+          const int c = 16 * ct + l16;                 // this lane's token in the chunk
+          if (c < n) {
+            float* orow = a.o + obase + (int64_t)c * HD;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int c = 16 * ct + 4 * g + i;
-            float* ob = a.o + (tok0 + 16 * ct + i) * HD + (int64_t)h * D;   // uniform
-            if (c < n) {
-#pragma unroll
-              for (int sl = 0; sl < SPW; ++sl) ob[olane + 16 * sl] = O[sl][i];
-            }
+            for (int sl = 0; sl < SPW; ++sl) *reinterpret_cast<f32x4*>(orow + 16 * sl) = OT[sl];
           }
         }
       }
@@ -1005,7 +1026,7 @@ void prefill_kernel(PrefillArgs a) {
         for (int t = 0; t < 4; ++t)
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks) ka[t][ks] = ld_perm_swz(sKtT, L::LDT, 16 * (kb + t), 32 * ks, lane);
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (!WU) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const f32x4 gam = *reinterpret_cast<const f32x4*>(sGam + 16 * (kb + t) + 4 * g);

@@ -23,9 +23,10 @@
  *     values in (0, 1]. beta: fp32 [T, H] in [0, 1]. States are fp32
  *     [.., H, d_v, d_k] (d_k contiguous). o is fp32 [T, H, d_v].
  *   - Supported: d_k = d_v in {64, 128}; chunk = 64.
- *   - Alignment: q, k, v, per-key alpha and every state 16 bytes (8 bytes
- *     for bf16 q, k in kda_decode_step); scalar alpha, beta and o 4 bytes;
- *     cu_seqlens_dev 8 bytes; workspace 16 bytes. Otherwise KDA_ERR_ALIGN.
+ *   - Alignment: q, k, v, per-key alpha, every state and the prefill's o
+ *     16 bytes (8 bytes for bf16 q, k in kda_decode_step); scalar alpha,
+ *     beta and the decode steps' o 4 bytes; cu_seqlens_dev 8 bytes;
+ *     workspace 16 bytes. Otherwise KDA_ERR_ALIGN.
  *   - All compute entry points are asynchronous on the caller's hipStream_t
  *     (passed as void*, NULL = default stream).
  *   - Errors: negative status codes are detected on the host before anything

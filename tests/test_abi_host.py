@@ -153,6 +153,8 @@ def test_prefill_host_rejections(K):
     assert "q" in K.kda_last_error()
     assert _prefill_raw(K, sh, cu, {"alpha": 0x50004}, need) == K.KDA_ERR_ALIGN   # per-key: 16 B
     assert _prefill_raw(K, sh, cu, {"fin": 0x80004}, need) == K.KDA_ERR_ALIGN
+    assert _prefill_raw(K, sh, cu, {"o": 0x70004}, need) == K.KDA_ERR_ALIGN       # o: 16 B (row stores)
+    assert "o" in K.kda_last_error()
     assert _prefill_raw(K, sh, cu, {"q": None}, need) == K.KDA_ERR_ARG
     assert _prefill_raw(K, sh, cu, {"fin": None}, need) == K.KDA_ERR_ARG
     assert _prefill_raw(K, sh, cu, {"cu_dev": None}, need) == K.KDA_ERR_ARG
