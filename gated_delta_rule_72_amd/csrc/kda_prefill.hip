@@ -39,18 +39,20 @@
 //       fp32 MFMA products per block column; V^T staged in LDS.
 //   P5  T~ = (I + L)^-1 Diag(beta) split into fp16 hi + lo; W = T~ (K*2^G)
 //       and U' = T~ V on MFMA from the same T~ tiles.
-//   P6  per slice: U = U' - W S0^T, O = Q~ S0^T + B U,
+//   P6  per slice: U = U' - W S0^T, O^T = S0 Q~^T + U^T B^T (a lane then
+//       holds four consecutive values of one token),
 //       S0^T <- 2^(G_n) S0^T + (K*2^(G_n-G))^T U. U enters its products as
 //       fp16 hi + lo; the state stays fp32. The next chunk's inputs are
 //       fetched (q, k rows straight into LDS) while P6 runs.
-// Two instantiations: OUT (the real chain: o, snapshots, final state) and MAP
+// Three instantiations: OUT (the real chain: o, snapshots, final state), MAP
 // (a segment's affine map: each wavefront advances its N rows, the chain from
 // S0 = 0, and its M rows, the chain with v = 0 from identity rows, side by side;
-// q, Q~, B and o are skipped). Long sequences with few heads are split into
-// segments: pass 1 maps every segment (and keeps each chunk's inverse from
-// P3-P4), a scan composes S_{s+1} = S_s M_s + N_s in fp32 from the initial
-// state, and pass 3 runs every segment in OUT mode from its true start,
-// loading the stored inverses instead of forming L and inverting it again.
+// q, Q~, B and o are skipped) and WU (OUT for the segments of a split sequence).
+// Long sequences with few heads are split into segments: pass 1 maps every
+// segment and keeps each chunk's W and U' (the products of P5), a scan composes
+// S_{s+1} = S_s M_s + N_s in fp32 from the initial state, and pass 3 (WU) runs
+// every segment from its true start, loading W and U' instead of forming L,
+// the inverse and P5 again; whole sequences of the same call run in OUT.
 // Accumulator layout of a 16x16 MFMA tile: lane l holds rows 4(l/16)+i,
 // column l%16. When an accumulator tile feeds the next product as its
 // K-operand, the K index is permuted (lane group g supplies rows 4g..4g+3 of
