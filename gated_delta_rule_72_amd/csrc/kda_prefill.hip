@@ -1089,13 +1089,21 @@ void prefill_kernel(PrefillArgs a) {
 // Segment scan: for every segmented sequence, head and block of 16 state rows,
 // S_{s+1} = S_s M_s + N_s for s = 0 .. n_segs-2 in fp32, from S_0 = the initial
 // state (or zeros); S_s is stored as the start state of segment s (S_0
-// included). Rows of S evolve independently.
+// included). Rows of S evolve independently. Four wavefronts; wavefront w forms
+// output columns [w D/4, (w+1) D/4) as 16x16 fp32 MFMA tiles (K = D in steps
+// of 4), with S_s as the A operand and M_s as the B operand, both from LDS: M
+// rows padded to D + 16 floats and S rows to D + 4, so that the four k rows
+// and the sixteen state rows a K-step reads fall on distinct banks. M_{s+1}
+// and N_{s+1} are fetched into registers while step s runs.
 template <int D>
 __global__ __launch_bounds__(256) void segment_scan_kernel(PrefillArgs a) {
   constexpr int RB = 16;                        // rows per workgroup
+  constexpr int LDM = D + 16, LDSS = D + 4;     // LDS row strides (floats) of M and S
+  constexpr int TPW = D / 64;                   // 16-column output tiles per wavefront
+  constexpr int MV = D * D / 4 / 256;           // 16-byte pieces of M per thread
   extern __shared__ __align__(16) unsigned char smem[];
-  float* sM = reinterpret_cast<float*>(smem);   // [D][D]
-  float* sS = sM + D * D;                       // [RB][D]
+  float* sM = reinterpret_cast<float*>(smem);   // [D][LDM]
+  float* sS = sM + D * LDM;                     // [RB][LDSS]
   const int nrb = D / RB;
   const int n = blockIdx.x / (a.H * nrb);
   const int rem = blockIdx.x % (a.H * nrb);
@@ -1104,39 +1112,68 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(PrefillArgs a) {
   const int ns = a.items[first].n_segs;
   if (ns <= 1) return;
   const int64_t DD = (int64_t)D * D;
-  const int tid = threadIdx.x;
-  const int r = tid / 16, c0 = tid % 16;        // output row r, columns c0 + 16 j
+  const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, g = lane >> 4, l16 = lane & 15;
   {
     const float* S0 = a.init ? a.init + ((int64_t)n * a.H + h) * DD + (int64_t)rb * RB * D : nullptr;
     float* out0 = a.seg_states + ((int64_t)first * a.H + h) * DD + (int64_t)rb * RB * D;
     for (int e = tid; e < RB * D; e += 256) {
       const float x = S0 ? S0[e] : 0.f;
-      sS[e] = x;
+      sS[(e / D) * LDSS + e % D] = x;
       out0[e] = x;
     }
   }
-  for (int s = 0; s <= ns - 2; ++s) {
-    const float* M = a.seg_maps + ((int64_t)(first + s) * a.H + h) * 2 * DD;
+  // M_s (all D x D) and this block's rows of N_s in the accumulator layout:
+  // lane (g, l16) of wavefront w holds rows 4g + i, column w D/4 + 16t + l16
+  f32x4 mreg[MV], nreg[TPW];
+  auto fetch = [&](int seg) {
+    const float* M = a.seg_maps + ((int64_t)(first + seg) * a.H + h) * 2 * DD;
+#pragma unroll
+    for (int j = 0; j < MV; ++j) mreg[j] = reinterpret_cast<const f32x4*>(M)[tid + 256 * j];
     const float* Nm = M + DD + (int64_t)rb * RB * D;
-    __syncthreads();
-    for (int e = 4 * tid; e < D * D; e += 4 * 256)
-      *reinterpret_cast<f32x4*>(sM + e) = *reinterpret_cast<const f32x4*>(M + e);
-    __syncthreads();
-    float acc[D / 16];
 #pragma unroll
-    for (int j = 0; j < D / 16; ++j) acc[j] = Nm[r * D + c0 + 16 * j];
-    for (int k = 0; k < D; ++k) {
-      const float sv = sS[r * D + k];
+    for (int t = 0; t < TPW; ++t)
 #pragma unroll
-      for (int j = 0; j < D / 16; ++j) acc[j] += sv * sM[k * D + c0 + 16 * j];
+      for (int i = 0; i < 4; ++i) nreg[t][i] = Nm[(4 * g + i) * D + (D / 4) * wave + 16 * t + l16];
+  };
+  auto put_M = [&]() {
+#pragma unroll
+    for (int j = 0; j < MV; ++j) {
+      const int e = 4 * (tid + 256 * j);          // element (e / D, e % D) of M
+      *reinterpret_cast<f32x4*>(sM + (e / D) * LDM + e % D) = mreg[j];
     }
-    __syncthreads();
+  };
+  fetch(0);
+  put_M();
+  __syncthreads();
+  for (int s = 0; s <= ns - 2; ++s) {
+    f32x4 nadd[TPW];                              // N_s, added after the products
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) nadd[t] = nreg[t];
+    if (s + 1 <= ns - 2) fetch(s + 1);            // in flight during this step
+    f32x4 acc[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) acc[t] = f32x4{0, 0, 0, 0};
+#pragma unroll 8
+    for (int ks = 0; ks < D / 4; ++ks) {
+      const float av = sS[l16 * LDSS + 4 * ks + g];
+#pragma unroll
+      for (int t = 0; t < TPW; ++t)
+        acc[t] = mfma_f32(av, sM[(4 * ks + g) * LDM + (D / 4) * wave + 16 * t + l16], acc[t]);
+    }
+    __syncthreads();                              // every wavefront is done with S_s and M_s
     float* out = a.seg_states + ((int64_t)(first + s + 1) * a.H + h) * DD + (int64_t)rb * RB * D;
 #pragma unroll
-    for (int j = 0; j < D / 16; ++j) {
-      sS[r * D + c0 + 16 * j] = acc[j];
-      out[r * D + c0 + 16 * j] = acc[j];
+    for (int t = 0; t < TPW; ++t) {
+      const int col = (D / 4) * wave + 16 * t + l16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x = acc[t][i] + nadd[t][i];
+        sS[(4 * g + i) * LDSS + col] = x;
+        out[(4 * g + i) * D + col] = x;
+      }
     }
+    if (s + 1 <= ns - 2) put_M();
+    __syncthreads();
   }
 }
 
@@ -1235,7 +1272,7 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
   if (a.seg_chunks == 0) return launch_pass<D, BF16, PK, false, false>(a, s);
   hipError_t e = launch_pass<D, BF16, PK, true, false>(a, s);   // pass 1: segment maps, W and U' per chunk
   if (e != hipSuccess) return e;
-  constexpr int scan_lds = (D * D + 16 * D) * 4;
+  constexpr int scan_lds = (D * (D + 16) + 16 * (D + 4)) * 4;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(segment_scan_kernel<D>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, scan_lds);
   if (e != hipSuccess) return e;
