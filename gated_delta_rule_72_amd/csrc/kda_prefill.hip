@@ -859,7 +859,8 @@ void prefill_kernel(PrefillArgs a) {
       __syncthreads();
       // W[:, 16kt..16kt+15] for kt = wave, wave + NW, ... and U' = T~ V for the
       // wavefront's own value slices (K = 64), sharing each T~ hi/lo tile read;
-      // U' stays in registers for P6.
+      // U' stays in registers for P6. W is formed transposed (K^T as the A
+      // operand), so a lane holds four consecutive columns of one row of W.
       {
         f32x4 acc[KT / NW][4];
 #pragma unroll
@@ -887,8 +888,8 @@ void prefill_kernel(PrefillArgs a) {
           for (int ct = 0; ct < 4; ++ct) {
 #pragma unroll
             for (int kj = 0; kj < KT / NW; ++kj) {
-              acc[kj][ct] = mfma_f16(th[ct], bk[kj], acc[kj][ct]);
-              acc[kj][ct] = mfma_f16(tl[ct], bk[kj], acc[kj][ct]);
+              acc[kj][ct] = mfma_f16(bk[kj], th[ct], acc[kj][ct]);
+              acc[kj][ct] = mfma_f16(bk[kj], tl[ct], acc[kj][ct]);
             }
 #pragma unroll
             for (int sl = 0; sl < SPW; ++sl) {
@@ -897,13 +898,19 @@ void prefill_kernel(PrefillArgs a) {
             }
           }
         }
+        // lane (g, l16): W[16ct + l16][16kt + 4g .. +3], one 8-byte write per
+        // tile; the map pass keeps this chunk's W (the LDS image) from here too
 #pragma unroll
         for (int kj = 0; kj < KT / NW; ++kj)
 #pragma unroll
-          for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              sW[(16 * ct + 4 * g + i) * L::LDQ + 16 * (wave + NW * kj) + l16] = (_Float16)acc[kj][ct][i];
+          for (int ct = 0; ct < 4; ++ct) {
+            const f16x4 w4 = {(_Float16)acc[kj][ct][0], (_Float16)acc[kj][ct][1], (_Float16)acc[kj][ct][2],
+                              (_Float16)acc[kj][ct][3]};
+            const int off = (16 * ct + l16) * L::LDQ + 16 * (wave + NW * kj) + 4 * g;
+            *reinterpret_cast<f16x4*>(sW + off) = w4;
+            if constexpr (MAP)
+              *reinterpret_cast<f16x4*>(wu_base + (int64_t)ch * WU_BYTES + 2 * off) = w4;
+          }
       }
       __syncthreads();
     }  // !WU: P4, P5
@@ -932,12 +939,9 @@ void prefill_kernel(PrefillArgs a) {
     }
 
     if constexpr (MAP) {
-      // keep this chunk's W (the LDS image) and U' (one tile per lane) for pass 3;
+      // keep this chunk's U' (one tile per lane) for pass 3 (W was kept in P5);
       // issued after the prefetch, so the stores drain while the chains run
       unsigned char* rec = wu_base + (int64_t)ch * WU_BYTES;
-      const unsigned char* wsrc = reinterpret_cast<const unsigned char*>(sW);
-      for (int e = tid; e < W_BYTES / 16; e += NT)
-        *reinterpret_cast<f32x4*>(rec + 16 * e) = *reinterpret_cast<const f32x4*>(wsrc + 16 * e);
       f32x4* up = reinterpret_cast<f32x4*>(rec + W_BYTES);
 #pragma unroll
       for (int sl = 0; sl < SPW; ++sl)
