@@ -24,12 +24,14 @@
 // (four wavefronts, one per SIMD); each wavefront keeps its slices
 // transposed, S0^T, in MFMA accumulator layout (fp32) for the whole item.
 // Per chunk:
-//   P1  raw q, k (fp16) from rows staged in LDS by the previous chunk, and
-//       the decay cumsum G (fp32); beta; 2^G_n.
+//   P1  the decay cumsum G (fp32); beta; 2^G_n. bf16 q, k rows were staged
+//       in LDS by the previous chunk and are read there directly by P2, P3;
+//       fp32 inputs are copied to fp16 here.
 //   P2  decayed operands in LDS: Q~ = Q*2^G [c][k], K^T*2^G and
 //       (K*2^(G_n-G))^T [k][c] (fp16).
 //   P3  Gram tile pairs on MFMA: L (fp32) and B (fp16). Scalar gate: exact
-//       fp16 products K K^T, Q K^T scaled by 2^(G_r-G_i) in fp32. Per-key
+//       products K K^T, Q K^T of the inputs (bf16 MFMA on bf16 inputs, fp16
+//       MFMA on the fp16 copy of fp32 ones) scaled by 2^(G_r-G_i) in fp32. Per-key
 //       gate: three-term bf16 products (hi*hi + hi*lo + lo*hi) of operands
 //       decayed relative to the first token of each 16-row block, so every
 //       factor stays in fp32/bf16 range. Two wavefronts then invert the four
@@ -58,6 +60,8 @@
 // K-operand, the K index is permuted (lane group g supplies rows 4g..4g+3 of
 // each of two tiles) and the other operand is read with the same permutation,
 // so no data moves between lanes.
+#include <type_traits>
+
 #include "kda_internal.h"
 
 namespace kda {
@@ -143,7 +147,9 @@ struct Lds {
   // small arrays: G_n[D], 2^G_n[D], beta[64], scalar G[64], scan partials[4][D]
   static constexpr int SMALL_BYTES = (2 * D + 2 * C + 4 * D) * 4;
   static constexpr int OFF_A = OFF_SMALL + SMALL_BYTES;             // region A (aliased)
-  // region A, phase P1..P3: G [64][LDG] f32 (per-key), raw K, raw Q [64][LDQ] f16
+  // region A, phase P1..P3: G [64][LDG] f32 (per-key), raw K, raw Q: bf16 inputs
+  // as staged rows [64][D] bf16 (chunk-permuted, see raw_swz; staged during the
+  // previous chunk's P6, when region A holds only W), fp32 inputs as [64][LDQ] fp16
   static constexpr int A_G = 0;
   static constexpr int A_RK = A_G + C * LDG * 4;
   static constexpr int A_RQ = A_RK + C * LDQ * 2;
@@ -155,11 +161,8 @@ struct Lds {
   static constexpr int A_VT = A_TL + C * LDT * 2;
   static constexpr int A_END2 = A_VT + D * LDT * 2;
   static constexpr int A_BYTES = A_END1 > A_END2 ? A_END1 : A_END2;
-  // raw bf16 q rows of the next chunk [64][D], staged during P6 into the T~
-  // space (dead after P5) below raw K (written again in P1 after q is read)
-  static constexpr int A_QSTAGE = A_TH;
-  static_assert(A_QSTAGE + C * D * 2 <= A_RK, "q staging must not reach raw K");
-  static_assert(A_QSTAGE >= A_W + C * LDQ * 2, "q staging must not touch W");
+  static_assert(A_RK >= A_W + C * LDQ * 2, "raw K/Q staging (during P6) must not touch W");
+  static_assert(C * D * 2 <= C * LDQ * 2, "a staged raw [64][D] bf16 block fits its region");
   static constexpr int TOTAL = OFF_A + A_BYTES;
 };
 
@@ -227,6 +230,51 @@ __device__ __forceinline__ void stage_rows_lds(const uint16_t* src, uint32_t HD,
     const uint16_t* gp = src + (uint32_t)(row < n ? row : 0) * HD + 8 * (lane % LPR);
     __builtin_amdgcn_global_load_lds((gvoid_t*)gp, (lvoid_t*)(static_cast<char*>(lds) + 1024 * i),
                                      16, 0, 0);
+  }
+}
+
+// Chunk permutation of the staged raw q and k rows: LDS chunk p (16 bytes) of
+// row r holds chunk p ^ raw_swz<D>(r) of the row, so that sixteen consecutive
+// rows read at one chunk index (the Gram operand reads) fall on distinct banks.
+template <int D>
+__device__ __forceinline__ int raw_swz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+
+// stage_rows_lds with that permutation (lane l of an instruction still writes
+// base + 16 l; it fetches the matching chunk of its row).
+template <int D, int NW>
+__device__ __forceinline__ void stage_rows_lds_swz(const uint16_t* src, uint32_t HD, int n, void* lds,
+                                                   int wave, int lane) {
+  constexpr int LPR = D / 8;
+  constexpr int RPI = 64 / LPR;
+  constexpr int INSTR = C / RPI;
+  static_assert(INSTR % NW == 0, "every wavefront issues the same number of rows");
+#pragma unroll
+  for (int j = 0; j < INSTR / NW; ++j) {
+    const int i = wave + NW * j;
+    const int row = i * RPI + lane / LPR;
+    const int chunk = (lane % LPR) ^ raw_swz<D>(row);
+    const uint16_t* gp = src + (uint32_t)(row < n ? row : 0) * HD + 8 * chunk;
+    __builtin_amdgcn_global_load_lds((gvoid_t*)gp, (lvoid_t*)(static_cast<char*>(lds) + 1024 * i),
+                                     16, 0, 0);
+  }
+}
+
+// Elements 8ch .. 8ch+7 of staged raw row r (bf16 bits), zero for rows past
+// the chunk end (they hold a copy of row 0).
+template <int D>
+__device__ __forceinline__ uint4 raw_chunk(const unsigned char* base, int r, int ch, bool live) {
+  // unconditional load, then a mask (a conditional load would toggle exec)
+  const uint4 w = *reinterpret_cast<const uint4*>(base + (r * D + 8 * (ch ^ raw_swz<D>(r))) * 2);
+  const uint32_t m = live ? 0xFFFFFFFFu : 0u;
+  return uint4{w.x & m, w.y & m, w.z & m, w.w & m};
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 w) { return __builtin_bit_cast(bf16x8, w); }
+__device__ __forceinline__ void bf16x8_to_f32(uint4 w, float (&x)[8]) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = bf16_bits_to_f32(u[e] & 0xFFFFu);
+    x[2 * e + 1] = bf16_bits_to_f32(u[e] >> 16);
   }
 }
 
@@ -466,11 +514,11 @@ void prefill_kernel(PrefillArgs a) {
       if constexpr (v_in_lds)
         stage_rows_lds<D, NW>(static_cast<const uint16_t*>(a.v) + row0, HDu, min(C, item.n_tokens),
                           smem + L::OFF_QT, wave, lane);
-      stage_rows_lds<D, NW>(static_cast<const uint16_t*>(a.k) + row0, HDu, min(C, item.n_tokens),
-                        smem + L::OFF_KHT, wave, lane);
+      stage_rows_lds_swz<D, NW>(static_cast<const uint16_t*>(a.k) + row0, HDu, min(C, item.n_tokens),
+                                regA + L::A_RK, wave, lane);
       if constexpr (!MAP)
-        stage_rows_lds<D, NW>(static_cast<const uint16_t*>(a.q) + row0, HDu, min(C, item.n_tokens),
-                          regA + L::A_QSTAGE, wave, lane);
+        stage_rows_lds_swz<D, NW>(static_cast<const uint16_t*>(a.q) + row0, HDu, min(C, item.n_tokens),
+                                  regA + L::A_RQ, wave, lane);
     }
     if constexpr (BF16) {
       __builtin_amdgcn_s_waitcnt(0);   // staged rows have landed in LDS
@@ -509,27 +557,14 @@ void prefill_kernel(PrefillArgs a) {
         for (int ct = 0; ct < 4; ++ct) Up[sl][ct] = up[((SPW * wave + sl) * 4 + ct) * 64 + lane];
     }
 
-    // ---- P1: raw q, k (fp16), cumulative log2 decay, beta ---------------------
+    // ---- P1: cumulative log2 decay, beta; fp32 inputs: q, k to fp16 ---------
+    // (bf16 q, k are read straight from their staged rows in P2 and P3)
+    if constexpr (!BF16) {
 #pragma unroll
-    for (int j = 0; j < CR::GPT; ++j) {
-      const int gi = tid + j * NT;
-      const int c = gi / (D / 8), k8 = gi % (D / 8);
-      f16x8 kh, qh;
-      if constexpr (BF16) {
-        // staged bf16 rows [64][D] (unpadded); rows >= n are stale and zeroed here
-        const uint4 kw = *reinterpret_cast<const uint4*>(smem + L::OFF_KHT + (c * D + 8 * k8) * 2);
-        const uint4 qw = MAP ? uint4{0, 0, 0, 0}
-                             : *reinterpret_cast<const uint4*>(regA + L::A_QSTAGE + (c * D + 8 * k8) * 2);
-        const uint32_t kk4[4] = {kw.x, kw.y, kw.z, kw.w}, qq4[4] = {qw.x, qw.y, qw.z, qw.w};
-        const bool live = c < n;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kh[2 * e] = (_Float16)(live ? bf16_bits_to_f32(kk4[e] & 0xFFFFu) : 0.f);
-          kh[2 * e + 1] = (_Float16)(live ? bf16_bits_to_f32(kk4[e] >> 16) : 0.f);
-          qh[2 * e] = (_Float16)(live ? bf16_bits_to_f32(qq4[e] & 0xFFFFu) : 0.f);
-          qh[2 * e + 1] = (_Float16)(live ? bf16_bits_to_f32(qq4[e] >> 16) : 0.f);
-        }
-      } else {
+      for (int j = 0; j < CR::GPT; ++j) {
+        const int gi = tid + j * NT;
+        const int c = gi / (D / 8), k8 = gi % (D / 8);
+        f16x8 kh, qh;
         float x[8];
         unpack_group<BF16>(regs.k[j], x);
 #pragma unroll
@@ -537,9 +572,9 @@ void prefill_kernel(PrefillArgs a) {
         unpack_group<BF16>(regs.q[j], x);
 #pragma unroll
         for (int e = 0; e < 8; ++e) qh[e] = (_Float16)x[e];
+        *reinterpret_cast<f16x8*>(sRK + c * L::LDQ + 8 * k8) = kh;
+        if constexpr (!MAP) *reinterpret_cast<f16x8*>(sRQ + c * L::LDQ + 8 * k8) = qh;
       }
-      *reinterpret_cast<f16x8*>(sRK + c * L::LDQ + 8 * k8) = kh;
-      if constexpr (!MAP) *reinterpret_cast<f16x8*>(sRQ + c * L::LDQ + 8 * k8) = qh;
     }
     float gloc[PER_KEY ? CR::TPB : 1];
     if constexpr (PER_KEY) {
@@ -586,8 +621,20 @@ void prefill_kernel(PrefillArgs a) {
     for (int j = 0; j < CR::GPT; ++j) {
       const int gi = tid + j * NT;
       const int c = gi / (D / 8), k8 = gi % (D / 8);
-      const f16x8 kx = *reinterpret_cast<const f16x8*>(sRK + c * L::LDQ + 8 * k8);
-      const f16x8 qx = MAP ? f16x8{} : *reinterpret_cast<const f16x8*>(sRQ + c * L::LDQ + 8 * k8);
+      float kx[8], qx[8] = {};
+      if constexpr (BF16) {
+        bf16x8_to_f32(raw_chunk<D>(regA + L::A_RK, c, k8, c < n), kx);
+        if constexpr (!MAP) bf16x8_to_f32(raw_chunk<D>(regA + L::A_RQ, c, k8, c < n), qx);
+      } else {
+        const f16x8 kh = *reinterpret_cast<const f16x8*>(sRK + c * L::LDQ + 8 * k8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kx[e] = (float)kh[e];
+        if constexpr (!MAP) {
+          const f16x8 qh = *reinterpret_cast<const f16x8*>(sRQ + c * L::LDQ + 8 * k8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qx[e] = (float)qh[e];
+        }
+      }
       f16x8 qt;
       // scalar gate: one factor pair per token, computed once in P1
       const float dec_c = PER_KEY ? 0.f : sDec[c], rem_c = PER_KEY ? 0.f : sRem[c];
@@ -600,8 +647,8 @@ void prefill_kernel(PrefillArgs a) {
           dec = exp2_hw(gc);
           rem = exp2_hw(sGL[kk] - gc);
         }
-        const float kf = (float)kx[e];
-        qt[e] = (_Float16)((float)qx[e] * dec);
+        const float kf = kx[e];
+        qt[e] = (_Float16)(qx[e] * dec);
         if constexpr (!WU) sKhT[kk * L::LDT + swz(kk, c)] = (_Float16)(kf * dec);   // (W, P5)
         sKtT[kk * L::LDT + swz(kk, c)] = (_Float16)(kf * rem);
       }
@@ -626,21 +673,36 @@ void prefill_kernel(PrefillArgs a) {
         if (!gram_run<NW>(wave, run, R, I0, I1)) break;
         const int r = 16 * R + l16;                  // this lane's row of L / B
         if constexpr (!PER_KEY) {
-          // exact fp16 products of the staged inputs; decay applied per element
-          f16x8 kr[D / 32], qr[D / 32];
+          // exact products of the inputs (bf16 MFMA on the staged bf16 rows, fp16
+          // MFMA on the fp16 copy of fp32 inputs); decay applied per element
+          using OpT = typename std::conditional<BF16, bf16x8, f16x8>::type;
+          auto gram_op = [&](const unsigned char* raw, const _Float16* cp, int row0, int ks) -> OpT {
+            if constexpr (BF16) {
+              const int row = row0 + l16;
+              return as_bf16x8(raw_chunk<D>(raw, row, 4 * ks + g, row < n));
+            } else {
+              return ld_std(cp, L::LDQ, row0, 32 * ks, lane);
+            }
+          };
+          OpT kr[D / 32], qr[D / 32];
 #pragma unroll
           for (int ks = 0; ks < D / 32; ++ks) {
-            kr[ks] = ld_std(sRK, L::LDQ, 16 * R, 32 * ks, lane);
-            if constexpr (!MAP) qr[ks] = ld_std(sRQ, L::LDQ, 16 * R, 32 * ks, lane);
+            kr[ks] = gram_op(regA + L::A_RK, sRK, 16 * R, ks);
+            if constexpr (!MAP) qr[ks] = gram_op(regA + L::A_RQ, sRQ, 16 * R, ks);
           }
           const float gr = sGs[r], br = sBeta[r];
           for (int I = I0; I <= I1; ++I) {
             f32x4 accL = {0, 0, 0, 0}, accB = {0, 0, 0, 0};
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks) {
-              const f16x8 ki = ld_std(sRK, L::LDQ, 16 * I, 32 * ks, lane);
-              if constexpr (!WU) accL = mfma_f16(ki, kr[ks], accL);
-              if constexpr (!MAP) accB = mfma_f16(ki, qr[ks], accB);
+              const OpT ki = gram_op(regA + L::A_RK, sRK, 16 * I, ks);
+              if constexpr (BF16) {
+                if constexpr (!WU) accL = mfma_bf16(ki, kr[ks], accL);
+                if constexpr (!MAP) accB = mfma_bf16(ki, qr[ks], accB);
+              } else {
+                if constexpr (!WU) accL = mfma_f16(ki, kr[ks], accL);
+                if constexpr (!MAP) accB = mfma_f16(ki, qr[ks], accB);
+              }
             }
             const int i0 = 16 * I + 4 * g;           // columns i0..i0+3 of row r
             const f32x4 gi = *reinterpret_cast<const f32x4*>(sGs + i0);
@@ -675,18 +737,30 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int ks = 0; ks < D / 32; ++ks) {
               const int k0 = 32 * ks + 8 * g;
-              const f16x8 kraw = *reinterpret_cast<const f16x8*>(sRK + r * L::LDQ + k0);
-              const f16x8 iraw = *reinterpret_cast<const f16x8*>(sRK + i * L::LDQ + k0);
-              f16x8 qraw = {};
-              if constexpr (!MAP) qraw = *reinterpret_cast<const f16x8*>(sRQ + r * L::LDQ + k0);
+              float kraw[8], iraw[8], qraw[8] = {};
+              if constexpr (BF16) {
+                bf16x8_to_f32(raw_chunk<D>(regA + L::A_RK, r, 4 * ks + g, r < n), kraw);
+                bf16x8_to_f32(raw_chunk<D>(regA + L::A_RK, i, 4 * ks + g, i < n), iraw);
+                if constexpr (!MAP) bf16x8_to_f32(raw_chunk<D>(regA + L::A_RQ, r, 4 * ks + g, r < n), qraw);
+              } else {
+                const f16x8 kh16 = *reinterpret_cast<const f16x8*>(sRK + r * L::LDQ + k0);
+                const f16x8 ih16 = *reinterpret_cast<const f16x8*>(sRK + i * L::LDQ + k0);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) { kraw[e] = (float)kh16[e]; iraw[e] = (float)ih16[e]; }
+                if constexpr (!MAP) {
+                  const f16x8 qh16 = *reinterpret_cast<const f16x8*>(sRQ + r * L::LDQ + k0);
+#pragma unroll
+                  for (int e = 0; e < 8; ++e) qraw[e] = (float)qh16[e];
+                }
+              }
               bf16x8 kh, kl, qh, ql, ih, il;
 #pragma unroll
               for (int e = 0; e < 8; ++e) {
                 const int kk = k0 + e;
                 const float gref = sG[(16 * R) * L::LDG + kk];
                 const float f = exp2_hw(sG[r * L::LDG + kk] - gref);
-                const float kv = (float)kraw[e] * f, qv = (float)qraw[e] * f;
-                const float iv = (float)iraw[e] * exp2_hw(gref - sG[i * L::LDG + kk]);
+                const float kv = kraw[e] * f, qv = qraw[e] * f;
+                const float iv = iraw[e] * exp2_hw(gref - sG[i * L::LDG + kk]);
                 kh[e] = (__bf16)kv; kl[e] = (__bf16)(kv - (float)kh[e]);
                 qh[e] = (__bf16)qv; ql[e] = (__bf16)(qv - (float)qh[e]);
                 ih[e] = (__bf16)iv; il[e] = (__bf16)(iv - (float)ih[e]);
@@ -921,7 +995,7 @@ void prefill_kernel(PrefillArgs a) {
     if constexpr (WU) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
     // prefetch the next chunk's raw inputs while the chain runs (bf16 q, k go
-    // to LDS: the K^T buffer is not read again in this chunk)
+    // to the raw K/Q region, which P6 does not read)
     if (ch + 1 < n_chunks) {
       const int n_next = min(C, item.n_tokens - (ch + 1) * C);
       load_chunk<D, BF16, PER_KEY, NT>(regs, a, tok0 + C, n_next, h, tid, v_in_regs);
@@ -930,11 +1004,11 @@ void prefill_kernel(PrefillArgs a) {
         if constexpr (v_in_lds)
           stage_rows_lds<D, NW>(static_cast<const uint16_t*>(a.v) + row0, HDu, n_next, smem + L::OFF_QT,
                             wave, lane);
-        stage_rows_lds<D, NW>(static_cast<const uint16_t*>(a.k) + row0, HDu, n_next, smem + L::OFF_KHT,
-                          wave, lane);
+        stage_rows_lds_swz<D, NW>(static_cast<const uint16_t*>(a.k) + row0, HDu, n_next, regA + L::A_RK,
+                                  wave, lane);
         if constexpr (!MAP)
-          stage_rows_lds<D, NW>(static_cast<const uint16_t*>(a.q) + row0, HDu, n_next, regA + L::A_QSTAGE,
-                            wave, lane);
+          stage_rows_lds_swz<D, NW>(static_cast<const uint16_t*>(a.q) + row0, HDu, n_next, regA + L::A_RQ,
+                                    wave, lane);
       }
     }
 
