@@ -86,11 +86,13 @@ typedef __attribute__((address_space(3))) void lvoid_t;
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 
-// [k][c] fp16 arrays (K^T, K~^T, V^T) rotate each row by 8 * ((k / 8) % 8)
-// columns, so that the transposed staging writes of 16 consecutive
-// 8-channel groups land on distinct LDS banks; aligned groups of 4 and 8
-// columns stay contiguous, which is all the MFMA operand reads need.
-__device__ __forceinline__ int swz(int k, int c) { return (c + 8 * ((k >> 3) & 7)) & 63; }
+// [k][c] fp16 arrays (K^T, K~^T, V^T) rotate each row by 8 * ((k / 16) % 8)
+// columns. The transposed staging writes of 16 consecutive 8-channel groups
+// then land on distinct LDS banks, and so do the operand reads of 16
+// consecutive rows (one rotation per 16-row tile, rows 72 halves apart);
+// aligned groups of 4 and 8 columns stay contiguous, which is all the MFMA
+// operand reads need.
+__device__ __forceinline__ int swz(int k, int c) { return (c + 8 * ((k >> 4) & 7)) & 63; }
 
 // Row (l%16) of a row-major fp16 matrix, the 8 K-elements of lane group
 // g = l/16 in the standard order: k0 + 8g .. k0 + 8g + 7.
@@ -135,6 +137,8 @@ template <int D>
 struct Lds {
   static constexpr int LDQ = D + 8;   // row stride of [64][D] fp16 arrays
   static constexpr int LDT = C + 8;   // row stride of [D][64] / [64][64] fp16 arrays
+  static constexpr int LDTT = C + 16; // row stride of T~ hi/lo: 160 bytes, so the
+                                      // 16-byte operand reads of 16 rows hit distinct banks
   static constexpr int LDL = C + 4;   // row stride of the fp32 64x64 L / inverse
   static constexpr int LDG = D + 4;   // row stride of per-key G [64][D] fp32
   // persistent through a chunk
@@ -154,11 +158,11 @@ struct Lds {
   static constexpr int A_RK = A_G + C * LDG * 4;
   static constexpr int A_RQ = A_RK + C * LDQ * 2;
   static constexpr int A_END1 = A_RQ + C * LDQ * 2;
-  // region A, phase P4..P6: W [64][LDQ] f16, T~ hi/lo [64][LDT] f16, V^T [D][LDT] f16
+  // region A, phase P4..P6: W [64][LDQ] f16, T~ hi/lo [64][LDTT] f16, V^T [D][LDT] f16
   static constexpr int A_W = 0;
   static constexpr int A_TH = A_W + C * LDQ * 2;
-  static constexpr int A_TL = A_TH + C * LDT * 2;
-  static constexpr int A_VT = A_TL + C * LDT * 2;
+  static constexpr int A_TL = A_TH + C * LDTT * 2;
+  static constexpr int A_VT = A_TL + C * LDTT * 2;
   static constexpr int A_END2 = A_VT + D * LDT * 2;
   static constexpr int A_BYTES = A_END1 > A_END2 ? A_END1 : A_END2;
   static_assert(A_RK >= A_W + C * LDQ * 2, "raw K/Q staging (during P6) must not touch W");
@@ -927,8 +931,8 @@ void prefill_kernel(PrefillArgs a) {
           th[e] = (_Float16)tv;
           tl[e] = (_Float16)(tv - (float)th[e]);
         }
-        *reinterpret_cast<f16x8*>(sTh + c * L::LDT + i0) = th;
-        *reinterpret_cast<f16x8*>(sTl + c * L::LDT + i0) = tl;
+        *reinterpret_cast<f16x8*>(sTh + c * L::LDTT + i0) = th;
+        *reinterpret_cast<f16x8*>(sTl + c * L::LDTT + i0) = tl;
       }
       __syncthreads();
       // W[:, 16kt..16kt+15] for kt = wave, wave + NW, ... and U' = T~ V for the
@@ -950,8 +954,8 @@ void prefill_kernel(PrefillArgs a) {
           f16x8 th[4], tl[4], bk[KT / NW], bv[SPW];
 #pragma unroll
           for (int ct = 0; ct < 4; ++ct) {
-            th[ct] = ld_std(sTh, L::LDT, 16 * ct, 32 * ks, lane);
-            tl[ct] = ld_std(sTl, L::LDT, 16 * ct, 32 * ks, lane);
+            th[ct] = ld_std(sTh, L::LDTT, 16 * ct, 32 * ks, lane);
+            tl[ct] = ld_std(sTl, L::LDTT, 16 * ct, 32 * ks, lane);
           }
 #pragma unroll
           for (int kj = 0; kj < KT / NW; ++kj) bk[kj] = ld_std_swz(sKhT, L::LDT, 16 * (wave + NW * kj), 32 * ks, lane);
