@@ -353,9 +353,10 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<D, BF16, PER_KEY, NT>& R, c
 // inversion as one unit each, per SIMD:
 //   four wavefronts:  w0: R3 I0-2 | w1: R2 I0-1, R1 I0 | w2: R0 I0, R1 I1, inv 0,1
 //                     | w3: R2 I2, R3 I3, inv 2,3                       (3/3/3/3)
-//   eight wavefronts (w and w+4 share a SIMD): w0: R0 I0, R1 I1, inv 0,1 |
-//                     w1: R2 I2, R3 I3, inv 2,3 | w2: R3 I0-1 | w3: R3 I2, R2 I1 |
-//                     w6: R2 I0 | w7: R1 I0                            (3/3/3/3)
+//   eight wavefronts (w and w+4 share a SIMD): wavefront b < 4 computes the
+//                     diagonal pair (b, b) and inverts block b, so only one
+//                     pair precedes each inversion; w4: R3 I0-1 | w5: R3 I2,
+//                     R2 I1 | w6: R2 I0 | w7: R1 I0          (3/3/2/2 per SIMD)
 // Four 12-bit run codes in the 16-bit fields of one 64-bit constant (field w
 // for wavefront w): the lookup is register arithmetic, not a memory load.
 constexpr uint64_t pack_runs(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
@@ -373,10 +374,10 @@ __device__ __forceinline__ bool gram_run(int wave_lane, int run, int& R, int& I0
     packed = run == 0 ? kRun0 : kRun1;
   } else {
     static_assert(NW == 8, "four or eight wavefronts");
-    constexpr uint64_t kRun0Lo = pack_runs(0x000, 0x222, 0x301, 0x322);   // wavefronts 0-3
-    constexpr uint64_t kRun0Hi = pack_runs(0xFFF, 0xFFF, 0x200, 0x100);   // wavefronts 4-7
-    constexpr uint64_t kRun1Lo = pack_runs(0x111, 0x333, 0xFFF, 0x211);
-    constexpr uint64_t kRun1Hi = pack_runs(0xFFF, 0xFFF, 0xFFF, 0xFFF);
+    constexpr uint64_t kRun0Lo = pack_runs(0x000, 0x111, 0x222, 0x333);   // wavefronts 0-3
+    constexpr uint64_t kRun0Hi = pack_runs(0x301, 0x322, 0x200, 0x100);   // wavefronts 4-7
+    constexpr uint64_t kRun1Lo = pack_runs(0xFFF, 0xFFF, 0xFFF, 0xFFF);
+    constexpr uint64_t kRun1Hi = pack_runs(0xFFF, 0x211, 0xFFF, 0xFFF);
     const bool hi = (wave & 7) >= 4;
     packed = run == 0 ? (hi ? kRun0Hi : kRun0Lo) : (hi ? kRun1Hi : kRun1Lo);
   }
@@ -387,15 +388,18 @@ __device__ __forceinline__ bool gram_run(int wave_lane, int run, int& R, int& I0
   I1 = code & 15;
   return true;
 }
-// Diagonal blocks this wavefront inverts after its runs (d0, d1), or false.
+// Diagonal blocks this wavefront inverts after its runs (d0, d1; equal when it
+// inverts one block), or false.
 template <int NW>
 __device__ __forceinline__ bool gram_diag(int wave, int& d0, int& d1) {
-  const int w0 = 2, w1 = 3;                      // four wavefronts
-  const int v0 = 0, v1 = 1;                      // eight wavefronts
-  const int wa = NW == 4 ? w0 : v0, wb = NW == 4 ? w1 : v1;
-  if (wave == wa) { d0 = 0; d1 = 1; return true; }
-  if (wave == wb) { d0 = 2; d1 = 3; return true; }
-  return false;
+  if constexpr (NW == 4) {
+    if (wave == 2) { d0 = 0; d1 = 1; return true; }
+    if (wave == 3) { d0 = 2; d1 = 3; return true; }
+    return false;
+  } else {
+    if (wave < 4) { d0 = wave; d1 = wave; return true; }
+    return false;
+  }
 }
 
 __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
@@ -804,8 +808,9 @@ void prefill_kernel(PrefillArgs a) {
       int d0, d1;
       if (!WU && gram_diag<NW>(wave, d0, d1)) {
         // Replace L_bb by the inverse of the unit lower block I + L_bb for the
-        // two diagonal blocks this wavefront computed: lane groups 0-1 take
-        // block d0, 2-3 block d1, one column j per lane (groups 0 and 2
+        // diagonal blocks this wavefront computed: lane groups 0-1 take block
+        // d0, 2-3 block d1 (the same block when it inverts one: both halves
+        // then store the same values), one column j per lane (groups 0 and 2
         // store). Right-looking: once x_i is final, every later row r takes
         // -L[r][i] x_i, read from row i of the transposed copy in the block's
         // upper triangle.
