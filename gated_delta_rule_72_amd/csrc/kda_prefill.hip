@@ -353,16 +353,20 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<D, BF16, PER_KEY, NT>& R, c
 // inversion as one unit each, per SIMD:
 //   four wavefronts:  w0: R3 I0-2 | w1: R2 I0-1, R1 I0 | w2: R0 I0, R1 I1, inv 0,1
 //                     | w3: R2 I2, R3 I3, inv 2,3                       (3/3/3/3)
-//   eight wavefronts (w and w+4 share a SIMD): wavefront b < 4 computes the
-//                     diagonal pair (b, b) and inverts block b, so only one
-//                     pair precedes each inversion; w4: R3 I0-1 | w5: R3 I2,
-//                     R2 I1 | w6: R2 I0 | w7: R1 I0          (3/3/2/2 per SIMD)
+//   eight wavefronts (w and w+4 share a SIMD), scalar gate (cheap pairs):
+//                     wavefront b < 4 computes the diagonal pair (b, b) and
+//                     inverts block b, so only one pair precedes each
+//                     inversion; w4: R3 I0-1 | w5: R3 I2, R2 I1 | w6: R2 I0 |
+//                     w7: R1 I0. Per-key gate (a pair costs more than an
+//                     inversion): w0: R0 I0, R1 I1, inv 0,1 | w1: R2 I2, R3 I3,
+//                     inv 2,3 | w2: R3 I0-1 | w3: R3 I2, R2 I1 | w6: R2 I0 |
+//                     w7: R1 I0                                (3/3/3/3)
 // Four 12-bit run codes in the 16-bit fields of one 64-bit constant (field w
 // for wavefront w): the lookup is register arithmetic, not a memory load.
 constexpr uint64_t pack_runs(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
   return (uint64_t)w0 | ((uint64_t)w1 << 16) | ((uint64_t)w2 << 32) | ((uint64_t)w3 << 48);
 }
-template <int NW>
+template <int NW, bool PER_KEY>
 __device__ __forceinline__ bool gram_run(int wave_lane, int run, int& R, int& I0, int& I1) {
   // per wavefront and run a nibble triple (R, I0, I1); 0xFFF = no run. The
   // wavefront index is uniform: the selection runs on scalar registers.
@@ -374,10 +378,14 @@ __device__ __forceinline__ bool gram_run(int wave_lane, int run, int& R, int& I0
     packed = run == 0 ? kRun0 : kRun1;
   } else {
     static_assert(NW == 8, "four or eight wavefronts");
-    constexpr uint64_t kRun0Lo = pack_runs(0x000, 0x111, 0x222, 0x333);   // wavefronts 0-3
-    constexpr uint64_t kRun0Hi = pack_runs(0x301, 0x322, 0x200, 0x100);   // wavefronts 4-7
-    constexpr uint64_t kRun1Lo = pack_runs(0xFFF, 0xFFF, 0xFFF, 0xFFF);
-    constexpr uint64_t kRun1Hi = pack_runs(0xFFF, 0x211, 0xFFF, 0xFFF);
+    constexpr uint64_t kRun0Lo = !PER_KEY ? pack_runs(0x000, 0x111, 0x222, 0x333)    // wavefronts 0-3
+                                          : pack_runs(0x000, 0x222, 0x301, 0x322);
+    constexpr uint64_t kRun0Hi = !PER_KEY ? pack_runs(0x301, 0x322, 0x200, 0x100)    // wavefronts 4-7
+                                          : pack_runs(0xFFF, 0xFFF, 0x200, 0x100);
+    constexpr uint64_t kRun1Lo = !PER_KEY ? pack_runs(0xFFF, 0xFFF, 0xFFF, 0xFFF)
+                                          : pack_runs(0x111, 0x333, 0xFFF, 0x211);
+    constexpr uint64_t kRun1Hi = !PER_KEY ? pack_runs(0xFFF, 0x211, 0xFFF, 0xFFF)
+                                          : pack_runs(0xFFF, 0xFFF, 0xFFF, 0xFFF);
     const bool hi = (wave & 7) >= 4;
     packed = run == 0 ? (hi ? kRun0Hi : kRun0Lo) : (hi ? kRun1Hi : kRun1Lo);
   }
@@ -390,11 +398,12 @@ __device__ __forceinline__ bool gram_run(int wave_lane, int run, int& R, int& I0
 }
 // Diagonal blocks this wavefront inverts after its runs (d0, d1; equal when it
 // inverts one block), or false.
-template <int NW>
+template <int NW, bool PER_KEY>
 __device__ __forceinline__ bool gram_diag(int wave, int& d0, int& d1) {
-  if constexpr (NW == 4) {
-    if (wave == 2) { d0 = 0; d1 = 1; return true; }
-    if (wave == 3) { d0 = 2; d1 = 3; return true; }
+  if constexpr (NW == 4 || PER_KEY) {
+    const int wa = NW == 4 ? 2 : 0;              // the two wavefronts that invert
+    if (wave == wa) { d0 = 0; d1 = 1; return true; }
+    if (wave == wa + 1) { d0 = 2; d1 = 3; return true; }
     return false;
   } else {
     if (wave < 4) { d0 = wave; d1 = wave; return true; }
@@ -678,7 +687,7 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int run = 0; run < 2; ++run) {
         int R, I0, I1;
-        if (!gram_run<NW>(wave, run, R, I0, I1)) break;
+        if (!gram_run<NW, PER_KEY>(wave, run, R, I0, I1)) break;
         const int r = 16 * R + l16;                  // this lane's row of L / B
         if constexpr (!PER_KEY) {
           // exact products of the inputs (bf16 MFMA on the staged bf16 rows, fp16
@@ -806,7 +815,7 @@ void prefill_kernel(PrefillArgs a) {
         }
       }
       int d0, d1;
-      if (!WU && gram_diag<NW>(wave, d0, d1)) {
+      if (!WU && gram_diag<NW, PER_KEY>(wave, d0, d1)) {
         // Replace L_bb by the inverse of the unit lower block I + L_bb for the
         // diagonal blocks this wavefront computed: lane groups 0-1 take block
         // d0, 2-3 block d1 (the same block when it inverts one: both halves
