@@ -247,8 +247,9 @@ def test_pageable_host_snapshots_rejected_by_binding():
 @pytest.mark.parametrize("gate", ["scalar", "per_key"])
 def test_segmented_every_variant(d, dtype, gate):
     """Forced 128-token segments for every (d, input dtype, gate) variant: the
-    map pass, its stored inverses, the scan and the output pass, on a varlen
-    pack with a ragged tail, snapshots and initial states."""
+    map pass, its stored W and U', the scan, the output pass of the split
+    sequences and that of the whole ones, on a varlen pack with a ragged tail,
+    snapshots and initial states."""
     dev = device()
     w = custom(f"segvar_{d}_{dtype}_{gate}", H=2, d=d, lens=(700, 130, 0, 64), gate=gate, dtype=dtype,
                interval=64, seed=21)
