@@ -215,11 +215,13 @@ __device__ __forceinline__ void unpack_group(const RawGroup<BF16>& r, float (&x)
 template <int D>
 constexpr int waves_for() { return D == 128 ? 8 : 4; }
 
-// bf16 inputs: the raw q and k rows of a chunk go straight from HBM into LDS
+// bf16 inputs: raw rows of a chunk go straight from HBM into LDS
 // (global_load_lds_dwordx4: lane l's 16 bytes land at base + 16 l), into
 // buffers that are dead during the state passing, so the prefetch of the
 // next chunk holds no registers. Rows past the chunk end are loaded from row
 // 0 and zeroed when they are read. `src` is the workgroup-uniform chunk base.
+// This form (rows in order) stages v in the map pass; q and k use the
+// chunk-permuted form below.
 template <int D, int NW>
 __device__ __forceinline__ void stage_rows_lds(const uint16_t* src, uint32_t HD, int n, void* lds,
                                                int wave, int lane) {
