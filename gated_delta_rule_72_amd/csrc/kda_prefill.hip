@@ -54,7 +54,10 @@
 // segment and keeps each chunk's W and U' (the products of P5), a scan composes
 // S_{s+1} = S_s M_s + N_s in fp32 from the initial state, and pass 3 (WU) runs
 // every segment from its true start, loading W and U' instead of forming L,
-// the inverse and P5 again; whole sequences of the same call run in OUT.
+// the inverse and P5 again; whole sequences of the same call run in OUT. For
+// the scalar gate with bf16 inputs at d = 128, pass 3 is a kernel of its own
+// (prefill_wu_pipe_kernel) in which four wavefronts run the chain while the
+// other four prepare the next chunk's operands.
 // Accumulator layout of a 16x16 MFMA tile: lane l holds rows 4(l/16)+i,
 // column l%16. When an accumulator tile feeds the next product as its
 // K-operand, the K index is permuted (lane group g supplies rows 4g..4g+3 of
@@ -1184,6 +1187,405 @@ void prefill_kernel(PrefillArgs a) {
   }
 }
 
+// ---- Pass 3, scalar gate, bf16 inputs, d = 128: chain and producer wavefronts
+// Only P6 depends on the state; P1-P3 of a chunk (decay scan, Q~ and K~^T, the
+// output Gram B) need its raw rows alone. In this form of pass 3 wavefronts
+// 0-3 (one per SIMD) run the chain, each on 32 state rows (two slices), and
+// wavefronts 4-7 prepare the next chunk: they fetch its raw q/k rows, alpha and
+// stored W, scan its decay and form Q~, K~^T and B in the other half of a
+// double buffer. A chain wavefront reads every shared operand once for both of
+// its slices, so P6 reads half the LDS bytes of the eight-slice form. Each
+// chunk takes two barrier intervals:
+//   A: chain: U = U' - W S0^T (chunk c)
+//      producers: raw rows of c+1 into LDS, its decay scan, the fetch of its W
+//   B: chain: O and the state update (chunk c), then the fetch of U' (c+1)
+//      producers: Q~ and K~^T of c+1, the fetch of c+2's raw rows, B of c+1,
+//      W of c+1 into LDS (the chain read chunk c's in interval A)
+// The fetches sit where they least delay the chain's o stores, which share
+// the compute unit's vector memory path with them.
+// Every product is the one the other pass-3 form computes, in the same order,
+// so both give the same bits.
+template <int D>
+struct LdsPipe {
+  using L = Lds<D>;
+  static constexpr int QT = 0;                                  // Q~    [64][LDQ] f16
+  static constexpr int KTT = QT + C * L::LDQ * 2;               // K~^T  [D][LDT] f16 (swizzled)
+  static constexpr int BG = KTT + D * L::LDT * 2;               // B     [64][LDT] f16
+  static constexpr int GS = BG + C * L::LDT * 2;                // G[64], 2^G[64], 2^(G_n-G)[64], 2^G_n[D] f32
+  static constexpr int BUF = GS + ((3 * C + D) * 4 + 511) / 512 * 512;   // one buffer
+  static constexpr int OFF_W = 2 * BUF;                         // W     [64][LDQ] f16 (the stored image)
+  static constexpr int OFF_RK = OFF_W + C * L::LDQ * 2;         // raw k [64][D] bf16 (raw_swz)
+  static constexpr int OFF_RQ = OFF_RK + C * D * 2;             // raw q
+  static constexpr int TOTAL = OFF_RQ + C * D * 2;
+  static_assert(BUF % 512 == 0 && OFF_W % 512 == 0, "buffers keep the bank alignment of the other form");
+};
+
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_wu_pipe_kernel(PrefillArgs a) {
+  static_assert(D == 128, "four chain wavefronts of 32 state rows");
+  constexpr int NC = 4, NP = 4;                  // chain and producer wavefronts
+  constexpr int NPT = 64 * NP;                   // producer threads
+  using L = Lds<D>;
+  using P = LdsPipe<D>;
+  constexpr int SPW = D / (16 * NC);             // state slices per chain wavefront
+  constexpr int KT = D / 16;
+  constexpr int LPR = D / 8;                     // lanes per raw row (16 bytes each)
+  constexpr int RPI = 64 / LPR;                  // raw rows per wavefront instruction
+  constexpr int RI = C / RPI / NP;               // raw-row instructions per producer and tensor
+  static_assert(RI * RPI * NP == C, "every producer stages the same number of rows");
+  constexpr int GPT = C * D / 8 / NPT;           // P2: 8-element groups per producer thread
+  static_assert(GPT * 8 * NPT == C * D, "P2 covers the chunk");
+  extern __shared__ __align__(16) unsigned char smem[];
+  _Float16* sW = reinterpret_cast<_Float16*>(smem + P::OFF_W);
+  unsigned char* rawK = smem + P::OFF_RK;
+  unsigned char* rawQ = smem + P::OFF_RQ;
+
+  const int wave = threadIdx.x / 64;
+  const bool chain = wave < NC;                  // (uniform per wavefront)
+  const int pw = wave - NC;                      // producer wavefront index
+  // Per-lane indices (ptid: producer thread index) are refreshed from an
+  // opaque copy of the thread index at every chunk: hoisted out of the loop,
+  // the addresses derived from them would hold registers for the whole item.
+  int tid = threadIdx.x, lane = tid % 64, g = lane >> 4, l16 = lane & 15, ptid = tid - 64 * NC;
+  auto refresh = [&]() __attribute__((always_inline)) {
+    asm volatile("" : "+v"(tid));
+    lane = tid % 64;
+    g = lane >> 4;
+    l16 = lane & 15;
+    ptid = tid - 64 * NC;
+  };
+  const int item_idx = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const PrefillItem item = a.items[item_idx];
+  if (item.n_segs <= 1) return;                  // (uniform) whole sequences run in the other pass
+  constexpr int W_BYTES = (int)wu_w_bytes(D);
+  static_assert(W_BYTES == C * L::LDQ * 2, "stored W layout");
+  constexpr int64_t WU_BYTES = (int64_t)wu_chunk_bytes(D);
+  const unsigned char* wu_base =
+      static_cast<const unsigned char*>(a.seg_wu) + ((int64_t)item_idx * a.H + h) * a.seg_chunks * WU_BYTES;
+  const int64_t HD = (int64_t)a.H * D;
+  const int64_t DD = (int64_t)D * D;
+  const uint32_t HDu = (uint32_t)a.H * D;
+  const int n_chunks = (item.n_tokens + C - 1) / C;
+  if (n_chunks == 0) return;                     // (uniform; a segment is never empty)
+  auto chunk_len = [&](int ch) { return min(C, item.n_tokens - ch * C); };
+
+  // chain: start state of the segment (from the scan), S0^T in accumulator
+  // layout; slice sl covers state rows 16 (SPW wave + sl) .. +15
+  f32x4 ST[SPW][KT];
+  if (chain) {
+    const float* src = a.seg_states + ((int64_t)item_idx * a.H + h) * DD;
+#pragma unroll
+    for (int sl = 0; sl < SPW; ++sl) {
+      const int row = 16 * (SPW * wave + sl) + l16;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) ST[sl][kt] = *reinterpret_cast<const f32x4*>(src + row * D + 16 * kt + 4 * g);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0): see the other form's start state
+
+  // ---- producer side ------------------------------------------------------------
+  // raw q/k rows of one chunk in registers, in the order stage_rows_lds_swz
+  // lays them out (instruction i = pw + NP j: rows i RPI + lane / LPR, lane l
+  // holds the bytes that land at 1024 i + 16 l); rows past the end are row 0.
+  // alpha: producer 0, token `lane`.
+  // The same registers carry the chain's U' of the next chunk and the
+  // producers' raw rows of the chunk after it (live across a whole chunk on
+  // either side): carry[j] = k rows, carry[RI + j] = q rows; chain: U' tile
+  // (sl, ct) at carry[4 sl + ct].
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  static_assert(2 * RI == 4 * SPW, "one carry array fits both roles");
+  i32x4 carry[2 * RI];
+  float pre_alpha = 1.f;
+  auto fetch_raw = [&](int ch) __attribute__((always_inline)) {
+    const int n = chunk_len(ch);
+    const int64_t tok0 = item.tok_begin + (int64_t)ch * C;
+    const int64_t row0 = (tok0 * a.H + h) * D;
+    const uint16_t* kb = static_cast<const uint16_t*>(a.k) + row0;
+    const uint16_t* qb = static_cast<const uint16_t*>(a.q) + row0;
+#pragma unroll
+    for (int j = 0; j < RI; ++j) {
+      const int i = pw + NP * j;
+      const int row = i * RPI + lane / LPR;
+      const uint32_t off = (uint32_t)(row < n ? row : 0) * HDu + 8u * (uint32_t)((lane % LPR) ^ raw_swz<D>(row));
+      carry[j] = *reinterpret_cast<const i32x4*>(kb + off);
+      carry[RI + j] = *reinterpret_cast<const i32x4*>(qb + off);
+    }
+    // loads in this form are unconditional, with clamped addresses (the
+    // rows past the end are masked where they are used): a load under a lane
+    // mask, or a select right after one, makes the compiler wait there for
+    // every load in flight
+    pre_alpha = a.alpha[(tok0 + min(lane, n - 1)) * a.H + h];
+  };
+  auto put_raw = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < RI; ++j) {
+      const int i = pw + NP * j;
+      *reinterpret_cast<i32x4*>(rawK + 1024 * i + 16 * lane) = carry[j];
+      *reinterpret_cast<i32x4*>(rawQ + 1024 * i + 16 * lane) = carry[RI + j];
+    }
+  };
+  // P1: cumulative log2 decay of the staged chunk (n tokens; producer 0) into
+  // buffer b
+  auto p1 = [&](int b, int n) __attribute__((always_inline)) {
+    if (pw == 0) {
+      float* gs = reinterpret_cast<float*>(smem + b * P::BUF + P::GS);
+      const float gcum = wave_inclusive_scan(log2_hw(lane < n ? pre_alpha : 1.f), lane);
+      const float gl = __shfl(gcum, C - 1);
+      const float gam = exp2_hw(gl);
+      gs[lane] = gcum;
+      gs[C + lane] = exp2_hw(gcum);
+      gs[2 * C + lane] = exp2_hw(gl - gcum);
+#pragma unroll
+      for (int k0 = 0; k0 < D; k0 += 64) gs[3 * C + k0 + lane] = gam;
+    }
+  };
+  // P2: Q~ and K~^T of the staged chunk into buffer b
+  auto p2 = [&](int b, int n) __attribute__((always_inline)) {
+    unsigned char* buf = smem + b * P::BUF;
+    _Float16* sQt = reinterpret_cast<_Float16*>(buf + P::QT);
+    _Float16* sKtT = reinterpret_cast<_Float16*>(buf + P::KTT);
+    const float* sDec = reinterpret_cast<const float*>(buf + P::GS) + C;
+    const float* sRem = sDec + C;
+#pragma unroll
+    for (int j = 0; j < GPT; ++j) {
+      const int gi = ptid + j * NPT;
+      const int c = gi / (D / 8), k8 = gi % (D / 8);
+      float kx[8], qx[8];
+      bf16x8_to_f32(raw_chunk<D>(rawK, c, k8, c < n), kx);
+      bf16x8_to_f32(raw_chunk<D>(rawQ, c, k8, c < n), qx);
+      const float dec = sDec[c], rem = sRem[c];
+      f16x8 qt;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kk = 8 * k8 + e;
+        qt[e] = (_Float16)(qx[e] * dec);
+        sKtT[kk * L::LDT + swz(kk, c)] = (_Float16)(kx[e] * rem);
+      }
+      *reinterpret_cast<f16x8*>(sQt + c * L::LDQ + 8 * k8) = qt;
+    }
+  };
+  // P3: the lower tiles of B = tril_incl(Q K^T) with the decay, into buffer b
+  // (upper tiles stay zero from the start); the four-wavefront run schedule
+  auto p3 = [&](int b, int n) __attribute__((always_inline)) {
+    unsigned char* buf = smem + b * P::BUF;
+    _Float16* sB = reinterpret_cast<_Float16*>(buf + P::BG);
+    const float* sGs = reinterpret_cast<const float*>(buf + P::GS);
+#pragma unroll
+    for (int run = 0; run < 2; ++run) {
+      int R, I0, I1;
+      if (!gram_run<NP, false>(pw, run, R, I0, I1)) break;
+      const int r = 16 * R + l16;
+      bf16x8 qr[D / 32];
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) qr[ks] = as_bf16x8(raw_chunk<D>(rawQ, r, 4 * ks + g, r < n));
+      const float gr = sGs[r];
+      for (int I = I0; I <= I1; ++I) {
+        f32x4 accB = {0, 0, 0, 0};
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+          const int i = 16 * I + l16;
+          accB = mfma_bf16(as_bf16x8(raw_chunk<D>(rawK, i, 4 * ks + g, i < n)), qr[ks], accB);
+        }
+        const int i0 = 16 * I + 4 * g;
+        const f32x4 gi = *reinterpret_cast<const f32x4*>(sGs + i0);
+        f16x4 bv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float f = exp2_hw(fminf(gr - gi[e], 0.f));
+          bv[e] = (_Float16)((i0 + e <= r) ? accB[e] * f : 0.f);
+        }
+        *reinterpret_cast<f16x4*>(sB + r * L::LDT + i0) = bv;
+      }
+    }
+  };
+  // stored W of chunk ch: producers, through registers
+  constexpr int W_VEC = W_BYTES / 16;
+  constexpr int W_PER_T = (W_VEC + NPT - 1) / NPT;
+  f32x4 wreg[W_PER_T];
+  auto fetch_w = [&](int ch) __attribute__((always_inline)) {
+    const f32x4* rec = reinterpret_cast<const f32x4*>(wu_base + (int64_t)ch * WU_BYTES);
+#pragma unroll
+    for (int j = 0; j < W_PER_T; ++j) wreg[j] = rec[min(ptid + j * NPT, W_VEC - 1)];
+  };
+  auto put_w = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < W_PER_T; ++j) {
+      const int e = ptid + j * NPT;
+      if (e < W_VEC) reinterpret_cast<f32x4*>(sW)[e] = wreg[j];
+    }
+  };
+  // ---- chain side: stored U' of chunk ch (this wavefront's slices) -------------
+  auto fetch_up = [&](int ch) __attribute__((always_inline)) {
+    const i32x4* up = reinterpret_cast<const i32x4*>(wu_base + (int64_t)ch * WU_BYTES + W_BYTES);
+#pragma unroll
+    for (int sl = 0; sl < SPW; ++sl)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) carry[4 * sl + ct] = up[((SPW * wave + sl) * 4 + ct) * 64 + lane];
+  };
+
+  // ---- prologue: chunk 0's operands in buffer 0, W(0) in LDS (producers),
+  // U'(0) (chain) ----------------------------------------------------------------
+  if (chain) {
+    fetch_up(0);
+  } else {
+    fetch_raw(0);
+    fetch_w(0);
+    for (int e = ptid; e < 2 * 6 * 256; e += NPT) {   // upper tiles of both B buffers
+      const int bb = e / (6 * 256), t = (e / 256) % 6, rr = (e % 256) / 16, cc = e % 16;
+      const int R = t < 3 ? 0 : (t < 5 ? 1 : 2);
+      const int I = t < 3 ? t + 1 : (t < 5 ? t - 1 : 3);
+      reinterpret_cast<_Float16*>(smem + bb * P::BUF + P::BG)[(16 * R + rr) * L::LDT + 16 * I + cc] = (_Float16)0.f;
+    }
+    put_raw();
+    p1(0, chunk_len(0));
+  }
+  __syncthreads();
+  refresh();
+  if (!chain) {
+    if (n_chunks > 1) fetch_raw(1);
+    p2(0, chunk_len(0));
+    p3(0, chunk_len(0));
+    put_w();
+  }
+  __syncthreads();
+
+  for (int ch = 0; ch < n_chunks; ++ch) {
+    const int b = ch & 1, nb = b ^ 1;
+    const bool has_next = ch + 1 < n_chunks;
+    const int64_t tok0 = item.tok_begin + (int64_t)ch * C;
+    const int n = chunk_len(ch);
+    refresh();
+
+    // ---- interval A ---------------------------------------------------------
+    f16x8 sop[SPW][D / 32], uh[SPW][2], ul[SPW][2];
+    if (chain) {
+      // U = U' - W S0^T (W (-S0^T) accumulated into U' directly)
+      f32x4 U[SPW][4];
+#pragma unroll
+      for (int sl = 0; sl < SPW; ++sl)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) U[sl][ct] = __builtin_bit_cast(f32x4, carry[4 * sl + ct]);
+#pragma unroll
+      for (int sl = 0; sl < SPW; ++sl)
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) sop[sl][ks] = pack_perm(ST[sl][2 * ks], ST[sl][2 * ks + 1]);
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        f16x8 w[4], nsop[SPW];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) w[ct] = ld_perm(sW, L::LDQ, 16 * ct, 32 * ks, lane);
+#pragma unroll
+        for (int sl = 0; sl < SPW; ++sl) nsop[sl] = -sop[sl][ks];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int sl = 0; sl < SPW; ++sl) U[sl][ct] = mfma_f16(w[ct], nsop[sl], U[sl][ct]);
+      }
+#pragma unroll
+      for (int sl = 0; sl < SPW; ++sl)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) split_perm(U[sl][2 * ks], U[sl][2 * ks + 1], uh[sl][ks], ul[sl][ks]);
+    } else if (has_next) {
+      put_raw();                                 // chunk ch+1's raw rows (fetched an interval ago)
+      p1(nb, chunk_len(ch + 1));
+      fetch_w(ch + 1);
+    }
+    __syncthreads();
+
+    // ---- interval B ---------------------------------------------------------
+    if (chain) {
+      const _Float16* sQt = reinterpret_cast<const _Float16*>(smem + b * P::BUF + P::QT);
+      const _Float16* sKtT = reinterpret_cast<const _Float16*>(smem + b * P::BUF + P::KTT);
+      const _Float16* sB = reinterpret_cast<const _Float16*>(smem + b * P::BUF + P::BG);
+      const float* sGam = reinterpret_cast<const float*>(smem + b * P::BUF + P::GS) + 3 * C;
+      // O^T = S0 Q~^T + U^T B^T, one 16-token tile at a time; lane (g, l16)
+      // holds O[token 16ct + l16][values 16 slice + 4g .. +3]
+      const int64_t obase = tok0 * HD + (int64_t)h * D + 16 * SPW * wave + 4 * g;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        f16x8 qa[D / 32], ba[2];
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) qa[ks] = ld_perm(sQt, L::LDQ, 16 * ct, 32 * ks, lane);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) ba[ks] = ld_perm(sB, L::LDT, 16 * ct, 32 * ks, lane);
+        f32x4 OT[SPW];
+#pragma unroll
+        for (int sl = 0; sl < SPW; ++sl) OT[sl] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+          for (int sl = 0; sl < SPW; ++sl) OT[sl] = mfma_f16(sop[sl][ks], qa[ks], OT[sl]);
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int sl = 0; sl < SPW; ++sl) {
+            OT[sl] = mfma_f16(uh[sl][ks], ba[ks], OT[sl]);
+            OT[sl] = mfma_f16(ul[sl][ks], ba[ks], OT[sl]);
+          }
+        const int c = 16 * ct + l16;
+        if (c < n) {
+          float* orow = a.o + obase + (int64_t)c * HD;
+#pragma unroll
+          for (int sl = 0; sl < SPW; ++sl) *reinterpret_cast<f32x4*>(orow + 16 * sl) = OT[sl];
+        }
+      }
+      // S^T <- 2^(G_n) S^T + K~^T U, four row tiles per batch
+#pragma unroll
+      for (int kb = 0; kb < KT; kb += 4) {
+        f16x8 ka[4][2];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) ka[t][ks] = ld_perm_swz(sKtT, L::LDT, 16 * (kb + t), 32 * ks, lane);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const f32x4 gam = *reinterpret_cast<const f32x4*>(sGam + 16 * (kb + t) + 4 * g);
+#pragma unroll
+          for (int sl = 0; sl < SPW; ++sl) ST[sl][kb + t] *= gam;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int sl = 0; sl < SPW; ++sl) {
+              ST[sl][kb + t] = mfma_f16(ka[t][ks], uh[sl][ks], ST[sl][kb + t]);
+              ST[sl][kb + t] = mfma_f16(ka[t][ks], ul[sl][ks], ST[sl][kb + t]);
+            }
+        }
+      }
+      // snapshot after this chunk if the sequence position is a multiple of the interval
+      if (a.interval > 0) {
+        const int64_t pos = item.tok_in_seq + (int64_t)ch * C + n;
+        if (pos % a.interval == 0) {
+          const int64_t slot = item.snap_base + pos / a.interval - 1;
+          float* dst = a.snapshots + (slot * a.H + h) * DD;
+#pragma unroll
+          for (int sl = 0; sl < SPW; ++sl)
+#pragma unroll
+            for (int kt = 0; kt < KT; ++kt)
+              *reinterpret_cast<f32x4*>(dst + (16 * (SPW * wave + sl) + l16) * D + 16 * kt + 4 * g) = ST[sl][kt];
+        }
+      }
+      if (has_next) fetch_up(ch + 1);
+    } else if (has_next) {
+      const int n_next = chunk_len(ch + 1);
+      p2(nb, n_next);
+      if (ch + 2 < n_chunks) fetch_raw(ch + 2);
+      p3(nb, n_next);
+      put_w();                                   // W of chunk ch+1 (interval A read chunk ch's)
+    }
+    __syncthreads();
+  }
+
+  if (chain && item.seg == item.n_segs - 1) {
+    float* dst = a.final_state + ((int64_t)item.seq * a.H + h) * DD;
+#pragma unroll
+    for (int sl = 0; sl < SPW; ++sl)
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+        *reinterpret_cast<f32x4*>(dst + (16 * (SPW * wave + sl) + l16) * D + 16 * kt + 4 * g) = ST[sl][kt];
+  }
+}
+
 // Segment scan: for every segmented sequence, head and block of 16 state rows,
 // S_{s+1} = S_s M_s + N_s for s = 0 .. n_segs-2 in fp32, from S_0 = the initial
 // state (or zeros); S_s is stored as the start state of segment s (S_0
@@ -1365,6 +1767,18 @@ hipError_t launch_pass(const PrefillArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_wu_pipe(const PrefillArgs& a, hipStream_t s) {
+  using P = LdsPipe<D>;
+  static_assert(P::TOTAL <= 160 * 1024, "LDS budget");
+  auto kern = prefill_wu_pipe_kernel<D>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, P::TOTAL);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(a.n_items * a.H), dim3(512), P::TOTAL, s, a);
+  return hipGetLastError();
+}
+
 template <int D, bool BF16, bool PK>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
   if (a.seg_chunks == 0) return launch_pass<D, BF16, PK, false, false>(a, s);
@@ -1377,7 +1791,10 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(segment_scan_kernel<D>, dim3(a.num_seqs * a.H * (D / 16)), dim3(256), scan_lds, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = launch_pass<D, BF16, PK, false, true>(a, s);              // pass 3: every segment
+  if constexpr (D == 128 && BF16 && !PK)
+    e = launch_wu_pipe<D>(a, s);                                  // pass 3: every segment
+  else
+    e = launch_pass<D, BF16, PK, false, true>(a, s);
   if (e != hipSuccess || !a.any_whole) return e;
   return launch_pass<D, BF16, PK, false, false>(a, s);          // sequences that are not split
 }
