@@ -438,7 +438,7 @@ def main(argv=None):
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": stored_traffic(w.name),
                      "kernel": "kda_prefill_chunked = build_items + prefill_kernel pass 1 + "
-                               "segment_scan + prefill_kernel pass 3 (automatic segment plan)",
+                               "segment_scan + prefill_wu_pipe_kernel pass 3 (automatic segment plan)",
                      "algorithmic_bytes_per_launch": int(pb), "algorithmic_flops_per_launch": int(pf),
                      "frac_of_measured_copy": round(gbs / ceilings["copy_GBs"], 4),
                      "mfma_tflops": round(tfl, 2), "mfma_frac": round(tfl / MFMA_F16_PEAK_TFLOPS, 4),
