@@ -146,11 +146,14 @@ def test_prefix_split_resume_bitwise():
     assert torch.equal(o[:N], o1) and torch.equal(o[N:], o2) and torch.equal(fin, f2)
 
 
-@pytest.mark.parametrize("segment_tokens", [64, 192, 1024])
+@pytest.mark.parametrize("segment_tokens", [64, 128, 192, 1024])
 @pytest.mark.parametrize("gate", ["scalar", "per_key"])
 def test_segmented_plan_matches_oracle(segment_tokens, gate):
     """Forced segment plans (segment maps, fp32 scan, reruns) on a varlen pack
-    with snapshots and initial states."""
+    with snapshots and initial states. At d=128 with the scalar gate and bf16
+    inputs the reruns are the two-role pass-3 kernel: segments of one chunk
+    (nothing to prepare ahead), two chunks (no chunk after the next) and more,
+    with ragged last segments."""
     dev = device()
     w = custom(f"seg_{segment_tokens}_{gate}", H=2, d=128, lens=(2000, 70, 0, 1280, 64), gate=gate,
                interval=128, seed=16)
