@@ -1202,7 +1202,9 @@ void prefill_kernel(PrefillArgs a) {
 //      producers: Q~ and K~^T of c+1, the fetch of c+2's raw rows, B of c+1,
 //      W of c+1 into LDS (the chain read chunk c's in interval A)
 // The fetches sit where they least delay the chain's o stores, which share
-// the compute unit's vector memory path with them.
+// the compute unit's vector memory path with them. Everything this kernel
+// moves through HBM is touched once (raw rows, stored W and U', o), so those
+// accesses are nontemporal.
 // Every product is the one the other pass-3 form computes, in the same order,
 // so both give the same bits.
 template <int D>
@@ -1308,8 +1310,8 @@ void prefill_wu_pipe_kernel(PrefillArgs a) {
       const int i = pw + NP * j;
       const int row = i * RPI + lane / LPR;
       const uint32_t off = (uint32_t)(row < n ? row : 0) * HDu + 8u * (uint32_t)((lane % LPR) ^ raw_swz<D>(row));
-      carry[j] = *reinterpret_cast<const i32x4*>(kb + off);
-      carry[RI + j] = *reinterpret_cast<const i32x4*>(qb + off);
+      carry[j] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(kb + off));
+      carry[RI + j] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(qb + off));
     }
     // loads in this form are unconditional, with clamped addresses (the
     // rows past the end are masked where they are used): a load under a lane
@@ -1406,7 +1408,7 @@ void prefill_wu_pipe_kernel(PrefillArgs a) {
   auto fetch_w = [&](int ch) __attribute__((always_inline)) {
     const f32x4* rec = reinterpret_cast<const f32x4*>(wu_base + (int64_t)ch * WU_BYTES);
 #pragma unroll
-    for (int j = 0; j < W_PER_T; ++j) wreg[j] = rec[min(ptid + j * NPT, W_VEC - 1)];
+    for (int j = 0; j < W_PER_T; ++j) wreg[j] = __builtin_nontemporal_load(rec + min(ptid + j * NPT, W_VEC - 1));
   };
   auto put_w = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -1421,7 +1423,7 @@ void prefill_wu_pipe_kernel(PrefillArgs a) {
 #pragma unroll
     for (int sl = 0; sl < SPW; ++sl)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) carry[4 * sl + ct] = up[((SPW * wave + sl) * 4 + ct) * 64 + lane];
+      for (int ct = 0; ct < 4; ++ct) carry[4 * sl + ct] = __builtin_nontemporal_load(up + ((SPW * wave + sl) * 4 + ct) * 64 + lane);
   };
 
   // ---- prologue: chunk 0's operands in buffer 0, W(0) in LDS (producers),
@@ -1527,7 +1529,7 @@ void prefill_wu_pipe_kernel(PrefillArgs a) {
         if (c < n) {
           float* orow = a.o + obase + (int64_t)c * HD;
 #pragma unroll
-          for (int sl = 0; sl < SPW; ++sl) *reinterpret_cast<f32x4*>(orow + 16 * sl) = OT[sl];
+          for (int sl = 0; sl < SPW; ++sl) __builtin_nontemporal_store(OT[sl], reinterpret_cast<f32x4*>(orow + 16 * sl));
         }
       }
       // S^T <- 2^(G_n) S^T + K~^T U, four row tiles per batch
