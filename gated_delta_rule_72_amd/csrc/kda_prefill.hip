@@ -1290,7 +1290,8 @@ void prefill_wu_pipe_kernel(PrefillArgs a) {
   // raw q/k rows of one chunk in registers, in the order stage_rows_lds_swz
   // lays them out (instruction i = pw + NP j: rows i RPI + lane / LPR, lane l
   // holds the bytes that land at 1024 i + 16 l); rows past the end are row 0.
-  // alpha: producer 0, token `lane`.
+  // pre_alpha: alpha of token `lane` (clamped to the chunk); every producer
+  // loads it, producer 0 scans it.
   // The same registers carry the chain's U' of the next chunk and the
   // producers' raw rows of the chunk after it (live across a whole chunk on
   // either side): carry[j] = k rows, carry[RI + j] = q rows; chain: U' tile
