@@ -1284,7 +1284,9 @@ void prefill_wu_pipe_kernel(PrefillArgs a) {
       for (int kt = 0; kt < KT; ++kt) ST[sl][kt] = *reinterpret_cast<const f32x4*>(src + row * D + 16 * kt + 4 * g);
     }
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0): see the other form's start state
+  // vmcnt(0): the start state has landed (left pending into the loop, it
+  // makes the compiler wait for all memory traffic at its first use)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 
   // ---- producer side ------------------------------------------------------------
   // raw q/k rows of one chunk in registers, in the order stage_rows_lds_swz
