@@ -287,6 +287,25 @@ __device__ __forceinline__ void bf16x8_to_f32(uint4 w, float (&x)[8]) {
   }
 }
 
+// hi + lo bf16 split of eight values, two per conversion: hi rounds to
+// nearest, lo is the rounded remainder (hi + lo carries about 16 bits).
+__device__ __forceinline__ void split8_bf16(const float (&x)[8], bf16x8& hi, bf16x8& lo) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const bf16x2 hp = __builtin_convertvector(f32x2{x[2 * p], x[2 * p + 1]}, bf16x2);
+    const uint32_t hb = __builtin_bit_cast(uint32_t, hp);
+    const float r0 = x[2 * p] - __uint_as_float(hb << 16);
+    const float r1 = x[2 * p + 1] - __uint_as_float(hb & 0xFFFF0000u);
+    h[p] = hb;
+    l[p] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
+  }
+  hi = __builtin_bit_cast(bf16x8, uint4{h[0], h[1], h[2], h[3]});
+  lo = __builtin_bit_cast(bf16x8, uint4{l[0], l[1], l[2], l[3]});
+}
+
 // A contiguous block of n_kib KiB from HBM into LDS, one KiB per wavefront
 // instruction (lane l moves bytes 16 l .. 16 l + 15 of it).
 template <int NW>
@@ -775,18 +794,20 @@ void prefill_kernel(PrefillArgs a) {
                   for (int e = 0; e < 8; ++e) qraw[e] = (float)qh16[e];
                 }
               }
-              bf16x8 kh, kl, qh, ql, ih, il;
+              float kv[8], qv[8], iv[8];
 #pragma unroll
               for (int e = 0; e < 8; ++e) {
                 const int kk = k0 + e;
                 const float gref = sG[(16 * R) * L::LDG + kk];
                 const float f = exp2_hw(sG[r * L::LDG + kk] - gref);
-                const float kv = kraw[e] * f, qv = qraw[e] * f;
-                const float iv = iraw[e] * exp2_hw(gref - sG[i * L::LDG + kk]);
-                kh[e] = (__bf16)kv; kl[e] = (__bf16)(kv - (float)kh[e]);
-                qh[e] = (__bf16)qv; ql[e] = (__bf16)(qv - (float)qh[e]);
-                ih[e] = (__bf16)iv; il[e] = (__bf16)(iv - (float)ih[e]);
+                kv[e] = kraw[e] * f;
+                qv[e] = qraw[e] * f;
+                iv[e] = iraw[e] * exp2_hw(gref - sG[i * L::LDG + kk]);
               }
+              bf16x8 kh, kl, qh, ql, ih, il;
+              split8_bf16(kv, kh, kl);
+              if constexpr (!MAP) split8_bf16(qv, qh, ql);
+              split8_bf16(iv, ih, il);
               if constexpr (!WU) {
                 accL = mfma_bf16(ih, kh, accL);
                 accL = mfma_bf16(ih, kl, accL);
