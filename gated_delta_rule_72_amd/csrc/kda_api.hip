@@ -43,15 +43,38 @@ constexpr int64_t kChunk = 64;
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-int check_shape(const kda_shape* s) {
+// d_k and d_v each 64 or 128; `square` additionally requires d_k = d_v (the
+// backward pass and the layer front end).
+int check_shape(const kda_shape* s, bool square = false) {
   if (!s) return fail(KDA_ERR_ARG, "shape is NULL");
   if (s->num_heads <= 0) return fail(KDA_ERR_SHAPE, "num_heads must be positive (got %d)", s->num_heads);
-  if (s->d_k != s->d_v || (s->d_k != 64 && s->d_k != 128))
-    return fail(KDA_ERR_SHAPE, "d_k = d_v in {64, 128} required (got d_k=%d d_v=%d)", s->d_k, s->d_v);
+  if ((s->d_k != 64 && s->d_k != 128) || (s->d_v != 64 && s->d_v != 128))
+    return fail(KDA_ERR_SHAPE, "d_k and d_v must each be 64 or 128 (got d_k=%d d_v=%d)", s->d_k, s->d_v);
+  if (square && s->d_k != s->d_v)
+    return fail(KDA_ERR_SHAPE, "this entry point needs d_k = d_v (got d_k=%d d_v=%d)", s->d_k, s->d_v);
   if (s->qkv_dtype != KDA_BF16 && s->qkv_dtype != KDA_F32)
     return fail(KDA_ERR_ARG, "qkv_dtype must be KDA_BF16 or KDA_F32 (got %d)", s->qkv_dtype);
   if (s->gate != KDA_GATE_SCALAR && s->gate != KDA_GATE_PER_KEY)
     return fail(KDA_ERR_ARG, "gate must be KDA_GATE_SCALAR or KDA_GATE_PER_KEY (got %d)", s->gate);
+  if ((int64_t)s->num_heads * 2 > INT32_MAX / 128) return fail(KDA_ERR_SHAPE, "num_heads too large");
+  return KDA_OK;
+}
+
+// Byte ranges [p, p + n) that must not overlap (an output against the inputs).
+struct Range {
+  const void* p;
+  size_t n;
+  const char* name;
+};
+bool overlap(const Range& a, const Range& b) {
+  if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+int check_disjoint(const Range& out, const Range* ins, int n_in) {
+  for (int i = 0; i < n_in; ++i)
+    if (overlap(out, ins[i]))
+      return fail(KDA_ERR_ARG, "%s overlaps %s (outputs must not alias inputs)", out.name, ins[i].name);
   return KDA_OK;
 }
 
@@ -119,6 +142,24 @@ struct PrefillPlan {
   size_t items_off, first_off, maps_off, states_off, wu_off, bytes;
 };
 
+// The kernels run square heads, d = d_k = d_v. Rows of the state evolve
+// independently (each row sees only its own value channel), which gives the
+// two rectangular shapes:
+//   d_v = 2 d_k: every head's d_v rows split into two value heads of d_k rows
+//     (H' = 2H, qk_shift = 1; v, o and the states are laid out alike);
+//   d_k = 2 d_v: the values and states are padded with zero rows to d_k in
+//     the workspace (zero rows stay zero), the outputs copied back.
+struct Geometry {
+  int d;          // kernel head size
+  int H;          // kernel head count
+  int qk_shift;
+  bool pad;       // d_k = 2 d_v
+};
+Geometry geometry(const kda_shape* s) {
+  if (s->d_v == 2 * s->d_k) return {s->d_k, 2 * s->num_heads, 1, false};
+  return {s->d_k, s->num_heads, 0, s->d_k == 2 * s->d_v};
+}
+
 PrefillPlan plan_prefill(const kda_shape* s, int32_t num_seqs, const int64_t* cu,
                          int64_t segment_tokens, int cus) {
   PrefillPlan p{};
@@ -152,7 +193,7 @@ PrefillPlan plan_prefill(const kda_shape* s, int32_t num_seqs, const int64_t* cu
     if (!split) p.any_whole = 1;
   }
   p.n_items = (int32_t)items;
-  const size_t H = (size_t)s->num_heads, DD = (size_t)s->d_k * s->d_v;
+  const size_t H = (size_t)s->num_heads, DD = (size_t)s->d_k * s->d_k;
   size_t off = 0;
   p.items_off = off;
   off += round_up(sizeof(kda::PrefillItem) * (size_t)(items > 0 ? items : 1));
@@ -166,6 +207,40 @@ PrefillPlan plan_prefill(const kda_shape* s, int32_t num_seqs, const int64_t* cu
   if (seg > 0) off += round_up((size_t)items * H * (size_t)seg * kda::wu_chunk_bytes(s->d_k));
   p.bytes = off;
   return p;
+}
+
+// The kernels' plan (square heads of the geometry) followed, for padded heads,
+// by the padded values, initial state, o, final state and snapshots.
+struct FullPlan {
+  Geometry geo;
+  PrefillPlan kern;
+  size_t v_off, init_off, o_off, fin_off, snap_off, bytes;
+};
+FullPlan plan_full(const kda_shape* s, int32_t num_seqs, const int64_t* cu, int64_t interval,
+                   int64_t segment_tokens, int cus) {
+  FullPlan f{};
+  f.geo = geometry(s);
+  kda_shape ks = *s;
+  ks.num_heads = f.geo.H;
+  ks.d_k = ks.d_v = f.geo.d;
+  f.kern = plan_prefill(&ks, num_seqs, cu, segment_tokens, cus);
+  size_t off = f.kern.bytes;
+  if (f.geo.pad) {
+    const size_t T = (size_t)cu[num_seqs], H = (size_t)s->num_heads, d = (size_t)f.geo.d;
+    const size_t es = s->qkv_dtype == KDA_BF16 ? 2 : 4, DD = d * d * sizeof(float);
+    f.v_off = off;
+    off += round_up(T * H * d * es);
+    f.init_off = off;
+    off += round_up((size_t)num_seqs * H * DD);
+    f.o_off = off;
+    off += round_up(T * H * d * sizeof(float));
+    f.fin_off = off;
+    off += round_up((size_t)num_seqs * H * DD);
+    f.snap_off = off;
+    off += round_up((size_t)snapshot_slots(num_seqs, cu, interval) * H * DD);
+  }
+  f.bytes = off;
+  return f;
 }
 
 int check_prefill_args(const kda_shape* shape, int32_t num_seqs, const int64_t* cu,
@@ -270,8 +345,8 @@ int kda_prefill_workspace_size(const kda_shape* shape, int32_t num_seqs,
   if (!bytes) return fail(KDA_ERR_ARG, "bytes is NULL");
   int rc = check_prefill_args(shape, num_seqs, cu_seqlens_host, chunk, snapshot_interval, segment_tokens);
   if (rc != KDA_OK) return rc;
-  *bytes = plan_prefill(shape, num_seqs, cu_seqlens_host, segment_tokens,
-                        segment_tokens < 0 ? device_cu_count() : 0).bytes;
+  *bytes = plan_full(shape, num_seqs, cu_seqlens_host, snapshot_interval, segment_tokens,
+                     segment_tokens < 0 ? device_cu_count() : 0).bytes;
   g_err[0] = '\0';
   return KDA_OK;
 }
@@ -302,8 +377,33 @@ int kda_prefill_chunked(const kda_shape* shape, int32_t num_seqs,
                          {cu_seqlens_dev, 8, "cu_seqlens_dev"}, {workspace, 16, "workspace"}};
   rc = check_align(reqs, (int)(sizeof reqs / sizeof reqs[0]));
   if (rc != KDA_OK) return rc;
-  const PrefillPlan plan = plan_prefill(shape, num_seqs, cu_seqlens_host, segment_tokens,
-                                        segment_tokens < 0 ? device_cu_count() : 0);
+  {
+    // o, the final states and the snapshots are written while the inputs are
+    // still read: none may overlap an input (final_state may only be
+    // initial_state itself) or another output
+    const size_t H = (size_t)shape->num_heads, es = shape->qkv_dtype == KDA_BF16 ? 2 : 4;
+    const size_t tokh = (size_t)T * H, st = (size_t)shape->d_k * shape->d_v * sizeof(float);
+    const size_t a_n = tokh * (shape->gate == KDA_GATE_PER_KEY ? (size_t)shape->d_k : 1) * sizeof(float);
+    const Range ins[] = {{q, tokh * shape->d_k * es, "q"}, {k, tokh * shape->d_k * es, "k"},
+                         {v, tokh * shape->d_v * es, "v"}, {alpha, a_n, "alpha"},
+                         {beta, tokh * sizeof(float), "beta"},
+                         {initial_state, (size_t)num_seqs * H * st, "initial_state"},
+                         {cu_seqlens_dev, ((size_t)num_seqs + 1) * sizeof(int64_t), "cu_seqlens_dev"},
+                         {workspace, workspace_bytes, "workspace"}};
+    const int n_in = (int)(sizeof ins / sizeof ins[0]);
+    const Range ro{o, tokh * shape->d_v * sizeof(float), "o"};
+    const Range rf{final_state, (size_t)num_seqs * H * st, "final_state"};
+    const Range rs{n_snap > 0 ? snapshots : nullptr, (size_t)n_snap * H * st, "snapshots"};
+    if ((rc = check_disjoint(ro, ins, n_in)) != KDA_OK) return rc;
+    if (final_state != initial_state && (rc = check_disjoint(rf, ins, n_in)) != KDA_OK) return rc;
+    if (final_state == initial_state && (rc = check_disjoint(rf, ins + 6, n_in - 6)) != KDA_OK) return rc;
+    if ((rc = check_disjoint(rs, ins, n_in)) != KDA_OK) return rc;
+    const Range outs[] = {ro, rf};
+    if ((rc = check_disjoint(rs, outs, 2)) != KDA_OK) return rc;
+    if ((rc = check_disjoint(ro, outs + 1, 1)) != KDA_OK) return rc;
+  }
+  const FullPlan plan = plan_full(shape, num_seqs, cu_seqlens_host, snapshot_interval, segment_tokens,
+                                  segment_tokens < 0 ? device_cu_count() : 0);
   if (num_seqs > 0 && (!workspace || workspace_bytes < plan.bytes))
     return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", plan.bytes,
                 workspace ? workspace_bytes : (size_t)0);
@@ -317,26 +417,52 @@ int kda_prefill_chunked(const kda_shape* shape, int32_t num_seqs,
     if (rc != KDA_OK) return rc;
   }
 
+  const Geometry& geo = plan.geo;
+  const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  char* ws = static_cast<char*>(workspace);
   kda::PrefillArgs a{};
   a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.init = initial_state;
   a.o = o; a.final_state = final_state; a.snapshots = snaps_dev;
+  hipError_t e = hipSuccess;
+  const size_t H = (size_t)shape->num_heads, es = shape->qkv_dtype == KDA_BF16 ? 2 : 4;
+  const int64_t dsz = geo.d, vrow = (int64_t)shape->d_v, half = (int64_t)shape->d_v * geo.d * 4;
+  if (geo.pad) {
+    // d_k = 2 d_v: values and states padded with zero rows in the workspace
+    a.v = ws + plan.v_off;
+    a.o = reinterpret_cast<float*>(ws + plan.o_off);
+    a.final_state = reinterpret_cast<float*>(ws + plan.fin_off);
+    a.snapshots = n_snap > 0 ? reinterpret_cast<float*>(ws + plan.snap_off) : nullptr;
+    e = kda::launch_copy_rows(v, ws + plan.v_off, T * (int64_t)H, vrow * es, dsz * es, vrow * es, (dsz - vrow) * es, st);
+    if (e == hipSuccess && initial_state) {
+      a.init = reinterpret_cast<const float*>(ws + plan.init_off);
+      e = kda::launch_copy_rows(initial_state, ws + plan.init_off, (int64_t)num_seqs * H, half, 2 * half, half,
+                                half, st);
+    }
+    if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "prefill padding failed: %s", hipGetErrorString(e));
+  }
   a.cu_dev = cu_seqlens_dev;
   a.num_seqs = num_seqs;
-  a.H = shape->num_heads;
+  a.H = geo.H;
+  a.qk_shift = geo.qk_shift;
   a.interval = snapshot_interval;
-  a.seg_chunks = plan.seg_chunks;
-  a.n_items = plan.n_items;
-  char* ws = static_cast<char*>(workspace);
-  a.items = reinterpret_cast<kda::PrefillItem*>(ws + plan.items_off);
-  a.seq_first_item = reinterpret_cast<int32_t*>(ws + plan.first_off);
-  a.seg_maps = plan.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.maps_off) : nullptr;
-  a.seg_states = plan.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.states_off) : nullptr;
-  a.seg_wu = plan.seg_chunks > 0 ? static_cast<void*>(ws + plan.wu_off) : nullptr;
-  a.any_whole = plan.any_whole;
-  hipError_t e = kda::launch_prefill(a, shape->d_k, shape->qkv_dtype == KDA_BF16,
-                                     shape->gate == KDA_GATE_PER_KEY,
-                                     static_cast<hipStream_t>(hip_stream));
+  a.seg_chunks = plan.kern.seg_chunks;
+  a.n_items = plan.kern.n_items;
+  a.items = reinterpret_cast<kda::PrefillItem*>(ws + plan.kern.items_off);
+  a.seq_first_item = reinterpret_cast<int32_t*>(ws + plan.kern.first_off);
+  a.seg_maps = plan.kern.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.kern.maps_off) : nullptr;
+  a.seg_states = plan.kern.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.kern.states_off) : nullptr;
+  a.seg_wu = plan.kern.seg_chunks > 0 ? static_cast<void*>(ws + plan.kern.wu_off) : nullptr;
+  a.any_whole = plan.kern.any_whole;
+  e = kda::launch_prefill(a, geo.d, shape->qkv_dtype == KDA_BF16, shape->gate == KDA_GATE_PER_KEY, st);
   if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "prefill launch failed: %s", hipGetErrorString(e));
+  if (geo.pad) {
+    e = kda::launch_copy_rows(a.o, o, T * (int64_t)H, dsz * 4, vrow * 4, vrow * 4, 0, st);
+    if (e == hipSuccess)
+      e = kda::launch_copy_rows(a.final_state, final_state, (int64_t)num_seqs * H, 2 * half, half, half, 0, st);
+    if (e == hipSuccess && n_snap > 0)
+      e = kda::launch_copy_rows(a.snapshots, snaps_dev, n_snap * (int64_t)H, 2 * half, half, half, 0, st);
+    if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "prefill output copy failed: %s", hipGetErrorString(e));
+  }
   g_err[0] = '\0';
   return KDA_OK;
 }
@@ -361,8 +487,18 @@ int kda_decode_step(const kda_shape* shape, int32_t batch, const void* q, const 
                          {beta, 4, "beta"}, {state, 16, "state"}, {o, 4, "o"}};
   rc = check_align(reqs, (int)(sizeof reqs / sizeof reqs[0]));
   if (rc != KDA_OK) return rc;
+  {
+    const size_t bh = (size_t)batch * shape->num_heads, es = shape->qkv_dtype == KDA_BF16 ? 2 : 4;
+    const size_t a_n = bh * (shape->gate == KDA_GATE_PER_KEY ? (size_t)shape->d_k : 1) * sizeof(float);
+    const Range ins[] = {{q, bh * shape->d_k * es, "q"}, {k, bh * shape->d_k * es, "k"},
+                         {v, bh * shape->d_v * es, "v"}, {alpha, a_n, "alpha"}, {beta, bh * sizeof(float), "beta"},
+                         {state, bh * shape->d_k * shape->d_v * sizeof(float), "state"}};
+    rc = check_disjoint(Range{o, bh * shape->d_v * sizeof(float), "o"}, ins, 6);
+    if (rc == KDA_OK) rc = check_disjoint(ins[5], ins, 5);
+    if (rc != KDA_OK) return rc;
+  }
   kda::DecodeArgs a{q, k, v, alpha, beta, state, o, batch, shape->num_heads};
-  hipError_t e = kda::launch_decode(a, shape->d_k, shape->qkv_dtype == KDA_BF16,
+  hipError_t e = kda::launch_decode(a, shape->d_k, shape->d_v, shape->qkv_dtype == KDA_BF16,
                                     shape->gate == KDA_GATE_PER_KEY,
                                     static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "decode launch failed: %s", hipGetErrorString(e));
@@ -394,8 +530,22 @@ int kda_decode_tokens(const kda_shape* shape, int32_t batch, int32_t n_tok, cons
                          {token_states, 16, "token_states"}, {commit, 4, "commit"}};
   rc = check_align(reqs, (int)(sizeof reqs / sizeof reqs[0]));
   if (rc != KDA_OK) return rc;
+  {
+    const size_t bh = (size_t)batch * shape->num_heads, bnh = bh * (size_t)n_tok;
+    const size_t es = shape->qkv_dtype == KDA_BF16 ? 2 : 4, st = (size_t)shape->d_k * shape->d_v * sizeof(float);
+    const size_t a_n = bnh * (shape->gate == KDA_GATE_PER_KEY ? (size_t)shape->d_k : 1) * sizeof(float);
+    const Range ins[] = {{q, bnh * shape->d_k * es, "q"}, {k, bnh * shape->d_k * es, "k"},
+                         {v, bnh * shape->d_v * es, "v"}, {alpha, a_n, "alpha"}, {beta, bnh * sizeof(float), "beta"},
+                         {commit, (size_t)batch * sizeof(int32_t), "commit"}, {state, bh * st, "state"}};
+    const Range ro{o, bnh * shape->d_v * sizeof(float), "o"}, rt{token_states, bnh * st, "token_states"};
+    rc = check_disjoint(ro, ins, 7);
+    if (rc == KDA_OK) rc = check_disjoint(rt, ins, 7);
+    if (rc == KDA_OK) rc = check_disjoint(ins[6], ins, 6);
+    if (rc == KDA_OK) rc = check_disjoint(ro, &rt, 1);
+    if (rc != KDA_OK) return rc;
+  }
   kda::DecodeArgs a{q, k, v, alpha, beta, state, o, batch, shape->num_heads, n_tok, token_states, commit};
-  hipError_t e = kda::launch_decode_tokens(a, shape->d_k, shape->qkv_dtype == KDA_BF16,
+  hipError_t e = kda::launch_decode_tokens(a, shape->d_k, shape->d_v, shape->qkv_dtype == KDA_BF16,
                                            shape->gate == KDA_GATE_PER_KEY,
                                            static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "decode launch failed: %s", hipGetErrorString(e));
@@ -408,7 +558,7 @@ int kda_layer_front(const kda_shape* shape, int32_t num_seqs, const int64_t* cu_
                     const float* conv_w, const void* conv_state_in, const float* alpha_logit,
                     float alpha_bias, const float* beta_logit, void* q, void* k, void* v, float* alpha,
                     float* beta, void* conv_state_out, void* hip_stream) {
-  int rc = check_shape(shape);
+  int rc = check_shape(shape, true);
   if (rc != KDA_OK) return rc;
   rc = check_cu(num_seqs, cu_seqlens_host);
   if (rc != KDA_OK) return rc;
@@ -474,7 +624,7 @@ int kda_layer_back(const kda_shape* shape, int64_t num_tokens, const float* o, c
 int kda_prefill_backward_workspace_size(const kda_shape* shape, int32_t num_seqs,
                                         const int64_t* cu_seqlens_host, size_t* bytes) {
   if (!bytes) return fail(KDA_ERR_ARG, "bytes is NULL");
-  int rc = check_shape(shape);
+  int rc = check_shape(shape, true);
   if (rc != KDA_OK) return rc;
   rc = check_cu(num_seqs, cu_seqlens_host);
   if (rc != KDA_OK) return rc;
@@ -489,7 +639,7 @@ int kda_prefill_backward(const kda_shape* shape, int32_t num_seqs, const int64_t
                          const float* d_final_state, float* dq, float* dk, float* dv, float* dalpha,
                          float* dbeta, float* d_initial_state, void* workspace, size_t workspace_bytes,
                          void* hip_stream) {
-  int rc = check_shape(shape);
+  int rc = check_shape(shape, true);
   if (rc != KDA_OK) return rc;
   rc = check_cu(num_seqs, cu_seqlens_host);
   if (rc != KDA_OK) return rc;
@@ -505,6 +655,27 @@ int kda_prefill_backward(const kda_shape* shape, int32_t num_seqs, const int64_t
                          {cu_seqlens_dev, 8, "cu_seqlens_dev"}, {workspace, 16, "workspace"}};
   rc = check_align(reqs, (int)(sizeof reqs / sizeof reqs[0]));
   if (rc != KDA_OK) return rc;
+  {
+    // every gradient is written while the inputs are read: no output may
+    // overlap an input or another output, except d_initial_state = d_final_state
+    const size_t H = (size_t)shape->num_heads, d = (size_t)shape->d_k, es = shape->qkv_dtype == KDA_BF16 ? 2 : 4;
+    const size_t tokh = (size_t)T * H, st = (size_t)num_seqs * H * d * d * sizeof(float);
+    const size_t a_n = tokh * (shape->gate == KDA_GATE_PER_KEY ? d : 1) * sizeof(float);
+    const Range ins[] = {{q, tokh * d * es, "q"}, {k, tokh * d * es, "k"}, {v, tokh * d * es, "v"},
+                         {alpha, a_n, "alpha"}, {beta, tokh * sizeof(float), "beta"},
+                         {initial_state, st, "initial_state"}, {d_o, tokh * d * sizeof(float), "d_o"},
+                         {cu_seqlens_dev, ((size_t)num_seqs + 1) * sizeof(int64_t), "cu_seqlens_dev"},
+                         {workspace, workspace_bytes, "workspace"}, {d_final_state, st, "d_final_state"}};
+    const Range outs[] = {{dq, tokh * d * sizeof(float), "dq"}, {dk, tokh * d * sizeof(float), "dk"},
+                          {dv, tokh * d * sizeof(float), "dv"}, {dalpha, a_n, "dalpha"},
+                          {dbeta, tokh * sizeof(float), "dbeta"}, {d_initial_state, st, "d_initial_state"}};
+    for (int i = 0; i < 6 && rc == KDA_OK; ++i) {
+      const bool same = i == 5 && d_initial_state == d_final_state;
+      rc = check_disjoint(outs[i], ins, same ? 9 : 10);
+      if (rc == KDA_OK && i + 1 < 6) rc = check_disjoint(outs[i], outs + i + 1, 5 - i);
+    }
+    if (rc != KDA_OK) return rc;
+  }
   if (num_seqs == 0) {
     g_err[0] = '\0';
     return KDA_OK;

@@ -377,8 +377,11 @@ __global__ __launch_bounds__(D * 4) void scan_kernel(BackwardArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) R[t][i] = (chain == 0 && 16 * t + 4 * gq + i == 16 * w + l16) ? 1.f : 0.f;
   } else {
+    // a split sequence's end gradients all come from seg_end (the last
+    // segment's is d_final, copied there by segment_end_kernel): this launch
+    // writes d_initial, which may be the d_final buffer
     const float* src = nullptr;
-    if (seg + 1 < n_seg) src = a.seg_end + (item * a.H + h) * DD + rowoff;
+    if (n_seg > 1) src = a.seg_end + (item * a.H + h) * DD + rowoff;
     else if (a.d_final) src = a.d_final + ((int64_t)n * a.H + h) * DD + rowoff;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
@@ -483,6 +486,13 @@ __global__ __launch_bounds__(D * 4) void segment_end_kernel(BackwardArgs a) {
   const float* df = a.d_final ? a.d_final + ((int64_t)n * a.H + h) * DD + rowoff : nullptr;
 #pragma unroll
   for (int t = 0; t < NT; ++t) R[t] = df ? *reinterpret_cast<const f32x4*>(df + 16 * t + 4 * gq) : f32x4{0.f, 0.f, 0.f, 0.f};
+  {
+    // the last segment's own slot (otherwise unused) takes d_final, so that the
+    // output scan never reads d_final while it writes d_initial
+    float* e = a.seg_end + ((ib + ns - 1) * a.H + h) * DD + rowoff;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4*>(e + 16 * t + 4 * gq) = R[t];
+  }
   for (int64_t s = ns - 1; s >= 1; --s) {
     // maps are stored as the scan stores dS: element (r, c) of M at [c * D + r]
     const float* M = a.seg_maps + ((ib + s) * a.H + h) * 2 * DD;

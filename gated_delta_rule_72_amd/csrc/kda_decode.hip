@@ -19,12 +19,12 @@
 // rekurencyjny zmienia przy serwowaniu", item 2) and the state after a chosen
 // prefix goes back to HBM.
 //
-// Mapping (D = d_k = d_v in {64, 128}): one workgroup per (sequence, head),
-// D/32 wavefronts, 32 state rows per wavefront. A row is D/4 lanes wide (one
-// 16-byte float4 per lane), so a wavefront holds G = 256/D rows side by side
-// and every load instruction moves G consecutive rows (1 KiB). Each lane group
+// Mapping (d_k = DK, d_v = DV, each 64 or 128): one workgroup per (sequence,
+// head), DV/32 wavefronts, 32 state rows per wavefront. A row is DK/4 lanes
+// wide (one 16-byte float4 per lane), so a wavefront holds G = 256/DK rows side
+// by side and every load instruction moves G consecutive rows (1 KiB). Each lane group
 // keeps R = 32/G rows in registers and finishes all 2R dot products of its
-// rows with one butterfly reduce-scatter: log2(D/4) shuffle steps in which
+// rows with one butterfly reduce-scatter: log2(DK/4) shuffle steps in which
 // the number of live partial sums halves, leaving lane j of the group with
 // the full sum of value j.
 #include "kda_internal.h"
@@ -82,9 +82,9 @@ __device__ __forceinline__ float group_allreduce(float x) {
 // MULTI: n_tok tokens per sequence ([batch, n_tok, H, d] inputs), the state
 // kept in registers between them; the state after token t goes to
 // token_states (if given) and, for t + 1 == commit, back to `state`.
-template <int D, bool BF16, bool PER_KEY, bool MULTI>
-__global__ __launch_bounds__(D * 2) void decode_kernel(DecodeArgs a) {
-  constexpr int LPR = D / 4;      // lanes per state row
+template <int DK, int DV, bool BF16, bool PER_KEY, bool MULTI>
+__global__ __launch_bounds__(DV * 2) void decode_kernel(DecodeArgs a) {
+  constexpr int LPR = DK / 4;     // lanes per state row
   constexpr int G = 64 / LPR;     // rows side by side in a wavefront
   constexpr int R = 32 / G;       // rows per lane group
   static_assert(2 * R == LPR, "one reduced value per lane");
@@ -97,12 +97,12 @@ __global__ __launch_bounds__(D * 2) void decode_kernel(DecodeArgs a) {
   const int li = lane % LPR;      // lane within the group; owns columns 4li..4li+3
 
   // rows of this lane group: wave*32 + r*G + g, r = 0..R-1
-  float* state = a.state + (int64_t)bh * D * D;
+  float* state = a.state + (int64_t)bh * DV * DK;
   f32x4 s[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int row = wave * 32 + r * G + g;
-    s[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(state + (int64_t)row * D + 4 * li));
+    s[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(state + (int64_t)row * DK + 4 * li));
   }
 
   const int n_tok = MULTI ? a.n_tok : 1;
@@ -119,25 +119,25 @@ __global__ __launch_bounds__(D * 2) void decode_kernel(DecodeArgs a) {
   // a token's inputs; the next token's are fetched while the current one runs
   auto load_token = [&](int t) {
     const int64_t tok = MULTI ? ((int64_t)b * n_tok + t) * a.H + h : bh;   // (sequence, token, head)
-    const int64_t vec_off = tok * D;
+    const int64_t k_off = tok * DK;
     TokenIn x;
-    x.k = load4<BF16>(a.k, vec_off + 4 * li);
-    x.q = load4<BF16>(a.q, vec_off + 4 * li);
+    x.k = load4<BF16>(a.k, k_off + 4 * li);
+    x.q = load4<BF16>(a.q, k_off + 4 * li);
     if constexpr (PER_KEY) {
-      x.a = *reinterpret_cast<const f32x4*>(a.alpha + vec_off + 4 * li);
+      x.a = *reinterpret_cast<const f32x4*>(a.alpha + k_off + 4 * li);
     } else {
       const float al = a.alpha[tok];
       x.a = f32x4{al, al, al, al};
     }
     x.beta = a.beta[tok];
-    x.v = load1<BF16>(a.v, vec_off + my_row);
+    x.v = load1<BF16>(a.v, tok * DV + my_row);
     return x;
   };
   TokenIn next = load_token(0);
 
   for (int t = 0; t < n_tok; ++t) {
     const int64_t tok = MULTI ? ((int64_t)b * n_tok + t) * a.H + h : bh;   // (sequence, token, head)
-    const int64_t vec_off = tok * D;
+    const int64_t v_off = tok * DV;
     const TokenIn cur = next;
     if (MULTI && t + 1 < n_tok) next = load_token(t + 1);
     const f32x4 kv = cur.k, qv = cur.q, av = cur.a;
@@ -158,11 +158,11 @@ __global__ __launch_bounds__(D * 2) void decode_kernel(DecodeArgs a) {
     float u = 0.f;
     if ((li & 1) == 0) u = beta * (cur.v - red);
     const float u_pair = xor_lane<1>(u);
-    if (li & 1) a.o[vec_off + my_row] = red + u_pair * kq;
+    if (li & 1) a.o[v_off + my_row] = red + u_pair * kq;
 
     // u of row r sits in lane 2r of each lane group: read it wave-wide and keep
     // the copy of this lane's group
-    float* snap = (MULTI && a.token_states) ? a.token_states + tok * D * D : nullptr;
+    float* snap = (MULTI && a.token_states) ? a.token_states + tok * DV * DK : nullptr;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float ur = 0.f;
@@ -174,37 +174,39 @@ __global__ __launch_bounds__(D * 2) void decode_kernel(DecodeArgs a) {
       s[r] = s[r] + ur * kv;
       const int row = wave * 32 + r * G + g;
       if (MULTI && snap)
-        __builtin_nontemporal_store(s[r], reinterpret_cast<f32x4*>(snap + (int64_t)row * D + 4 * li));
+        __builtin_nontemporal_store(s[r], reinterpret_cast<f32x4*>(snap + (int64_t)row * DK + 4 * li));
       if (t + 1 == commit)
-        __builtin_nontemporal_store(s[r], reinterpret_cast<f32x4*>(state + (int64_t)row * D + 4 * li));
+        __builtin_nontemporal_store(s[r], reinterpret_cast<f32x4*>(state + (int64_t)row * DK + 4 * li));
     }
   }
 }
 
-template <int D, bool BF16, bool PK, bool MULTI>
+template <int DK, int DV, bool BF16, bool PK, bool MULTI>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((decode_kernel<D, BF16, PK, MULTI>), dim3(a.batch * a.H), dim3(D * 2), 0, s, a);
+  hipLaunchKernelGGL((decode_kernel<DK, DV, BF16, PK, MULTI>), dim3(a.batch * a.H), dim3(DV * 2), 0, s, a);
   return hipGetLastError();
 }
 
+template <int DK, int DV, bool MULTI>
+hipError_t launch_dt(const DecodeArgs& a, bool bf16, bool per_key, hipStream_t s) {
+  if (bf16) return per_key ? launch_t<DK, DV, true, true, MULTI>(a, s) : launch_t<DK, DV, true, false, MULTI>(a, s);
+  return per_key ? launch_t<DK, DV, false, true, MULTI>(a, s) : launch_t<DK, DV, false, false, MULTI>(a, s);
+}
+
 template <bool MULTI>
-hipError_t launch_any(const DecodeArgs& a, int d, bool bf16, bool per_key, hipStream_t s) {
-  if (d == 64) {
-    if (bf16) return per_key ? launch_t<64, true, true, MULTI>(a, s) : launch_t<64, true, false, MULTI>(a, s);
-    return per_key ? launch_t<64, false, true, MULTI>(a, s) : launch_t<64, false, false, MULTI>(a, s);
-  }
-  if (bf16) return per_key ? launch_t<128, true, true, MULTI>(a, s) : launch_t<128, true, false, MULTI>(a, s);
-  return per_key ? launch_t<128, false, true, MULTI>(a, s) : launch_t<128, false, false, MULTI>(a, s);
+hipError_t launch_any(const DecodeArgs& a, int dk, int dv, bool bf16, bool per_key, hipStream_t s) {
+  if (dk == 64) return dv == 64 ? launch_dt<64, 64, MULTI>(a, bf16, per_key, s) : launch_dt<64, 128, MULTI>(a, bf16, per_key, s);
+  return dv == 64 ? launch_dt<128, 64, MULTI>(a, bf16, per_key, s) : launch_dt<128, 128, MULTI>(a, bf16, per_key, s);
 }
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, bool per_key, hipStream_t s) {
-  return launch_any<false>(a, d, bf16, per_key, s);
+hipError_t launch_decode(const DecodeArgs& a, int dk, int dv, bool bf16, bool per_key, hipStream_t s) {
+  return launch_any<false>(a, dk, dv, bf16, per_key, s);
 }
 
-hipError_t launch_decode_tokens(const DecodeArgs& a, int d, bool bf16, bool per_key, hipStream_t s) {
-  return launch_any<true>(a, d, bf16, per_key, s);
+hipError_t launch_decode_tokens(const DecodeArgs& a, int dk, int dv, bool bf16, bool per_key, hipStream_t s) {
+  return launch_any<true>(a, dk, dv, bf16, per_key, s);
 }
 
 }  // namespace kda

@@ -52,8 +52,8 @@ struct DecodeArgs {
   float* token_states;       // [batch, n_tok, H, dv, dk] or null
   const int32_t* commit;     // [batch] tokens to commit to `state`, or null (all)
 };
-hipError_t launch_decode(const DecodeArgs& a, int d, bool bf16, bool per_key, hipStream_t s);
-hipError_t launch_decode_tokens(const DecodeArgs& a, int d, bool bf16, bool per_key, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, int dk, int dv, bool bf16, bool per_key, hipStream_t s);
+hipError_t launch_decode_tokens(const DecodeArgs& a, int dk, int dv, bool bf16, bool per_key, hipStream_t s);
 
 // One unit of prefill work: a contiguous run of chunks of one sequence (the
 // whole sequence, or one segment of it).
@@ -85,8 +85,16 @@ struct PrefillArgs {
                              // LDS layout the map pass leaves it in) and U' (fp32, one
                              // accumulator tile per lane), reused by pass 3
   int32_t any_whole;         // segmented plan: some sequence is not split (needs its own pass)
+  int32_t qk_shift;          // 0, or 1 when d_v = 2 d_k: H counts value heads of d_k state rows,
+                             // and value head h takes q, k, alpha, beta of head h >> 1 of H / 2
 };
 hipError_t launch_prefill(PrefillArgs a, int d, bool bf16, bool per_key, hipStream_t s);
+// Row copy with zero fill, in 16-byte units: for r < n_rows, bytes [0, copy) of
+// dst row r (stride dst_stride) take those of src row r (stride src_stride)
+// and bytes [copy, copy + fill) are zeroed. All sizes and strides are multiples
+// of 16 and both pointers 16-byte aligned.
+hipError_t launch_copy_rows(const void* src, void* dst, int64_t n_rows, int64_t src_stride,
+                            int64_t dst_stride, int64_t copy, int64_t fill, hipStream_t s);
 // Bytes of one chunk's stored W and U' at d = d_k = d_v: W as 64 rows of d + 8
 // fp16 (the LDS row stride, a whole number of KiB), then U' as 64 x d fp32.
 constexpr size_t wu_w_bytes(int d) { return (size_t)64 * (d + 8) * 2; }

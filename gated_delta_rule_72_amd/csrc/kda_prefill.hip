@@ -330,44 +330,52 @@ struct ChunkRegs {
 // Every address is a workgroup-uniform base (scalar registers, cheap to
 // recompute per access) plus one 32-bit per-lane offset that does not depend
 // on the loop index, so no per-access offsets are kept live.
+// h is the value head (v, o and the state); q, k, alpha and beta belong to head
+// h >> qk_shift of a.H >> qk_shift (qk_shift = 1: d_v = 2 d_k, each head's state
+// rows split into two value heads of d_k rows that share q, k and the gates).
 template <int D, bool BF16, bool PER_KEY, int NT>
 __device__ __forceinline__ void load_chunk(ChunkRegs<D, BF16, PER_KEY, NT>& R, const PrefillArgs& a,
                                            int64_t tok0, int n, int h, int tid, bool load_v) {
   using CR = ChunkRegs<D, BF16, PER_KEY, NT>;
   constexpr int ROWS_PER_PASS = NT / (D / 8);     // tokens covered by one group pass
-  const int64_t HD = (int64_t)a.H * D;            // elements per token (all heads)
-  const int64_t row0 = (tok0 * a.H + h) * D;      // first element of this chunk and head
+  const int Hq = a.H >> a.qk_shift, hq = h >> a.qk_shift;
+  const int64_t HD = (int64_t)a.H * D;            // v elements per token (all heads)
+  const int64_t HDq = (int64_t)Hq * D;            // q/k/alpha elements per token
+  const int64_t row0 = (tok0 * a.H + h) * D;      // first v element of this chunk and head
+  const int64_t rowq0 = (tok0 * Hq + hq) * D;     // first q/k element
   const int c0 = tid / (D / 8), k8 = tid % (D / 8);
   const uint32_t lane_off = (uint32_t)c0 * (uint32_t)HD + 8u * k8;
+  const uint32_t lane_offq = (uint32_t)c0 * (uint32_t)HDq + 8u * k8;
 #pragma unroll
   for (int j = 0; j < CR::GPT; ++j) {
     const int c = c0 + j * ROWS_PER_PASS;
     const bool valid = c < n;
-    const int64_t ub = row0 + (int64_t)j * ROWS_PER_PASS * HD;   // uniform
+    const int64_t ub = row0 + (int64_t)j * ROWS_PER_PASS * HD;    // uniform
+    const int64_t ubq = rowq0 + (int64_t)j * ROWS_PER_PASS * HDq;
     if constexpr (BF16) {
       R.v[j] = load_group<true>(static_cast<const uint16_t*>(a.v) + ub, lane_off, valid && load_v);
     } else {
-      R.k[j] = load_group<false>(static_cast<const float*>(a.k) + ub, lane_off, valid);
-      R.q[j] = load_group<false>(static_cast<const float*>(a.q) + ub, lane_off, valid);
+      R.k[j] = load_group<false>(static_cast<const float*>(a.k) + ubq, lane_offq, valid);
+      R.q[j] = load_group<false>(static_cast<const float*>(a.q) + ubq, lane_offq, valid);
       R.v[j] = load_group<false>(static_cast<const float*>(a.v) + ub, lane_off, valid && load_v);
     }
   }
   const int wave = tid / 64, lane = tid % 64;
   if constexpr (PER_KEY) {
     const int kcol = tid % D, cb = tid / D;
-    const uint32_t a_off = (uint32_t)(CR::TPB * cb) * (uint32_t)HD + (uint32_t)kcol;
+    const uint32_t a_off = (uint32_t)(CR::TPB * cb) * (uint32_t)HDq + (uint32_t)kcol;
 #pragma unroll
     for (int j = 0; j < CR::TPB; ++j) {
       const int c = CR::TPB * cb + j;
-      const float* ab = a.alpha + row0 + (int64_t)j * HD;          // uniform
+      const float* ab = a.alpha + rowq0 + (int64_t)j * HDq;        // uniform
       R.alpha[j] = c < n ? ab[a_off] : 1.f;
     }
   } else {
-    const float* ab = a.alpha + tok0 * a.H + h;
-    R.alpha[0] = (wave == 0 && lane < n) ? ab[(uint32_t)lane * a.H] : 1.f;
+    const float* ab = a.alpha + tok0 * Hq + hq;
+    R.alpha[0] = (wave == 0 && lane < n) ? ab[(uint32_t)lane * Hq] : 1.f;
   }
-  const float* bb = a.beta + tok0 * a.H + h;
-  R.beta = (wave == 0 && lane < n) ? bb[(uint32_t)lane * a.H] : 0.f;
+  const float* bb = a.beta + tok0 * Hq + hq;
+  R.beta = (wave == 0 && lane < n) ? bb[(uint32_t)lane * Hq] : 0.f;
 }
 
 // Gram tile pairs (R, I), R >= I, as runs of one row block per wavefront:
@@ -546,19 +554,22 @@ void prefill_kernel(PrefillArgs a) {
   __builtin_amdgcn_s_waitcnt(0x0F70);
 
   const int n_chunks = (item.n_tokens + C - 1) / C;
-  const uint32_t HDu = (uint32_t)a.H * D;
+  const uint32_t HDu = (uint32_t)a.H * D;                       // v row stride (elements)
+  const int Hq = a.H >> a.qk_shift, hq = h >> a.qk_shift;       // q/k head (see load_chunk)
+  const uint32_t HDqu = (uint32_t)Hq * D;                       // q/k row stride
   CR regs;
   if (n_chunks > 0) {
     load_chunk<D, BF16, PER_KEY, NT>(regs, a, item.tok_begin, min(C, item.n_tokens), h, tid, v_in_regs);
     if constexpr (BF16) {
       const int64_t row0 = (item.tok_begin * a.H + h) * D;
+      const int64_t rowq0 = (item.tok_begin * Hq + hq) * D;
       if constexpr (v_in_lds)
         stage_rows_lds<D, NW>(static_cast<const uint16_t*>(a.v) + row0, HDu, min(C, item.n_tokens),
                           smem + L::OFF_QT, wave, lane);
-      stage_rows_lds_swz<D, NW>(static_cast<const uint16_t*>(a.k) + row0, HDu, min(C, item.n_tokens),
+      stage_rows_lds_swz<D, NW>(static_cast<const uint16_t*>(a.k) + rowq0, HDqu, min(C, item.n_tokens),
                                 regA + L::A_RK, wave, lane);
       if constexpr (!MAP)
-        stage_rows_lds_swz<D, NW>(static_cast<const uint16_t*>(a.q) + row0, HDu, min(C, item.n_tokens),
+        stage_rows_lds_swz<D, NW>(static_cast<const uint16_t*>(a.q) + rowq0, HDqu, min(C, item.n_tokens),
                                   regA + L::A_RQ, wave, lane);
     }
     if constexpr (BF16) {
@@ -1045,13 +1056,14 @@ void prefill_kernel(PrefillArgs a) {
       load_chunk<D, BF16, PER_KEY, NT>(regs, a, tok0 + C, n_next, h, tid, v_in_regs);
       if constexpr (BF16) {
         const int64_t row0 = ((tok0 + C) * a.H + h) * D;
+        const int64_t rowq0 = ((tok0 + C) * Hq + hq) * D;
         if constexpr (v_in_lds)
           stage_rows_lds<D, NW>(static_cast<const uint16_t*>(a.v) + row0, HDu, n_next, smem + L::OFF_QT,
                             wave, lane);
-        stage_rows_lds_swz<D, NW>(static_cast<const uint16_t*>(a.k) + row0, HDu, n_next, regA + L::A_RK,
+        stage_rows_lds_swz<D, NW>(static_cast<const uint16_t*>(a.k) + rowq0, HDqu, n_next, regA + L::A_RK,
                                   wave, lane);
         if constexpr (!MAP)
-          stage_rows_lds_swz<D, NW>(static_cast<const uint16_t*>(a.q) + row0, HDu, n_next, regA + L::A_RQ,
+          stage_rows_lds_swz<D, NW>(static_cast<const uint16_t*>(a.q) + rowq0, HDqu, n_next, regA + L::A_RQ,
                                     wave, lane);
       }
     }
@@ -1818,14 +1830,38 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (D == 128 && BF16 && !PK)
-    e = launch_wu_pipe<D>(a, s);                                  // pass 3: every segment
+    e = launch_wu_pipe<D>(a, s);                                  // pass 3: every segment (qk_shift is 0 at d = 128)
   else
     e = launch_pass<D, BF16, PK, false, true>(a, s);
   if (e != hipSuccess || !a.any_whole) return e;
   return launch_pass<D, BF16, PK, false, false>(a, s);          // sequences that are not split
 }
 
+// Row copy with zero fill (see launch_copy_rows): one 16-byte piece per thread,
+// blockIdx.y over rows in steps of 65535.
+__global__ __launch_bounds__(256) void copy_rows_kernel(const uint4* src, uint4* dst, int64_t n_rows,
+                                                        int64_t src_stride, int64_t dst_stride, int64_t copy,
+                                                        int64_t fill) {
+  const int64_t piece = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 16-byte piece within the row
+  if (piece >= copy + fill) return;
+  for (int64_t r = blockIdx.y; r < n_rows; r += gridDim.y) {
+    uint4* d = dst + r * dst_stride + piece;
+    if (piece < copy) *d = src[r * src_stride + piece];
+    else *d = uint4{0u, 0u, 0u, 0u};
+  }
+}
+
 }  // namespace
+
+hipError_t launch_copy_rows(const void* src, void* dst, int64_t n_rows, int64_t src_stride, int64_t dst_stride,
+                            int64_t copy, int64_t fill, hipStream_t s) {
+  if (n_rows <= 0 || copy + fill <= 0) return hipSuccess;
+  const int64_t pieces = (copy + fill) / 16;
+  const dim3 grid((unsigned)((pieces + 255) / 256), (unsigned)(n_rows < 65535 ? n_rows : 65535));
+  hipLaunchKernelGGL(copy_rows_kernel, grid, dim3(256), 0, s, static_cast<const uint4*>(src),
+                     static_cast<uint4*>(dst), n_rows, src_stride / 16, dst_stride / 16, copy / 16, fill / 16);
+  return hipGetLastError();
+}
 
 hipError_t launch_prefill(PrefillArgs a, int d, bool bf16, bool per_key, hipStream_t s) {
   hipLaunchKernelGGL(build_items_kernel, dim3(1), dim3(256), 0, s, a);

@@ -96,7 +96,7 @@ def make_shape(num_heads: int, d_k: int, d_v: int, qkv_dtype: torch.dtype, per_k
 
 # ---- the C ABI, name for name ----------------------------------------------
 # The library sees raw pointers, so each binding first checks what a pointer
-# cannot tell it: dtype and contiguity of every tensor passed.
+# cannot tell it: dtype, contiguity, device and shape of every tensor passed.
 
 def _args(fn: str, shape: Optional[KdaShape], **named) -> None:
     """named: name=(tensor or None, expected dtype; "qkv" = the shape's q/k/v dtype)."""
@@ -109,6 +109,37 @@ def _args(fn: str, shape: Optional[KdaShape], **named) -> None:
             raise TypeError(f"{fn}: {name} must be {dt} (got {t.dtype})")
         if not t.is_contiguous():
             raise ValueError(f"{fn}: {name} must be contiguous")
+
+
+def _geom(fn: str, device: torch.device, host_ok=(), **named) -> None:
+    """named: name=(tensor or None, expected shape tuple). Every tensor must be
+    on `device` (the kernels dereference its pointer there); names in host_ok
+    may instead be pinned host memory."""
+    for name, (t, sh) in named.items():
+        if t is not None and tuple(t.shape) != tuple(sh):
+            raise ValueError(f"{fn}: {name} has shape {tuple(t.shape)}, expected {tuple(sh)}")
+    if device.type != "cuda":
+        raise ValueError(f"{fn}: the kernels need GPU tensors (got {device})")
+    for name, (t, sh) in named.items():
+        if t is None:
+            continue
+        if t.device != device:
+            if name in host_ok and t.device.type == "cpu" and (t.numel() == 0 or t.is_pinned()):
+                continue
+            raise ValueError(f"{fn}: {name} is on {t.device}, expected {device}")
+
+
+def _cu_host(fn: str, cu_seqlens_host: torch.Tensor, T: Optional[int] = None) -> torch.Tensor:
+    cu = cu_seqlens_host.to("cpu", torch.int64).contiguous()
+    if cu.dim() != 1 or cu.numel() < 1:
+        raise ValueError(f"{fn}: cu_seqlens must be a 1-D tensor of N+1 offsets")
+    if T is not None and int(cu[-1]) != T:
+        raise ValueError(f"{fn}: cu_seqlens[-1] = {int(cu[-1])} must equal the token count {T}")
+    return cu
+
+
+def _alpha_shape(shape: KdaShape, lead) -> tuple:
+    return tuple(lead) + ((shape.num_heads, shape.d_k) if shape.gate == KDA_GATE_PER_KEY else (shape.num_heads,))
 
 
 F32, I64, I32_ = torch.float32, torch.int64, torch.int32
@@ -149,8 +180,17 @@ def kda_prefill_chunked(shape: KdaShape, cu_seqlens_host: torch.Tensor, cu_seqle
     _args("kda_prefill_chunked", shape, q=(q, "qkv"), k=(k, "qkv"), v=(v, "qkv"), alpha=(alpha, F32),
           beta=(beta, F32), initial_state=(initial_state, F32), o=(o, F32), final_state=(final_state, F32),
           snapshots=(snapshots, F32), cu_seqlens_dev=(cu_seqlens_dev, I64))
-    cu = cu_seqlens_host.to("cpu", torch.int64).contiguous()
+    T = q.shape[0]
+    cu = _cu_host("kda_prefill_chunked", cu_seqlens_host, T)
+    N, H, dk, dv = cu.numel() - 1, shape.num_heads, shape.d_k, shape.d_v
+    n_snap = kda_snapshot_count(cu, snapshot_interval)
     dev = q.device
+    _geom("kda_prefill_chunked", dev, ("snapshots",), q=(q, (T, H, dk)), k=(k, (T, H, dk)), v=(v, (T, H, dv)),
+          alpha=(alpha, _alpha_shape(shape, (T,))), beta=(beta, (T, H)), initial_state=(initial_state, (N, H, dv, dk)),
+          o=(o, (T, H, dv)), final_state=(final_state, (N, H, dv, dk)), snapshots=(snapshots, (n_snap, H, dv, dk)),
+          cu_seqlens_dev=(cu_seqlens_dev, (N + 1,)))
+    if workspace.device != dev:
+        raise ValueError(f"kda_prefill_chunked: workspace is on {workspace.device}, expected {dev}")
     s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream_ptr(dev)
     _check("kda_prefill_chunked", load().kda_prefill_chunked(
         ctypes.byref(shape), cu.numel() - 1, _ptr(cu), _ptr(cu_seqlens_dev), int(chunk),
@@ -162,6 +202,10 @@ def kda_prefill_chunked(shape: KdaShape, cu_seqlens_host: torch.Tensor, cu_seqle
 def kda_decode_step(shape: KdaShape, batch: int, q, k, v, alpha, beta, state, o, stream=None) -> None:
     _args("kda_decode_step", shape, q=(q, "qkv"), k=(k, "qkv"), v=(v, "qkv"), alpha=(alpha, F32),
           beta=(beta, F32), state=(state, F32), o=(o, F32))
+    B, H, dk, dv = int(batch), shape.num_heads, shape.d_k, shape.d_v
+    _geom("kda_decode_step", q.device, q=(q, (B, H, dk)), k=(k, (B, H, dk)), v=(v, (B, H, dv)),
+          alpha=(alpha, _alpha_shape(shape, (B,))), beta=(beta, (B, H)), state=(state, (B, H, dv, dk)),
+          o=(o, (B, H, dv)))
     s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream_ptr(q.device)
     _check("kda_decode_step", load().kda_decode_step(
         ctypes.byref(shape), int(batch), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
@@ -173,6 +217,10 @@ def kda_decode_tokens(shape: KdaShape, batch: int, n_tok: int, q, k, v, alpha, b
     _args("kda_decode_tokens", shape, q=(q, "qkv"), k=(k, "qkv"), v=(v, "qkv"), alpha=(alpha, F32),
           beta=(beta, F32), state=(state, F32), o=(o, F32), token_states=(token_states, F32),
           commit=(commit, I32_))
+    B, n, H, dk, dv = int(batch), int(n_tok), shape.num_heads, shape.d_k, shape.d_v
+    _geom("kda_decode_tokens", q.device, q=(q, (B, n, H, dk)), k=(k, (B, n, H, dk)), v=(v, (B, n, H, dv)),
+          alpha=(alpha, _alpha_shape(shape, (B, n))), beta=(beta, (B, n, H)), state=(state, (B, H, dv, dk)),
+          o=(o, (B, n, H, dv)), token_states=(token_states, (B, n, H, dv, dk)), commit=(commit, (B,)))
     s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream_ptr(q.device)
     _check("kda_decode_tokens", load().kda_decode_tokens(
         ctypes.byref(shape), int(batch), int(n_tok), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta),
@@ -186,7 +234,14 @@ def kda_layer_front(shape: KdaShape, cu_seqlens_host: torch.Tensor, cu_seqlens_d
           conv_state_in=(conv_state_in, "qkv"), alpha_logit=(alpha_logit, F32), beta_logit=(beta_logit, F32),
           q=(q, "qkv"), k=(k, "qkv"), v=(v, "qkv"), alpha=(alpha, F32), beta=(beta, F32),
           conv_state_out=(conv_state_out, "qkv"), cu_seqlens_dev=(cu_seqlens_dev, I64))
-    cu = cu_seqlens_host.to("cpu", torch.int64).contiguous()
+    T = xq.shape[0]
+    cu = _cu_host("kda_layer_front", cu_seqlens_host, T)
+    N, H, d = cu.numel() - 1, shape.num_heads, shape.d_k
+    td = (T, H, d)
+    _geom("kda_layer_front", xq.device, xq=(xq, td), xk=(xk, td), xv=(xv, td), conv_w=(conv_w, (3, H, d, 4)),
+          conv_state_in=(conv_state_in, (N, 3, 3, H, d)), alpha_logit=(alpha_logit, _alpha_shape(shape, (T,))),
+          beta_logit=(beta_logit, (T, H)), q=(q, td), k=(k, td), v=(v, td), alpha=(alpha, _alpha_shape(shape, (T,))),
+          beta=(beta, (T, H)), conv_state_out=(conv_state_out, (N, 3, 3, H, d)), cu_seqlens_dev=(cu_seqlens_dev, (N + 1,)))
     s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream_ptr(xq.device)
     _check("kda_layer_front", load().kda_layer_front(
         ctypes.byref(shape), cu.numel() - 1, _ptr(cu), _ptr(cu_seqlens_dev), _ptr(xq), _ptr(xk), _ptr(xv),
@@ -198,6 +253,9 @@ def kda_layer_back(shape: KdaShape, num_tokens: int, o, g_logit, norm_w, eps: fl
                    stream=None) -> None:
     _args("kda_layer_back", shape, o=(o, F32), g_logit=(g_logit, F32), norm_w=(norm_w, F32),
           out=(out, torch.bfloat16 if out_dtype == KDA_BF16 else F32))
+    rows = (int(num_tokens), shape.num_heads, shape.d_v)
+    _geom("kda_layer_back", o.device, o=(o, rows), g_logit=(g_logit, rows), norm_w=(norm_w, (shape.d_v,)),
+          out=(out, rows))
     s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream_ptr(o.device)
     _check("kda_layer_back", load().kda_layer_back(
         ctypes.byref(shape), int(num_tokens), _ptr(o), _ptr(g_logit), _ptr(norm_w), float(eps), int(out_dtype),
@@ -220,7 +278,16 @@ def kda_prefill_backward(shape: KdaShape, cu_seqlens_host: torch.Tensor, cu_seql
           beta=(beta, F32), initial_state=(initial_state, F32), d_o=(d_o, F32), d_final_state=(d_final_state, F32),
           dq=(dq, F32), dk=(dk, F32), dv=(dv, F32), dalpha=(dalpha, F32), dbeta=(dbeta, F32),
           d_initial_state=(d_initial_state, F32), cu_seqlens_dev=(cu_seqlens_dev, I64))
-    cu = cu_seqlens_host.to("cpu", torch.int64).contiguous()
+    T = q.shape[0]
+    cu = _cu_host("kda_prefill_backward", cu_seqlens_host, T)
+    N, H, dk, dv = cu.numel() - 1, shape.num_heads, shape.d_k, shape.d_v
+    a_sh = _alpha_shape(shape, (T,))
+    _geom("kda_prefill_backward", q.device, q=(q, (T, H, dk)), k=(k, (T, H, dk)), v=(v, (T, H, dv)),
+          alpha=(alpha, a_sh), beta=(beta, (T, H)), initial_state=(initial_state, (N, H, dv, dk)),
+          d_o=(d_o, (T, H, dv)), d_final_state=(d_final_state, (N, H, dv, dk)), dq=(dq, (T, H, dk)),
+          dk=(dk, (T, H, dk)), dv=(dv, (T, H, dv)), dalpha=(dalpha, a_sh), dbeta=(dbeta, (T, H)),
+          d_initial_state=(d_initial_state, (N, H, dv, dk)), cu_seqlens_dev=(cu_seqlens_dev, (N + 1,)),
+          workspace=(workspace, tuple(workspace.shape)))
     s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream_ptr(q.device)
     _check("kda_prefill_backward", load().kda_prefill_backward(
         ctypes.byref(shape), cu.numel() - 1, _ptr(cu), _ptr(cu_seqlens_dev), _ptr(q), _ptr(k), _ptr(v),
@@ -230,6 +297,24 @@ def kda_prefill_backward(shape: KdaShape, cu_seqlens_host: torch.Tensor, cu_seql
 
 
 # ---- convenience wrappers: allocate outputs with torch, then call the ABI ----
+
+def _cu_pair(cu_seqlens: Optional[torch.Tensor], cu_seqlens_host: Optional[torch.Tensor], T: int,
+             dev: torch.device):
+    """(device copy, host copy) of the offsets: one is derived from the other
+    when only one is given, one sequence of T tokens when neither is."""
+    if cu_seqlens_host is None:
+        cu_seqlens_host = (cu_seqlens.to("cpu", torch.int64) if cu_seqlens is not None
+                           else torch.tensor([0, T], dtype=torch.int64))
+    cu_seqlens_host = cu_seqlens_host.to("cpu", torch.int64).contiguous()
+    if cu_seqlens is None:
+        cu_seqlens = cu_seqlens_host.to(dev)
+    cu_seqlens = cu_seqlens.to(dev, torch.int64).contiguous()
+    if cu_seqlens.numel() != cu_seqlens_host.numel():
+        raise ValueError("cu_seqlens and cu_seqlens_host differ in length")
+    if int(cu_seqlens_host[-1]) != T:
+        raise ValueError(f"cu_seqlens[-1] = {int(cu_seqlens_host[-1])} must equal the token count {T}")
+    return cu_seqlens, cu_seqlens_host
+
 
 def _contig(*ts):
     for t in ts:
@@ -262,11 +347,8 @@ def prefill_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: to
     _shapes("prefill_chunked", k=(k, (T, H, dk)), v=(v, (T, H, dv)), beta=(beta, (T, H)),
             alpha=(alpha, (T, H, dk) if alpha.dim() == 3 else (T, H)))
     dev = q.device
-    if cu_seqlens is None:
-        cu_seqlens = torch.tensor([0, T], dtype=torch.int64, device=dev)
-    if cu_seqlens_host is None:
-        cu_seqlens_host = cu_seqlens.to("cpu")
-    cu_dev = cu_seqlens.to(dev, torch.int64).contiguous()
+    cu_seqlens, cu_seqlens_host = _cu_pair(cu_seqlens, cu_seqlens_host, T, dev)
+    cu_dev = cu_seqlens
     N = cu_seqlens_host.numel() - 1
     _contig(q, k, v, alpha, beta, initial_state)
     per_key = alpha.dim() == 3
@@ -336,11 +418,7 @@ def layer_front(xq: torch.Tensor, xk: torch.Tensor, xv: torch.Tensor, conv_w: to
             beta_logit=(beta_logit, (T, H)),
             alpha_logit=(alpha_logit, (T, H, d) if alpha_logit.dim() == 3 else (T, H)))
     dev = xq.device
-    if cu_seqlens is None:
-        cu_seqlens = torch.tensor([0, T], dtype=torch.int64, device=dev)
-    if cu_seqlens_host is None:
-        cu_seqlens_host = cu_seqlens.to("cpu")
-    cu_dev = cu_seqlens.to(dev, torch.int64).contiguous()
+    cu_dev, cu_seqlens_host = _cu_pair(cu_seqlens, cu_seqlens_host, T, dev)
     N = cu_seqlens_host.numel() - 1
     _contig(xq, xk, xv, conv_w, alpha_logit, beta_logit, conv_state)
     shape = make_shape(H, d, d, xq.dtype, alpha_logit.dim() == 3)
@@ -377,11 +455,7 @@ def prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: t
     _shapes("prefill_backward", k=(k, (T, H, dk_)), v=(v, (T, H, dv_)), beta=(beta, (T, H)), d_o=(d_o, (T, H, dv_)),
             alpha=(alpha, (T, H, dk_) if alpha.dim() == 3 else (T, H)))
     dev = q.device
-    if cu_seqlens is None:
-        cu_seqlens = torch.tensor([0, T], dtype=torch.int64, device=dev)
-    if cu_seqlens_host is None:
-        cu_seqlens_host = cu_seqlens.to("cpu")
-    cu_dev = cu_seqlens.to(dev, torch.int64).contiguous()
+    cu_dev, cu_seqlens_host = _cu_pair(cu_seqlens, cu_seqlens_host, T, dev)
     N = cu_seqlens_host.numel() - 1
     _contig(q, k, v, alpha, beta, d_o, initial_state, d_final_state)
     shape = make_shape(H, dk_, dv_, q.dtype, alpha.dim() == 3)

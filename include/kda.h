@@ -22,7 +22,12 @@
  *     alpha: fp32 [T, H] (KDA_GATE_SCALAR) or [T, H, d_k] (KDA_GATE_PER_KEY),
  *     values in (0, 1]. beta: fp32 [T, H] in [0, 1]. States are fp32
  *     [.., H, d_v, d_k] (d_k contiguous). o is fp32 [T, H, d_v].
- *   - Supported: d_k = d_v in {64, 128}; chunk = 64.
+ *   - Supported: d_k and d_v each 64 or 128 (the state is d_v x d_k, page
+ *     "Modele hybrydowe…", section "Atencja liniowa: stan o stałym rozmiarze");
+ *     kda_prefill_backward and kda_layer_front need d_k = d_v (KDA_ERR_SHAPE
+ *     otherwise: their kernels run square heads only); chunk = 64.
+ *   - Outputs must not overlap inputs or each other (KDA_ERR_ARG), except
+ *     where an entry point states an exact alias it allows.
  *   - Alignment: q, k, v, per-key alpha, every state and the prefill's o
  *     16 bytes (8 bytes for bf16 q, k in kda_decode_step); scalar alpha,
  *     beta and the decode steps' o 4 bytes; cu_seqlens_dev 8 bytes;
@@ -41,7 +46,11 @@
  * fp16 MFMA with fp32 accumulation; see kda_prefill_chunked):
  *     |q|, |k| entries <= 16, |v| entries <= 4096, state entries <= 4096, and,
  *     for the per-key gate, within each aligned block of 16 tokens of a chunk
- *     every key channel's decay product stays above 2^-100.
+ *     every key channel's decay product stays above 2^-100 (any alpha above
+ *     0.0131 per token satisfies it). The page's gate is any alpha in (0, 1);
+ *     below this limit a decay factor formed relative to the block's first
+ *     token leaves the fp32 range and the outputs become inf or NaN. The
+ *     library does not read alpha on the host, so it cannot reject such input.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -129,7 +138,8 @@ int kda_prefill_workspace_size(const kda_shape* shape, int32_t num_seqs,
  *   sequences ([n_snap, H, d_v, d_k], see kda_snapshot_count).
  * initial_state: [num_seqs, H, d_v, d_k] or NULL (zeros). May alias
  *   final_state.
- * o: [T, H, d_v] (must not alias inputs); final_state: [num_seqs, H, d_v, d_k];
+ * o: [T, H, d_v]; final_state: [num_seqs, H, d_v, d_k]; neither may overlap
+ *   an input (KDA_ERR_ARG), except final_state = initial_state exactly;
  * snapshots: NULL iff the slot count is 0. Device memory, or pinned host
  *   memory (hipHostMalloc; torch pin_memory=True): the kernels then write the
  *   snapshot states over the bus while the prefill runs, which offloads them
@@ -138,6 +148,11 @@ int kda_prefill_workspace_size(const kda_shape* shape, int32_t num_seqs,
  *   planning host memory for checkpoints). Pageable host memory is rejected
  *   with KDA_ERR_ARG.
  * workspace: device memory of at least kda_prefill_workspace_size bytes.
+ * Rectangular heads: rows of the state evolve independently (row i sees only
+ *   value channel i), so d_v = 2 d_k runs each head as two value heads of d_k
+ *   rows sharing q, k and the gates, and d_k = 2 d_v pads v and the states
+ *   with zero rows to d_k inside the workspace (zero rows stay zero) and
+ *   copies o, the final states and the snapshots back.
  */
 int kda_prefill_chunked(const kda_shape* shape, int32_t num_seqs,
                         const int64_t* cu_seqlens_host, const int64_t* cu_seqlens_dev,
@@ -255,7 +270,9 @@ int kda_prefill_backward_workspace_size(const kda_shape* shape, int32_t num_seqs
  * decay over any 32 consecutive tokens is at least 2^-120 per channel, so the
  * decay factors relative to the chunk's middle row stay inside fp32.
  * Errors as kda_prefill_chunked; KDA_ERR_WORKSPACE if workspace_bytes is below
- * kda_prefill_backward_workspace_size. num_seqs == 0 is a no-op. */
+ * kda_prefill_backward_workspace_size. num_seqs == 0 is a no-op.
+ * d_initial_state may be the d_final_state buffer (it is written after every
+ * read of d_final_state); no other output may overlap an input. */
 int kda_prefill_backward(const kda_shape* shape, int32_t num_seqs,
                          const int64_t* cu_seqlens_host, const int64_t* cu_seqlens_dev,
                          const void* q, const void* k, const void* v,

@@ -51,7 +51,7 @@ def check_prefill(inp: dict, outs, interval: int, heads=None, o_tol=O_TOL, state
 
 
 def custom(name, H, d, lens, gate="per_key", dtype="bf16", s0_std=0.02, interval=0, seed=0,
-           alpha_bias=5.0, alpha_std=1.0):
-    return wl.Workload(name, H=H, dk=d, dv=d, seq_lens=tuple(lens), dtype=dtype, gate=gate,
+           alpha_bias=5.0, alpha_std=1.0, dv=None):
+    return wl.Workload(name, H=H, dk=d, dv=d if dv is None else dv, seq_lens=tuple(lens), dtype=dtype, gate=gate,
                        alpha_bias=alpha_bias, alpha_std=alpha_std, s0_std=s0_std, interval=interval,
                        seed=seed)

@@ -108,7 +108,7 @@ def test_workspace_size_plans(K):
 
 
 @pytest.mark.parametrize("field,value,code", [
-    ("d_k", 96, "KDA_ERR_SHAPE"), ("d_v", 64, "KDA_ERR_SHAPE"), ("num_heads", 0, "KDA_ERR_SHAPE"),
+    ("d_k", 96, "KDA_ERR_SHAPE"), ("d_v", 96, "KDA_ERR_SHAPE"), ("num_heads", 0, "KDA_ERR_SHAPE"),
     ("qkv_dtype", 7, "KDA_ERR_ARG"), ("gate", 2, "KDA_ERR_ARG")])
 def test_bad_shapes_rejected(K, field, value, code):
     sh = K.make_shape(2, 128, 128, torch.bfloat16, False)
@@ -134,8 +134,9 @@ def _fake(addr):
 def _prefill_raw(K, sh, cu, ptrs, ws_bytes, interval=0, seg=0):
     cu = cu.contiguous()
     lib = K.load()
-    p = dict(cu_dev=0x10000, q=0x20000, k=0x30000, v=0x40000, alpha=0x50000, beta=0x60000, init=None,
-             o=0x70000, fin=0x80000, snaps=None, ws=0x90000)
+    # fake addresses 16 MiB apart: far enough that no two buffers overlap
+    p = dict(cu_dev=0x1000000, q=0x2000000, k=0x3000000, v=0x4000000, alpha=0x5000000, beta=0x6000000, init=None,
+             o=0x7000000, fin=0x8000000, snaps=None, ws=0x9000000)
     p.update(ptrs)
     f = lambda n: None if p[n] is None else _fake(p[n])  # noqa: E731
     return lib.kda_prefill_chunked(ctypes.byref(sh), cu.numel() - 1, ctypes.c_void_p(cu.data_ptr()),
@@ -149,11 +150,11 @@ def test_prefill_host_rejections(K):
     sh = K.make_shape(2, 64, 64, torch.bfloat16, True)
     cu = torch.tensor([0, 100, 300], dtype=torch.int64)
     need = K.kda_prefill_workspace_size(sh, cu, 64, 0, 0)
-    assert _prefill_raw(K, sh, cu, {"q": 0x20008}, need) == K.KDA_ERR_ALIGN
+    assert _prefill_raw(K, sh, cu, {"q": 0x2000008}, need) == K.KDA_ERR_ALIGN
     assert "q" in K.kda_last_error()
-    assert _prefill_raw(K, sh, cu, {"alpha": 0x50004}, need) == K.KDA_ERR_ALIGN   # per-key: 16 B
-    assert _prefill_raw(K, sh, cu, {"fin": 0x80004}, need) == K.KDA_ERR_ALIGN
-    assert _prefill_raw(K, sh, cu, {"o": 0x70004}, need) == K.KDA_ERR_ALIGN       # o: 16 B (row stores)
+    assert _prefill_raw(K, sh, cu, {"alpha": 0x5000004}, need) == K.KDA_ERR_ALIGN   # per-key: 16 B
+    assert _prefill_raw(K, sh, cu, {"fin": 0x8000004}, need) == K.KDA_ERR_ALIGN
+    assert _prefill_raw(K, sh, cu, {"o": 0x7000004}, need) == K.KDA_ERR_ALIGN       # o: 16 B (row stores)
     assert "o" in K.kda_last_error()
     assert _prefill_raw(K, sh, cu, {"q": None}, need) == K.KDA_ERR_ARG
     assert _prefill_raw(K, sh, cu, {"fin": None}, need) == K.KDA_ERR_ARG
@@ -165,10 +166,35 @@ def test_prefill_host_rejections(K):
     assert "snapshot" in K.kda_last_error()
     # scalar gate needs only 4-byte alpha
     sh_s = K.make_shape(2, 64, 64, torch.bfloat16, False)
-    assert _prefill_raw(K, sh_s, cu, {"alpha": 0x50004, "q": 0x20008}, need) == K.KDA_ERR_ALIGN
+    assert _prefill_raw(K, sh_s, cu, {"alpha": 0x5000004, "q": 0x2000008}, need) == K.KDA_ERR_ALIGN
     assert "q" in K.kda_last_error()
+    # outputs must not overlap inputs (o over k; final state over q); the final
+    # state may be the initial state itself, but not overlap it partially
+    assert _prefill_raw(K, sh, cu, {"o": 0x3000000}, need) == K.KDA_ERR_ARG
+    assert "overlaps" in K.kda_last_error() and "o" in K.kda_last_error()
+    assert _prefill_raw(K, sh, cu, {"fin": 0x2000010}, need) == K.KDA_ERR_ARG
+    assert _prefill_raw(K, sh, cu, {"init": 0xA000000, "fin": 0xA000010}, need) == K.KDA_ERR_ARG
     # nothing to do: no sequences
     assert _prefill_raw(K, sh, torch.tensor([0], dtype=torch.int64), {}, 0) == K.KDA_OK
+
+
+def test_rectangular_heads_plan(K):
+    """d_v = 2 d_k runs as twice the value heads of d_k rows (same plan as a
+    square problem with 2H heads); d_k = 2 d_v pads the values and states to
+    d_k rows in the workspace."""
+    cu = torch.tensor([0, 300, 700], dtype=torch.int64)
+    wide = K.kda_prefill_workspace_size(K.make_shape(3, 64, 128, torch.bfloat16, True), cu, 64, 64, 0)
+    sq = K.kda_prefill_workspace_size(K.make_shape(6, 64, 64, torch.bfloat16, True), cu, 64, 64, 0)
+    assert wide == sq
+    narrow = K.kda_prefill_workspace_size(K.make_shape(3, 128, 64, torch.bfloat16, True), cu, 64, 64, 0)
+    base = K.kda_prefill_workspace_size(K.make_shape(3, 128, 128, torch.bfloat16, True), cu, 64, 64, 0)
+    T, H, n_snap = 700, 3, 4 + 6
+    padded = T * H * 128 * 2 + T * H * 128 * 4 + (2 * 2 + n_snap) * H * 128 * 128 * 4
+    assert base + padded <= narrow <= base + padded + 6 * 256
+    # the backward and the layer front end need d_k = d_v
+    with pytest.raises(K.KdaError) as e:
+        K.kda_prefill_backward_workspace_size(K.make_shape(3, 64, 128, torch.bfloat16, True), cu)
+    assert e.value.code == K.KDA_ERR_SHAPE
 
 
 def test_decode_host_rejections(K):
@@ -176,7 +202,7 @@ def test_decode_host_rejections(K):
     f = _fake
 
     def call(sh, batch, **kw):
-        p = dict(q=0x1000, k=0x2000, v=0x3000, alpha=0x4000, beta=0x5000, state=0x6000, o=0x7000)
+        p = dict(q=0x100000, k=0x200000, v=0x300000, alpha=0x400000, beta=0x500000, state=0x600000, o=0x700000)
         p.update(kw)
         a = [None if p[n] is None else f(p[n]) for n in ("q", "k", "v", "alpha", "beta", "state", "o")]
         return lib.kda_decode_step(ctypes.byref(sh), batch, *a, None)
@@ -186,19 +212,22 @@ def test_decode_host_rejections(K):
     assert call(bf, 0) == K.KDA_OK                      # empty batch: nothing enqueued
     assert call(bf, -1) == K.KDA_ERR_ARG
     assert call(bf, 2, state=None) == K.KDA_ERR_ARG
-    assert call(bf, 2, q=0x1004) == K.KDA_ERR_ALIGN     # bf16 q: 8 B
-    assert call(fp, 2, q=0x1008) == K.KDA_ERR_ALIGN     # fp32 q: 16 B
-    assert call(bf, 2, state=0x6008) == K.KDA_ERR_ALIGN
-    assert call(bf, 2, alpha=0x4004) == K.KDA_ERR_ALIGN  # per-key alpha: 16 B
-    bad = K.make_shape(4, 64, 128, torch.bfloat16, True)
+    assert call(bf, 2, q=0x100004) == K.KDA_ERR_ALIGN     # bf16 q: 8 B
+    assert call(fp, 2, q=0x100008) == K.KDA_ERR_ALIGN     # fp32 q: 16 B
+    assert call(bf, 2, state=0x600008) == K.KDA_ERR_ALIGN
+    assert call(bf, 2, alpha=0x400004) == K.KDA_ERR_ALIGN  # per-key alpha: 16 B
+    bad = K.make_shape(4, 96, 128, torch.bfloat16, True)
     assert call(bad, 2) == K.KDA_ERR_SHAPE
+    # o must not overlap the state or an input (B=2, H=4, d=128: state 512 KiB)
+    assert call(bf, 2, o=0x600000 + 4096) == K.KDA_ERR_ARG and "overlaps" in K.kda_last_error()
+    assert call(bf, 2, state=0x100000) == K.KDA_ERR_ARG
 
 
 def test_decode_tokens_host_rejections(K):
     lib = K.load()
 
     def call(sh, batch, n, **kw):
-        p = dict(q=0x1000, k=0x2000, v=0x3000, alpha=0x4000, beta=0x5000, state=0x6000, o=0x7000,
+        p = dict(q=0x100000, k=0x200000, v=0x300000, alpha=0x400000, beta=0x500000, state=0x600000, o=0x700000,
                  ts=None, commit=None)
         p.update(kw)
         a = [None if p[x] is None else _fake(p[x]) for x in ("q", "k", "v", "alpha", "beta", "state", "o", "ts",
@@ -209,8 +238,8 @@ def test_decode_tokens_host_rejections(K):
     assert call(bf, 0, 4) == K.KDA_OK and call(bf, 3, 0) == K.KDA_OK      # nothing to do
     assert call(bf, 2, -1) == K.KDA_ERR_ARG
     assert call(bf, 2, 4, o=None) == K.KDA_ERR_ARG
-    assert call(bf, 2, 4, ts=0x8008) == K.KDA_ERR_ALIGN
-    assert call(bf, 2, 4, commit=0x9002) == K.KDA_ERR_ALIGN
+    assert call(bf, 2, 4, ts=0x800008) == K.KDA_ERR_ALIGN
+    assert call(bf, 2, 4, commit=0x900002) == K.KDA_ERR_ALIGN
     assert call(bf, 1 << 20, 1 << 10) == K.KDA_ERR_SHAPE
 
 
@@ -267,8 +296,9 @@ def test_backward_host_rejections(K):
     assert need > 0
 
     def call(shape, cu_h, ws_bytes, **kw):
-        p = dict(cu_dev=0x100, q=0x1000, k=0x2000, v=0x3000, a=0x4000, b=0x5000, init=None, do=0x6000, df=None,
-                 dq=0x7000, dk=0x8000, dv=0x9000, da=0xA000, db=0xB000, di=None, ws=0x100000)
+        p = dict(cu_dev=0x100, q=0x1000000, k=0x2000000, v=0x3000000, a=0x4000000, b=0x5000000, init=None,
+                 do=0x6000000, df=None, dq=0x7000000, dk=0x8000000, dv=0x9000000, da=0xA000000, db=0xB000000, di=None,
+                 ws=0x10000000)
         p.update(kw)
         f = lambda n: None if p[n] is None else _fake(p[n])  # noqa: E731
         return lib.kda_prefill_backward(ctypes.byref(shape), cu_h.numel() - 1,
@@ -281,15 +311,19 @@ def test_backward_host_rejections(K):
     assert call(sh, cu, need, do=None) == K.KDA_ERR_ARG
     assert call(sh, cu, need, da=None) == K.KDA_ERR_ARG
     assert call(sh, cu, need, cu_dev=None) == K.KDA_ERR_ARG
-    assert call(sh, cu, need, q=0x1008) == K.KDA_ERR_ALIGN                           # 16 B
-    assert call(sh, cu, need, a=0x4004) == K.KDA_ERR_ALIGN                           # per-key alpha: 16 B
-    assert call(sh, cu, need, df=0xC008) == K.KDA_ERR_ALIGN
-    assert call(sh, cu, need, di=0xD004) == K.KDA_ERR_ALIGN
+    assert call(sh, cu, need, q=0x1000008) == K.KDA_ERR_ALIGN                           # 16 B
+    assert call(sh, cu, need, a=0x4000004) == K.KDA_ERR_ALIGN                           # per-key alpha: 16 B
+    assert call(sh, cu, need, df=0xC000008) == K.KDA_ERR_ALIGN
+    assert call(sh, cu, need, di=0xD000004) == K.KDA_ERR_ALIGN
     assert call(sh, cu, need - 1) == K.KDA_ERR_WORKSPACE
     assert call(sh, cu, need, ws=None) == K.KDA_ERR_WORKSPACE
     assert "workspace" in K.kda_last_error()
     bad = K.make_shape(2, 64, 128, torch.bfloat16, True)
     assert call(bad, cu, need) == K.KDA_ERR_SHAPE
+    # gradients must not overlap the inputs or each other; d_initial may only be d_final itself
+    assert call(sh, cu, need, dq=0x2000000) == K.KDA_ERR_ARG and "overlaps" in K.kda_last_error()
+    assert call(sh, cu, need, db=0x9000000 + 64) == K.KDA_ERR_ARG
+    assert call(sh, cu, need, df=0xC000000, di=0xC000010) == K.KDA_ERR_ARG
     # the plan grows with the work: more chunks, more workspace
     more = K.kda_prefill_backward_workspace_size(sh, torch.tensor([0, 100, 300, 1000], dtype=torch.int64))
     assert more > need
@@ -316,6 +350,24 @@ def test_binding_checks_dtypes_and_shapes(K):
     qb = q.to(torch.bfloat16)
     with pytest.raises(ValueError, match="beta"):
         K.prefill_chunked(qb, qb, qb, f32(5, 2), f32(5, 3))
+    # host tensors would hand host pointers to the kernels
+    with pytest.raises(ValueError, match="GPU"):
+        K.kda_decode_step(sh, 5, qb, qb, qb, f32(5, 2), f32(5, 2), f32(5, 2, 64, 64), f32(5, 2, 64))
+    # the offsets must describe exactly the tokens given
+    with pytest.raises(ValueError, match="cu_seqlens"):
+        K.prefill_chunked(qb, qb, qb, f32(5, 2), f32(5, 2), cu_seqlens_host=torch.tensor([0, 2, 3]))
+    with pytest.raises(ValueError, match="cu_seqlens"):
+        K.prefill_chunked(qb, qb, qb, f32(5, 2), f32(5, 2), cu_seqlens=torch.tensor([0, 5]),
+                          cu_seqlens_host=torch.tensor([0, 2, 5]))
+    # low-level binding: state and offsets are checked against the shape
+    shp = K.make_shape(2, 64, 64, torch.bfloat16, False)
+    cu = torch.tensor([0, 2, 5])
+    ws = torch.zeros(16, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="initial_state"):
+        K.kda_prefill_chunked(shp, cu, cu, qb, qb, qb, f32(5, 2), f32(5, 2), f32(1, 2, 64, 64), f32(5, 2, 64),
+                              f32(2, 2, 64, 64), None, ws)
+    with pytest.raises(ValueError, match="state"):
+        K.kda_decode_step(shp, 5, qb, qb, qb, f32(5, 2), f32(5, 2), f32(4, 2, 64, 64), f32(5, 2, 64))
 
 
 def test_input_generators_keep_fp32_under_another_default_dtype():

@@ -39,6 +39,20 @@ def test_decode_small(d, gate, dtype):
     _check_decode(di, s0, o)
 
 
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64)])
+@pytest.mark.parametrize("gate", ["scalar", "per_key"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_decode_rectangular_heads(dk, dv, gate, dtype):
+    """d_k != d_v: d_v/32 wavefronts of 32 state rows, rows d_k/4 lanes wide."""
+    dev = device()
+    w = wl.DECODE.with_(dk=dk, dv=dv, H=3, seq_lens=(1,) * 5, gate=gate, dtype=dtype, seed=23)
+    di = wl.make_decode_inputs(w, dev)
+    s0 = di["state"].clone()
+    o = kda.decode_step(di["q"], di["k"], di["v"], di["alpha"], di["beta"], di["state"])
+    torch.cuda.synchronize()
+    _check_decode(di, s0, o)
+
+
 def test_decode_config_full():
     """B=256 H=16 d=128 per-key alpha; every (sequence, head) checked."""
     dev = device()

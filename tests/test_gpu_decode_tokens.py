@@ -126,12 +126,27 @@ def test_out_of_range_commit_is_clamped():
     assert torch.equal(state[2], ts[2, 0])
 
 
-def test_draft_full_size_sampled_heads():
-    """B=256 sequences x 4 draft tokens, H=16, d=128, per-key alpha: heads 0
-    and 11 of every sequence against the oracle, every per-token state."""
+def test_draft_full_size_all_heads():
+    """B=256 sequences x 4 draft tokens, H=16, d=128, per-key alpha: every
+    head of every sequence against the oracle, every per-token state."""
     B, n, H, d = 256, 4, 16, 128
     w, inp, x = _inputs(B, n, H, d, "per_key", "bf16", seed=36)
     state = inp["initial_state"].clone()
     o, ts = kda.decode_tokens(x["q"], x["k"], x["v"], x["alpha"], x["beta"], state, keep_token_states=True)
     torch.cuda.synchronize()
-    _oracle_check(inp, o, state, ts, heads=(0, 11))
+    _oracle_check(inp, o, state, ts)
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64)])
+@pytest.mark.parametrize("gate", ["scalar", "per_key"])
+def test_decode_tokens_rectangular_heads(dk, dv, gate):
+    """d_k != d_v: the d_v x d_k state, per-token states and the committed
+    state against the oracle."""
+    B, n, H = 5, 3, 2
+    w = custom(f"draft_rect_{dk}x{dv}", H=H, d=dk, dv=dv, lens=(n,) * B, gate=gate, seed=37)
+    inp = wl.make_prefill_inputs(w, device())
+    x = {name: inp[name].view(B, n, *inp[name].shape[1:]) for name in ("q", "k", "v", "alpha", "beta")}
+    state = inp["initial_state"].clone()
+    o, ts = kda.decode_tokens(x["q"], x["k"], x["v"], x["alpha"], x["beta"], state, keep_token_states=True)
+    torch.cuda.synchronize()
+    _oracle_check(inp, o, state, ts)

@@ -33,6 +33,20 @@ MUTANTS = {
          "      for (int32_t j = 0; j < dk; ++j) s[j] = s[j] * at[j];\n")],
     "initial_state_ignored": [("J->init ? (double)", "0 ? (double)")],
     "sequence_offset_ignored": [("const int64_t t_begin = J->cu[n],", "const int64_t t_begin = 0 * J->cu[n],")],
+    # the comparison's normaliser taken across slices instead of per slice
+    "checker_o_running_max": [("""    if (o_cand) {
+      for (int32_t n = 0; n < num_seqs; ++n)
+        for (int32_t h = 0; h < H; ++h) {
+          double num = 0.0, den = 0.0;""", """    if (o_cand) {
+      double den = 0.0;
+      for (int32_t n = 0; n < num_seqs; ++n)
+        for (int32_t h = 0; h < H; ++h) {
+          double num = 0.0;""")],
+    "checker_state_global_max": [
+        ("""        double rel = slice_rel(final_cand + s * state_elems, f_buf + s * state_elems, state_elems, &nonfinite);""",
+         """        double rel = s ? 0.0 : slice_rel(final_cand, f_buf, (int64_t)num_seqs * H * state_elems, &nonfinite);"""),
+        ("""        double rel = slice_rel(snap_cand + s * state_elems, s_buf + s * state_elems, state_elems, &nonfinite);""",
+         """        double rel = s ? 0.0 : slice_rel(snap_cand, s_buf, n_snap * H * state_elems, &nonfinite);""")],
     "snapshot_one_token_late": [("if (J->interval > 0 && J->snap && (t + 1) % J->interval == 0) {",
                                  "if (J->interval > 0 && J->snap && t % J->interval == 0 && t > 0) {"),
                                 ("const int64_t slot = J->snap_base[n] + (t + 1) / J->interval - 1;",

@@ -366,6 +366,45 @@ def test_ref_check_flags_corruption_and_nonfinite():
     assert rc == oracle.MISMATCH and rep["nonfinite"] == 1
 
 
+def test_ref_check_normalises_each_slice():
+    """The tolerance is relative to each (sequence, head) slice's own largest
+    reference value (reading R13 of the comparison): a head 1000 times larger
+    than another must not hide a 1 % error in the small one. The large slice
+    comes first (head 0, sequence 0), so a normaliser carried over from an
+    earlier slice, or taken over the whole tensor, passes what must fail."""
+    rng = np.random.default_rng(13)
+    lens = [48, 40]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T, H, dk, dv = int(cu[-1]), 2, 8, 8
+    q, k, v, alpha, beta, s0 = rand_inputs(rng, T, H, dk, dv, 1, n_seqs=2)
+    v[:, 0] *= 1000.0
+    s0[:, 0] *= 1000.0
+    s0[0] *= 1000.0
+    v[cu[0]:cu[1]] *= 1000.0
+    o, fin, snaps = oracle.run(q, k, v, alpha, beta, cu, s0, interval=8)
+    assert np.abs(o[:, 0]).max() > 300 * np.abs(o[cu[1]:, 1]).max()
+    rc, rep = oracle.ref_check(q, k, v, alpha, beta, cu, s0, 8, o, fin, snaps)
+    assert rc == oracle.OK
+
+    def planted(ref, idx, small):
+        x = ref.astype(np.float32).copy()
+        x[idx] += np.float32(0.01 * np.abs(small).max())
+        return x
+
+    # o: sequence 1, head 1 (the small slice)
+    o_bad = planted(o, (cu[1] + 7, 1, 3), o[cu[1]:, 1])
+    rc, rep = oracle.ref_check(q, k, v, alpha, beta, cu, s0, 8, o_bad, fin, snaps)
+    assert rc == oracle.MISMATCH and 0.005 < rep["o_rel"] < 0.02, rep
+    # final state and a snapshot of sequence 1, head 1
+    f_bad = planted(fin, (1, 1, 2, 5), fin[1, 1])
+    rc, rep = oracle.ref_check(q, k, v, alpha, beta, cu, s0, 8, o, f_bad, snaps)
+    assert rc == oracle.MISMATCH and 0.005 < rep["final_rel"] < 0.02, rep
+    n0 = lens[0] // 8
+    s_bad = planted(snaps, (n0 + 2, 1, 4, 1), snaps[n0 + 2, 1])
+    rc, rep = oracle.ref_check(q, k, v, alpha, beta, cu, s0, 8, o, fin, s_bad)
+    assert rc == oracle.MISMATCH and 0.005 < rep["snap_rel"] < 0.02, rep
+
+
 def test_thread_count_does_not_change_results():
     rng = np.random.default_rng(12)
     lens = [70, 3, 40]
