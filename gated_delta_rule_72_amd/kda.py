@@ -280,13 +280,13 @@ def kda_prefill_backward(shape: KdaShape, cu_seqlens_host: torch.Tensor, cu_seql
           d_initial_state=(d_initial_state, F32), cu_seqlens_dev=(cu_seqlens_dev, I64))
     T = q.shape[0]
     cu = _cu_host("kda_prefill_backward", cu_seqlens_host, T)
-    N, H, dk, dv = cu.numel() - 1, shape.num_heads, shape.d_k, shape.d_v
+    N, H, Dk, Dv = cu.numel() - 1, shape.num_heads, shape.d_k, shape.d_v
     a_sh = _alpha_shape(shape, (T,))
-    _geom("kda_prefill_backward", q.device, q=(q, (T, H, dk)), k=(k, (T, H, dk)), v=(v, (T, H, dv)),
-          alpha=(alpha, a_sh), beta=(beta, (T, H)), initial_state=(initial_state, (N, H, dv, dk)),
-          d_o=(d_o, (T, H, dv)), d_final_state=(d_final_state, (N, H, dv, dk)), dq=(dq, (T, H, dk)),
-          dk=(dk, (T, H, dk)), dv=(dv, (T, H, dv)), dalpha=(dalpha, a_sh), dbeta=(dbeta, (T, H)),
-          d_initial_state=(d_initial_state, (N, H, dv, dk)), cu_seqlens_dev=(cu_seqlens_dev, (N + 1,)),
+    _geom("kda_prefill_backward", q.device, q=(q, (T, H, Dk)), k=(k, (T, H, Dk)), v=(v, (T, H, Dv)),
+          alpha=(alpha, a_sh), beta=(beta, (T, H)), initial_state=(initial_state, (N, H, Dv, Dk)),
+          d_o=(d_o, (T, H, Dv)), d_final_state=(d_final_state, (N, H, Dv, Dk)), dq=(dq, (T, H, Dk)),
+          dk=(dk, (T, H, Dk)), dv=(dv, (T, H, Dv)), dalpha=(dalpha, a_sh), dbeta=(dbeta, (T, H)),
+          d_initial_state=(d_initial_state, (N, H, Dv, Dk)), cu_seqlens_dev=(cu_seqlens_dev, (N + 1,)),
           workspace=(workspace, tuple(workspace.shape)))
     s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream_ptr(q.device)
     _check("kda_prefill_backward", load().kda_prefill_backward(
