@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/kda.h"
 #include "kda_internal.h"
@@ -320,45 +321,13 @@ BackwardPlan plan_backward(const kda_shape* s, int32_t num_seqs, const int64_t* 
   return p;
 }
 
-}  // namespace
-
-extern "C" {
-
-int kda_abi_version(void) { return KDA_ABI_VERSION; }
-
-const char* kda_last_error(void) { return g_err; }
-
-int kda_snapshot_count(int32_t num_seqs, const int64_t* cu_seqlens_host, int64_t interval,
-                       int64_t* n_snap) {
-  if (!n_snap) return fail(KDA_ERR_ARG, "n_snap is NULL");
-  int rc = check_cu(num_seqs, cu_seqlens_host);
-  if (rc != KDA_OK) return rc;
-  if (interval < 0) return fail(KDA_ERR_SHAPE, "interval must be >= 0");
-  *n_snap = snapshot_slots(num_seqs, cu_seqlens_host, interval);
-  g_err[0] = '\0';
-  return KDA_OK;
-}
-
-int kda_prefill_workspace_size(const kda_shape* shape, int32_t num_seqs,
-                               const int64_t* cu_seqlens_host, int32_t chunk,
-                               int64_t snapshot_interval, int64_t segment_tokens, size_t* bytes) {
-  if (!bytes) return fail(KDA_ERR_ARG, "bytes is NULL");
-  int rc = check_prefill_args(shape, num_seqs, cu_seqlens_host, chunk, snapshot_interval, segment_tokens);
-  if (rc != KDA_OK) return rc;
-  *bytes = plan_full(shape, num_seqs, cu_seqlens_host, snapshot_interval, segment_tokens,
-                     segment_tokens < 0 ? device_cu_count() : 0).bytes;
-  g_err[0] = '\0';
-  return KDA_OK;
-}
-
-int kda_prefill_chunked(const kda_shape* shape, int32_t num_seqs,
-                        const int64_t* cu_seqlens_host, const int64_t* cu_seqlens_dev,
-                        int32_t chunk, int64_t snapshot_interval, int64_t segment_tokens,
-                        const void* q, const void* k, const void* v,
-                        const float* alpha, const float* beta,
-                        const float* initial_state,
-                        float* o, float* final_state, float* snapshots,
-                        void* workspace, size_t workspace_bytes, void* hip_stream) {
+// Every host check of a prefill call, before anything is planned or enqueued.
+int validate_prefill(const kda_shape* shape, int32_t num_seqs, const int64_t* cu_seqlens_host,
+                     const int64_t* cu_seqlens_dev, int32_t chunk, int64_t snapshot_interval,
+                     int64_t segment_tokens, const void* q, const void* k, const void* v,
+                     const float* alpha, const float* beta, const float* initial_state, const float* o,
+                     const float* final_state, const float* snapshots, const void* workspace,
+                     size_t workspace_bytes) {
   int rc = check_prefill_args(shape, num_seqs, cu_seqlens_host, chunk, snapshot_interval, segment_tokens);
   if (rc != KDA_OK) return rc;
   const int64_t T = cu_seqlens_host[num_seqs];
@@ -402,6 +371,89 @@ int kda_prefill_chunked(const kda_shape* shape, int32_t num_seqs,
     if ((rc = check_disjoint(rs, outs, 2)) != KDA_OK) return rc;
     if ((rc = check_disjoint(ro, outs + 1, 1)) != KDA_OK) return rc;
   }
+  return KDA_OK;
+}
+
+// ---- static scratch of the allocation-free prefill ------------------------------
+// kda_prefill_chunked_noalloc takes its work table from this array instead of a
+// caller's workspace. Each GPU holds its own copy for the life of the process;
+// host code uses the device address that hipGetSymbolAddress returns for the
+// current device, never the array's name (a host-side stand-in).
+constexpr size_t kScratchBytes = 1u << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; NULL with the HIP error's text
+// in g_err if the lookup fails.
+void* scratch_address() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    fail(KDA_ERR_DEVICE, "no current HIP device (or device index above %d)", kMaxDevices - 1);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      fail(KDA_ERR_DEVICE, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+      return nullptr;
+    }
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_last_error(void) { return g_err; }
+
+int kda_snapshot_count(int32_t num_seqs, const int64_t* cu_seqlens_host, int64_t interval,
+                       int64_t* n_snap) {
+  if (!n_snap) return fail(KDA_ERR_ARG, "n_snap is NULL");
+  int rc = check_cu(num_seqs, cu_seqlens_host);
+  if (rc != KDA_OK) return rc;
+  if (interval < 0) return fail(KDA_ERR_SHAPE, "interval must be >= 0");
+  *n_snap = snapshot_slots(num_seqs, cu_seqlens_host, interval);
+  g_err[0] = '\0';
+  return KDA_OK;
+}
+
+int kda_prefill_workspace_size(const kda_shape* shape, int32_t num_seqs,
+                               const int64_t* cu_seqlens_host, int32_t chunk,
+                               int64_t snapshot_interval, int64_t segment_tokens, size_t* bytes) {
+  if (!bytes) return fail(KDA_ERR_ARG, "bytes is NULL");
+  int rc = check_prefill_args(shape, num_seqs, cu_seqlens_host, chunk, snapshot_interval, segment_tokens);
+  if (rc != KDA_OK) return rc;
+  *bytes = plan_full(shape, num_seqs, cu_seqlens_host, snapshot_interval, segment_tokens,
+                     segment_tokens < 0 ? device_cu_count() : 0).bytes;
+  g_err[0] = '\0';
+  return KDA_OK;
+}
+
+int kda_prefill_chunked(const kda_shape* shape, int32_t num_seqs,
+                        const int64_t* cu_seqlens_host, const int64_t* cu_seqlens_dev,
+                        int32_t chunk, int64_t snapshot_interval, int64_t segment_tokens,
+                        const void* q, const void* k, const void* v,
+                        const float* alpha, const float* beta,
+                        const float* initial_state,
+                        float* o, float* final_state, float* snapshots,
+                        void* workspace, size_t workspace_bytes, void* hip_stream) {
+  int rc = validate_prefill(shape, num_seqs, cu_seqlens_host, cu_seqlens_dev, chunk, snapshot_interval,
+                            segment_tokens, q, k, v, alpha, beta, initial_state, o, final_state, snapshots,
+                            workspace, workspace_bytes);
+  if (rc != KDA_OK) return rc;
+  const int64_t T = cu_seqlens_host[num_seqs];
+  const int64_t n_snap = snapshot_slots(num_seqs, cu_seqlens_host, snapshot_interval);
   const FullPlan plan = plan_full(shape, num_seqs, cu_seqlens_host, snapshot_interval, segment_tokens,
                                   segment_tokens < 0 ? device_cu_count() : 0);
   if (num_seqs > 0 && (!workspace || workspace_bytes < plan.bytes))
@@ -465,6 +517,34 @@ int kda_prefill_chunked(const kda_shape* shape, int32_t num_seqs,
   }
   g_err[0] = '\0';
   return KDA_OK;
+}
+
+int kda_prefill_chunked_noalloc(const kda_shape* shape, int32_t num_seqs,
+                                const int64_t* cu_seqlens_host, const int64_t* cu_seqlens_dev,
+                                int32_t chunk, int64_t snapshot_interval,
+                                const void* q, const void* k, const void* v,
+                                const float* alpha, const float* beta, const float* initial_state,
+                                float* o, float* final_state, float* snapshots, void* hip_stream) {
+  // never segmented: the work table (one 40-byte item per sequence and the
+  // first-item index) is all the scratch the kernels use
+  int rc = validate_prefill(shape, num_seqs, cu_seqlens_host, cu_seqlens_dev, chunk, snapshot_interval, 0, q, k, v,
+                            alpha, beta, initial_state, o, final_state, snapshots, nullptr, 0);
+  if (rc != KDA_OK) return rc;
+  const size_t need = plan_full(shape, num_seqs, cu_seqlens_host, snapshot_interval, 0, 0).bytes;
+  if (need > kScratchBytes)
+    return fail(KDA_ERR_WORKSPACE,
+                "kda_prefill_chunked_noalloc: this call needs %zu bytes of scratch, the static scratch holds %zu "
+                "(about 23000 sequences with d_v >= d_k; far fewer tokens with d_k = 2 d_v)",
+                need, kScratchBytes);
+  if (num_seqs == 0) {
+    g_err[0] = '\0';
+    return KDA_OK;
+  }
+  void* ws = scratch_address();
+  if (!ws) return KDA_ERR_DEVICE;
+  return kda_prefill_chunked(shape, num_seqs, cu_seqlens_host, cu_seqlens_dev, chunk, snapshot_interval, 0, q, k,
+                             v, alpha, beta, initial_state, o, final_state, snapshots, ws, kScratchBytes,
+                             hip_stream);
 }
 
 int kda_decode_step(const kda_shape* shape, int32_t batch, const void* q, const void* k,

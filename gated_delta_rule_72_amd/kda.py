@@ -52,6 +52,7 @@ def load() -> ctypes.CDLL:
         "kda_prefill_workspace_size": ([P, I32, P, I32, I64, I64, P], ctypes.c_int),
         "kda_prefill_chunked": ([P, I32, P, P, I32, I64, I64, P, P, P, P, P, P, P, P, P, P, SZ, P],
                                 ctypes.c_int),
+        "kda_prefill_chunked_noalloc": ([P, I32, P, P, I32, I64, P, P, P, P, P, P, P, P, P, P], ctypes.c_int),
         "kda_decode_step": ([P, I32, P, P, P, P, P, P, P, P], ctypes.c_int),
         "kda_decode_tokens": ([P, I32, I32, P, P, P, P, P, P, P, P, P, P], ctypes.c_int),
         "kda_layer_front": ([P, I32, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, P, P],
@@ -70,7 +71,7 @@ def load() -> ctypes.CDLL:
 
 
 EXPORTED = ("kda_abi_version", "kda_last_error", "kda_snapshot_count", "kda_prefill_workspace_size",
-            "kda_prefill_chunked", "kda_decode_step", "kda_decode_tokens", "kda_layer_front",
+            "kda_prefill_chunked", "kda_prefill_chunked_noalloc", "kda_decode_step", "kda_decode_tokens", "kda_layer_front",
             "kda_layer_back", "kda_prefill_backward_workspace_size", "kda_prefill_backward")
 
 
@@ -197,6 +198,30 @@ def kda_prefill_chunked(shape: KdaShape, cu_seqlens_host: torch.Tensor, cu_seqle
         int(snapshot_interval), int(segment_tokens), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state),
         _ptr(o), _ptr(final_state), _ptr(snapshots), _ptr(workspace),
         ctypes.c_size_t(workspace.numel() * workspace.element_size()), s))
+
+
+def kda_prefill_chunked_noalloc(shape: KdaShape, cu_seqlens_host: torch.Tensor, cu_seqlens_dev: torch.Tensor,
+                                q, k, v, alpha, beta, initial_state, o, final_state, snapshots,
+                                chunk: int = CHUNK, snapshot_interval: int = 0, stream=None) -> None:
+    """kda_prefill_chunked with no workspace (the library's static scratch, never
+    segmented). Same tensor checks as kda_prefill_chunked."""
+    _args("kda_prefill_chunked_noalloc", shape, q=(q, "qkv"), k=(k, "qkv"), v=(v, "qkv"), alpha=(alpha, F32),
+          beta=(beta, F32), initial_state=(initial_state, F32), o=(o, F32), final_state=(final_state, F32),
+          snapshots=(snapshots, F32), cu_seqlens_dev=(cu_seqlens_dev, I64))
+    T = q.shape[0]
+    cu = _cu_host("kda_prefill_chunked_noalloc", cu_seqlens_host, T)
+    N, H, dk, dv = cu.numel() - 1, shape.num_heads, shape.d_k, shape.d_v
+    n_snap = kda_snapshot_count(cu, snapshot_interval)
+    dev = q.device
+    _geom("kda_prefill_chunked_noalloc", dev, ("snapshots",), q=(q, (T, H, dk)), k=(k, (T, H, dk)),
+          v=(v, (T, H, dv)), alpha=(alpha, _alpha_shape(shape, (T,))), beta=(beta, (T, H)),
+          initial_state=(initial_state, (N, H, dv, dk)), o=(o, (T, H, dv)), final_state=(final_state, (N, H, dv, dk)),
+          snapshots=(snapshots, (n_snap, H, dv, dk)), cu_seqlens_dev=(cu_seqlens_dev, (N + 1,)))
+    s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream_ptr(dev)
+    _check("kda_prefill_chunked_noalloc", load().kda_prefill_chunked_noalloc(
+        ctypes.byref(shape), cu.numel() - 1, _ptr(cu), _ptr(cu_seqlens_dev), int(chunk), int(snapshot_interval),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state), _ptr(o), _ptr(final_state),
+        _ptr(snapshots), s))
 
 
 def kda_decode_step(shape: KdaShape, batch: int, q, k, v, alpha, beta, state, o, stream=None) -> None:

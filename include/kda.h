@@ -163,6 +163,28 @@ int kda_prefill_chunked(const kda_shape* shape, int32_t num_seqs,
                         float* o, float* final_state, float* snapshots,
                         void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* kda_prefill_chunked without a workspace argument, for callers that cannot
+ * allocate device memory around the call: code under HIP graph capture,
+ * serving loops that forbid allocation, harnesses that allow none. It calls no
+ * allocating routine; the work table lives in a static device array of the
+ * library (1 MiB per GPU, held until the process ends).
+ * Arguments and results as kda_prefill_chunked with segment_tokens = 0 (each
+ * (sequence, head) chain runs in one workgroup, never segmented).
+ * Limit: the call's work table must fit the 1 MiB array, which holds about
+ * 23000 sequences when d_v >= d_k; with d_k = 2 d_v the zero-padded values
+ * and states come from it too, so only calls of a few hundred tokens fit.
+ * Beyond it: KDA_ERR_WORKSPACE, nothing enqueued.
+ * Calls on one GPU share that array: two calls that overlap in time on one
+ * GPU (different streams, or different host threads) race and must not be
+ * issued; calls ordered on one stream are safe. KDA_ERR_DEVICE if the
+ * array's device address cannot be looked up on the current device. */
+int kda_prefill_chunked_noalloc(const kda_shape* shape, int32_t num_seqs,
+                                const int64_t* cu_seqlens_host, const int64_t* cu_seqlens_dev,
+                                int32_t chunk, int64_t snapshot_interval,
+                                const void* q, const void* k, const void* v,
+                                const float* alpha, const float* beta, const float* initial_state,
+                                float* o, float* final_state, float* snapshots, void* hip_stream);
+
 /* One decode step for `batch` independent sequences (one new token each),
  * updating the fp32 state in place: O(1) work per token, one read and one
  * write of S (page "kda-graft", ailist.pro, section "2. Decode: O(1) против

@@ -39,7 +39,8 @@ def K():
 def test_kda_header_symbols_exported(K):
     names = _declared("kda.h")
     assert set(names) == {"kda_abi_version", "kda_last_error", "kda_snapshot_count",
-                          "kda_prefill_workspace_size", "kda_prefill_chunked", "kda_decode_step",
+                          "kda_prefill_workspace_size", "kda_prefill_chunked", "kda_prefill_chunked_noalloc",
+                          "kda_decode_step",
                           "kda_decode_tokens", "kda_layer_front", "kda_layer_back",
                           "kda_prefill_backward_workspace_size", "kda_prefill_backward"}
     lib = ctypes.CDLL(K.LIB_PATH)
@@ -195,6 +196,36 @@ def test_rectangular_heads_plan(K):
     with pytest.raises(K.KdaError) as e:
         K.kda_prefill_backward_workspace_size(K.make_shape(3, 64, 128, torch.bfloat16, True), cu)
     assert e.value.code == K.KDA_ERR_SHAPE
+
+
+def test_noalloc_prefill_host_rejections(K):
+    """The allocation-free prefill: argument errors and a work table larger than
+    its static scratch are rejected on the host (nothing is dereferenced)."""
+    lib = K.load()
+
+    def call(sh, cu, interval=0, **kw):
+        p = dict(cu_dev=0x10000000, q=0x20000000, k=0x30000000, v=0x40000000, alpha=0x50000000, beta=0x60000000,
+                 init=None, o=0x70000000, fin=0x80000000, snaps=None)
+        p.update(kw)
+        f = lambda n: None if p[n] is None else _fake(p[n])  # noqa: E731
+        cu = cu.contiguous()
+        return lib.kda_prefill_chunked_noalloc(ctypes.byref(sh), cu.numel() - 1, ctypes.c_void_p(cu.data_ptr()),
+                                               f("cu_dev"), 64, interval, f("q"), f("k"), f("v"), f("alpha"),
+                                               f("beta"), f("init"), f("o"), f("fin"), f("snaps"), None)
+
+    sh = K.make_shape(2, 64, 64, torch.bfloat16, True)
+    cu = torch.tensor([0, 100, 300], dtype=torch.int64)
+    assert call(sh, torch.tensor([0], dtype=torch.int64)) == K.KDA_OK          # no sequences
+    assert call(sh, cu, q=0x20000008) == K.KDA_ERR_ALIGN
+    assert call(sh, cu, fin=None) == K.KDA_ERR_ARG
+    assert call(sh, cu, interval=100) == K.KDA_ERR_SHAPE
+    assert call(sh, cu, o=0x30000000) == K.KDA_ERR_ARG                         # o overlaps k
+    # 40000 short sequences need a work table larger than the 1 MiB scratch
+    many = torch.arange(0, 40001, dtype=torch.int64)
+    assert call(sh, many) == K.KDA_ERR_WORKSPACE and "scratch" in K.kda_last_error()
+    # d_k = 2 d_v pads values and states in the scratch too: 3000 tokens do not fit
+    narrow = K.make_shape(2, 128, 64, torch.bfloat16, True)
+    assert call(narrow, torch.tensor([0, 100, 3000], dtype=torch.int64)) == K.KDA_ERR_WORKSPACE
 
 
 def test_decode_host_rejections(K):
