@@ -443,6 +443,109 @@ __device__ __forceinline__ bool gram_diag(int wave, int& d0, int& d1) {
   }
 }
 
+// Two fp32 accumulator tiles (t1 may be zero) as hi + lo bf16 permuted-K
+// operands: hi rounds to nearest, lo is the rounded remainder.
+__device__ __forceinline__ void split_tiles_bf16(f32x4 t0, f32x4 t1, bf16x8& hi, bf16x8& lo) {
+  const float x[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+  split8_bf16(x, hi, lo);
+}
+// c + a b as three bf16 products (hi hi + hi lo + lo hi), fp32 accumulation.
+__device__ __forceinline__ f32x4 mfma_split3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, f32x4 c) {
+  c = mfma_bf16(ah, bh, c);
+  c = mfma_bf16(ah, bl, c);
+  return mfma_bf16(al, bh, c);
+}
+// T~ rows 16R + 4g + i, column col of one accumulator tile (lane (g, l16)),
+// scaled by beta_col, as fp16 hi + lo.
+template <class L>
+__device__ __forceinline__ void put_t_tile(_Float16* sTh, _Float16* sTl, f32x4 a, float b, int row0, int col) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float t = a[i] * b;
+    const _Float16 th = (_Float16)t;
+    sTh[(row0 + i) * L::LDTT + col] = th;
+    sTl[(row0 + i) * L::LDTT + col] = (_Float16)(t - (float)th);
+  }
+}
+
+// Off-diagonal blocks of block column I of A = (I + L)^-1 (sL holds L below
+// the diagonal blocks and A_RR on them, fp32 row-major): one wavefront, the
+// column's tiles in accumulator layout (lane (g, l16): rows 4g+i, column
+// l16), every product a permuted-K split-bf16 MFMA over two 16-row tiles.
+template <int I, class L>
+__device__ __forceinline__ void inverse_column(const float* sL, const float* sBeta, _Float16* sTh, _Float16* sTl,
+                                               int lane) {
+  const int g = lane >> 4, l16 = lane & 15;
+  f32x4 Acol[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) Acol[I][i] = sL[(16 * I + 4 * g + i) * L::LDL + 16 * I + l16];
+  const float bcol = sBeta[16 * I + l16];
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int R = I + 1; R < 4; ++R) {
+    const float* lrow = sL + (16 * R + l16) * L::LDL;
+    // acc = sum_{m=I}^{R-1} L_Rm A_mI
+    f32x4 acc = zero;
+#pragma unroll
+    for (int m0 = I; m0 < R; m0 += 2) {
+      const bool two = m0 + 1 < R;
+      const f32x4 la = *reinterpret_cast<const f32x4*>(lrow + 16 * m0 + 4 * g);
+      const f32x4 lb = two ? *reinterpret_cast<const f32x4*>(lrow + 16 * (m0 + 1) + 4 * g) : zero;
+      bf16x8 ah, al, bh, bl;
+      split_tiles_bf16(la, lb, ah, al);
+      split_tiles_bf16(Acol[m0], two ? Acol[m0 + 1] : zero, bh, bl);
+      acc = mfma_split3(ah, al, bh, bl, acc);
+    }
+    // A_RI = -A_RR acc
+    bf16x8 ah, al, bh, bl;
+    split_tiles_bf16(*reinterpret_cast<const f32x4*>(lrow + 16 * R + 4 * g), zero, ah, al);
+    split_tiles_bf16(acc, zero, bh, bl);
+    const f32x4 res = mfma_split3(ah, al, bh, bl, zero);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Acol[R][i] = -res[i];
+    put_t_tile<L>(sTh, sTl, Acol[R], bcol, 16 * R + 4 * g, 16 * I + l16);
+  }
+}
+
+// The rest of T~ for wavefront w of the NW - 3 that run no column chain: the
+// diagonal blocks A_RR Diag(beta) (R = w, w + NW - 3, ..) and, on the last of
+// those wavefronts, zeros above the diagonal.
+template <int NW, class L>
+__device__ __forceinline__ void inverse_rest(const float* sL, const float* sBeta, _Float16* sTh, _Float16* sTl, int w,
+                                             int lane) {
+  constexpr int NR = NW - 3;
+  const int row = lane >> 2, c4 = 4 * (lane & 3);     // 16 rows x 4 column groups of 4
+#pragma unroll
+  for (int R = 0; R < 4; ++R) {
+    if (R % NR != w) continue;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(sL + (16 * R + row) * L::LDL + 16 * R + c4);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(sBeta + 16 * R + c4);
+    f16x4 th, tl;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float t = a[e] * b[e];
+      th[e] = (_Float16)t;
+      tl[e] = (_Float16)(t - (float)th[e]);
+    }
+    *reinterpret_cast<f16x4*>(sTh + (16 * R + row) * L::LDTT + 16 * R + c4) = th;
+    *reinterpret_cast<f16x4*>(sTl + (16 * R + row) * L::LDTT + 16 * R + c4) = tl;
+  }
+  if (w == NR - 1) {
+    // blocks (R, I), I > R: 6 blocks x 16 rows x 16 columns, 8 halves per piece
+    const f16x8 z = {};
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      const int p = lane + 64 * j;                     // 192 pieces of 8 halves
+      const int blk = p / 32, r = (p % 32) / 2, half = p % 2;
+      const int R = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
+      const int I = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+      const int off = (16 * R + r) * L::LDTT + 16 * I + 8 * half;
+      *reinterpret_cast<f16x8*>(sTh + off) = z;
+      *reinterpret_cast<f16x8*>(sTl + off) = z;
+    }
+  }
+}
+
 __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) {
@@ -895,48 +998,21 @@ void prefill_kernel(PrefillArgs a) {
     __syncthreads();
 
     if constexpr (!WU) {
-      // ---- P4: A = (I + L)^-1 -------------------------------------------------
+      // ---- P4: A = (I + L)^-1, written as T~ = A Diag(beta) (fp16 hi + lo) --
       // The diagonal blocks A_RR are in place (P3). Block column I of the
       // off-diagonal part is one dependent chain on wavefront I (I = 0, 1, 2),
-      //   A_RI = -A_RR (L_RI A_II + sum_{I<m<R} L_Rm A_mI),   R = I+1 .. 3,
-      // on fp32 MFMA with the column's earlier blocks kept in accumulator
-      // registers; A_RI is stored at block (I, R). Meanwhile every wavefront
-      // stages V^T.
-      if (wave < 3) {
-        const int I = wave;
-        f32x4 Acol[4];                                  // A_mI, m > I (accumulator layout)
-#pragma unroll
-        for (int R = 1; R < 4; ++R) {
-          if (R > I) {
-            f32x4 acc = {0, 0, 0, 0};
-            // L_RI A_II, A_II read from LDS in the standard K order
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-              const float av = sL[(16 * R + l16) * L::LDL + 16 * I + 4 * ks + g];
-              const float bv = sL[(16 * I + 4 * ks + g) * L::LDL + 16 * I + l16];
-              acc = mfma_f32(av, bv, acc);
-            }
-            // L_Rm A_mI for I < m < R, A_mI from registers (permuted K: k = 4g + ks)
-#pragma unroll
-            for (int m = 1; m < 3; ++m) {
-              if (m > I && m < R) {
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                  acc = mfma_f32(sL[(16 * R + l16) * L::LDL + 16 * m + 4 * g + ks], Acol[m][ks], acc);
-              }
-            }
-            // -A_RR acc, acc as the permuted-K operand
-            f32x4 res = {0, 0, 0, 0};
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-              res = mfma_f32(sL[(16 * R + l16) * L::LDL + 16 * R + 4 * g + ks], acc[ks], res);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              Acol[R][i] = -res[i];
-              sL[(16 * I + 4 * g + i) * L::LDL + 16 * R + l16] = -res[i];
-            }
-          }
-        }
+      //   A_RI = -A_RR (sum_{I<=m<R} L_Rm A_mI),   R = I+1 .. 3,
+      // on split-bf16 MFMA (three-term products of hi + lo operands, about 16
+      // significant bits, fp32 range and accumulation), with the column's
+      // blocks kept in accumulator registers; each A_RI goes straight into T~.
+      // The other wavefronts write the diagonal blocks of T~ and zero the
+      // blocks above the diagonal. Meanwhile every wavefront stages V^T.
+      {
+        const int wv = __builtin_amdgcn_readfirstlane(wave);
+        if (wv == 0) inverse_column<0, L>(sL, sBeta, sTh, sTl, lane);
+        else if (wv == 1) inverse_column<1, L>(sL, sBeta, sTh, sTl, lane);
+        else if (wv == 2) inverse_column<2, L>(sL, sBeta, sTh, sTl, lane);
+        else inverse_rest<NW, L>(sL, sBeta, sTh, sTl, wv - 3, lane);
       }
       // V^T [v][c] into region A (G and raw q, k are dead after P3)
       {
@@ -964,28 +1040,7 @@ void prefill_kernel(PrefillArgs a) {
       }
       __syncthreads();
 
-      // ---- P5: T~ = A Diag(beta) as fp16 hi + lo; W = T~ (K * 2^G) ------------
-      for (int e8 = tid; e8 < C * C / 8; e8 += NT) {
-        const int c = e8 / 8, i0 = 8 * (e8 % 8);
-        const int Rb = c / 16, Ib = i0 / 16;
-        // A_RI (R > I) sits at block (I, R); diagonal blocks in place; zero above
-        const int src = (Rb > Ib) ? (16 * Ib + c % 16) * L::LDL + 16 * Rb + i0 % 16 : c * L::LDL + i0;
-        const float keep = (Rb >= Ib) ? 1.f : 0.f;
-        const f32x4 a0 = *reinterpret_cast<const f32x4*>(sL + src);
-        const f32x4 a1 = *reinterpret_cast<const f32x4*>(sL + src + 4);
-        const f32x4 b0 = *reinterpret_cast<const f32x4*>(sBeta + i0);
-        const f32x4 b1 = *reinterpret_cast<const f32x4*>(sBeta + i0 + 4);
-        f16x8 th, tl;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float tv = keep * (e < 4 ? a0[e] * b0[e] : a1[e - 4] * b1[e - 4]);
-          th[e] = (_Float16)tv;
-          tl[e] = (_Float16)(tv - (float)th[e]);
-        }
-        *reinterpret_cast<f16x8*>(sTh + c * L::LDTT + i0) = th;
-        *reinterpret_cast<f16x8*>(sTl + c * L::LDTT + i0) = tl;
-      }
-      __syncthreads();
+      // ---- P5: W = T~ (K * 2^G), U' = T~ V --------------------------------------
       // W[:, 16kt..16kt+15] for kt = wave, wave + NW, ... and U' = T~ V for the
       // wavefront's own value slices (K = 64), sharing each T~ hi/lo tile read;
       // U' stays in registers for P6. W is formed transposed (K^T as the A
@@ -1040,6 +1095,15 @@ void prefill_kernel(PrefillArgs a) {
             if constexpr (MAP)
               *reinterpret_cast<f16x4*>(wu_base + (int64_t)ch * WU_BYTES + 2 * off) = w4;
           }
+        if constexpr (MAP) {
+          // and its U' (one accumulator tile per lane): issued before the
+          // barrier, so the record drains while the other wavefronts finish P5
+          f32x4* up = reinterpret_cast<f32x4*>(wu_base + (int64_t)ch * WU_BYTES + W_BYTES);
+#pragma unroll
+          for (int sl = 0; sl < SPW; ++sl)
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) up[((SPW * wave + sl) * 4 + ct) * 64 + lane] = Up[sl][ct];
+        }
       }
       __syncthreads();
     }  // !WU: P4, P5
@@ -1068,16 +1132,7 @@ void prefill_kernel(PrefillArgs a) {
       }
     }
 
-    if constexpr (MAP) {
-      // keep this chunk's U' (one tile per lane) for pass 3 (W was kept in P5);
-      // issued after the prefetch, so the stores drain while the chains run
-      unsigned char* rec = wu_base + (int64_t)ch * WU_BYTES;
-      f32x4* up = reinterpret_cast<f32x4*>(rec + W_BYTES);
-#pragma unroll
-      for (int sl = 0; sl < SPW; ++sl)
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) up[((SPW * wave + sl) * 4 + ct) * 64 + lane] = Up[sl][ct];
-    }
+
 
     // ---- P6: state passing for this wavefront's slices ---------------------
     // Every A-operand tile read from LDS (T~, W, Q~, B, K~^T) feeds the MFMAs of
@@ -1216,6 +1271,345 @@ void prefill_kernel(PrefillArgs a) {
       for (int kt = 0; kt < KT; ++kt)
         *reinterpret_cast<f32x4*>(dst + (16 * (SPW * wave + sl % SPW) + l16) * D + 16 * kt + 4 * g) =
             ST[sl][kt];
+    }
+  }
+}
+
+// ---- Pass 1 (segment maps), scalar gate, bf16 inputs, d = 128 -------------
+// Every product that contracts over the 64 chunk rows (W = T~ (K * 2^G),
+// U' = T~ V and the state update with K~^T) takes its K or V operand straight
+// from the raw token-major rows staged in LDS, through the LDS transpose read
+// (ds_read_b64_tr_b16: in each group of 16 lanes, lane j names the 8 bytes at
+// row base + j/4, columns c0 + 4 (j % 4) .. +3, and lane i receives column
+// c0 + i of those four rows, one row per element). No transposed copy of K or
+// V is written. The scalar gate's decay factors go where the operands are
+// formed instead: 2^G_c multiplies the K operand of W in registers, and
+// 2^(G_n - G_c) multiplies row c of U before the state update,
+//     (K * 2^(G_n - G))^T U = K^T (2^(G_n - G) * U),
+// whose K^T operand is then the raw bf16 row data itself (U as bf16 hi + lo).
+// The raw k rows of a chunk are double-buffered (the update of chunk c reads
+// them while chunk c+1's are staged); v rows are read only in P5.
+template <int D>
+struct LdsMap {
+  using L = Lds<D>;
+  static constexpr int RK = 0;                                  // raw k [2][64][D] bf16 (raw_swz)
+  static constexpr int RV = RK + 2 * C * D * 2;                 // raw v [64][D] bf16 (raw_swz)
+  static constexpr int LM = RV + C * D * 2;                     // L / A [64][LDL] f32
+  static constexpr int TH = LM + C * L::LDL * 4;                // T~ hi [64][LDTT] f16
+  static constexpr int TL = TH + C * L::LDTT * 2;               // T~ lo
+  static constexpr int WB = TL + C * L::LDTT * 2;               // W [64][LDQ] f16 (the stored image)
+  static constexpr int SM = WB + C * L::LDQ * 2;                // G[64], 2^G[64], 2^(G_n-G)[64], beta[64]
+  static constexpr int TOTAL = SM + 4 * C * 4 + 16;             // + 2^G_n
+  static_assert(RV % 512 == 0 && LM % 512 == 0 && WB % 512 == 0, "buffers keep the bank alignment");
+};
+
+// Eight raw values x[c][col0 + (lane % 16)] of staged rows [64][D] bf16
+// (chunk-permuted, raw_swz): c = r0 + {0..3} from the first transpose read,
+// r1 + {0..3} from the second; r0 and r1 are this lane group's row bases.
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+template <int D>
+__device__ __forceinline__ bf16x8 tr_rows(const unsigned char* raw, int r0, int r1, int col0, int lane) {
+  const int j = lane & 15;
+  const int col = col0 + 4 * (j & 3);
+  auto piece = [&](int r) __attribute__((always_inline)) {
+    const int rr = r + (j >> 2);
+    const unsigned char* p = raw + rr * (D * 2) + (((col >> 3) ^ raw_swz<D>(rr)) << 4) + ((col >> 2) & 1) * 8;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(p));
+  };
+  const bf16x4_t a = piece(r0), b = piece(r1);
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ f16x8 bf16x8_to_f16(bf16x8 x, const float (&scale)[8]) {
+  f16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (_Float16)((float)x[e] * scale[e]);
+  return r;
+}
+
+template <int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_map_kernel(PrefillArgs a) {
+  static_assert(D == 128, "eight wavefronts of one N and one M slice");
+  constexpr int NW = 8, NT = 512, KT = D / 16;
+  using L = Lds<D>;
+  using P = LdsMap<D>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* sL = reinterpret_cast<float*>(smem + P::LM);
+  _Float16* sTh = reinterpret_cast<_Float16*>(smem + P::TH);
+  _Float16* sTl = reinterpret_cast<_Float16*>(smem + P::TL);
+  _Float16* sW = reinterpret_cast<_Float16*>(smem + P::WB);
+  float* sGs = reinterpret_cast<float*>(smem + P::SM);          // [64] G (log2, cumulative)
+  float* sDec = sGs + C;                                          // [64] 2^G (0 past the chunk end)
+  float* sRem = sDec + C;                                         // [64] 2^(G_n - G)
+  float* sBeta = sRem + C;                                        // [64]
+  float* sGam = sBeta + C;                                        // 2^G_n
+  unsigned char* rawV = smem + P::RV;
+
+  const int wave = threadIdx.x / 64;
+  const int item_idx = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const PrefillItem item = a.items[item_idx];
+  if (item.n_segs <= 1) return;                  // (uniform) whole sequences need no map
+  constexpr int W_BYTES = (int)wu_w_bytes(D);
+  constexpr int64_t WU_BYTES = (int64_t)wu_chunk_bytes(D);
+  unsigned char* wu_base =
+      static_cast<unsigned char*>(a.seg_wu) + ((int64_t)item_idx * a.H + h) * a.seg_chunks * WU_BYTES;
+  const int64_t DD = (int64_t)D * D;
+  const uint32_t HDu = (uint32_t)a.H * D;
+  const int n_chunks = (item.n_tokens + C - 1) / C;
+
+  // slice 0: the N rows 16 wave .. +15 (chain from S = 0), slice 1: the same
+  // rows of M (chain from the identity with v = 0); S^T in accumulator layout
+  f32x4 ST[2][KT];
+  {
+    const int l16 = threadIdx.x & 15, g = (threadIdx.x & 63) >> 4;
+    const int row = 16 * wave + l16;
+#pragma unroll
+    for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ST[0][kt][i] = 0.f;
+        ST[1][kt][i] = (row == 16 * kt + 4 * g + i) ? 1.f : 0.f;
+      }
+  }
+
+  float pre_alpha = 1.f, pre_beta = 0.f;          // wavefront 0: token `lane` of the next chunk
+  auto stage = [&](int ch) __attribute__((always_inline)) {
+    const int n = min(C, item.n_tokens - ch * C);
+    const int64_t tok0 = item.tok_begin + (int64_t)ch * C;
+    const int64_t row0 = (tok0 * a.H + h) * D;
+    const int lane = threadIdx.x & 63;
+    stage_rows_lds_swz<D, NW>(static_cast<const uint16_t*>(a.k) + row0, HDu, n, smem + P::RK + (ch & 1) * C * D * 2,
+                              wave, lane);
+    stage_rows_lds_swz<D, NW>(static_cast<const uint16_t*>(a.v) + row0, HDu, n, rawV, wave, lane);
+    if (wave == 0) {
+      const int64_t t = (tok0 + min(lane, n - 1)) * a.H + h;
+      pre_alpha = lane < n ? a.alpha[t] : 1.f;
+      pre_beta = lane < n ? a.beta[t] : 0.f;
+    }
+  };
+  if (n_chunks > 0) stage(0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int ch = 0; ch < n_chunks; ++ch) {
+    const int n = min(C, item.n_tokens - ch * C);
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));                // per-lane indices re-derived every chunk
+    const int lane = tid & 63, g = lane >> 4, l16 = lane & 15;
+    const unsigned char* rawK = smem + P::RK + (ch & 1) * C * D * 2;
+
+    // ---- P1: cumulative log2 decay (wavefront 0) ----------------------------
+    if (wave == 0) {
+      const float gcum = wave_inclusive_scan(log2_hw(pre_alpha), lane);
+      const float gl = __shfl(gcum, C - 1);
+      sGs[lane] = gcum;
+      sDec[lane] = lane < n ? exp2_hw(gcum) : 0.f;
+      sRem[lane] = exp2_hw(gl - gcum);
+      sBeta[lane] = pre_beta;
+      if (lane == 0) sGam[0] = exp2_hw(gl);
+    }
+    __syncthreads();
+
+    // ---- P3: Gram tiles L = beta_r K K^T 2^(G_r - G_i) (strictly lower), then
+    // the inverses of the four diagonal blocks (the eight-wavefront schedule)
+#pragma unroll
+    for (int run = 0; run < 2; ++run) {
+      int R, I0, I1;
+      if (!gram_run<NW, false>(wave, run, R, I0, I1)) break;
+      const int r = 16 * R + l16;
+      bf16x8 kr[D / 32];
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) kr[ks] = as_bf16x8(raw_chunk<D>(rawK, 16 * R + l16, 4 * ks + g, r < n));
+      const float gr = sGs[r], br = sBeta[r];
+      for (int I = I0; I <= I1; ++I) {
+        f32x4 accL = {0, 0, 0, 0};
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+          const int i = 16 * I + l16;
+          accL = mfma_bf16(as_bf16x8(raw_chunk<D>(rawK, i, 4 * ks + g, i < n)), kr[ks], accL);
+        }
+        const int i0 = 16 * I + 4 * g;
+        const f32x4 gi = *reinterpret_cast<const f32x4*>(sGs + i0);
+        f32x4 lv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lv[e] = (i0 + e < r) ? accL[e] * exp2_hw(fminf(gr - gi[e], 0.f)) * br : 0.f;
+        *reinterpret_cast<f32x4*>(sL + r * L::LDL + i0) = lv;
+        if (I == R) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (i0 + e < r) sL[(i0 + e) * L::LDL + r] = lv[e];
+        }
+      }
+    }
+    {
+      int d0, d1;
+      if (gram_diag<NW, false>(wave, d0, d1)) {
+        __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): the tiles are in LDS
+        __builtin_amdgcn_wave_barrier();
+        const int b = g < 2 ? d0 : d1;
+        float* Lb = sL + (16 * b) * L::LDL + 16 * b;
+        float x[16];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) x[rr] = (rr == l16) ? 1.f : 0.f;
+#pragma unroll
+        for (int i = 0; i < 15; ++i) {
+          float col[16];
+#pragma unroll
+          for (int q4 = i / 4; q4 < 4; ++q4) {
+            const f32x4 t = *reinterpret_cast<const f32x4*>(Lb + i * L::LDL + 4 * q4);
+            col[4 * q4] = t[0]; col[4 * q4 + 1] = t[1]; col[4 * q4 + 2] = t[2]; col[4 * q4 + 3] = t[3];
+          }
+#pragma unroll
+          for (int rr = i + 1; rr < 16; ++rr) x[rr] -= col[rr] * x[i];
+        }
+        __builtin_amdgcn_wave_barrier();
+        if ((g & 1) == 0) {
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) Lb[rr * L::LDL + l16] = x[rr];
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- P4: off-diagonal blocks of (I + L)^-1 into T~ = A Diag(beta) --------
+    {
+      const int wv = __builtin_amdgcn_readfirstlane(wave);
+      if (wv == 0) inverse_column<0, L>(sL, sBeta, sTh, sTl, lane);
+      else if (wv == 1) inverse_column<1, L>(sL, sBeta, sTh, sTl, lane);
+      else if (wv == 2) inverse_column<2, L>(sL, sBeta, sTh, sTl, lane);
+      else inverse_rest<NW, L>(sL, sBeta, sTh, sTl, wv - 3, lane);
+    }
+    __syncthreads();
+
+    // ---- P5: W^T tile kt = wave and U' for value slice `wave` ----------------
+    // K operand of W: raw k^T read transposed, times 2^G_c; V operand of U':
+    // raw v^T read transposed (bf16 values are exact in fp16).
+    f32x4 Up[4];
+    {
+      f32x4 accW[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) { accW[ct] = f32x4{0, 0, 0, 0}; Up[ct] = f32x4{0, 0, 0, 0}; }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        f16x8 th[4], tl[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          th[ct] = ld_std(sTh, L::LDTT, 16 * ct, 32 * ks, lane);
+          tl[ct] = ld_std(sTl, L::LDTT, 16 * ct, 32 * ks, lane);
+        }
+        const int c0 = 32 * ks + 8 * g;              // this lane group's chunk rows c0 .. c0 + 7
+        float dec[8];
+        {
+          const f32x4 d0 = *reinterpret_cast<const f32x4*>(sDec + c0);
+          const f32x4 d1 = *reinterpret_cast<const f32x4*>(sDec + c0 + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { dec[e] = d0[e]; dec[4 + e] = d1[e]; }
+        }
+        const float one[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+        const f16x8 bk = bf16x8_to_f16(tr_rows<D>(rawK, c0, c0 + 4, 16 * wave, lane), dec);
+        const f16x8 bv = bf16x8_to_f16(tr_rows<D>(rawV, c0, c0 + 4, 16 * wave, lane), one);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          accW[ct] = mfma_f16(bk, th[ct], accW[ct]);
+          accW[ct] = mfma_f16(bk, tl[ct], accW[ct]);
+          Up[ct] = mfma_f16(th[ct], bv, Up[ct]);
+          Up[ct] = mfma_f16(tl[ct], bv, Up[ct]);
+        }
+      }
+      // W[16ct + l16][16 wave + 4g .. +3] into LDS and straight into the stored
+      // record (the LDS image), then this slice's U' (one tile per lane); both
+      // issued before the barrier, so the record drains meanwhile
+      unsigned char* rec = wu_base + (int64_t)ch * WU_BYTES;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const f16x4 w4 = {(_Float16)accW[ct][0], (_Float16)accW[ct][1], (_Float16)accW[ct][2], (_Float16)accW[ct][3]};
+        const int off = (16 * ct + l16) * L::LDQ + 16 * wave + 4 * g;
+        *reinterpret_cast<f16x4*>(sW + off) = w4;
+        *reinterpret_cast<f16x4*>(rec + 2 * off) = w4;
+      }
+      f32x4* up = reinterpret_cast<f32x4*>(rec + W_BYTES);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) up[(wave * 4 + ct) * 64 + lane] = Up[ct];
+    }
+    __syncthreads();
+
+    // next chunk's raw rows (k into the other buffer, v over this chunk's,
+    // which P5 has finished reading), alpha and beta, while the chain runs
+    if (ch + 1 < n_chunks) stage(ch + 1);
+
+    // ---- P6: U = U' - W S0^T; S^T <- 2^G_n S^T + K^T (2^(G_n - G) * U) -------
+    {
+      f32x4 U[2][4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) { U[0][ct] = Up[ct]; U[1][ct] = f32x4{0, 0, 0, 0}; }
+      f16x8 sop[2][D / 32];
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) sop[sl][ks] = pack_perm(ST[sl][2 * ks], ST[sl][2 * ks + 1]);
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        f16x8 w[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) w[ct] = ld_perm(sW, L::LDQ, 16 * ct, 32 * ks, lane);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+          for (int sl = 0; sl < 2; ++sl) U[sl][ct] = mfma_f16(w[ct], -sop[sl][ks], U[sl][ct]);
+      }
+      // rows c = 16ct + 4g + i of U times 2^(G_n - G_c), as bf16 hi + lo
+      // permuted-K operands (K = chunk row, two steps of 32)
+      bf16x8 uh[2][2], ul[2][2];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const f32x4 rem = *reinterpret_cast<const f32x4*>(sRem + 16 * ct + 4 * g);
+#pragma unroll
+        for (int sl = 0; sl < 2; ++sl) U[sl][ct] *= rem;
+      }
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) split_tiles_bf16(U[sl][2 * ks], U[sl][2 * ks + 1], uh[sl][ks], ul[sl][ks]);
+      const float gam = sGam[0];
+#pragma unroll
+      for (int kb = 0; kb < KT; kb += 4) {
+        bf16x8 ka[4][2];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+            ka[t][ks] = tr_rows<D>(rawK, 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * (kb + t), lane);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+#pragma unroll
+          for (int sl = 0; sl < 2; ++sl) ST[sl][kb + t] *= gam;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int sl = 0; sl < 2; ++sl) {
+              ST[sl][kb + t] = mfma_bf16(ka[t][ks], uh[sl][ks], ST[sl][kb + t]);
+              ST[sl][kb + t] = mfma_bf16(ka[t][ks], ul[sl][ks], ST[sl][kb + t]);
+            }
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);               // the next chunk's rows have landed in LDS
+    __syncthreads();
+  }
+
+  // the segment's map: N rows (slice 0) then M rows (slice 1)
+  {
+    const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
+    float* maps = a.seg_maps + ((int64_t)item_idx * a.H + h) * 2 * DD;   // [M, N]
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) {
+      float* dst = maps + (sl == 0 ? DD : 0);
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt)
+        *reinterpret_cast<f32x4*>(dst + (16 * wave + l16) * D + 16 * kt + 4 * g) = ST[sl][kt];
     }
   }
 }
@@ -1817,10 +2211,26 @@ hipError_t launch_wu_pipe(const PrefillArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_map(const PrefillArgs& a, hipStream_t s) {
+  using P = LdsMap<D>;
+  static_assert(P::TOTAL <= 160 * 1024, "LDS budget");
+  auto kern = prefill_map_kernel<D>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, P::TOTAL);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(a.n_items * a.H), dim3(512), P::TOTAL, s, a);
+  return hipGetLastError();
+}
+
 template <int D, bool BF16, bool PK>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
   if (a.seg_chunks == 0) return launch_pass<D, BF16, PK, false, false>(a, s);
-  hipError_t e = launch_pass<D, BF16, PK, true, false>(a, s);   // pass 1: segment maps, W and U' per chunk
+  hipError_t e;                                                 // pass 1: segment maps, W and U' per chunk
+  if constexpr (D == 128 && BF16 && !PK)
+    e = launch_map<D>(a, s);
+  else
+    e = launch_pass<D, BF16, PK, true, false>(a, s);
   if (e != hipSuccess) return e;
   constexpr int scan_lds = (D * (D + 16) + 16 * (D + 4)) * 4;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(segment_scan_kernel<D>),
