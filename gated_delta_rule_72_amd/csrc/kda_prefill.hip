@@ -449,12 +449,6 @@ __device__ __forceinline__ void split_tiles_bf16(f32x4 t0, f32x4 t1, bf16x8& hi,
   const float x[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
   split8_bf16(x, hi, lo);
 }
-// c + a b as three bf16 products (hi hi + hi lo + lo hi), fp32 accumulation.
-__device__ __forceinline__ f32x4 mfma_split3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, f32x4 c) {
-  c = mfma_bf16(ah, bh, c);
-  c = mfma_bf16(ah, bl, c);
-  return mfma_bf16(al, bh, c);
-}
 // T~ rows 16R + 4g + i, column col of one accumulator tile (lane (g, l16)),
 // scaled by beta_col, as fp16 hi + lo.
 template <class L>
@@ -469,42 +463,46 @@ __device__ __forceinline__ void put_t_tile(_Float16* sTh, _Float16* sTl, f32x4 a
 }
 
 // Off-diagonal blocks of block column I of A = (I + L)^-1 (sL holds L below
-// the diagonal blocks and A_RR on them, fp32 row-major): one wavefront, the
-// column's tiles in accumulator layout (lane (g, l16): rows 4g+i, column
-// l16), every product a permuted-K split-bf16 MFMA over two 16-row tiles.
+// the diagonal blocks and A_RR on them, fp32 row-major): one wavefront, on
+// fp32 MFMA (16x16x4, no operand conversion). The column's tiles stay in
+// accumulator layout (lane (g, l16): rows 4g+i, column l16) and enter the
+// next products as the permuted-K operand (K-step s: lane group g supplies
+// k = 4g + s), against rows of L and A_RR read in the same order, all of
+// them read before the chain starts.
 template <int I, class L>
 __device__ __forceinline__ void inverse_column(const float* sL, const float* sBeta, _Float16* sTh, _Float16* sTl,
                                                int lane) {
   const int g = lane >> 4, l16 = lane & 15;
-  f32x4 Acol[4];
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4 Acol[4], lrow[4][3], drow[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) Acol[I][i] = sL[(16 * I + 4 * g + i) * L::LDL + 16 * I + l16];
-  const float bcol = sBeta[16 * I + l16];
-  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int R = I + 1; R < 4; ++R) {
-    const float* lrow = sL + (16 * R + l16) * L::LDL;
+    const float* lr = sL + (16 * R + l16) * L::LDL;
+#pragma unroll
+    for (int m = I; m < R; ++m) lrow[R][m - I] = *reinterpret_cast<const f32x4*>(lr + 16 * m + 4 * g);
+    drow[R] = *reinterpret_cast<const f32x4*>(lr + 16 * R + 4 * g);
+  }
+  const float bcol = sBeta[16 * I + l16];
+#pragma unroll
+  for (int R = I + 1; R < 4; ++R) {
     // acc = sum_{m=I}^{R-1} L_Rm A_mI
     f32x4 acc = zero;
 #pragma unroll
-    for (int m0 = I; m0 < R; m0 += 2) {
-      const bool two = m0 + 1 < R;
-      const f32x4 la = *reinterpret_cast<const f32x4*>(lrow + 16 * m0 + 4 * g);
-      const f32x4 lb = two ? *reinterpret_cast<const f32x4*>(lrow + 16 * (m0 + 1) + 4 * g) : zero;
-      bf16x8 ah, al, bh, bl;
-      split_tiles_bf16(la, lb, ah, al);
-      split_tiles_bf16(Acol[m0], two ? Acol[m0 + 1] : zero, bh, bl);
-      acc = mfma_split3(ah, al, bh, bl, acc);
-    }
+    for (int m = I; m < R; ++m)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) acc = mfma_f32(lrow[R][m - I][ks], Acol[m][ks], acc);
     // A_RI = -A_RR acc
-    bf16x8 ah, al, bh, bl;
-    split_tiles_bf16(*reinterpret_cast<const f32x4*>(lrow + 16 * R + 4 * g), zero, ah, al);
-    split_tiles_bf16(acc, zero, bh, bl);
-    const f32x4 res = mfma_split3(ah, al, bh, bl, zero);
+    f32x4 res = zero;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) res = mfma_f32(drow[R][ks], acc[ks], res);
 #pragma unroll
     for (int i = 0; i < 4; ++i) Acol[R][i] = -res[i];
-    put_t_tile<L>(sTh, sTl, Acol[R], bcol, 16 * R + 4 * g, 16 * I + l16);
   }
+  // T~_RI = A_RI Diag(beta), written once the chain is done
+#pragma unroll
+  for (int R = I + 1; R < 4; ++R) put_t_tile<L>(sTh, sTl, Acol[R], bcol, 16 * R + 4 * g, 16 * I + l16);
 }
 
 // The rest of T~ for wavefront w of the NW - 3 that run no column chain: the
@@ -1002,9 +1000,8 @@ void prefill_kernel(PrefillArgs a) {
       // The diagonal blocks A_RR are in place (P3). Block column I of the
       // off-diagonal part is one dependent chain on wavefront I (I = 0, 1, 2),
       //   A_RI = -A_RR (sum_{I<=m<R} L_Rm A_mI),   R = I+1 .. 3,
-      // on split-bf16 MFMA (three-term products of hi + lo operands, about 16
-      // significant bits, fp32 range and accumulation), with the column's
-      // blocks kept in accumulator registers; each A_RI goes straight into T~.
+      // on fp32 MFMA with the column's blocks kept in accumulator registers;
+      // each A_RI goes straight into T~.
       // The other wavefronts write the diagonal blocks of T~ and zero the
       // blocks above the diagonal. Meanwhile every wavefront stages V^T.
       {
@@ -1452,16 +1449,22 @@ void prefill_map_kernel(PrefillArgs a) {
         float x[16];
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) x[rr] = (rr == l16) ? 1.f : 0.f;
+        // row i of the transposed copy (L[r][i] for r > i) is read three
+        // steps ahead of its use, so the substitution waits on no LDS read
+        constexpr int AHEAD = 3;
+        f32x4 rows[AHEAD + 1][4];
+        auto fetch = [&](int i) __attribute__((always_inline)) {
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            if (q4 >= i / 4) rows[i % (AHEAD + 1)][q4] = *reinterpret_cast<const f32x4*>(Lb + i * L::LDL + 4 * q4);
+        };
+#pragma unroll
+        for (int i = 0; i < AHEAD; ++i) fetch(i);
 #pragma unroll
         for (int i = 0; i < 15; ++i) {
-          float col[16];
+          if (i + AHEAD < 15) fetch(i + AHEAD);
 #pragma unroll
-          for (int q4 = i / 4; q4 < 4; ++q4) {
-            const f32x4 t = *reinterpret_cast<const f32x4*>(Lb + i * L::LDL + 4 * q4);
-            col[4 * q4] = t[0]; col[4 * q4 + 1] = t[1]; col[4 * q4 + 2] = t[2]; col[4 * q4 + 3] = t[3];
-          }
-#pragma unroll
-          for (int rr = i + 1; rr < 16; ++rr) x[rr] -= col[rr] * x[i];
+          for (int rr = i + 1; rr < 16; ++rr) x[rr] -= rows[i % (AHEAD + 1)][rr / 4][rr % 4] * x[i];
         }
         __builtin_amdgcn_wave_barrier();
         if ((g & 1) == 0) {
@@ -1560,7 +1563,8 @@ void prefill_map_kernel(PrefillArgs a) {
           for (int sl = 0; sl < 2; ++sl) U[sl][ct] = mfma_f16(w[ct], -sop[sl][ks], U[sl][ct]);
       }
       // rows c = 16ct + 4g + i of U times 2^(G_n - G_c), as bf16 hi + lo
-      // permuted-K operands (K = chunk row, two steps of 32)
+      // permuted-K operands (K = chunk row, two steps of 32): the raw k^T
+      // operand is then the staged bf16 data itself, with no conversion
       bf16x8 uh[2][2], ul[2][2];
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
