@@ -359,7 +359,20 @@ def cpu_baseline(w, inp, tokens: int):
     return {"value": tokens / secs, "unit": "tokens/s", "cores": int(rep["threads"]), "kind": "oracle",
             "sample": (f"first {tokens} of {w.T} tokens" if tokens < w.T else f"all {w.T} tokens")
                       + f" of {w.name}, all {w.H} heads, fp64 token-by-token recurrence",
-            "seconds": round(secs, 3)}
+            "seconds": round(secs, 3), "cpu_model": cpu_model()}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (first "model name" of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def main(argv=None):
@@ -492,7 +505,7 @@ def main(argv=None):
         result["layer_front_back"] = layer
     if not args.no_backward and not args.prefill_only:
         bwd = {}
-        for bw in (wl.KDA_LAYER, wl.LONG_PREFILL):
+        for bw in (wl.KDA_LAYER, wl.LONG_PREFILL, wl.VARLEN):
             bms, ws_bytes, with_init = time_backward(kda, torch, bw, max(3, args.steps // 5), 1)
             bb, bf = backward_algorithmic(bw.T, bw.H, bw.dk, bw.num_seqs, bw.gate == "per_key",
                                           qkv_bytes=2 if bw.dtype == "bf16" else 4, with_init=with_init)

@@ -3,6 +3,7 @@
 // Nothing is enqueued before every check has passed.
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -409,6 +410,114 @@ void* scratch_address() {
   return addr[dev];
 }
 
+// Heads are independent in the backward. When the plan for all heads would
+// need more than kBackwardBudget bytes of workspace, the heads run in groups
+// of Hg: each group's inputs are gathered into contiguous [.., Hg, ..]
+// slices of the workspace, the backward runs on them, and the gradients are
+// scattered back.
+constexpr size_t kBackwardBudget = (size_t)48 << 30;
+// KDA_BACKWARD_BUDGET_BYTES in the environment lowers (or raises) the budget,
+// read at every call (tests force small groups with it).
+size_t backward_budget() {
+  const char* e = getenv("KDA_BACKWARD_BUDGET_BYTES");
+  if (!e || !*e) return kBackwardBudget;
+  const unsigned long long v = strtoull(e, nullptr, 10);
+  return v > 0 ? (size_t)v : kBackwardBudget;
+}
+struct GroupedBackward {
+  int Hg, groups;
+  BackwardPlan plan;                       // of one group of Hg heads
+  // gathered inputs and group outputs (offsets into the workspace)
+  size_t q_off, k_off, v_off, a_off, b_off, init_off, do_off, df_off;
+  size_t dq_off, dk_off, dv_off, da_off, db_off, di_off, bytes;
+};
+GroupedBackward plan_backward_grouped(const kda_shape* s, int32_t num_seqs, const int64_t* cu, int cus) {
+  GroupedBackward g{};
+  const int H = s->num_heads;
+  const size_t budget = backward_budget();
+  for (int groups = 1; groups <= H; ++groups) {
+    const int Hg = (H + groups - 1) / groups;
+    if (groups > 1 && (H + Hg - 1) / Hg != groups) continue;     // same Hg as fewer groups
+    kda_shape gs = *s;
+    gs.num_heads = Hg;
+    g.Hg = Hg;
+    g.groups = groups;
+    g.plan = plan_backward(&gs, num_seqs, cu, cus);
+    size_t plan_bytes = g.plan.bytes;
+    if (H % Hg) {                          // the last, smaller group plans its own segments
+      gs.num_heads = H % Hg;
+      const size_t last = plan_backward(&gs, num_seqs, cu, cus).bytes;
+      plan_bytes = last > plan_bytes ? last : plan_bytes;
+    }
+    size_t off = round_up(plan_bytes);
+    if (groups > 1) {
+      const size_t T = (size_t)cu[num_seqs], d = (size_t)s->d_k, N = (size_t)num_seqs;
+      const size_t es = s->qkv_dtype == KDA_BF16 ? 2 : 4;
+      const size_t a_el = s->gate == KDA_GATE_PER_KEY ? d : 1, st = N * Hg * d * d * 4;
+      auto take = [&](size_t& o, size_t n) { o = off; off += round_up(n); };
+      take(g.q_off, T * Hg * d * es); take(g.k_off, T * Hg * d * es); take(g.v_off, T * Hg * d * es);
+      take(g.a_off, T * Hg * a_el * 4); take(g.b_off, T * Hg * 4); take(g.init_off, st);
+      take(g.do_off, T * Hg * d * 4); take(g.df_off, st);
+      take(g.dq_off, T * Hg * d * 4); take(g.dk_off, T * Hg * d * 4); take(g.dv_off, T * Hg * d * 4);
+      take(g.da_off, T * Hg * a_el * 4); take(g.db_off, T * Hg * 4); take(g.di_off, st);
+    }
+    g.bytes = off;
+    if (g.bytes <= budget || Hg == 1) break;
+  }
+  return g;
+}
+
+// One backward launch sequence (forward recompute, then the backward kernels)
+// on H = shape->num_heads heads whose tensors start at the given pointers.
+int run_backward(const kda_shape* shape, int32_t num_seqs, const int64_t* cu_seqlens_dev, const BackwardPlan& plan,
+                 const void* q, const void* k, const void* v, const float* alpha, const float* beta,
+                 const float* initial_state, const float* d_o, const float* d_final_state, float* dq, float* dk,
+                 float* dv, float* dalpha, float* dbeta, float* d_initial_state, char* ws, hipStream_t st) {
+  const bool bf16 = shape->qkv_dtype == KDA_BF16, pk = shape->gate == KDA_GATE_PER_KEY;
+  // 1. the forward again, keeping the state after every 64 tokens
+  kda::PrefillArgs f{};
+  f.q = q; f.k = k; f.v = v; f.alpha = alpha; f.beta = beta; f.init = initial_state;
+  f.o = reinterpret_cast<float*>(ws + plan.o_off);
+  f.final_state = reinterpret_cast<float*>(ws + plan.fin_off);
+  f.snapshots = plan.n_snap > 0 ? reinterpret_cast<float*>(ws + plan.snap_off) : nullptr;
+  f.cu_dev = cu_seqlens_dev;
+  f.num_seqs = num_seqs;
+  f.H = shape->num_heads;
+  f.interval = kChunk;
+  f.seg_chunks = plan.fwd.seg_chunks;
+  f.n_items = plan.fwd.n_items;
+  f.items = reinterpret_cast<kda::PrefillItem*>(ws + plan.fwd.items_off);
+  f.seq_first_item = reinterpret_cast<int32_t*>(ws + plan.fwd.first_off);
+  f.seg_maps = plan.fwd.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.fwd.maps_off) : nullptr;
+  f.seg_states = plan.fwd.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.fwd.states_off) : nullptr;
+  f.seg_wu = plan.fwd.seg_chunks > 0 ? static_cast<void*>(ws + plan.fwd.wu_off) : nullptr;
+  f.any_whole = plan.fwd.any_whole;
+  hipError_t e = kda::launch_prefill(f, shape->d_k, bf16, pk, st);
+  if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "backward: forward launch failed: %s", hipGetErrorString(e));
+
+  // 2. the backward kernels
+  kda::BackwardArgs b{};
+  b.q = q; b.k = k; b.v = v; b.alpha = alpha; b.beta = beta; b.init = initial_state;
+  b.d_o = d_o; b.d_final = d_final_state;
+  b.dq = dq; b.dk = dk; b.dv = dv; b.dalpha = dalpha; b.dbeta = dbeta; b.d_init = d_initial_state;
+  b.cu_dev = cu_seqlens_dev;
+  b.num_seqs = num_seqs;
+  b.H = shape->num_heads;
+  b.n_chunks = plan.n_chunks;
+  b.states = reinterpret_cast<const float*>(ws + plan.snap_off);
+  b.chunk_base = reinterpret_cast<int64_t*>(ws + plan.cb_off);
+  b.snap_base = reinterpret_cast<int64_t*>(ws + plan.sb_off);
+  b.item_base = reinterpret_cast<int64_t*>(ws + plan.ib_off);
+  b.seg_chunks = plan.seg_chunks;
+  b.n_items = plan.n_items;
+  b.seg_maps = plan.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.maps_off) : nullptr;
+  b.seg_end = plan.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.ends_off) : nullptr;
+  b.ws = reinterpret_cast<float*>(ws + plan.ws_off);
+  e = kda::launch_backward(b, shape->d_k, bf16, pk, st);
+  if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "backward launch failed: %s", hipGetErrorString(e));
+  return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -708,7 +817,7 @@ int kda_prefill_backward_workspace_size(const kda_shape* shape, int32_t num_seqs
   if (rc != KDA_OK) return rc;
   rc = check_cu(num_seqs, cu_seqlens_host);
   if (rc != KDA_OK) return rc;
-  *bytes = plan_backward(shape, num_seqs, cu_seqlens_host, device_cu_count()).bytes;
+  *bytes = plan_backward_grouped(shape, num_seqs, cu_seqlens_host, device_cu_count()).bytes;
   g_err[0] = '\0';
   return KDA_OK;
 }
@@ -760,55 +869,66 @@ int kda_prefill_backward(const kda_shape* shape, int32_t num_seqs, const int64_t
     g_err[0] = '\0';
     return KDA_OK;
   }
-  const BackwardPlan plan = plan_backward(shape, num_seqs, cu_seqlens_host, device_cu_count());
-  if (!workspace || workspace_bytes < plan.bytes)
-    return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", plan.bytes,
+  const GroupedBackward gp = plan_backward_grouped(shape, num_seqs, cu_seqlens_host, device_cu_count());
+  if (!workspace || workspace_bytes < gp.bytes)
+    return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", gp.bytes,
                 workspace ? workspace_bytes : (size_t)0);
   char* ws = static_cast<char*>(workspace);
   const hipStream_t st = static_cast<hipStream_t>(hip_stream);
-  const bool bf16 = shape->qkv_dtype == KDA_BF16, pk = shape->gate == KDA_GATE_PER_KEY;
-
-  // 1. the forward again, keeping the state after every 64 tokens
-  kda::PrefillArgs f{};
-  f.q = q; f.k = k; f.v = v; f.alpha = alpha; f.beta = beta; f.init = initial_state;
-  f.o = reinterpret_cast<float*>(ws + plan.o_off);
-  f.final_state = reinterpret_cast<float*>(ws + plan.fin_off);
-  f.snapshots = plan.n_snap > 0 ? reinterpret_cast<float*>(ws + plan.snap_off) : nullptr;
-  f.cu_dev = cu_seqlens_dev;
-  f.num_seqs = num_seqs;
-  f.H = shape->num_heads;
-  f.interval = kChunk;
-  f.seg_chunks = plan.fwd.seg_chunks;
-  f.n_items = plan.fwd.n_items;
-  f.items = reinterpret_cast<kda::PrefillItem*>(ws + plan.fwd.items_off);
-  f.seq_first_item = reinterpret_cast<int32_t*>(ws + plan.fwd.first_off);
-  f.seg_maps = plan.fwd.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.fwd.maps_off) : nullptr;
-  f.seg_states = plan.fwd.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.fwd.states_off) : nullptr;
-  f.seg_wu = plan.fwd.seg_chunks > 0 ? static_cast<void*>(ws + plan.fwd.wu_off) : nullptr;
-  f.any_whole = plan.fwd.any_whole;
-  hipError_t e = kda::launch_prefill(f, shape->d_k, bf16, pk, st);
-  if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "backward: forward launch failed: %s", hipGetErrorString(e));
-
-  // 2. the backward kernels
-  kda::BackwardArgs b{};
-  b.q = q; b.k = k; b.v = v; b.alpha = alpha; b.beta = beta; b.init = initial_state;
-  b.d_o = d_o; b.d_final = d_final_state;
-  b.dq = dq; b.dk = dk; b.dv = dv; b.dalpha = dalpha; b.dbeta = dbeta; b.d_init = d_initial_state;
-  b.cu_dev = cu_seqlens_dev;
-  b.num_seqs = num_seqs;
-  b.H = shape->num_heads;
-  b.n_chunks = plan.n_chunks;
-  b.states = reinterpret_cast<const float*>(ws + plan.snap_off);
-  b.chunk_base = reinterpret_cast<int64_t*>(ws + plan.cb_off);
-  b.snap_base = reinterpret_cast<int64_t*>(ws + plan.sb_off);
-  b.item_base = reinterpret_cast<int64_t*>(ws + plan.ib_off);
-  b.seg_chunks = plan.seg_chunks;
-  b.n_items = plan.n_items;
-  b.seg_maps = plan.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.maps_off) : nullptr;
-  b.seg_end = plan.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.ends_off) : nullptr;
-  b.ws = reinterpret_cast<float*>(ws + plan.ws_off);
-  e = kda::launch_backward(b, shape->d_k, bf16, pk, st);
-  if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "backward launch failed: %s", hipGetErrorString(e));
+  if (gp.groups == 1) {
+    rc = run_backward(shape, num_seqs, cu_seqlens_dev, gp.plan, q, k, v, alpha, beta, initial_state, d_o,
+                      d_final_state, dq, dk, dv, dalpha, dbeta, d_initial_state, ws, st);
+    if (rc != KDA_OK) return rc;
+    g_err[0] = '\0';
+    return KDA_OK;
+  }
+  // heads in groups: gather, run, scatter (row copies over tokens or sequences)
+  const int H = shape->num_heads;
+  const int64_t N = num_seqs, d = shape->d_k;
+  const int64_t es = shape->qkv_dtype == KDA_BF16 ? 2 : 4;
+  const int64_t a_el = shape->gate == KDA_GATE_PER_KEY ? d : 1, dd4 = d * d * 4;
+  for (int h0 = 0; h0 < H; h0 += gp.Hg) {
+    const int hg = H - h0 < gp.Hg ? H - h0 : gp.Hg;
+    kda_shape gs = *shape;
+    gs.num_heads = hg;
+    const BackwardPlan plan = plan_backward(&gs, num_seqs, cu_seqlens_host, device_cu_count());
+    auto at = [&](size_t off) { return ws + off; };
+    // gather: rows of T tokens (or N sequences), this group's heads
+    auto gather = [&](const void* src, size_t dst_off, int64_t rows, int64_t head_bytes) {
+      return kda::launch_copy_rows(static_cast<const char*>(src) + h0 * head_bytes, at(dst_off), rows, H * head_bytes,
+                                   hg * head_bytes, hg * head_bytes, 0, st);
+    };
+    auto scatter = [&](size_t src_off, void* dst, int64_t rows, int64_t head_bytes) {
+      return kda::launch_copy_rows(at(src_off), static_cast<char*>(dst) + h0 * head_bytes, rows, hg * head_bytes,
+                                   H * head_bytes, hg * head_bytes, 0, st);
+    };
+    hipError_t e = gather(q, gp.q_off, T, d * es);
+    if (e == hipSuccess) e = gather(k, gp.k_off, T, d * es);
+    if (e == hipSuccess) e = gather(v, gp.v_off, T, d * es);
+    if (e == hipSuccess) e = gather(alpha, gp.a_off, T, a_el * 4);
+    if (e == hipSuccess) e = gather(beta, gp.b_off, T, 4);
+    if (e == hipSuccess) e = gather(d_o, gp.do_off, T, d * 4);
+    if (e == hipSuccess && initial_state) e = gather(initial_state, gp.init_off, N, dd4);
+    if (e == hipSuccess && d_final_state) e = gather(d_final_state, gp.df_off, N, dd4);
+    if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "backward gather failed: %s", hipGetErrorString(e));
+    rc = run_backward(&gs, num_seqs, cu_seqlens_dev, plan, at(gp.q_off), at(gp.k_off), at(gp.v_off),
+                      reinterpret_cast<const float*>(at(gp.a_off)), reinterpret_cast<const float*>(at(gp.b_off)),
+                      initial_state ? reinterpret_cast<const float*>(at(gp.init_off)) : nullptr,
+                      reinterpret_cast<const float*>(at(gp.do_off)),
+                      d_final_state ? reinterpret_cast<const float*>(at(gp.df_off)) : nullptr,
+                      reinterpret_cast<float*>(at(gp.dq_off)), reinterpret_cast<float*>(at(gp.dk_off)),
+                      reinterpret_cast<float*>(at(gp.dv_off)), reinterpret_cast<float*>(at(gp.da_off)),
+                      reinterpret_cast<float*>(at(gp.db_off)),
+                      d_initial_state ? reinterpret_cast<float*>(at(gp.di_off)) : nullptr, ws, st);
+    if (rc != KDA_OK) return rc;
+    e = scatter(gp.dq_off, dq, T, d * 4);
+    if (e == hipSuccess) e = scatter(gp.dk_off, dk, T, d * 4);
+    if (e == hipSuccess) e = scatter(gp.dv_off, dv, T, d * 4);
+    if (e == hipSuccess) e = scatter(gp.da_off, dalpha, T, a_el * 4);
+    if (e == hipSuccess) e = scatter(gp.db_off, dbeta, T, 4);
+    if (e == hipSuccess && d_initial_state) e = scatter(gp.di_off, d_initial_state, N, dd4);
+    if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "backward scatter failed: %s", hipGetErrorString(e));
+  }
   g_err[0] = '\0';
   return KDA_OK;
 }

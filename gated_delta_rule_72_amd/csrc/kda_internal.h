@@ -89,10 +89,10 @@ struct PrefillArgs {
                              // and value head h takes q, k, alpha, beta of head h >> 1 of H / 2
 };
 hipError_t launch_prefill(PrefillArgs a, int d, bool bf16, bool per_key, hipStream_t s);
-// Row copy with zero fill, in 16-byte units: for r < n_rows, bytes [0, copy) of
-// dst row r (stride dst_stride) take those of src row r (stride src_stride)
-// and bytes [copy, copy + fill) are zeroed. All sizes and strides are multiples
-// of 16 and both pointers 16-byte aligned.
+// Row copy with zero fill: for r < n_rows, bytes [0, copy) of dst row r
+// (stride dst_stride) take those of src row r (stride src_stride) and bytes
+// [copy, copy + fill) are zeroed. Sizes, strides and both pointers are
+// multiples of 4 bytes (moved in 16-byte pieces when all are multiples of 16).
 hipError_t launch_copy_rows(const void* src, void* dst, int64_t n_rows, int64_t src_stride,
                             int64_t dst_stride, int64_t copy, int64_t fill, hipStream_t s);
 // Bytes of one chunk's stored W and U' at d = d_k = d_v: W as 64 rows of d + 8

@@ -2114,79 +2114,116 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(PrefillArgs a) {
 }
 
 // Work table. Unsegmented: one item per sequence, longest first (ties keep
-// sequence order). Segmented: each sequence is cut into runs of seg_chunks
-// chunks, items in sequence then segment order, with each sequence's first
-// item recorded. Every item carries the first snapshot slot of its sequence.
-// A single workgroup; lengths come from the device copy of cu_seqlens.
-__global__ __launch_bounds__(256) void build_items_kernel(PrefillArgs a) {
+// sequence order) for packs of up to kSortMax sequences, sequence order
+// beyond. Segmented: each sequence is cut into runs of seg_chunks chunks,
+// items in sequence then segment order, with each sequence's first item
+// recorded. Every item carries the first snapshot slot of its sequence.
+// A single workgroup of 1024 threads; lengths come from the device copy of
+// cu_seqlens. The longest-first order is a bitonic sort in LDS of the keys
+// (~len << 32 | n), O(N log^2 N) over the workgroup.
+constexpr int kSortMax = 8192;
+__global__ __launch_bounds__(1024) void build_items_kernel(PrefillArgs a) {
+  constexpr int NT = 1024;
+  extern __shared__ __align__(16) unsigned char smem[];
+  int64_t* snap_base = reinterpret_cast<int64_t*>(smem);                // [kSortMax] (sorted plans)
+  uint64_t* keys = reinterpret_cast<uint64_t*>(smem + kSortMax * 8);    // [kSortMax]
   __shared__ int64_t carry_snap;
   __shared__ int32_t carry_items;
-  __shared__ int64_t part_snap[256];
-  __shared__ int32_t part_items[256];
+  __shared__ int64_t part_snap[NT];
+  __shared__ int32_t part_items[NT];
   const int32_t N = a.num_seqs;
   const int64_t* cu = a.cu_dev;
   const int64_t seg_tokens = (int64_t)a.seg_chunks * C;
-  if (threadIdx.x == 0) { carry_snap = 0; carry_items = 0; }
+  const bool sorted = a.seg_chunks == 0 && N <= kSortMax;
+  const int tid = threadIdx.x;
+  if (tid == 0) { carry_snap = 0; carry_items = 0; }
   __syncthreads();
-  for (int32_t base = 0; base < N; base += 256) {
-    const int32_t n = base + threadIdx.x;
+  // prefix sums over sequences (snapshot slots, items) in blocks of NT
+  for (int32_t base = 0; base < N; base += NT) {
+    const int32_t n = base + tid;
     const int64_t len = n < N ? cu[n + 1] - cu[n] : 0;
     const int64_t ns = (n < N && a.interval > 0) ? len / a.interval : 0;
     int32_t nseg = n < N ? 1 : 0;
     if (n < N && seg_tokens > 0 && len > seg_tokens) nseg = (int32_t)((len + seg_tokens - 1) / seg_tokens);
-    part_snap[threadIdx.x] = ns;
-    part_items[threadIdx.x] = nseg;
+    part_snap[tid] = ns;
+    part_items[tid] = nseg;
     __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      const int64_t ys = threadIdx.x >= off ? part_snap[threadIdx.x - off] : 0;
-      const int32_t yi = threadIdx.x >= off ? part_items[threadIdx.x - off] : 0;
+    for (int off = 1; off < NT; off <<= 1) {
+      const int64_t ys = tid >= off ? part_snap[tid - off] : 0;
+      const int32_t yi = tid >= off ? part_items[tid - off] : 0;
       __syncthreads();
-      part_snap[threadIdx.x] += ys;
-      part_items[threadIdx.x] += yi;
+      part_snap[tid] += ys;
+      part_items[tid] += yi;
       __syncthreads();
     }
     if (n < N) {
-      const int64_t snap_base = carry_snap + part_snap[threadIdx.x] - ns;
-      const int32_t first = carry_items + part_items[threadIdx.x] - nseg;
-      if (a.seg_chunks == 0) {
-        int32_t rank = n;
-        if (N <= 8192) {  // longest first for load balance
-          rank = 0;
-          for (int32_t m = 0; m < N; ++m) {
-            const int64_t lm = cu[m + 1] - cu[m];
-            rank += (lm > len) || (lm == len && m < n);
-          }
-        }
+      const int64_t sb = carry_snap + part_snap[tid] - ns;
+      const int32_t first = carry_items + part_items[tid] - nseg;
+      if (sorted) {
+        snap_base[n] = sb;
+        keys[n] = ((uint64_t)(~(uint32_t)len) << 32) | (uint32_t)n;   // ascending: longest first
+      } else if (a.seg_chunks == 0) {
         PrefillItem it;
         it.tok_begin = cu[n];
         it.tok_in_seq = 0;
-        it.snap_base = snap_base;
+        it.snap_base = sb;
         it.n_tokens = (int32_t)len;
         it.seq = n;
         it.seg = 0;
         it.n_segs = 1;
-        a.items[rank] = it;
+        a.items[n] = it;
       } else {
         a.seq_first_item[n] = first;
-        for (int32_t s = 0; s < nseg; ++s) {
+        for (int32_t sg = 0; sg < nseg; ++sg) {
           PrefillItem it;
-          it.tok_in_seq = (int64_t)s * seg_tokens;
+          it.tok_in_seq = (int64_t)sg * seg_tokens;
           it.tok_begin = cu[n] + it.tok_in_seq;
-          it.snap_base = snap_base;
+          it.snap_base = sb;
           it.n_tokens = (int32_t)(nseg == 1 ? len : min(seg_tokens, len - it.tok_in_seq));
           it.seq = n;
-          it.seg = s;
+          it.seg = sg;
           it.n_segs = nseg;
-          a.items[first + s] = it;
+          a.items[first + sg] = it;
         }
       }
     }
     __syncthreads();
-    if (threadIdx.x == 255) {
-      carry_snap += part_snap[255];
-      carry_items += part_items[255];
+    if (tid == NT - 1) {
+      carry_snap += part_snap[NT - 1];
+      carry_items += part_items[NT - 1];
     }
     __syncthreads();
+  }
+  if (!sorted) return;                           // (uniform)
+  // bitonic sort of the keys, padded to a power of two with the largest key
+  int P = 1;
+  while (P < N) P <<= 1;
+  for (int e = N + tid; e < P; e += NT) keys[e] = ~(uint64_t)0;
+  __syncthreads();
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int e = tid; e < P; e += NT) {
+        const int f = e ^ j;
+        if (f > e) {
+          const uint64_t x = keys[e], y = keys[f];
+          const bool up = (e & k) == 0;
+          if ((x > y) == up) { keys[e] = y; keys[f] = x; }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int p = tid; p < N; p += NT) {
+    const int32_t n = (int32_t)(keys[p] & 0xFFFFFFFFu);
+    PrefillItem it;
+    it.tok_begin = cu[n];
+    it.tok_in_seq = 0;
+    it.snap_base = snap_base[n];
+    it.n_tokens = (int32_t)(cu[n + 1] - cu[n]);
+    it.seq = n;
+    it.seg = 0;
+    it.n_segs = 1;
+    a.items[p] = it;
   }
 }
 
@@ -2251,17 +2288,17 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
   return launch_pass<D, BF16, PK, false, false>(a, s);          // sequences that are not split
 }
 
-// Row copy with zero fill (see launch_copy_rows): one 16-byte piece per thread,
-// blockIdx.y over rows in steps of 65535.
-__global__ __launch_bounds__(256) void copy_rows_kernel(const uint4* src, uint4* dst, int64_t n_rows,
-                                                        int64_t src_stride, int64_t dst_stride, int64_t copy,
-                                                        int64_t fill) {
-  const int64_t piece = (int64_t)blockIdx.x * 256 + threadIdx.x;   // 16-byte piece within the row
+// Row copy with zero fill (see launch_copy_rows): one piece (16 or 4 bytes)
+// per thread, blockIdx.y over rows in steps of 65535.
+template <class T>
+__global__ __launch_bounds__(256) void copy_rows_kernel(const T* src, T* dst, int64_t n_rows, int64_t src_stride,
+                                                        int64_t dst_stride, int64_t copy, int64_t fill) {
+  const int64_t piece = (int64_t)blockIdx.x * 256 + threadIdx.x;   // piece within the row
   if (piece >= copy + fill) return;
   for (int64_t r = blockIdx.y; r < n_rows; r += gridDim.y) {
-    uint4* d = dst + r * dst_stride + piece;
+    T* d = dst + r * dst_stride + piece;
     if (piece < copy) *d = src[r * src_stride + piece];
-    else *d = uint4{0u, 0u, 0u, 0u};
+    else *d = T{};
   }
 }
 
@@ -2270,16 +2307,27 @@ __global__ __launch_bounds__(256) void copy_rows_kernel(const uint4* src, uint4*
 hipError_t launch_copy_rows(const void* src, void* dst, int64_t n_rows, int64_t src_stride, int64_t dst_stride,
                             int64_t copy, int64_t fill, hipStream_t s) {
   if (n_rows <= 0 || copy + fill <= 0) return hipSuccess;
-  const int64_t pieces = (copy + fill) / 16;
+  const uintptr_t all = reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst) |
+                        (uintptr_t)src_stride | (uintptr_t)dst_stride | (uintptr_t)copy | (uintptr_t)fill;
+  const int unit = (all & 15) == 0 ? 16 : 4;        // 16-byte pieces where everything allows
+  const int64_t pieces = (copy + fill) / unit;
   const dim3 grid((unsigned)((pieces + 255) / 256), (unsigned)(n_rows < 65535 ? n_rows : 65535));
-  hipLaunchKernelGGL(copy_rows_kernel, grid, dim3(256), 0, s, static_cast<const uint4*>(src),
-                     static_cast<uint4*>(dst), n_rows, src_stride / 16, dst_stride / 16, copy / 16, fill / 16);
+  if (unit == 16)
+    hipLaunchKernelGGL(copy_rows_kernel<uint4>, grid, dim3(256), 0, s, static_cast<const uint4*>(src),
+                       static_cast<uint4*>(dst), n_rows, src_stride / 16, dst_stride / 16, copy / 16, fill / 16);
+  else
+    hipLaunchKernelGGL(copy_rows_kernel<uint32_t>, grid, dim3(256), 0, s, static_cast<const uint32_t*>(src),
+                       static_cast<uint32_t*>(dst), n_rows, src_stride / 4, dst_stride / 4, copy / 4, fill / 4);
   return hipGetLastError();
 }
 
 hipError_t launch_prefill(PrefillArgs a, int d, bool bf16, bool per_key, hipStream_t s) {
-  hipLaunchKernelGGL(build_items_kernel, dim3(1), dim3(256), 0, s, a);
-  hipError_t e = hipGetLastError();
+  constexpr int items_lds = kSortMax * 16;       // snapshot bases and sort keys
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(build_items_kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, items_lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(build_items_kernel, dim3(1), dim3(1024), items_lds, s, a);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (d == 64) {
     if (bf16) return per_key ? launch_t<64, true, true>(a, s) : launch_t<64, true, false>(a, s);

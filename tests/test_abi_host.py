@@ -432,3 +432,23 @@ def test_product_package_never_uses_the_oracle():
                 src = open(os.path.join(dirpath, fn)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle\b", src, flags=re.M), fn
                 assert "kda_oracle" not in src and "liboracle" not in src, fn
+
+
+def test_backward_workspace_in_head_groups(K, monkeypatch):
+    """Above the workspace budget (KDA_BACKWARD_BUDGET_BYTES, read at every
+    call) the backward plans its heads in groups: a smaller workspace that
+    still holds one head's plan plus its gathered inputs and gradients."""
+    cu = torch.tensor([0, 1100, 1700, 1703, 1703], dtype=torch.int64)
+    sh = K.make_shape(5, 64, 64, torch.bfloat16, True)
+    full = K.kda_prefill_backward_workspace_size(sh, cu)
+    one = K.kda_prefill_backward_workspace_size(K.make_shape(1, 64, 64, torch.bfloat16, True), cu)
+    monkeypatch.setenv("KDA_BACKWARD_BUDGET_BYTES", "1")
+    per_head = K.kda_prefill_backward_workspace_size(sh, cu)
+    T, d = 1703, 64
+    gathered = 3 * T * d * 2 + T * d * 4 + T * 4 + 4 * d * d * 4 + T * d * 4 + 4 * d * d * 4
+    outs = 3 * T * d * 4 + T * d * 4 + T * 4 + 4 * d * d * 4
+    assert one + gathered + outs <= per_head < full
+    monkeypatch.setenv("KDA_BACKWARD_BUDGET_BYTES", str(full - 1))
+    assert per_head <= K.kda_prefill_backward_workspace_size(sh, cu) < full
+    monkeypatch.delenv("KDA_BACKWARD_BUDGET_BYTES")
+    assert K.kda_prefill_backward_workspace_size(sh, cu) == full

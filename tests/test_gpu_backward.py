@@ -187,6 +187,59 @@ def test_backward_d_initial_may_be_d_final():
     _check(inp, d_o, d_f, (dq, dk, dv, da, db, buf))
 
 
+def _abi_backward(inp, d_o, d_final, d_initial):
+    """kda_prefill_backward through the C ABI with caller-chosen d_final and
+    d_initial buffers (they may be one buffer)."""
+    T, H, dk = inp["q"].shape
+    dv = inp["v"].shape[2]
+    f32 = dict(dtype=torch.float32, device=d_o.device)
+    dq, dk_, dv_ = torch.empty((T, H, dk), **f32), torch.empty((T, H, dk), **f32), torch.empty((T, H, dv), **f32)
+    da, db = torch.empty(inp["alpha"].shape, **f32), torch.empty((T, H), **f32)
+    shape = kda.make_shape(H, dk, dv, inp["q"].dtype, inp["alpha"].dim() == 3)
+    ws = torch.empty(kda.kda_prefill_backward_workspace_size(shape, inp["cu_seqlens_host"]), dtype=torch.uint8,
+                     device=d_o.device)
+    kda.kda_prefill_backward(shape, inp["cu_seqlens_host"], inp["cu_seqlens"], inp["q"], inp["k"], inp["v"],
+                             inp["alpha"], inp["beta"], inp["initial_state"], d_o, d_final, dq, dk_, dv_, da, db,
+                             d_initial, ws)
+    torch.cuda.synchronize()
+    return (dq, dk_, dv_, da, db, d_initial), ws.numel()
+
+
+@pytest.mark.parametrize("H,d,gate,dtype", [(5, 64, "per_key", "bf16"), (3, 128, "scalar", "fp32")])
+@pytest.mark.parametrize("budget", ["one_head", "below_full"])
+def test_backward_in_head_groups(H, d, gate, dtype, budget, monkeypatch):
+    """A workspace budget below what all heads need at once runs the heads in
+    groups (inputs gathered per group into the workspace, gradients scattered
+    back), here one head per group or groups of ceil(H/2) with a smaller last
+    group, on the shape whose state-gradient scan is cut into segments: a
+    smaller workspace, every gradient against the oracle, and d_initial
+    written over d_final equal bit for bit to separate buffers."""
+    w = custom(f"bwd_groups_{H}_{d}_{gate}", H=H, d=d, lens=(1100, 600, 3, 0), gate=gate, dtype=dtype,
+               s0_std=0.05, seed=88)
+    inp, d_o, d_f = _grads_in(w, device(), seed=89)
+    _, full = _abi_backward(inp, d_o, d_f, torch.empty_like(d_f))
+    monkeypatch.setenv("KDA_BACKWARD_BUDGET_BYTES", "1" if budget == "one_head" else str(full - 1))
+    got, grouped = _abi_backward(inp, d_o, d_f, torch.empty_like(d_f))
+    print(f"workspace {full} -> {grouped} bytes", flush=True)
+    assert grouped < full
+    _check(inp, d_o, d_f, got)
+    buf = d_f.clone()
+    alias, _ = _abi_backward(inp, d_o, buf, buf)
+    for x, r in zip(alias, got):
+        assert torch.equal(x, r)
+
+
+def test_backward_varlen_full_size():
+    """The varlen workload (32 packed sequences of U[1024, 32768] tokens, H=32,
+    d=128, per-key gate, initial states) at full size in the benchmark's
+    launch configuration; heads 0-3 and 28-31 against the oracle (about a
+    minute of host time, one thread per head)."""
+    w = wl.VARLEN
+    inp, d_o, d_f = _grads_in(w, device(), seed=92)
+    got = _run(inp, d_o, d_f)
+    _check(inp, d_o, d_f, got, heads=(0, 1, 2, 3, 28, 29, 30, 31))
+
+
 def test_backward_per_key_decay_at_the_limit():
     """Key channels whose decay over every 32 tokens is 2^-119.5, just inside
     the backward's stated limit of 2^-120 (decay factors relative to a chunk's

@@ -325,3 +325,20 @@ def test_per_key_decay_at_the_forward_limit(d, segment_tokens):
     inp = wl.make_prefill_inputs(w, dev)
     inp["alpha"] = _near_limit_alpha(inp, 99.5, 16)
     check_prefill(inp, run_prefill(inp, w.interval, segment_tokens), w.interval)
+
+
+@pytest.mark.parametrize("n_seqs,hi,d,gate", [(3000, 300, 64, "per_key"), (2000, 200, 128, "scalar"),
+                                              (9000, 40, 64, "per_key")])
+def test_many_short_sequences(n_seqs, hi, d, gate):
+    """Thousands of short packed sequences (lengths U[0, hi], empty ones
+    included) with snapshots every 64 tokens: up to 8192 sequences the work
+    table is sorted longest first, beyond that it keeps sequence order; every
+    sequence, snapshot and final state against the oracle."""
+    rng = np.random.Generator(np.random.PCG64(90 + d))
+    lens = tuple(int(x) for x in rng.integers(0, hi, endpoint=True, size=n_seqs))
+    w = custom(f"many_{n_seqs}_{d}_{gate}", H=2 if n_seqs < 8192 else 1, d=d, lens=lens, gate=gate,
+               interval=64, seed=91)
+    inp = wl.make_prefill_inputs(w, device())
+    outs = run_prefill(inp, w.interval)
+    assert outs[2].shape[0] == sum(L // 64 for L in lens)
+    check_prefill(inp, outs, w.interval)
