@@ -1305,6 +1305,7 @@ struct LdsMap {
 // r1 + {0..3} from the second; r0 and r1 are this lane group's row bases.
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 template <int D>
 __device__ __forceinline__ bf16x8 tr_rows(const unsigned char* raw, int r0, int r1, int col0, int lane) {
   const int j = lane & 15;
@@ -1542,6 +1543,10 @@ void prefill_map_kernel(PrefillArgs a) {
     if (ch + 1 < n_chunks) stage(ch + 1);
 
     // ---- P6: U = U' - W S0^T; S^T <- 2^G_n S^T + K^T (2^(G_n - G) * U) -------
+    // The M slice enters U only through its fp16 image. Once that image is
+    // zero in every lane of the wavefront (every |M| entry at most 2^-25), its
+    // U is zero and its step is exactly M <- 2^G_n M; since 2^G_n <= 1 the
+    // image stays zero, and the wavefront runs the N slice alone from then on.
     {
       f32x4 U[2][4];
 #pragma unroll
@@ -1551,6 +1556,14 @@ void prefill_map_kernel(PrefillArgs a) {
       for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) sop[sl][ks] = pack_perm(ST[sl][2 * ks], ST[sl][2 * ks + 1]);
+      uint32_t mbits = 0;
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        const i32x4 w4 = __builtin_bit_cast(i32x4, sop[1][ks]);
+        mbits |= (uint32_t)(w4[0] | w4[1] | w4[2] | w4[3]);
+      }
+      // +0 and -0 both count as zero
+      const bool m_live = __builtin_amdgcn_ballot_w64((mbits & 0x7FFF7FFFu) != 0) != 0;
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) {
         f16x8 w[4];
@@ -1558,9 +1571,11 @@ void prefill_map_kernel(PrefillArgs a) {
         for (int ct = 0; ct < 4; ++ct) w[ct] = ld_perm(sW, L::LDQ, 16 * ct, 32 * ks, lane);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
+        for (int ct = 0; ct < 4; ++ct) U[0][ct] = mfma_f16(w[ct], -sop[0][ks], U[0][ct]);
+        if (m_live) {
 #pragma unroll
-          for (int sl = 0; sl < 2; ++sl) U[sl][ct] = mfma_f16(w[ct], -sop[sl][ks], U[sl][ct]);
+          for (int ct = 0; ct < 4; ++ct) U[1][ct] = mfma_f16(w[ct], -sop[1][ks], U[1][ct]);
+        }
       }
       // rows c = 16ct + 4g + i of U times 2^(G_n - G_c), as bf16 hi + lo
       // permuted-K operands (K = chunk row, two steps of 32): the raw k^T
@@ -1573,9 +1588,11 @@ void prefill_map_kernel(PrefillArgs a) {
         for (int sl = 0; sl < 2; ++sl) U[sl][ct] *= rem;
       }
 #pragma unroll
-      for (int sl = 0; sl < 2; ++sl)
+      for (int ks = 0; ks < 2; ++ks) split_tiles_bf16(U[0][2 * ks], U[0][2 * ks + 1], uh[0][ks], ul[0][ks]);
+      if (m_live) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) split_tiles_bf16(U[sl][2 * ks], U[sl][2 * ks + 1], uh[sl][ks], ul[sl][ks]);
+        for (int ks = 0; ks < 2; ++ks) split_tiles_bf16(U[1][2 * ks], U[1][2 * ks + 1], uh[1][ks], ul[1][ks]);
+      }
       const float gam = sGam[0];
 #pragma unroll
       for (int kb = 0; kb < KT; kb += 4) {
@@ -1591,12 +1608,17 @@ void prefill_map_kernel(PrefillArgs a) {
 #pragma unroll
           for (int sl = 0; sl < 2; ++sl) ST[sl][kb + t] *= gam;
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
+          for (int ks = 0; ks < 2; ++ks) {
+            ST[0][kb + t] = mfma_bf16(ka[t][ks], uh[0][ks], ST[0][kb + t]);
+            ST[0][kb + t] = mfma_bf16(ka[t][ks], ul[0][ks], ST[0][kb + t]);
+          }
+          if (m_live) {
 #pragma unroll
-            for (int sl = 0; sl < 2; ++sl) {
-              ST[sl][kb + t] = mfma_bf16(ka[t][ks], uh[sl][ks], ST[sl][kb + t]);
-              ST[sl][kb + t] = mfma_bf16(ka[t][ks], ul[sl][ks], ST[sl][kb + t]);
+            for (int ks = 0; ks < 2; ++ks) {
+              ST[1][kb + t] = mfma_bf16(ka[t][ks], uh[1][ks], ST[1][kb + t]);
+              ST[1][kb + t] = mfma_bf16(ka[t][ks], ul[1][ks], ST[1][kb + t]);
             }
+          }
         }
       }
     }
@@ -1729,7 +1751,7 @@ void prefill_wu_pipe_kernel(PrefillArgs a) {
   // producers' raw rows of the chunk after it (live across a whole chunk on
   // either side): carry[j] = k rows, carry[RI + j] = q rows; chain: U' tile
   // (sl, ct) at carry[4 sl + ct].
-  typedef int i32x4 __attribute__((ext_vector_type(4)));
+
   static_assert(2 * RI == 4 * SPW, "one carry array fits both roles");
   i32x4 carry[2 * RI];
   float pre_alpha = 1.f;
