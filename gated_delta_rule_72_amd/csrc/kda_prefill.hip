@@ -183,15 +183,14 @@ struct RawGroup<false> { f32x4 a, b; };
 // `base` is uniform over the workgroup (scalar registers); `off` is the lane's
 // 32-bit element offset from it, so loads use the scalar-base addressing form.
 template <bool BF16>
-__device__ __forceinline__ RawGroup<BF16> load_group(const void* base, uint32_t off, bool valid) {
+__device__ __forceinline__ RawGroup<BF16> load_group(const void* base, uint32_t off) {
   RawGroup<BF16> r;
   if constexpr (BF16) {
-    r.w = valid ? *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off)
-                : uint4{0, 0, 0, 0};
+    r.w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
   } else {
     const float* p = static_cast<const float*>(base) + off;
-    r.a = valid ? *reinterpret_cast<const f32x4*>(p) : f32x4{0, 0, 0, 0};
-    r.b = valid ? *reinterpret_cast<const f32x4*>(p + 4) : f32x4{0, 0, 0, 0};
+    r.a = *reinterpret_cast<const f32x4*>(p);
+    r.b = *reinterpret_cast<const f32x4*>(p + 4);
   }
   return r;
 }
@@ -328,61 +327,58 @@ struct ChunkRegs {
 };
 
 // Every address is a workgroup-uniform base (scalar registers, cheap to
-// recompute per access) plus one 32-bit per-lane offset that does not depend
-// on the loop index, so no per-access offsets are kept live.
+// recompute per access) plus a 32-bit per-lane offset.
 // h is the value head (v, o and the state); q, k, alpha and beta belong to head
 // h >> qk_shift of a.H >> qk_shift (qk_shift = 1: d_v = 2 d_k, each head's state
 // rows split into two value heads of d_k rows that share q, k and the gates).
 template <int D, bool BF16, bool PER_KEY, int NT>
 __device__ __forceinline__ void load_chunk(ChunkRegs<D, BF16, PER_KEY, NT>& R, const PrefillArgs& a,
                                            int64_t tok0, int n, int h, int tid, bool load_v) {
+  // Every load is unconditional: rows and tokens past the chunk's n (>= 1)
+  // read row n - 1 again, and their values are masked where they are used
+  // (unpack_masked, the decay scan, beta). A load under a lane mask, or a
+  // select right after one, costs a branch per load and can make the compiler
+  // wait for every load in flight.
   using CR = ChunkRegs<D, BF16, PER_KEY, NT>;
   constexpr int ROWS_PER_PASS = NT / (D / 8);     // tokens covered by one group pass
   const int Hq = a.H >> a.qk_shift, hq = h >> a.qk_shift;
-  const int64_t HD = (int64_t)a.H * D;            // v elements per token (all heads)
-  const int64_t HDq = (int64_t)Hq * D;            // q/k/alpha elements per token
+  const uint32_t HD = (uint32_t)a.H * D;          // v elements per token (all heads)
+  const uint32_t HDq = (uint32_t)Hq * D;          // q/k/alpha elements per token
   const int64_t row0 = (tok0 * a.H + h) * D;      // first v element of this chunk and head
   const int64_t rowq0 = (tok0 * Hq + hq) * D;     // first q/k element
   const int c0 = tid / (D / 8), k8 = tid % (D / 8);
-  const uint32_t lane_off = (uint32_t)c0 * (uint32_t)HD + 8u * k8;
-  const uint32_t lane_offq = (uint32_t)c0 * (uint32_t)HDq + 8u * k8;
+  const int last = n - 1;
 #pragma unroll
   for (int j = 0; j < CR::GPT; ++j) {
-    const int c = c0 + j * ROWS_PER_PASS;
-    const bool valid = c < n;
-    const int64_t ub = row0 + (int64_t)j * ROWS_PER_PASS * HD;    // uniform
-    const int64_t ubq = rowq0 + (int64_t)j * ROWS_PER_PASS * HDq;
+    const uint32_t c = (uint32_t)min(c0 + j * ROWS_PER_PASS, last);
+    const uint32_t off = c * HD + 8u * k8, offq = c * HDq + 8u * k8;
     if constexpr (BF16) {
-      R.v[j] = load_group<true>(static_cast<const uint16_t*>(a.v) + ub, lane_off, valid && load_v);
+      if (load_v) R.v[j] = load_group<true>(static_cast<const uint16_t*>(a.v) + row0, off);
     } else {
-      R.k[j] = load_group<false>(static_cast<const float*>(a.k) + ubq, lane_offq, valid);
-      R.q[j] = load_group<false>(static_cast<const float*>(a.q) + ubq, lane_offq, valid);
-      R.v[j] = load_group<false>(static_cast<const float*>(a.v) + ub, lane_off, valid && load_v);
+      R.k[j] = load_group<false>(static_cast<const float*>(a.k) + rowq0, offq);
+      R.q[j] = load_group<false>(static_cast<const float*>(a.q) + rowq0, offq);
+      if (load_v) R.v[j] = load_group<false>(static_cast<const float*>(a.v) + row0, off);
     }
   }
-  const int wave = tid / 64, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   if constexpr (PER_KEY) {
     const int kcol = tid % D, cb = tid / D;
-    const uint32_t a_off = (uint32_t)(CR::TPB * cb) * (uint32_t)HDq + (uint32_t)kcol;
 #pragma unroll
     for (int j = 0; j < CR::TPB; ++j) {
-      const int c = CR::TPB * cb + j;
-      const float* ab = a.alpha + rowq0 + (int64_t)j * HDq;        // uniform
-      R.alpha[j] = c < n ? ab[a_off] : 1.f;
+      const uint32_t c = (uint32_t)min(CR::TPB * cb + j, last);
+      R.alpha[j] = a.alpha[rowq0 + c * HDq + kcol];
     }
   } else {
-    const float* ab = a.alpha + tok0 * Hq + hq;
-    R.alpha[0] = (wave == 0 && lane < n) ? ab[(uint32_t)lane * Hq] : 1.f;
+    R.alpha[0] = wave == 0 ? a.alpha[(tok0 + min(lane, last)) * Hq + hq] : 1.f;
   }
-  const float* bb = a.beta + tok0 * Hq + hq;
-  R.beta = (wave == 0 && lane < n) ? bb[(uint32_t)lane * Hq] : 0.f;
+  R.beta = wave == 0 ? a.beta[(tok0 + min(lane, last)) * Hq + hq] : 0.f;
 }
 
 // Gram tile pairs (R, I), R >= I, as runs of one row block per wavefront:
 // run `run` of wavefront `wave` covers (R, I0..I1); false when it has none.
-// Two wavefronts compute two diagonal pairs each and then invert both
-// diagonal blocks together (gram_diag). Balance counts a pair and an
-// inversion as one unit each, per SIMD:
+// A wavefront whose runs end on diagonal pairs then inverts those diagonal
+// blocks (gram_diag). Balance counts a pair and an inversion as one unit
+// each, per SIMD:
 //   four wavefronts:  w0: R3 I0-2 | w1: R2 I0-1, R1 I0 | w2: R0 I0, R1 I1, inv 0,1
 //                     | w3: R2 I2, R3 I3, inv 2,3                       (3/3/3/3)
 //   eight wavefronts (w and w+4 share a SIMD), scalar gate (cheap pairs):
@@ -390,9 +386,10 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<D, BF16, PER_KEY, NT>& R, c
 //                     inverts block b, so only one pair precedes each
 //                     inversion; w4: R3 I0-1 | w5: R3 I2, R2 I1 | w6: R2 I0 |
 //                     w7: R1 I0. Per-key gate (a pair costs more than an
-//                     inversion): w0: R0 I0, R1 I1, inv 0,1 | w1: R2 I2, R3 I3,
-//                     inv 2,3 | w2: R3 I0-1 | w3: R3 I2, R2 I1 | w6: R2 I0 |
-//                     w7: R1 I0                                (3/3/3/3)
+//                     inversion, and the pairs of a run share their row
+//                     operands): w0: R3 I0-1 | w1: R3 I2-3, inv 3 | w2: R2
+//                     I0-1 | w3: R2 I2, inv 2 | w4: R1 I0 | w5: R1 I1, inv 1 |
+//                     w6: R0 I0, inv 0 | w7: none
 // Four 12-bit run codes in the 16-bit fields of one 64-bit constant (field w
 // for wavefront w): the lookup is register arithmetic, not a memory load.
 constexpr uint64_t pack_runs(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
@@ -411,11 +408,10 @@ __device__ __forceinline__ bool gram_run(int wave_lane, int run, int& R, int& I0
   } else {
     static_assert(NW == 8, "four or eight wavefronts");
     constexpr uint64_t kRun0Lo = !PER_KEY ? pack_runs(0x000, 0x111, 0x222, 0x333)    // wavefronts 0-3
-                                          : pack_runs(0x000, 0x222, 0x301, 0x322);
+                                          : pack_runs(0x301, 0x323, 0x201, 0x222);
     constexpr uint64_t kRun0Hi = !PER_KEY ? pack_runs(0x301, 0x322, 0x200, 0x100)    // wavefronts 4-7
-                                          : pack_runs(0xFFF, 0xFFF, 0x200, 0x100);
-    constexpr uint64_t kRun1Lo = !PER_KEY ? pack_runs(0xFFF, 0xFFF, 0xFFF, 0xFFF)
-                                          : pack_runs(0x111, 0x333, 0xFFF, 0x211);
+                                          : pack_runs(0x100, 0x111, 0x000, 0xFFF);
+    constexpr uint64_t kRun1Lo = pack_runs(0xFFF, 0xFFF, 0xFFF, 0xFFF);
     constexpr uint64_t kRun1Hi = !PER_KEY ? pack_runs(0xFFF, 0x211, 0xFFF, 0xFFF)
                                           : pack_runs(0xFFF, 0xFFF, 0xFFF, 0xFFF);
     const bool hi = (wave & 7) >= 4;
@@ -432,11 +428,15 @@ __device__ __forceinline__ bool gram_run(int wave_lane, int run, int& R, int& I0
 // inverts one block), or false.
 template <int NW, bool PER_KEY>
 __device__ __forceinline__ bool gram_diag(int wave, int& d0, int& d1) {
-  if constexpr (NW == 4 || PER_KEY) {
-    const int wa = NW == 4 ? 2 : 0;              // the two wavefronts that invert
-    if (wave == wa) { d0 = 0; d1 = 1; return true; }
-    if (wave == wa + 1) { d0 = 2; d1 = 3; return true; }
+  if constexpr (NW == 4) {
+    if (wave == 2) { d0 = 0; d1 = 1; return true; }
+    if (wave == 3) { d0 = 2; d1 = 3; return true; }
     return false;
+  } else if constexpr (PER_KEY) {
+    // the wavefront whose run ends on the diagonal pair (b, b) inverts block b
+    const int b = wave == 6 ? 0 : wave == 5 ? 1 : wave == 3 ? 2 : wave == 1 ? 3 : -1;
+    d0 = d1 = b;
+    return b >= 0;
   } else {
     if (wave < 4) { d0 = wave; d1 = wave; return true; }
     return false;
@@ -721,10 +721,10 @@ void prefill_kernel(PrefillArgs a) {
         float x[8];
         unpack_group<BF16>(regs.k[j], x);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) kh[e] = (_Float16)x[e];
+        for (int e = 0; e < 8; ++e) kh[e] = (_Float16)(c < n ? x[e] : 0.f);
         unpack_group<BF16>(regs.q[j], x);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qh[e] = (_Float16)x[e];
+        for (int e = 0; e < 8; ++e) qh[e] = (_Float16)(c < n ? x[e] : 0.f);
         *reinterpret_cast<f16x8*>(sRK + c * L::LDQ + 8 * k8) = kh;
         if constexpr (!MAP) *reinterpret_cast<f16x8*>(sRQ + c * L::LDQ + 8 * k8) = qh;
       }
@@ -737,13 +737,13 @@ void prefill_kernel(PrefillArgs a) {
       float run = 0.f;
 #pragma unroll
       for (int j = 0; j < CR::TPB; ++j) {
-        run += log2_hw(regs.alpha[j]);
+        run += log2_hw(CR::TPB * cb + j < n ? regs.alpha[j] : 1.f);
         gloc[j] = run;
       }
       sPart[cb * D + kcol] = run;
     } else {
       if (wave == 0) {
-        const float gcum = wave_inclusive_scan(log2_hw(regs.alpha[0]), lane);
+        const float gcum = wave_inclusive_scan(log2_hw(lane < n ? regs.alpha[0] : 1.f), lane);
         sGs[lane] = gcum;
         const float gl = __shfl(gcum, C - 1);
         const float gam = exp2_hw(gl);
@@ -754,7 +754,7 @@ void prefill_kernel(PrefillArgs a) {
         if (D > 64) { sGL[lane + 64] = gl; sGam[lane + 64] = gam; }
       }
     }
-    if (wave == 0) sBeta[lane] = regs.beta;
+    if (wave == 0) sBeta[lane] = lane < n ? regs.beta : 0.f;
     __syncthreads();
     if constexpr (PER_KEY) {
       const int kcol = tid % D, cb = tid / D;
@@ -882,62 +882,84 @@ void prefill_kernel(PrefillArgs a) {
           // three-term bf16 products of operands decayed relative to token 16R:
           // row side 2^(G_r - G_16R) <= 1, column side 2^(G_16R - G_i) (<= 1
           // for i <= 16R, bounded inside block R). L and B share the column
-          // operand and the row-side factors.
+          // operand and the row-side factors. K-steps run outermost, so the
+          // row side of a K-step is formed once for every pair of the run;
+          // each tile still accumulates its K-steps in order.
+          constexpr int MAXI = NW == 4 ? 3 : 2;      // longest run (gram_run)
           const float br = sBeta[r];
-          for (int I = I0; I <= I1; ++I) {
-            const int i = 16 * I + l16;              // this lane's row of the column block
-            f32x4 accL = {0, 0, 0, 0}, accB = {0, 0, 0, 0};
+          f32x4 accL[MAXI], accB[MAXI];
 #pragma unroll
-            for (int ks = 0; ks < D / 32; ++ks) {
-              const int k0 = 32 * ks + 8 * g;
-              float kraw[8], iraw[8], qraw[8] = {};
-              if constexpr (BF16) {
-                bf16x8_to_f32(raw_chunk<D>(regA + L::A_RK, r, 4 * ks + g, r < n), kraw);
-                bf16x8_to_f32(raw_chunk<D>(regA + L::A_RK, i, 4 * ks + g, i < n), iraw);
-                if constexpr (!MAP) bf16x8_to_f32(raw_chunk<D>(regA + L::A_RQ, r, 4 * ks + g, r < n), qraw);
-              } else {
-                const f16x8 kh16 = *reinterpret_cast<const f16x8*>(sRK + r * L::LDQ + k0);
-                const f16x8 ih16 = *reinterpret_cast<const f16x8*>(sRK + i * L::LDQ + k0);
+          for (int t = 0; t < MAXI; ++t) { accL[t] = f32x4{0, 0, 0, 0}; accB[t] = f32x4{0, 0, 0, 0}; }
 #pragma unroll
-                for (int e = 0; e < 8; ++e) { kraw[e] = (float)kh16[e]; iraw[e] = (float)ih16[e]; }
-                if constexpr (!MAP) {
-                  const f16x8 qh16 = *reinterpret_cast<const f16x8*>(sRQ + r * L::LDQ + k0);
+          for (int ks = 0; ks < D / 32; ++ks) {
+            const int k0 = 32 * ks + 8 * g;
+            float kraw[8], qraw[8] = {};
+            if constexpr (BF16) {
+              bf16x8_to_f32(raw_chunk<D>(regA + L::A_RK, r, 4 * ks + g, r < n), kraw);
+              if constexpr (!MAP) bf16x8_to_f32(raw_chunk<D>(regA + L::A_RQ, r, 4 * ks + g, r < n), qraw);
+            } else {
+              const f16x8 kh16 = *reinterpret_cast<const f16x8*>(sRK + r * L::LDQ + k0);
 #pragma unroll
-                  for (int e = 0; e < 8; ++e) qraw[e] = (float)qh16[e];
-                }
-              }
-              float kv[8], qv[8], iv[8];
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const int kk = k0 + e;
-                const float gref = sG[(16 * R) * L::LDG + kk];
-                const float f = exp2_hw(sG[r * L::LDG + kk] - gref);
-                kv[e] = kraw[e] * f;
-                qv[e] = qraw[e] * f;
-                iv[e] = iraw[e] * exp2_hw(gref - sG[i * L::LDG + kk]);
-              }
-              bf16x8 kh, kl, qh, ql, ih, il;
-              split8_bf16(kv, kh, kl);
-              if constexpr (!MAP) split8_bf16(qv, qh, ql);
-              split8_bf16(iv, ih, il);
-              if constexpr (!WU) {
-                accL = mfma_bf16(ih, kh, accL);
-                accL = mfma_bf16(ih, kl, accL);
-                accL = mfma_bf16(il, kh, accL);
-              }
+              for (int e = 0; e < 8; ++e) kraw[e] = (float)kh16[e];
               if constexpr (!MAP) {
-                accB = mfma_bf16(ih, qh, accB);
-                accB = mfma_bf16(ih, ql, accB);
-                accB = mfma_bf16(il, qh, accB);
+                const f16x8 qh16 = *reinterpret_cast<const f16x8*>(sRQ + r * L::LDQ + k0);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qraw[e] = (float)qh16[e];
               }
             }
+            float kv[8], qv[8], gref[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int kk = k0 + e;
+              gref[e] = sG[(16 * R) * L::LDG + kk];
+              const float f = exp2_hw(sG[r * L::LDG + kk] - gref[e]);
+              kv[e] = kraw[e] * f;
+              qv[e] = qraw[e] * f;
+            }
+            bf16x8 kh, kl, qh, ql;
+            split8_bf16(kv, kh, kl);
+            if constexpr (!MAP) split8_bf16(qv, qh, ql);
+#pragma unroll
+            for (int t = 0; t < MAXI; ++t) {
+              const int I = I0 + t;
+              if (I > I1) break;                     // (uniform)
+              const int i = 16 * I + l16;            // this lane's row of the column block
+              float iraw[8];
+              if constexpr (BF16) {
+                bf16x8_to_f32(raw_chunk<D>(regA + L::A_RK, i, 4 * ks + g, i < n), iraw);
+              } else {
+                const f16x8 ih16 = *reinterpret_cast<const f16x8*>(sRK + i * L::LDQ + k0);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) iraw[e] = (float)ih16[e];
+              }
+              float iv[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) iv[e] = iraw[e] * exp2_hw(gref[e] - sG[i * L::LDG + k0 + e]);
+              bf16x8 ih, il;
+              split8_bf16(iv, ih, il);
+              if constexpr (!WU) {
+                accL[t] = mfma_bf16(ih, kh, accL[t]);
+                accL[t] = mfma_bf16(ih, kl, accL[t]);
+                accL[t] = mfma_bf16(il, kh, accL[t]);
+              }
+              if constexpr (!MAP) {
+                accB[t] = mfma_bf16(ih, qh, accB[t]);
+                accB[t] = mfma_bf16(ih, ql, accB[t]);
+                accB[t] = mfma_bf16(il, qh, accB[t]);
+              }
+            }
+          }
+#pragma unroll
+          for (int t = 0; t < MAXI; ++t) {
+            const int I = I0 + t;
+            if (I > I1) break;                       // (uniform)
             const int i0 = 16 * I + 4 * g;
             f32x4 lv;
             f16x4 bv;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              lv[e] = (i0 + e < r) ? accL[e] * br : 0.f;
-              bv[e] = (_Float16)((i0 + e <= r) ? accB[e] : 0.f);
+              lv[e] = (i0 + e < r) ? accL[t][e] * br : 0.f;
+              bv[e] = (_Float16)((i0 + e <= r) ? accB[t][e] : 0.f);
             }
             if constexpr (!WU) *reinterpret_cast<f32x4*>(sL + r * L::LDL + i0) = lv;
             if constexpr (!MAP) *reinterpret_cast<f16x4*>(sB + r * L::LDT + i0) = bv;
@@ -1030,6 +1052,8 @@ void prefill_kernel(PrefillArgs a) {
             }
           } else {
             unpack_group<BF16>(regs.v[j], x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = c < n ? x[e] : 0.f;   // rows past n repeat row n - 1
           }
 #pragma unroll
           for (int e = 0; e < 8; ++e) sVT[(8 * k8 + e) * L::LDT + swz(8 * k8 + e, c)] = (_Float16)x[e];
