@@ -99,6 +99,25 @@ def stored_traffic(name: str):
     return int(b.group(1))
 
 
+def stored_mfma(name: str):
+    """MFMA busy percentage per kernel of a workload's prefill, from the
+    counter summary profiles/mfma_activity_prefill.md (rocprofv3 pass over
+    SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE), or None if it is missing or
+    was taken on other kernel sources."""
+    import re
+    path = os.path.join(ROOT, "profiles", "mfma_activity_prefill.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"^sources_sha256_16:\s*([0-9a-f]{16})\s*$", text, flags=re.M)
+    if not m or m.group(1) != kernel_sources_digest():
+        return None
+    out = {}
+    for k, v in re.findall(r"^mfma_busy_pct " + re.escape(name) + r" (\S+): ([0-9.]+)$", text, flags=re.M):
+        out[k] = float(v)
+    return out or None
+
+
 def measure_ceilings(torch, reps: int = 5) -> dict:
     """Measured device ceilings (libkda_calib.so, include/kda_calib.h): a
     streaming 16-byte copy of 1 GiB and a dense fp16 MFMA loop, each timed with
@@ -450,6 +469,7 @@ def main(argv=None):
                    "gate": w.gate, "chunk": w.chunk, "qkv": w.dtype, "snapshot_interval": w.interval},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": stored_traffic(w.name),
+                     "mfma_busy_pct_counters": stored_mfma(w.name),
                      "kernel": "kda_prefill_chunked = build_items + prefill_kernel pass 1 + "
                                "segment_scan + prefill_wu_pipe_kernel pass 3 (automatic segment plan)",
                      "algorithmic_bytes_per_launch": int(pb), "algorithmic_flops_per_launch": int(pf),
@@ -479,7 +499,8 @@ def main(argv=None):
             other[ow.name] = {"ms_per_call": round(oavg, 4), "tokens_per_s": round(ow.T / (oavg * 1e-3), 1),
                               "hbm_GBs": round(ogbs, 1), "hbm_frac": round(ogbs / HBM_PEAK_GBS, 4),
                               "mfma_frac": round(of / (oavg * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
-                              "algorithmic_bytes": int(ob), "algorithmic_flops": int(of), "calls": len(oms)}
+                              "algorithmic_bytes": int(ob), "algorithmic_flops": int(of), "calls": len(oms),
+                              "mfma_busy_pct_counters": stored_mfma(ow.name)}
             if on_snap:
                 hms, _ = time_prefill(kda, torch, oinp, ow, max(5, args.steps // 2), args.warmup, snaps_on_host=True)
                 other[ow.name]["ms_per_call_snapshots_to_pinned_host"] = round(sum(hms) / len(hms), 4)

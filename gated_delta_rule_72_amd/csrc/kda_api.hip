@@ -414,8 +414,10 @@ void* scratch_address() {
 // need more than kBackwardBudget bytes of workspace, the heads run in groups
 // of Hg: each group's inputs are gathered into contiguous [.., Hg, ..]
 // slices of the workspace, the backward runs on them, and the gradients are
-// scattered back.
-constexpr size_t kBackwardBudget = (size_t)48 << 30;
+// scattered back. 96 GiB, a third of an MI355X's HBM, keeps the long-prefill
+// shape (T = 262144, H = 16, d = 128: about 75 GB) in one group and leaves room
+// for the caller's tensors beside the largest packs.
+constexpr size_t kBackwardBudget = (size_t)96 << 30;
 // KDA_BACKWARD_BUDGET_BYTES in the environment lowers (or raises) the budget,
 // read at every call (tests force small groups with it).
 size_t backward_budget() {

@@ -267,10 +267,10 @@ int kda_layer_back(const kda_shape* shape, int64_t num_tokens, const float* o,
  * caller-owned, 16-byte aligned). It holds the recomputed forward (its states
  * after every 64 tokens) and about 1 MB per (chunk, head) at d = 128
  * (0.3 MB at d = 64) of intermediate fp32 arrays. Heads are independent, so
- * when that would exceed 48 GiB the backward runs the heads in the fewest
+ * when that would exceed 96 GiB the backward runs the heads in the fewest
  * equal groups that fit (each group's inputs gathered into the workspace and
  * its gradients scattered back); the environment variable
- * KDA_BACKWARD_BUDGET_BYTES, read at every call, replaces the 48 GiB. */
+ * KDA_BACKWARD_BUDGET_BYTES, read at every call, replaces the 96 GiB. */
 int kda_prefill_backward_workspace_size(const kda_shape* shape, int32_t num_seqs,
                                         const int64_t* cu_seqlens_host, size_t* bytes);
 
