@@ -1309,7 +1309,9 @@ void prefill_kernel(PrefillArgs a) {
 //     (K * 2^(G_n - G))^T U = K^T (2^(G_n - G) * U),
 // whose K^T operand is then the raw bf16 row data itself (U as bf16 hi + lo).
 // The raw k rows of a chunk are double-buffered (the update of chunk c reads
-// them while chunk c+1's are staged); v rows are read only in P5.
+// them while chunk c+1's are staged); v rows are read only in P5. So are the
+// per-chunk small arrays: wavefront 0 scans chunk c+1's decay right after its
+// state update of chunk c, so that chunk c+1 starts with its Gram tiles.
 template <int D>
 struct LdsMap {
   using L = Lds<D>;
@@ -1319,8 +1321,9 @@ struct LdsMap {
   static constexpr int TH = LM + C * L::LDL * 4;                // T~ hi [64][LDTT] f16
   static constexpr int TL = TH + C * L::LDTT * 2;               // T~ lo
   static constexpr int WB = TL + C * L::LDTT * 2;               // W [64][LDQ] f16 (the stored image)
-  static constexpr int SM = WB + C * L::LDQ * 2;                // G[64], 2^G[64], 2^(G_n-G)[64], beta[64]
-  static constexpr int TOTAL = SM + 4 * C * 4 + 16;             // + 2^G_n
+  static constexpr int SM = WB + C * L::LDQ * 2;                // [2] x {G, 2^G, 2^(G_n-G), beta}[64], 2^G_n
+  static constexpr int SMF = 4 * C + 4;                         // floats per small-array buffer
+  static constexpr int TOTAL = SM + 2 * SMF * 4;
   static_assert(RV % 512 == 0 && LM % 512 == 0 && WB % 512 == 0, "buffers keep the bank alignment");
 };
 
@@ -1361,11 +1364,9 @@ void prefill_map_kernel(PrefillArgs a) {
   _Float16* sTh = reinterpret_cast<_Float16*>(smem + P::TH);
   _Float16* sTl = reinterpret_cast<_Float16*>(smem + P::TL);
   _Float16* sW = reinterpret_cast<_Float16*>(smem + P::WB);
-  float* sGs = reinterpret_cast<float*>(smem + P::SM);          // [64] G (log2, cumulative)
-  float* sDec = sGs + C;                                          // [64] 2^G (0 past the chunk end)
-  float* sRem = sDec + C;                                         // [64] 2^(G_n - G)
-  float* sBeta = sRem + C;                                        // [64]
-  float* sGam = sBeta + C;                                        // 2^G_n
+  // small arrays of chunk ch in buffer ch & 1: G (log2, cumulative), 2^G (0
+  // past the chunk end), 2^(G_n - G), beta (each [64]), then 2^G_n
+  auto sSm = [&](int ch) { return reinterpret_cast<float*>(smem + P::SM) + (ch & 1) * P::SMF; };
   unsigned char* rawV = smem + P::RV;
 
   const int wave = threadIdx.x / 64;
@@ -1410,8 +1411,24 @@ void prefill_map_kernel(PrefillArgs a) {
       pre_beta = lane < n ? a.beta[t] : 0.f;
     }
   };
+  // P1: cumulative log2 decay of chunk ch (wavefront 0) into its small arrays
+  auto p1 = [&](int ch) __attribute__((always_inline)) {
+    if (wave == 0) {
+      const int n = min(C, item.n_tokens - ch * C);
+      const int lane = threadIdx.x & 63;
+      float* sm = sSm(ch);
+      const float gcum = wave_inclusive_scan(log2_hw(pre_alpha), lane);
+      const float gl = __shfl(gcum, C - 1);
+      sm[lane] = gcum;
+      sm[C + lane] = lane < n ? exp2_hw(gcum) : 0.f;
+      sm[2 * C + lane] = exp2_hw(gl - gcum);
+      sm[3 * C + lane] = pre_beta;
+      if (lane == 0) sm[4 * C] = exp2_hw(gl);
+    }
+  };
   if (n_chunks > 0) stage(0);
   __builtin_amdgcn_s_waitcnt(0);
+  if (n_chunks > 0) p1(0);
   __syncthreads();
 
   for (int ch = 0; ch < n_chunks; ++ch) {
@@ -1420,18 +1437,11 @@ void prefill_map_kernel(PrefillArgs a) {
     asm volatile("" : "+v"(tid));                // per-lane indices re-derived every chunk
     const int lane = tid & 63, g = lane >> 4, l16 = lane & 15;
     const unsigned char* rawK = smem + P::RK + (ch & 1) * C * D * 2;
-
-    // ---- P1: cumulative log2 decay (wavefront 0) ----------------------------
-    if (wave == 0) {
-      const float gcum = wave_inclusive_scan(log2_hw(pre_alpha), lane);
-      const float gl = __shfl(gcum, C - 1);
-      sGs[lane] = gcum;
-      sDec[lane] = lane < n ? exp2_hw(gcum) : 0.f;
-      sRem[lane] = exp2_hw(gl - gcum);
-      sBeta[lane] = pre_beta;
-      if (lane == 0) sGam[0] = exp2_hw(gl);
-    }
-    __syncthreads();
+    const float* sGs = sSm(ch);                  // P1 of this chunk ran at the end of the last
+    const float* sDec = sGs + C;
+    const float* sRem = sGs + 2 * C;
+    const float* sBeta = sGs + 3 * C;
+    const float* sGam = sGs + 4 * C;
 
     // ---- P3: Gram tiles L = beta_r K K^T 2^(G_r - G_i) (strictly lower), then
     // the inverses of the four diagonal blocks (the eight-wavefront schedule)
@@ -1645,6 +1655,10 @@ void prefill_map_kernel(PrefillArgs a) {
           }
         }
       }
+    }
+    if (ch + 1 < n_chunks) {
+      __builtin_amdgcn_s_waitcnt(0);             // the next chunk's rows, alpha and beta have landed
+      p1(ch + 1);                                // into the other buffer (this chunk's is still read)
     }
     __builtin_amdgcn_s_waitcnt(0);               // the next chunk's rows have landed in LDS
     __syncthreads();
