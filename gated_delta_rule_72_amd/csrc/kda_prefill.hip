@@ -1308,24 +1308,6 @@ void prefill_kernel(PrefillArgs a) {
 // 2^(G_n - G_c) multiplies row c of U before the state update,
 //     (K * 2^(G_n - G))^T U = K^T (2^(G_n - G) * U),
 // whose K^T operand is then the raw bf16 row data itself (U as bf16 hi + lo).
-// The raw k rows of a chunk are double-buffered (the update of chunk c reads
-// them while chunk c+1's are staged); v rows are read only in P5. So are the
-// per-chunk small arrays: wavefront 0 scans chunk c+1's decay right after its
-// state update of chunk c, so that chunk c+1 starts with its Gram tiles.
-template <int D>
-struct LdsMap {
-  using L = Lds<D>;
-  static constexpr int RK = 0;                                  // raw k [2][64][D] bf16 (raw_swz)
-  static constexpr int RV = RK + 2 * C * D * 2;                 // raw v [64][D] bf16 (raw_swz)
-  static constexpr int LM = RV + C * D * 2;                     // L / A [64][LDL] f32
-  static constexpr int TH = LM + C * L::LDL * 4;                // T~ hi [64][LDTT] f16
-  static constexpr int TL = TH + C * L::LDTT * 2;               // T~ lo
-  static constexpr int WB = TL + C * L::LDTT * 2;               // W [64][LDQ] f16 (the stored image)
-  static constexpr int SM = WB + C * L::LDQ * 2;                // [2] x {G, 2^G, 2^(G_n-G), beta}[64], 2^G_n
-  static constexpr int SMF = 4 * C + 4;                         // floats per small-array buffer
-  static constexpr int TOTAL = SM + 2 * SMF * 4;
-  static_assert(RV % 512 == 0 && LM % 512 == 0 && WB % 512 == 0, "buffers keep the bank alignment");
-};
 
 // Eight raw values x[c][col0 + (lane % 16)] of staged rows [64][D] bf16
 // (chunk-permuted, raw_swz): c = r0 + {0..3} from the first transpose read,
@@ -1352,114 +1334,156 @@ __device__ __forceinline__ f16x8 bf16x8_to_f16(bf16x8 x, const float (&scale)[8]
   return r;
 }
 
+// Twelve wavefronts in two roles. Wavefronts 4-11 (producers) run the phases
+// that do not depend on the state, for chunk c+1, on the eight-wavefront
+// schedules: the Gram tiles and diagonal inversions, the inverse T~, and W and
+// U' (into LDS for the chain and into the stored record). The producers also
+// carry the M rows (16 each). M enters U only through its fp16 image; once
+// that image is zero in every lane of a wavefront (every |M| entry at most
+// 2^-25), its U is zero and its step is exactly M <- 2^G_n M, and since
+// 2^G_n <= 1 the image stays zero, so the wavefront stops forming products
+// for it. Wavefronts 0-3 (chain) run the N rows (32 each) through chunk c
+// meanwhile. A chunk takes three barrier intervals:
+//   A: chain: U = U' - W S0^T and the state update (chunk c)
+//      producers: the fetch of c+1's v rows and c+2's k rows into registers,
+//      the Gram tiles of c+1 and their inversions
+//   B: producers: c+1's v rows into LDS, the inverse T~ of c+1; the M step
+//      (chunk c)
+//   C: producers: W and U' of c+1, c+2's k rows into LDS, the decay scan of
+//      c+2 (producer 0)
+// The raw k rows are double-buffered: chunk c+2's wait in registers until
+// interval C, when the chain and the M step are done with chunk c's buffer.
+// The small arrays are triple-buffered, W double-buffered. The raw rows travel
+// through registers, not LDS-bound loads: a barrier after an LDS-bound load
+// waits for it to land. Each product accumulates its K-steps in a fixed
+// order, so the record and the maps do not depend on the timing of the roles.
 template <int D>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void prefill_map_kernel(PrefillArgs a) {
-  static_assert(D == 128, "eight wavefronts of one N and one M slice");
-  constexpr int NW = 8, NT = 512, KT = D / 16;
+struct LdsMapChain {
   using L = Lds<D>;
-  using P = LdsMap<D>;
+  static constexpr int RK = 0;                                  // raw k [2][64][D] bf16 (raw_swz)
+  static constexpr int RV = RK + 2 * C * D * 2;                 // raw v [64][D] bf16 (raw_swz)
+  static constexpr int LM = RV + C * D * 2;                     // L / A [64][LDL] f32
+  static constexpr int TH = LM + C * L::LDL * 4;                // T~ hi [64][LDTT] f16
+  static constexpr int TL = TH + C * L::LDTT * 2;               // T~ lo
+  static constexpr int WB = TL + C * L::LDTT * 2;               // W [2][64][LDQ] f16 (the stored image)
+  static constexpr int UP = WB + 2 * C * L::LDQ * 2;            // U' [slice 8][tile 4][lane 64] f32x4
+  static constexpr int SM = UP + (D / 16) * 4 * 64 * 16;        // [3] x {G, 2^G, 2^(G_n-G), beta}[64], 2^G_n
+  static constexpr int SMF = 4 * C + 4;                         // floats per small-array buffer
+  static constexpr int TOTAL = SM + 3 * SMF * 4;
+  static_assert(RV % 512 == 0 && LM % 512 == 0 && TH % 512 == 0 && TL % 512 == 0 && WB % 512 == 0 &&
+                UP % 512 == 0 && (C * L::LDQ * 2) % 512 == 0, "buffers start on a 512-byte boundary (bank alignment)");
+};
+
+template <int D>
+__global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void prefill_map_chain_kernel(PrefillArgs a) {
+  static_assert(D == 128, "four chain wavefronts of 32 N rows, eight producers of 16 M rows");
+  constexpr int NC = 4, NP = 8;                  // chain and producer wavefronts
+  constexpr int KT = D / 16;
+  constexpr int LPR = D / 8;                     // lanes per raw row (16 bytes each)
+  constexpr int RPI = 64 / LPR;                  // raw rows per wavefront instruction
+  constexpr int RI = C / RPI / NP;               // raw-row instructions per producer and tensor
+  static_assert(RI * RPI * NP == C, "every producer moves the same number of rows");
+  using L = Lds<D>;
+  using P = LdsMapChain<D>;
   extern __shared__ __align__(16) unsigned char smem[];
   float* sL = reinterpret_cast<float*>(smem + P::LM);
   _Float16* sTh = reinterpret_cast<_Float16*>(smem + P::TH);
   _Float16* sTl = reinterpret_cast<_Float16*>(smem + P::TL);
-  _Float16* sW = reinterpret_cast<_Float16*>(smem + P::WB);
-  // small arrays of chunk ch in buffer ch & 1: G (log2, cumulative), 2^G (0
-  // past the chunk end), 2^(G_n - G), beta (each [64]), then 2^G_n
-  auto sSm = [&](int ch) { return reinterpret_cast<float*>(smem + P::SM) + (ch & 1) * P::SMF; };
   unsigned char* rawV = smem + P::RV;
+  f32x4* sUp = reinterpret_cast<f32x4*>(smem + P::UP);
+  auto rawK = [&](int ch) { return smem + P::RK + (ch & 1) * C * D * 2; };
+  auto sWb = [&](int ch) { return reinterpret_cast<_Float16*>(smem + P::WB + (ch & 1) * C * L::LDQ * 2); };
+  auto sSm = [&](int ch) { return reinterpret_cast<float*>(smem + P::SM) + (ch % 3) * P::SMF; };
 
-  const int wave = threadIdx.x / 64;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  const bool chain = wave < NC;                  // (uniform per wavefront)
+  const int pw = wave - NC;                      // producer index
+  int tid = threadIdx.x, lane = tid % 64, g = lane >> 4, l16 = lane & 15;
+  auto refresh = [&]() __attribute__((always_inline)) {
+    asm volatile("" : "+v"(tid));
+    lane = tid % 64;
+    g = lane >> 4;
+    l16 = lane & 15;
+  };
   const int item_idx = blockIdx.x / a.H, h = blockIdx.x % a.H;
   const PrefillItem item = a.items[item_idx];
   if (item.n_segs <= 1) return;                  // (uniform) whole sequences need no map
   constexpr int W_BYTES = (int)wu_w_bytes(D);
+  static_assert(W_BYTES == C * L::LDQ * 2, "stored W layout");
   constexpr int64_t WU_BYTES = (int64_t)wu_chunk_bytes(D);
   unsigned char* wu_base =
       static_cast<unsigned char*>(a.seg_wu) + ((int64_t)item_idx * a.H + h) * a.seg_chunks * WU_BYTES;
   const int64_t DD = (int64_t)D * D;
   const uint32_t HDu = (uint32_t)a.H * D;
   const int n_chunks = (item.n_tokens + C - 1) / C;
+  if (n_chunks == 0) return;                     // (uniform; a segment is never empty)
+  auto chunk_len = [&](int ch) { return min(C, item.n_tokens - ch * C); };
 
-  // slice 0: the N rows 16 wave .. +15 (chain from S = 0), slice 1: the same
-  // rows of M (chain from the identity with v = 0); S^T in accumulator layout
-  f32x4 ST[2][KT];
-  {
-    const int l16 = threadIdx.x & 15, g = (threadIdx.x & 63) >> 4;
-    const int row = 16 * wave + l16;
+  // ---- producer phases ----------------------------------------------------------
+  i32x4 carry_k[RI], carry_v[RI];
+  // raw rows of chunk ch into registers, in the order stage_rows_lds_swz lays
+  // them out (instruction i = pw + NP j: rows i RPI + lane / LPR; lane l holds
+  // the 16 bytes that land at 1024 i + 16 l); rows past the end are row 0
+  auto fetch_rows = [&](const void* src, int ch, i32x4 (&carry)[RI]) __attribute__((always_inline)) {
+    const int n = chunk_len(ch);
+    const uint16_t* base = static_cast<const uint16_t*>(src) + ((item.tok_begin + (int64_t)ch * C) * a.H + h) * D;
 #pragma unroll
-    for (int kt = 0; kt < KT; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ST[0][kt][i] = 0.f;
-        ST[1][kt][i] = (row == 16 * kt + 4 * g + i) ? 1.f : 0.f;
-      }
-  }
-
-  float pre_alpha = 1.f, pre_beta = 0.f;          // wavefront 0: token `lane` of the next chunk
-  auto stage = [&](int ch) __attribute__((always_inline)) {
-    const int n = min(C, item.n_tokens - ch * C);
-    const int64_t tok0 = item.tok_begin + (int64_t)ch * C;
-    const int64_t row0 = (tok0 * a.H + h) * D;
-    const int lane = threadIdx.x & 63;
-    stage_rows_lds_swz<D, NW>(static_cast<const uint16_t*>(a.k) + row0, HDu, n, smem + P::RK + (ch & 1) * C * D * 2,
-                              wave, lane);
-    stage_rows_lds_swz<D, NW>(static_cast<const uint16_t*>(a.v) + row0, HDu, n, rawV, wave, lane);
-    if (wave == 0) {
-      const int64_t t = (tok0 + min(lane, n - 1)) * a.H + h;
-      pre_alpha = lane < n ? a.alpha[t] : 1.f;
-      pre_beta = lane < n ? a.beta[t] : 0.f;
+    for (int j = 0; j < RI; ++j) {
+      const int i = pw + NP * j;
+      const int row = i * RPI + lane / LPR;
+      const uint32_t off = (uint32_t)(row < n ? row : 0) * HDu + 8u * (uint32_t)((lane % LPR) ^ raw_swz<D>(row));
+      carry[j] = __builtin_nontemporal_load(reinterpret_cast<const i32x4*>(base + off));
     }
   };
-  // P1: cumulative log2 decay of chunk ch (wavefront 0) into its small arrays
+  auto put_rows = [&](unsigned char* dst, const i32x4 (&carry)[RI]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < RI; ++j) *reinterpret_cast<i32x4*>(dst + 1024 * (pw + NP * j) + 16 * lane) = carry[j];
+  };
+  float pre_alpha = 1.f, pre_beta = 0.f;         // producer 0: token `lane` of a later chunk
+  auto fetch_ab = [&](int ch) __attribute__((always_inline)) {
+    if (pw == 0) {
+      const int64_t t = (item.tok_begin + (int64_t)ch * C + min(lane, chunk_len(ch) - 1)) * a.H + h;
+      pre_alpha = a.alpha[t];
+      pre_beta = a.beta[t];
+    }
+  };
+  // P1: cumulative log2 decay of chunk ch (producer 0)
   auto p1 = [&](int ch) __attribute__((always_inline)) {
-    if (wave == 0) {
-      const int n = min(C, item.n_tokens - ch * C);
-      const int lane = threadIdx.x & 63;
+    if (pw == 0) {
+      const int n = chunk_len(ch);
       float* sm = sSm(ch);
-      const float gcum = wave_inclusive_scan(log2_hw(pre_alpha), lane);
+      const float gcum = wave_inclusive_scan(log2_hw(lane < n ? pre_alpha : 1.f), lane);
       const float gl = __shfl(gcum, C - 1);
-      sm[lane] = gcum;
-      sm[C + lane] = lane < n ? exp2_hw(gcum) : 0.f;
-      sm[2 * C + lane] = exp2_hw(gl - gcum);
-      sm[3 * C + lane] = pre_beta;
-      if (lane == 0) sm[4 * C] = exp2_hw(gl);
+      sm[lane] = gcum;                                   // G
+      sm[C + lane] = lane < n ? exp2_hw(gcum) : 0.f;      // 2^G (0 past the chunk end)
+      sm[2 * C + lane] = exp2_hw(gl - gcum);              // 2^(G_n - G)
+      sm[3 * C + lane] = lane < n ? pre_beta : 0.f;       // beta
+      if (lane == 0) sm[4 * C] = exp2_hw(gl);             // 2^G_n
     }
   };
-  if (n_chunks > 0) stage(0);
-  __builtin_amdgcn_s_waitcnt(0);
-  if (n_chunks > 0) p1(0);
-  __syncthreads();
-
-  for (int ch = 0; ch < n_chunks; ++ch) {
-    const int n = min(C, item.n_tokens - ch * C);
-    int tid = threadIdx.x;
-    asm volatile("" : "+v"(tid));                // per-lane indices re-derived every chunk
-    const int lane = tid & 63, g = lane >> 4, l16 = lane & 15;
-    const unsigned char* rawK = smem + P::RK + (ch & 1) * C * D * 2;
-    const float* sGs = sSm(ch);                  // P1 of this chunk ran at the end of the last
-    const float* sDec = sGs + C;
-    const float* sRem = sGs + 2 * C;
+  // P3: Gram tiles L = beta_r K K^T 2^(G_r - G_i) (strictly lower) on the
+  // eight-wavefront run schedule, then the inverses of the diagonal blocks
+  auto p3 = [&](int ch) __attribute__((always_inline)) {
+    const int n = chunk_len(ch);
+    const unsigned char* rk = rawK(ch);
+    const float* sGs = sSm(ch);
     const float* sBeta = sGs + 3 * C;
-    const float* sGam = sGs + 4 * C;
-
-    // ---- P3: Gram tiles L = beta_r K K^T 2^(G_r - G_i) (strictly lower), then
-    // the inverses of the four diagonal blocks (the eight-wavefront schedule)
 #pragma unroll
     for (int run = 0; run < 2; ++run) {
       int R, I0, I1;
-      if (!gram_run<NW, false>(wave, run, R, I0, I1)) break;
+      if (!gram_run<NP, false>(pw, run, R, I0, I1)) break;
       const int r = 16 * R + l16;
       bf16x8 kr[D / 32];
 #pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) kr[ks] = as_bf16x8(raw_chunk<D>(rawK, 16 * R + l16, 4 * ks + g, r < n));
+      for (int ks = 0; ks < D / 32; ++ks) kr[ks] = as_bf16x8(raw_chunk<D>(rk, r, 4 * ks + g, r < n));
       const float gr = sGs[r], br = sBeta[r];
       for (int I = I0; I <= I1; ++I) {
         f32x4 accL = {0, 0, 0, 0};
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) {
           const int i = 16 * I + l16;
-          accL = mfma_bf16(as_bf16x8(raw_chunk<D>(rawK, i, 4 * ks + g, i < n)), kr[ks], accL);
+          accL = mfma_bf16(as_bf16x8(raw_chunk<D>(rk, i, 4 * ks + g, i < n)), kr[ks], accL);
         }
         const int i0 = 16 * I + 4 * g;
         const f32x4 gi = *reinterpret_cast<const f32x4*>(sGs + i0);
@@ -1474,208 +1498,282 @@ void prefill_map_kernel(PrefillArgs a) {
         }
       }
     }
-    {
-      int d0, d1;
-      if (gram_diag<NW, false>(wave, d0, d1)) {
-        __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): the tiles are in LDS
-        __builtin_amdgcn_wave_barrier();
-        const int b = g < 2 ? d0 : d1;
-        float* Lb = sL + (16 * b) * L::LDL + 16 * b;
-        float x[16];
+    int d0, d1;
+    if (gram_diag<NP, false>(pw, d0, d1)) {
+      __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): the tiles are in LDS
+      __builtin_amdgcn_wave_barrier();
+      const int b = g < 2 ? d0 : d1;
+      float* Lb = sL + (16 * b) * L::LDL + 16 * b;
+      float x[16];
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) x[rr] = (rr == l16) ? 1.f : 0.f;
-        // row i of the transposed copy (L[r][i] for r > i) is read three
-        // steps ahead of its use, so the substitution waits on no LDS read
-        constexpr int AHEAD = 3;
-        f32x4 rows[AHEAD + 1][4];
-        auto fetch = [&](int i) __attribute__((always_inline)) {
+      for (int rr = 0; rr < 16; ++rr) x[rr] = (rr == l16) ? 1.f : 0.f;
+      // row i of the transposed copy is read one step ahead of its use; its
+      // offset is tied to x[i-1] through an empty asm, so the reads cannot be
+      // hoisted together (the whole block in registers spills at three
+      // wavefronts per SIMD)
+      f32x4 rows[2][4];
+      auto fetch = [&](int i) __attribute__((always_inline)) {
+        int off = i * L::LDL;
+        if (i > 0) asm volatile("" : "+v"(off) : "v"(x[i - 1]));
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4)
-            if (q4 >= i / 4) rows[i % (AHEAD + 1)][q4] = *reinterpret_cast<const f32x4*>(Lb + i * L::LDL + 4 * q4);
-        };
+        for (int q4 = 0; q4 < 4; ++q4)
+          if (q4 >= i / 4) rows[i & 1][q4] = *reinterpret_cast<const f32x4*>(Lb + off + 4 * q4);
+      };
+      fetch(0);
 #pragma unroll
-        for (int i = 0; i < AHEAD; ++i) fetch(i);
+      for (int i = 0; i < 15; ++i) {
+        if (i + 1 < 15) fetch(i + 1);
 #pragma unroll
-        for (int i = 0; i < 15; ++i) {
-          if (i + AHEAD < 15) fetch(i + AHEAD);
+        for (int rr = i + 1; rr < 16; ++rr) x[rr] -= rows[i & 1][rr / 4][rr % 4] * x[i];
+      }
+      __builtin_amdgcn_wave_barrier();
+      if ((g & 1) == 0) {
 #pragma unroll
-          for (int rr = i + 1; rr < 16; ++rr) x[rr] -= rows[i % (AHEAD + 1)][rr / 4][rr % 4] * x[i];
-        }
-        __builtin_amdgcn_wave_barrier();
-        if ((g & 1) == 0) {
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) Lb[rr * L::LDL + l16] = x[rr];
-        }
+        for (int rr = 0; rr < 16; ++rr) Lb[rr * L::LDL + l16] = x[rr];
       }
     }
-    __syncthreads();
-
-    // ---- P4: off-diagonal blocks of (I + L)^-1 into T~ = A Diag(beta) --------
-    {
-      const int wv = __builtin_amdgcn_readfirstlane(wave);
-      if (wv == 0) inverse_column<0, L>(sL, sBeta, sTh, sTl, lane);
-      else if (wv == 1) inverse_column<1, L>(sL, sBeta, sTh, sTl, lane);
-      else if (wv == 2) inverse_column<2, L>(sL, sBeta, sTh, sTl, lane);
-      else inverse_rest<NW, L>(sL, sBeta, sTh, sTl, wv - 3, lane);
-    }
-    __syncthreads();
-
-    // ---- P5: W^T tile kt = wave and U' for value slice `wave` ----------------
-    // K operand of W: raw k^T read transposed, times 2^G_c; V operand of U':
-    // raw v^T read transposed (bf16 values are exact in fp16).
-    f32x4 Up[4];
-    {
-      f32x4 accW[4];
+  };
+  // P4: T~ = (I + L)^-1 Diag(beta): column chains on producers 0-2, the
+  // diagonal blocks and zeros on producers 3-7
+  auto p4 = [&](int ch) __attribute__((always_inline)) {
+    const float* sBeta = sSm(ch) + 3 * C;
+    if (pw == 0) inverse_column<0, L>(sL, sBeta, sTh, sTl, lane);
+    else if (pw == 1) inverse_column<1, L>(sL, sBeta, sTh, sTl, lane);
+    else if (pw == 2) inverse_column<2, L>(sL, sBeta, sTh, sTl, lane);
+    else inverse_rest<NP, L>(sL, sBeta, sTh, sTl, pw - 3, lane);
+  };
+  // P5: W^T tile kt = pw and U' for value slice pw of chunk ch: W into LDS and
+  // the record, U' into LDS (for the chain) and the record
+  auto p5 = [&](int ch) __attribute__((always_inline)) {
+    const unsigned char* rk = rawK(ch);
+    const float* sDec = sSm(ch) + C;
+    _Float16* sW = sWb(ch);
+    f32x4 accW[4], Up[4];
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) { accW[ct] = f32x4{0, 0, 0, 0}; Up[ct] = f32x4{0, 0, 0, 0}; }
+    for (int ct = 0; ct < 4; ++ct) { accW[ct] = f32x4{0, 0, 0, 0}; Up[ct] = f32x4{0, 0, 0, 0}; }
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        f16x8 th[4], tl[4];
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          th[ct] = ld_std(sTh, L::LDTT, 16 * ct, 32 * ks, lane);
-          tl[ct] = ld_std(sTl, L::LDTT, 16 * ct, 32 * ks, lane);
-        }
-        const int c0 = 32 * ks + 8 * g;              // this lane group's chunk rows c0 .. c0 + 7
-        float dec[8];
-        {
-          const f32x4 d0 = *reinterpret_cast<const f32x4*>(sDec + c0);
-          const f32x4 d1 = *reinterpret_cast<const f32x4*>(sDec + c0 + 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) { dec[e] = d0[e]; dec[4 + e] = d1[e]; }
-        }
-        const float one[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
-        const f16x8 bk = bf16x8_to_f16(tr_rows<D>(rawK, c0, c0 + 4, 16 * wave, lane), dec);
-        const f16x8 bv = bf16x8_to_f16(tr_rows<D>(rawV, c0, c0 + 4, 16 * wave, lane), one);
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          accW[ct] = mfma_f16(bk, th[ct], accW[ct]);
-          accW[ct] = mfma_f16(bk, tl[ct], accW[ct]);
-          Up[ct] = mfma_f16(th[ct], bv, Up[ct]);
-          Up[ct] = mfma_f16(tl[ct], bv, Up[ct]);
-        }
-      }
-      // W[16ct + l16][16 wave + 4g .. +3] into LDS and straight into the stored
-      // record (the LDS image), then this slice's U' (one tile per lane); both
-      // issued before the barrier, so the record drains meanwhile
-      unsigned char* rec = wu_base + (int64_t)ch * WU_BYTES;
+    for (int ks = 0; ks < 2; ++ks) {
+      f16x8 th[4], tl[4];
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
-        const f16x4 w4 = {(_Float16)accW[ct][0], (_Float16)accW[ct][1], (_Float16)accW[ct][2], (_Float16)accW[ct][3]};
-        const int off = (16 * ct + l16) * L::LDQ + 16 * wave + 4 * g;
-        *reinterpret_cast<f16x4*>(sW + off) = w4;
-        *reinterpret_cast<f16x4*>(rec + 2 * off) = w4;
+        th[ct] = ld_std(sTh, L::LDTT, 16 * ct, 32 * ks, lane);
+        tl[ct] = ld_std(sTl, L::LDTT, 16 * ct, 32 * ks, lane);
       }
-      f32x4* up = reinterpret_cast<f32x4*>(rec + W_BYTES);
+      const int c0 = 32 * ks + 8 * g;
+      float dec[8];
+      {
+        const f32x4 d0 = *reinterpret_cast<const f32x4*>(sDec + c0);
+        const f32x4 d1 = *reinterpret_cast<const f32x4*>(sDec + c0 + 4);
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) up[(wave * 4 + ct) * 64 + lane] = Up[ct];
-    }
-    __syncthreads();
-
-    // next chunk's raw rows (k into the other buffer, v over this chunk's,
-    // which P5 has finished reading), alpha and beta, while the chain runs
-    if (ch + 1 < n_chunks) stage(ch + 1);
-
-    // ---- P6: U = U' - W S0^T; S^T <- 2^G_n S^T + K^T (2^(G_n - G) * U) -------
-    // The M slice enters U only through its fp16 image. Once that image is
-    // zero in every lane of the wavefront (every |M| entry at most 2^-25), its
-    // U is zero and its step is exactly M <- 2^G_n M; since 2^G_n <= 1 the
-    // image stays zero, and the wavefront runs the N slice alone from then on.
-    {
-      f32x4 U[2][4];
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) { U[0][ct] = Up[ct]; U[1][ct] = f32x4{0, 0, 0, 0}; }
-      f16x8 sop[2][D / 32];
-#pragma unroll
-      for (int sl = 0; sl < 2; ++sl)
-#pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) sop[sl][ks] = pack_perm(ST[sl][2 * ks], ST[sl][2 * ks + 1]);
-      uint32_t mbits = 0;
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) {
-        const i32x4 w4 = __builtin_bit_cast(i32x4, sop[1][ks]);
-        mbits |= (uint32_t)(w4[0] | w4[1] | w4[2] | w4[3]);
+        for (int e = 0; e < 4; ++e) { dec[e] = d0[e]; dec[4 + e] = d1[e]; }
       }
-      // +0 and -0 both count as zero
-      const bool m_live = __builtin_amdgcn_ballot_w64((mbits & 0x7FFF7FFFu) != 0) != 0;
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) {
-        f16x8 w[4];
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) w[ct] = ld_perm(sW, L::LDQ, 16 * ct, 32 * ks, lane);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) U[0][ct] = mfma_f16(w[ct], -sop[0][ks], U[0][ct]);
-        if (m_live) {
-#pragma unroll
-          for (int ct = 0; ct < 4; ++ct) U[1][ct] = mfma_f16(w[ct], -sop[1][ks], U[1][ct]);
-        }
-      }
-      // rows c = 16ct + 4g + i of U times 2^(G_n - G_c), as bf16 hi + lo
-      // permuted-K operands (K = chunk row, two steps of 32): the raw k^T
-      // operand is then the staged bf16 data itself, with no conversion
-      bf16x8 uh[2][2], ul[2][2];
+      const float one[8] = {1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+      const f16x8 bk = bf16x8_to_f16(tr_rows<D>(rk, c0, c0 + 4, 16 * pw, lane), dec);
+      const f16x8 bv = bf16x8_to_f16(tr_rows<D>(rawV, c0, c0 + 4, 16 * pw, lane), one);
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
-        const f32x4 rem = *reinterpret_cast<const f32x4*>(sRem + 16 * ct + 4 * g);
-#pragma unroll
-        for (int sl = 0; sl < 2; ++sl) U[sl][ct] *= rem;
+        accW[ct] = mfma_f16(bk, th[ct], accW[ct]);
+        accW[ct] = mfma_f16(bk, tl[ct], accW[ct]);
+        Up[ct] = mfma_f16(th[ct], bv, Up[ct]);
+        Up[ct] = mfma_f16(tl[ct], bv, Up[ct]);
       }
+    }
+    unsigned char* rec = wu_base + (int64_t)ch * WU_BYTES;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) split_tiles_bf16(U[0][2 * ks], U[0][2 * ks + 1], uh[0][ks], ul[0][ks]);
-      if (m_live) {
+    for (int ct = 0; ct < 4; ++ct) {
+      const f16x4 w4 = {(_Float16)accW[ct][0], (_Float16)accW[ct][1], (_Float16)accW[ct][2], (_Float16)accW[ct][3]};
+      const int off = (16 * ct + l16) * L::LDQ + 16 * pw + 4 * g;
+      *reinterpret_cast<f16x4*>(sW + off) = w4;
+      *reinterpret_cast<f16x4*>(rec + 2 * off) = w4;
+    }
+    f32x4* up = reinterpret_cast<f32x4*>(rec + W_BYTES);
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) split_tiles_bf16(U[1][2 * ks], U[1][2 * ks + 1], uh[1][ks], ul[1][ks]);
+    for (int ct = 0; ct < 4; ++ct) {
+      sUp[(pw * 4 + ct) * 64 + lane] = Up[ct];
+      up[(pw * 4 + ct) * 64 + lane] = Up[ct];
+    }
+  };
+
+  // ---- state steps (NS slices: two on the chain, one on a producer) -----------
+  // U = U' - W S0^T of chunk ch (U' from LDS on the chain, zero for M), times
+  // 2^(G_n - G_c) by row, as bf16 hi + lo permuted-K operands; false (nothing
+  // formed) for an M slice whose fp16 image is zero
+  bf16x8 uh[2][2], ul[2][2];
+  auto ustep = [&](int ch, auto& ST) __attribute__((always_inline)) -> bool {
+    constexpr int NS = sizeof(ST) / sizeof(ST[0]);
+    const _Float16* sW = sWb(ch);
+    const float* sRem = sSm(ch) + 2 * C;
+    f16x8 sop[NS][D / 32];
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl)
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) sop[sl][ks] = pack_perm(ST[sl][2 * ks], ST[sl][2 * ks + 1]);
+    if constexpr (NS == 1) {
+      uint32_t bits = 0;
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        const i32x4 w4 = __builtin_bit_cast(i32x4, sop[0][ks]);
+        bits |= (uint32_t)(w4[0] | w4[1] | w4[2] | w4[3]);
       }
-      const float gam = sGam[0];
+      if (__builtin_amdgcn_ballot_w64((bits & 0x7FFF7FFFu) != 0) == 0) return false;   // +0 and -0
+    }
+    f32x4 U[NS][4];
 #pragma unroll
-      for (int kb = 0; kb < KT; kb += 4) {
-        bf16x8 ka[4][2];
+    for (int sl = 0; sl < NS; ++sl)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        U[sl][ct] = NS == 1 ? f32x4{0, 0, 0, 0} : sUp[((2 * wave + sl) * 4 + ct) * 64 + lane];
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      f16x8 w[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) w[ct] = ld_perm(sW, L::LDQ, 16 * ct, 32 * ks, lane);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int sl = 0; sl < NS; ++sl) U[sl][ct] = mfma_f16(w[ct], -sop[sl][ks], U[sl][ct]);
+    }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const f32x4 rem = *reinterpret_cast<const f32x4*>(sRem + 16 * ct + 4 * g);
+#pragma unroll
+      for (int sl = 0; sl < NS; ++sl) U[sl][ct] *= rem;
+    }
+#pragma unroll
+    for (int sl = 0; sl < NS; ++sl)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) split_tiles_bf16(U[sl][2 * ks], U[sl][2 * ks + 1], uh[sl][ks], ul[sl][ks]);
+    return true;
+  };
+  // S^T <- 2^G_n S^T + K^T (2^(G_n - G) * U) of chunk ch (live: U was formed)
+  auto update = [&](int ch, bool live, auto& ST) __attribute__((always_inline)) {
+    constexpr int NS = sizeof(ST) / sizeof(ST[0]);
+    const unsigned char* rk = rawK(ch);
+    const float gam = sSm(ch)[4 * C];
+#pragma unroll
+    for (int kb = 0; kb < KT; kb += 4) {
+      bf16x8 ka[4][2];
+      if (live) {
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
           for (int ks = 0; ks < 2; ++ks)
-            ka[t][ks] = tr_rows<D>(rawK, 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * (kb + t), lane);
-        __builtin_amdgcn_sched_barrier(0);
+            ka[t][ks] = tr_rows<D>(rk, 32 * ks + 4 * g, 32 * ks + 16 + 4 * g, 16 * (kb + t), lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < 4; ++t) {
 #pragma unroll
-          for (int sl = 0; sl < 2; ++sl) ST[sl][kb + t] *= gam;
+        for (int sl = 0; sl < NS; ++sl) ST[sl][kb + t] *= gam;
+        if (live) {
 #pragma unroll
-          for (int ks = 0; ks < 2; ++ks) {
-            ST[0][kb + t] = mfma_bf16(ka[t][ks], uh[0][ks], ST[0][kb + t]);
-            ST[0][kb + t] = mfma_bf16(ka[t][ks], ul[0][ks], ST[0][kb + t]);
-          }
-          if (m_live) {
+          for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-              ST[1][kb + t] = mfma_bf16(ka[t][ks], uh[1][ks], ST[1][kb + t]);
-              ST[1][kb + t] = mfma_bf16(ka[t][ks], ul[1][ks], ST[1][kb + t]);
+            for (int sl = 0; sl < NS; ++sl) {
+              ST[sl][kb + t] = mfma_bf16(ka[t][ks], uh[sl][ks], ST[sl][kb + t]);
+              ST[sl][kb + t] = mfma_bf16(ka[t][ks], ul[sl][ks], ST[sl][kb + t]);
             }
-          }
         }
       }
     }
-    if (ch + 1 < n_chunks) {
-      __builtin_amdgcn_s_waitcnt(0);             // the next chunk's rows, alpha and beta have landed
-      p1(ch + 1);                                // into the other buffer (this chunk's is still read)
-    }
-    __builtin_amdgcn_s_waitcnt(0);               // the next chunk's rows have landed in LDS
-    __syncthreads();
-  }
-
-  // the segment's map: N rows (slice 0) then M rows (slice 1)
-  {
-    const int lane = threadIdx.x & 63, g = lane >> 4, l16 = lane & 15;
-    float* maps = a.seg_maps + ((int64_t)item_idx * a.H + h) * 2 * DD;   // [M, N]
+  };
+  // The two roles run separate loops (each holds only its own state in
+  // registers); both pass the same barriers: four in the prologue, three a
+  // chunk.
+  float* maps = a.seg_maps + ((int64_t)item_idx * a.H + h) * 2 * DD;   // [M, N]
+  if (chain) {
+    // N rows 32 wave + 16 sl + l16 from S = 0; S^T in accumulator layout
+    f32x4 SN[2][KT];
 #pragma unroll
-    for (int sl = 0; sl < 2; ++sl) {
-      float* dst = maps + (sl == 0 ? DD : 0);
+    for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) SN[sl][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < 4; ++b) __syncthreads();                // the producers' prologue
+    for (int ch = 0; ch < n_chunks; ++ch) {
+      refresh();
+      ustep(ch, SN);                             // interval A
+      update(ch, true, SN);
+      __syncthreads();
+      __syncthreads();                           // interval B
+      __syncthreads();                           // interval C
+    }
+    refresh();
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl)
 #pragma unroll
       for (int kt = 0; kt < KT; ++kt)
-        *reinterpret_cast<f32x4*>(dst + (16 * wave + l16) * D + 16 * kt + 4 * g) = ST[sl][kt];
-    }
+        *reinterpret_cast<f32x4*>(maps + DD + (32 * wave + 16 * sl + l16) * D + 16 * kt + 4 * g) = SN[sl][kt];
+    return;
   }
+  // producers: M rows 16 pw + l16 from the identity
+  f32x4 SMr[1][KT];
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) SMr[0][kt][i] = (16 * pw + l16 == 16 * kt + 4 * g + i) ? 1.f : 0.f;
+
+  // ---- prologue: chunk 0 prepared, chunk 1's k rows and decay scan -------------
+  fetch_rows(a.k, 0, carry_k);
+  fetch_rows(a.v, 0, carry_v);
+  fetch_ab(0);
+  put_rows(rawK(0), carry_k);
+  put_rows(rawV, carry_v);
+  p1(0);
+  if (n_chunks > 1) {
+    fetch_rows(a.k, 1, carry_k);
+    fetch_ab(1);
+  }
+  __syncthreads();
+  refresh();
+  p3(0);
+  if (n_chunks > 1) put_rows(rawK(1), carry_k);
+  __syncthreads();
+  refresh();
+  p4(0);
+  __syncthreads();
+  refresh();
+  p5(0);
+  if (n_chunks > 1) p1(1);
+  __syncthreads();
+
+  bool m_live = true;                            // this wavefront's M image is nonzero
+  for (int ch = 0; ch < n_chunks; ++ch) {
+    const bool has_next = ch + 1 < n_chunks, has_next2 = ch + 2 < n_chunks;
+    refresh();
+    // ---- interval A ---------------------------------------------------------
+    if (has_next) fetch_rows(a.v, ch + 1, carry_v);
+    if (has_next) p3(ch + 1);
+    if (has_next2) {                             // (after P3: not live across it)
+      fetch_rows(a.k, ch + 2, carry_k);
+      fetch_ab(ch + 2);
+    }
+    __syncthreads();
+    refresh();
+    // ---- interval B ---------------------------------------------------------
+    if (has_next) {
+      put_rows(rawV, carry_v);                   // v rows of chunk ch were read in the last interval C
+      p4(ch + 1);
+    }
+    if (m_live) m_live = ustep(ch, SMr);
+    update(ch, m_live, SMr);
+    __syncthreads();
+    refresh();
+    // ---- interval C ---------------------------------------------------------
+    if (has_next) {
+      p5(ch + 1);
+      if (has_next2) {
+        put_rows(rawK(ch + 2), carry_k);         // k rows of chunk ch were read in intervals A and B
+        p1(ch + 2);                              // small arrays of chunk ch-1
+      }
+    }
+    __syncthreads();
+  }
+  refresh();
+#pragma unroll
+  for (int kt = 0; kt < KT; ++kt)
+    *reinterpret_cast<f32x4*>(maps + (16 * pw + l16) * D + 16 * kt + 4 * g) = SMr[0][kt];
 }
 
 // ---- Pass 3, scalar gate, bf16 inputs, d = 128: chain and producer wavefronts
@@ -2313,14 +2411,14 @@ hipError_t launch_wu_pipe(const PrefillArgs& a, hipStream_t s) {
 }
 
 template <int D>
-hipError_t launch_map(const PrefillArgs& a, hipStream_t s) {
-  using P = LdsMap<D>;
+hipError_t launch_map_chain(const PrefillArgs& a, hipStream_t s) {
+  using P = LdsMapChain<D>;
   static_assert(P::TOTAL <= 160 * 1024, "LDS budget");
-  auto kern = prefill_map_kernel<D>;
+  auto kern = prefill_map_chain_kernel<D>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, P::TOTAL);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(a.n_items * a.H), dim3(512), P::TOTAL, s, a);
+  hipLaunchKernelGGL(kern, dim3(a.n_items * a.H), dim3(768), P::TOTAL, s, a);
   return hipGetLastError();
 }
 
@@ -2329,7 +2427,7 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
   if (a.seg_chunks == 0) return launch_pass<D, BF16, PK, false, false>(a, s);
   hipError_t e;                                                 // pass 1: segment maps, W and U' per chunk
   if constexpr (D == 128 && BF16 && !PK)
-    e = launch_map<D>(a, s);
+    e = launch_map_chain<D>(a, s);
   else
     e = launch_pass<D, BF16, PK, true, false>(a, s);
   if (e != hipSuccess) return e;
