@@ -58,7 +58,10 @@ int check_shape(const kda_shape* s, bool square = false) {
     return fail(KDA_ERR_ARG, "qkv_dtype must be KDA_BF16 or KDA_F32 (got %d)", s->qkv_dtype);
   if (s->gate != KDA_GATE_SCALAR && s->gate != KDA_GATE_PER_KEY)
     return fail(KDA_ERR_ARG, "gate must be KDA_GATE_SCALAR or KDA_GATE_PER_KEY (got %d)", s->gate);
-  if ((int64_t)s->num_heads * 2 > INT32_MAX / 128) return fail(KDA_ERR_SHAPE, "num_heads too large");
+  // the kernels form element and byte offsets within one 64-token chunk of a
+  // [T][H][128] fp32 tensor in 32 bits
+  if ((int64_t)s->num_heads * 128 * 64 * 4 > INT32_MAX)
+    return fail(KDA_ERR_SHAPE, "num_heads must be at most 65535 (got %d)", s->num_heads);
   return KDA_OK;
 }
 

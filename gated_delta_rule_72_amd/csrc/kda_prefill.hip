@@ -1440,14 +1440,17 @@ void prefill_map_chain_kernel(PrefillArgs a) {
 #pragma unroll
     for (int j = 0; j < RI; ++j) *reinterpret_cast<i32x4*>(dst + 1024 * (pw + NP * j) + 16 * lane) = carry[j];
   };
-  float pre_alpha = 1.f, pre_beta = 0.f;         // producer 0: token `lane` of a later chunk
+  // alpha and beta of token `lane` of a later chunk (every producer loads
+  // them, producer 0 scans them)
+  float pre_alpha = 1.f, pre_beta = 0.f;
   auto fetch_ab = [&](int ch) __attribute__((always_inline)) {
-    if (pw == 0) {
-      const int64_t t = (item.tok_begin + (int64_t)ch * C + min(lane, chunk_len(ch) - 1)) * a.H + h;
-      pre_alpha = a.alpha[t];
-      pre_beta = a.beta[t];
-    }
+    const int64_t t = (item.tok_begin + (int64_t)ch * C + min(lane, chunk_len(ch) - 1)) * a.H + h;
+    pre_alpha = a.alpha[t];
+    pre_beta = a.beta[t];
   };
+  // the loaded alpha and beta are waited for here (p1 can then follow record
+  // stores without waiting for them)
+  auto land_ab = [&]() __attribute__((always_inline)) { asm volatile("" : "+v"(pre_alpha), "+v"(pre_beta)); };
   // P1: cumulative log2 decay of chunk ch (producer 0)
   auto p1 = [&](int ch) __attribute__((always_inline)) {
     if (pw == 0) {
@@ -1715,20 +1718,24 @@ void prefill_map_chain_kernel(PrefillArgs a) {
     for (int i = 0; i < 4; ++i) SMr[0][kt][i] = (16 * pw + l16 == 16 * kt + 4 * g + i) ? 1.f : 0.f;
 
   // ---- prologue: chunk 0 prepared, chunk 1's k rows and decay scan -------------
+  // Every fetch and every put of raw rows is unconditional (past the last
+  // chunk they repeat it): the wait for a load then has the same count on
+  // every path, where a load or a store under a branch makes the compiler
+  // wait for all memory traffic in flight.
+  const int last = n_chunks - 1;
   fetch_rows(a.k, 0, carry_k);
   fetch_rows(a.v, 0, carry_v);
   fetch_ab(0);
   put_rows(rawK(0), carry_k);
   put_rows(rawV, carry_v);
   p1(0);
-  if (n_chunks > 1) {
-    fetch_rows(a.k, 1, carry_k);
-    fetch_ab(1);
-  }
+  fetch_rows(a.k, min(1, last), carry_k);
+  fetch_ab(min(1, last));
   __syncthreads();
   refresh();
   p3(0);
-  if (n_chunks > 1) put_rows(rawK(1), carry_k);
+  put_rows(rawK(1), carry_k);
+  land_ab();
   __syncthreads();
   refresh();
   p4(0);
@@ -1743,31 +1750,24 @@ void prefill_map_chain_kernel(PrefillArgs a) {
     const bool has_next = ch + 1 < n_chunks, has_next2 = ch + 2 < n_chunks;
     refresh();
     // ---- interval A ---------------------------------------------------------
-    if (has_next) fetch_rows(a.v, ch + 1, carry_v);
+    fetch_rows(a.v, min(ch + 1, last), carry_v);
     if (has_next) p3(ch + 1);
-    if (has_next2) {                             // (after P3: not live across it)
-      fetch_rows(a.k, ch + 2, carry_k);
-      fetch_ab(ch + 2);
-    }
+    fetch_rows(a.k, min(ch + 2, last), carry_k); // (after P3: not live across it)
+    fetch_ab(min(ch + 2, last));
     __syncthreads();
     refresh();
     // ---- interval B ---------------------------------------------------------
-    if (has_next) {
-      put_rows(rawV, carry_v);                   // v rows of chunk ch were read in the last interval C
-      p4(ch + 1);
-    }
+    put_rows(rawV, carry_v);                     // v rows of chunk ch were read in the last interval C
+    if (has_next) p4(ch + 1);
     if (m_live) m_live = ustep(ch, SMr);
     update(ch, m_live, SMr);
     __syncthreads();
     refresh();
     // ---- interval C ---------------------------------------------------------
-    if (has_next) {
-      p5(ch + 1);
-      if (has_next2) {
-        put_rows(rawK(ch + 2), carry_k);         // k rows of chunk ch were read in intervals A and B
-        p1(ch + 2);                              // small arrays of chunk ch-1
-      }
-    }
+    put_rows(rawK(ch + 2), carry_k);             // k rows of chunk ch were read in intervals A and B
+    land_ab();
+    if (has_next) p5(ch + 1);
+    if (has_next2) p1(ch + 2);                   // small arrays of chunk ch-1
     __syncthreads();
   }
   refresh();
@@ -1787,13 +1787,11 @@ void prefill_map_chain_kernel(PrefillArgs a) {
 // chunk takes two barrier intervals:
 //   A: chain: U = U' - W S0^T (chunk c)
 //      producers: raw rows of c+1 into LDS, its decay scan, the fetch of its W
-//   B: chain: O and the state update (chunk c), then the fetch of U' (c+1)
+//   B: chain: the fetch of U' (c+1), O and the state update (chunk c)
 //      producers: Q~ and K~^T of c+1, the fetch of c+2's raw rows, B of c+1,
 //      W of c+1 into LDS (the chain read chunk c's in interval A)
-// The fetches sit where they least delay the chain's o stores, which share
-// the compute unit's vector memory path with them. Everything this kernel
-// moves through HBM is touched once (raw rows, stored W and U', o), so those
-// accesses are nontemporal.
+// Everything this kernel moves through HBM is touched once (raw rows, stored
+// W and U', o), so those accesses are nontemporal.
 // Every product is the one the other pass-3 form computes, in the same order,
 // so both give the same bits.
 template <int D>
@@ -2018,77 +2016,55 @@ void prefill_wu_pipe_kernel(PrefillArgs a) {
       for (int ct = 0; ct < 4; ++ct) carry[4 * sl + ct] = __builtin_nontemporal_load(up + ((SPW * wave + sl) * 4 + ct) * 64 + lane);
   };
 
-  // ---- prologue: chunk 0's operands in buffer 0, W(0) in LDS (producers),
-  // U'(0) (chain) ----------------------------------------------------------------
+  // The two roles run separate loops (each holds only its own operands in
+  // registers), with the same barriers: two in the prologue, two a chunk.
+  // Every fetch and every put is unconditional (past the last chunk they
+  // repeat it): a load or a store under a branch makes the compiler wait for
+  // all memory traffic in flight where the paths join.
+  const int last = n_chunks - 1;
   if (chain) {
     fetch_up(0);
-  } else {
-    fetch_raw(0);
-    fetch_w(0);
-    for (int e = ptid; e < 2 * 6 * 256; e += NPT) {   // upper tiles of both B buffers
-      const int bb = e / (6 * 256), t = (e / 256) % 6, rr = (e % 256) / 16, cc = e % 16;
-      const int R = t < 3 ? 0 : (t < 5 ? 1 : 2);
-      const int I = t < 3 ? t + 1 : (t < 5 ? t - 1 : 3);
-      reinterpret_cast<_Float16*>(smem + bb * P::BUF + P::BG)[(16 * R + rr) * L::LDT + 16 * I + cc] = (_Float16)0.f;
-    }
-    put_raw();
-    p1(0, chunk_len(0));
-  }
-  __syncthreads();
-  refresh();
-  if (!chain) {
-    if (n_chunks > 1) fetch_raw(1);
-    p2(0, chunk_len(0));
-    p3(0, chunk_len(0));
-    put_w();
-  }
-  __syncthreads();
-
-  for (int ch = 0; ch < n_chunks; ++ch) {
-    const int b = ch & 1, nb = b ^ 1;
-    const bool has_next = ch + 1 < n_chunks;
-    const int64_t tok0 = item.tok_begin + (int64_t)ch * C;
-    const int n = chunk_len(ch);
-    refresh();
-
-    // ---- interval A ---------------------------------------------------------
-    f16x8 sop[SPW][D / 32], uh[SPW][2], ul[SPW][2];
-    if (chain) {
-      // U = U' - W S0^T (W (-S0^T) accumulated into U' directly)
-      f32x4 U[SPW][4];
-#pragma unroll
-      for (int sl = 0; sl < SPW; ++sl)
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) U[sl][ct] = __builtin_bit_cast(f32x4, carry[4 * sl + ct]);
-#pragma unroll
-      for (int sl = 0; sl < SPW; ++sl)
-#pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks) sop[sl][ks] = pack_perm(ST[sl][2 * ks], ST[sl][2 * ks + 1]);
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) {
-        f16x8 w[4], nsop[SPW];
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) w[ct] = ld_perm(sW, L::LDQ, 16 * ct, 32 * ks, lane);
-#pragma unroll
-        for (int sl = 0; sl < SPW; ++sl) nsop[sl] = -sop[sl][ks];
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-          for (int sl = 0; sl < SPW; ++sl) U[sl][ct] = mfma_f16(w[ct], nsop[sl], U[sl][ct]);
-      }
-#pragma unroll
-      for (int sl = 0; sl < SPW; ++sl)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) split_perm(U[sl][2 * ks], U[sl][2 * ks + 1], uh[sl][ks], ul[sl][ks]);
-    } else if (has_next) {
-      put_raw();                                 // chunk ch+1's raw rows (fetched an interval ago)
-      p1(nb, chunk_len(ch + 1));
-      fetch_w(ch + 1);
-    }
+    __syncthreads();                             // the producers' prologue
     __syncthreads();
-
-    // ---- interval B ---------------------------------------------------------
-    if (chain) {
+    for (int ch = 0; ch < n_chunks; ++ch) {
+      const int b = ch & 1;
+      const int64_t tok0 = item.tok_begin + (int64_t)ch * C;
+      const int n = chunk_len(ch);
+      refresh();
+      // ---- interval A: U = U' - W S0^T (W (-S0^T) accumulated into U' directly)
+      f16x8 sop[SPW][D / 32], uh[SPW][2], ul[SPW][2];
+      {
+        f32x4 U[SPW][4];
+#pragma unroll
+        for (int sl = 0; sl < SPW; ++sl)
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) U[sl][ct] = __builtin_bit_cast(f32x4, carry[4 * sl + ct]);
+#pragma unroll
+        for (int sl = 0; sl < SPW; ++sl)
+#pragma unroll
+          for (int ks = 0; ks < D / 32; ++ks) sop[sl][ks] = pack_perm(ST[sl][2 * ks], ST[sl][2 * ks + 1]);
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks) {
+          f16x8 w[4], nsop[SPW];
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) w[ct] = ld_perm(sW, L::LDQ, 16 * ct, 32 * ks, lane);
+#pragma unroll
+          for (int sl = 0; sl < SPW; ++sl) nsop[sl] = -sop[sl][ks];
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int sl = 0; sl < SPW; ++sl) U[sl][ct] = mfma_f16(w[ct], nsop[sl], U[sl][ct]);
+        }
+#pragma unroll
+        for (int sl = 0; sl < SPW; ++sl)
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) split_perm(U[sl][2 * ks], U[sl][2 * ks + 1], uh[sl][ks], ul[sl][ks]);
+      }
+      __syncthreads();
+      // ---- interval B: O and the state update of chunk ch -------------------------
+      // U' of the next chunk is fetched first: the o stores then come after
+      // it, and interval A's wait for it does not wait for them
+      fetch_up(min(ch + 1, last));
       const _Float16* sQt = reinterpret_cast<const _Float16*>(smem + b * P::BUF + P::QT);
       const _Float16* sKtT = reinterpret_cast<const _Float16*>(smem + b * P::BUF + P::KTT);
       const _Float16* sB = reinterpret_cast<const _Float16*>(smem + b * P::BUF + P::BG);
@@ -2159,24 +2135,54 @@ void prefill_wu_pipe_kernel(PrefillArgs a) {
               *reinterpret_cast<f32x4*>(dst + (16 * (SPW * wave + sl) + l16) * D + 16 * kt + 4 * g) = ST[sl][kt];
         }
       }
-      if (has_next) fetch_up(ch + 1);
-    } else if (has_next) {
-      const int n_next = chunk_len(ch + 1);
-      p2(nb, n_next);
-      if (ch + 2 < n_chunks) fetch_raw(ch + 2);
-      p3(nb, n_next);
-      put_w();                                   // W of chunk ch+1 (interval A read chunk ch's)
+      __syncthreads();
     }
-    __syncthreads();
+    if (item.seg == item.n_segs - 1) {
+      float* dst = a.final_state + ((int64_t)item.seq * a.H + h) * DD;
+#pragma unroll
+      for (int sl = 0; sl < SPW; ++sl)
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt)
+          *reinterpret_cast<f32x4*>(dst + (16 * (SPW * wave + sl) + l16) * D + 16 * kt + 4 * g) = ST[sl][kt];
+    }
+    return;
   }
 
-  if (chain && item.seg == item.n_segs - 1) {
-    float* dst = a.final_state + ((int64_t)item.seq * a.H + h) * DD;
-#pragma unroll
-    for (int sl = 0; sl < SPW; ++sl)
-#pragma unroll
-      for (int kt = 0; kt < KT; ++kt)
-        *reinterpret_cast<f32x4*>(dst + (16 * (SPW * wave + sl) + l16) * D + 16 * kt + 4 * g) = ST[sl][kt];
+  // ---- producers: prologue (chunk 0's operands in buffer 0, W(0) in LDS) ---------
+  fetch_raw(0);
+  fetch_w(0);
+  for (int e = ptid; e < 2 * 6 * 256; e += NPT) {     // upper tiles of both B buffers
+    const int bb = e / (6 * 256), t = (e / 256) % 6, rr = (e % 256) / 16, cc = e % 16;
+    const int R = t < 3 ? 0 : (t < 5 ? 1 : 2);
+    const int I = t < 3 ? t + 1 : (t < 5 ? t - 1 : 3);
+    reinterpret_cast<_Float16*>(smem + bb * P::BUF + P::BG)[(16 * R + rr) * L::LDT + 16 * I + cc] = (_Float16)0.f;
+  }
+  put_raw();
+  p1(0, chunk_len(0));
+  __syncthreads();
+  refresh();
+  fetch_raw(min(1, last));
+  p2(0, chunk_len(0));
+  p3(0, chunk_len(0));
+  put_w();
+  __syncthreads();
+  for (int ch = 0; ch < n_chunks; ++ch) {
+    const int nb = (ch & 1) ^ 1;
+    const bool has_next = ch + 1 < n_chunks;
+    refresh();
+    // ---- interval A: chunk ch+1's raw rows into LDS, its decay scan, the fetch of its W
+    put_raw();
+    if (has_next) p1(nb, chunk_len(ch + 1));
+    fetch_w(min(ch + 1, last));
+    __syncthreads();
+    // ---- interval B: Q~ and K~^T of ch+1, the fetch of ch+2's raw rows, B of
+    // ch+1, W of ch+1 into LDS (the chain read chunk ch's in interval A)
+    refresh();
+    if (has_next) p2(nb, chunk_len(ch + 1));
+    fetch_raw(min(ch + 2, last));
+    if (has_next) p3(nb, chunk_len(ch + 1));
+    put_w();
+    __syncthreads();
   }
 }
 

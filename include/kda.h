@@ -77,7 +77,7 @@ typedef enum { KDA_BF16 = 0, KDA_F32 = 1 } kda_dtype;
 typedef enum { KDA_GATE_SCALAR = 0, KDA_GATE_PER_KEY = 1 } kda_gate;
 
 typedef struct {
-  int32_t num_heads; /* H                                   */
+  int32_t num_heads; /* H, 1 .. 65535                       */
   int32_t d_k;       /* key / query channels per head       */
   int32_t d_v;       /* value channels per head             */
   int32_t qkv_dtype; /* kda_dtype of q, k, v                */

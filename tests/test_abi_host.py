@@ -110,6 +110,7 @@ def test_workspace_size_plans(K):
 
 @pytest.mark.parametrize("field,value,code", [
     ("d_k", 96, "KDA_ERR_SHAPE"), ("d_v", 96, "KDA_ERR_SHAPE"), ("num_heads", 0, "KDA_ERR_SHAPE"),
+    ("num_heads", 65536, "KDA_ERR_SHAPE"),
     ("qkv_dtype", 7, "KDA_ERR_ARG"), ("gate", 2, "KDA_ERR_ARG")])
 def test_bad_shapes_rejected(K, field, value, code):
     sh = K.make_shape(2, 128, 128, torch.bfloat16, False)
