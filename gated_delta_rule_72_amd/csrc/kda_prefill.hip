@@ -1790,6 +1790,9 @@ void prefill_map_chain_kernel(PrefillArgs a) {
 //   B: chain: the fetch of U' (c+1), O and the state update (chunk c)
 //      producers: Q~ and K~^T of c+1, the fetch of c+2's raw rows, B of c+1,
 //      W of c+1 into LDS (the chain read chunk c's in interval A)
+// The producers' fetch of raw rows sits after Q~ and K~^T: issued at the start
+// of interval B it delays the chain's o stores, which share the compute
+// unit's vector memory path with it (pass 3 then takes about 10 % longer).
 // Everything this kernel moves through HBM is touched once (raw rows, stored
 // W and U', o), so those accesses are nontemporal.
 // Every product is the one the other pass-3 form computes, in the same order,
