@@ -81,9 +81,13 @@ __device__ __forceinline__ float group_allreduce(float x) {
 
 // MULTI: n_tok tokens per sequence ([batch, n_tok, H, d] inputs), the state
 // kept in registers between them; the state after token t goes to
-// token_states (if given) and, for t + 1 == commit, back to `state`.
-template <int DK, int DV, bool BF16, bool PER_KEY, bool MULTI>
-__global__ __launch_bounds__(DV * 2) void decode_kernel(DecodeArgs a) {
+// token_states (KEEP: token_states given) and, for t + 1 == commit, back to
+// `state`. KEEP is a template flag so that the per-token stores are not under
+// a branch: with them under one, the wait for the next token's inputs would
+// also wait for the stores.
+template <int DK, int DV, bool BF16, bool PER_KEY, bool MULTI, bool KEEP>
+__global__ __launch_bounds__(DV * 2) __attribute__((amdgpu_waves_per_eu(1, KEEP ? 2 : 8)))
+void decode_kernel(DecodeArgs a) {
   constexpr int LPR = DK / 4;     // lanes per state row
   constexpr int G = 64 / LPR;     // rows side by side in a wavefront
   constexpr int R = 32 / G;       // rows per lane group
@@ -135,11 +139,22 @@ __global__ __launch_bounds__(DV * 2) void decode_kernel(DecodeArgs a) {
   };
   TokenIn next = load_token(0);
 
-  for (int t = 0; t < n_tok; ++t) {
+  // this lane's element offset in the state, re-derived from an opaque copy
+  // of the thread index where it is used: hoisted out of the token loop, the
+  // addresses of the R rows would hold 2R registers for the whole call
+  auto lane_elem = [&]() __attribute__((always_inline)) {
+    int tid = threadIdx.x;
+    if constexpr (MULTI) asm volatile("" : "+v"(tid));
+    return (wave * 32 + (tid % 64) / LPR) * DK + 4 * (tid % LPR);
+  };
+  auto step = [&](int t) __attribute__((always_inline)) {
     const int64_t tok = MULTI ? ((int64_t)b * n_tok + t) * a.H + h : bh;   // (sequence, token, head)
     const int64_t v_off = tok * DV;
     const TokenIn cur = next;
-    if (MULTI && t + 1 < n_tok) next = load_token(t + 1);
+    // unconditional (the last token fetches itself again): a load under a
+    // branch leaves the wait counts path-dependent, and the compiler then
+    // waits for this token's stores before the next token starts
+    if constexpr (MULTI) next = load_token(min(t + 1, n_tok - 1));
     const f32x4 kv = cur.k, qv = cur.q, av = cur.a;
     const float beta = cur.beta;
 
@@ -158,11 +173,20 @@ __global__ __launch_bounds__(DV * 2) void decode_kernel(DecodeArgs a) {
     float u = 0.f;
     if ((li & 1) == 0) u = beta * (cur.v - red);
     const float u_pair = xor_lane<1>(u);
-    if (li & 1) a.o[v_off + my_row] = red + u_pair * kq;
+    if constexpr (MULTI) {
+      // o of the pair's row: the odd lane holds s'.q, the even lane u; both
+      // lanes form the same sum from the same operands and store the same
+      // bits to the same address, so no branch skips the even lanes' store
+      const float r_pair = xor_lane<1>(red);
+      a.o[v_off + my_row] = (li & 1) ? red + u_pair * kq : r_pair + u * kq;
+    } else {
+      if (li & 1) a.o[v_off + my_row] = red + u_pair * kq;
+    }
 
     // u of row r sits in lane 2r of each lane group: read it wave-wide and keep
     // the copy of this lane's group
-    float* snap = (MULTI && a.token_states) ? a.token_states + tok * DV * DK : nullptr;
+    float* snap = KEEP ? a.token_states + tok * DV * DK : nullptr;
+    const int elem = MULTI ? lane_elem() : 0;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float ur = 0.f;
@@ -172,18 +196,37 @@ __global__ __launch_bounds__(DV * 2) void decode_kernel(DecodeArgs a) {
         if (g == gg) ur = x;
       }
       s[r] = s[r] + ur * kv;
-      const int row = wave * 32 + r * G + g;
-      if (MULTI && snap)
-        __builtin_nontemporal_store(s[r], reinterpret_cast<f32x4*>(snap + (int64_t)row * DK + 4 * li));
-      if (t + 1 == commit)
+      if constexpr (KEEP)
+        __builtin_nontemporal_store(s[r], reinterpret_cast<f32x4*>(snap + elem + r * G * DK));   // row wave*32 + r*G + g
+      if constexpr (!MULTI) {
+        const int row = wave * 32 + r * G + g;
         __builtin_nontemporal_store(s[r], reinterpret_cast<f32x4*>(state + (int64_t)row * DK + 4 * li));
+      }
     }
+  };
+  if constexpr (!MULTI) {
+    step(0);
+  } else {
+    // The tokens up to the commit point, the committed state, then the rest:
+    // a store under a per-token test would leave the wait counts
+    // path-dependent.
+    for (int t = 0; t < commit; ++t) step(t);
+    if (commit > 0) {
+      const int elem = lane_elem();
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        __builtin_nontemporal_store(s[r], reinterpret_cast<f32x4*>(state + elem + r * G * DK));
+    }
+    for (int t = commit; t < n_tok; ++t) step(t);
   }
 }
 
 template <int DK, int DV, bool BF16, bool PK, bool MULTI>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((decode_kernel<DK, DV, BF16, PK, MULTI>), dim3(a.batch * a.H), dim3(DV * 2), 0, s, a);
+  if (MULTI && a.token_states)
+    hipLaunchKernelGGL((decode_kernel<DK, DV, BF16, PK, MULTI, MULTI>), dim3(a.batch * a.H), dim3(DV * 2), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<DK, DV, BF16, PK, MULTI, false>), dim3(a.batch * a.H), dim3(DV * 2), 0, s, a);
   return hipGetLastError();
 }
 
