@@ -61,6 +61,14 @@ def test_decode_tokens_small(d, gate, dtype):
     for b, c in enumerate(commit.tolist()):
         want = inp["initial_state"][b] if c == 0 else ts[b, c - 1]
         assert torch.equal(state2[b], want), (b, c)
+    # per-token states and a commit point in one call: the same states, the
+    # same outputs and the same committed state
+    state3 = inp["initial_state"].clone()
+    o3, ts3 = kda.decode_tokens(x["q"], x["k"], x["v"], x["alpha"], x["beta"], state3, commit=commit,
+                                keep_token_states=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o3, o) and torch.equal(ts3, ts)
+    assert torch.equal(state3, state2)
 
 
 def test_one_token_equals_decode_step_bitwise():
