@@ -55,8 +55,10 @@
 // S_{s+1} = S_s M_s + N_s in fp32 from the initial state, and pass 3 (WU) runs
 // every segment from its true start, loading W and U' instead of forming L,
 // the inverse and P5 again; whole sequences of the same call run in OUT. For
-// the scalar gate with bf16 inputs at d = 128, pass 3 is a kernel of its own
-// (prefill_wu_pipe_kernel) in which four wavefronts run the chain while the
+// the scalar gate with bf16 inputs at d = 128, both passes are kernels of their
+// own: in pass 1 (prefill_map_chain_kernel) four wavefronts carry the N rows
+// while eight form the next chunk's state-free phases and carry the M rows; in
+// pass 3 (prefill_wu_pipe_kernel) four wavefronts run the chain while the
 // other four prepare the next chunk's operands.
 // Accumulator layout of a 16x16 MFMA tile: lane l holds rows 4(l/16)+i,
 // column l%16. When an accumulator tile feeds the next product as its
