@@ -274,7 +274,9 @@ def layer_algorithmic(T, H, d, n_seqs, per_key, qkv_bytes=2, out_bytes=2):
 
 def time_layer(kda, torch, w, steps, warmup):
     """HIP-event times of kda_layer_front (with carried conv state in and out)
-    and kda_layer_back, and of front + kda_prefill_chunked + back."""
+    and kda_layer_back, of front + kda_prefill_chunked + back, and of front +
+    kda_layer_prefill (the recurrence and the back end in one call, gate
+    logits in the q/k/v dtype)."""
     from gated_delta_rule_72_amd import workloads as wl
     dev = torch.device("cuda:0")
     li = wl.make_layer_inputs(w, dev)
@@ -290,6 +292,9 @@ def time_layer(kda, torch, w, steps, warmup):
     o = torch.empty((T, H, d), dtype=torch.float32, device=dev)
     fin = torch.empty((w.num_seqs, H, d, d), dtype=torch.float32, device=dev)
     ws = torch.empty(max(kda.kda_prefill_workspace_size(shape, cu_h, 64, 0), 1), dtype=torch.uint8, device=dev)
+    g_qkv = li["g_logit"].to(li["xq"].dtype)
+    ws_l = torch.empty(max(kda.kda_layer_prefill_workspace_size(shape, cu_h, 64, 0), 1), dtype=torch.uint8,
+                       device=dev)
 
     def front():
         kda.kda_layer_front(shape, cu_h, li["cu_seqlens"], li["xq"], li["xk"], li["xv"], li["conv_w"],
@@ -304,9 +309,15 @@ def time_layer(kda, torch, w, steps, warmup):
                                 o, fin, None, ws)
         back(o)
 
+    def layer_one_call():
+        front()
+        kda.kda_layer_prefill(shape, cu_h, li["cu_seqlens"], q, k, v, alpha, beta, pinp["initial_state"], g_qkv,
+                              li["norm_w"], 1e-6, kda.KDA_BF16, out, fin, None, ws_l)
+
     res = {}
     stream = torch.cuda.current_stream()
-    for name, fn in (("front", front), ("back", lambda: back(li["o"])), ("layer", layer)):
+    for name, fn in (("front", front), ("back", lambda: back(li["o"])), ("layer", layer),
+                     ("layer_one_call", layer_one_call)):
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
@@ -522,7 +533,10 @@ def main(argv=None):
                 "back_hbm_frac": round(bb / (t["back"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "front_algorithmic_bytes": int(fb), "back_algorithmic_bytes": int(bb),
                 "front_recurrence_back_ms": round(t["layer"], 4),
-                "front_recurrence_back_tokens_per_s": round(lw.T / (t["layer"] * 1e-3), 1)}
+                "front_recurrence_back_tokens_per_s": round(lw.T / (t["layer"] * 1e-3), 1),
+                "front_then_layer_prefill_ms": round(t["layer_one_call"], 4),
+                "front_then_layer_prefill_tokens_per_s": round(lw.T / (t["layer_one_call"] * 1e-3), 1),
+                "layer_prefill_back_end_fused": bool(lw.dk == 128 and lw.dtype == "bf16" and lw.gate == "scalar")}
         result["layer_front_back"] = layer
     if not args.no_backward and not args.prefill_only:
         bwd = {}

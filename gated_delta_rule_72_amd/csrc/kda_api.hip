@@ -144,6 +144,7 @@ int device_cu_count() {
 struct PrefillPlan {
   int32_t seg_chunks, n_items;
   int32_t any_whole;   // segmented: some sequence is short enough to stay whole
+  int64_t whole_tokens;  // segmented: tokens of the sequences that stay whole
   size_t items_off, first_off, maps_off, states_off, wu_off, bytes;
 };
 
@@ -195,7 +196,10 @@ PrefillPlan plan_prefill(const kda_shape* s, int32_t num_seqs, const int64_t* cu
     const int64_t st = seg * kChunk;
     const bool split = st > 0 && len > st;
     items += split ? (len + st - 1) / st : 1;
-    if (!split) p.any_whole = 1;
+    if (!split) {
+      p.any_whole = 1;
+      p.whole_tokens += len;
+    }
   }
   p.n_items = (int32_t)items;
   const size_t H = (size_t)s->num_heads, DD = (size_t)s->d_k * s->d_k;
@@ -246,6 +250,28 @@ FullPlan plan_full(const kda_shape* s, int32_t num_seqs, const int64_t* cu, int6
   }
   f.bytes = off;
   return f;
+}
+
+// Workspace of kda_layer_prefill: the prefill's own plan, then the 16-byte sink
+// of the back end fused into pass 3, or, where it does not apply, an fp32 o
+// [T, H, d] that the separate back-end kernel reads.
+struct LayerPlan {
+  FullPlan pre;
+  bool fused;
+  size_t aux_off, bytes;
+};
+LayerPlan plan_layer(const kda_shape* s, int32_t num_seqs, const int64_t* cu, int64_t interval,
+                     int64_t segment_tokens, int cus) {
+  LayerPlan l{};
+  l.pre = plan_full(s, num_seqs, cu, interval, segment_tokens, cus);
+  // pass 3 of the scalar-gate bf16 d = 128 form carries the fused back end;
+  // it runs the segments of split sequences, so every sequence with tokens
+  // must be split (empty ones only take their final state from the other pass)
+  l.fused = s->d_k == 128 && s->qkv_dtype == KDA_BF16 && s->gate == KDA_GATE_SCALAR &&
+            l.pre.kern.seg_chunks > 0 && l.pre.kern.whole_tokens == 0;
+  l.aux_off = round_up(l.pre.bytes);
+  l.bytes = l.aux_off + (l.fused ? kAlign : round_up((size_t)cu[num_seqs] * s->num_heads * s->d_v * sizeof(float)));
+  return l;
 }
 
 int check_prefill_args(const kda_shape* shape, int32_t num_seqs, const int64_t* cu,
@@ -329,22 +355,22 @@ BackwardPlan plan_backward(const kda_shape* s, int32_t num_seqs, const int64_t* 
 int validate_prefill(const kda_shape* shape, int32_t num_seqs, const int64_t* cu_seqlens_host,
                      const int64_t* cu_seqlens_dev, int32_t chunk, int64_t snapshot_interval,
                      int64_t segment_tokens, const void* q, const void* k, const void* v,
-                     const float* alpha, const float* beta, const float* initial_state, const float* o,
+                     const float* alpha, const float* beta, const float* initial_state, const void* o,
                      const float* final_state, const float* snapshots, const void* workspace,
-                     size_t workspace_bytes) {
+                     size_t workspace_bytes, size_t o_elem = 4, const char* o_name = "o") {
   int rc = check_prefill_args(shape, num_seqs, cu_seqlens_host, chunk, snapshot_interval, segment_tokens);
   if (rc != KDA_OK) return rc;
   const int64_t T = cu_seqlens_host[num_seqs];
   const int64_t n_snap = snapshot_slots(num_seqs, cu_seqlens_host, snapshot_interval);
   if (num_seqs > 0 && !cu_seqlens_dev) return fail(KDA_ERR_ARG, "cu_seqlens_dev is NULL");
   if (T > 0 && (!q || !k || !v || !alpha || !beta || !o))
-    return fail(KDA_ERR_ARG, "q, k, v, alpha, beta and o must be non-NULL when T > 0");
+    return fail(KDA_ERR_ARG, "q, k, v, alpha, beta and %s must be non-NULL when T > 0", o_name);
   if (num_seqs > 0 && !final_state) return fail(KDA_ERR_ARG, "final_state is NULL");
   if (n_snap > 0 && !snapshots)
     return fail(KDA_ERR_ARG, "snapshots is NULL but %lld snapshot slots are due", (long long)n_snap);
   const uintptr_t a_alpha = shape->gate == KDA_GATE_PER_KEY ? 16 : 4;
   const PtrReq reqs[] = {{q, 16, "q"}, {k, 16, "k"}, {v, 16, "v"}, {alpha, a_alpha, "alpha"},
-                         {beta, 4, "beta"}, {initial_state, 16, "initial_state"}, {o, 16, "o"},
+                         {beta, 4, "beta"}, {initial_state, 16, "initial_state"}, {o, 16, o_name},
                          {final_state, 16, "final_state"},
                          {n_snap > 0 ? snapshots : nullptr, 16, "snapshots"},
                          {cu_seqlens_dev, 8, "cu_seqlens_dev"}, {workspace, 16, "workspace"}};
@@ -364,7 +390,7 @@ int validate_prefill(const kda_shape* shape, int32_t num_seqs, const int64_t* cu
                          {cu_seqlens_dev, ((size_t)num_seqs + 1) * sizeof(int64_t), "cu_seqlens_dev"},
                          {workspace, workspace_bytes, "workspace"}};
     const int n_in = (int)(sizeof ins / sizeof ins[0]);
-    const Range ro{o, tokh * shape->d_v * sizeof(float), "o"};
+    const Range ro{o, tokh * shape->d_v * o_elem, o_name};
     const Range rf{final_state, (size_t)num_seqs * H * st, "final_state"};
     const Range rs{n_snap > 0 ? snapshots : nullptr, (size_t)n_snap * H * st, "snapshots"};
     if ((rc = check_disjoint(ro, ins, n_in)) != KDA_OK) return rc;
@@ -811,6 +837,111 @@ int kda_layer_back(const kda_shape* shape, int64_t num_tokens, const float* o, c
   kda::LayerBackArgs a{o, g_logit, norm_w, out, eps, num_tokens * shape->num_heads};
   hipError_t e = kda::launch_layer_back(a, shape->d_v, out_dtype == KDA_BF16, static_cast<hipStream_t>(hip_stream));
   if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "layer back launch failed: %s", hipGetErrorString(e));
+  g_err[0] = '\0';
+  return KDA_OK;
+}
+
+int kda_layer_prefill_workspace_size(const kda_shape* shape, int32_t num_seqs,
+                                     const int64_t* cu_seqlens_host, int32_t chunk,
+                                     int64_t snapshot_interval, int64_t segment_tokens, size_t* bytes) {
+  if (!bytes) return fail(KDA_ERR_ARG, "bytes is NULL");
+  int rc = check_shape(shape, true);
+  if (rc != KDA_OK) return rc;
+  rc = check_prefill_args(shape, num_seqs, cu_seqlens_host, chunk, snapshot_interval, segment_tokens);
+  if (rc != KDA_OK) return rc;
+  *bytes = plan_layer(shape, num_seqs, cu_seqlens_host, snapshot_interval, segment_tokens,
+                      segment_tokens < 0 ? device_cu_count() : 0).bytes;
+  g_err[0] = '\0';
+  return KDA_OK;
+}
+
+int kda_layer_prefill(const kda_shape* shape, int32_t num_seqs,
+                      const int64_t* cu_seqlens_host, const int64_t* cu_seqlens_dev,
+                      int32_t chunk, int64_t snapshot_interval, int64_t segment_tokens,
+                      const void* q, const void* k, const void* v,
+                      const float* alpha, const float* beta, const float* initial_state,
+                      const void* g_logit, const float* norm_w, float eps, int32_t out_dtype,
+                      void* out, float* final_state, float* snapshots,
+                      void* workspace, size_t workspace_bytes, void* hip_stream) {
+  int rc = check_shape(shape, true);
+  if (rc != KDA_OK) return rc;
+  if (out_dtype != KDA_BF16 && out_dtype != KDA_F32)
+    return fail(KDA_ERR_ARG, "out_dtype must be KDA_BF16 or KDA_F32 (got %d)", out_dtype);
+  if (!(eps >= 0.f)) return fail(KDA_ERR_ARG, "eps must be >= 0");
+  const size_t out_es = out_dtype == KDA_BF16 ? 2 : 4;
+  rc = validate_prefill(shape, num_seqs, cu_seqlens_host, cu_seqlens_dev, chunk, snapshot_interval, segment_tokens,
+                        q, k, v, alpha, beta, initial_state, out, final_state, snapshots, workspace, workspace_bytes,
+                        out_es, "out");
+  if (rc != KDA_OK) return rc;
+  const int64_t T = cu_seqlens_host[num_seqs];
+  const int64_t n_snap = snapshot_slots(num_seqs, cu_seqlens_host, snapshot_interval);
+  const size_t H = (size_t)shape->num_heads, d = (size_t)shape->d_v, es = shape->qkv_dtype == KDA_BF16 ? 2 : 4;
+  if (T > 0) {
+    if (!g_logit || !norm_w) return fail(KDA_ERR_ARG, "g_logit and norm_w must be non-NULL when T > 0");
+    const PtrReq reqs[] = {{g_logit, 16, "g_logit"}, {norm_w, 16, "norm_w"}};
+    rc = check_align(reqs, 2);
+    if (rc != KDA_OK) return rc;
+    const size_t st = d * d * sizeof(float);
+    const Range ins[] = {{g_logit, (size_t)T * H * d * es, "g_logit"}, {norm_w, d * sizeof(float), "norm_w"}};
+    const Range outs[] = {{out, (size_t)T * H * d * out_es, "out"}, {final_state, (size_t)num_seqs * H * st, "final_state"},
+                          {n_snap > 0 ? snapshots : nullptr, (size_t)n_snap * H * st, "snapshots"}};
+    for (const Range& o : outs)
+      if ((rc = check_disjoint(o, ins, 2)) != KDA_OK) return rc;
+  }
+  const LayerPlan plan = plan_layer(shape, num_seqs, cu_seqlens_host, snapshot_interval, segment_tokens,
+                                    segment_tokens < 0 ? device_cu_count() : 0);
+  if (num_seqs > 0 && (!workspace || workspace_bytes < plan.bytes))
+    return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", plan.bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  if (num_seqs == 0) {
+    g_err[0] = '\0';
+    return KDA_OK;
+  }
+  char* ws = static_cast<char*>(workspace);
+  const hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (!plan.fused) {
+    // the recurrence into an fp32 o in the workspace, then the back-end kernel
+    float* o = reinterpret_cast<float*>(ws + plan.aux_off);
+    rc = kda_prefill_chunked(shape, num_seqs, cu_seqlens_host, cu_seqlens_dev, chunk, snapshot_interval,
+                             segment_tokens, q, k, v, alpha, beta, initial_state, o, final_state, snapshots,
+                             workspace, plan.aux_off, hip_stream);
+    if (rc != KDA_OK) return rc;
+    kda::LayerBackArgs b{o, g_logit, norm_w, out, eps, T * (int64_t)H, shape->qkv_dtype == KDA_BF16};
+    const hipError_t e = kda::launch_layer_back(b, (int)d, out_dtype == KDA_BF16, st);
+    if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "layer back launch failed: %s", hipGetErrorString(e));
+    g_err[0] = '\0';
+    return KDA_OK;
+  }
+  float* snaps_dev = nullptr;
+  if (n_snap > 0) {
+    rc = resolve_snapshots(snapshots, &snaps_dev);
+    if (rc != KDA_OK) return rc;
+  }
+  const PrefillPlan& kp = plan.pre.kern;
+  kda::PrefillArgs a{};
+  a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.init = initial_state;
+  a.o = nullptr; a.final_state = final_state; a.snapshots = snaps_dev;
+  a.cu_dev = cu_seqlens_dev;
+  a.num_seqs = num_seqs;
+  a.H = shape->num_heads;
+  a.qk_shift = 0;
+  a.interval = snapshot_interval;
+  a.seg_chunks = kp.seg_chunks;
+  a.n_items = kp.n_items;
+  a.items = reinterpret_cast<kda::PrefillItem*>(ws + kp.items_off);
+  a.seq_first_item = reinterpret_cast<int32_t*>(ws + kp.first_off);
+  a.seg_maps = reinterpret_cast<float*>(ws + kp.maps_off);
+  a.seg_states = reinterpret_cast<float*>(ws + kp.states_off);
+  a.seg_wu = static_cast<void*>(ws + kp.wu_off);
+  a.any_whole = kp.any_whole;
+  a.g_logit = g_logit;
+  a.norm_w = norm_w;
+  a.out = out;
+  a.out_sink = ws + plan.aux_off;
+  a.eps = eps;
+  a.out_bf16 = out_dtype == KDA_BF16;
+  const hipError_t e = kda::launch_prefill(a, (int)d, true, false, st);
+  if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "layer prefill launch failed: %s", hipGetErrorString(e));
   g_err[0] = '\0';
   return KDA_OK;
 }

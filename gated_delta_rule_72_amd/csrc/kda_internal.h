@@ -17,6 +17,19 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
+// sigmoid with the hardware reciprocal (1 ulp) instead of an IEEE divide (the
+// layer's gates and output gate; the prefill's fused back end uses the same one,
+// so fused and separate back ends give the same bits)
+__device__ __forceinline__ float sigmoid_rcp(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
 // Four consecutive q/k/v elements starting at element index `idx`.
 template <bool BF16>
 __device__ __forceinline__ f32x4 load4(const void* base, int64_t idx) {
@@ -87,6 +100,17 @@ struct PrefillArgs {
   int32_t any_whole;         // segmented plan: some sequence is not split (needs its own pass)
   int32_t qk_shift;          // 0, or 1 when d_v = 2 d_k: H counts value heads of d_k state rows,
                              // and value head h takes q, k, alpha, beta of head h >> 1 of H / 2
+  // Layer back end fused into pass 3 (scalar gate, bf16, d = 128, every
+  // sequence split): when `out` is set, pass 3 writes
+  // out = o * rsqrt(mean over d of o^2 + eps) * norm_w * sigmoid(g_logit)
+  // ([T, H, d], bf16 or fp32 as out_bf16) instead of o
+  const void* g_logit;       // [T, H, d] bf16
+  const float* norm_w;       // [d]
+  void* out;
+  void* out_sink;            // 16 bytes of workspace: stores of rows past a chunk's end land
+                             // there (their values are discarded)
+  float eps;
+  int32_t out_bf16;
 };
 hipError_t launch_prefill(PrefillArgs a, int d, bool bf16, bool per_key, hipStream_t s);
 // Row copy with zero fill: for r < n_rows, bytes [0, copy) of dst row r
@@ -118,10 +142,13 @@ hipError_t launch_layer_front(const LayerFrontArgs& a, int d, bool bf16, bool pe
 
 // Layer back end: RMSNorm over d_v times a sigmoid output gate.
 struct LayerBackArgs {
-  const float *o, *g_logit, *norm_w;
+  const float* o;
+  const void* g_logit;              // fp32, or bf16 when g_bf16
+  const float* norm_w;
   void* out;
   float eps;
   int64_t rows;                     // T * H
+  int32_t g_bf16;
 };
 hipError_t launch_layer_back(const LayerBackArgs& a, int d, bool out_bf16, hipStream_t s);
 

@@ -22,17 +22,6 @@
 namespace kda {
 namespace {
 
-// sigmoid with the hardware reciprocal (1 ulp) instead of an IEEE divide
-__device__ __forceinline__ float sigmoidf_(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-// two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
-}
-
 // One row segment of 8 channels as loaded: 16 bytes of bf16 or 32 bytes of fp32.
 template <bool BF16> struct Raw8;
 template <> struct Raw8<true> { uint4 w; };
@@ -145,12 +134,12 @@ __global__ __launch_bounds__(256) void layer_front_kernel(LayerFrontArgs a, int3
       if (t >= a.T) break;
       if constexpr (PER_KEY) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) al[i][e] = sigmoidf_(al[i][e] + a.alpha_bias);
+        for (int e = 0; e < 8; ++e) al[i][e] = sigmoid_rcp(al[i][e] + a.alpha_bias);
         if (live) store8<false>(a.alpha, t * HD + ch0, al[i]);
       } else {
-        if (lead) a.alpha[t * a.H + h] = sigmoidf_(al[i][0] + a.alpha_bias);
+        if (lead) a.alpha[t * a.H + h] = sigmoid_rcp(al[i][0] + a.alpha_bias);
       }
-      if (lead) a.beta[t * a.H + h] = sigmoidf_(bl[i]);
+      if (lead) a.beta[t * a.H + h] = sigmoid_rcp(bl[i]);
     }
     return;
   }
@@ -225,7 +214,7 @@ __global__ __launch_bounds__(256) void layer_front_kernel(LayerFrontArgs a, int3
       }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) y[e] = y[e] * sigmoidf_(y[e]);            // SiLU
+    for (int e = 0; e < 8; ++e) y[e] = y[e] * sigmoid_rcp(y[e]);            // SiLU
     if (j < 2) {                                                        // q, k: unit rows
       float ss = 0.f;
 #pragma unroll
@@ -271,7 +260,10 @@ __global__ __launch_bounds__(256) void layer_conv_state_kernel(LayerFrontArgs a)
   }
 }
 
-template <int D, bool OUT_BF16>
+// The row's sum of squares: each lane's 8 values in order as fused
+// multiply-adds, then the xor-pairwise sum over the row's lanes (the
+// prefill's fused back end forms the same sum in the same order).
+template <int D, bool OUT_BF16, bool G_BF16>
 __global__ __launch_bounds__(256) void layer_back_kernel(LayerBackArgs a) {
   constexpr int CG = D / 8;
   constexpr int RPB = 256 / CG;                  // rows per workgroup
@@ -281,15 +273,15 @@ __global__ __launch_bounds__(256) void layer_back_kernel(LayerBackArgs a) {
   const int64_t off = (live ? row : 0) * D + 8 * cg;
   float o[8], g[8], w[8];
   load8<false>(a.o, off, o);
-  load8<false>(a.g_logit, off, g);
+  load8<G_BF16>(a.g_logit, off, g);
   load8<false>(a.norm_w, 8 * cg, w);
   float ss = 0.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) ss += o[e] * o[e];
+  for (int e = 0; e < 8; ++e) ss = __builtin_fmaf(o[e], o[e], ss);
   ss = row_sum<CG>(ss);
   const float r = __builtin_amdgcn_rsqf(ss / D + a.eps);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = o[e] * r * w[e] * sigmoidf_(g[e]);
+  for (int e = 0; e < 8; ++e) o[e] = o[e] * r * w[e] * sigmoid_rcp(g[e]);
   if (live) store8<OUT_BF16>(a.out, off, o);
 }
 
@@ -326,8 +318,13 @@ hipError_t back_t(const LayerBackArgs& a, bool out_bf16, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
   constexpr int RPB = 256 / (D / 8);
   const dim3 grid((unsigned)((a.rows + RPB - 1) / RPB));
-  if (out_bf16) hipLaunchKernelGGL((layer_back_kernel<D, true>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((layer_back_kernel<D, false>), grid, dim3(256), 0, s, a);
+  if (a.g_bf16) {
+    if (out_bf16) hipLaunchKernelGGL((layer_back_kernel<D, true, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((layer_back_kernel<D, false, true>), grid, dim3(256), 0, s, a);
+  } else {
+    if (out_bf16) hipLaunchKernelGGL((layer_back_kernel<D, true, false>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((layer_back_kernel<D, false, false>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -59,7 +59,12 @@
 // own: in pass 1 (prefill_map_chain_kernel) four wavefronts carry the N rows
 // while eight form the next chunk's state-free phases and carry the M rows; in
 // pass 3 (prefill_wu_pipe_kernel) four wavefronts run the chain while the
-// other four prepare the next chunk's operands.
+// other four prepare the next chunk's operands. Pass 3 can also apply the KDA
+// layer's back end (RMSNorm over d, norm weights, sigmoid output gate) to each
+// chunk's output tile on chip and write the layer output instead of o: the
+// chain wavefronts form each row's sum of squares in the order the separate
+// back-end kernel does (same bits), the producers stage the gate logits and
+// store the bf16 output rows through LDS, whole rows at a time.
 // Accumulator layout of a 16x16 MFMA tile: lane l holds rows 4(l/16)+i,
 // column l%16. When an accumulator tile feeds the next product as its
 // K-operand, the K index is permuted (lane group g supplies rows 4g..4g+3 of
@@ -1812,9 +1817,23 @@ struct LdsPipe {
   static constexpr int OFF_RQ = OFF_RK + C * D * 2;             // raw q
   static constexpr int TOTAL = OFF_RQ + C * D * 2;
   static_assert(BUF % 512 == 0 && OFF_W % 512 == 0, "buffers keep the bank alignment of the other form");
+  // fused back end only: each chain wavefront's share of a row's sum of
+  // squares [64][4] f32 (then 64 floats the lanes without a share write),
+  // norm_w [D], and one chunk's output-gate logits [64][D] bf16, which the
+  // chain overwrites in place with the bf16 output rows
+  static constexpr int OFF_PART = TOTAL;
+  static constexpr int OFF_NW = OFF_PART + (4 * C + 64) * 4;
+  static constexpr int LDG = 2 * D + 16;                         // gate / output row stride (bytes)
+  static constexpr int OFF_G = OFF_NW + D * 4;
+  static constexpr int TOTAL_EPI = OFF_G + C * LDG;
 };
 
-template <int D>
+// What pass 3 writes per token: o (fp32), or the layer output after the
+// fused back end in bf16 or fp32
+enum { EPI_O = 0, EPI_BF16 = 1, EPI_F32 = 2 };
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int D, int EPI>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_wu_pipe_kernel(PrefillArgs a) {
   static_assert(D == 128, "four chain wavefronts of 32 state rows");
@@ -1834,6 +1853,9 @@ void prefill_wu_pipe_kernel(PrefillArgs a) {
   _Float16* sW = reinterpret_cast<_Float16*>(smem + P::OFF_W);
   unsigned char* rawK = smem + P::OFF_RK;
   unsigned char* rawQ = smem + P::OFF_RQ;
+  [[maybe_unused]] float* sPart = reinterpret_cast<float*>(smem + P::OFF_PART);
+  [[maybe_unused]] float* sNw = reinterpret_cast<float*>(smem + P::OFF_NW);
+  [[maybe_unused]] unsigned char* sG = smem + P::OFF_G;
 
   const int wave = threadIdx.x / 64;
   const bool chain = wave < NC;                  // (uniform per wavefront)
@@ -2012,6 +2034,39 @@ void prefill_wu_pipe_kernel(PrefillArgs a) {
       if (e < W_VEC) reinterpret_cast<f32x4*>(sW)[e] = wreg[j];
     }
   };
+  // output-gate logits of chunk ch (fused back end): rows as the raw rows,
+  // into registers, then into LDS for the chain (rows past the end repeat the last)
+  [[maybe_unused]] i32x4 greg[EPI != EPI_O ? RI : 1];
+  [[maybe_unused]] auto fetch_g = [&](int ch) __attribute__((always_inline)) {
+    const int n = chunk_len(ch);
+    const uint16_t* gb = static_cast<const uint16_t*>(a.g_logit) + ((item.tok_begin + (int64_t)ch * C) * a.H + h) * D;
+#pragma unroll
+    for (int j = 0; j < RI; ++j) {
+      const int row = (pw + NP * j) * RPI + lane / LPR;
+      greg[j] = *reinterpret_cast<const i32x4*>(gb + (uint32_t)min(row, n - 1) * HDu + 8u * (uint32_t)(lane % LPR));
+    }
+  };
+  [[maybe_unused]] auto put_g = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < RI; ++j) {
+      const int row = (pw + NP * j) * RPI + lane / LPR;
+      *reinterpret_cast<i32x4*>(sG + row * P::LDG + 16 * (lane % LPR)) = greg[j];
+    }
+  };
+  // bf16 output rows of chunk chp (np tokens) from LDS, where the chain left
+  // them: whole rows, 16 bytes a lane; rows past the end repeat the last one
+  // (same bytes), and with real false everything goes to the sink
+  [[maybe_unused]] auto store_out = [&](int chp, int np, bool real) __attribute__((always_inline)) {
+    const int64_t tb = item.tok_begin + (int64_t)chp * C;
+#pragma unroll
+    for (int j = 0; j < RI; ++j) {
+      const int row = min((pw + NP * j) * RPI + lane / LPR, np - 1);
+      const i32x4 v = *reinterpret_cast<const i32x4*>(sG + row * P::LDG + 16 * (lane % LPR));
+      uint16_t* dst = real ? static_cast<uint16_t*>(a.out) + ((tb + row) * a.H + h) * D + 8 * (lane % LPR)
+                           : static_cast<uint16_t*>(a.out_sink);
+      __builtin_nontemporal_store(v, reinterpret_cast<i32x4*>(dst));
+    }
+  };
   // ---- chain side: stored U' of chunk ch (this wavefront's slices) -------------
   auto fetch_up = [&](int ch) __attribute__((always_inline)) {
     const i32x4* up = reinterpret_cast<const i32x4*>(wu_base + (int64_t)ch * WU_BYTES + W_BYTES);
@@ -2028,9 +2083,47 @@ void prefill_wu_pipe_kernel(PrefillArgs a) {
   // all memory traffic in flight where the paths join.
   const int last = n_chunks - 1;
   if (chain) {
+    // fused back end: the chunk's O tiles, held from interval B into the next
+    // interval A, where every chain wavefront's share of each row's sum of
+    // squares is in LDS and the back end runs between that interval's products
+    [[maybe_unused]] f32x4 Oh[EPI != EPI_O ? 4 : 1][SPW];
+    // fused back end of one 16-token tile ct of a chunk whose outputs start at
+    // element eb and hold n tokens: out = o rsqrt(mean o^2 + eps) norm_w sigmoid(g)
+    [[maybe_unused]] auto epi_tile = [&](int ct, int64_t eb, int n) __attribute__((always_inline)) {
+      const float* nw = sNw + 16 * SPW * wave + 4 * g;
+      const int c = 16 * ct + l16;
+      const f32x4 pp = *reinterpret_cast<const f32x4*>(sPart + 4 * c);
+      const float ss = (pp[0] + pp[1]) + (pp[2] + pp[3]);
+      const float r = __builtin_amdgcn_rsqf(ss / D + a.eps);
+#pragma unroll
+      for (int sl = 0; sl < SPW; ++sl) {
+        const f32x4 w4 = *reinterpret_cast<const f32x4*>(nw + 16 * sl);
+        const u32x2 gb = *reinterpret_cast<const u32x2*>(sG + c * P::LDG + 2 * (16 * SPW * wave + 16 * sl + 4 * g));
+        const float gv[4] = {bf16_bits_to_f32(gb[0] & 0xFFFFu), bf16_bits_to_f32(gb[0] >> 16),
+                             bf16_bits_to_f32(gb[1] & 0xFFFFu), bf16_bits_to_f32(gb[1] >> 16)};
+        f32x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = Oh[ct][sl][e] * r * w4[e] * sigmoid_rcp(gv[e]);
+        if constexpr (EPI == EPI_BF16) {
+          // in place of the logits just read; the producers store whole rows
+          *reinterpret_cast<u32x2*>(sG + c * P::LDG + 2 * (16 * SPW * wave + 16 * sl + 4 * g)) =
+              u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+        } else {
+          // unconditional stores (rows past the end go to the sink): a store
+          // under a lane mask makes the waits of interval A drain these stores
+          const int64_t off = eb + (int64_t)c * HD + 16 * sl;
+          float* dst = c < n ? static_cast<float*>(a.out) + off : static_cast<float*>(a.out_sink);
+          *reinterpret_cast<f32x4*>(dst) = y;
+        }
+      }
+    };
     fetch_up(0);
     __syncthreads();                             // the producers' prologue
     __syncthreads();
+    // fused back end: U'(0) has landed before the loop (vmcnt(0)), so at the
+    // loop head both ways in agree that U' is complete, and interval A waits
+    // for none of the back end's memory traffic
+    if constexpr (EPI != EPI_O) __builtin_amdgcn_s_waitcnt(0x0F70);
     for (int ch = 0; ch < n_chunks; ++ch) {
       const int b = ch & 1;
       const int64_t tok0 = item.tok_begin + (int64_t)ch * C;
@@ -2059,6 +2152,10 @@ void prefill_wu_pipe_kernel(PrefillArgs a) {
           for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
             for (int sl = 0; sl < SPW; ++sl) U[sl][ct] = mfma_f16(w[ct], nsop[sl], U[sl][ct]);
+          // fused back end of the previous chunk (a full one), tile ks, between
+          // these products (at the first chunk every row goes to the sink)
+          if constexpr (EPI != EPI_O)
+            epi_tile(ks, (tok0 - C) * HD + (int64_t)h * D + 16 * SPW * wave + 4 * g, ch > 0 ? C : 0);
         }
 #pragma unroll
         for (int sl = 0; sl < SPW; ++sl)
@@ -2070,13 +2167,13 @@ void prefill_wu_pipe_kernel(PrefillArgs a) {
       // U' of the next chunk is fetched first: the o stores then come after
       // it, and interval A's wait for it does not wait for them
       fetch_up(min(ch + 1, last));
+      const int64_t obase = tok0 * HD + (int64_t)h * D + 16 * SPW * wave + 4 * g;
       const _Float16* sQt = reinterpret_cast<const _Float16*>(smem + b * P::BUF + P::QT);
       const _Float16* sKtT = reinterpret_cast<const _Float16*>(smem + b * P::BUF + P::KTT);
       const _Float16* sB = reinterpret_cast<const _Float16*>(smem + b * P::BUF + P::BG);
       const float* sGam = reinterpret_cast<const float*>(smem + b * P::BUF + P::GS) + 3 * C;
       // O^T = S0 Q~^T + U^T B^T, one 16-token tile at a time; lane (g, l16)
       // holds O[token 16ct + l16][values 16 slice + 4g .. +3]
-      const int64_t obase = tok0 * HD + (int64_t)h * D + 16 * SPW * wave + 4 * g;
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
         f16x8 qa[D / 32], ba[2];
@@ -2099,10 +2196,39 @@ void prefill_wu_pipe_kernel(PrefillArgs a) {
             OT[sl] = mfma_f16(ul[sl][ks], ba[ks], OT[sl]);
           }
         const int c = 16 * ct + l16;
-        if (c < n) {
-          float* orow = a.o + obase + (int64_t)c * HD;
+        if constexpr (EPI == EPI_O) {
+          if (c < n) {
+            float* orow = a.o + obase + (int64_t)c * HD;
 #pragma unroll
-          for (int sl = 0; sl < SPW; ++sl) __builtin_nontemporal_store(OT[sl], reinterpret_cast<f32x4*>(orow + 16 * sl));
+            for (int sl = 0; sl < SPW; ++sl)
+              __builtin_nontemporal_store(OT[sl], reinterpret_cast<f32x4*>(orow + 16 * sl));
+          }
+        } else {
+          // this wavefront's share of row c's sum of squares, formed as the
+          // back end's 16 lanes of 8 values form it: lane group g holds values
+          // 4g .. 4g+3 of each 16-value slice, so an odd group continues its
+          // even neighbour's running sum (the first four of a lane's eight), and
+          // the pairwise sums over lanes, then slices, follow the xor order
+          float part = 0.f;
+#pragma unroll
+          for (int sl = 0; sl < SPW; ++sl) {
+            float s0 = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s0 = __builtin_fmaf(OT[sl][e], OT[sl][e], s0);
+            // lane groups 1 and 3 take the running sums of groups 0 and 2
+            // (v_permlane16_swap: odd rows of the first operand come from the
+            // even rows of the second)
+            float s1 = __uint_as_float(
+                __builtin_amdgcn_permlane16_swap(__float_as_uint(s0), __float_as_uint(s0), false, false)[0]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s1 = __builtin_fmaf(OT[sl][e], OT[sl][e], s1);
+            // groups g and g ^ 2 add their sums (v_permlane32_swap exchanges the halves)
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s1), __float_as_uint(s1), false, false);
+            s1 = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+            part = sl == 0 ? s1 : part + s1;
+            Oh[ct][sl] = OT[sl];
+          }
+          sPart[(g & 1) ? 4 * c + wave : 4 * C + lane] = part;
         }
       }
       // S^T <- 2^(G_n) S^T + K~^T U, four row tiles per batch
@@ -2142,6 +2268,13 @@ void prefill_wu_pipe_kernel(PrefillArgs a) {
       }
       __syncthreads();
     }
+    if constexpr (EPI != EPI_O) {
+      // fused back end of the last chunk
+      const int64_t tl = item.tok_begin + (int64_t)last * C;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) epi_tile(ct, tl * HD + (int64_t)h * D + 16 * SPW * wave + 4 * g, chunk_len(last));
+    }
+    if constexpr (EPI == EPI_BF16) __syncthreads();    // the producers store the last chunk's rows
     if (item.seg == item.n_segs - 1) {
       float* dst = a.final_state + ((int64_t)item.seq * a.H + h) * DD;
 #pragma unroll
@@ -2156,6 +2289,10 @@ void prefill_wu_pipe_kernel(PrefillArgs a) {
   // ---- producers: prologue (chunk 0's operands in buffer 0, W(0) in LDS) ---------
   fetch_raw(0);
   fetch_w(0);
+  if constexpr (EPI != EPI_O) {
+    fetch_g(0);
+    for (int e = ptid; e < D; e += NPT) sNw[e] = a.norm_w[e];
+  }
   for (int e = ptid; e < 2 * 6 * 256; e += NPT) {     // upper tiles of both B buffers
     const int bb = e / (6 * 256), t = (e / 256) % 6, rr = (e % 256) / 16, cc = e % 16;
     const int R = t < 3 ? 0 : (t < 5 ? 1 : 2);
@@ -2176,6 +2313,7 @@ void prefill_wu_pipe_kernel(PrefillArgs a) {
     const bool has_next = ch + 1 < n_chunks;
     refresh();
     // ---- interval A: chunk ch+1's raw rows into LDS, its decay scan, the fetch of its W
+    // (and of chunk ch's output-gate logits)
     put_raw();
     if (has_next) p1(nb, chunk_len(ch + 1));
     fetch_w(min(ch + 1, last));
@@ -2187,7 +2325,16 @@ void prefill_wu_pipe_kernel(PrefillArgs a) {
     fetch_raw(min(ch + 2, last));
     if (has_next) p3(nb, chunk_len(ch + 1));
     put_w();
+    if constexpr (EPI == EPI_BF16) store_out(ch - 1, C, ch > 0);   // chunk ch-1's rows (full), then
+    if constexpr (EPI != EPI_O) {                                  // chunk ch's logits in their place
+      put_g();
+      fetch_g(min(ch + 1, last));
+    }
     __syncthreads();
+  }
+  if constexpr (EPI == EPI_BF16) {
+    __syncthreads();                             // the chain's back end of the last chunk
+    store_out(last, chunk_len(last), true);
   }
 }
 
@@ -2409,15 +2556,16 @@ hipError_t launch_pass(const PrefillArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, int EPI>
 hipError_t launch_wu_pipe(const PrefillArgs& a, hipStream_t s) {
   using P = LdsPipe<D>;
-  static_assert(P::TOTAL <= 160 * 1024, "LDS budget");
-  auto kern = prefill_wu_pipe_kernel<D>;
+  constexpr int lds = EPI == EPI_O ? P::TOTAL : P::TOTAL_EPI;
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  auto kern = prefill_wu_pipe_kernel<D, EPI>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, P::TOTAL);
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(a.n_items * a.H), dim3(512), P::TOTAL, s, a);
+  hipLaunchKernelGGL(kern, dim3(a.n_items * a.H), dim3(512), lds, s, a);
   return hipGetLastError();
 }
 
@@ -2435,6 +2583,9 @@ hipError_t launch_map_chain(const PrefillArgs& a, hipStream_t s) {
 
 template <int D, bool BF16, bool PK>
 hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
+  // fused back end: split sequences only (a whole pass may still run, for
+  // empty sequences' final states, and writes no o)
+  if (a.out != nullptr && a.seg_chunks == 0) return hipErrorInvalidValue;
   if (a.seg_chunks == 0) return launch_pass<D, BF16, PK, false, false>(a, s);
   hipError_t e;                                                 // pass 1: segment maps, W and U' per chunk
   if constexpr (D == 128 && BF16 && !PK)
@@ -2449,10 +2600,14 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(segment_scan_kernel<D>, dim3(a.num_seqs * a.H * (D / 16)), dim3(256), scan_lds, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if constexpr (D == 128 && BF16 && !PK)
-    e = launch_wu_pipe<D>(a, s);                                  // pass 3: every segment (qk_shift is 0 at d = 128)
-  else
+  if constexpr (D == 128 && BF16 && !PK) {                      // pass 3: every segment (qk_shift is 0 at d = 128)
+    if (a.out == nullptr) e = launch_wu_pipe<D, EPI_O>(a, s);
+    else if (a.out_bf16) e = launch_wu_pipe<D, EPI_BF16>(a, s);
+    else e = launch_wu_pipe<D, EPI_F32>(a, s);
+  } else {
+    if (a.out != nullptr) return hipErrorInvalidValue;          // the fused back end has this form only
     e = launch_pass<D, BF16, PK, false, true>(a, s);
+  }
   if (e != hipSuccess || !a.any_whole) return e;
   return launch_pass<D, BF16, PK, false, false>(a, s);          // sequences that are not split
 }

@@ -58,6 +58,9 @@ def load() -> ctypes.CDLL:
         "kda_layer_front": ([P, I32, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P, P, P, P, P, P],
                             ctypes.c_int),
         "kda_layer_back": ([P, I64, P, P, P, ctypes.c_float, I32, P, P], ctypes.c_int),
+        "kda_layer_prefill_workspace_size": ([P, I32, P, I32, I64, I64, P], ctypes.c_int),
+        "kda_layer_prefill": ([P, I32, P, P, I32, I64, I64, P, P, P, P, P, P, P, P, ctypes.c_float, I32, P, P, P,
+                               P, SZ, P], ctypes.c_int),
         "kda_prefill_backward_workspace_size": ([P, I32, P, P], ctypes.c_int),
         "kda_prefill_backward": ([P, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
                                  ctypes.c_int),
@@ -72,7 +75,8 @@ def load() -> ctypes.CDLL:
 
 EXPORTED = ("kda_abi_version", "kda_last_error", "kda_snapshot_count", "kda_prefill_workspace_size",
             "kda_prefill_chunked", "kda_prefill_chunked_noalloc", "kda_decode_step", "kda_decode_tokens", "kda_layer_front",
-            "kda_layer_back", "kda_prefill_backward_workspace_size", "kda_prefill_backward")
+            "kda_layer_back", "kda_layer_prefill_workspace_size", "kda_layer_prefill",
+            "kda_prefill_backward_workspace_size", "kda_prefill_backward")
 
 
 def _check(fn: str, rc: int) -> None:
@@ -287,6 +291,45 @@ def kda_layer_back(shape: KdaShape, num_tokens: int, o, g_logit, norm_w, eps: fl
         _ptr(out), s))
 
 
+def kda_layer_prefill_workspace_size(shape: KdaShape, cu_seqlens_host: torch.Tensor, chunk: int = CHUNK,
+                                     snapshot_interval: int = 0, segment_tokens: int = -1) -> int:
+    cu = cu_seqlens_host.to("cpu", torch.int64).contiguous()
+    out = ctypes.c_size_t(0)
+    _check("kda_layer_prefill_workspace_size",
+           load().kda_layer_prefill_workspace_size(ctypes.byref(shape), cu.numel() - 1, _ptr(cu), int(chunk),
+                                                   int(snapshot_interval), int(segment_tokens), ctypes.byref(out)))
+    return out.value
+
+
+def kda_layer_prefill(shape: KdaShape, cu_seqlens_host: torch.Tensor, cu_seqlens_dev: torch.Tensor,
+                      q, k, v, alpha, beta, initial_state, g_logit, norm_w, eps: float, out_dtype: int, out,
+                      final_state, snapshots, workspace: torch.Tensor, chunk: int = CHUNK,
+                      snapshot_interval: int = 0, segment_tokens: int = -1, stream=None) -> None:
+    """Enqueues the recurrence and the layer back end (out instead of o)."""
+    _args("kda_layer_prefill", shape, q=(q, "qkv"), k=(k, "qkv"), v=(v, "qkv"), alpha=(alpha, F32),
+          beta=(beta, F32), initial_state=(initial_state, F32), g_logit=(g_logit, "qkv"), norm_w=(norm_w, F32),
+          out=(out, torch.bfloat16 if out_dtype == KDA_BF16 else F32), final_state=(final_state, F32),
+          snapshots=(snapshots, F32), cu_seqlens_dev=(cu_seqlens_dev, I64))
+    T = q.shape[0]
+    cu = _cu_host("kda_layer_prefill", cu_seqlens_host, T)
+    N, H, dk, dv = cu.numel() - 1, shape.num_heads, shape.d_k, shape.d_v
+    n_snap = kda_snapshot_count(cu, snapshot_interval)
+    dev = q.device
+    _geom("kda_layer_prefill", dev, ("snapshots",), q=(q, (T, H, dk)), k=(k, (T, H, dk)), v=(v, (T, H, dv)),
+          alpha=(alpha, _alpha_shape(shape, (T,))), beta=(beta, (T, H)), initial_state=(initial_state, (N, H, dv, dk)),
+          g_logit=(g_logit, (T, H, dv)), norm_w=(norm_w, (dv,)), out=(out, (T, H, dv)),
+          final_state=(final_state, (N, H, dv, dk)), snapshots=(snapshots, (n_snap, H, dv, dk)),
+          cu_seqlens_dev=(cu_seqlens_dev, (N + 1,)))
+    if workspace.device != dev:
+        raise ValueError(f"kda_layer_prefill: workspace is on {workspace.device}, expected {dev}")
+    s = ctypes.c_void_p(stream.cuda_stream) if stream is not None else _stream_ptr(dev)
+    _check("kda_layer_prefill", load().kda_layer_prefill(
+        ctypes.byref(shape), cu.numel() - 1, _ptr(cu), _ptr(cu_seqlens_dev), int(chunk), int(snapshot_interval),
+        int(segment_tokens), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(initial_state),
+        _ptr(g_logit), _ptr(norm_w), float(eps), int(out_dtype), _ptr(out), _ptr(final_state), _ptr(snapshots),
+        _ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size()), s))
+
+
 def kda_prefill_backward_workspace_size(shape: KdaShape, cu_seqlens_host: torch.Tensor) -> int:
     cu = cu_seqlens_host.to("cpu", torch.int64).contiguous()
     out = ctypes.c_size_t(0)
@@ -466,6 +509,36 @@ def layer_back(o: torch.Tensor, g_logit: torch.Tensor, norm_w: torch.Tensor, eps
     out = torch.empty((T, H, dv), dtype=out_dtype, device=o.device)
     kda_layer_back(shape, T, o, g_logit, norm_w, eps, KDA_BF16 if out_dtype == torch.bfloat16 else KDA_F32, out)
     return out
+
+
+def layer_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,
+                  g_logit: torch.Tensor, norm_w: torch.Tensor, eps: float = 1e-6,
+                  cu_seqlens: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
+                  snapshot_interval: int = 0, cu_seqlens_host: Optional[torch.Tensor] = None,
+                  segment_tokens: int = -1, out_dtype: torch.dtype = torch.bfloat16):
+    """The recurrence and the layer back end in one call: inputs as
+    prefill_chunked (d_k = d_v) plus g_logit [T,H,d] in the q/k/v dtype and
+    norm_w [d] fp32. Returns (out [T,H,d] in out_dtype, final_state, snapshots)."""
+    T, H, dk = q.shape
+    dv = v.shape[2]
+    _shapes("layer_prefill", k=(k, (T, H, dk)), v=(v, (T, H, dv)), beta=(beta, (T, H)),
+            alpha=(alpha, (T, H, dk) if alpha.dim() == 3 else (T, H)), g_logit=(g_logit, (T, H, dv)),
+            norm_w=(norm_w, (dv,)))
+    dev = q.device
+    cu_dev, cu_seqlens_host = _cu_pair(cu_seqlens, cu_seqlens_host, T, dev)
+    N = cu_seqlens_host.numel() - 1
+    _contig(q, k, v, alpha, beta, initial_state, g_logit, norm_w)
+    shape = make_shape(H, dk, dv, q.dtype, alpha.dim() == 3)
+    n_snap = kda_snapshot_count(cu_seqlens_host, snapshot_interval)
+    out = torch.empty((T, H, dv), dtype=out_dtype, device=dev)
+    fin = torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev)
+    snaps = torch.empty((n_snap, H, dv, dk), dtype=torch.float32, device=dev)
+    ws_bytes = kda_layer_prefill_workspace_size(shape, cu_seqlens_host, CHUNK, snapshot_interval, segment_tokens)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    kda_layer_prefill(shape, cu_seqlens_host, cu_dev, q, k, v, alpha, beta, initial_state, g_logit, norm_w, eps,
+                      KDA_BF16 if out_dtype == torch.bfloat16 else KDA_F32, out, fin,
+                      snaps if n_snap > 0 else None, ws, CHUNK, snapshot_interval, segment_tokens)
+    return out, fin, snaps
 
 
 def prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, alpha: torch.Tensor, beta: torch.Tensor,

@@ -263,6 +263,42 @@ int kda_layer_back(const kda_shape* shape, int64_t num_tokens, const float* o,
                    const float* g_logit, const float* norm_w, float eps, int32_t out_dtype,
                    void* out, void* hip_stream);
 
+/* Bytes of device workspace kda_layer_prefill needs (host-only; errors as
+ * kda_layer_prefill's validation). */
+int kda_layer_prefill_workspace_size(const kda_shape* shape, int32_t num_seqs,
+                                     const int64_t* cu_seqlens_host, int32_t chunk,
+                                     int64_t snapshot_interval, int64_t segment_tokens,
+                                     size_t* bytes);
+
+/* The recurrence and the back end of a KDA layer in one call (page "kda-graft:
+ * Qwen2.5-0.5B с трансплантированным KDA", ailist.pro, section "Идея и
+ * архитектура": the recurrence sits between the layer's projections and its
+ * norm and output gate):
+ *   out = o * rsqrt(mean over d of o^2 + eps) * norm_w * sigmoid(g_logit)
+ * per (token, head), o being what kda_prefill_chunked computes for the same
+ * arguments. For the scalar gate with bf16 q, k, v at d = 128, when the plan
+ * splits every non-empty sequence into segments (segment_tokens shorter than
+ * each of them, or -1 with fewer (sequence, head) chains than compute units), the
+ * last pass of the prefill applies the back end to each chunk's output tile
+ * on chip and o never reaches memory. Otherwise the prefill writes an fp32 o
+ * into the workspace and the back-end kernel of kda_layer_back reads it. Either
+ * way out has the bits of kda_prefill_chunked followed by kda_layer_back with
+ * g_logit widened to fp32.
+ * Arguments as kda_prefill_chunked (final_state, snapshots and their rules
+ * included), with d_k = d_v (KDA_ERR_SHAPE otherwise) and
+ *   g_logit: [T, H, d] in the qkv dtype; norm_w: fp32 [d]; eps >= 0;
+ *   out: [T, H, d] in out_dtype (KDA_BF16 or KDA_F32), overlapping no input;
+ *   workspace: at least kda_layer_prefill_workspace_size bytes.
+ * Alignment: g_logit, norm_w and out 16 bytes. */
+int kda_layer_prefill(const kda_shape* shape, int32_t num_seqs,
+                      const int64_t* cu_seqlens_host, const int64_t* cu_seqlens_dev,
+                      int32_t chunk, int64_t snapshot_interval, int64_t segment_tokens,
+                      const void* q, const void* k, const void* v,
+                      const float* alpha, const float* beta, const float* initial_state,
+                      const void* g_logit, const float* norm_w, float eps, int32_t out_dtype,
+                      void* out, float* final_state, float* snapshots,
+                      void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* Workspace bytes of kda_prefill_backward for this packing (device memory,
  * caller-owned, 16-byte aligned). It holds the recomputed forward (its states
  * after every 64 tokens) and about 1 MB per (chunk, head) at d = 128

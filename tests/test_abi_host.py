@@ -42,6 +42,7 @@ def test_kda_header_symbols_exported(K):
                           "kda_prefill_workspace_size", "kda_prefill_chunked", "kda_prefill_chunked_noalloc",
                           "kda_decode_step",
                           "kda_decode_tokens", "kda_layer_front", "kda_layer_back",
+                          "kda_layer_prefill_workspace_size", "kda_layer_prefill",
                           "kda_prefill_backward_workspace_size", "kda_prefill_backward"}
     lib = ctypes.CDLL(K.LIB_PATH)
     for n in names:
@@ -317,6 +318,54 @@ def test_layer_host_rejections(K):
     assert back(pk, 4, eps=float("nan")) == K.KDA_ERR_ARG
     assert back(pk, 4, out=None) == K.KDA_ERR_ARG
     assert back(pk, 4, g=0x2004) == K.KDA_ERR_ALIGN
+
+
+def test_layer_prefill_plan_and_host_rejections(K):
+    lib = K.load()
+    sc = K.make_shape(2, 128, 128, torch.bfloat16, False)
+    pk = K.make_shape(2, 64, 64, torch.bfloat16, True)
+    cu = torch.tensor([0, 1100, 1100, 1741], dtype=torch.int64)     # an empty sequence in the pack
+    T, H, d = 1741, 2, 128
+    # fused form (every non-empty sequence split): the prefill's plan and a 256-byte sink
+    pre = K.kda_prefill_workspace_size(sc, cu, 64, 0, 256)
+    lay = K.kda_layer_prefill_workspace_size(sc, cu, 64, 0, 256)
+    assert pre < lay <= (pre + 255) // 256 * 256 + 256
+    # composed form (unsegmented, or a sequence that stays whole): an fp32 o in the workspace
+    for shape, c, seg in ((sc, cu, 0), (sc, torch.tensor([0, 1100, 1200], dtype=torch.int64), 256), (pk, cu, 256)):
+        pre = K.kda_prefill_workspace_size(shape, c, 64, 0, seg)
+        t, dd = int(c[-1]), shape.d_v
+        assert K.kda_layer_prefill_workspace_size(shape, c, 64, 0, seg) >= pre + t * H * dd * 4
+    with pytest.raises(K.KdaError):
+        K.kda_layer_prefill_workspace_size(K.make_shape(2, 64, 128, torch.bfloat16, False), cu)
+
+    def call(sh, cu_h, ws_bytes=1 << 40, out_dtype=K.KDA_BF16, eps=1e-6, seg=256, **kw):
+        p = dict(cu_dev=0x100, q=0x100000, k=0x200000, v=0x300000, a=0x400000, b=0x500000, s0=None,
+                 g=0x600000, w=0x700000, out=0x800000, fin=0x900000, snaps=None, ws=0x10000000)
+        p.update(kw)
+        f = lambda n: None if p[n] is None else _fake(p[n])  # noqa: E731
+        return lib.kda_layer_prefill(ctypes.byref(sh), cu_h.numel() - 1,
+                                     cu_h.numpy().ctypes.data_as(ctypes.c_void_p), f("cu_dev"), 64, 0, seg,
+                                     f("q"), f("k"), f("v"), f("a"), f("b"), f("s0"), f("g"), f("w"),
+                                     ctypes.c_float(eps), out_dtype, f("out"), f("fin"), f("snaps"), f("ws"),
+                                     ctypes.c_size_t(ws_bytes), None)
+
+    assert call(sc, torch.tensor([0], dtype=torch.int64)) == K.KDA_OK        # no sequences
+    assert call(K.make_shape(2, 128, 64, torch.bfloat16, False), cu) == K.KDA_ERR_SHAPE
+    assert "d_k = d_v" in K.kda_last_error()
+    assert call(sc, cu, out_dtype=99) == K.KDA_ERR_ARG
+    assert call(sc, cu, eps=-1.0) == K.KDA_ERR_ARG
+    assert call(sc, cu, g=None) == K.KDA_ERR_ARG
+    assert call(sc, cu, w=None) == K.KDA_ERR_ARG
+    assert call(sc, cu, out=None) == K.KDA_ERR_ARG and "out" in K.kda_last_error()
+    assert call(sc, cu, g=0x600008) == K.KDA_ERR_ALIGN
+    assert call(sc, cu, out=0x800008) == K.KDA_ERR_ALIGN
+    assert call(sc, cu, out=0x600000) == K.KDA_ERR_ARG and "g_logit" in K.kda_last_error()
+    assert call(sc, cu, fin=0x700000) == K.KDA_ERR_ARG and "norm_w" in K.kda_last_error()
+    assert call(sc, cu, out=0x100000) == K.KDA_ERR_ARG and "alias" in K.kda_last_error()   # out over q
+    assert call(sc, cu, ws_bytes=16) == K.KDA_ERR_WORKSPACE
+    assert call(sc, cu, ws=None) == K.KDA_ERR_WORKSPACE
+    # out in bf16 is half the size of o: an out just past q's end is fine for validation
+    assert call(sc, cu, out=0x100000 + T * H * d * 2, k=0x2000000, ws_bytes=16) == K.KDA_ERR_WORKSPACE
 
 
 def test_backward_host_rejections(K):
