@@ -264,11 +264,13 @@ LayerPlan plan_layer(const kda_shape* s, int32_t num_seqs, const int64_t* cu, in
                      int64_t segment_tokens, int cus) {
   LayerPlan l{};
   l.pre = plan_full(s, num_seqs, cu, interval, segment_tokens, cus);
-  // pass 3 of the scalar-gate bf16 d = 128 form carries the fused back end;
-  // it runs the segments of split sequences, so every sequence with tokens
-  // must be split (empty ones only take their final state from the other pass)
-  l.fused = s->d_k == 128 && s->qkv_dtype == KDA_BF16 && s->gate == KDA_GATE_SCALAR &&
-            l.pre.kern.seg_chunks > 0 && l.pre.kern.whole_tokens == 0;
+  // pass 3 carries the fused back end in two forms, the scalar gate at d = 128
+  // and the per-key (KDA) gate at d = 64, both with bf16 inputs; it runs the
+  // segments of split sequences, so every sequence with tokens must be split
+  // (empty ones only take their final state from the other pass)
+  const bool form = s->qkv_dtype == KDA_BF16 && ((s->d_k == 128 && s->gate == KDA_GATE_SCALAR) ||
+                                                 (s->d_k == 64 && s->gate == KDA_GATE_PER_KEY));
+  l.fused = form && l.pre.kern.seg_chunks > 0 && l.pre.kern.whole_tokens == 0;
   l.aux_off = round_up(l.pre.bytes);
   l.bytes = l.aux_off + (l.fused ? kAlign : round_up((size_t)cu[num_seqs] * s->num_heads * s->d_v * sizeof(float)));
   return l;
@@ -940,7 +942,7 @@ int kda_layer_prefill(const kda_shape* shape, int32_t num_seqs,
   a.out_sink = ws + plan.aux_off;
   a.eps = eps;
   a.out_bf16 = out_dtype == KDA_BF16;
-  const hipError_t e = kda::launch_prefill(a, (int)d, true, false, st);
+  const hipError_t e = kda::launch_prefill(a, (int)d, true, shape->gate == KDA_GATE_PER_KEY, st);
   if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "layer prefill launch failed: %s", hipGetErrorString(e));
   g_err[0] = '\0';
   return KDA_OK;

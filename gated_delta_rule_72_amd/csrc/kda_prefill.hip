@@ -178,7 +178,18 @@ struct Lds {
   static_assert(A_RK >= A_W + C * LDQ * 2, "raw K/Q staging (during P6) must not touch W");
   static_assert(C * D * 2 <= C * LDQ * 2, "a staged raw [64][D] bf16 block fits its region");
   static constexpr int TOTAL = OFF_A + A_BYTES;
+  // fused back end (pass 3 only): each wavefront's share of a row's sum of
+  // squares [64][up to 8] f32 (then 64 floats the lanes without a share
+  // write), norm_w [D]
+  static constexpr int OFF_EPI = TOTAL;
+  static constexpr int OFF_ENW = OFF_EPI + (8 * C + 64) * 4;
+  static constexpr int TOTAL_EPI = OFF_ENW + D * 4;
 };
+
+// What pass 3 writes per token: o (fp32), or the layer output after the
+// fused back end in bf16 or fp32
+enum { EPI_O = 0, EPI_BF16 = 1, EPI_F32 = 2 };
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <bool BF16>
 struct RawGroup;  // 8 consecutive q/k/v elements of one token
@@ -560,10 +571,11 @@ __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
   return x;
 }
 
-template <int D, bool BF16, bool PER_KEY, bool MAP, bool WU, int NW>
+template <int D, bool BF16, bool PER_KEY, bool MAP, bool WU, int NW, int EPI = EPI_O>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void prefill_kernel(PrefillArgs a) {
   static_assert(!(MAP && WU), "the map pass forms W and U' itself");
+  static_assert(EPI == EPI_O || (WU && BF16), "the fused back end runs in pass 3 of bf16 inputs");
   constexpr int NT = 64 * NW;    // threads
   using L = Lds<D>;
   using CR = ChunkRegs<D, BF16, PER_KEY, NT>;
@@ -588,6 +600,8 @@ void prefill_kernel(PrefillArgs a) {
   float* sRem = sPart + C;
   unsigned char* regA = smem + L::OFF_A;
   float* sG = reinterpret_cast<float*>(regA + L::A_G);
+  [[maybe_unused]] float* sEP = reinterpret_cast<float*>(smem + L::OFF_EPI);
+  [[maybe_unused]] float* sENw = reinterpret_cast<float*>(smem + L::OFF_ENW);
   _Float16* sRK = reinterpret_cast<_Float16*>(regA + L::A_RK);
   _Float16* sRQ = reinterpret_cast<_Float16*>(regA + L::A_RQ);
   // WU: the stored W is loaded into the L buffer (no inverse is formed there)
@@ -665,6 +679,8 @@ void prefill_kernel(PrefillArgs a) {
   const uint32_t HDu = (uint32_t)a.H * D;                       // v row stride (elements)
   const int Hq = a.H >> a.qk_shift, hq = h >> a.qk_shift;       // q/k head (see load_chunk)
   const uint32_t HDqu = (uint32_t)Hq * D;                       // q/k row stride
+  if constexpr (EPI != EPI_O)
+    for (int e = tid; e < D; e += NT) sENw[e] = a.norm_w[e];    // read after the barriers below
   CR regs;
   if (n_chunks > 0) {
     load_chunk<D, BF16, PER_KEY, NT>(regs, a, item.tok_begin, min(C, item.n_tokens), h, tid, v_in_regs);
@@ -685,6 +701,47 @@ void prefill_kernel(PrefillArgs a) {
       __syncthreads();
     }
   }
+
+  // Fused back end (pass 3 of the KDA layer): a chunk's O tiles and output-gate
+  // logits are held until the next chunk starts, when every wavefront's share
+  // of each row's sum of squares is in LDS; one 16-token tile ct of a chunk
+  // whose outputs start at element eb and hold n_ tokens (rows at or past n_
+  // go to the sink): out = o rsqrt(mean o^2 + eps) norm_w sigmoid(g). The
+  // shares combine pairwise in wavefront order, the order in which the
+  // separate back-end kernel's xor shuffles combine its lanes (same bits).
+  [[maybe_unused]] f32x4 Oh[EPI != EPI_O ? 4 : 1];
+  [[maybe_unused]] u32x2 gh[EPI != EPI_O ? 4 : 1];
+  [[maybe_unused]] auto epi_tile = [&](int ct, int64_t eb, int n_, int g_, int l16_) __attribute__((always_inline)) {
+    const int c = 16 * ct + l16_;
+    float ss;
+    if constexpr (NW == 4) {
+      const f32x4 pp = *reinterpret_cast<const f32x4*>(sEP + 4 * c);
+      ss = (pp[0] + pp[1]) + (pp[2] + pp[3]);
+    } else {
+      const f32x4 p0 = *reinterpret_cast<const f32x4*>(sEP + 8 * c);
+      const f32x4 p1 = *reinterpret_cast<const f32x4*>(sEP + 8 * c + 4);
+      ss = ((p0[0] + p0[1]) + (p0[2] + p0[3])) + ((p1[0] + p1[1]) + (p1[2] + p1[3]));
+    }
+    const float r = __builtin_amdgcn_rsqf(ss / D + a.eps);
+    const int w_ = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+    const f32x4 w4 = *reinterpret_cast<const f32x4*>(sENw + 16 * w_ + 4 * g_);
+    const u32x2 gb = gh[ct];
+    const float gv[4] = {bf16_bits_to_f32(gb[0] & 0xFFFFu), bf16_bits_to_f32(gb[0] >> 16),
+                         bf16_bits_to_f32(gb[1] & 0xFFFFu), bf16_bits_to_f32(gb[1] >> 16)};
+    f32x4 y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = Oh[ct][e] * r * w4[e] * sigmoid_rcp(gv[e]);
+    // unconditional stores (rows past the end go to the sink): a store under
+    // a lane mask makes later waits for loads drain these stores
+    const int64_t off = eb + (int64_t)c * HD;
+    if constexpr (EPI == EPI_BF16) {
+      uint16_t* dst = c < n_ ? static_cast<uint16_t*>(a.out) + off : static_cast<uint16_t*>(a.out_sink);
+      *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+    } else {
+      float* dst = c < n_ ? static_cast<float*>(a.out) + off : static_cast<float*>(a.out_sink);
+      *reinterpret_cast<f32x4*>(dst) = y;
+    }
+  };
 
   for (int ch = 0; ch < n_chunks; ++ch) {
     const int64_t tok0 = item.tok_begin + (int64_t)ch * C;
@@ -715,6 +772,21 @@ void prefill_kernel(PrefillArgs a) {
       for (int sl = 0; sl < SPW; ++sl)
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) Up[sl][ct] = up[((SPW * wave + sl) * 4 + ct) * 64 + lane];
+    }
+    if constexpr (EPI != EPI_O) {
+      // this chunk's output-gate logits (rows past the end read the last
+      // row), then the back end of the previous chunk (a full one; at the
+      // first chunk every row goes to the sink)
+      const int64_t eb = tok0 * HD + (int64_t)h * D + 16 * wave + 4 * g;
+      u32x2 gn[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        gn[ct] = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(a.g_logit) + eb +
+                                                 (int64_t)min(16 * ct + l16, n - 1) * HD);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) epi_tile(ct, eb - C * HD, ch > 0 ? C : 0, g, l16);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) gh[ct] = gn[ct];
     }
 
     // ---- P1: cumulative log2 decay, beta; fp32 inputs: q, k to fp16 ---------
@@ -1230,10 +1302,30 @@ void prefill_kernel(PrefillArgs a) {
               OT[sl] = mfma_f16(ul[sl][ks], ba[ks], OT[sl]);
             }
           const int c = 16 * ct + l16;                 // this lane's token in the chunk
-          if (c < n) {
-            float* orow = a.o + obase + (int64_t)c * HD;
+          if constexpr (EPI == EPI_O) {
+            if (c < n) {
+              float* orow = a.o + obase + (int64_t)c * HD;
 #pragma unroll
-            for (int sl = 0; sl < SPW; ++sl) *reinterpret_cast<f32x4*>(orow + 16 * sl) = OT[sl];
+              for (int sl = 0; sl < SPW; ++sl) *reinterpret_cast<f32x4*>(orow + 16 * sl) = OT[sl];
+            }
+          } else {
+            // this wavefront's share of row c's sum of squares, formed as the
+            // back end's lanes of 8 values form theirs: lane group g holds
+            // values 4g .. 4g+3 of the slice, so an odd group continues its
+            // even neighbour's running sum (v_permlane16_swap: odd rows of
+            // the first operand come from even rows of the second), and groups
+            // g and g ^ 2 then add (v_permlane32_swap exchanges the halves)
+            static_assert(SPW == 1, "one slice a wavefront");
+            float s0 = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s0 = __builtin_fmaf(OT[0][e], OT[0][e], s0);
+            float s1 = __uint_as_float(
+                __builtin_amdgcn_permlane16_swap(__float_as_uint(s0), __float_as_uint(s0), false, false)[0]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s1 = __builtin_fmaf(OT[0][e], OT[0][e], s1);
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(s1), __float_as_uint(s1), false, false);
+            sEP[(g & 1) ? NW * c + wave : NW * C + lane] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+            Oh[ct] = OT[0];
           }
         }
       }
@@ -1279,6 +1371,17 @@ void prefill_kernel(PrefillArgs a) {
     __syncthreads();
   }
 
+  if constexpr (EPI != EPI_O) {
+    // the back end of the last chunk (its shares are in LDS since the loop's
+    // last barrier)
+    if (n_chunks > 0) {
+      const int lane = tid % 64, g = lane >> 4, l16 = lane & 15;
+      const int64_t tl = item.tok_begin + (int64_t)(n_chunks - 1) * C;
+      const int nl = item.n_tokens - (n_chunks - 1) * C;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) epi_tile(ct, tl * HD + (int64_t)h * D + 16 * wave + 4 * g, nl, g, l16);
+    }
+  }
   // end of the item: the final state (OUT, last segment of the sequence) or the
   // segment's map (MAP: N rows from the first SPW slices, M rows from the rest)
   if constexpr (!MAP) {
@@ -1827,11 +1930,6 @@ struct LdsPipe {
   static constexpr int OFF_G = OFF_NW + D * 4;
   static constexpr int TOTAL_EPI = OFF_G + C * LDG;
 };
-
-// What pass 3 writes per token: o (fp32), or the layer output after the
-// fused back end in bf16 or fp32
-enum { EPI_O = 0, EPI_BF16 = 1, EPI_F32 = 2 };
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int D, int EPI>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -2543,16 +2641,17 @@ __global__ __launch_bounds__(1024) void build_items_kernel(PrefillArgs a) {
   }
 }
 
-template <int D, bool BF16, bool PK, bool MAP, bool WU>
+template <int D, bool BF16, bool PK, bool MAP, bool WU, int EPI = EPI_O>
 hipError_t launch_pass(const PrefillArgs& a, hipStream_t s) {
   using L = Lds<D>;
-  static_assert(L::TOTAL <= 160 * 1024, "LDS budget");
+  constexpr int lds = EPI == EPI_O ? L::TOTAL : L::TOTAL_EPI;
+  static_assert(lds <= 160 * 1024, "LDS budget");
   constexpr int NT = 64 * waves_for<D>();
-  auto kern = prefill_kernel<D, BF16, PK, MAP, WU, waves_for<D>()>;
+  auto kern = prefill_kernel<D, BF16, PK, MAP, WU, waves_for<D>(), EPI>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, L::TOTAL);
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(a.n_items * a.H), dim3(NT), L::TOTAL, s, a);
+  hipLaunchKernelGGL(kern, dim3(a.n_items * a.H), dim3(NT), lds, s, a);
   return hipGetLastError();
 }
 
@@ -2604,9 +2703,13 @@ hipError_t launch_t(const PrefillArgs& a, hipStream_t s) {
     if (a.out == nullptr) e = launch_wu_pipe<D, EPI_O>(a, s);
     else if (a.out_bf16) e = launch_wu_pipe<D, EPI_BF16>(a, s);
     else e = launch_wu_pipe<D, EPI_F32>(a, s);
-  } else {
-    if (a.out != nullptr) return hipErrorInvalidValue;          // the fused back end has this form only
+  } else if (a.out == nullptr) {
     e = launch_pass<D, BF16, PK, false, true>(a, s);
+  } else if constexpr (D == 64 && BF16 && PK) {                 // the KDA layer's form
+    e = a.out_bf16 ? launch_pass<D, BF16, PK, false, true, EPI_BF16>(a, s)
+                   : launch_pass<D, BF16, PK, false, true, EPI_F32>(a, s);
+  } else {
+    return hipErrorInvalidValue;                                  // no fused back end in this form
   }
   if (e != hipSuccess || !a.any_whole) return e;
   return launch_pass<D, BF16, PK, false, false>(a, s);          // sequences that are not split

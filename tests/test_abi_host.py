@@ -326,12 +326,17 @@ def test_layer_prefill_plan_and_host_rejections(K):
     pk = K.make_shape(2, 64, 64, torch.bfloat16, True)
     cu = torch.tensor([0, 1100, 1100, 1741], dtype=torch.int64)     # an empty sequence in the pack
     T, H, d = 1741, 2, 128
-    # fused form (every non-empty sequence split): the prefill's plan and a 256-byte sink
-    pre = K.kda_prefill_workspace_size(sc, cu, 64, 0, 256)
-    lay = K.kda_layer_prefill_workspace_size(sc, cu, 64, 0, 256)
-    assert pre < lay <= (pre + 255) // 256 * 256 + 256
-    # composed form (unsegmented, or a sequence that stays whole): an fp32 o in the workspace
-    for shape, c, seg in ((sc, cu, 0), (sc, torch.tensor([0, 1100, 1200], dtype=torch.int64), 256), (pk, cu, 256)):
+    # fused forms (scalar gate at d = 128, per-key gate at d = 64, bf16, every
+    # non-empty sequence split): the prefill's plan and a 256-byte sink
+    for shape in (sc, pk):
+        pre = K.kda_prefill_workspace_size(shape, cu, 64, 0, 256)
+        lay = K.kda_layer_prefill_workspace_size(shape, cu, 64, 0, 256)
+        assert pre < lay <= (pre + 255) // 256 * 256 + 256
+    # composed form (unsegmented, a sequence that stays whole, another form):
+    # an fp32 o in the workspace
+    pk128 = K.make_shape(2, 128, 128, torch.bfloat16, True)
+    for shape, c, seg in ((sc, cu, 0), (sc, torch.tensor([0, 1100, 1200], dtype=torch.int64), 256), (pk, cu, 0),
+                          (pk128, cu, 256)):
         pre = K.kda_prefill_workspace_size(shape, c, 64, 0, seg)
         t, dd = int(c[-1]), shape.d_v
         assert K.kda_layer_prefill_workspace_size(shape, c, 64, 0, seg) >= pre + t * H * dd * 4

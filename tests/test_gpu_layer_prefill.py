@@ -2,10 +2,11 @@
 in one call) through the C ABI.
 
 Against kda_prefill_chunked followed by kda_layer_back with the gate logits
-widened to fp32: bit for bit, in the fused form (scalar gate, bf16, d = 128,
-every sequence split: the back end runs on each chunk's output tile on chip
-and forms the row sums of squares in the back-end kernel's order) and in the
-composed one (every other shape and plan). Against the fp64 oracle (token
+widened to fp32: bit for bit, in the fused forms (bf16 inputs with the scalar
+gate at d = 128 or the per-key gate at d = 64, every sequence split: the back
+end runs on each chunk's output tile on chip and forms the row sums of
+squares in the back-end kernel's order) and in the composed one (every other
+shape and plan). Against the fp64 oracle (token
 recurrence of oracle/kda_oracle.c, back end of oracle/layer.py): max error over
 a (sequence, head) slice relative to that slice's max |reference|, 5e-3 for
 bf16 out (the recurrence's 2e-3, which RMSNorm rescales per token, and one
@@ -48,7 +49,7 @@ def _fused(inp, g, norm_w, interval, seg, out_dtype):
 
 def _fused_form(w, seg):
     """Whether kda_layer_prefill takes the fused form for this workload."""
-    if not (w.dk == 128 and w.dv == 128 and w.dtype == "bf16" and w.gate == "scalar"):
+    if w.dtype != "bf16" or w.dk != w.dv or (w.dk, w.gate) not in ((128, "scalar"), (64, "per_key")):
         return False
     if seg == 0:
         return False
@@ -66,10 +67,13 @@ CASES = [
     ("fused_pack", dict(H=2, d=128, lens=(1100, 0, 641, 300), dtype="bf16", gate="scalar"), 256, 128, True),
     # fused, automatic plan on one sequence
     ("fused_auto", dict(H=2, d=128, lens=(4096 + 33,), dtype="bf16", gate="scalar"), -1, 0, True),
+    # fused, the KDA layer's form (per-key gate, d = 64)
+    ("fused_pk64", dict(H=2, d=64, lens=(1100, 0, 641, 300), dtype="bf16", gate="per_key"), 256, 128, True),
     # composed: a sequence stays whole
     ("mixed", dict(H=2, d=128, lens=(1100, 100), dtype="bf16", gate="scalar"), 256, 0, False),
-    # composed: unsegmented plan, per-key gate, fp32 inputs, d = 64
+    # composed: unsegmented plans, per-key gate at d = 128, fp32 inputs
     ("unsegmented", dict(H=3, d=128, lens=(700, 65), dtype="bf16", gate="scalar"), 0, 64, False),
+    ("per_key_d128", dict(H=2, d=128, lens=(700, 300), dtype="bf16", gate="per_key"), 256, 0, False),
     ("per_key_d64", dict(H=2, d=64, lens=(150, 7, 64), dtype="bf16", gate="per_key"), -1, 64, False),
     ("fp32_d64", dict(H=2, d=64, lens=(300,), dtype="fp32"), 128, 0, False),
 ]
@@ -117,8 +121,10 @@ def _rel_slices(y, ref, cu):
     return worst
 
 
-@pytest.mark.parametrize("name,kw,seg", [("fused_pack", CASES[0][1], 256), ("per_key_d64", CASES[4][1], -1)],
-                         ids=["fused", "composed"])
+@pytest.mark.parametrize("name,kw,seg", [("fused_pack", CASES[0][1], 256), ("fused_pk64", CASES[2][1], 256),
+                                         ("per_key_d64", dict(H=2, d=64, lens=(150, 7, 64), dtype="bf16",
+                                                              gate="per_key"), -1)],
+                         ids=["fused", "fused_pk64", "composed"])
 def test_layer_prefill_matches_oracle(name, kw, seg):
     w = custom(f"lp_{name}", s0_std=0.02, seed=61, **kw)
     inp, g, norm_w = _inputs(w, 62)
@@ -148,4 +154,22 @@ def test_layer_prefill_long_prefill_shape():
     ref = _oracle_out(inp, g, norm_w, heads)
     err = _rel_slices(y[:, heads].float().cpu().numpy().astype(np.float64), ref, inp["cu_seqlens_host"].numpy())
     print(f"long prefill: out vs oracle (heads {heads}) {err:.3e}", flush=True)
+    assert err <= 5e-3
+
+
+def test_layer_prefill_kda_layer_shape():
+    """The KDA-layer workload (T = 8192, H = 14, d = 64, per-key gate, bf16)
+    with the automatic plan (the fused form): out equal bit for bit to the
+    separate calls and within tolerance of the oracle, every head."""
+    w = wl.KDA_LAYER
+    assert _fused_form(w, -1)
+    inp, g, norm_w = _inputs(w, 64)
+    y, fin, _ = _fused(inp, g, norm_w, 0, -1, torch.bfloat16)
+    y_ref, fin_ref, _ = _separate(inp, g, norm_w, 0, -1, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref)
+    assert torch.equal(fin, fin_ref)
+    ref = _oracle_out(inp, g, norm_w)
+    err = _rel_slices(y.float().cpu().numpy().astype(np.float64), ref, inp["cu_seqlens_host"].numpy())
+    print(f"KDA layer shape: out vs oracle {err:.3e}", flush=True)
     assert err <= 5e-3
