@@ -709,8 +709,8 @@ void prefill_kernel(PrefillArgs a) {
   // go to the sink): out = o rsqrt(mean o^2 + eps) norm_w sigmoid(g). The
   // shares combine pairwise in wavefront order, the order in which the
   // separate back-end kernel's xor shuffles combine its lanes (same bits).
-  [[maybe_unused]] f32x4 Oh[EPI != EPI_O ? 4 : 1];
-  [[maybe_unused]] u32x2 gh[EPI != EPI_O ? 4 : 1];
+  [[maybe_unused]] f32x4 Oh[EPI != EPI_O ? 4 : 1] = {};   // (the first chunk's back end reads them:
+  [[maybe_unused]] u32x2 gh[EPI != EPI_O ? 4 : 1] = {};   // its stores go to the sink)
   [[maybe_unused]] auto epi_tile = [&](int ct, int64_t eb, int n_, int g_, int l16_) __attribute__((always_inline)) {
     const int c = 16 * ct + l16_;
     float ss;
@@ -2184,7 +2184,8 @@ void prefill_wu_pipe_kernel(PrefillArgs a) {
     // fused back end: the chunk's O tiles, held from interval B into the next
     // interval A, where every chain wavefront's share of each row's sum of
     // squares is in LDS and the back end runs between that interval's products
-    [[maybe_unused]] f32x4 Oh[EPI != EPI_O ? 4 : 1][SPW];
+    [[maybe_unused]] f32x4 Oh[EPI != EPI_O ? 4 : 1][SPW] = {};   // (read by the first chunk's back end,
+                                                                 // whose rows go to the sink)
     // fused back end of one 16-token tile ct of a chunk whose outputs start at
     // element eb and hold n tokens: out = o rsqrt(mean o^2 + eps) norm_w sigmoid(g)
     [[maybe_unused]] auto epi_tile = [&](int ct, int64_t eb, int n) __attribute__((always_inline)) {
