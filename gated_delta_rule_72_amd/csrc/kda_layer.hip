@@ -95,12 +95,49 @@ constexpr int64_t kFrontLongRows = 32768;       // token rows from which a workg
 // Front end. The token rows are [T, H*D]; a lane owns one group of 8
 // consecutive channels, so one wavefront load reads 64 x 8 channels of a row
 // in one contiguous piece (1 KB in bf16). A workgroup covers one block of 64
-// channel groups for TPT consecutive tokens with four wavefronts: q, k and v
-// convolutions and the gates. Each issues all its loads (its TPT rows, the 3
-// rows before them and its taps) before its first store, so no wait on a load
-// also waits on its own stores, and forms the 4-tap convolution in registers.
-// The CG lanes of one (token, head) are an aligned lane group (H*CG groups per
-// row, CG | 64), which the L2 norm reduces with shuffles.
+// channel groups for TPT consecutive tokens: one wavefront each for the q, k
+// and v convolutions, and for the per-key gate (a [T, H, d] tensor in and
+// out, as heavy as a convolution) a fourth one for the gates; the scalar
+// gates (two values per token and head) are formed by the v wavefront after
+// its stores, so every resident wavefront of a scalar-gate launch streams rows.
+// Each wavefront issues all its loads (its TPT rows, the 3 rows before them
+// and its taps) before its first store, so no wait on a load also waits on its
+// own stores, and forms the 4-tap convolution in registers. The CG lanes of one
+// (token, head) are an aligned lane group (H*CG groups per row, CG | 64), which
+// the L2 norm reduces with shuffles.
+template <bool PER_KEY, int TPT>
+struct FrontGates {
+  float al[TPT][PER_KEY ? 8 : 1], bl[TPT];
+  __device__ __forceinline__ void load(const LayerFrontArgs& a, int64_t tfirst, int64_t HD, int64_t ch0, int h) {
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      const int64_t t = tfirst + i < a.T ? tfirst + i : a.T - 1;
+      if constexpr (PER_KEY) load8<false>(a.alpha_logit, t * HD + ch0, al[i]);
+      else al[i][0] = a.alpha_logit[t * a.H + h];
+      bl[i] = a.beta_logit[t * a.H + h];
+    }
+  }
+  __device__ __forceinline__ void store(const LayerFrontArgs& a, int64_t tfirst, int64_t HD, int64_t ch0, int h,
+                                        bool live, bool lead) {
+#pragma unroll
+    for (int i = 0; i < TPT; ++i) {
+      const int64_t t = tfirst + i;
+      if (t >= a.T) break;
+      if constexpr (PER_KEY) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) al[i][e] = sigmoid_rcp(al[i][e] + a.alpha_bias);
+        if (live) store8<false>(a.alpha, t * HD + ch0, al[i]);
+      } else {
+        if (lead) a.alpha[t * a.H + h] = sigmoid_rcp(al[i][0] + a.alpha_bias);
+      }
+      if (lead) a.beta[t * a.H + h] = sigmoid_rcp(bl[i]);
+    }
+  }
+};
+
+template <bool PER_KEY>
+constexpr int front_waves() { return PER_KEY ? 4 : 3; }
+
 template <int D, bool BF16, bool PER_KEY, int TPT>
 __global__ __launch_bounds__(256) void layer_front_kernel(LayerFrontArgs a, int32_t n_cblocks) {
   constexpr int CG = D / 8;
@@ -117,30 +154,12 @@ __global__ __launch_bounds__(256) void layer_front_kernel(LayerFrontArgs a, int3
   const int h = g / CG;
   const int64_t HD = (int64_t)a.H * D;
   const int64_t ch0 = (int64_t)g * 8;            // = h*D + 8*(g % CG)
+  const bool lead = live && (g % CG) == 0;       // one lane per (token, head)
 
-  if (j == 3) {                                  // gates
-    const bool lead = live && (g % CG) == 0;     // one lane per (token, head)
-    float al[TPT][PER_KEY ? 8 : 1], bl[TPT];
-#pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      const int64_t t = tfirst + i < a.T ? tfirst + i : a.T - 1;
-      if constexpr (PER_KEY) load8<false>(a.alpha_logit, t * HD + ch0, al[i]);
-      else al[i][0] = a.alpha_logit[t * a.H + h];
-      bl[i] = a.beta_logit[t * a.H + h];
-    }
-#pragma unroll
-    for (int i = 0; i < TPT; ++i) {
-      const int64_t t = tfirst + i;
-      if (t >= a.T) break;
-      if constexpr (PER_KEY) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) al[i][e] = sigmoid_rcp(al[i][e] + a.alpha_bias);
-        if (live) store8<false>(a.alpha, t * HD + ch0, al[i]);
-      } else {
-        if (lead) a.alpha[t * a.H + h] = sigmoid_rcp(al[i][0] + a.alpha_bias);
-      }
-      if (lead) a.beta[t * a.H + h] = sigmoid_rcp(bl[i]);
-    }
+  FrontGates<PER_KEY, TPT> gates;
+  if (PER_KEY && j == 3) {                       // gates
+    gates.load(a, tfirst, HD, ch0, h);
+    gates.store(a, tfirst, HD, ch0, h, live, lead);
     return;
   }
 
@@ -158,6 +177,7 @@ __global__ __launch_bounds__(256) void layer_front_kernel(LayerFrontArgs a, int3
       else zero_raw<BF16>(win[r]);
     }
   }
+  if (!PER_KEY && j == 2) gates.load(a, tfirst, HD, ch0, h);   // before any store of this wavefront
   f32x4 w[8];                                    // taps of the lane's 8 channels, oldest first
 #pragma unroll
   for (int e = 0; e < 8; ++e) w[e] = *reinterpret_cast<const f32x4*>(a.conv_w + ((int64_t)j * HD + ch0 + e) * 4);
@@ -226,6 +246,7 @@ __global__ __launch_bounds__(256) void layer_front_kernel(LayerFrontArgs a, int3
     }
     if (live && t < a.T) store8<BF16>(y_out, t * HD + ch0, y);
   }
+  if (!PER_KEY && j == 2) gates.store(a, tfirst, HD, ch0, h, live, lead);
 }
 
 // Carried convolution state after each sequence: its last 3 inputs, oldest
@@ -290,8 +311,8 @@ hipError_t front_t(const LayerFrontArgs& a, hipStream_t s) {
   if (a.T > 0) {
     const int32_t n_cblocks = (a.H * (D / 8) + kGroupsPerBlock - 1) / kGroupsPerBlock;
     const int64_t tiles = (a.T + TPT - 1) / TPT;
-    hipLaunchKernelGGL((layer_front_kernel<D, BF16, PK, TPT>), dim3((unsigned)(tiles * n_cblocks)), dim3(256), 0, s,
-                       a, n_cblocks);
+    hipLaunchKernelGGL((layer_front_kernel<D, BF16, PK, TPT>), dim3((unsigned)(tiles * n_cblocks)),
+                       dim3(64 * front_waves<PK>()), 0, s, a, n_cblocks);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
