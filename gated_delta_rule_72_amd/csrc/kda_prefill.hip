@@ -349,9 +349,11 @@ struct ChunkRegs {
 // h is the value head (v, o and the state); q, k, alpha and beta belong to head
 // h >> qk_shift of a.H >> qk_shift (qk_shift = 1: d_v = 2 d_k, each head's state
 // rows split into two value heads of d_k rows that share q, k and the gates).
+//
+// Rows (v; fp32 q and k) of one chunk into registers.
 template <int D, bool BF16, bool PER_KEY, int NT>
-__device__ __forceinline__ void load_chunk(ChunkRegs<D, BF16, PER_KEY, NT>& R, const PrefillArgs& a,
-                                           int64_t tok0, int n, int h, int tid, bool load_v) {
+__device__ __forceinline__ void load_chunk_rows(ChunkRegs<D, BF16, PER_KEY, NT>& R, const PrefillArgs& a,
+                                                int64_t tok0, int n, int h, int tid, bool load_v) {
   // Every load is unconditional: rows and tokens past the chunk's n (>= 1)
   // read row n - 1 again, and their values are masked where they are used
   // (unpack_masked, the decay scan, beta). A load under a lane mask, or a
@@ -378,6 +380,16 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<D, BF16, PER_KEY, NT>& R, c
       if (load_v) R.v[j] = load_group<false>(static_cast<const float*>(a.v) + row0, off);
     }
   }
+}
+// alpha and beta of one chunk into registers (unconditional, as above).
+template <int D, bool BF16, bool PER_KEY, int NT>
+__device__ __forceinline__ void load_chunk_gates(ChunkRegs<D, BF16, PER_KEY, NT>& R, const PrefillArgs& a,
+                                                 int64_t tok0, int n, int h, int tid) {
+  using CR = ChunkRegs<D, BF16, PER_KEY, NT>;
+  const int Hq = a.H >> a.qk_shift, hq = h >> a.qk_shift;
+  const uint32_t HDq = (uint32_t)Hq * D;
+  const int64_t rowq0 = (tok0 * Hq + hq) * D;
+  const int last = n - 1;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
   if constexpr (PER_KEY) {
     const int kcol = tid % D, cb = tid / D;
@@ -390,6 +402,13 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<D, BF16, PER_KEY, NT>& R, c
     R.alpha[0] = wave == 0 ? a.alpha[(tok0 + min(lane, last)) * Hq + hq] : 1.f;
   }
   R.beta = wave == 0 ? a.beta[(tok0 + min(lane, last)) * Hq + hq] : 0.f;
+}
+// Both parts of a chunk's register inputs.
+template <int D, bool BF16, bool PER_KEY, int NT>
+__device__ __forceinline__ void load_chunk(ChunkRegs<D, BF16, PER_KEY, NT>& R, const PrefillArgs& a,
+                                           int64_t tok0, int n, int h, int tid, bool load_v) {
+  load_chunk_rows<D, BF16, PER_KEY, NT>(R, a, tok0, n, h, tid, load_v);
+  load_chunk_gates<D, BF16, PER_KEY, NT>(R, a, tok0, n, h, tid);
 }
 
 // Gram tile pairs (R, I), R >= I, as runs of one row block per wavefront:
@@ -835,6 +854,14 @@ void prefill_kernel(PrefillArgs a) {
     }
     if (wave == 0) sBeta[lane] = lane < n ? regs.beta : 0.f;
     __syncthreads();
+    // The next chunk's register inputs are fetched as soon as this chunk's
+    // are consumed (gates here, rows after P4), so their loads spread over the
+    // chunk instead of queueing behind each other before P6. The fetches are
+    // unconditional: the last chunk fetches itself again.
+    const int ch_next = min(ch + 1, n_chunks - 1);
+    const int64_t tok_next = item.tok_begin + (int64_t)ch_next * C;
+    const int n_next = min(C, item.n_tokens - ch_next * C);
+    load_chunk_gates<D, BF16, PER_KEY, NT>(regs, a, tok_next, n_next, h, tid);
     if constexpr (PER_KEY) {
       const int kcol = tid % D, cb = tid / D;
       float pre = 0.f;
@@ -1139,6 +1166,7 @@ void prefill_kernel(PrefillArgs a) {
         }
       }
       __syncthreads();
+      load_chunk_rows<D, BF16, PER_KEY, NT>(regs, a, tok_next, n_next, h, tid, v_in_regs);
 
       // ---- P5: W = T~ (K * 2^G), U' = T~ V --------------------------------------
       // W[:, 16kt..16kt+15] for kt = wave, wave + NW, ... and U' = T~ V for the
@@ -1215,9 +1243,8 @@ void prefill_kernel(PrefillArgs a) {
 
     // prefetch the next chunk's raw inputs while the chain runs (bf16 q, k go
     // to the raw K/Q region, which P6 does not read)
+    if constexpr (WU) load_chunk_rows<D, BF16, PER_KEY, NT>(regs, a, tok_next, n_next, h, tid, v_in_regs);
     if (ch + 1 < n_chunks) {
-      const int n_next = min(C, item.n_tokens - (ch + 1) * C);
-      load_chunk<D, BF16, PER_KEY, NT>(regs, a, tok0 + C, n_next, h, tid, v_in_regs);
       if constexpr (BF16) {
         const int64_t row0 = ((tok0 + C) * a.H + h) * D;
         const int64_t rowq0 = ((tok0 + C) * Hq + hq) * D;
