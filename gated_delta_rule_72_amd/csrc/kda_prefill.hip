@@ -1486,8 +1486,8 @@ __device__ __forceinline__ f16x8 bf16x8_to_f16(bf16x8 x, const float (&scale)[8]
 //      the Gram tiles of c+1 and their inversions
 //   B: producers: c+1's v rows into LDS, the inverse T~ of c+1; the M step
 //      (chunk c)
-//   C: producers: W and U' of c+1, c+2's k rows into LDS, the decay scan of
-//      c+2 (producer 0)
+//   C: producers: W and U' of c+1, c+2's k rows into LDS; chain wavefront 0:
+//      the decay scan of c+2 (the chain is otherwise idle in B and C)
 // The raw k rows are double-buffered: chunk c+2's wait in registers until
 // interval C, when the chain and the M step are done with chunk c's buffer.
 // The small arrays are triple-buffered, W double-buffered. The raw rows travel
@@ -1577,8 +1577,8 @@ void prefill_map_chain_kernel(PrefillArgs a) {
 #pragma unroll
     for (int j = 0; j < RI; ++j) *reinterpret_cast<i32x4*>(dst + 1024 * (pw + NP * j) + 16 * lane) = carry[j];
   };
-  // alpha and beta of token `lane` of a later chunk (every producer loads
-  // them, producer 0 scans them)
+  // alpha and beta of token `lane` of a later chunk (every wavefront of the
+  // role that scans them loads them)
   float pre_alpha = 1.f, pre_beta = 0.f;
   auto fetch_ab = [&](int ch) __attribute__((always_inline)) {
     const int64_t t = (item.tok_begin + (int64_t)ch * C + min(lane, chunk_len(ch) - 1)) * a.H + h;
@@ -1588,9 +1588,10 @@ void prefill_map_chain_kernel(PrefillArgs a) {
   // the loaded alpha and beta are waited for here (p1 can then follow record
   // stores without waiting for them)
   auto land_ab = [&]() __attribute__((always_inline)) { asm volatile("" : "+v"(pre_alpha), "+v"(pre_beta)); };
-  // P1: cumulative log2 decay of chunk ch (producer 0)
-  auto p1 = [&](int ch) __attribute__((always_inline)) {
-    if (pw == 0) {
+  // P1: cumulative log2 decay of chunk ch (by the wavefront with `mine` set:
+  // producer 0 in the prologue, chain wavefront 0 in the loop)
+  auto p1 = [&](int ch, bool mine) __attribute__((always_inline)) {
+    if (mine) {
       const int n = chunk_len(ch);
       float* sm = sSm(ch);
       const float gcum = wave_inclusive_scan(log2_hw(lane < n ? pre_alpha : 1.f), lane);
@@ -1835,9 +1836,12 @@ void prefill_map_chain_kernel(PrefillArgs a) {
       refresh();
       ustep(ch, SN);                             // interval A
       update(ch, true, SN);
+      fetch_ab(min(ch + 2, n_chunks - 1));       // for the decay scan of chunk ch+2
       __syncthreads();
       __syncthreads();                           // interval B
-      __syncthreads();                           // interval C
+      land_ab();                                 // interval C: the decay scan of ch+2
+      if (ch + 2 < n_chunks) p1(ch + 2, wave == 0);   // (small arrays of chunk ch-1)
+      __syncthreads();
     }
     refresh();
 #pragma unroll
@@ -1865,7 +1869,7 @@ void prefill_map_chain_kernel(PrefillArgs a) {
   fetch_ab(0);
   put_rows(rawK(0), carry_k);
   put_rows(rawV, carry_v);
-  p1(0);
+  p1(0, pw == 0);
   fetch_rows(a.k, min(1, last), carry_k);
   fetch_ab(min(1, last));
   __syncthreads();
@@ -1879,18 +1883,17 @@ void prefill_map_chain_kernel(PrefillArgs a) {
   __syncthreads();
   refresh();
   p5(0);
-  if (n_chunks > 1) p1(1);
+  if (n_chunks > 1) p1(1, pw == 0);
   __syncthreads();
 
   bool m_live = true;                            // this wavefront's M image is nonzero
   for (int ch = 0; ch < n_chunks; ++ch) {
-    const bool has_next = ch + 1 < n_chunks, has_next2 = ch + 2 < n_chunks;
+    const bool has_next = ch + 1 < n_chunks;
     refresh();
     // ---- interval A ---------------------------------------------------------
     fetch_rows(a.v, min(ch + 1, last), carry_v);
     if (has_next) p3(ch + 1);
     fetch_rows(a.k, min(ch + 2, last), carry_k); // (after P3: not live across it)
-    fetch_ab(min(ch + 2, last));
     __syncthreads();
     refresh();
     // ---- interval B ---------------------------------------------------------
@@ -1902,9 +1905,7 @@ void prefill_map_chain_kernel(PrefillArgs a) {
     refresh();
     // ---- interval C ---------------------------------------------------------
     put_rows(rawK(ch + 2), carry_k);             // k rows of chunk ch were read in intervals A and B
-    land_ab();
     if (has_next) p5(ch + 1);
-    if (has_next2) p1(ch + 2);                   // small arrays of chunk ch-1
     __syncthreads();
   }
   refresh();
