@@ -144,6 +144,8 @@ int device_cu_count() {
 struct PrefillPlan {
   int32_t seg_chunks, n_items;
   int32_t any_whole;   // segmented: some sequence is short enough to stay whole
+  int32_t one_seq;     // one sequence: the kernels form the work items themselves
+  int64_t one_tok0, one_len;
   int64_t whole_tokens;  // segmented: tokens of the sequences that stay whole
   size_t items_off, first_off, maps_off, states_off, wu_off, bytes;
 };
@@ -202,6 +204,11 @@ PrefillPlan plan_prefill(const kda_shape* s, int32_t num_seqs, const int64_t* cu
     }
   }
   p.n_items = (int32_t)items;
+  if (num_seqs == 1) {
+    p.one_seq = 1;
+    p.one_tok0 = cu[0];
+    p.one_len = cu[1] - cu[0];
+  }
   const size_t H = (size_t)s->num_heads, DD = (size_t)s->d_k * s->d_k;
   size_t off = 0;
   p.items_off = off;
@@ -525,6 +532,9 @@ int run_backward(const kda_shape* shape, int32_t num_seqs, const int64_t* cu_seq
   f.seg_states = plan.fwd.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.fwd.states_off) : nullptr;
   f.seg_wu = plan.fwd.seg_chunks > 0 ? static_cast<void*>(ws + plan.fwd.wu_off) : nullptr;
   f.any_whole = plan.fwd.any_whole;
+  f.one_seq = plan.fwd.one_seq;
+  f.one_tok0 = plan.fwd.one_tok0;
+  f.one_len = plan.fwd.one_len;
   hipError_t e = kda::launch_prefill(f, shape->d_k, bf16, pk, st);
   if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "backward: forward launch failed: %s", hipGetErrorString(e));
 
@@ -647,6 +657,9 @@ int kda_prefill_chunked(const kda_shape* shape, int32_t num_seqs,
   a.seg_states = plan.kern.seg_chunks > 0 ? reinterpret_cast<float*>(ws + plan.kern.states_off) : nullptr;
   a.seg_wu = plan.kern.seg_chunks > 0 ? static_cast<void*>(ws + plan.kern.wu_off) : nullptr;
   a.any_whole = plan.kern.any_whole;
+  a.one_seq = plan.kern.one_seq;
+  a.one_tok0 = plan.kern.one_tok0;
+  a.one_len = plan.kern.one_len;
   e = kda::launch_prefill(a, geo.d, shape->qkv_dtype == KDA_BF16, shape->gate == KDA_GATE_PER_KEY, st);
   if (e != hipSuccess) return fail(KDA_ERR_DEVICE, "prefill launch failed: %s", hipGetErrorString(e));
   if (geo.pad) {
@@ -936,6 +949,9 @@ int kda_layer_prefill(const kda_shape* shape, int32_t num_seqs,
   a.seg_states = reinterpret_cast<float*>(ws + kp.states_off);
   a.seg_wu = static_cast<void*>(ws + kp.wu_off);
   a.any_whole = kp.any_whole;
+  a.one_seq = kp.one_seq;
+  a.one_tok0 = kp.one_tok0;
+  a.one_len = kp.one_len;
   a.g_logit = g_logit;
   a.norm_w = norm_w;
   a.out = out;

@@ -98,6 +98,11 @@ struct PrefillArgs {
                              // LDS layout the map pass leaves it in) and U' (fp32, one
                              // accumulator tile per lane), reused by pass 3
   int32_t any_whole;         // segmented plan: some sequence is not split (needs its own pass)
+  // One sequence (num_seqs = 1): the kernels form each work item from its
+  // first token and length (segments of seg_chunks chunks, or the whole
+  // sequence) and no work table is built
+  int32_t one_seq;
+  int64_t one_tok0, one_len;
   int32_t qk_shift;          // 0, or 1 when d_v = 2 d_k: H counts value heads of d_k state rows,
                              // and value head h takes q, k, alpha, beta of head h >> 1 of H / 2
   // Layer back end fused into pass 3 (scalar gate, bf16, d = 128, every

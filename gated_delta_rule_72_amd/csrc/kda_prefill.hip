@@ -79,6 +79,24 @@ namespace {
 
 constexpr int C = 64;  // chunk length
 
+// Work item idx: from the table build_items_kernel writes, or, with one
+// sequence, formed here exactly as that kernel would (segments of seg_chunks
+// chunks, or the whole sequence).
+__device__ __forceinline__ PrefillItem work_item(const PrefillArgs& a, int idx) {
+  if (!a.one_seq) return a.items[idx];
+  const int64_t st = (int64_t)a.seg_chunks * C;
+  const bool split = st > 0 && a.one_len > st;
+  PrefillItem it;
+  it.n_segs = split ? (int32_t)((a.one_len + st - 1) / st) : 1;
+  it.tok_in_seq = split ? (int64_t)idx * st : 0;
+  it.tok_begin = a.one_tok0 + it.tok_in_seq;
+  it.n_tokens = (int32_t)(split ? min(st, a.one_len - it.tok_in_seq) : a.one_len);
+  it.snap_base = 0;
+  it.seq = 0;
+  it.seg = split ? idx : 0;
+  return it;
+}
+
 
 __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -632,7 +650,7 @@ void prefill_kernel(PrefillArgs a) {
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
   const int g = lane >> 4, l16 = lane & 15;
   const int item_idx = blockIdx.x / a.H, h = blockIdx.x % a.H;
-  const PrefillItem item = a.items[item_idx];
+  const PrefillItem item = work_item(a, item_idx);
   if constexpr (MAP || WU) {
     // every segment of a split sequence: the maps of all but the last feed the
     // scan, and each chunk's W and U' are kept for pass 3 (WU)
@@ -1544,7 +1562,7 @@ void prefill_map_chain_kernel(PrefillArgs a) {
     l16 = lane & 15;
   };
   const int item_idx = blockIdx.x / a.H, h = blockIdx.x % a.H;
-  const PrefillItem item = a.items[item_idx];
+  const PrefillItem item = work_item(a, item_idx);
   if (item.n_segs <= 1) return;                  // (uniform) whole sequences need no map
   constexpr int W_BYTES = (int)wu_w_bytes(D);
   static_assert(W_BYTES == C * L::LDQ * 2, "stored W layout");
@@ -1998,7 +2016,7 @@ void prefill_wu_pipe_kernel(PrefillArgs a) {
     ptid = tid - 64 * NC;
   };
   const int item_idx = blockIdx.x / a.H, h = blockIdx.x % a.H;
-  const PrefillItem item = a.items[item_idx];
+  const PrefillItem item = work_item(a, item_idx);
   if (item.n_segs <= 1) return;                  // (uniform) whole sequences run in the other pass
   constexpr int W_BYTES = (int)wu_w_bytes(D);
   static_assert(W_BYTES == C * L::LDQ * 2, "stored W layout");
@@ -2487,8 +2505,8 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(PrefillArgs a) {
   const int n = blockIdx.x / (a.H * nrb);
   const int rem = blockIdx.x % (a.H * nrb);
   const int h = rem / nrb, rb = rem % nrb;
-  const int first = a.seq_first_item[n];
-  const int ns = a.items[first].n_segs;
+  const int first = a.one_seq ? 0 : a.seq_first_item[n];
+  const int ns = work_item(a, first).n_segs;
   if (ns <= 1) return;
   const int64_t DD = (int64_t)D * D;
   const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64, g = lane >> 4, l16 = lane & 15;
@@ -2778,13 +2796,15 @@ hipError_t launch_copy_rows(const void* src, void* dst, int64_t n_rows, int64_t 
 }
 
 hipError_t launch_prefill(PrefillArgs a, int d, bool bf16, bool per_key, hipStream_t s) {
-  constexpr int items_lds = kSortMax * 16;       // snapshot bases and sort keys
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(build_items_kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, items_lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(build_items_kernel, dim3(1), dim3(1024), items_lds, s, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (!a.one_seq) {                              // (one sequence: the kernels form the items)
+    constexpr int items_lds = kSortMax * 16;     // snapshot bases and sort keys
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(build_items_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, items_lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(build_items_kernel, dim3(1), dim3(1024), items_lds, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (d == 64) {
     if (bf16) return per_key ? launch_t<64, true, true>(a, s) : launch_t<64, true, false>(a, s);
     return per_key ? launch_t<64, false, true>(a, s) : launch_t<64, false, false>(a, s);
