@@ -442,9 +442,10 @@ __device__ __forceinline__ void load_chunk(ChunkRegs<D, BF16, PER_KEY, NT>& R, c
 //                     inversion; w4: R3 I0-1 | w5: R3 I2, R2 I1 | w6: R2 I0 |
 //                     w7: R1 I0. Per-key gate (a pair costs more than an
 //                     inversion, and the pairs of a run share their row
-//                     operands): w0: R3 I0-1 | w1: R3 I2-3, inv 3 | w2: R2
-//                     I0-1 | w3: R2 I2, inv 2 | w4: R1 I0 | w5: R1 I1, inv 1 |
-//                     w6: R0 I0, inv 0 | w7: none
+//                     operands): w0: R3 I0-1 | w1: R3 I2-3, inv 3 | w2: R2 I0 |
+//                     w3: R2 I2, inv 2 | w4: R1 I0 | w5: R2 I1 | w6: R0 I0,
+//                     inv 0 | w7: R1 I1, inv 1 (per SIMD two row operands, at
+//                     most three pairs and one or two inversions)
 // Four 12-bit run codes in the 16-bit fields of one 64-bit constant (field w
 // for wavefront w): the lookup is register arithmetic, not a memory load.
 constexpr uint64_t pack_runs(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
@@ -463,9 +464,9 @@ __device__ __forceinline__ bool gram_run(int wave_lane, int run, int& R, int& I0
   } else {
     static_assert(NW == 8, "four or eight wavefronts");
     constexpr uint64_t kRun0Lo = !PER_KEY ? pack_runs(0x000, 0x111, 0x222, 0x333)    // wavefronts 0-3
-                                          : pack_runs(0x301, 0x323, 0x201, 0x222);
+                                          : pack_runs(0x301, 0x323, 0x200, 0x222);
     constexpr uint64_t kRun0Hi = !PER_KEY ? pack_runs(0x301, 0x322, 0x200, 0x100)    // wavefronts 4-7
-                                          : pack_runs(0x100, 0x111, 0x000, 0xFFF);
+                                          : pack_runs(0x100, 0x211, 0x000, 0x111);
     constexpr uint64_t kRun1Lo = pack_runs(0xFFF, 0xFFF, 0xFFF, 0xFFF);
     constexpr uint64_t kRun1Hi = !PER_KEY ? pack_runs(0xFFF, 0x211, 0xFFF, 0xFFF)
                                           : pack_runs(0xFFF, 0xFFF, 0xFFF, 0xFFF);
@@ -489,7 +490,7 @@ __device__ __forceinline__ bool gram_diag(int wave, int& d0, int& d1) {
     return false;
   } else if constexpr (PER_KEY) {
     // the wavefront whose run ends on the diagonal pair (b, b) inverts block b
-    const int b = wave == 6 ? 0 : wave == 5 ? 1 : wave == 3 ? 2 : wave == 1 ? 3 : -1;
+    const int b = wave == 6 ? 0 : wave == 7 ? 1 : wave == 3 ? 2 : wave == 1 ? 3 : -1;
     d0 = d1 = b;
     return b >= 0;
   } else {
