@@ -720,6 +720,21 @@ void prefill_kernel(PrefillArgs a) {
   if constexpr (EPI != EPI_O)
     for (int e = tid; e < D; e += NT) sENw[e] = a.norm_w[e];    // read after the barriers below
   CR regs;
+  // Per-key gate: the local part of a chunk's decay scan (thread: channel
+  // tid % D, tokens TPB cb .. TPB cb + TPB-1) runs before the chunk starts
+  // (for chunk c + 1 at the end of chunk c, on its prefetched alpha), with
+  // the block totals in sPart, so P1 combines them behind one barrier.
+  float gloc[PER_KEY ? CR::TPB : 1];
+  [[maybe_unused]] auto local_scan = [&](int n_) __attribute__((always_inline)) {
+    const int kcol = tid % D, cb = tid / D;
+    float run = 0.f;
+#pragma unroll
+    for (int j = 0; j < CR::TPB; ++j) {
+      run += log2_hw(CR::TPB * cb + j < n_ ? regs.alpha[j] : 1.f);
+      gloc[j] = run;
+    }
+    sPart[cb * D + kcol] = run;
+  };
   if (n_chunks > 0) {
     load_chunk<D, BF16, PER_KEY, NT>(regs, a, item.tok_begin, min(C, item.n_tokens), h, tid, v_in_regs);
     if constexpr (BF16) {
@@ -734,10 +749,9 @@ void prefill_kernel(PrefillArgs a) {
         stage_rows_lds_swz<D, NW>(static_cast<const uint16_t*>(a.q) + rowq0, HDqu, min(C, item.n_tokens),
                                   regA + L::A_RQ, wave, lane);
     }
-    if constexpr (BF16) {
-      __builtin_amdgcn_s_waitcnt(0);   // staged rows have landed in LDS
-      __syncthreads();
-    }
+    if constexpr (PER_KEY) local_scan(min(C, item.n_tokens));
+    if constexpr (BF16) __builtin_amdgcn_s_waitcnt(0);   // staged rows have landed in LDS
+    __syncthreads();
   }
 
   // Fused back end (pass 3 of the KDA layer): a chunk's O tiles and output-gate
@@ -846,18 +860,18 @@ void prefill_kernel(PrefillArgs a) {
         if constexpr (!MAP) *reinterpret_cast<f16x8*>(sRQ + c * L::LDQ + 8 * k8) = qh;
       }
     }
-    float gloc[PER_KEY ? CR::TPB : 1];
     if constexpr (PER_KEY) {
-      // thread: channel tid % D, tokens TPB cb .. TPB cb + TPB-1; local scan,
-      // then the block totals are combined through LDS.
+      // the local scans (gloc, sPart) ran before this chunk: combine the
+      // block totals of the earlier token blocks
       const int kcol = tid % D, cb = tid / D;
-      float run = 0.f;
+      float pre = 0.f;
+      for (int b = 0; b < cb; ++b) pre += sPart[b * D + kcol];
 #pragma unroll
-      for (int j = 0; j < CR::TPB; ++j) {
-        run += log2_hw(CR::TPB * cb + j < n ? regs.alpha[j] : 1.f);
-        gloc[j] = run;
+      for (int j = 0; j < CR::TPB; ++j) sG[(CR::TPB * cb + j) * L::LDG + kcol] = pre + gloc[j];
+      if (cb == NT / D - 1) {
+        sGL[kcol] = pre + gloc[CR::TPB - 1];
+        sGam[kcol] = exp2_hw(pre + gloc[CR::TPB - 1]);
       }
-      sPart[cb * D + kcol] = run;
     } else {
       if (wave == 0) {
         const float gcum = wave_inclusive_scan(log2_hw(lane < n ? regs.alpha[0] : 1.f), lane);
@@ -881,18 +895,6 @@ void prefill_kernel(PrefillArgs a) {
     const int64_t tok_next = item.tok_begin + (int64_t)ch_next * C;
     const int n_next = min(C, item.n_tokens - ch_next * C);
     load_chunk_gates<D, BF16, PER_KEY, NT>(regs, a, tok_next, n_next, h, tid);
-    if constexpr (PER_KEY) {
-      const int kcol = tid % D, cb = tid / D;
-      float pre = 0.f;
-      for (int b = 0; b < cb; ++b) pre += sPart[b * D + kcol];
-#pragma unroll
-      for (int j = 0; j < CR::TPB; ++j) sG[(CR::TPB * cb + j) * L::LDG + kcol] = pre + gloc[j];
-      if (cb == NT / D - 1) {
-        sGL[kcol] = pre + gloc[CR::TPB - 1];
-        sGam[kcol] = exp2_hw(pre + gloc[CR::TPB - 1]);
-      }
-      __syncthreads();
-    }
 
     // ---- P2: decayed operands ------------------------------------------------
 #pragma unroll
@@ -1413,6 +1415,7 @@ void prefill_kernel(PrefillArgs a) {
             *reinterpret_cast<f32x4*>(dst + (16 * (SPW * wave + sl) + l16) * D + 16 * kt + 4 * g) = ST[sl][kt];
       }
     }
+    if constexpr (PER_KEY) local_scan(n_next);     // the next chunk's (P1 of this one read sPart)
     if constexpr (BF16) __builtin_amdgcn_s_waitcnt(0);   // staged rows have landed in LDS
     __syncthreads();
   }
