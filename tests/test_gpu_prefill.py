@@ -105,11 +105,15 @@ def test_run_twice_bitwise_deterministic():
         assert torch.equal(x, y)
 
 
+@pytest.mark.parametrize("d,gate", [(64, "per_key"), (128, "scalar")])
 @pytest.mark.parametrize("segment_tokens", [0, 128])
-def test_packed_equals_solo_bitwise(segment_tokens):
-    """With a fixed segment plan a sequence's results do not depend on the pack."""
+def test_packed_equals_solo_bitwise(segment_tokens, d, gate):
+    """With a fixed segment plan a sequence's results do not depend on the pack.
+    A pack runs from the work table; a single sequence forms its work items in
+    the kernels, so this also checks that both give the same items (at d = 128
+    with the scalar gate, through the two-role map pass and output pass)."""
     dev = device()
-    w = custom("packing", H=2, d=64, lens=(300, 0, 65, 128, 700), gate="per_key", interval=64, seed=14)
+    w = custom(f"packing_{d}_{gate}", H=2, d=d, lens=(300, 0, 65, 128, 700), gate=gate, interval=64, seed=14)
     inp = wl.make_prefill_inputs(w, dev)
     o, fin, snaps = run_prefill(inp, w.interval, segment_tokens)
     cu = inp["cu_seqlens_host"].tolist()
