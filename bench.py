@@ -409,7 +409,7 @@ def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-tokens", type=int, default=262144,
                     help="token prefix the CPU oracle baseline runs on (0 = skip)")
     ap.add_argument("--skip-decode", action="store_true")
