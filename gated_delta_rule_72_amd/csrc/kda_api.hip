@@ -307,6 +307,7 @@ struct BackwardPlan {
   int64_t n_chunks, n_snap, n_items;
   int32_t seg_chunks;
   size_t o_off, fin_off, snap_off, cb_off, sb_off, ib_off, maps_off, ends_off, ws_off, bytes;
+  bool s0_in_place;   // one sequence: the forward's 64-token states land in the chunk-start array
 };
 
 BackwardPlan plan_backward(const kda_shape* s, int32_t num_seqs, const int64_t* cu, int cus) {
@@ -342,8 +343,12 @@ BackwardPlan plan_backward(const kda_shape* s, int32_t num_seqs, const int64_t* 
   off += round_up(T * H * D * sizeof(float));
   p.fin_off = off;
   off += round_up((size_t)num_seqs * H * D * D * sizeof(float));
+  // With one sequence, the state after 64 (j + 1) tokens is the start state
+  // of chunk j + 1, unit (j + 1) H + h of the backward's chunk-start array:
+  // the forward writes it there and needs no state slots of its own.
+  p.s0_in_place = num_seqs == 1;
   p.snap_off = off;
-  off += round_up((size_t)p.n_snap * H * D * D * sizeof(float));
+  if (!p.s0_in_place) off += round_up((size_t)p.n_snap * H * D * D * sizeof(float));
   p.cb_off = off;
   off += round_up(((size_t)num_seqs + 1) * sizeof(int64_t));
   p.sb_off = off;
@@ -519,7 +524,15 @@ int run_backward(const kda_shape* shape, int32_t num_seqs, const int64_t* cu_seq
   f.q = q; f.k = k; f.v = v; f.alpha = alpha; f.beta = beta; f.init = initial_state;
   f.o = reinterpret_cast<float*>(ws + plan.o_off);
   f.final_state = reinterpret_cast<float*>(ws + plan.fin_off);
-  f.snapshots = plan.n_snap > 0 ? reinterpret_cast<float*>(ws + plan.snap_off) : nullptr;
+  // (one sequence: straight into the chunk-start array from its unit H on; a
+  // state after the last token, when the length is a multiple of 64, lands
+  // on the first unit of the array after it, which the reverse scan writes
+  // before anything reads it)
+  float* s0_array = reinterpret_cast<float*>(ws + plan.ws_off) +
+                    kda::bwd::dd_off(kda::bwd::S0M, plan.n_chunks * shape->num_heads, shape->d_k);
+  f.snapshots = plan.n_snap <= 0 ? nullptr
+                : plan.s0_in_place ? s0_array + (int64_t)shape->num_heads * shape->d_k * shape->d_k
+                                   : reinterpret_cast<float*>(ws + plan.snap_off);
   f.cu_dev = cu_seqlens_dev;
   f.num_seqs = num_seqs;
   f.H = shape->num_heads;
@@ -547,7 +560,8 @@ int run_backward(const kda_shape* shape, int32_t num_seqs, const int64_t* cu_seq
   b.num_seqs = num_seqs;
   b.H = shape->num_heads;
   b.n_chunks = plan.n_chunks;
-  b.states = reinterpret_cast<const float*>(ws + plan.snap_off);
+  b.states = plan.s0_in_place ? nullptr : reinterpret_cast<const float*>(ws + plan.snap_off);
+  b.s0_in_place = plan.s0_in_place ? 1 : 0;
   b.chunk_base = reinterpret_cast<int64_t*>(ws + plan.cb_off);
   b.snap_base = reinterpret_cast<int64_t*>(ws + plan.sb_off);
   b.item_base = reinterpret_cast<int64_t*>(ws + plan.ib_off);

@@ -183,6 +183,7 @@ __global__ __launch_bounds__(256) void prep_kernel(BackwardArgs a) {
   if (p.c == 0) {
     if (a.init) src = a.init + ((int64_t)p.n * a.H + h) * D * D;
   } else {
+    if (a.s0_in_place) return;          // (uniform) the forward wrote it in place
     src = a.states + ((a.snap_base[p.n] + p.c - 1) * a.H + h) * D * D;
   }
   float* dst = ws + dd_off(S0M, units, D) + b * D * D;

@@ -189,6 +189,9 @@ struct BackwardArgs {
   int32_t num_seqs, H;
   int64_t n_chunks;          // chunks over all sequences
   const float* states;       // forward states after every 64 tokens, snapshot slot order
+  int32_t s0_in_place;       // one sequence: the forward wrote those states straight into
+                             // the chunk-start array (ws, S0M from its unit H on), so only a
+                             // sequence's first chunk takes its start state from init
   int64_t* chunk_base;       // workspace [N+1]: first chunk of each sequence
   int64_t* snap_base;        // workspace [N+1]: first 64-token state slot of each sequence
   int64_t* item_base;        // workspace [N+1]: first scan segment of each sequence
