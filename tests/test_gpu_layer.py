@@ -90,6 +90,50 @@ def test_front_without_state_and_state_handoff_bitwise():
         assert torch.equal(p2[5], full[5])
 
 
+@pytest.mark.parametrize("gate", ["scalar", "per_key"])
+def test_front_long_pack_matches_oracle(gate):
+    """A pack past 32768 rows, where a workgroup takes 8-token tiles:
+    sequence starts inside and at the edges of tiles, empty and one-token
+    sequences, and a ragged last tile."""
+    lens = (9000, 1, 0, 3, 17000, 2, 6813)       # T = 32819
+    w = custom(f"front_long_{gate}", H=2, d=64, lens=lens, gate=gate, seed=44)
+    li = wl.make_layer_inputs(w, device())
+    q, k, v, a, b, st = _front(li)
+    torch.cuda.synchronize()
+    cu = li["cu_seqlens_host"].numpy()
+    rq, rk, rv, ra, rb, rst = L.layer_front(_np(li["xq"]), _np(li["xk"]), _np(li["xv"]), _np(li["conv_w"]), cu,
+                                            _np(li["conv_state"]), _np(li["alpha_logit"]), 5.0,
+                                            _np(li["beta_logit"]))
+    for name, x, r in (("q", q, rq), ("k", k, rk), ("v", v, rv)):
+        err = _rel(_np_f(x), r, cu)
+        print(f"{name}: {err:.3e}", flush=True)
+        assert err <= 4e-3, (name, err)
+    assert np.max(np.abs(a.cpu().numpy() - ra)) <= 1e-5
+    assert np.max(np.abs(b.cpu().numpy() - rb)) <= 1e-5
+    assert np.array_equal(_np_f(st), rst)
+
+
+@pytest.mark.parametrize("gate", ["scalar", "per_key"])
+def test_front_long_path_equals_short_path_bitwise(gate):
+    """One sequence of 40013 rows takes the 8-token-tile launch; its two
+    halves, each under 32768 rows and joined by the carried state, take the
+    4-token-tile launch. Every output is the same bits."""
+    w = custom(f"front_split_{gate}", H=2, d=128, lens=(40013,), gate=gate, seed=45)
+    li = wl.make_layer_inputs(w, device())
+    full = _front(li)
+    T = 40013
+    for a in (20000, 8195):
+        part = lambda s, e, stt: kda.layer_front(  # noqa: E731
+            li["xq"][s:e].contiguous(), li["xk"][s:e].contiguous(), li["xv"][s:e].contiguous(), li["conv_w"],
+            li["alpha_logit"][s:e].contiguous(), li["beta_logit"][s:e].contiguous(), conv_state=stt)
+        p1 = part(0, a, li["conv_state"])
+        p2 = part(a, T, p1[5])
+        torch.cuda.synchronize()
+        for i in range(5):
+            assert torch.equal(torch.cat([p1[i], p2[i]]), full[i]), (a, i)
+        assert torch.equal(p2[5], full[5])
+
+
 def test_front_all_sequences_empty_passes_state_through():
     dev = device()
     H, d = 2, 64
