@@ -178,9 +178,31 @@ __global__ __launch_bounds__(256) void layer_front_kernel(LayerFrontArgs a, int3
     }
   }
   if (!PER_KEY && j == 2) gates.load(a, tfirst, HD, ch0, h);   // before any store of this wavefront
-  f32x4 w[8];                                    // taps of the lane's 8 channels, oldest first
+  // Taps of the lane's 8 channels, oldest first. The wavefront's 8 KB (16 B
+  // per channel) are read in whole 1 KB pieces and passed through LDS, where
+  // lane l's 8 pieces sit in 8 consecutive 16-byte slots permuted by l mod 8,
+  // so the 8 lanes of one read phase hit distinct banks. Only this wavefront
+  // touches its slots: no workgroup barrier.
+  f32x4 w[8];
+  {
+    __shared__ f32x4 tap_lds[3][kGroupsPerBlock * 8];
+    const float* tb = a.conv_w + ((int64_t)j * HD + (int64_t)cblock * (kGroupsPerBlock * 8)) * 4;
+    f32x4 pc[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) w[e] = *reinterpret_cast<const f32x4*>(a.conv_w + ((int64_t)j * HD + ch0 + e) * 4);
+    for (int e = 0; e < 8; ++e) {
+      const int u = e * 64 + lane;               // channel cblock*512 + u
+      if (cblock * kGroupsPerBlock + u / 8 < G) pc[e] = *reinterpret_cast<const f32x4*>(tb + u * 4);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int u = e * 64 + lane, l = u / 8;
+      if (cblock * kGroupsPerBlock + l < G) tap_lds[j][l * 8 + ((u % 8) ^ (l % 8))] = pc[e];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w[e] = tap_lds[j][lane * 8 + (e ^ (lane % 8))];
+  }
 
   // sequence of each token (wave-uniform, so scalar): last n with cu[n] <= t
   int seq[TPT];
