@@ -150,30 +150,46 @@ __global__ __launch_bounds__(256) void prep_kernel(BackwardArgs a) {
   __syncthreads();
   const int cref = ref_row(p.len);
   float* ws = a.ws;
-  for (int idx = tid; idx < C * D; idx += 256) {
-    const int r = idx / D, j = idx % D;
-    float qv = 0.f, kv = 0.f, vv = 0.f, dov = 0.f;
+  // four consecutive channels per thread: 8-byte bf16 (16-byte fp32) loads
+  // and 16-byte stores
+  for (int i4 = tid; i4 < C * D / 4; i4 += 256) {
+    const int idx = 4 * i4, r = idx / D, j = idx % D;
+    f32x4 qv = {0.f, 0.f, 0.f, 0.f}, kv = qv, vv = qv, dov = qv;
     if (r < p.len) {
       const int64_t e = ((p.t0 + r) * a.H + h) * D + j;
-      qv = load1<BF16>(a.q, e);
-      kv = load1<BF16>(a.k, e);
-      vv = load1<BF16>(a.v, e);
-      dov = a.d_o[e];
+      qv = load4<BF16>(a.q, e);
+      kv = load4<BF16>(a.k, e);
+      vv = load4<BF16>(a.v, e);
+      dov = *reinterpret_cast<const f32x4*>(a.d_o + e);
     }
-    const float G = sG[r * LDG + j], Gc = sG[cref * LDG + j], Gn = sG[(C - 1) * LDG + j];
     const float be = sB[r];
-    const float eRel = __expf(G - Gc), eInv = __expf(Gc - G), eAbs = __expf(G), eTail = __expf(Gn - G);
+    f32x4 kp, km, qp, xa, qa, kt, yb, xp, gg;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float G = sG[r * LDG + j + i], Gc = sG[cref * LDG + j + i], Gn = sG[(C - 1) * LDG + j + i];
+      const float eRel = __expf(G - Gc), eInv = __expf(Gc - G), eAbs = __expf(G), eTail = __expf(Gn - G);
+      kp[i] = kv[i] * eRel;
+      km[i] = kv[i] * eInv;
+      qp[i] = qv[i] * eRel;
+      xa[i] = be * (kv[i] * eAbs);
+      qa[i] = qv[i] * eAbs;
+      kt[i] = kv[i] * eTail;
+      yb[i] = be * vv[i];
+      xp[i] = be * (kv[i] * eRel);
+      gg[i] = G;
+    }
     const int64_t o = b * C * D + idx;
-    ws[nd_off(KP, units, D) + o] = kv * eRel;
-    ws[nd_off(KM, units, D) + o] = kv * eInv;
-    ws[nd_off(QP, units, D) + o] = qv * eRel;
-    ws[nd_off(XA, units, D) + o] = be * (kv * eAbs);
-    ws[nd_off(QA, units, D) + o] = qv * eAbs;
-    ws[nd_off(KT, units, D) + o] = kv * eTail;
-    ws[nd_off(YB, units, D) + o] = be * vv;
-    ws[nd_off(DOF, units, D) + o] = dov;
-    ws[nd_off(XP, units, D) + o] = be * (kv * eRel);
-    ws[nd_off(GG, units, D) + o] = G;
+    auto st = [&](int arr, f32x4 x) { *reinterpret_cast<f32x4*>(ws + nd_off(arr, units, D) + o) = x; };
+    st(KP, kp);
+    st(KM, km);
+    st(QP, qp);
+    st(XA, xa);
+    st(QA, qa);
+    st(KT, kt);
+    st(YB, yb);
+    st(DOF, dov);
+    st(XP, xp);
+    st(GG, gg);
   }
   if (tid < D) ws[egn_off(units, D) + b * D + tid] = __expf(sG[(C - 1) * LDG + tid]);
   if (tid < C) ws[beta_off(units, D) + b * C + tid] = sB[tid];
