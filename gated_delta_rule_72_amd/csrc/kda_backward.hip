@@ -226,7 +226,7 @@ struct GemmArgs {
 };
 
 // One workgroup = one 64 x 64 output tile of one unit; four wavefronts of 16
-// rows. K advances in blocks of 32 staged in LDS: A as [m][k] (row stride 36)
+// rows. C's ldc, its column offsets and its base are multiples of 4 floats. K advances in blocks of 32 staged in LDS: A as [m][k] (row stride 36)
 // and B as [k][n] (row stride 80), strides that put the 64 lanes of each
 // operand read on distinct banks.
 template <bool TA, bool TB>
@@ -278,22 +278,28 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
       for (int ks = 0; ks < KB / 4; ++ks) {
         const float av = As[(16 * w + l16) * LDA + 4 * ks + gq];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc[t] = mfma4(av, Bs[(4 * ks + gq) * LDB + 16 * t + l16], acc[t]);
+        for (int t = 0; t < 4; ++t) acc[t] = mfma4(Bs[(4 * ks + gq) * LDB + 16 * t + l16], av, acc[t]);
       }
       __syncthreads();
     }
   }
+  // the tiles were formed transposed (B as the MFMA's first operand), so a
+  // lane holds 4 consecutive columns of one row: one 16-byte store per tile
+  const int row = m0 + 16 * w + l16;
+  const float rsc = g.rs ? g.rs[b * g.srs + row] : 1.f;
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < 4; ++t) {
+    const int col0 = n0 + 16 * t + 4 * gq;
+    f32x4 x;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int row = m0 + 16 * w + 4 * gq + i, col = n0 + 16 * t + l16;
-      float x = g.alpha * acc[t][i];
-      if ((g.mask == 1 && row <= col) || (g.mask == 2 && row < col)) x = 0.f;
-      if (g.rs) x *= g.rs[b * g.srs + row];
-      float* cp = Cp + (int64_t)row * g.ldc + col;
-      *cp = g.accumulate ? *cp + x : x;
+      x[i] = g.alpha * acc[t][i];
+      if ((g.mask == 1 && row <= col0 + i) || (g.mask == 2 && row < col0 + i)) x[i] = 0.f;
+      if (g.rs) x[i] *= rsc;
     }
+    f32x4* cp = reinterpret_cast<f32x4*>(Cp + (int64_t)row * g.ldc + col0);
+    *cp = g.accumulate ? *cp + x : x;
+  }
 }
 
 // ---- (I + L)^-1 with L = strict_lower(Diag(beta) P): one column per lane --
